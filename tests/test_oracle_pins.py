@@ -1,0 +1,361 @@
+"""Pins for the CPU oracle: each check ties an oracle function to something other than
+itself -- values printed on the pages (tests/golden), closed forms, invariants, library
+routines, or brute force on tiny inputs."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+from scipy.special import expit
+
+from conftest import golden
+import oracle as O
+import workloads as W
+
+F32 = np.float32
+
+
+# ------------------------------------------------------------------ activation quantization
+def test_act_worked_example_p5():
+    g = golden("act_int8_worked_example.json")
+    x = np.array([g["input"]], F32)
+    q, s = O.quant_act(x)
+    assert q.tolist() == [g["codes"]]
+    assert abs(float(s[0]) - g["scale_approx"]) < g["scale_abs_tol"]
+    xhat = O.dequant_act(q, s)[0]
+    assert np.allclose(np.round(xhat, 3), g["dequant_3dp"], atol=1.5e-3)
+    # the same codes when the input is first rounded to bfloat16
+    xb = W.bf16_values(W.to_bf16(x))
+    qb, _ = O.quant_act(xb)
+    assert qb.tolist() == [g["codes"]]
+
+
+def test_act_outlier_example_p5():
+    g = golden("act_outlier_example.json")
+    q, s = O.quant_act(np.array([g["input"]], F32))
+    assert q.tolist() == [g["codes"]]
+    assert abs(float(s[0]) - g["scale_approx"]) < g["scale_abs_tol"]
+
+
+def test_act_page1_snippet_reading_same_codes():
+    """P1 section 3.3 adds eps=1e-8 to the scale and clamps to [-128, 127]; the chosen reading
+    (no eps, [-127, 127]) gives the same codes on both printed examples."""
+    for name in ("act_int8_worked_example.json", "act_outlier_example.json"):
+        x = np.array([golden(name)["input"]], F32)
+        amax = np.max(np.abs(x), axis=1, keepdims=True)
+        s_eps = (amax / F32(127) + F32(1e-8)).astype(F32)
+        q_eps = np.clip(np.rint(x / s_eps), -128, 127).astype(np.int8)
+        q, _ = O.quant_act(x)
+        assert np.array_equal(q, q_eps)
+
+
+def test_act_bruteforce_elementwise():
+    """Element-by-element pure-python evaluation of the per-token rule on a small matrix."""
+    x = W.bf16_values(W.random_activations(5, 7, 37, outlier_cols=2, outlier_scale=30.0))
+    q, s = O.quant_act(x)
+    for m in range(x.shape[0]):
+        amax = F32(0)
+        for v in x[m]:
+            amax = max(amax, F32(abs(v)))
+        sm = F32(amax / F32(127))
+        assert s[m] == sm
+        for kk in range(x.shape[1]):
+            r = F32(x[m, kk] / sm)
+            lo = np.floor(r)
+            frac = r - lo
+            ref = lo + 1 if frac > 0.5 or (frac == 0.5 and lo % 2 == 1) else lo
+            assert q[m, kk] == int(max(-127, min(127, ref)))
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 6), st.integers(1, 70), st.integers(0, 2**31 - 1), st.floats(1e-3, 1e3))
+def test_act_properties(M, K, seed, mag):
+    x = (np.random.default_rng(seed).standard_normal((M, K)) * mag).astype(F32)
+    q, s = O.quant_act(x)
+    assert q.dtype == np.int8 and s.dtype == F32
+    assert np.all(np.abs(q.astype(int)) <= 127)
+    # the abs-max element maps to +-127
+    for m in range(M):
+        i = np.argmax(np.abs(x[m]))
+        assert abs(int(q[m, i])) == 127
+    # round-trip bound |x - q s| <= s/2 (with float32 slack)
+    err = np.abs(x.astype(np.float64) - O.dequant_act(q, s))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 1e-5))
+    # idempotence on the dequantized grid
+    q2, s2 = O.quant_act(O.dequant_act(q, s).astype(F32))
+    assert np.array_equal(q2, q)
+
+
+def test_act_zero_and_nonfinite_rows():
+    x = np.array([[0, 0, 0, 0], [1, np.nan, 2, 3], [np.inf, 1, 2, 3], [-4, 2, 0, 1]], F32)
+    q, s = O.quant_act(x)
+    assert s[0] == 0 and not q[0].any()
+    assert np.isnan(s[1]) and not q[1].any()
+    assert np.isnan(s[2]) and not q[2].any()
+    assert q[3].tolist() == [-127, 64, 0, 32] and s[3] == F32(F32(4) / F32(127))
+
+
+# ------------------------------------------------------------------ weight quantization
+def test_sym_groupwise_reference_example_p3():
+    g = golden("sym_groupwise_reference.json")
+    x = np.array(g["input"], F32)
+    # the page's groups run along the last dimension; the oracle groups along K (rows), so
+    # the page's [2, 4] example is the transpose: K = 4, N = 2.
+    codes, scales, zeros = O.quant_weight(x.T, g["group_size"], asymmetric=False)
+    assert zeros is None
+    assert codes.T.tolist() == g["codes_hand_derived"]
+    assert codes.min() >= -7 and codes.max() <= 7
+    restored = O.dequant_weight(codes, scales, None, g["group_size"])
+    err = np.abs(x.T.astype(np.float64) - restored)
+    assert np.all(err <= scales.astype(np.float64) / 2 + g["bound_abs_slack"])
+    assert scales[0].tolist() == [F32(F32(1) / F32(7)), F32(F32(3) / F32(7))]
+    zc, zs, _ = O.quant_weight(np.zeros((4, 1), F32), 4, asymmetric=False)
+    assert not zc.any() and zs[0, 0] == 0
+    assert not O.dequant_weight(zc, zs, None, 4).any()
+    with pytest.raises(ValueError):
+        O.quant_weight(np.ones((3, 2), F32), 2, asymmetric=False)   # groups cannot cross
+    with pytest.raises(ValueError):
+        O.quant_weight(np.ones((4, 2), F32), 0, asymmetric=False)
+
+
+def test_sym_rounding_uses_ieee_division():
+    """0.5 / fl32(1/7) = 3.4999998 in float32 -> code 3, whereas the real-valued quotient
+    0.5 / (1/7) = 3.5 would round (half to even) to 4: the page example's third element pins
+    that the quotient is taken in float32 against the stored float32 scale."""
+    codes, _, _ = O.quant_weight(np.array([[0.0], [-1.0], [0.5], [0.25]], F32), 4, False)
+    assert codes[2, 0] == 3
+    s = F32(F32(1) / F32(7))
+    assert F32(0.5) / s < 3.5 and np.rint(0.5 / (1.0 / 7.0)) == 4
+
+
+def test_asym_range_example_p2():
+    g = golden("asym_range_example.json")
+    w = np.array([[g["w_min"]], [0.0], [0.4], [g["w_max"]]], F32)
+    codes, scales, zeros = O.quant_weight(w, 4, asymmetric=True)
+    s = float(scales[0, 0])
+    assert abs(s - g["scale_approx"]) < 1e-6
+    assert int(zeros[0, 0]) in g["zero_point_choices"]
+    assert codes[1, 0] == zeros[0, 0]              # float 0 maps exactly to z
+    assert codes.min() >= 0 and codes.max() <= g["levels"]
+    assert codes[0, 0] == 0 and codes[3, 0] == 15   # ends of the range
+    xhat = O.dequant_weight(codes, scales, zeros, 4)
+    assert xhat[1, 0] == 0.0
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.sampled_from([4, 8, 32, 64, 128]), st.integers(1, 4), st.integers(1, 9),
+       st.integers(0, 2**31 - 1), st.booleans(), st.floats(-0.05, 0.05))
+def test_weight_properties(g, G, N, seed, asym, shift):
+    rs = np.random.default_rng(seed)
+    w = (rs.standard_normal((g * G, N)) * 0.02 + shift).astype(F32)
+    if G > 1:
+        w[:g, 0] = 0.0                                   # an all-zero group
+    codes, scales, zeros = O.quant_weight(w, g, asym)
+    lo, hi = (0, 15) if asym else (-7, 7)
+    assert codes.min() >= lo and codes.max() <= hi
+    xhat = O.dequant_weight(codes, scales, zeros, g)
+    s_full = np.repeat(scales.astype(np.float64), g, axis=0)
+    assert np.all(np.abs(w - xhat) <= s_full / 2 * (1 + 1e-5) + 1e-12)
+    if G > 1:
+        assert scales[0, 0] == 0 and not codes[:g, 0].any() and not xhat[:g, 0].any()
+    if asym:
+        # zero is represented exactly: every group's zero point is a valid code
+        assert zeros.max() <= 15
+        # groups straddling zero use both ends of the range when max = -min
+    else:
+        # symmetric: the abs-max element of each nonzero group reaches +-7
+        wg = w.reshape(G, g, N)
+        cg = codes.reshape(G, g, N)
+        for i, n in itertools.product(range(G), range(N)):
+            if scales[i, n] > 0:
+                j = np.argmax(np.abs(wg[i, :, n]))
+                assert abs(int(cg[i, j, n])) == 7
+
+
+def test_weight_nonfinite_rejected():
+    w = np.zeros((4, 2), F32)
+    w[1, 1] = np.nan
+    with pytest.raises(ValueError):
+        O.quant_weight(w, 4, False)
+
+
+# ------------------------------------------------------------------ GEMM
+def _tiny_problem(seed, M, K, N, g, asym):
+    x = W.bf16_values(W.random_activations(seed, M, K, outlier_cols=1, outlier_scale=10.0))
+    w = W.random_weights(seed + 1, K, N)
+    xq, sx = O.quant_act(x)
+    codes, scales, zeros = O.quant_weight(w, g, asym)
+    return xq, sx, codes, scales, zeros
+
+
+@pytest.mark.parametrize("M,K,N,g,asym", [(3, 64, 5, 32, False), (5, 128, 7, 64, True),
+                                          (2, 256, 3, 128, True), (4, 96, 6, 32, True)])
+def test_partials_bruteforce(M, K, N, g, asym):
+    xq, sx, codes, scales, zeros = _tiny_problem(11, M, K, N, g, asym)
+    P = O.gemm_partials(xq, codes, zeros, g)
+    for m, n, i in itertools.product(range(M), range(N), range(K // g)):
+        z = int(zeros[i, n]) if asym else 0
+        ref = 0
+        for kk in range(i * g, (i + 1) * g):
+            ref += int(xq[m, kk]) * (int(codes[kk, n]) - z)
+        assert P[m, n, i] == ref
+
+
+@pytest.mark.parametrize("M,K,N,g,asym", [(3, 64, 5, 32, False), (5, 128, 7, 64, True),
+                                          (6, 512, 9, 128, False), (2, 256, 4, 64, True)])
+def test_gemm_bruteforce_dequant(M, K, N, g, asym):
+    """Y equals (s_x * x_q) @ (s_w * (q - z)) evaluated term by term in float64."""
+    xq, sx, codes, scales, zeros = _tiny_problem(23, M, K, N, g, asym)
+    Y = O.gemm(xq, sx, codes, scales, zeros, g)
+    for m, n in itertools.product(range(M), range(N)):
+        ref = 0.0
+        for kk in range(K):
+            i = kk // g
+            z = float(zeros[i, n]) if asym else 0.0
+            ref += (float(sx[m]) * float(xq[m, kk])) * (float(scales[i, n]) * (float(codes[kk, n]) - z))
+        assert abs(Y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref)) + 1e-15
+
+
+def test_zero_point_expansion_p5():
+    """P5 section 7: sum x (q - z) = sum x q - z sum x (zp_x = 0), exactly in integers."""
+    xq, sx, codes, scales, zeros = _tiny_problem(3, 4, 256, 6, 64, True)
+    P = O.gemm_partials(xq, codes, zeros, 64)
+    P_nozp = O.gemm_partials(xq, codes, None, 64)
+    rs = xq.astype(np.int64).reshape(4, 4, 64).sum(axis=2)           # [M, G]
+    assert np.array_equal(P, P_nozp - zeros.astype(np.int64).T[None, :, :] * rs[:, None, :])
+
+
+def test_integer_matmul_when_one_group_unit_scales():
+    rs = np.random.default_rng(1)
+    xq = rs.integers(-127, 128, (5, 64)).astype(np.int8)
+    codes = rs.integers(-7, 8, (64, 3)).astype(np.int8)
+    ones = np.ones((1, 3), F32)
+    Y = O.gemm(xq, np.ones(5, F32), codes, ones, None, 64)
+    assert np.array_equal(Y, (xq.astype(np.int64) @ codes.astype(np.int64)).astype(np.float64))
+    P = O.gemm_partials(xq, codes, None, 64)
+    assert np.array_equal(P[:, :, 0], xq.astype(np.int64) @ codes.astype(np.int64))
+
+
+def test_per_channel_closed_form_p5():
+    """With g = K the epilogue is P5 section 8.3: Y[i, j] = s_x[i] s_w[j] acc_int32[i, j]."""
+    xq, sx, codes, scales, zeros = _tiny_problem(9, 6, 256, 5, 256, False)
+    acc = xq.astype(np.int64) @ codes.astype(np.int64)
+    Y = O.gemm(xq, sx, codes, scales, None, 256)
+    ref = sx.astype(np.float64)[:, None] * scales[0].astype(np.float64)[None, :] * acc
+    assert np.allclose(Y, ref, rtol=1e-14, atol=0)
+
+
+def test_gemm_linear_in_scales_and_rows():
+    xq, sx, codes, scales, zeros = _tiny_problem(4, 4, 256, 6, 128, True)
+    Y = O.gemm(xq, sx, codes, scales, zeros, 128)
+    Y2 = O.gemm(xq, sx * F32(2), codes, scales, zeros, 128)
+    assert np.array_equal(Y2, 2 * Y)
+    perm = np.array([2, 0, 3, 1])
+    assert np.array_equal(O.gemm(xq[perm], sx[perm], codes, scales, zeros, 128), Y[perm])
+
+
+# ------------------------------------------------------------------ silu / requant
+def test_silu_mul_library_and_identity():
+    rs = np.random.default_rng(0)
+    gu = W.bf16_values(W.to_bf16(rs.standard_normal((5, 16)).astype(F32) * 4))
+    h = O.silu_mul(gu)
+    g, u = gu[:, :8].astype(np.float64), gu[:, 8:].astype(np.float64)
+    assert np.allclose(h, g * expit(g) * u, rtol=1e-13, atol=0)
+    # silu(x) - silu(-x) = x: catches a sign error in the exponent
+    x = np.linspace(-9, 9, 37)
+    sp = O.silu_mul(np.concatenate([x[None], np.ones((1, 37))], 1))
+    sm = O.silu_mul(np.concatenate([-x[None], np.ones((1, 37))], 1))
+    assert np.allclose(sp - sm, x[None], atol=1e-12)
+    assert O.silu_mul(np.array([[0.0, 5.0]]))[0, 0] == 0.0
+
+
+def test_silu_mul_quant_is_per_row():
+    rs = np.random.default_rng(2)
+    gu = rs.standard_normal((6, 32)).astype(F32)
+    q, s = O.silu_mul_quant(gu)
+    h = O.silu_mul(gu).astype(F32)
+    q2, s2 = O.quant_act(h)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    assert np.all(np.abs(q.astype(int)).max(axis=1) == 127)
+
+
+# ------------------------------------------------------------------ MoE
+def test_moe_align_invariants():
+    rs = np.random.default_rng(7)
+    T, k, E = 37, 4, 9
+    ids = np.stack([rs.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    rows, off, inv = O.moe_align(ids, E)
+    assert sorted(rows.tolist()) == list(range(T * k))               # each (t, j) once
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(ids.ravel(), minlength=E))]))
+    for e in range(E):
+        seg = rows[off[e]:off[e + 1]]
+        assert np.all(ids.ravel()[seg] == e) and np.all(np.diff(seg) > 0)   # stable
+    for t, j in itertools.product(range(T), range(k)):
+        assert rows[inv[t, j]] == t * k + j
+    with pytest.raises(ValueError):
+        O.moe_align(np.array([[E]], np.int32), E)
+
+
+def _moe_small(E=3, T=9, k=2, H=128, I=64, g=64, asym=True, seed=5):
+    rs = np.random.default_rng(seed)
+    x = W.bf16_values(W.random_activations(seed, T, H))
+    ids = np.stack([rs.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    wts = rs.random((T, k)).astype(F32)
+    experts = {}
+    for e in range(E):
+        wgu = W.random_weights(seed * 10 + e, H, 2 * I)
+        wd = W.random_weights(seed * 10 + e + 100, I, H)
+        experts[e] = O.quant_weight(wgu, g, asym) + O.quant_weight(wd, g, asym)
+    return x, ids, wts, experts, E, I, g
+
+
+def test_moe_single_expert_reduces_to_dense_chain():
+    x, ids, wts, experts, E, I, g = _moe_small(E=1, k=1)
+    ids[:] = 0
+    wts[:] = 1.0
+    r = O.moe_layer(x, ids, wts, lambda e: experts[e], 1, I, g)
+    cg, sg, zg, cd, sd, zd = experts[0]
+    xq, sx = O.quant_act(x)
+    gu = O.bf16_rne(O.gemm(xq, sx, cg, sg, zg, g))
+    hq, sh = O.silu_mul_quant(gu)
+    y = O.bf16_rne(O.gemm(hq, sh, cd, sd, zd, g))
+    assert np.array_equal(r["out"], O.bf16_rne(y.astype(np.float64)))
+
+
+def test_moe_token_permutation_and_combine_linearity():
+    x, ids, wts, experts, E, I, g = _moe_small()
+    f = lambda e: experts[e]
+    r = O.moe_layer(x, ids, wts, f, E, I, g)
+    perm = np.random.default_rng(0).permutation(x.shape[0])
+    rp = O.moe_layer(x[perm], ids[perm], wts[perm], f, E, I, g)
+    assert np.array_equal(rp["out64"], r["out64"][perm])
+    r2 = O.moe_layer(x, ids, wts * F32(2), f, E, I, g)
+    assert np.allclose(r2["out64"], 2 * r["out64"], rtol=1e-15, atol=0)
+    # swapping the order of a token's choices (ids and weights together) changes nothing
+    # beyond float64 summation order
+    rs_ = O.moe_layer(x, ids[:, ::-1].copy(), wts[:, ::-1].copy(), f, E, I, g)
+    assert np.allclose(rs_["out64"], r["out64"], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ closed forms / bf16
+def test_size_closed_forms():
+    c = golden("size_closed_forms.json")
+    assert O.effective_bits(4, 16, 0, 128) * 128 == c["g128_bits"]
+    assert O.effective_bits(4, 16, 0, 32) * 128 == c["g32_bits"]
+    assert round(O.compression_vs_fp16(128), 2) == c["g128_ratio_2dp"]
+    assert round(O.compression_vs_fp16(32), 2) == c["g32_ratio_2dp"]
+    assert O.effective_bits(4, 32, 0, 128) == 4.25
+    assert O.effective_bits(4, 32, 8, 128) == 4.3125
+    assert O.effective_bits(4, 32, 8, 64) == 4.625
+    n = 4096 * 14336
+    assert O.memory_bytes(n, 4, n // 128, 4) == n / 2 + n // 128 * 4
+
+
+def test_bf16_rne_matches_torch():
+    rs = np.random.default_rng(3)
+    v = np.concatenate([rs.standard_normal(20000) * 10.0 ** rs.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1e-40, -3e-39, 3.3e38, 1.0 + 2**-8, 1.0 + 3 * 2**-8]]).astype(F32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(O.bf16_rne(v), ref)
+    assert np.isinf(O.bf16_rne(np.array([3.5e38]))[0])
