@@ -1,0 +1,344 @@
+"""Benchmark of the W4A8 hot path on one MI355X.
+
+Headline (the `value`): the decode-shape fused gate/up projection, K=4096, N=14336,
+symmetric INT4 g128 weights from N(0, 0.02), bf16 activations N(0, 1) with 0.1% outlier
+channels x50.  One step = for M in (1, 8, 32): per-token INT8 quantization of X[M, K]
+followed by the W4A8 GEMM (bf16 out).  value = weight+scale bytes streamed per step / step
+time, in GB/s.  Each GEMM reads a different one of 16 device copies of the packed weights
+(16 x 31.2 MB > the 256 MB Infinity Cache), so weights come from HBM.
+
+Extra fields (same JSON line): prefill INT8 TOPS of the projection pair at M=4096
+(asymmetric g128), and MoE layer tokens/s of the 64-expert top-6 layer (T=512) and the
+256-expert top-8 decode layer (T=64, asymmetric g64).
+
+`roofline` is the decode GEMM at M=32 (the dominant kernel of the step), timed with HIP
+events on the launch stream inside the timed region; `cpu_baseline` is the CPU oracle on
+the same decode step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=16, help="device copies of the decode weights")
+    p.add_argument("--no-extra", action="store_true", help="skip the prefill and MoE figures")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--only", default="", help="comma list of legs: decode,prefill,moe")
+    p.add_argument("--no-graph", action="store_true", help="launch the decode steps eagerly")
+    return p.parse_args()
+
+
+def random_device_blobs(L, d, E, seed, dev):
+    """E packed expert blobs of desc d, generated on the device: codes uniform over the
+    format's range, scales |N(0, 0.02)|/7 + 1e-4, zero points in [4, 11].  The header bytes
+    come from the library's packer (they are never read by the kernels)."""
+    import torch
+    n = L.w4a8_packed_size(d)
+    G = d.K // d.group_size
+    Np = (d.N + 15) // 16 * 16
+    hdr = L.w4a8_pack_codes(L.desc(128, d.N, d.group_size, d.asymmetric), np.zeros((128, d.N), np.int8),
+                            np.zeros((128 // d.group_size, d.N), np.float32),
+                            np.zeros((128 // d.group_size, d.N), np.uint8) if d.asymmetric else None)[:256].copy()
+    # patch K and the section table of the header for the real desc
+    import struct
+    codes_b = Np * d.K // 2
+    al = lambda v: (v + 255) // 256 * 256
+    so = al(256 + codes_b)
+    zo = al(so + Np * G * 4)
+    struct.pack_into("<iiii", hdr, 16, d.K, d.N, d.group_size, d.asymmetric)
+    struct.pack_into("<7Q", hdr, 40, 256, codes_b, so, Np * G * 4, zo, Np * G if d.asymmetric else 0, n)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    buf = torch.empty(E * n, dtype=torch.uint8, device=dev)
+    for e in range(E):
+        b = buf[e * n:(e + 1) * n]
+        b[:256].copy_(torch.from_numpy(hdr))
+        if d.asymmetric:
+            nib = torch.randint(0, 16, (codes_b, 2), device=dev, generator=g, dtype=torch.int16)
+        else:
+            nib = torch.randint(-7, 8, (codes_b, 2), device=dev, generator=g, dtype=torch.int16) & 0xF
+        b[256:256 + codes_b].copy_((nib[:, 0] | (nib[:, 1] << 4)).to(torch.uint8))
+        sc = (torch.randn(Np * G, device=dev, generator=g).abs() * (0.02 / 7) + 1e-4).float()
+        b[so:so + Np * G * 4].copy_(sc.view(torch.uint8))
+        if d.asymmetric:
+            b[zo:zo + Np * G].copy_(torch.randint(4, 12, (Np * G,), device=dev, generator=g).to(torch.uint8))
+    return buf, n
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every launch below uses)."""
+
+    def __init__(self, torch):
+        self.t = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.t.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.t.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        self.t.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+# ---------------------------------------------------------------------------------- decode
+def decode_leg(args, L, W, torch, dev):
+    cfg = W.C2
+    d = L.desc(cfg.K, cfg.N, cfg.group_size, cfg.asymmetric)
+    _, Wt = W.dense_inputs(cfg, M=1)
+    host = L.w4a8_pack(d, Wt)
+    n = L.w4a8_packed_size(d)
+    copies = torch.empty((args.copies, n), dtype=torch.uint8, device=dev)
+    one = torch.from_numpy(host).to(dev)
+    for c in range(args.copies):
+        copies[c].copy_(one)
+    Ms = W.C2_M
+    X, Xq, sx, Y = {}, {}, {}, {}
+    for M in Ms:
+        Xb, _ = W.dense_inputs(W.with_decode_m(cfg, M))
+        X[M] = Xb.to(dev)
+        Xq[M] = torch.empty((M, cfg.K), dtype=torch.int8, device=dev)
+        sx[M] = torch.empty(M, dtype=torch.float32, device=dev)
+        Y[M] = torch.empty((M, cfg.N), dtype=torch.bfloat16, device=dev)
+    wbytes = cfg.K * cfg.N // 2 + (cfg.K // cfg.group_size) * cfg.N * 4   # codes + scales
+    counter = [0]
+
+    def step():
+        for M in Ms:
+            c = counter[0] % args.copies
+            counter[0] += 1
+            L.w4a8_quant_act(X[M], Xq[M], sx[M])
+            L.w4a8_gemm(Xq[M], sx[M], copies[c], d, Y[M], L.W4A8_OUT_BF16)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # One graph holds `per_graph` steps, a whole period of the weight-copy rotation, so
+    # replaying it keeps every GEMM on a copy that was not read for 15 launches.
+    per_graph = args.copies
+    counter[0] = 0
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                step()
+        graph.replay()
+        torch.cuda.synchronize()
+    reps = max(1, (args.steps + per_graph - 1) // per_graph)
+    steps = reps * per_graph
+    t0 = time.perf_counter()
+    if graph is not None:
+        for _ in range(reps):
+            graph.replay()
+    else:
+        for _ in range(steps):
+            step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt * 1e3 / steps
+    value = len(Ms) * wbytes * steps / dt / 1e9
+    # the dominant kernel (decode GEMM, M = 32) timed launch by launch with HIP events on
+    # its stream, on rotating weight copies
+    kt = Timer(torch)
+    for i in range(64):
+        s = kt.start()
+        L.w4a8_gemm(Xq[32], sx[32], copies[i % args.copies], d, Y[32], L.W4A8_OUT_BF16)
+        kt.stop(s)
+    k_ms = kt.mean_ms()
+    M = 32
+    kbytes = wbytes + M * cfg.K + 4 * M + 2 * M * cfg.N    # + Xq, sx, Y (bf16)
+    achieved = kbytes / (k_ms * 1e-3) / 1e9
+    return dict(value=value, ms_per_step=ms_step, steps=steps, weight_bytes=wbytes, kernel_ms=k_ms,
+                kernel_bytes=kbytes, achieved=achieved, kernel=L.w4a8_kernel_name(d, 32), host_blob=host, Wt=Wt,
+                graph=graph is not None)
+
+
+def cpu_baseline(args, leg, W):
+    """The oracle on the same decode step (weights quantized once, outside the timing)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cfg = W.C2
+    codes, scales, zeros = O.quant_weight(leg["Wt"], cfg.group_size, cfg.asymmetric)
+    xs = {M: W.bf16_values(W.dense_inputs(W.with_decode_m(cfg, M))[0]) for M in W.C2_M}
+
+    def one_step():
+        for M in W.C2_M:
+            q, s = O.quant_act(xs[M])
+            O.bf16_rne(O.gemm(q, s, codes, scales, zeros, cfg.group_size))
+
+    one_step()                                        # warm-up
+    n, t0 = 0, time.perf_counter()
+    while True:
+        one_step()
+        n += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds or n >= 50:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": len(W.C2_M) * leg["weight_bytes"] * n / dt / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} full decode steps (quant + GEMM for M=1,8,32; K=4096, N=14336) in {dt:.1f} s; "
+                      f"numpy/BLAS, weights quantized once beforehand"}
+
+
+# ---------------------------------------------------------------------------------- prefill
+def prefill_leg(args, L, W, torch, dev, steps):
+    out = {}
+    for cfg in (W.C3_UP, W.C3_DOWN):
+        d = L.desc(cfg.K, cfg.N, cfg.group_size, cfg.asymmetric)
+        _, Wt = W.dense_inputs(cfg, M=1)
+        blob = torch.from_numpy(L.w4a8_pack(d, Wt)).to(dev)
+        del Wt
+        X = W.random_activations(cfg.seed + 7919, cfg.M, cfg.K).to(dev)
+        Xq = torch.empty((cfg.M, cfg.K), dtype=torch.int8, device=dev)
+        sx = torch.empty(cfg.M, dtype=torch.float32, device=dev)
+        Y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            L.w4a8_quant_act(X, Xq, sx)
+            L.w4a8_gemm(Xq, sx, blob, d, Y)
+        tg, tq = Timer(torch), Timer(torch)
+        for _ in range(steps):
+            s = tq.start()
+            L.w4a8_quant_act(X, Xq, sx)
+            tq.stop(s)
+            s = tg.start()
+            L.w4a8_gemm(Xq, sx, blob, d, Y)
+            tg.stop(s)
+        g_ms, q_ms = tg.mean_ms(), tq.mean_ms()
+        ops = 2.0 * cfg.M * cfg.N * cfg.K
+        out[cfg.name] = dict(gemm_ms=g_ms, quant_ms=q_ms, tops=ops / (g_ms * 1e-3) / 1e12,
+                             tops_with_quant=ops / ((g_ms + q_ms) * 1e-3) / 1e12,
+                             frac_int8_peak=ops / (g_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                             kernel=L.w4a8_kernel_name(d, cfg.M))
+        del blob, X, Xq, Y
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------------- MoE
+def moe_leg(args, L, W, torch, dev, steps):
+    out = {}
+    for cfg, seed in ((W.C4, 4), (W.C5, 5)):
+        ids, w = W.moe_routing(cfg)
+        gud = L.desc(cfg.H, 2 * cfg.I, cfg.group_size, cfg.asymmetric)
+        dd = L.desc(cfg.I, cfg.H, cfg.group_size, cfg.asymmetric)
+        gu, gstride = random_device_blobs(L, gud, cfg.E, seed * 7, dev)
+        dn, dstride = random_device_blobs(L, dd, cfg.E, seed * 11, dev)
+        X = W.moe_activations(cfg).to(dev)
+        ids_d = torch.from_numpy(ids).to(dev)
+        w_d = torch.from_numpy(w).to(dev)
+        ws = torch.empty(L.w4a8_moe_workspace_size(cfg.T, cfg.topk, cfg.H, cfg.I, cfg.E), dtype=torch.uint8,
+                         device=dev)
+        o = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+
+        def run():
+            L.w4a8_moe_forward(X, ids_d, w_d, cfg.E, gu, gstride, gud, dn, dstride, dd, ws, o)
+
+        for _ in range(3):
+            run()
+        t = Timer(torch)
+        for _ in range(steps):
+            s = t.start()
+            run()
+            t.stop(s)
+        ms = t.mean_ms()
+        touched = len(set(ids.ravel().tolist()))
+        wbytes = touched * (gstride + dstride)
+        out[cfg.name] = dict(layer_ms=ms, tokens_per_s=cfg.T / (ms * 1e-3), experts_touched=touched,
+                             weight_gbs=wbytes / (ms * 1e-3) / 1e9,
+                             frac_hbm=wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        del gu, dn, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import moe_token_int8_amd as L
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    L.lib()
+    legs = set(args.only.split(",")) if args.only else {"decode", "prefill", "moe"}
+    if args.no_extra:
+        legs = {"decode"}
+    print(f"[bench] decode leg: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
+    leg = decode_leg(args, L, W, torch, dev)
+    extra = {}
+    if "prefill" in legs:
+        print("[bench] prefill leg", file=sys.stderr, flush=True)
+        extra["prefill"] = prefill_leg(args, L, W, torch, dev, steps=10)
+    if "moe" in legs:
+        print("[bench] moe leg", file=sys.stderr, flush=True)
+        extra["moe"] = moe_leg(args, L, W, torch, dev, steps=20)
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args, leg, W)
+    rec = {
+        "metric": "W4A8 decode GEMM weight GB/s (M in {1,8,32}, K=4096, N=14336, quant+GEMM per step)",
+        "value": round(leg["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": leg["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(leg["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "decode_dense_linear", "M": list(W.C2_M), "K": W.C2.K, "N": W.C2.N,
+                   "group_size": W.C2.group_size, "asymmetric": False, "weight_copies": args.copies,
+                   "hip_graph": leg["graph"],
+                   "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(leg["achieved"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(leg["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": leg["kernel"], "kernel_ms": round(leg["kernel_ms"], 5),
+                     "kernel_bytes": leg["kernel_bytes"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

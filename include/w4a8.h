@@ -1,0 +1,246 @@
+/*
+ * w4a8.h -- C ABI of the MI355X (gfx950) W4A8 linear / MoE-expert library.
+ *
+ * W4A8: weights stored as 4-bit integers in groups along K with one float32
+ * scale (and, in asymmetric mode, one integer zero point) per group and output
+ * column; activations quantized per token to INT8 at run time; an INT8 x INT8
+ * -> INT32 GEMM whose weight nibbles are unpacked inside the kernel, with the
+ * weight and activation scales applied in a float32 epilogue.
+ *
+ * Sources (cited as P1..P5 with the page's own section names):
+ *   P1 "Kimi 2.7 MoE: from 4-bit storage to INT8 (W4A8)"                (pwwt.cn)
+ *   P2 "Kimi 2.7 MoE W4A8: 4-bit storage to INT8, deployment notes"     (xdnf.cn)
+ *   P3 "Quantization: formats, error and the real execution path"       (wineandchord.com)
+ *   P4 "Choosing a weight-quantization scheme and locating kernel hits" (xbrilliance.ai)
+ *   P5 "Inference quantization, chapter 1: the Linear layer"            (sgdbs.github.io)
+ *
+ * Conventions for every entry point
+ *   - Matrices are row-major.  X is [M, K], W is [K, N], Y is [M, N] (P5 section 1:
+ *     M = batch * seq_len, K = hidden, N = out features).
+ *   - The caller owns every buffer, host and device.  GPU entry points only
+ *     enqueue work on `stream` (a hipStream_t, NULL = the null stream) and never
+ *     allocate, free or synchronize.  Device pointers must stay valid until the
+ *     enqueued work completes.
+ *   - Return value: W4A8_OK (0) or a negative w4a8_status.  All argument checks
+ *     run on the host before anything is enqueued, so an error return means
+ *     nothing was launched.  W4A8_EHIP reports a launch failure seen right after
+ *     enqueueing.  There is no fallback path: a shape or format the kernels do
+ *     not implement returns W4A8_EUNSUPPORTED (P3 "Correctness contract" item 6
+ *     and P4: a fallback must be explicit and observable).
+ *   - Device buffers read with 128-bit loads (Xq, Hq, blobs) must be 16-byte
+ *     aligned; the library checks this and returns W4A8_EINVAL otherwise.
+ *   - Calls are thread-safe; the library keeps no mutable global state.
+ */
+#ifndef W4A8_H
+#define W4A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A8_OK = 0,
+    W4A8_EINVAL = -1,        /* bad argument: null pointer, bad shape, group not tiling K, ... */
+    W4A8_ESIZE = -2,         /* a caller-provided buffer is smaller than required             */
+    W4A8_EUNSUPPORTED = -3,  /* valid request the kernels do not implement (no fallback)       */
+    W4A8_EHIP = -4           /* the HIP runtime reported an error when launching               */
+} w4a8_status;
+
+typedef enum { W4A8_OUT_BF16 = 0, W4A8_OUT_F32 = 1 } w4a8_out_dtype;
+
+/* Weight format description (P3 "Four independent dimensions": object, format,
+ * granularity, execution types must each be stated).
+ *   K, N        weight matrix W[K, N]
+ *   group_size  g: consecutive k sharing one scale per column (P5 section 8.4);
+ *               must divide K.  Kernels implement g in {64, 128}; pack accepts
+ *               g in {32, 64, 128, 256}.
+ *   asymmetric  0: signed codes q in [-7, 7], zero point 0 (P3 "Basic mapping",
+ *                  symmetric form);
+ *               1: unsigned codes q in [0, 15] with a uint8 zero point z per
+ *                  group, w ~ s (q - z) (P3 "Basic mapping"; P5 section 6). */
+typedef struct {
+    int32_t K;
+    int32_t N;
+    int32_t group_size;
+    int32_t asymmetric;
+} w4a8_wdesc;
+
+/* ------------------------------------------------------------------------------------
+ * Packed weight blob ("the checkpoint"): header + codes + scales [+ zeros].
+ * P3 "Calibration and conversion" asks the converted artifact to record format,
+ * signedness, packing, scale axis and group size; the header does.
+ *
+ *   offset 0    header, W4A8_HEADER_BYTES bytes, little endian:
+ *               char magic[8] = "W4A8BLB1"; uint32 version = 1; uint32 layout = 1;
+ *               int32 K, N, group_size, asymmetric; uint32 scale_dtype = 0 (fp32);
+ *               uint32 zero_dtype = 0 (uint8); uint64 codes_off, codes_bytes,
+ *               scales_off, scales_bytes, zeros_off, zeros_bytes, total_bytes;
+ *               the rest is zero.
+ *   codes       Np = N rounded up to 16 (padding columns hold code 0, scale 0).
+ *               Superblock = 16 columns x 128 rows = 1024 bytes, stored as 64
+ *               lanes x 16 bytes; superblocks run over k first, then over the
+ *               column tile:  superblock index = (n / 16) * (K / 128) + k / 128.
+ *               Inside a superblock, for kk = k % 128 and c = n % 16:
+ *                 half = kk / 64, r = kk % 64, lane = (r / 16) * 16 + c, j = r % 16,
+ *                 byte = lane * 16 + half * 8 + (j / 8) * 4 + (j % 4),
+ *                 nibble = (j % 8) / 4   (0 = low 4 bits, 1 = high 4 bits).
+ *               So one 128-bit load per lane fetches 16 k of one column for two
+ *               64-deep MFMA steps, and the low/high nibbles of a 32-bit word are
+ *               the k and k+4 operands of the same byte position (P1 section 5.1:
+ *               tile format matched to the MFMA operand; P1 section 7, third pitfall).
+ *               Symmetric codes are stored as 4-bit two's complement; asymmetric
+ *               codes as unsigned 0..15.  Two codes per byte (P1 section 5.2).
+ *   scales      float32 [Np/16][K/g][16]: scale of (group i, column n) at
+ *               ((n/16) * (K/g) + i) * 16 + n % 16.
+ *   zeros       (asymmetric only) uint8, same index as scales.
+ *   Every section starts on a 256-byte boundary.
+ * ------------------------------------------------------------------------------------ */
+#define W4A8_HEADER_BYTES 256
+
+/* Bytes of the blob for `d` (header + codes + scales + zeros + alignment padding), the
+ * M = N b/8 + N_groups M_meta + M_pad term of P3 "Basic mapping" with the padding
+ * explicit.  Returns 0 if `d` is invalid. */
+size_t w4a8_packed_size(const w4a8_wdesc* d);
+
+/* Offline RTN quantization + packing on the host (P3 "Basic mapping"; P3 symmetric
+ * group-wise reference; P2 section 2.1).  W_host: float32 [K, N] row-major, finite.
+ * Per (group, column): symmetric s = fl32(max|w| / 7), q = clamp(rint(fl32(w / s)), -7, 7);
+ * asymmetric lo = min(0, min w), hi = max(0, max w), s = fl32(fl32(hi - lo) / 15),
+ * z = clamp(rint(fl32(-lo / s)), 0, 15), q = clamp(rint(fl32(w / s)) + z, 0, 15); an
+ * all-zero group gets s = 0, z = 0, q = 0.  Round half to even, IEEE float32 division.
+ * Writes w4a8_packed_size(d) bytes to blob_host.  EINVAL: bad desc, group not tiling K,
+ * non-finite weight; ESIZE: blob_bytes too small. */
+int w4a8_pack(const w4a8_wdesc* d, const float* W_host, void* blob_host, size_t blob_bytes);
+
+/* Pack externally produced codes (e.g. from GPTQ/AWQ, P2 section 3.2) without
+ * re-quantizing.  codes: int8 [K, N] in [-7, 7] (symmetric) or [0, 15] (asymmetric);
+ * scales: float32 [K/g, N]; zeros: uint8 [K/g, N] in [0, 15] (asymmetric) or NULL.
+ * EINVAL on out-of-range codes or zero points. */
+int w4a8_pack_codes(const w4a8_wdesc* d, const int8_t* codes, const float* scales,
+                    const uint8_t* zeros, void* blob_host, size_t blob_bytes);
+
+/* Inverse of the packing, on the host: checks the header and writes codes [K, N],
+ * scales [K/g, N] and (asymmetric) zeros [K/g, N]; d_out receives the header's desc.
+ * Any output pointer may be NULL to skip it.  EINVAL on a bad header. */
+int w4a8_unpack_codes(const void* blob_host, size_t blob_bytes, w4a8_wdesc* d_out,
+                      int8_t* codes, float* scales, uint8_t* zeros);
+
+/* Host check that blob_host's header describes `d` and fits in blob_bytes; to be run
+ * once when a blob is loaded (GPU entry points trust the desc they are given). */
+int w4a8_blob_check(const void* blob_host, size_t blob_bytes, const w4a8_wdesc* d);
+
+/* ------------------------------------------------------------------------------------
+ * GPU entry points
+ * ------------------------------------------------------------------------------------ */
+
+/* Per-token dynamic INT8 activation quantization (P1 section 3.3; P5 section 8.3;
+ * P2 section 3.3: a quantize node before each Linear).
+ *   X_bf16  device, bfloat16 [M, K] with row stride ldx >= K elements
+ *   Xq      device, int8 [M, K] dense (row stride K), 16-byte aligned, K % 16 == 0
+ *   sx      device, float32 [M]
+ * Per row: amax = max|x|; s = fl32(amax / 127); q = clamp(rint(fl32(x / s)), -127, 127)
+ * (divisor 1 when s == 0).  A row containing NaN or Inf gets s = NaN and q = 0.
+ * M == 0 is a no-op. */
+int w4a8_quant_act(const void* X_bf16, int M, int K, int ldx, int8_t* Xq, float* sx,
+                   void* stream);
+
+/* W4A8 GEMM Y = (s_x * Xq) (s_w * (q - z)) (P5 section 4 ideal path; P5 section 8.3
+ * epilogue Y[i, j] = s_x[i] s_w[j] acc[i, j], applied per K-group of P5 section 8.4).
+ *   Xq, sx    device, from w4a8_quant_act ([M, K] int8 dense, [M] float32)
+ *   blob_dev  device copy of a blob packed for `d` (K % 128 == 0 required)
+ *   Y         device, [M, N] with row stride ldy >= N, bfloat16 or float32 (out_dtype)
+ * The INT4 nibbles are unpacked in registers into INT8 MFMA operands; each group's INT32
+ * partial sum is scaled by its float32 weight scale into a float32 accumulator, the
+ * row scale is applied last, then the bfloat16 cast rounds to nearest even.  No
+ * dequantized weight is ever written to memory (P1 section 4.4 step 4; P5 section 3.2).
+ * M == 0 is a no-op. */
+int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob_dev,
+              const w4a8_wdesc* d, void* Y, int ldy, int out_dtype, void* stream);
+
+/* Test export of the same main loop: INT32 per-group partial sums
+ * P[m, n, i] = sum_{k in group i} Xq[m, k] (q[k, n] - z[i, n]) written to device
+ * int32 [M, N, K/g].  (P3 "Correctness contract" item 3: the accumulator covers the
+ * reduction: |P| <= g * 127 * 15 < 2^31.) */
+int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob_dev, const w4a8_wdesc* d,
+                       int32_t* P, void* stream);
+
+/* MoE dispatch by expert (P1 section 4.4, steps 2-3).
+ *   topk_ids       device int32 [T, k], each in [0, E)
+ *   sorted_rows    device int32 [T*k]: routed rows r = t*k + j grouped by expert,
+ *                  ascending r inside an expert (stable counting sort)
+ *   expert_offsets device int32 [E+1]: exclusive prefix sum of rows per expert
+ *   inv            device int32 [T, k]: position of row t*k + j in sorted_rows
+ * Ids outside [0, E) are counted nowhere and their inv entry is -1; the host cannot see
+ * device ids, so callers validate routing upstream.  E <= 1024, T*k <= 2^24. */
+int w4a8_moe_align(const int32_t* topk_ids, int T, int k, int E, int32_t* sorted_rows,
+                   int32_t* expert_offsets, int32_t* inv, void* stream);
+
+/* Expert-grouped W4A8 GEMM (P1 section 4.4 step 4, "the performance key").
+ *   Xq, sx         device activations; if `gather` is non-NULL, output row r (in sorted
+ *                  order) reads Xq/sx row gather[r] / k (token of the routed row);
+ *                  if NULL, row r reads row r (rows already permuted)
+ *   gather         device int32 [rows] or NULL (pass sorted_rows from w4a8_moe_align)
+ *   k              top-k (divisor for gather; ignored when gather is NULL)
+ *   expert_offsets device int32 [E+1]; rows [off[e], off[e+1]) use expert e
+ *   rows           T*k, total rows (= off[E])
+ *   blobs_dev      device, E blobs of desc `d`, expert e at blobs_dev + e * expert_stride
+ *   Y              device [rows, N] bfloat16 or float32, dense
+ * Experts with no rows read no weights. */
+int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int k,
+                  const int32_t* expert_offsets, int E, int rows, const void* blobs_dev,
+                  size_t expert_stride, const w4a8_wdesc* d, void* Y, int out_dtype,
+                  void* stream);
+
+/* SiLU-gated expert activation + per-row INT8 requantization for the down projection
+ * (P1 section 1 names SiLU; P1 section 3.1: per-expert activation scales).
+ *   GU_bf16  device bfloat16 [R, 2I]: gate = columns [0, I), up = [I, 2I)
+ *   Hq, sh   device int8 [R, I] (16-byte aligned, I % 16 == 0), float32 [R]
+ * h = fl32(g / (1 + exp(-g)) * u) in float32, then the per-token rule of w4a8_quant_act. */
+int w4a8_silu_mul_quant(const void* GU_bf16, int R, int I, int8_t* Hq, float* sh,
+                        void* stream);
+
+/* Un-permute and top-k weighted combine (P1 section 4.3: dequantize to 16-bit, multiply
+ * by the gate weight, accumulate; kept out of the integer domain).
+ *   Yd_bf16  device bfloat16 [T*k, H] in sorted order
+ *   inv      device int32 [T, k] from w4a8_moe_align
+ *   topk_w   device float32 [T, k]
+ *   out      device bfloat16 [T, H]
+ * out[t] = bf16(sum_{j=0..k-1} topk_w[t, j] * Yd[inv[t, j]]) in float32, j ascending. */
+int w4a8_moe_combine(const void* Yd_bf16, const int32_t* inv, const float* topk_w, int T,
+                     int k, int H, void* out_bf16, void* stream);
+
+/* Workspace bytes needed by w4a8_moe_forward for the given sizes (0 if invalid). */
+size_t w4a8_moe_workspace_size(int T, int k, int H, int I, int E);
+
+/* One MoE expert layer, the steps of P1 section 4.4 chained on `stream`:
+ * quant_act(X) -> moe_align -> moe_gemm(gate/up, gathered) -> silu_mul_quant ->
+ * moe_gemm(down) -> moe_combine.
+ *   X_bf16      device [T, H]; topk_ids / topk_w device [T, k]
+ *   gu_blobs    E blobs of desc gu_desc (K = H, N = 2I), stride gu_stride
+ *   d_blobs     E blobs of desc d_desc (K = I, N = H), stride d_stride
+ *   workspace   device, >= w4a8_moe_workspace_size(T, k, H, I, E) bytes, 256-aligned
+ *   out_bf16    device [T, H] */
+int w4a8_moe_forward(const void* X_bf16, const int32_t* topk_ids, const float* topk_w, int T,
+                     int k, int E, const void* gu_blobs, size_t gu_stride,
+                     const w4a8_wdesc* gu_desc, const void* d_blobs, size_t d_stride,
+                     const w4a8_wdesc* d_desc, void* workspace, size_t workspace_bytes,
+                     void* out_bf16, void* stream);
+
+/* Name of the kernel variant w4a8_gemm resolves to for (d, M), or "unsupported"
+ * (P4: record target and resolved backend so a silent fallback is visible). */
+const char* w4a8_kernel_name(const w4a8_wdesc* d, int M);
+
+/* Human-readable text of a w4a8_status. */
+const char* w4a8_status_string(int status);
+
+/* Library ABI version (1). */
+int w4a8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A8_H */

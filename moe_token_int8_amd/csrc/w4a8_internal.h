@@ -1,0 +1,22 @@
+// Internal declarations shared by the host and device translation units of the library.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/w4a8.h"
+
+namespace w4a8 {
+
+constexpr int SB_K = 128;   // superblock depth: 16 columns x 128 k = 1 KiB of packed codes
+
+struct Layout {
+    int K, N, Np, g, G, asym;
+    size_t codes_off, codes_bytes, scales_off, scales_bytes, zeros_off, zeros_bytes, total;
+};
+
+bool desc_valid(const w4a8_wdesc* d);
+int desc_status(const w4a8_wdesc* d);   // OK, EINVAL (bad desc) or EUNSUPPORTED (layout)
+Layout layout_of(const w4a8_wdesc* d);
+
+}  // namespace w4a8

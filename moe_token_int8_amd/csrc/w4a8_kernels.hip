@@ -1,0 +1,907 @@
+// gfx950 (CDNA4) kernels and GPU entry points of the W4A8 library.
+//
+// Sources (cited as P1..P5 with the page's own section names):
+//   P1 "Kimi 2.7 MoE: from 4-bit storage to INT8 (W4A8)"              (pwwt.cn)
+//   P3 "Quantization: formats, error and the real execution path"     (wineandchord.com)
+//   P5 "Inference quantization, chapter 1: the Linear layer"          (sgdbs.github.io)
+//
+// Data path of the GEMM (P5 section 4 "ideal path", P1 sections 4.4 and 5.2):
+//   packed INT4 codes --128-bit load--> registers --shift/mask--> INT8 MFMA operand
+//   INT8 x INT8 -> INT32 per K-group (v_mfma_i32_16x16x64_i8)
+//   per group: acc_f32 = fma(float(P_group), s_w[group, n], acc_f32)
+//   end: y = acc_f32 * s_x[m] -> bfloat16 (round to nearest even) or float32.
+// Dequantized weights never leave registers.
+//
+// MFMA 16x16x64 i8 operand convention used throughout: lane l supplies 16 bytes of
+// A row (l % 16) and of B column (l % 16), both for k in [16*(l/16), 16*(l/16)+16) of
+// the 64-deep step, in the same byte order, so every product pairs the same k on both
+// sides.  The INT32 result of lane l is C[4*(l/16) + i][l % 16], i = 0..3.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "w4a8_internal.h"
+
+namespace w4a8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------------------
+// small device helpers
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+// Block-wide max of |x| bit patterns (non-negative floats order like unsigned integers;
+// NaN patterns sort above +Inf).  nwaves <= 16.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red, int nwaves) {
+    v = wave_max_u32(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    uint32_t r = 0;
+    for (int w = 0; w < nwaves; ++w) r = max(r, red[w]);
+    return r;
+}
+
+// One element of the per-token rule q = clamp(rint(fl32(x / d)), -127, 127).
+// x * (1/d) is within 2.3e-5 of fl32(x / d) for |x / d| <= 127.00001, so whenever its
+// distance to the nearest integer is below 0.4999 both round to the same integer; the
+// rare near-tie (and tiny-scale rows) take the IEEE division.
+__device__ __forceinline__ int quant_one(float x, float d, float inv, bool fast) {
+    const float r = x * inv;
+    float q = rintf(r);
+    if (__builtin_expect(!fast || fabsf(r - q) > 0.4999f, 0)) q = rintf(x / d);
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return (int)q;
+}
+
+struct RowScale {
+    float s, d, inv;
+    bool finite, fast;
+};
+
+__device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
+    RowScale r;
+    r.finite = amax_bits < 0x7f800000u;
+    const float amax = __uint_as_float(amax_bits);
+    r.s = r.finite ? amax / 127.0f : __uint_as_float(0x7fc00000u);
+    r.d = (r.finite && r.s > 0.0f) ? r.s : 1.0f;
+    r.inv = 1.0f / r.d;
+    r.fast = r.d >= 1e-30f;
+    return r;
+}
+
+// ------------------------------------------------------------------------------------
+// per-token INT8 activation quantization (P1 section 3.3, P5 section 8.3)
+// One 256-thread workgroup per row; each thread holds IT x 8 bf16 values in registers
+// so the row is read from HBM once.
+// ------------------------------------------------------------------------------------
+template <int IT>
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ X, int K, int ldx,
+                                                        int8_t* __restrict__ Xq, float* __restrict__ sx) {
+    __shared__ uint32_t red[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const uint16_t* xr = X + size_t(row) * size_t(ldx);
+    uint4 v[IT];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int k = (it * 256 + tid) * 8;
+        v[it] = make_uint4(0, 0, 0, 0);
+        if (k < K) v[it] = *reinterpret_cast<const uint4*>(xr + k);
+        const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            amax = max(amax, (w[j] & 0x7fffu) << 16);
+            amax = max(amax, w[j] & 0x7fff0000u);
+        }
+    }
+    amax = block_max_u32(amax, red, 4);
+    const RowScale rs = row_scale(amax);
+    int8_t* qr = Xq + size_t(row) * size_t(K);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int k = (it * 256 + tid) * 8;
+        if (k >= K) continue;
+        const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+        uint32_t out[2] = {0, 0};
+        if (rs.finite) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int q0 = quant_one(bf16_to_f32(w[j] & 0xffffu), rs.d, rs.inv, rs.fast);
+                const int q1 = quant_one(bf16_to_f32(w[j] >> 16), rs.d, rs.inv, rs.fast);
+                const uint32_t pair = (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8);
+                out[j >> 1] |= pair << ((j & 1) * 16);
+            }
+        }
+        *reinterpret_cast<uint2*>(qr + k) = make_uint2(out[0], out[1]);
+    }
+    if (tid == 0) sx[row] = rs.s;
+}
+
+// ------------------------------------------------------------------------------------
+// SiLU-gated activation + per-row requantization (P1 section 1 and section 3.1)
+// ------------------------------------------------------------------------------------
+template <int IT>
+__global__ __launch_bounds__(256) void silu_quant_kernel(const uint16_t* __restrict__ GU, int I,
+                                                         int8_t* __restrict__ Hq, float* __restrict__ sh) {
+    __shared__ uint32_t red[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const uint16_t* gp = GU + size_t(row) * size_t(2 * I);
+    const uint16_t* up = gp + I;
+    float h[IT][8];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int k = (it * 256 + tid) * 8;
+        uint4 gv = make_uint4(0, 0, 0, 0), uv = make_uint4(0, 0, 0, 0);
+        if (k < I) {
+            gv = *reinterpret_cast<const uint4*>(gp + k);
+            uv = *reinterpret_cast<const uint4*>(up + k);
+        }
+        const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w}, u4[4] = {uv.x, uv.y, uv.z, uv.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t gb = (j & 1) ? (g4[j >> 1] >> 16) : (g4[j >> 1] & 0xffffu);
+            const uint32_t ub = (j & 1) ? (u4[j >> 1] >> 16) : (u4[j >> 1] & 0xffffu);
+            const float g = bf16_to_f32(gb), u = bf16_to_f32(ub);
+            const float sg = g / (1.0f + expf(-g));
+            h[it][j] = sg * u;
+            amax = max(amax, __float_as_uint(h[it][j]) & 0x7fffffffu);
+        }
+    }
+    amax = block_max_u32(amax, red, 4);
+    const RowScale rs = row_scale(amax);
+    int8_t* qr = Hq + size_t(row) * size_t(I);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int k = (it * 256 + tid) * 8;
+        if (k >= I) continue;
+        uint32_t out[2] = {0, 0};
+        if (rs.finite) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int q = quant_one(h[it][j], rs.d, rs.inv, rs.fast);
+                out[j >> 2] |= (uint32_t(q) & 0xffu) << ((j & 3) * 8);
+            }
+        }
+        *reinterpret_cast<uint2*>(qr + k) = make_uint2(out[0], out[1]);
+    }
+    if (tid == 0) sh[row] = rs.s;
+}
+
+// ------------------------------------------------------------------------------------
+// W4A8 GEMM, decode variant (M-tiles of 16 or 32 rows; dense decode and per-expert tiles)
+//
+// Workgroup = NT column tiles (16 columns each) x KW K-slices, one wave per (tile, slice).
+// Each chunk of CS = KW*SBN superblocks (128 k each) is processed in one shot:
+//   1. the workgroup loads the chunk's activation rows [MT x 128*CS] into LDS (these loads
+//      are issued first, so waiting for them never waits on the weight stream);
+//   2. every wave issues the loads of all SBN of its weight superblocks (16 bytes per lane
+//      per superblock) and of their group scales / zero points, then consumes them in
+//      issue order while later ones are still in flight;
+//   3. activation fragments come from LDS (ds_read, counted separately from the weight
+//      loads).
+// So every weight byte of a chunk is requested from HBM at once, activations are read
+// from L2 once per workgroup, and the dequantized weights exist only in registers.
+// The KW slices' float32 accumulators are summed in slice order through LDS (the result
+// does not depend on scheduling), then the row scale is applied and the tile stored.
+// ------------------------------------------------------------------------------------
+enum { MODE_OUT = 0, MODE_PARTIALS = 1 };
+
+struct GemmArgs {
+    const int8_t* Xq;
+    const float* sx;
+    int M, K, N, G;
+    const uint8_t* blob;      // blob of expert 0 (or the only blob)
+    size_t codes_off, scales_off, zeros_off, expert_stride;
+    void* Y;
+    int ldy;
+    int out_f32;              // 1: float32 output, 0: bfloat16
+    int32_t* P;               // partials export [M, N, G]
+    const int32_t* gather;    // MoE: source token row = gather[r] / topk
+    int topk;
+    const int32_t* offsets;   // MoE: expert row offsets [E+1]
+    int E;
+};
+
+// Unpack two packed words (16 codes of one column) into one MFMA B operand.
+// Symmetric: two's-complement nibbles moved to the high half of each byte -> 16 * q
+// (exact; the 1/16 is folded into the group scale).  Asymmetric: unsigned nibbles in the
+// low half, then (q + 128 - z) ^ 0x80 per byte = q - z as int8 with no borrow between
+// bytes (q + 128 - z lies in [113, 143]).
+template <bool ASYM>
+__device__ __forceinline__ v4i unpack_b(uint32_t w0, uint32_t w1, uint32_t zc) {
+    v4i b;
+    if (!ASYM) {
+        b[0] = int((w0 << 4) & 0xF0F0F0F0u);
+        b[1] = int(w0 & 0xF0F0F0F0u);
+        b[2] = int((w1 << 4) & 0xF0F0F0F0u);
+        b[3] = int(w1 & 0xF0F0F0F0u);
+    } else {
+        b[0] = int(((w0 & 0x0F0F0F0Fu) + zc) ^ 0x80808080u);
+        b[1] = int((((w0 >> 4) & 0x0F0F0F0Fu) + zc) ^ 0x80808080u);
+        b[2] = int(((w1 & 0x0F0F0F0Fu) + zc) ^ 0x80808080u);
+        b[3] = int((((w1 >> 4) & 0x0F0F0F0Fu) + zc) ^ 0x80808080u);
+    }
+    return b;
+}
+
+struct TileRows {
+    int rbeg, rend, expert;
+};
+
+// MoE: the slot-th MT-row tile over experts in expert order (each expert's rows split into
+// ceil(rows_e / MT) tiles).  Every wave evaluates this identically, so the workgroup agrees
+// without a barrier.  expert = -1 when the slot is past the last tile.
+template <int MT>
+__device__ __forceinline__ TileRows moe_tile(const GemmArgs& a, int slot, int lane) {
+    TileRows tr{0, 0, -1};
+    int base = 0;
+    for (int c = 0; c < a.E; c += 64) {
+        const int e = c + lane;
+        const int cnt = e < a.E ? a.offsets[e + 1] - a.offsets[e] : 0;
+        const int t = (cnt + MT - 1) / MT;
+        int incl = t;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        const int excl = incl - t;
+        const unsigned long long hit = __ballot(slot >= base + excl && slot < base + incl);
+        if (hit) {
+            const int src = __ffsll((long long)hit) - 1;
+            const int ef = __shfl(e, src, 64);
+            const int tl = slot - base - __shfl(excl, src, 64);
+            const int e0 = a.offsets[ef], e1 = a.offsets[ef + 1];
+            tr.rbeg = e0 + tl * MT;
+            tr.rend = min(e1, tr.rbeg + MT);
+            tr.expert = ef;
+            return tr;
+        }
+        base += __shfl(incl, 63, 64);
+    }
+    return tr;
+}
+
+template <int MS, int NT, int KW, int SBN>
+struct DecodeShape {
+    static constexpr int MT = 16 * MS;
+    static constexpr int NTHR = 64 * NT * KW;
+    static constexpr int CS = KW * SBN;                        // superblocks per chunk
+    static constexpr int ROWB = CS * SB_K + 16;                // padded LDS row stride
+    static constexpr int APT = (MT * CS * 8 + NTHR - 1) / NTHR;  // 16-byte A pieces / thread
+    static constexpr size_t LDS_A = size_t(MT) * ROWB;
+    static constexpr size_t LDS_RED = size_t(KW > 1 ? KW - 1 : 1) * NT * MS * 4 * 64 * 4;
+    static constexpr size_t LDS = LDS_A > LDS_RED ? LDS_A : LDS_RED;
+};
+
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE>
+__global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
+    using S = DecodeShape<MS, NT, KW, SBN>;
+    constexpr int MT = S::MT, NTHR = S::NTHR, CS = S::CS, ROWB = S::ROWB, APT = S::APT;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = wave % NT, q = wave / NT;
+    const int ntiles = (a.N + 15) / 16;
+    const int tile = blockIdx.x * NT + t;
+    const bool tvalid = tile < ntiles;
+    const int tile_c = tvalid ? tile : ntiles - 1;
+    const int nsb = a.K / SB_K;
+
+    int rbeg, rend;
+    const uint8_t* blob = a.blob;
+    if (!MOE) {
+        rbeg = blockIdx.y * MT;
+        rend = min(a.M, rbeg + MT);
+    } else {
+        const TileRows tr = moe_tile<MT>(a, blockIdx.y, lane);
+        if (tr.expert < 0) return;                       // uniform over the workgroup
+        rbeg = tr.rbeg;
+        rend = tr.rend;
+        blob = a.blob + size_t(tr.expert) * a.expert_stride;
+    }
+    const int nrows = rend - rbeg;
+    const uint8_t* codes = blob + a.codes_off;
+    const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
+    const uint8_t* zeros = blob + a.zeros_off;
+
+    // row scales of the rows this lane stores, fetched before anything else so the
+    // epilogue never waits on a load
+    float sxr[MS][4];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sxr[ms][i] = 0.0f;
+            const int row = rbeg + ms * 16 + 4 * (lane >> 4) + i;
+            if (MODE != MODE_PARTIALS && q == 0 && row < rend) {
+                const int srow = (MOE && a.gather) ? a.gather[row] / a.topk : row;
+                sxr[ms][i] = a.sx[srow];
+            }
+        }
+
+    float accf[MS][4];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accf[ms][i] = 0.0f;
+    const v4i zero4 = {0, 0, 0, 0};
+
+    for (int cb = 0; cb < nsb; cb += CS) {
+        const int clen = min(CS, nsb - cb);
+        const int rowpieces = clen * 8;                  // 16-byte pieces per row in this chunk
+        // 1. activation rows of the chunk (first in this wave's load queue)
+        uint4 ap[APT];
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int p = tid + i * NTHR;
+            const int row = p / rowpieces, c = p - row * rowpieces;
+            ap[i] = make_uint4(0, 0, 0, 0);
+            if (row < nrows) {
+                int src = rbeg + row;
+                if (MOE && a.gather) src = a.gather[src] / a.topk;
+                ap[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(src) * a.K + size_t(cb) * SB_K + c * 16);
+            }
+        }
+        // 2. this wave's weight superblocks, scales and zero points
+        const int s0 = cb + q * SBN;
+        const int s_end = min(cb + clen, s0 + SBN);
+        uint4 bq[SBN];
+        float sc[SBN][GPS];
+        uint32_t zq[SBN][GPS];
+#pragma unroll
+        for (int s = 0; s < SBN; ++s) {
+            const int sb = min(s0 + s, nsb - 1);
+            bq[s] = *reinterpret_cast<const uint4*>(codes + (size_t(tile_c) * nsb + sb) * 1024 + lane * 16);
+#pragma unroll
+            for (int gi = 0; gi < GPS; ++gi) {
+                const size_t mi = (size_t(tile_c) * a.G + size_t(sb) * GPS + gi) * 16 + (lane & 15);
+                sc[s][gi] = scales[mi];
+                if (ASYM) zq[s][gi] = zeros[mi];
+            }
+        }
+        // 3. activations to LDS (zero rows past the tile's end)
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int p = tid + i * NTHR;
+            const int row = p / rowpieces, c = p - row * rowpieces;
+            if (row < MT) *reinterpret_cast<uint4*>(smem + row * ROWB + c * 16) = ap[i];
+        }
+        __syncthreads();
+        // 4. MFMA over this wave's superblocks
+#pragma unroll
+        for (int s = 0; s < SBN; ++s) {
+            const int sb = s0 + s;
+            if (sb >= s_end) break;
+            v4i acc[MS];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int gi = (GPS == 2) ? h : 0;
+                const uint32_t w0 = h ? bq[s].z : bq[s].x;
+                const uint32_t w1 = h ? bq[s].w : bq[s].y;
+                const uint32_t zc = ASYM ? (128u - zq[s][gi]) * 0x01010101u : 0u;
+                const v4i b = unpack_b<ASYM>(w0, w1, zc);
+                const bool first = (GPS == 2) || h == 0;
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) {
+                    const uint4 av = *reinterpret_cast<const uint4*>(
+                        smem + (ms * 16 + (lane & 15)) * ROWB + (sb - cb) * SB_K + h * 64 + 16 * (lane >> 4));
+                    const v4i A = {int(av.x), int(av.y), int(av.z), int(av.w)};
+                    acc[ms] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, b, first ? zero4 : acc[ms], 0, 0, 0);
+                }
+                if (GPS == 2 || h == 1) {
+                    if (MODE == MODE_PARTIALS) {
+                        const int col = tile * 16 + (lane & 15);
+#pragma unroll
+                        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int row = rbeg + ms * 16 + 4 * (lane >> 4) + i;
+                                if (tvalid && row < rend && col < a.N) {
+                                    const int v = ASYM ? acc[ms][i] : (acc[ms][i] >> 4);
+                                    a.P[(size_t(row) * a.N + col) * a.G + size_t(sb) * GPS + gi] = v;
+                                }
+                            }
+                    } else {
+                        const float scl = ASYM ? sc[s][gi] : sc[s][gi] * 0.0625f;
+#pragma unroll
+                        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) accf[ms][i] = fmaf((float)acc[ms][i], scl, accf[ms][i]);
+                    }
+                }
+            }
+        }
+        __syncthreads();                                 // LDS is rewritten by the next chunk
+    }
+    if (MODE == MODE_PARTIALS) return;
+
+    // slice-ordered reduction through LDS, row scale, store
+    float* red = reinterpret_cast<float*>(smem);
+    constexpr int NV = MS * 4;
+    if (KW > 1) {
+        if (q > 0) {
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    red[(((q - 1) * NT + t) * NV + ms * 4 + i) * 64 + lane] = accf[ms][i];
+        }
+        __syncthreads();
+        if (q != 0) return;
+#pragma unroll
+        for (int w = 1; w < KW; ++w)
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accf[ms][i] += red[(((w - 1) * NT + t) * NV + ms * 4 + i) * 64 + lane];
+    }
+    const int col = tile * 16 + (lane & 15);
+    if (!tvalid || col >= a.N) return;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = rbeg + ms * 16 + 4 * (lane >> 4) + i;
+            if (row >= rend) continue;
+            const float y = accf[ms][i] * sxr[ms][i];
+            if (a.out_f32)
+                reinterpret_cast<float*>(a.Y)[size_t(row) * a.ldy + col] = y;
+            else
+                reinterpret_cast<uint16_t*>(a.Y)[size_t(row) * a.ldy + col] = (uint16_t)f32_to_bf16_rne(y);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// MoE align: stable counting sort of routed rows by expert (P1 section 4.4 dispatch).
+// One 1024-thread workgroup.  Rows are cut into B blocks of L consecutive rows; block b's
+// per-expert counts live at cnt[e * (B + 1) + b] (padded stride: conflict-free in both
+// passes).  Positions: off[e] + counts of earlier blocks + order inside the block.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restrict__ ids, int R, int E, int L,
+                                                         int B, int32_t* __restrict__ sorted_rows,
+                                                         int32_t* __restrict__ offsets, int32_t* __restrict__ inv) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    int* cnt = reinterpret_cast<int*>(smem);   // E * (B + 1)
+    int* wsum = cnt + E * (B + 1);             // 16 wave totals
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int stride = B + 1;
+    for (int i = tid; i < E * stride; i += 1024) cnt[i] = 0;
+    __syncthreads();
+    if (tid < B) {
+        const int r1 = min(R, (tid + 1) * L);
+        for (int r = tid * L; r < r1; ++r) {
+            const int e = ids[r];
+            if (e >= 0 && e < E) cnt[e * stride + tid]++;
+        }
+    }
+    __syncthreads();
+    // per-expert totals (E <= 1024: one thread per expert), then a block exclusive scan
+    int tot = 0;
+    if (tid < E)
+        for (int b = 0; b < B; ++b) tot += cnt[tid * stride + b];
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += wsum[w];
+    const int off = wbase + incl - tot;
+    if (tid < E) {
+        offsets[tid] = off;
+        if (tid == E - 1) offsets[E] = off + tot;
+        int run = off;
+        for (int b = 0; b < B; ++b) {
+            const int c = cnt[tid * stride + b];
+            cnt[tid * stride + b] = run;
+            run += c;
+        }
+    }
+    if (E == 0 && tid == 0) offsets[0] = 0;
+    __syncthreads();
+    if (tid < B) {
+        const int r1 = min(R, (tid + 1) * L);
+        for (int r = tid * L; r < r1; ++r) {
+            const int e = ids[r];
+            if (e >= 0 && e < E) {
+                const int pos = cnt[e * stride + tid]++;
+                sorted_rows[pos] = r;
+                inv[r] = pos;
+            } else {
+                inv[r] = -1;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// un-permute + top-k weighted combine (P1 section 4.3): float32, j ascending.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __restrict__ Yd,
+                                                          const int32_t* __restrict__ inv,
+                                                          const float* __restrict__ w, int k, int H,
+                                                          uint16_t* __restrict__ out) {
+    const int t = blockIdx.x;
+    for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int r = inv[t * k + j];
+            if (r < 0) continue;
+            const float wj = w[t * k + j];
+            const uint4 v = *reinterpret_cast<const uint4*>(Yd + size_t(r) * H + c);
+            const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] = fmaf(wj, bf16_to_f32(x[i] & 0xffffu), acc[2 * i]);
+                acc[2 * i + 1] = fmaf(wj, bf16_to_f32(x[i] >> 16), acc[2 * i + 1]);
+            }
+        }
+        uint4 o;
+        o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+        o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+        o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+        o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+        *reinterpret_cast<uint4*>(out + size_t(t) * H + c) = o;
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// host-side launch helpers
+// ------------------------------------------------------------------------------------
+static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? W4A8_OK : W4A8_EHIP;
+}
+
+static int row_iters(int K) {
+    int it = (K + 2047) / 2048;
+    int p = 1;
+    while (p < it) p <<= 1;
+    return p;
+}
+
+template <int IT>
+static void launch_quant(const uint16_t* X, int M, int K, int ldx, int8_t* Xq, float* sx, hipStream_t s) {
+    quant_act_kernel<IT><<<dim3(M), dim3(256), 0, s>>>(X, K, ldx, Xq, sx);
+}
+
+template <int IT>
+static void launch_silu(const uint16_t* GU, int R, int I, int8_t* Hq, float* sh, hipStream_t s) {
+    silu_quant_kernel<IT><<<dim3(R), dim3(256), 0, s>>>(GU, I, Hq, sh);
+}
+
+// Variant table of the decode GEMM.  (NT, KW, SBN): column tiles per workgroup, K slices,
+// superblocks per slice; chosen so that one chunk covers K whenever it fits.
+struct DecodeCfg {
+    int ms, nt, kw, sbn;
+};
+
+static DecodeCfg decode_cfg(int K, int mt) {
+    const int nsb = K / SB_K;
+    DecodeCfg c{mt / 16, 4, 4, 8};
+    if (nsb > 32 && mt == 16) {     // long K: 8 slices of up to 8 superblocks, 2 tiles
+        c.nt = 2;
+        c.kw = 8;
+        c.sbn = 8;
+    } else {                        // one chunk of up to 32 superblocks (more chunks if longer)
+        const int per = (nsb + 3) / 4;
+        c.sbn = per <= 2 ? 2 : (per <= 4 ? 4 : 8);
+    }
+    return c;
+}
+
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE>
+static void launch_decode_t(const GemmArgs& a, dim3 grid, hipStream_t s) {
+    using S = DecodeShape<MS, NT, KW, SBN>;
+    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE>;
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(S::LDS));
+    (void)attr;
+    kern<<<grid, dim3(S::NTHR), S::LDS, s>>>(a);
+}
+
+template <int MS, int GPS, bool ASYM, int MODE, bool MOE>
+static void launch_decode_shape(const GemmArgs& a, const DecodeCfg& c, dim3 grid, hipStream_t s) {
+    if (c.kw == 8) {
+        if constexpr (MS == 1) launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE>(a, grid, s);
+    } else if (c.sbn == 2) launch_decode_t<MS, 4, 4, 2, GPS, ASYM, MODE, MOE>(a, grid, s);
+    else if (c.sbn == 4) launch_decode_t<MS, 4, 4, 4, GPS, ASYM, MODE, MOE>(a, grid, s);
+    else launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE>(a, grid, s);
+}
+
+template <int MODE, bool MOE>
+static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool asym, dim3 grid, hipStream_t s) {
+#define W4A8_DEC(MS_, GPS_, ASYM_) launch_decode_shape<MS_, GPS_, ASYM_, MODE, MOE>(a, c, grid, s)
+    if (c.ms == 1) {
+        if (gps == 1) { if (asym) W4A8_DEC(1, 1, true); else W4A8_DEC(1, 1, false); }
+        else { if (asym) W4A8_DEC(1, 2, true); else W4A8_DEC(1, 2, false); }
+    } else {
+        if (gps == 1) { if (asym) W4A8_DEC(2, 1, true); else W4A8_DEC(2, 1, false); }
+        else { if (asym) W4A8_DEC(2, 2, true); else W4A8_DEC(2, 2, false); }
+    }
+#undef W4A8_DEC
+}
+
+static dim3 decode_grid(const Layout& L, const DecodeCfg& c, int ytiles) {
+    const int ntiles = L.Np / 16;
+    return dim3((ntiles + c.nt - 1) / c.nt, ytiles);
+}
+
+static bool kernel_format_ok(const w4a8_wdesc* d) {
+    return d->group_size == 64 || d->group_size == 128;
+}
+
+static int dense_mt(int M) { return M <= 16 ? 16 : 32; }
+
+static GemmArgs make_args(const Layout& L, const int8_t* Xq, const float* sx, int M, const void* blob) {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.Xq = Xq;
+    a.sx = sx;
+    a.M = M;
+    a.K = L.K;
+    a.N = L.N;
+    a.G = L.G;
+    a.blob = static_cast<const uint8_t*>(blob);
+    a.codes_off = L.codes_off;
+    a.scales_off = L.scales_off;
+    a.zeros_off = L.zeros_off;
+    return a;
+}
+
+static int check_gemm_desc(const w4a8_wdesc* d) {
+    int st = desc_status(d);
+    if (st) return st;
+    if (!kernel_format_ok(d)) return W4A8_EUNSUPPORTED;
+    return W4A8_OK;
+}
+
+}  // namespace w4a8
+
+using namespace w4a8;
+
+extern "C" {
+
+int w4a8_quant_act(const void* X, int M, int K, int ldx, int8_t* Xq, float* sx, void* stream) {
+    if (M < 0 || K <= 0 || ldx < K) return W4A8_EINVAL;
+    if (M == 0) return W4A8_OK;
+    if (!X || !Xq || !sx) return W4A8_EINVAL;
+    if (K % 16 || ldx % 8 || !aligned16(X) || !aligned16(Xq)) return W4A8_EINVAL;
+    if (K > 65536) return W4A8_EUNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* x = static_cast<const uint16_t*>(X);
+    switch (row_iters(K)) {
+        case 1: launch_quant<1>(x, M, K, ldx, Xq, sx, s); break;
+        case 2: launch_quant<2>(x, M, K, ldx, Xq, sx, s); break;
+        case 4: launch_quant<4>(x, M, K, ldx, Xq, sx, s); break;
+        case 8: launch_quant<8>(x, M, K, ldx, Xq, sx, s); break;
+        case 16: launch_quant<16>(x, M, K, ldx, Xq, sx, s); break;
+        case 32: launch_quant<32>(x, M, K, ldx, Xq, sx, s); break;
+        default: return W4A8_EUNSUPPORTED;
+    }
+    return launch_status();
+}
+
+int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const w4a8_wdesc* d, void* Y,
+              int ldy, int out_dtype, void* stream) {
+    int st = check_gemm_desc(d);
+    if (st) return st;
+    if (M < 0 || (out_dtype != W4A8_OUT_BF16 && out_dtype != W4A8_OUT_F32)) return W4A8_EINVAL;
+    if (M == 0) return W4A8_OK;
+    if (!Xq || !sx || !blob || !Y || ldy < d->N) return W4A8_EINVAL;
+    if (!aligned16(Xq) || !aligned16(blob)) return W4A8_EINVAL;
+    const Layout L = layout_of(d);
+    GemmArgs a = make_args(L, Xq, sx, M, blob);
+    a.Y = Y;
+    a.ldy = ldy;
+    a.out_f32 = out_dtype == W4A8_OUT_F32;
+    const int mt = dense_mt(M);
+    const DecodeCfg c = decode_cfg(L.K, mt);
+    const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
+    launch_decode<MODE_OUT, false>(a, c, SB_K / d->group_size, d->asymmetric, grid, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob, const w4a8_wdesc* d, int32_t* P, void* stream) {
+    int st = check_gemm_desc(d);
+    if (st) return st;
+    if (M < 0) return W4A8_EINVAL;
+    if (M == 0) return W4A8_OK;
+    if (!Xq || !blob || !P) return W4A8_EINVAL;
+    if (!aligned16(Xq) || !aligned16(blob)) return W4A8_EINVAL;
+    const Layout L = layout_of(d);
+    GemmArgs a = make_args(L, Xq, nullptr, M, blob);
+    a.P = P;
+    const int mt = dense_mt(M);
+    const DecodeCfg c = decode_cfg(L.K, mt);
+    const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
+    launch_decode<MODE_PARTIALS, false>(a, c, SB_K / d->group_size, d->asymmetric, grid,
+                                        static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int w4a8_moe_align(const int32_t* ids, int T, int k, int E, int32_t* sorted_rows, int32_t* offsets, int32_t* inv,
+                   void* stream) {
+    if (T < 0 || k <= 0 || E <= 0 || E > 1024) return W4A8_EINVAL;
+    if (!offsets) return W4A8_EINVAL;
+    const long long R = (long long)T * k;
+    if (R > (1 << 24)) return W4A8_EUNSUPPORTED;
+    if (R > 0 && (!ids || !sorted_rows || !inv)) return W4A8_EINVAL;
+    const int LDS_INTS = 12288;
+    int Bmax = std::min(1024, LDS_INTS / E - 1);
+    if (Bmax < 1) Bmax = 1;
+    int L = R > 0 ? int((R + Bmax - 1) / Bmax) : 1;
+    int B = R > 0 ? int((R + L - 1) / L) : 0;
+    size_t lds = (size_t(E) * (B + 1) + 16) * sizeof(int);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    moe_align_kernel<<<dim3(1), dim3(1024), lds, s>>>(ids, int(R), E, L, B, sorted_rows, offsets, inv);
+    return launch_status();
+}
+
+static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gather, int k, const int32_t* offsets,
+                         int E, int rows, const void* blobs, size_t stride, const w4a8_wdesc* d, void* Y,
+                         int out_dtype, int mt, hipStream_t s) {
+    const Layout L = layout_of(d);
+    GemmArgs a = make_args(L, Xq, sx, rows, blobs);
+    a.Y = Y;
+    a.ldy = L.N;
+    a.out_f32 = out_dtype == W4A8_OUT_F32;
+    a.gather = gather;
+    a.topk = k;
+    a.offsets = offsets;
+    a.E = E;
+    a.expert_stride = stride;
+    const int slots = rows / mt + std::min(E, rows) + 1;
+    const DecodeCfg c = decode_cfg(L.K, mt);
+    launch_decode<MODE_OUT, true>(a, c, SB_K / d->group_size, d->asymmetric, decode_grid(L, c, slots), s);
+    return launch_status();
+}
+
+int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int k, const int32_t* offsets, int E,
+                  int rows, const void* blobs, size_t stride, const w4a8_wdesc* d, void* Y, int out_dtype,
+                  void* stream) {
+    int st = check_gemm_desc(d);
+    if (st) return st;
+    if (rows < 0 || E <= 0 || (out_dtype != W4A8_OUT_BF16 && out_dtype != W4A8_OUT_F32)) return W4A8_EINVAL;
+    if (rows == 0) return W4A8_OK;
+    if (!Xq || !sx || !offsets || !blobs || !Y) return W4A8_EINVAL;
+    if (gather && k <= 0) return W4A8_EINVAL;
+    const Layout L = layout_of(d);
+    if (E > 1 && stride < L.total) return W4A8_EINVAL;
+    if (!aligned16(Xq) || !aligned16(blobs) || (stride & 15)) return W4A8_EINVAL;
+    const int mt = rows / E >= 16 ? 32 : 16;
+    return moe_gemm_impl(Xq, sx, gather, k, offsets, E, rows, blobs, stride, d, Y, out_dtype, mt,
+                         static_cast<hipStream_t>(stream));
+}
+
+int w4a8_silu_mul_quant(const void* GU, int R, int I, int8_t* Hq, float* sh, void* stream) {
+    if (R < 0 || I <= 0) return W4A8_EINVAL;
+    if (R == 0) return W4A8_OK;
+    if (!GU || !Hq || !sh) return W4A8_EINVAL;
+    if (I % 16 || !aligned16(GU) || !aligned16(Hq)) return W4A8_EINVAL;
+    if (I > 65536) return W4A8_EUNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* g = static_cast<const uint16_t*>(GU);
+    switch (row_iters(I)) {
+        case 1: launch_silu<1>(g, R, I, Hq, sh, s); break;
+        case 2: launch_silu<2>(g, R, I, Hq, sh, s); break;
+        case 4: launch_silu<4>(g, R, I, Hq, sh, s); break;
+        case 8: launch_silu<8>(g, R, I, Hq, sh, s); break;
+        default: return W4A8_EUNSUPPORTED;
+    }
+    return launch_status();
+}
+
+int w4a8_moe_combine(const void* Yd, const int32_t* inv, const float* w, int T, int k, int H, void* out,
+                     void* stream) {
+    if (T < 0 || k <= 0 || H <= 0) return W4A8_EINVAL;
+    if (T == 0) return W4A8_OK;
+    if (!Yd || !inv || !w || !out) return W4A8_EINVAL;
+    if (H % 8 || !aligned16(Yd) || !aligned16(out)) return W4A8_EINVAL;
+    moe_combine_kernel<<<dim3(T), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const uint16_t*>(Yd), inv, w, k, H, static_cast<uint16_t*>(out));
+    return launch_status();
+}
+
+// Workspace carve-up of w4a8_moe_forward (each piece 256-byte aligned).
+struct MoeWs {
+    size_t xq, sx, rows, offs, inv, gu, hq, sh, yd, total;
+};
+
+static MoeWs moe_ws(int T, int k, int H, int I, int E) {
+    auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const size_t R = size_t(T) * size_t(k);
+    MoeWs w;
+    size_t o = 0;
+    w.xq = o; o = al(o + size_t(T) * H);
+    w.sx = o; o = al(o + size_t(T) * 4);
+    w.rows = o; o = al(o + R * 4);
+    w.offs = o; o = al(o + size_t(E + 1) * 4);
+    w.inv = o; o = al(o + R * 4);
+    w.gu = o; o = al(o + R * size_t(2 * I) * 2);
+    w.hq = o; o = al(o + R * size_t(I));
+    w.sh = o; o = al(o + R * 4);
+    w.yd = o; o = al(o + R * size_t(H) * 2);
+    w.total = o;
+    return w;
+}
+
+size_t w4a8_moe_workspace_size(int T, int k, int H, int I, int E) {
+    if (T < 0 || k <= 0 || H <= 0 || I <= 0 || E <= 0) return 0;
+    return moe_ws(T, k, H, I, E).total;
+}
+
+int w4a8_moe_forward(const void* X, const int32_t* ids, const float* w, int T, int k, int E, const void* gu_blobs,
+                     size_t gu_stride, const w4a8_wdesc* gu_desc, const void* d_blobs, size_t d_stride,
+                     const w4a8_wdesc* d_desc, void* ws, size_t ws_bytes, void* out, void* stream) {
+    int st = check_gemm_desc(gu_desc);
+    if (st) return st;
+    st = check_gemm_desc(d_desc);
+    if (st) return st;
+    if (T < 0 || k <= 0 || E <= 0) return W4A8_EINVAL;
+    const int H = gu_desc->K, I2 = gu_desc->N;
+    if (I2 % 2 || d_desc->K != I2 / 2 || d_desc->N != H) return W4A8_EINVAL;
+    const int I = I2 / 2;
+    if (T == 0) return W4A8_OK;
+    if (!X || !ids || !w || !gu_blobs || !d_blobs || !ws || !out) return W4A8_EINVAL;
+    const MoeWs L = moe_ws(T, k, H, I, E);
+    if (ws_bytes < L.total) return W4A8_ESIZE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return W4A8_EINVAL;
+    uint8_t* b = static_cast<uint8_t*>(ws);
+    int8_t* xq = reinterpret_cast<int8_t*>(b + L.xq);
+    float* sx = reinterpret_cast<float*>(b + L.sx);
+    int32_t* rows = reinterpret_cast<int32_t*>(b + L.rows);
+    int32_t* offs = reinterpret_cast<int32_t*>(b + L.offs);
+    int32_t* inv = reinterpret_cast<int32_t*>(b + L.inv);
+    void* gu = b + L.gu;
+    int8_t* hq = reinterpret_cast<int8_t*>(b + L.hq);
+    float* sh = reinterpret_cast<float*>(b + L.sh);
+    void* yd = b + L.yd;
+    const int R = T * k;
+    if ((st = w4a8_quant_act(X, T, H, H, xq, sx, stream))) return st;
+    if ((st = w4a8_moe_align(ids, T, k, E, rows, offs, inv, stream))) return st;
+    if ((st = w4a8_moe_gemm(xq, sx, rows, k, offs, E, R, gu_blobs, gu_stride, gu_desc, gu, W4A8_OUT_BF16, stream)))
+        return st;
+    if ((st = w4a8_silu_mul_quant(gu, R, I, hq, sh, stream))) return st;
+    if ((st = w4a8_moe_gemm(hq, sh, nullptr, k, offs, E, R, d_blobs, d_stride, d_desc, yd, W4A8_OUT_BF16, stream)))
+        return st;
+    return w4a8_moe_combine(yd, inv, w, T, k, H, out, stream);
+}
+
+const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
+    if (check_gemm_desc(d) != W4A8_OK || M < 0) return "unsupported";
+    const bool asym = d->asymmetric;
+    const bool g64 = d->group_size == 64;
+    if (dense_mt(M) == 16)
+        return asym ? (g64 ? "w4a8_decode_m16_asym_g64" : "w4a8_decode_m16_asym_g128")
+                    : (g64 ? "w4a8_decode_m16_sym_g64" : "w4a8_decode_m16_sym_g128");
+    return asym ? (g64 ? "w4a8_decode_m32_asym_g64" : "w4a8_decode_m32_asym_g128")
+                : (g64 ? "w4a8_decode_m32_sym_g64" : "w4a8_decode_m32_sym_g128");
+}
+
+}  // extern "C"

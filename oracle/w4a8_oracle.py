@@ -305,7 +305,7 @@ def moe_layer(x, topk_ids, topk_w, expert, E: int, I: int, group_size: int):
     for j in range(k):
         out64 += w[:, j:j + 1] * yd[inv[:, j]].astype(np.float64)
     return dict(out=bf16_rne(out64), out64=out64, xq=xq, sx=sx, sorted_rows=sorted_rows,
-                offsets=offsets, inv=inv, gu=gu, hq=hq, sh=sh, yd=yd)
+                offsets=offsets, inv=inv, gu=gu, hq=hq, sh=sh, yd=yd, topk_w=w)
 
 
 # --------------------------------------------------------------------------------------

@@ -1,0 +1,407 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Integer work (activation codes, per-group INT32 partials, routing permutation) must match
+bit for bit; floating outputs pass the gates of gpu_cases.check_float_output."""
+import numpy as np
+import pytest
+import torch
+
+import moe_token_int8_amd as L
+import oracle as O
+import workloads as W
+from gpu_cases import DEV, bf16_ulp, check_float_output, device_blob, gpu_quant
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.lib()
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------- activation quantization
+@pytest.mark.parametrize("M,K,dist,outl,oscale,seed", [
+    (16, 1024, "normal", 4, 20.0, 101),        # single Linear input
+    (1, 4096, "normal", 4, 50.0, 102),         # decode shapes
+    (8, 4096, "normal", 4, 50.0, 102),
+    (32, 4096, "normal", 4, 50.0, 102),
+    (37, 2064, "normal", 0, 1.0, 7),           # ragged rows, K not a power of two
+    (64, 7168, "student_t3", 0, 1.0, 105),     # heavy-tailed MoE decode input
+    (512, 4096, "normal", 0, 1.0, 104),
+    (3, 16, "normal", 0, 1.0, 9),              # smallest K
+])
+def test_quant_act_bit_exact(M, K, dist, outl, oscale, seed):
+    _print(f"quant_act M={M} K={K} {dist}")
+    Xb = W.random_activations(seed, M, K, dist, outl, oscale)
+    Xq, sx = gpu_quant(Xb)
+    q, s = O.quant_act(W.bf16_values(Xb))
+    assert np.array_equal(Xq.cpu().numpy(), q)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), s.view(np.uint32))
+
+
+def test_quant_act_full_prefill_rows():
+    """Both prefill inputs at full size ([4096, 4096] and [4096, 14336])."""
+    for cfg in (W.C3_UP, W.C3_DOWN):
+        _print(f"quant_act {cfg.name}")
+        Xb = W.random_activations(cfg.seed + 7919, cfg.M, cfg.K)
+        Xq, sx = gpu_quant(Xb)
+        q, s = O.quant_act(W.bf16_values(Xb))
+        assert np.array_equal(Xq.cpu().numpy(), q)
+        assert np.array_equal(sx.cpu().numpy().view(np.uint32), s.view(np.uint32))
+
+
+def test_quant_act_edge_rows_and_strides():
+    x = W.bf16_values(W.random_activations(3, 6, 64))
+    x[1] = 0.0
+    x[2, 5] = np.nan
+    x[3, 7] = np.inf
+    x[4] = 1e-40                            # subnormal row: scale underflows towards 0
+    x[5, :] = 0.0
+    x[5, 0] = -3.0
+    big = torch.zeros((6, 96), dtype=torch.bfloat16)
+    big[:, :64] = torch.from_numpy(x).to(torch.bfloat16)
+    Xd = big.to(DEV)[:, :64]                # row stride 96 > K
+    Xq = torch.empty((6, 64), dtype=torch.int8, device=DEV)
+    sx = torch.empty(6, dtype=torch.float32, device=DEV)
+    L.w4a8_quant_act(Xd, Xq, sx)
+    q, s = O.quant_act(W.bf16_values(big[:, :64]))
+    assert np.array_equal(Xq.cpu().numpy(), q)
+    g = sx.cpu().numpy()
+    assert np.array_equal(np.isnan(g), np.isnan(s))
+    assert np.array_equal(g[~np.isnan(g)].view(np.uint32), s[~np.isnan(s)].view(np.uint32))
+
+
+def test_quant_act_near_ties_take_the_exact_division():
+    """Rows built so that many x/s land within a few ulps of .5: the fast reciprocal path
+    must hand these to the IEEE division."""
+    rs = np.random.default_rng(0)
+    amax = np.float32(1.0)
+    s = np.float32(amax / np.float32(127))
+    halves = (rs.integers(-126, 126, size=(8, 1024)) + 0.5).astype(np.float64)
+    x = (halves * np.float64(s)).astype(np.float32)
+    x[:, 0] = amax
+    xb = W.to_bf16(x)
+    Xq, sx = gpu_quant(xb)
+    q, so = O.quant_act(W.bf16_values(xb))
+    assert np.array_equal(Xq.cpu().numpy(), q)
+
+
+# ---------------------------------------------------------------- GEMM partials (exact)
+@pytest.mark.parametrize("M,K,N,g,asym", [
+    (16, 1024, 1024, 128, False),              # the single-Linear shape
+    (37, 512, 40, 64, True),                   # ragged M, ragged N (padded tile)
+    (5, 384, 48, 128, True),
+    (20, 256, 33, 64, False),
+    (1, 4096, 256, 128, False),
+    (64, 7168, 64, 64, True),                  # MoE decode expert shape (slice of N)
+])
+def test_partials_bit_exact(M, K, N, g, asym):
+    _print(f"partials M={M} K={K} N={N} g={g} asym={asym}")
+    Xb = W.random_activations(M * 7 + K, M, K, outlier_cols=2, outlier_scale=20.0)
+    Wt = W.random_weights(K + N, K, N)
+    Wt[:g, 0] = 0.0
+    d = L.desc(K, N, g, asym)
+    blob = device_blob(d, L.w4a8_pack(d, Wt))
+    Xq, sx = gpu_quant(Xb)
+    P = torch.full((M, N, K // g), -7, dtype=torch.int32, device=DEV)
+    L.w4a8_gemm_partials(Xq, blob, d, P)
+    q, s = O.quant_act(W.bf16_values(Xb))
+    codes, scales, zeros = O.quant_weight(Wt, g, asym)
+    assert np.array_equal(P.cpu().numpy(), O.gemm_partials(q, codes, zeros, g))
+
+
+def test_partials_decode_full_width():
+    cfg = W.with_decode_m(W.C2, 8)
+    Xb, Wt = W.dense_inputs(cfg)
+    d = L.desc(cfg.K, cfg.N, cfg.group_size, cfg.asymmetric)
+    blob = device_blob(d, L.w4a8_pack(d, Wt))
+    Xq, _ = gpu_quant(Xb)
+    P = torch.empty((8, cfg.N, cfg.K // cfg.group_size), dtype=torch.int32, device=DEV)
+    L.w4a8_gemm_partials(Xq, blob, d, P)
+    q, _ = O.quant_act(W.bf16_values(Xb))
+    codes, _, zeros = O.quant_weight(Wt, cfg.group_size, cfg.asymmetric)
+    assert np.array_equal(P.cpu().numpy(), O.gemm_partials(q, codes, zeros, cfg.group_size))
+
+
+# ---------------------------------------------------------------- GEMM outputs
+def _gemm_case(Xb, Wt, g, asym):
+    M, K = Xb.shape
+    N = Wt.shape[1]
+    d = L.desc(K, N, g, asym)
+    blob = device_blob(d, L.w4a8_pack(d, Wt))
+    Xq, sx = gpu_quant(Xb)
+    y32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    ybf = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_gemm(Xq, sx, blob, d, y32, L.W4A8_OUT_F32)
+    L.w4a8_gemm(Xq, sx, blob, d, ybf, L.W4A8_OUT_BF16)
+    q, s = O.quant_act(W.bf16_values(Xb))
+    codes, scales, zeros = O.quant_weight(Wt, g, asym)
+    Y64 = O.gemm(q, s, codes, scales, zeros, g)
+    return check_float_output(y32.cpu().numpy(), ybf.float().cpu().numpy(), Y64)
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_gemm_decode_shapes(M):
+    cfg = W.with_decode_m(W.C2, M)
+    _print(f"gemm {cfg.name}")
+    Xb, Wt = W.dense_inputs(cfg)
+    r = _gemm_case(Xb, Wt, cfg.group_size, cfg.asymmetric)
+    _print(r)
+
+
+def test_gemm_single_linear():
+    Xb, Wt = W.dense_inputs(W.C1)
+    _print(_gemm_case(Xb, Wt, 128, False))
+
+
+@pytest.mark.parametrize("M,K,N,g,asym", [(37, 512, 40, 64, True), (17, 1024, 96, 128, True),
+                                          (48, 256, 17, 64, False), (2, 128, 16, 128, True)])
+def test_gemm_ragged(M, K, N, g, asym):
+    Xb = W.random_activations(M + N, M, K, outlier_cols=1, outlier_scale=30.0)
+    Wt = W.random_weights(N + 3, K, N)
+    _print(_gemm_case(Xb, Wt, g, asym))
+
+
+def test_gemm_zero_and_nan_rows():
+    x = W.bf16_values(W.random_activations(4, 5, 256))
+    x[1] = 0.0
+    x[3, 9] = np.nan
+    Xb = W.to_bf16(x)
+    Wt = W.random_weights(5, 256, 32)
+    d = L.desc(256, 32, 128, True)
+    blob = device_blob(d, L.w4a8_pack(d, Wt))
+    Xq, sx = gpu_quant(Xb)
+    y = torch.empty((5, 32), dtype=torch.float32, device=DEV)
+    L.w4a8_gemm(Xq, sx, blob, d, y, L.W4A8_OUT_F32)
+    y = y.cpu().numpy()
+    assert np.all(y[1] == 0) and np.all(np.isnan(y[3]))
+    assert np.all(np.isfinite(y[[0, 2, 4]]))
+
+
+# ---------------------------------------------------------------- MoE pieces
+def _routing(seed, T, E, k, zipf=0.0):
+    cfg = W.MoEConfig("t", T, 128, 64, E, k, 64, False, seed, zipf_s=zipf)
+    return W.moe_routing(cfg)
+
+
+@pytest.mark.parametrize("T,E,k,zipf", [(512, 64, 6, 1.1), (64, 256, 8, 0.0), (5, 3, 2, 0.0), (1, 8, 1, 0.0),
+                                        (300, 1024, 4, 0.0)])
+def test_moe_align_exact(T, E, k, zipf):
+    ids, _ = _routing(T + E, T, E, k, zipf)
+    rows_ref, off_ref, inv_ref = O.moe_align(ids, E)
+    ids_d = torch.from_numpy(ids).to(DEV)
+    rows = torch.full((T * k,), -5, dtype=torch.int32, device=DEV)
+    off = torch.full((E + 1,), -5, dtype=torch.int32, device=DEV)
+    inv = torch.full((T, k), -5, dtype=torch.int32, device=DEV)
+    L.w4a8_moe_align(ids_d, E, rows, off, inv)
+    assert np.array_equal(off.cpu().numpy(), off_ref)
+    assert np.array_equal(rows.cpu().numpy(), rows_ref)
+    assert np.array_equal(inv.cpu().numpy(), inv_ref)
+
+
+def test_silu_mul_quant_vs_oracle():
+    """Codes may differ by 1 only where the float64 value of h/s lies within 1e-3 of a
+    rounding boundary (the GPU's expf and the oracle's float64 exp differ by a few ulps)."""
+    for R, I in [(3072, 1408), (512, 2048), (7, 32)]:
+        rs = np.random.default_rng(R)
+        gu = W.to_bf16((rs.standard_normal((R, 2 * I)) * 2).astype(np.float32))
+        g = gu.to(DEV)
+        Hq = torch.empty((R, I), dtype=torch.int8, device=DEV)
+        sh = torch.empty(R, dtype=torch.float32, device=DEV)
+        L.w4a8_silu_mul_quant(g, Hq, sh)
+        q, s = O.silu_mul_quant(W.bf16_values(gu))
+        sg = sh.cpu().numpy()
+        assert np.all(np.abs(sg.astype(np.float64) - s) <= 4 * np.spacing(s))
+        qg = Hq.cpu().numpy().astype(np.int64)
+        diff = np.abs(qg - q.astype(np.int64))
+        assert diff.max() <= 1
+        h = O.silu_mul(W.bf16_values(gu))
+        t = h / s.astype(np.float64)[:, None]
+        near = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-3
+        assert np.all(near[diff > 0])
+        _print(f"silu R={R} I={I}: {int((diff > 0).sum())} near-tie code differences of {diff.size}")
+
+
+def test_combine_vs_oracle():
+    T, k, H = 64, 8, 7168
+    ids, w = _routing(3, T, 256, k)
+    _, _, inv = O.moe_align(ids, 256)
+    rs = np.random.default_rng(1)
+    yd = W.to_bf16(rs.standard_normal((T * k, H)).astype(np.float32))
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_moe_combine(yd.to(DEV), torch.from_numpy(inv).to(DEV), torch.from_numpy(w).to(DEV), out)
+    ydv = W.bf16_values(yd).astype(np.float64)
+    ref64 = np.zeros((T, H))
+    for j in range(k):
+        ref64 += w[:, j:j + 1].astype(np.float64) * ydv[inv[:, j]]
+    got = out.float().cpu().numpy()
+    ref = O.bf16_rne(ref64)
+    diff = np.abs(got - ref)
+    assert np.all(diff <= bf16_ulp(ref) + 1e-6)
+    assert np.linalg.norm(got - ref64) / np.linalg.norm(ref64) < 3e-3
+
+
+def _moe_experts_rtn(cfg, experts_touched):
+    """Float weights quantized by the oracle (for the oracle) and packed by the library."""
+    dgu = L.desc(cfg.H, 2 * cfg.I, cfg.group_size, cfg.asymmetric)
+    dd = L.desc(cfg.I, cfg.H, cfg.group_size, cfg.asymmetric)
+    host_gu, host_d, qw = {}, {}, {}
+    for e in sorted(experts_touched):
+        Wgu, Wd = W.expert_weights(cfg, e)
+        host_gu[e] = L.w4a8_pack(dgu, Wgu)
+        host_d[e] = L.w4a8_pack(dd, Wd)
+        qw[e] = O.quant_weight(Wgu, cfg.group_size, cfg.asymmetric) + \
+            O.quant_weight(Wd, cfg.group_size, cfg.asymmetric)
+    return (dgu, dd, L.experts_to_device(dgu, cfg.E, host_gu), L.experts_to_device(dd, cfg.E, host_d), qw)
+
+
+def _moe_experts_codes(cfg, experts_touched, seed):
+    """Random well-formed codes per expert (sizes whose float weights are too slow to draw)."""
+    dgu = L.desc(cfg.H, 2 * cfg.I, cfg.group_size, cfg.asymmetric)
+    dd = L.desc(cfg.I, cfg.H, cfg.group_size, cfg.asymmetric)
+    host_gu, host_d, qw = {}, {}, {}
+    for e in sorted(experts_touched):
+        cg = W.random_codes(seed * 1009 + e, cfg.H, 2 * cfg.I, cfg.group_size, cfg.asymmetric)
+        cd = W.random_codes(seed * 2003 + e, cfg.I, cfg.H, cfg.group_size, cfg.asymmetric)
+        host_gu[e] = L.w4a8_pack_codes(dgu, *cg)
+        host_d[e] = L.w4a8_pack_codes(dd, *cd)
+        qw[e] = cg + cd
+    return (dgu, dd, L.experts_to_device(dgu, cfg.E, host_gu), L.experts_to_device(dd, cfg.E, host_d), qw)
+
+
+def _run_moe_forward(cfg, Xb, ids, w, gud, dd_):
+    T, k = ids.shape
+    ws = torch.empty(L.w4a8_moe_workspace_size(T, k, cfg.H, cfg.I, cfg.E), dtype=torch.uint8, device=DEV)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_moe_forward(Xb.to(DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), cfg.E,
+                       gud.blob, gud.stride, gud.desc, dd_.blob, dd_.stride, dd_.desc, ws, out)
+    return out, ws
+
+
+def _check_moe(out, ref, qw, group_size, flips_per_row=2):
+    """End-to-end gate against the oracle's own bf16 output.
+
+    The stages are pinned one by one above; end to end, two things may legitimately differ:
+    bf16 roundings of intermediate outputs (one step when a value sits on a rounding
+    boundary), and the requantization of silu(gate)*up, where a near-tie code can move by
+    +-1 (the GPU's expf and the oracle's float64 exp differ by ulps).  One such flip in
+    routed row r moves out[t, n] by at most w[t, j] * sh[r] * max_k |s_d (q - z)|[k, n].
+    Bound per element: 2 bf16 steps + flips_per_row of those for each routed row; normwise
+    1e-3 against the float64 output."""
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref_bf = ref["out"].astype(np.float64)
+    o64 = ref["out64"]
+    inv, sh = ref["inv"], ref["sh"].astype(np.float64)
+    T, k = inv.shape
+    srt, offs = ref["sorted_rows"], ref["offsets"]
+    flip = np.zeros_like(o64)
+    colmax = {}
+    for e, wts in qw.items():
+        cd, sd, zd = wts[3:]
+        deq = O.dequant_weight(cd, sd, zd, group_size)
+        colmax[e] = np.max(np.abs(deq), axis=0)
+    ids = np.empty(T * k, np.int64)
+    for e in range(len(offs) - 1):
+        ids[srt[offs[e]:offs[e + 1]]] = e
+    for t in range(T):
+        for j in range(k):
+            r = inv[t, j]
+            e = ids[t * k + j]
+            flip[t] += abs(ref["topk_w"][t, j]) * sh[r] * colmax[e]
+    rms = np.sqrt(np.mean(o64 ** 2))
+    nw = np.linalg.norm(got - ref_bf) / np.linalg.norm(o64)
+    err = np.abs(got - ref_bf)
+    allow = 2 * bf16_ulp(ref_bf) + flips_per_row * flip
+    stats = dict(normwise=float(nw), frac_bitexact=float(np.mean(got == ref_bf)),
+                 frac_within_1ulp=float(np.mean(err <= bf16_ulp(ref_bf))),
+                 max_err_over_rms=float(np.max(err) / rms), max_err_over_allow=float(np.max(err / allow)))
+    _print(stats)
+    assert nw < 1e-3, stats
+    assert np.all(err <= allow), stats
+    return stats
+
+
+@pytest.mark.parametrize("T,E,k,H,I,g,asym", [(9, 3, 2, 256, 128, 64, True), (40, 8, 2, 512, 256, 128, False),
+                                              (33, 16, 4, 256, 128, 128, True)])
+def test_moe_forward_small_rtn(T, E, k, H, I, g, asym):
+    cfg = W.MoEConfig("small", T, H, I, E, k, g, asym, 17 + T)
+    ids, w = W.moe_routing(cfg)
+    Xb = W.moe_activations(cfg)
+    dgu, dd, gud, ddv, qw = _moe_experts_rtn(cfg, set(ids.ravel().tolist()))
+    out, ws = _run_moe_forward(cfg, Xb, ids, w, gud, ddv)
+    ref = O.moe_layer(W.bf16_values(Xb), ids, w, lambda e: qw[e], E, I, g)
+    _check_moe(out, ref, qw, cfg.group_size)
+
+
+def test_moe_gemm_grouped_matches_per_expert_oracle():
+    """Gate/up grouped GEMM alone on the 64-expert top-6 routing (Zipf-skewed: one expert
+    gets most rows), float32 output, with random codes."""
+    cfg = W.C4
+    ids, w = W.moe_routing(cfg)
+    touched = set(ids.ravel().tolist())
+    dgu, dd, gud, ddv, qw = _moe_experts_codes(cfg, touched, 4)
+    Xb = W.moe_activations(cfg)
+    Xq, sx = gpu_quant(Xb)
+    T, k = ids.shape
+    rows = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    off = torch.empty(cfg.E + 1, dtype=torch.int32, device=DEV)
+    inv = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    L.w4a8_moe_align(torch.from_numpy(ids).to(DEV), cfg.E, rows, off, inv)
+    Y = torch.empty((T * k, 2 * cfg.I), dtype=torch.float32, device=DEV)
+    L.w4a8_moe_gemm(Xq, sx, rows, k, off, cfg.E, T * k, gud.blob, gud.stride, dgu, Y, L.W4A8_OUT_F32)
+    Ybf = torch.empty((T * k, 2 * cfg.I), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_moe_gemm(Xq, sx, rows, k, off, cfg.E, T * k, gud.blob, gud.stride, dgu, Ybf, L.W4A8_OUT_BF16)
+    q, s = O.quant_act(W.bf16_values(Xb))
+    srt, offs, _ = O.moe_align(ids, cfg.E)
+    Y = Y.cpu().numpy()
+    Ybf = Ybf.float().cpu().numpy()
+    Y64 = np.zeros(Y.shape)
+    for e in touched:
+        a, b = offs[e], offs[e + 1]
+        toks = srt[a:b] // k
+        c, sc, z = qw[e][:3]
+        Y64[a:b] = O.gemm(q[toks], s[toks], c, sc, z, cfg.group_size)
+    _print(check_float_output(Y, Ybf, Y64))
+
+
+def test_moe_forward_c4_full():
+    """The 64-expert top-6 layer at full size (T=512, H=4096, I=1408), random codes."""
+    cfg = W.C4
+    ids, w = W.moe_routing(cfg)
+    touched = set(ids.ravel().tolist())
+    dgu, dd, gud, ddv, qw = _moe_experts_codes(cfg, touched, 4)
+    Xb = W.moe_activations(cfg)
+    out, _ = _run_moe_forward(cfg, Xb, ids, w, gud, ddv)
+    ref = O.moe_layer(W.bf16_values(Xb), ids, w, lambda e: qw[e], cfg.E, cfg.I, cfg.group_size)
+    _check_moe(out, ref, qw, cfg.group_size)
+
+
+def test_moe_forward_c5_subset_tokens():
+    """The 256-expert top-8 asymmetric g64 layer (H=7168, I=2048) on 4 tokens (32 experts
+    touched), random codes; full T=64 is timed by the benchmark."""
+    cfg = W.C5
+    ids, w = W.moe_routing(cfg, T=4)
+    touched = set(ids.ravel().tolist())
+    dgu, dd, gud, ddv, qw = _moe_experts_codes(cfg, touched, 5)
+    Xb = W.moe_activations(cfg, T=4)
+    out, _ = _run_moe_forward(cfg, Xb, ids, w, gud, ddv)
+    ref = O.moe_layer(W.bf16_values(Xb), ids, w, lambda e: qw[e], cfg.E, cfg.I, cfg.group_size)
+    _check_moe(out, ref, qw, cfg.group_size)
+
+
+def test_moe_expert_with_no_rows_and_single_expert():
+    """E=1, k=1, weight 1: the MoE layer equals quant -> gemm -> silu-quant -> gemm."""
+    cfg = W.MoEConfig("one", 24, 256, 128, 4, 1, 128, True, 3)
+    ids = np.full((24, 1), 2, np.int32)              # experts 0, 1, 3 get no rows
+    w = np.ones((24, 1), np.float32)
+    dgu, dd, gud, ddv, qw = _moe_experts_rtn(cfg, {2})
+    Xb = W.moe_activations(cfg)
+    out, ws = _run_moe_forward(cfg, Xb, ids, w, gud, ddv)
+    ref = O.moe_layer(W.bf16_values(Xb), ids, w, lambda e: qw[e], cfg.E, cfg.I, cfg.group_size)
+    _check_moe(out, ref, qw, cfg.group_size)

@@ -1,0 +1,221 @@
+"""Host-only tests of the C-ABI library: exports, blob layout, offline pack parity with the
+oracle, argument validation.  No GPU and no kernel launch is needed: every error path
+returns before anything is enqueued."""
+import ctypes
+import os
+import re
+import struct
+
+import numpy as np
+import pytest
+
+import moe_token_int8_amd as L
+import oracle as O
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "w4a8.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    declared = set(re.findall(r"\b(w4a8_[a-z0-9_]+)\s*\(", hdr))
+    assert declared, "no declarations parsed"
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert declared == set(L.EXPORTED)
+    assert L.w4a8_version() == 1
+
+
+# ---------------------------------------------------------------- independent layout decoder
+def decode_blob(blob: np.ndarray):
+    """Reads a blob using only the layout text of include/w4a8.h (header fields, superblock
+    index, lane/byte/nibble formula, scale index)."""
+    magic = bytes(blob[:8])
+    assert magic == b"W4A8BLB1"
+    version, layout, K, N, g, asym, sdt, zdt = struct.unpack_from("<IIiiiiII", blob, 8)
+    assert (version, layout, sdt, zdt) == (1, 1, 0, 0)
+    co, cb, so, sb_, zo, zb, total = struct.unpack_from("<7Q", blob, 40)
+    Np = (N + 15) // 16 * 16
+    G = K // g
+    assert cb == Np * K // 2 and sb_ == Np * G * 4 and zb == (Np * G if asym else 0)
+    assert co == 256 and so % 256 == 0 and zo % 256 == 0 and total % 256 == 0
+    raw = blob[co:co + cb]
+    codes = np.zeros((K, N), np.int8)
+    for n in range(N):
+        for k in range(K):
+            kk, c = k % 128, n % 16
+            half, r = kk // 64, kk % 64
+            lane, j = (r // 16) * 16 + c, r % 16
+            sbi = (n // 16) * (K // 128) + k // 128
+            byte = sbi * 1024 + lane * 16 + half * 8 + (j // 8) * 4 + (j % 4)
+            nib = (j % 8) // 4
+            v = (int(raw[byte]) >> (4 * nib)) & 0xF
+            codes[k, n] = v - 16 if (not asym and v >= 8) else v
+    sc = np.frombuffer(blob[so:so + sb_].tobytes(), np.float32)
+    scales = np.zeros((G, N), np.float32)
+    zeros = np.zeros((G, N), np.uint8) if asym else None
+    for n in range(N):
+        for i in range(G):
+            idx = ((n // 16) * G + i) * 16 + n % 16
+            scales[i, n] = sc[idx]
+            if asym:
+                zeros[i, n] = blob[zo + idx]
+    # padding columns hold code 0 and scale 0
+    for n in range(N, Np):
+        for i in range(G):
+            assert sc[((n // 16) * G + i) * 16 + n % 16] == 0
+    return dict(K=K, N=N, g=g, asym=bool(asym), codes=codes, scales=scales, zeros=zeros, total=total)
+
+
+@pytest.mark.parametrize("K,N,g,asym", [(128, 16, 32, False), (256, 40, 64, True), (384, 19, 128, False),
+                                        (512, 33, 256, True), (256, 48, 128, True), (128, 1, 64, False)])
+def test_pack_matches_oracle_via_independent_decoder(K, N, g, asym):
+    Wt = W.random_weights(1000 + K + N, K, N)
+    Wt[:g, 0] = 0.0                                   # one all-zero group
+    d = L.desc(K, N, g, asym)
+    blob = L.w4a8_pack(d, Wt)
+    dec = decode_blob(blob)
+    codes, scales, zeros = O.quant_weight(Wt, g, asym)
+    assert (dec["K"], dec["N"], dec["g"], dec["asym"]) == (K, N, g, asym)
+    assert np.array_equal(dec["codes"], codes)
+    assert np.array_equal(dec["scales"].view(np.uint32), scales.view(np.uint32))
+    if asym:
+        assert np.array_equal(dec["zeros"], zeros)
+    # the library's own inverse agrees
+    d2, c2, s2, z2 = L.w4a8_unpack_codes(blob)
+    assert (d2.K, d2.N, d2.group_size, d2.asymmetric) == (K, N, g, int(asym))
+    assert np.array_equal(c2, codes) and np.array_equal(s2.view(np.uint32), scales.view(np.uint32))
+    if asym:
+        assert np.array_equal(z2, zeros)
+    # packing the oracle's codes reproduces the blob byte for byte
+    assert np.array_equal(L.w4a8_pack_codes(d, codes, scales, zeros), blob)
+    L.w4a8_blob_check(blob, d)
+
+
+def test_pack_page_examples_through_library():
+    # P3 symmetric group-wise reference example (transposed: groups along K)
+    x = np.array([[0.0, -1.0, 0.5, 0.25], [3.0, -2.0, 1.0, 0.0]], np.float32)
+    Wt = np.zeros((128, 16), np.float32)
+    Wt[:4, :2] = x.T
+    blob = L.w4a8_pack(L.desc(128, 16, 32, False), Wt)
+    dec = decode_blob(blob)
+    assert dec["codes"][:4, :2].T.tolist() == [[0, -7, 3, 2], [7, -5, 2, 0]]
+    # P2 range example (asymmetric): z = 8 and 0 maps to z
+    Wa = np.zeros((128, 16), np.float32)
+    Wa[:4, 0] = [-1.2, 0.0, 0.4, 1.2]
+    dec = decode_blob(L.w4a8_pack(L.desc(128, 16, 32, True), Wa))
+    assert dec["zeros"][0, 0] == 8 and dec["codes"][1, 0] == 8 and dec["codes"][0, 0] == 0
+
+
+@pytest.mark.parametrize("K,N,g,asym", [(4096, 14336, 128, False), (4096, 14336, 128, True),
+                                        (7168, 4096, 64, True), (1408, 4096, 128, False), (128, 5, 32, False)])
+def test_packed_size_formula(K, N, g, asym):
+    """P3 memory formula M = N b/8 + N_groups M_meta + M_pad with fp32 scales, uint8 zeros,
+    16-column padding, a 256-byte header and 256-byte section alignment."""
+    Np = (N + 15) // 16 * 16
+    G = K // g
+    a = lambda v: (v + 255) // 256 * 256
+    meta = 4 + (1 if asym else 0)
+    body = O.memory_bytes(Np * K, 4, Np * G, meta)
+    expect = a(a(a(256 + Np * K // 2) + Np * G * 4) + (Np * G if asym else 0))
+    assert L.w4a8_packed_size(L.desc(K, N, g, asym)) == expect
+    assert expect - 256 - body < 3 * 256                 # only alignment on top of the formula
+    # effective bits per weight without padding/header (P3 b_eff)
+    assert abs(body * 8 / (Np * K) - O.effective_bits(4, 32, 8 if asym else 0, g)) < 1e-12
+
+
+def test_validation_errors_host():
+    lib = L.lib()
+    bad = [L.desc(100, 16, 32, False), L.desc(128, 16, 48, False), L.desc(128, 0, 32, False),
+           L.desc(0, 16, 32, False), L.WDesc(128, 16, 32, 2)]
+    for d in bad:
+        assert L.w4a8_packed_size(d) == 0
+        assert lib.w4a8_pack(ctypes.byref(d), None, None, 0) == L.W4A8_EINVAL
+    # K not a multiple of the 128-deep superblock: valid grouping, layout unsupported
+    d = L.desc(192, 16, 64, False)
+    assert lib.w4a8_pack(ctypes.byref(d), None, None, 0) == L.W4A8_EUNSUPPORTED
+    d = L.desc(128, 16, 64, False)
+    Wt = np.zeros((128, 16), np.float32)
+    small = np.zeros(100, np.uint8)
+    assert lib.w4a8_pack(ctypes.byref(d), Wt.ctypes.data, small.ctypes.data, 100) == L.W4A8_ESIZE
+    Wt[3, 3] = np.inf
+    blob = np.zeros(L.w4a8_packed_size(d), np.uint8)
+    assert lib.w4a8_pack(ctypes.byref(d), Wt.ctypes.data, blob.ctypes.data, blob.nbytes) == L.W4A8_EINVAL
+    codes = np.full((128, 16), 8, np.int8)                # out of the symmetric range
+    scales = np.ones((2, 16), np.float32)
+    assert lib.w4a8_pack_codes(ctypes.byref(d), codes.ctypes.data, scales.ctypes.data, None,
+                               blob.ctypes.data, blob.nbytes) == L.W4A8_EINVAL
+    da = L.desc(128, 16, 64, True)
+    blob_a = np.zeros(L.w4a8_packed_size(da), np.uint8)
+    zeros = np.full((2, 16), 16, np.uint8)
+    codes[:] = 3
+    assert lib.w4a8_pack_codes(ctypes.byref(da), codes.ctypes.data, scales.ctypes.data, zeros.ctypes.data,
+                               blob_a.ctypes.data, blob_a.nbytes) == L.W4A8_EINVAL
+    # header checks
+    good = L.w4a8_pack(d, np.zeros((128, 16), np.float32))
+    with pytest.raises(L.W4A8Error):
+        L.w4a8_blob_check(good, L.desc(128, 32, 64, False))
+    broken = good.copy()
+    broken[0] = ord("X")
+    with pytest.raises(L.W4A8Error):
+        L.w4a8_unpack_codes(broken)
+    with pytest.raises(L.W4A8Error):
+        L.w4a8_blob_check(good[:200], d)
+
+
+def test_gpu_entry_points_validate_before_launch():
+    """Every rejected call returns before any HIP call, so this runs without a GPU."""
+    lib = L.lib()
+    d = L.desc(256, 32, 128, False)
+    fake = 0x10000            # aligned, never dereferenced: validation fails earlier
+    mis = 0x10001             # misaligned
+    E = L.W4A8_EINVAL
+    assert lib.w4a8_quant_act(fake, 0, 256, 256, fake, fake, None) == L.W4A8_OK       # M = 0
+    assert lib.w4a8_quant_act(fake, 4, 100, 100, fake, fake, None) == E               # K % 16
+    assert lib.w4a8_quant_act(fake, 4, 256, 128, fake, fake, None) == E               # ldx < K
+    assert lib.w4a8_quant_act(mis, 4, 256, 256, fake, fake, None) == E
+    assert lib.w4a8_quant_act(None, 4, 256, 256, fake, fake, None) == E
+    assert lib.w4a8_quant_act(fake, 4, 131072, 131072, fake, fake, None) == L.W4A8_EUNSUPPORTED
+    assert lib.w4a8_gemm(fake, fake, 0, fake, ctypes.byref(d), fake, 32, 0, None) == L.W4A8_OK
+    assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(d), fake, 32, 7, None) == E
+    assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(d), fake, 16, 0, None) == E   # ldy < N
+    assert lib.w4a8_gemm(mis, fake, 4, fake, ctypes.byref(d), fake, 32, 0, None) == E
+    assert lib.w4a8_gemm(fake, None, 4, fake, ctypes.byref(d), fake, 32, 0, None) == E
+    d32 = L.desc(256, 32, 32, False)         # packs, but no kernel implements g = 32
+    assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(d32), fake, 32, 0, None) == L.W4A8_EUNSUPPORTED
+    assert L.w4a8_kernel_name(d32, 4) == "unsupported"
+    dbad = L.desc(250, 32, 125, False)
+    assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(dbad), fake, 32, 0, None) == E
+    assert lib.w4a8_gemm_partials(fake, 4, fake, ctypes.byref(d), None, None) == E
+    assert lib.w4a8_moe_align(fake, 4, 2, 0, fake, fake, fake, None) == E
+    assert lib.w4a8_moe_align(fake, 4, 2, 2000, fake, fake, fake, None) == E
+    assert lib.w4a8_moe_align(fake, 4, 0, 8, fake, fake, fake, None) == E
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 0, fake, 4096, ctypes.byref(d), fake, 0, None) == L.W4A8_OK
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 0, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0, None) == E
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 64, ctypes.byref(d), fake, 0, None) == E  # stride
+    assert lib.w4a8_silu_mul_quant(fake, 4, 24, fake, fake, None) == E                # I % 16
+    assert lib.w4a8_silu_mul_quant(fake, 0, 32, fake, fake, None) == L.W4A8_OK
+    assert lib.w4a8_moe_combine(fake, fake, fake, 4, 2, 12, fake, None) == E          # H % 8
+    assert lib.w4a8_moe_combine(fake, fake, fake, 0, 2, 16, fake, None) == L.W4A8_OK
+    gu = L.desc(256, 64, 128, False)
+    dd = L.desc(32, 256, 32, False)           # K = I = 32 groups fine, but K % 128 != 0
+    ws = L.w4a8_moe_workspace_size(4, 2, 256, 32, 8)
+    assert ws > 0 and ws % 256 == 0
+    assert lib.w4a8_moe_forward(fake, fake, fake, 4, 2, 8, fake, 1 << 20, ctypes.byref(gu), fake, 1 << 20,
+                                ctypes.byref(dd), fake, ws, fake, None) == L.W4A8_EUNSUPPORTED
+    dd2 = L.desc(128, 256, 128, False)        # I = 128 but gate/up says I = 32
+    assert lib.w4a8_moe_forward(fake, fake, fake, 4, 2, 8, fake, 1 << 20, ctypes.byref(gu), fake, 1 << 20,
+                                ctypes.byref(dd2), fake, ws, fake, None) == E
+    gu2 = L.desc(256, 256, 128, False)
+    ws2 = L.w4a8_moe_workspace_size(4, 2, 256, 128, 8)
+    assert lib.w4a8_moe_forward(fake, fake, fake, 4, 2, 8, fake, 1 << 20, ctypes.byref(gu2), fake, 1 << 20,
+                                ctypes.byref(dd2), fake, ws2 - 256, fake, None) == L.W4A8_ESIZE
+    assert L.w4a8_moe_workspace_size(0, 0, 1, 1, 1) == 0
+
+
+def test_kernel_names_resolve():
+    for M, g, asym in [(1, 128, False), (32, 128, False), (8, 64, True), (4096, 128, True)]:
+        name = L.w4a8_kernel_name(L.desc(4096, 14336, g, asym), M)
+        assert name.startswith("w4a8_") and ("asym" in name) == asym and f"g{g}" in name
