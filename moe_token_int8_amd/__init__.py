@@ -22,7 +22,7 @@ HEADER_BYTES = 256
 
 EXPORTED = [
     "w4a8_packed_size", "w4a8_pack", "w4a8_pack_codes", "w4a8_unpack_codes", "w4a8_blob_check",
-    "w4a8_quant_act", "w4a8_gemm", "w4a8_gemm_partials", "w4a8_moe_align", "w4a8_moe_gemm",
+    "w4a8_quant_act", "w4a8_gemm", "w4a8_linear", "w4a8_gemm_partials", "w4a8_moe_align", "w4a8_moe_gemm",
     "w4a8_silu_mul_quant", "w4a8_moe_combine", "w4a8_moe_workspace_size", "w4a8_moe_forward",
     "w4a8_kernel_name", "w4a8_status_string", "w4a8_version",
 ]
@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "w4a8_blob_check": (I, [P, SZ, DP]),
             "w4a8_quant_act": (I, [P, I, I, I, P, P, VP]),
             "w4a8_gemm": (I, [P, P, I, P, DP, P, I, I, VP]),
+            "w4a8_linear": (I, [P, I, I, I, P, DP, P, I, I, P, P, VP]),
             "w4a8_gemm_partials": (I, [P, I, P, DP, P, VP]),
             "w4a8_moe_align": (I, [P, I, I, I, P, P, P, VP]),
             "w4a8_moe_gemm": (I, [P, P, P, I, P, I, I, P, SZ, DP, P, I, VP]),
@@ -192,6 +193,15 @@ def w4a8_gemm(Xq, sx, blob_dev, d: WDesc, Y, out_dtype: int = W4A8_OUT_BF16, str
     _require_cuda(Xq, sx, blob_dev, Y)
     _check(lib().w4a8_gemm(_ptr(Xq), _ptr(sx), Xq.shape[0], _ptr(blob_dev), ctypes.byref(d), _ptr(Y),
                            Y.stride(0), int(out_dtype), _stream(stream)), "w4a8_gemm")
+
+
+def w4a8_linear(X, blob_dev, d: WDesc, Y, Xq, sx, out_dtype: int = W4A8_OUT_BF16, stream=None) -> None:
+    """Quantize X (bf16 [M, K]) per token and multiply: Y = GEMM(quant(X)); Xq/sx receive the
+    activation codes and scales."""
+    _require_cuda(X, blob_dev, Y, Xq, sx)
+    M, K = X.shape
+    _check(lib().w4a8_linear(_ptr(X), M, K, X.stride(0), _ptr(blob_dev), ctypes.byref(d), _ptr(Y), Y.stride(0),
+                             int(out_dtype), _ptr(Xq), _ptr(sx), _stream(stream)), "w4a8_linear")
 
 
 def w4a8_gemm_partials(Xq, blob_dev, d: WDesc, P, stream=None) -> None:

@@ -57,14 +57,22 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red, int
     return r;
 }
 
-// One element of the per-token rule q = clamp(rint(fl32(x / d)), -127, 127).
-// x * (1/d) is within 2.3e-5 of fl32(x / d) for |x / d| <= 127.00001, so whenever its
-// distance to the nearest integer is below 0.4999 both round to the same integer; the
-// rare near-tie (and tiny-scale rows) take the IEEE division.
+// One element of the per-token rule q = clamp(rint(fl32(x / d)), -127, 127), branch free.
+// inv = RN(1/d) comes from one IEEE division per row.  q0 = RN(x * inv) is within 1.5 ulp of
+// x/d; one Newton correction q1 = RN(q0 + inv * (x - d * q0)) (residual through fma) has an
+// error far below 1 ulp before rounding, so q1 is faithful; by Markstein's theorem a second
+// correction from a faithful q1 with the correctly rounded reciprocal inv gives exactly
+// RN(x / d), the IEEE float32 quotient.  Rows with a tiny divisor (fast == false, uniform per
+// row) use the IEEE division directly.
 __device__ __forceinline__ int quant_one(float x, float d, float inv, bool fast) {
-    const float r = x * inv;
-    float q = rintf(r);
-    if (__builtin_expect(!fast || fabsf(r - q) > 0.4999f, 0)) q = rintf(x / d);
+    float q;
+    if (fast) {
+        const float q0 = x * inv;
+        const float q1 = fmaf(fmaf(-d, q0, x), inv, q0);
+        q = rintf(fmaf(fmaf(-d, q1, x), inv, q1));
+    } else {
+        q = rintf(x / d);
+    }
     q = fminf(fmaxf(q, -127.0f), 127.0f);
     return (int)q;
 }
@@ -74,7 +82,12 @@ struct RowScale {
     bool finite, fast;
 };
 
+// Scale of a row from the bit pattern of its abs-max.  With UNIFORM (the default) amax_bits
+// must be the same in every lane of the wave: it is broadcast from lane 0 so that the scale,
+// and the branch on `fast`, are wave-uniform.
+template <bool UNIFORM = true>
 __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
+    if (UNIFORM) amax_bits = __builtin_amdgcn_readfirstlane(amax_bits);
     RowScale r;
     r.finite = amax_bits < 0x7f800000u;
     const float amax = __uint_as_float(amax_bits);
@@ -204,8 +217,10 @@ __global__ __launch_bounds__(256) void silu_quant_kernel(const uint16_t* __restr
 enum { MODE_OUT = 0, MODE_PARTIALS = 1 };
 
 struct GemmArgs {
-    const int8_t* Xq;
-    const float* sx;
+    const int8_t* Xq;         // INT8 activations (or, fused path: where to write them)
+    const float* sx;          // row scales (or, fused path: where to write them)
+    const uint16_t* X;        // fused path: bfloat16 activations [M, ldx]
+    int ldx;
     int M, K, N, G;
     const uint8_t* blob;      // blob of expert 0 (or the only blob)
     size_t codes_off, scales_off, zeros_off, expert_stride;
@@ -286,17 +301,31 @@ struct DecodeShape {
     static constexpr int CS = KW * SBN;                        // superblocks per chunk
     static constexpr int ROWB = CS * SB_K + 16;                // padded LDS row stride
     static constexpr int APT = (MT * CS * 8 + NTHR - 1) / NTHR;  // 16-byte A pieces / thread
+    static constexpr int XPT = 4;                              // fused quant: bf16 pieces / thread
+    static constexpr int AIW = (MT * CS / 8 + NT * KW - 1) / (NT * KW);  // 1 KiB LDS loads / wave
+    // s_waitcnt immediate: vmcnt = SBN, the weight loads that every wave issues last, after its
+    // activation and scale loads, and always consumes; expcnt and lgkmcnt unconstrained
+    static constexpr int vm_wait() { return (SBN & 15) | ((SBN >> 4) << 14) | (7 << 4) | (15 << 8); }
     static constexpr size_t LDS_A = size_t(MT) * ROWB;
     static constexpr size_t LDS_RED = size_t(KW > 1 ? KW - 1 : 1) * NT * MS * 4 * 64 * 4;
-    static constexpr size_t LDS = LDS_A > LDS_RED ? LDS_A : LDS_RED;
+    static constexpr size_t LDS_SX = 32 * 4;               // row scales + row abs-max (fused)
+    static constexpr size_t LDS = LDS_A + LDS_RED + LDS_SX;
 };
 
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE>
+// FQ (fused quantization; dense, M * K <= 4 * 8 * threads, K % 512 == 0, one chunk): the
+// workgroup quantizes its own activation rows from bfloat16 with exactly the per-token rule
+// of quant_act_kernel (row abs-max: wave reductions merged by LDS atomic max), and
+// workgroup x = 0 also writes Xq and sx out.
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool FQ>
 __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     using S = DecodeShape<MS, NT, KW, SBN>;
     constexpr int MT = S::MT, NTHR = S::NTHR, CS = S::CS, ROWB = S::ROWB, APT = S::APT;
+    static_assert(!FQ || (MS == 1 && NT * KW == 16 && !MOE), "fused quantization layout");
     extern __shared__ __align__(16) uint8_t smem[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float* red = reinterpret_cast<float*>(smem + S::LDS_A);
+    float* sxs = reinterpret_cast<float*>(smem + S::LDS_A + S::LDS_RED);
+    // wave-derived indices are made explicitly uniform so per-slice loops branch on scalars
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = wave % NT, q = wave / NT;
     const int ntiles = (a.N + 15) / 16;
     const int tile = blockIdx.x * NT + t;
@@ -322,7 +351,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     const uint8_t* zeros = blob + a.zeros_off;
 
     // row scales of the rows this lane stores, fetched before anything else so the
-    // epilogue never waits on a load
+    // epilogue never waits on a load (fused path: computed below)
     float sxr[MS][4];
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms)
@@ -330,7 +359,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i) {
             sxr[ms][i] = 0.0f;
             const int row = rbeg + ms * 16 + 4 * (lane >> 4) + i;
-            if (MODE != MODE_PARTIALS && q == 0 && row < rend) {
+            if (!FQ && MODE != MODE_PARTIALS && q == 0 && row < rend) {
                 const int srow = (MOE && a.gather) ? a.gather[row] / a.topk : row;
                 sxr[ms][i] = a.sx[srow];
             }
@@ -342,48 +371,140 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) accf[ms][i] = 0.0f;
     const v4i zero4 = {0, 0, 0, 0};
+    if (FQ) {
+        if (tid < MT) reinterpret_cast<uint32_t*>(sxs + 16)[tid] = 0u;
+        __syncthreads();
+    }
 
     for (int cb = 0; cb < nsb; cb += CS) {
         const int clen = min(CS, nsb - cb);
-        const int rowpieces = clen * 8;                  // 16-byte pieces per row in this chunk
+        const int rowpieces = clen * 8;                  // 16-byte int8 pieces per row in this chunk
         // 1. activation rows of the chunk (first in this wave's load queue)
-        uint4 ap[APT];
+        uint4 xv[FQ ? S::XPT : 1];
+        if (!FQ) {
+            // straight into LDS (global_load_lds): the wave writes 1 KiB pieces of a row at
+            // M0 + 16 * lane.  Rows past the tile's end repeat a valid row (their outputs are
+            // never stored); lanes past the chunk's end are masked off.
+            const int parts = (rowpieces + 63) / 64;
 #pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int p = tid + i * NTHR;
-            const int row = p / rowpieces, c = p - row * rowpieces;
-            ap[i] = make_uint4(0, 0, 0, 0);
-            if (row < nrows) {
-                int src = rbeg + row;
-                if (MOE && a.gather) src = a.gather[src] / a.topk;
-                ap[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(src) * a.K + size_t(cb) * SB_K + c * 16);
+            for (int i = 0; i < S::AIW; ++i) {
+                const int ci = wave + i * (NT * KW);
+                if (ci < MT * parts) {
+                    const int row = ci / parts, part = ci - row * parts;
+                    int src = rbeg + min(row, nrows - 1);
+                    if (MOE && a.gather) src = a.gather[src] / a.topk;
+                    const int c = part * 64 + lane;
+                    if (c < rowpieces)
+                        __builtin_amdgcn_global_load_lds(
+                            a.Xq + size_t(src) * a.K + size_t(cb) * SB_K + c * 16,
+                            (__attribute__((address_space(3))) void*)(smem + row * ROWB + part * 1024), 16, 0, 0);
+                }
+            }
+        } else {
+            // piece p = tid + i * NTHR of the M x K bf16 block (8 values each); a row holds
+            // K / 8 pieces, a multiple of 64, so the 64 lanes of a wave share one row
+#pragma unroll
+            for (int i = 0; i < S::XPT; ++i) {
+                const int pc = tid + i * NTHR;
+                const int row = pc / (nsb * 16), c = pc - row * (nsb * 16);
+                xv[i] = make_uint4(0, 0, 0, 0);
+                if (row < nrows) xv[i] = *reinterpret_cast<const uint4*>(a.X + size_t(rbeg + row) * a.ldx + c * 8);
             }
         }
+        // keep the weight loads below the activation loads in program order
+        asm volatile("" ::: "memory");
         // 2. this wave's weight superblocks, scales and zero points
         const int s0 = cb + q * SBN;
         const int s_end = min(cb + clen, s0 + SBN);
         uint4 bq[SBN];
         float sc[SBN][GPS];
         uint32_t zq[SBN][GPS];
+        // 32-bit offsets from wave-uniform bases (a blob is far below 4 GiB): saddr-form loads,
+        // no 64-bit per-lane addresses to keep alive
+        const uint32_t boff = (uint32_t(tile_c) * uint32_t(nsb)) * 1024u + uint32_t(lane) * 16u;
+        const uint32_t moff = uint32_t(tile_c) * uint32_t(a.G) * 16u + uint32_t(lane & 15);
+        // group scales / zero points first, then the weights: the weight loads are the last
+        // SBN loads of the wave, which is what the activation wait below counts on
 #pragma unroll
         for (int s = 0; s < SBN; ++s) {
-            const int sb = min(s0 + s, nsb - 1);
-            bq[s] = *reinterpret_cast<const uint4*>(codes + (size_t(tile_c) * nsb + sb) * 1024 + lane * 16);
+            const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
 #pragma unroll
             for (int gi = 0; gi < GPS; ++gi) {
-                const size_t mi = (size_t(tile_c) * a.G + size_t(sb) * GPS + gi) * 16 + (lane & 15);
+                const uint32_t mi = moff + (sb * GPS + gi) * 16u;
                 sc[s][gi] = scales[mi];
                 if (ASYM) zq[s][gi] = zeros[mi];
             }
         }
-        // 3. activations to LDS (zero rows past the tile's end)
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int p = tid + i * NTHR;
-            const int row = p / rowpieces, c = p - row * rowpieces;
-            if (row < MT) *reinterpret_cast<uint4*>(smem + row * ROWB + c * 16) = ap[i];
+        for (int s = 0; s < SBN; ++s) {
+            const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
+            bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * 1024u));
         }
-        __syncthreads();
+        // 3. wait for this wave's activation loads only (the weight loads issued after them
+        //    stay in flight), or quantize the bf16 rows (fused path)
+        if (!FQ) {
+            __builtin_amdgcn_s_waitcnt(S::vm_wait());
+        } else {
+            uint32_t* rowmax = reinterpret_cast<uint32_t*>(sxs + 16);
+#pragma unroll
+            for (int i = 0; i < S::XPT; ++i) {
+                const int pc = tid + i * NTHR;
+                const int row = pc / (nsb * 16);
+                uint32_t amax = 0;
+                const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    amax = max(amax, (w[j] & 0x7fffu) << 16);
+                    amax = max(amax, w[j] & 0x7fff0000u);
+                }
+                amax = wave_max_u32(amax);
+                if (lane == 0 && row < nrows) atomicMax(rowmax + row, amax);
+            }
+            __syncthreads();
+            int8_t* xq_out = const_cast<int8_t*>(a.Xq);
+#pragma unroll
+            for (int i = 0; i < S::XPT; ++i) {
+                __builtin_amdgcn_sched_barrier(0);       // one piece at a time: bounded live range
+                const int pc = tid + i * NTHR;
+                const int row = pc / (nsb * 16), c = pc - row * (nsb * 16);
+                if (row >= MT) continue;
+                const bool rvalid = row < nrows;
+                const RowScale rs = row_scale(rvalid ? rowmax[row] : 0u);
+                const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+                uint32_t out[2] = {0, 0};
+                if (rvalid && rs.finite) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int q0 = quant_one(bf16_to_f32(w[j] & 0xffffu), rs.d, rs.inv, rs.fast);
+                        const int q1 = quant_one(bf16_to_f32(w[j] >> 16), rs.d, rs.inv, rs.fast);
+                        const uint32_t pair = (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8);
+                        out[j >> 1] |= pair << ((j & 1) * 16);
+                    }
+                }
+                *reinterpret_cast<uint2*>(smem + row * ROWB + c * 8) = make_uint2(out[0], out[1]);
+                if (rvalid && blockIdx.x == 0)
+                    *reinterpret_cast<uint2*>(xq_out + size_t(rbeg + row) * a.K + c * 8) = make_uint2(out[0], out[1]);
+            }
+            if (tid < MT) {
+                const bool rvalid = tid < nrows;
+                const RowScale rs = row_scale<false>(rvalid ? rowmax[tid] : 0u);
+                sxs[tid] = rvalid ? rs.s : 0.0f;
+                if (rvalid && blockIdx.x == 0) const_cast<float*>(a.sx)[rbeg + tid] = rs.s;
+            }
+        }
+        if (FQ) {
+            __syncthreads();
+        } else {
+            // every wave waited for its own LDS-direct loads above (their completion means the
+            // bytes are in LDS); a plain barrier then publishes them without draining the
+            // weight loads still in flight
+            __builtin_amdgcn_s_barrier();
+        }
+        if (FQ && MODE != MODE_PARTIALS && q == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sxr[0][i] = sxs[4 * (lane >> 4) + i];
+        }
         // 4. MFMA over this wave's superblocks
 #pragma unroll
         for (int s = 0; s < SBN; ++s) {
@@ -428,12 +549,11 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                 }
             }
         }
-        __syncthreads();                                 // LDS is rewritten by the next chunk
+        if (cb + CS < nsb) __syncthreads();              // LDS is rewritten by the next chunk
     }
     if (MODE == MODE_PARTIALS) return;
 
-    // slice-ordered reduction through LDS, row scale, store
-    float* red = reinterpret_cast<float*>(smem);
+    // slice-ordered reduction through its own LDS region, row scale, store
     constexpr int NV = MS * 4;
     if (KW > 1) {
         if (q > 0) {
@@ -465,6 +585,251 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                 reinterpret_cast<float*>(a.Y)[size_t(row) * a.ldy + col] = y;
             else
                 reinterpret_cast<uint16_t*>(a.Y)[size_t(row) * a.ldy + col] = (uint16_t)f32_to_bf16_rne(y);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// W4A8 GEMM, prefill variant (large M): v_mfma_i32_32x32x32_i8, 256 x 128 workgroup tile
+//
+// 8 waves in a 4 (M) x 2 (N) grid, each computing a 64 x 64 tile as 2 x 2 MFMA tiles of
+// 32 x 32.  Per 128-deep superblock the workgroup stages through LDS (double buffered):
+//   - the activation tile [256 x 128] int8, rows padded to 144 bytes (conflict-free
+//     16-byte fragment reads);
+//   - the weight tile [128 columns x 128 k] unpacked ONCE by the workgroup from its packed
+//     nibbles into INT8 (q - z) MFMA operands, so the four waves that share a column block
+//     do not repeat the unpack;
+//   - the group scales of its 128 columns.
+// Global loads run two superblocks ahead of the MFMAs through registers.
+//
+// 32x32x32 operand mapping: MFMA step j (0..3) of a superblock covers k in [32j, 32j+32);
+// lane L supplies row/column L % 32 and k in [32j + 16*(L/32), +16).  The unpacked weight
+// tile is stored as [j][L/32][column][16 bytes] so a fragment is one 16-byte LDS read per
+// lane.  The INT32 result of lane L, register r, is C[8*(r/4) + 4*(L/32) + r%4][L % 32].
+// ------------------------------------------------------------------------------------
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int PF_BM = 256, PF_BN = 128, PF_THREADS = 512;
+constexpr int PF_AROW = SB_K + 16;                       // padded activation row (bytes)
+constexpr int PF_A_BYTES = PF_BM * PF_AROW;              // 36864
+constexpr int PF_B_BYTES = PF_BN * SB_K;                 // unpacked int8 weights: 16384
+constexpr int PF_S_BYTES = (PF_BN / 16) * 2 * 64;        // scales of up to 2 groups: 1024
+constexpr int PF_STAGE = PF_A_BYTES + PF_B_BYTES + PF_S_BYTES;
+constexpr int PF_LDS = 2 * PF_STAGE;
+
+// Workgroup id -> (M tile, N tile).  Consecutive ids are dealt round robin to the 8 XCDs,
+// so each XCD is given a contiguous range of tile indices; inside it, tiles are walked in
+// groups of 4 M tiles so that workgroups running together on one XCD share activation and
+// weight tiles in its L2.
+__device__ __forceinline__ void prefill_tile(int b, int mtiles, int ntiles, int* mt, int* nt) {
+    const int T = mtiles * ntiles;
+    const int per = T / 8, rem = T % 8;
+    const int x = b % 8, j = b / 8;
+    const int t = x * per + min(x, rem) + j;
+    constexpr int GM = 4;
+    const int group = t / (GM * ntiles);
+    const int first = group * GM;
+    const int gsz = min(GM, mtiles - first);
+    const int in = t - group * GM * ntiles;
+    *mt = first + in % gsz;
+    *nt = in / gsz;
+}
+
+struct PfRegs {
+    uint4 a[4];     // activation pieces
+    uint4 b;        // 16 bytes of packed codes (one layout lane of one 16-column tile)
+    uint4 m;        // scales piece (threads that stage metadata)
+    uint32_t z;     // zero points of this thread's column, one byte per group
+};
+
+template <bool ASYM, int GPS, int MODE>
+__global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 3, wn = wave >> 2;
+    const int mtiles = (a.M + PF_BM - 1) / PF_BM;
+    const int ntl16 = (a.N + 15) / 16;                   // 16-column tiles in the blob
+    const int ntiles = (ntl16 + 7) / 8;
+    int mt, nt;
+    prefill_tile(blockIdx.x, mtiles, ntiles, &mt, &nt);
+    const int m0 = mt * PF_BM, t0 = nt * 8;              // first row, first 16-column tile
+    const int nsb = a.K / SB_K;
+    const uint8_t* codes = a.blob + a.codes_off;
+    const uint8_t* scales_b = a.blob + a.scales_off;
+    const uint8_t* zeros_b = a.blob + a.zeros_off;
+
+    // staging: thread tid owns layout lane (tid % 64) of 16-column tile (tid / 64)
+    const int b_tile = min(t0 + wave, ntl16 - 1);
+    const int st_q4 = lane >> 4, st_c = lane & 15;
+    const int nmeta_s = 8 * GPS * 4;                     // 16-byte scale pieces
+    auto gload = [&](PfRegs& r, int sb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = tid + i * PF_THREADS;
+            const int row = p >> 3, c = p & 7;
+            r.a[i] = make_uint4(0, 0, 0, 0);
+            if (m0 + row < a.M)
+                r.a[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(m0 + row) * a.K + size_t(sb) * SB_K + c * 16);
+        }
+        r.b = *reinterpret_cast<const uint4*>(codes + (size_t(b_tile) * nsb + sb) * 1024 + lane * 16);
+        if (ASYM) {
+            r.z = 0;
+#pragma unroll
+            for (int gi = 0; gi < GPS; ++gi)
+                r.z |= uint32_t(zeros_b[(size_t(b_tile) * a.G + size_t(sb) * GPS + gi) * 16 + st_c]) << (8 * gi);
+        }
+        if (tid < nmeta_s) {
+            const int tl = tid / (GPS * 4), gi = (tid / 4) % GPS, q4 = tid % 4;
+            const int tile = min(t0 + tl, ntl16 - 1);
+            r.m = *reinterpret_cast<const uint4*>(scales_b + ((size_t(tile) * a.G + size_t(sb) * GPS + gi) * 16 + q4 * 4) * 4);
+        }
+    };
+    auto lstore = [&](const PfRegs& r, int stage) {
+        uint8_t* st = smem + stage * PF_STAGE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = tid + i * PF_THREADS;
+            *reinterpret_cast<uint4*>(st + (p >> 3) * PF_AROW + (p & 7) * 16) = r.a[i];
+        }
+        // unpack the 32 codes: half h holds k = 64h + 16*q4 + [0, 16) -> MFMA step
+        // j = 2h + q4/2, lane half q4 % 2
+        const int col = wave * 16 + st_c;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int gi = (GPS == 2) ? h : 0;
+            const uint32_t zc = ASYM ? (128u - ((r.z >> (8 * gi)) & 0xffu)) * 0x01010101u : 0u;
+            const v4i u = unpack_b<ASYM>(h ? r.b.z : r.b.x, h ? r.b.w : r.b.y, zc);
+            const int j = 2 * h + (st_q4 >> 1), hl = st_q4 & 1;
+            *reinterpret_cast<v4i*>(st + PF_A_BYTES + ((j * 2 + hl) * PF_BN + col) * 16) = u;
+        }
+        if (tid < nmeta_s) {
+            const int tl = tid / (GPS * 4), gi = (tid / 4) % GPS, q4 = tid % 4;
+            *reinterpret_cast<uint4*>(st + PF_A_BYTES + PF_B_BYTES + ((tl * GPS + gi) * 16 + q4 * 4) * 4) = r.m;
+        }
+    };
+
+    v16i acc[2][2];
+    float accf[2][2][16];
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) accf[ms][ns][r] = 0.0f;
+    const v16i zero16 = {};
+
+    // per-lane constants of the fragment reads
+    const int l32 = lane & 31, hi = lane >> 5;
+    int a_off[2];
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) a_off[ms] = (wm * 64 + ms * 32 + l32) * PF_AROW + hi * 16;
+    int b_off[2], s_off[2], col_g[2];
+#pragma unroll
+    for (int ns = 0; ns < 2; ++ns) {
+        const int colw = wn * 64 + ns * 32 + l32;       // column inside the workgroup tile
+        b_off[ns] = PF_A_BYTES + (hi * PF_BN + colw) * 16;
+        s_off[ns] = PF_A_BYTES + PF_B_BYTES + (((colw >> 4) * GPS) * 16 + (colw & 15)) * 4;
+        col_g[ns] = t0 * 16 + colw;
+    }
+
+    auto compute = [&](int stage, int sb) {
+        const uint8_t* st = smem + stage * PF_STAGE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int gi = (GPS == 2) ? (j >> 1) : 0;
+            v4i A[2], B[2];
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms) {
+                const uint4 v = *reinterpret_cast<const uint4*>(st + a_off[ms] + j * 32);
+                A[ms] = v4i{int(v.x), int(v.y), int(v.z), int(v.w)};
+            }
+#pragma unroll
+            for (int ns = 0; ns < 2; ++ns) B[ns] = *reinterpret_cast<const v4i*>(st + b_off[ns] + j * 2 * PF_BN * 16);
+            const bool first = (GPS == 2) ? ((j & 1) == 0) : (j == 0);
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ms], B[ns], first ? zero16 : acc[ms][ns], 0, 0, 0);
+            const bool last = (GPS == 2) ? ((j & 1) == 1) : (j == 3);
+            if (last) {
+                if (MODE == MODE_PARTIALS) {
+#pragma unroll
+                    for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                        for (int ns = 0; ns < 2; ++ns) {
+                            const int col = col_g[ns];
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                                if (row < a.M && col < a.N) {
+                                    const int v = ASYM ? acc[ms][ns][r] : (acc[ms][ns][r] >> 4);
+                                    a.P[(size_t(row) * a.N + col) * a.G + size_t(sb) * GPS + gi] = v;
+                                }
+                            }
+                        }
+                } else {
+#pragma unroll
+                    for (int ns = 0; ns < 2; ++ns) {
+                        float scl = *reinterpret_cast<const float*>(st + s_off[ns] + gi * 64);
+                        if (!ASYM) scl *= 0.0625f;
+#pragma unroll
+                        for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                accf[ms][ns][r] = fmaf((float)acc[ms][ns][r], scl, accf[ms][ns][r]);
+                    }
+                }
+            }
+        }
+    };
+
+    // pipeline: register set s%2 holds the loads of superblock s; stage s%2 of LDS holds
+    // superblock s while it is computed
+    PfRegs R0, R1;
+    gload(R0, 0);
+    if (nsb > 1) gload(R1, 1);
+    lstore(R0, 0);
+    if (nsb > 2) gload(R0, 2);
+    __syncthreads();
+    for (int kb = 0; kb < nsb; kb += 2) {
+        // even superblock kb: stage 0; R1 holds kb+1, R0 holds kb+2
+        if (kb + 1 < nsb) lstore(R1, 1);
+        if (kb + 3 < nsb) gload(R1, kb + 3);
+        compute(0, kb);
+        __syncthreads();
+        if (kb + 1 >= nsb) break;
+        // odd superblock kb+1: stage 1; R0 holds kb+2, R1 holds kb+3
+        if (kb + 2 < nsb) lstore(R0, 0);
+        if (kb + 4 < nsb) gload(R0, kb + 4);
+        compute(1, kb + 1);
+        __syncthreads();
+    }
+    if (MODE == MODE_PARTIALS) return;
+
+    // row scales, then store
+#pragma unroll
+    for (int ms = 0; ms < 2; ++ms) {
+        float sxv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            sxv[r] = row < a.M ? a.sx[row] : 0.0f;
+        }
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+            const int col = col_g[ns];
+            if (col >= a.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                if (row >= a.M) continue;
+                const float y = accf[ms][ns][r] * sxv[r];
+                if (a.out_f32)
+                    reinterpret_cast<float*>(a.Y)[size_t(row) * a.ldy + col] = y;
+                else
+                    reinterpret_cast<uint16_t*>(a.Y)[size_t(row) * a.ldy + col] = (uint16_t)f32_to_bf16_rne(y);
+            }
         }
     }
 }
@@ -615,10 +980,10 @@ static DecodeCfg decode_cfg(int K, int mt) {
     return c;
 }
 
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE>
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool FQ = false>
 static void launch_decode_t(const GemmArgs& a, dim3 grid, hipStream_t s) {
     using S = DecodeShape<MS, NT, KW, SBN>;
-    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE>;
+    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, FQ>;
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(S::LDS));
     (void)attr;
@@ -646,6 +1011,26 @@ static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool a
     }
 #undef W4A8_DEC
 }
+
+template <bool ASYM, int GPS, int MODE>
+static void launch_prefill_t(const GemmArgs& a, hipStream_t s) {
+    auto kern = gemm_prefill_kernel<ASYM, GPS, MODE>;
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS);
+    (void)attr;
+    const int mtiles = (a.M + PF_BM - 1) / PF_BM;
+    const int ntiles = ((a.N + 15) / 16 + 7) / 8;
+    kern<<<dim3(mtiles * ntiles), dim3(PF_THREADS), PF_LDS, s>>>(a);
+}
+
+template <int MODE>
+static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s) {
+    if (gps == 1) { if (asym) launch_prefill_t<true, 1, MODE>(a, s); else launch_prefill_t<false, 1, MODE>(a, s); }
+    else { if (asym) launch_prefill_t<true, 2, MODE>(a, s); else launch_prefill_t<false, 2, MODE>(a, s); }
+}
+
+// Dense GEMMs with more rows than this use the prefill kernel.
+constexpr int PREFILL_MIN_M = 33;
 
 static dim3 decode_grid(const Layout& L, const DecodeCfg& c, int ytiles) {
     const int ntiles = L.Np / 16;
@@ -720,11 +1105,55 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
     a.Y = Y;
     a.ldy = ldy;
     a.out_f32 = out_dtype == W4A8_OUT_F32;
+    if (M >= PREFILL_MIN_M) {
+        launch_prefill<MODE_OUT>(a, SB_K / d->group_size, d->asymmetric, static_cast<hipStream_t>(stream));
+        return launch_status();
+    }
     const int mt = dense_mt(M);
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
     launch_decode<MODE_OUT, false>(a, c, SB_K / d->group_size, d->asymmetric, grid, static_cast<hipStream_t>(stream));
     return launch_status();
+}
+
+int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4a8_wdesc* d, void* Y, int ldy,
+                int out_dtype, int8_t* Xq, float* sx, void* stream) {
+    int st = check_gemm_desc(d);
+    if (st) return st;
+    if (M < 0 || K != d->K || (out_dtype != W4A8_OUT_BF16 && out_dtype != W4A8_OUT_F32)) return W4A8_EINVAL;
+    if (M == 0) return W4A8_OK;
+    if (!X || !blob || !Y || !Xq || !sx || ldy < d->N || ldx < K) return W4A8_EINVAL;
+    if (ldx % 8 || !aligned16(X) || !aligned16(Xq) || !aligned16(blob)) return W4A8_EINVAL;
+    const Layout L = layout_of(d);
+    // fused path: one chunk, the unfused kernel's workgroup layout (same summation order)
+    if (M <= 16 && size_t(M) * L.K <= 32768 && L.K % 512 == 0 && L.K / SB_K <= 32 && decode_cfg(L.K, 16).kw == 4) {
+        GemmArgs a = make_args(L, Xq, sx, M, blob);
+        a.X = static_cast<const uint16_t*>(X);
+        a.ldx = ldx;
+        a.Y = Y;
+        a.ldy = ldy;
+        a.out_f32 = out_dtype == W4A8_OUT_F32;
+        const DecodeCfg c = decode_cfg(L.K, 16);       // same layout as the unfused kernel
+        const dim3 grid = decode_grid(L, c, 1);
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const int gps = SB_K / d->group_size;
+        const bool asym = d->asymmetric;
+#define W4A8_FQ(SBN_, GPS_, ASYM_) launch_decode_t<1, 4, 4, SBN_, GPS_, ASYM_, MODE_OUT, false, true>(a, grid, s)
+        if (c.sbn == 2) {
+            if (gps == 1) { if (asym) W4A8_FQ(2, 1, true); else W4A8_FQ(2, 1, false); }
+            else { if (asym) W4A8_FQ(2, 2, true); else W4A8_FQ(2, 2, false); }
+        } else if (c.sbn == 4) {
+            if (gps == 1) { if (asym) W4A8_FQ(4, 1, true); else W4A8_FQ(4, 1, false); }
+            else { if (asym) W4A8_FQ(4, 2, true); else W4A8_FQ(4, 2, false); }
+        } else {
+            if (gps == 1) { if (asym) W4A8_FQ(8, 1, true); else W4A8_FQ(8, 1, false); }
+            else { if (asym) W4A8_FQ(8, 2, true); else W4A8_FQ(8, 2, false); }
+        }
+#undef W4A8_FQ
+        return launch_status();
+    }
+    if ((st = w4a8_quant_act(X, M, K, ldx, Xq, sx, stream))) return st;
+    return w4a8_gemm(Xq, sx, M, blob, d, Y, ldy, out_dtype, stream);
 }
 
 int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob, const w4a8_wdesc* d, int32_t* P, void* stream) {
@@ -737,6 +1166,10 @@ int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob, const w4a8_wde
     const Layout L = layout_of(d);
     GemmArgs a = make_args(L, Xq, nullptr, M, blob);
     a.P = P;
+    if (M >= PREFILL_MIN_M) {
+        launch_prefill<MODE_PARTIALS>(a, SB_K / d->group_size, d->asymmetric, static_cast<hipStream_t>(stream));
+        return launch_status();
+    }
     const int mt = dense_mt(M);
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
@@ -897,6 +1330,9 @@ const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
     if (check_gemm_desc(d) != W4A8_OK || M < 0) return "unsupported";
     const bool asym = d->asymmetric;
     const bool g64 = d->group_size == 64;
+    if (M >= PREFILL_MIN_M)
+        return asym ? (g64 ? "w4a8_prefill_asym_g64" : "w4a8_prefill_asym_g128")
+                    : (g64 ? "w4a8_prefill_sym_g64" : "w4a8_prefill_sym_g128");
     if (dense_mt(M) == 16)
         return asym ? (g64 ? "w4a8_decode_m16_asym_g64" : "w4a8_decode_m16_asym_g128")
                     : (g64 ? "w4a8_decode_m16_sym_g64" : "w4a8_decode_m16_sym_g128");

@@ -184,6 +184,87 @@ def test_gemm_zero_and_nan_rows():
     assert np.all(np.isfinite(y[[0, 2, 4]]))
 
 
+# ---------------------------------------------------------------- fused quant + GEMM
+@pytest.mark.parametrize("M,K,N,g,asym", [(1, 4096, 14336, 128, False), (8, 4096, 14336, 128, False),
+                                          (16, 4096, 1024, 128, True), (5, 512, 40, 64, True),
+                                          (3, 1024, 33, 128, False), (20, 256, 64, 64, True),
+                                          (2, 7168, 64, 64, True)])
+def test_linear_matches_quant_then_gemm(M, K, N, g, asym):
+    """w4a8_linear (one kernel for M <= 16) equals quant_act followed by gemm bit for bit,
+    and writes the same activation codes and scales."""
+    Xb = W.random_activations(M * 3 + K + N, M, K, outlier_cols=2, outlier_scale=40.0)
+    x = W.bf16_values(Xb)
+    if M > 2:
+        x[1] = 0.0
+        Xb = W.to_bf16(x)
+    Wt = W.random_weights(K + 2 * N, K, N)
+    d = L.desc(K, N, g, asym)
+    blob = device_blob(d, L.w4a8_pack(d, Wt))
+    X = Xb.to(DEV)
+    for dt, tdt in ((L.W4A8_OUT_F32, torch.float32), (L.W4A8_OUT_BF16, torch.bfloat16)):
+        Xq1, sx1 = gpu_quant(Xb)
+        Y1 = torch.empty((M, N), dtype=tdt, device=DEV)
+        L.w4a8_gemm(Xq1, sx1, blob, d, Y1, dt)
+        Xq2 = torch.full((M, K), 99, dtype=torch.int8, device=DEV)
+        sx2 = torch.full((M,), -1.0, dtype=torch.float32, device=DEV)
+        Y2 = torch.empty((M, N), dtype=tdt, device=DEV)
+        L.w4a8_linear(X, blob, d, Y2, Xq2, sx2, dt)
+        assert torch.equal(Xq1, Xq2)
+        assert torch.equal(sx1.view(torch.int32), sx2.view(torch.int32))
+        assert torch.equal(Y1.view(torch.int16 if tdt == torch.bfloat16 else torch.int32),
+                           Y2.view(torch.int16 if tdt == torch.bfloat16 else torch.int32))
+    q, s = O.quant_act(x)
+    assert np.array_equal(Xq2.cpu().numpy(), q)
+
+
+# ---------------------------------------------------------------- prefill-size GEMMs
+@pytest.mark.parametrize("M,K,N,g,asym", [(300, 1024, 300, 128, True), (257, 512, 129, 64, False),
+                                          (64, 384, 256, 128, False), (513, 256, 48, 64, True)])
+def test_prefill_partials_bit_exact(M, K, N, g, asym):
+    _print(f"prefill partials M={M} K={K} N={N} g={g} asym={asym}")
+    Xb = W.random_activations(M + K + N, M, K, outlier_cols=3, outlier_scale=25.0)
+    Wt = W.random_weights(K * 3 + N, K, N)
+    d = L.desc(K, N, g, asym)
+    assert L.w4a8_kernel_name(d, M).startswith("w4a8_prefill")
+    blob = device_blob(d, L.w4a8_pack(d, Wt))
+    Xq, _ = gpu_quant(Xb)
+    P = torch.full((M, N, K // g), -7, dtype=torch.int32, device=DEV)
+    L.w4a8_gemm_partials(Xq, blob, d, P)
+    q, _ = O.quant_act(W.bf16_values(Xb))
+    codes, _, zeros = O.quant_weight(Wt, g, asym)
+    assert np.array_equal(P.cpu().numpy(), O.gemm_partials(q, codes, zeros, g))
+
+
+@pytest.mark.parametrize("M,K,N,g,asym", [(300, 1024, 272, 128, True), (257, 512, 129, 64, False),
+                                          (33, 2048, 64, 128, True), (1000, 256, 1000, 64, True)])
+def test_prefill_outputs(M, K, N, g, asym):
+    Xb = W.random_activations(M * 5 + N, M, K, outlier_cols=2, outlier_scale=30.0)
+    Wt = W.random_weights(N * 7 + K, K, N)
+    _print(_gemm_case(Xb, Wt, g, asym))
+
+
+@pytest.mark.parametrize("cfg", [W.C3_UP, W.C3_DOWN], ids=lambda c: c.name)
+def test_prefill_full_size_sampled_rows(cfg):
+    """The projection pair at full size (M=4096) in the benchmark's launch configuration;
+    the oracle checks 48 sampled rows (every column)."""
+    _print(f"prefill full {cfg.name}")
+    Xb, Wt = W.dense_inputs(cfg)
+    d = L.desc(cfg.K, cfg.N, cfg.group_size, cfg.asymmetric)
+    blob = device_blob(d, L.w4a8_pack(d, Wt))
+    Xq, sx = gpu_quant(Xb)
+    y32 = torch.empty((cfg.M, cfg.N), dtype=torch.float32, device=DEV)
+    ybf = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_gemm(Xq, sx, blob, d, y32, L.W4A8_OUT_F32)
+    L.w4a8_gemm(Xq, sx, blob, d, ybf, L.W4A8_OUT_BF16)
+    rows = np.sort(np.random.default_rng(cfg.seed).choice(cfg.M, 48, replace=False))
+    rows[0], rows[-1] = 0, cfg.M - 1
+    q, s = O.quant_act(W.bf16_values(Xb)[rows])
+    assert np.array_equal(Xq.cpu().numpy()[rows], q)
+    codes, scales, zeros = O.quant_weight(Wt, cfg.group_size, cfg.asymmetric)
+    Y64 = O.gemm(q, s, codes, scales, zeros, cfg.group_size)
+    _print(check_float_output(y32.cpu().numpy()[rows], ybf.float().cpu().numpy()[rows], Y64))
+
+
 # ---------------------------------------------------------------- MoE pieces
 def _routing(seed, T, E, k, zipf=0.0):
     cfg = W.MoEConfig("t", T, 128, 64, E, k, 64, False, seed, zipf_s=zipf)
