@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+CALIB_BYTES = 256 << 20         # size of the calibration copy (--calib)
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
 
 
@@ -43,6 +44,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--only", default="", help="comma list of legs: decode,prefill,moe")
     p.add_argument("--no-graph", action="store_true", help="launch the decode steps eagerly")
+    p.add_argument("--calib", action="store_true",
+                   help="also run one plain copy kernel (torch.neg over 256 MiB of fp32) so that "
+                        "hardware byte counters can be scaled against a known size")
     return p.parse_args()
 
 
@@ -171,6 +175,13 @@ def decode_leg(args, L, W, torch, dev):
         kt.stop(s)
     kt.pairs = kt.pairs[1:]
     k_ms = kt.mean_ms() / 64
+    if args.calib:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)            # reads CALIB_BYTES, writes CALIB_BYTES
+        torch.cuda.synchronize()
+        del src, dst
     M = 32
     kbytes = wbytes + M * cfg.K + 4 * M + 2 * M * cfg.N    # + Xq, sx, Y (bf16)
     achieved = kbytes / (k_ms * 1e-3) / 1e9

@@ -57,6 +57,18 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red, int
     return r;
 }
 
+// Workgroup barrier for LDS hand-offs that leaves global loads in flight: wait for this
+// wave's LDS (and scalar) operations only, then s_barrier.  The empty asm statements keep
+// the compiler from moving memory accesses across it.  (__syncthreads would also drain
+// every outstanding global load of the wave.)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    // s_waitcnt: vmcnt 63 (no wait), expcnt 7 (no wait), lgkmcnt 0
+    __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // One element of the per-token rule q = clamp(rint(fl32(x / d)), -127, 127), branch free.
 // inv = RN(1/d) comes from one IEEE division per row.  q0 = RN(x * inv) is within 1.5 ulp of
 // x/d; one Newton correction q1 = RN(q0 + inv * (x - d * q0)) (residual through fma) has an
@@ -301,25 +313,23 @@ struct DecodeShape {
     static constexpr int CS = KW * SBN;                        // superblocks per chunk
     static constexpr int ROWB = CS * SB_K + 16;                // padded LDS row stride
     static constexpr int APT = (MT * CS * 8 + NTHR - 1) / NTHR;  // 16-byte A pieces / thread
-    static constexpr int XPT = 4;                              // fused quant: bf16 pieces / thread
-    static constexpr int AIW = (MT * CS / 8 + NT * KW - 1) / (NT * KW);  // 1 KiB LDS loads / wave
-    // s_waitcnt immediate: vmcnt = SBN, the weight loads that every wave issues last, after its
-    // activation and scale loads, and always consumes; expcnt and lgkmcnt unconstrained
-    static constexpr int vm_wait() { return (SBN & 15) | ((SBN >> 4) << 14) | (7 << 4) | (15 << 8); }
+    static constexpr int XPT = 1;                              // fused quant: bf16 pieces / thread
     static constexpr size_t LDS_A = size_t(MT) * ROWB;
     static constexpr size_t LDS_RED = size_t(KW > 1 ? KW - 1 : 1) * NT * MS * 4 * 64 * 4;
     static constexpr size_t LDS_SX = 32 * 4;               // row scales + row abs-max (fused)
     static constexpr size_t LDS = LDS_A + LDS_RED + LDS_SX;
 };
 
-// FQ (fused quantization; dense, M * K <= 4 * 8 * threads, K % 512 == 0, one chunk): the
+// FQ (fused quantization; dense, M * K <= 8 * threads, K % 512 == 0, one chunk): the
 // workgroup quantizes its own activation rows from bfloat16 with exactly the per-token rule
 // of quant_act_kernel (row abs-max: wave reductions merged by LDS atomic max), and
 // workgroup x = 0 also writes Xq and sx out.
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool FQ>
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool FQ, bool MULTI>
 __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     using S = DecodeShape<MS, NT, KW, SBN>;
     constexpr int MT = S::MT, NTHR = S::NTHR, CS = S::CS, ROWB = S::ROWB, APT = S::APT;
+    // weight superblocks requested before the activation hand-off (the rest right after it)
+    constexpr int BE = FQ ? SBN : (MS == 2 ? (SBN < 2 ? SBN : 2) : (SBN < 4 ? SBN : 4));
     static_assert(!FQ || (MS == 1 && NT * KW == 16 && !MOE), "fused quantization layout");
     extern __shared__ __align__(16) uint8_t smem[];
     float* red = reinterpret_cast<float*>(smem + S::LDS_A);
@@ -376,28 +386,30 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         __syncthreads();
     }
 
-    for (int cb = 0; cb < nsb; cb += CS) {
+    // one chunk of the K loop.  A K that fits one chunk (MULTI = false) runs it as
+    // straight-line code, so no loop-carried state forces conservative load waits.
+    auto chunk = [&](const int cb) __attribute__((always_inline)) {
         const int clen = min(CS, nsb - cb);
         const int rowpieces = clen * 8;                  // 16-byte int8 pieces per row in this chunk
-        // 1. activation rows of the chunk (first in this wave's load queue)
-        uint4 xv[FQ ? S::XPT : 1];
+        // Load order matters: every wave of the workgroup first requests its activation
+        // pieces and group scales, then a barrier, and only then the weight stream.  The
+        // memory pipeline of a compute unit serves requests roughly in order, so the small
+        // operands that gate the first MFMA never queue behind another wave's weights.
+        // 1. activation pieces (int8 rows, or bfloat16 rows for the fused path) into registers
+        uint4 xv[FQ ? S::XPT : S::APT];
         if (!FQ) {
-            // straight into LDS (global_load_lds): the wave writes 1 KiB pieces of a row at
-            // M0 + 16 * lane.  Rows past the tile's end repeat a valid row (their outputs are
-            // never stored); lanes past the chunk's end are masked off.
-            const int parts = (rowpieces + 63) / 64;
+            // piece p = tid + i * NTHR: row p / (CS * 8), 16 bytes at column p % (CS * 8);
+            // rows past the tile's end are neither loaded nor written (their MFMA outputs are
+            // never stored)
 #pragma unroll
-            for (int i = 0; i < S::AIW; ++i) {
-                const int ci = wave + i * (NT * KW);
-                if (ci < MT * parts) {
-                    const int row = ci / parts, part = ci - row * parts;
-                    int src = rbeg + min(row, nrows - 1);
+            for (int i = 0; i < S::APT; ++i) {
+                const int pc = tid + i * NTHR;
+                const int row = pc / (CS * 8), c = pc - row * (CS * 8);
+                xv[i] = make_uint4(0, 0, 0, 0);
+                if (row < nrows && c < rowpieces) {
+                    int src = rbeg + row;
                     if (MOE && a.gather) src = a.gather[src] / a.topk;
-                    const int c = part * 64 + lane;
-                    if (c < rowpieces)
-                        __builtin_amdgcn_global_load_lds(
-                            a.Xq + size_t(src) * a.K + size_t(cb) * SB_K + c * 16,
-                            (__attribute__((address_space(3))) void*)(smem + row * ROWB + part * 1024), 16, 0, 0);
+                    xv[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(src) * a.K + size_t(cb) * SB_K + c * 16);
                 }
             }
         } else {
@@ -411,9 +423,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                 if (row < nrows) xv[i] = *reinterpret_cast<const uint4*>(a.X + size_t(rbeg + row) * a.ldx + c * 8);
             }
         }
-        // keep the weight loads below the activation loads in program order
-        asm volatile("" ::: "memory");
-        // 2. this wave's weight superblocks, scales and zero points
+        // 2. this wave's group scales and zero points
         const int s0 = cb + q * SBN;
         const int s_end = min(cb + clen, s0 + SBN);
         uint4 bq[SBN];
@@ -423,8 +433,6 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         // no 64-bit per-lane addresses to keep alive
         const uint32_t boff = (uint32_t(tile_c) * uint32_t(nsb)) * 1024u + uint32_t(lane) * 16u;
         const uint32_t moff = uint32_t(tile_c) * uint32_t(a.G) * 16u + uint32_t(lane & 15);
-        // group scales / zero points first, then the weights: the weight loads are the last
-        // SBN loads of the wave, which is what the activation wait below counts on
 #pragma unroll
         for (int s = 0; s < SBN; ++s) {
             const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
@@ -435,16 +443,27 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                 if (ASYM) zq[s][gi] = zeros[mi];
             }
         }
+        // 3. issue fence: all small requests of the workgroup are out before any weight request
         asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // 4. this wave's first BE weight superblocks, in the order they are consumed; the rest
+        //    follow once the activations are in LDS, which keeps the activation loads from
+        //    queueing behind the whole weight stream
 #pragma unroll
-        for (int s = 0; s < SBN; ++s) {
+        for (int s = 0; s < BE; ++s) {
             const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
             bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * 1024u));
         }
-        // 3. wait for this wave's activation loads only (the weight loads issued after them
-        //    stay in flight), or quantize the bf16 rows (fused path)
+        // 5. activations into LDS (int8 as loaded, or quantized here from bfloat16).  Waits
+        //    are per register, so the weight loads stay in flight.
         if (!FQ) {
-            __builtin_amdgcn_s_waitcnt(S::vm_wait());
+#pragma unroll
+            for (int i = 0; i < S::APT; ++i) {
+                const int pc = tid + i * NTHR;
+                const int row = pc / (CS * 8), c = pc - row * (CS * 8);
+                if (row < nrows && c < rowpieces) *reinterpret_cast<uint4*>(smem + row * ROWB + c * 16) = xv[i];
+            }
         } else {
             uint32_t* rowmax = reinterpret_cast<uint32_t*>(sxs + 16);
 #pragma unroll
@@ -461,8 +480,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                 amax = wave_max_u32(amax);
                 if (lane == 0 && row < nrows) atomicMax(rowmax + row, amax);
             }
-            __syncthreads();
-            int8_t* xq_out = const_cast<int8_t*>(a.Xq);
+            lds_barrier();
 #pragma unroll
             for (int i = 0; i < S::XPT; ++i) {
                 __builtin_amdgcn_sched_barrier(0);       // one piece at a time: bounded live range
@@ -483,29 +501,24 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                     }
                 }
                 *reinterpret_cast<uint2*>(smem + row * ROWB + c * 8) = make_uint2(out[0], out[1]);
-                if (rvalid && blockIdx.x == 0)
-                    *reinterpret_cast<uint2*>(xq_out + size_t(rbeg + row) * a.K + c * 8) = make_uint2(out[0], out[1]);
             }
             if (tid < MT) {
                 const bool rvalid = tid < nrows;
                 const RowScale rs = row_scale<false>(rvalid ? rowmax[tid] : 0u);
                 sxs[tid] = rvalid ? rs.s : 0.0f;
-                if (rvalid && blockIdx.x == 0) const_cast<float*>(a.sx)[rbeg + tid] = rs.s;
             }
         }
-        if (FQ) {
-            __syncthreads();
-        } else {
-            // every wave waited for its own LDS-direct loads above (their completion means the
-            // bytes are in LDS); a plain barrier then publishes them without draining the
-            // weight loads still in flight
-            __builtin_amdgcn_s_barrier();
+        lds_barrier();
+#pragma unroll
+        for (int s = BE; s < SBN; ++s) {
+            const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
+            bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * 1024u));
         }
         if (FQ && MODE != MODE_PARTIALS && q == 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sxr[0][i] = sxs[4 * (lane >> 4) + i];
         }
-        // 4. MFMA over this wave's superblocks
+        // 6. MFMA over this wave's superblocks
 #pragma unroll
         for (int s = 0; s < SBN; ++s) {
             const int sb = s0 + s;
@@ -549,7 +562,26 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                 }
             }
         }
-        if (cb + CS < nsb) __syncthreads();              // LDS is rewritten by the next chunk
+        if (cb + CS < nsb) lds_barrier();                // LDS is rewritten by the next chunk
+    };
+    if constexpr (!MULTI) {
+        chunk(0);                                        // the launcher guarantees nsb <= CS
+    } else {
+        for (int cb = 0; cb < nsb; cb += CS) chunk(cb);
+    }
+    if (FQ && blockIdx.x == 0) {
+        // fused path: workgroup x = 0 exports the quantized rows and their scales, after its
+        // last weight load (global stores mixed into the load stream would force full waits)
+        int8_t* xq_out = const_cast<int8_t*>(a.Xq);
+#pragma unroll
+        for (int i = 0; i < S::XPT; ++i) {
+            const int pc = tid + i * NTHR;
+            const int row = pc / (nsb * 16), c = pc - row * (nsb * 16);
+            if (row < nrows)
+                *reinterpret_cast<uint2*>(xq_out + size_t(rbeg + row) * a.K + c * 8) =
+                    *reinterpret_cast<const uint2*>(smem + row * ROWB + c * 8);
+        }
+        if (tid < nrows) const_cast<float*>(a.sx)[rbeg + tid] = sxs[tid];
     }
     if (MODE == MODE_PARTIALS) return;
 
@@ -980,10 +1012,11 @@ static DecodeCfg decode_cfg(int K, int mt) {
     return c;
 }
 
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool FQ = false>
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool FQ = false,
+          bool MULTI = false>
 static void launch_decode_t(const GemmArgs& a, dim3 grid, hipStream_t s) {
     using S = DecodeShape<MS, NT, KW, SBN>;
-    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, FQ>;
+    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, FQ, MULTI>;
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(S::LDS));
     (void)attr;
@@ -993,9 +1026,13 @@ static void launch_decode_t(const GemmArgs& a, dim3 grid, hipStream_t s) {
 template <int MS, int GPS, bool ASYM, int MODE, bool MOE>
 static void launch_decode_shape(const GemmArgs& a, const DecodeCfg& c, dim3 grid, hipStream_t s) {
     if (c.kw == 8) {
-        if constexpr (MS == 1) launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE>(a, grid, s);
+        if constexpr (MS == 1) {
+            if (a.K > 64 * SB_K) launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE, false, true>(a, grid, s);
+            else launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE>(a, grid, s);
+        }
     } else if (c.sbn == 2) launch_decode_t<MS, 4, 4, 2, GPS, ASYM, MODE, MOE>(a, grid, s);
     else if (c.sbn == 4) launch_decode_t<MS, 4, 4, 4, GPS, ASYM, MODE, MOE>(a, grid, s);
+    else if (a.K > 32 * SB_K) launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, false, true>(a, grid, s);
     else launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE>(a, grid, s);
 }
 
@@ -1028,6 +1065,9 @@ static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s)
     if (gps == 1) { if (asym) launch_prefill_t<true, 1, MODE>(a, s); else launch_prefill_t<false, 1, MODE>(a, s); }
     else { if (asym) launch_prefill_t<true, 2, MODE>(a, s); else launch_prefill_t<false, 2, MODE>(a, s); }
 }
+
+// w4a8_linear fuses quantization into the GEMM up to this many activation values.
+constexpr size_t FUSED_MAX_ELEMS = 8192;
 
 // Dense GEMMs with more rows than this use the prefill kernel.
 constexpr int PREFILL_MIN_M = 33;
@@ -1126,7 +1166,11 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
     if (ldx % 8 || !aligned16(X) || !aligned16(Xq) || !aligned16(blob)) return W4A8_EINVAL;
     const Layout L = layout_of(d);
     // fused path: one chunk, the unfused kernel's workgroup layout (same summation order)
-    if (M <= 16 && size_t(M) * L.K <= 32768 && L.K % 512 == 0 && L.K / SB_K <= 32 && decode_cfg(L.K, 16).kw == 4) {
+    // Each workgroup quantizes all M x K activations itself, so the fused kernel pays off
+    // only while that redundant work is small next to the launch it saves.
+    static_assert(FUSED_MAX_ELEMS <= size_t(8) * DecodeShape<1, 4, 4, 8>::XPT * DecodeShape<1, 4, 4, 8>::NTHR,
+                  "fused path: one bfloat16 piece of 8 values per thread");
+    if (size_t(M) * L.K <= FUSED_MAX_ELEMS && L.K % 512 == 0 && L.K / SB_K <= 32 && decode_cfg(L.K, 16).kw == 4) {
         GemmArgs a = make_args(L, Xq, sx, M, blob);
         a.X = static_cast<const uint16_t*>(X);
         a.ldx = ldx;

@@ -188,9 +188,10 @@ def test_gemm_zero_and_nan_rows():
 @pytest.mark.parametrize("M,K,N,g,asym", [(1, 4096, 14336, 128, False), (8, 4096, 14336, 128, False),
                                           (16, 4096, 1024, 128, True), (5, 512, 40, 64, True),
                                           (3, 1024, 33, 128, False), (20, 256, 64, 64, True),
-                                          (2, 7168, 64, 64, True)])
+                                          (2, 7168, 64, 64, True), (2, 4096, 1024, 64, True),
+                                          (4, 2048, 96, 128, False)])
 def test_linear_matches_quant_then_gemm(M, K, N, g, asym):
-    """w4a8_linear (one kernel for M <= 16) equals quant_act followed by gemm bit for bit,
+    """w4a8_linear (one kernel for M * K <= 8192) equals quant_act followed by gemm bit for bit,
     and writes the same activation codes and scales."""
     Xb = W.random_activations(M * 3 + K + N, M, K, outlier_cols=2, outlier_scale=40.0)
     x = W.bf16_values(Xb)
