@@ -190,6 +190,24 @@ def decode_leg(args, L, W, torch, dev):
                 graph=graph is not None)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
+    when there is none or it was taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.txt")
+    src = os.path.join(ROOT, "moe_token_int8_amd", "csrc", "w4a8_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    if rec.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(args, leg, W):
     """The oracle on the same decode step (weights quantized once, outside the timing)."""
     import oracle as O
@@ -343,7 +361,8 @@ def main():
                    "hip_graph": leg["graph"],
                    "parallelism": "single_gpu"},
         "roofline": {"bound": "hbm", "achieved": round(leg["achieved"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(leg["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(leg["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(leg["kernel"]),
                      "kernel": leg["kernel"], "kernel_ms": round(leg["kernel_ms"], 5),
                      "kernel_bytes": leg["kernel_bytes"]},
         "cpu_baseline": cpu,
