@@ -313,27 +313,19 @@ struct DecodeShape {
     static constexpr int CS = KW * SBN;                        // superblocks per chunk
     static constexpr int ROWB = CS * SB_K + 16;                // padded LDS row stride
     static constexpr int APT = (MT * CS * 8 + NTHR - 1) / NTHR;  // 16-byte A pieces / thread
-    static constexpr int XPT = 1;                              // fused quant: bf16 pieces / thread
     static constexpr size_t LDS_A = size_t(MT) * ROWB;
     static constexpr size_t LDS_RED = size_t(KW > 1 ? KW - 1 : 1) * NT * MS * 4 * 64 * 4;
-    static constexpr size_t LDS_SX = 32 * 4;               // row scales + row abs-max (fused)
-    static constexpr size_t LDS = LDS_A + LDS_RED + LDS_SX;
+    static constexpr size_t LDS = LDS_A + LDS_RED;
 };
 
-// FQ (fused quantization; dense, M * K <= 8 * threads, K % 512 == 0, one chunk): the
-// workgroup quantizes its own activation rows from bfloat16 with exactly the per-token rule
-// of quant_act_kernel (row abs-max: wave reductions merged by LDS atomic max), and
-// workgroup x = 0 also writes Xq and sx out.
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool FQ, bool MULTI>
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI>
 __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     using S = DecodeShape<MS, NT, KW, SBN>;
     constexpr int MT = S::MT, NTHR = S::NTHR, CS = S::CS, ROWB = S::ROWB, APT = S::APT;
     // weight superblocks requested before the activation hand-off (the rest right after it)
-    constexpr int BE = FQ ? SBN : (MS == 2 ? (SBN < 2 ? SBN : 2) : (SBN < 4 ? SBN : 4));
-    static_assert(!FQ || (MS == 1 && NT * KW == 16 && !MOE), "fused quantization layout");
+    constexpr int BE = MS == 2 ? (SBN < 2 ? SBN : 2) : (SBN < 4 ? SBN : 4);
     extern __shared__ __align__(16) uint8_t smem[];
     float* red = reinterpret_cast<float*>(smem + S::LDS_A);
-    float* sxs = reinterpret_cast<float*>(smem + S::LDS_A + S::LDS_RED);
     // wave-derived indices are made explicitly uniform so per-slice loops branch on scalars
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = wave % NT, q = wave / NT;
@@ -361,7 +353,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     const uint8_t* zeros = blob + a.zeros_off;
 
     // row scales of the rows this lane stores, fetched before anything else so the
-    // epilogue never waits on a load (fused path: computed below)
+    // epilogue never waits on a load
     float sxr[MS][4];
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms)
@@ -369,7 +361,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i) {
             sxr[ms][i] = 0.0f;
             const int row = rbeg + ms * 16 + 4 * (lane >> 4) + i;
-            if (!FQ && MODE != MODE_PARTIALS && q == 0 && row < rend) {
+            if (MODE != MODE_PARTIALS && q == 0 && row < rend) {
                 const int srow = (MOE && a.gather) ? a.gather[row] / a.topk : row;
                 sxr[ms][i] = a.sx[srow];
             }
@@ -381,10 +373,6 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) accf[ms][i] = 0.0f;
     const v4i zero4 = {0, 0, 0, 0};
-    if (FQ) {
-        if (tid < MT) reinterpret_cast<uint32_t*>(sxs + 16)[tid] = 0u;
-        __syncthreads();
-    }
 
     // one chunk of the K loop.  A K that fits one chunk (MULTI = false) runs it as
     // straight-line code, so no loop-carried state forces conservative load waits.
@@ -395,32 +383,19 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         // pieces and group scales, then a barrier, and only then the weight stream.  The
         // memory pipeline of a compute unit serves requests roughly in order, so the small
         // operands that gate the first MFMA never queue behind another wave's weights.
-        // 1. activation pieces (int8 rows, or bfloat16 rows for the fused path) into registers
-        uint4 xv[FQ ? S::XPT : S::APT];
-        if (!FQ) {
-            // piece p = tid + i * NTHR: row p / (CS * 8), 16 bytes at column p % (CS * 8);
-            // rows past the tile's end are neither loaded nor written (their MFMA outputs are
-            // never stored)
+        // 1. activation pieces into registers: piece p = tid + i * NTHR is row p / (CS * 8),
+        //    16 bytes at column p % (CS * 8); rows past the tile's end are neither loaded nor
+        //    written (their MFMA outputs are never stored)
+        uint4 xv[S::APT];
 #pragma unroll
-            for (int i = 0; i < S::APT; ++i) {
-                const int pc = tid + i * NTHR;
-                const int row = pc / (CS * 8), c = pc - row * (CS * 8);
-                xv[i] = make_uint4(0, 0, 0, 0);
-                if (row < nrows && c < rowpieces) {
-                    int src = rbeg + row;
-                    if (MOE && a.gather) src = a.gather[src] / a.topk;
-                    xv[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(src) * a.K + size_t(cb) * SB_K + c * 16);
-                }
-            }
-        } else {
-            // piece p = tid + i * NTHR of the M x K bf16 block (8 values each); a row holds
-            // K / 8 pieces, a multiple of 64, so the 64 lanes of a wave share one row
-#pragma unroll
-            for (int i = 0; i < S::XPT; ++i) {
-                const int pc = tid + i * NTHR;
-                const int row = pc / (nsb * 16), c = pc - row * (nsb * 16);
-                xv[i] = make_uint4(0, 0, 0, 0);
-                if (row < nrows) xv[i] = *reinterpret_cast<const uint4*>(a.X + size_t(rbeg + row) * a.ldx + c * 8);
+        for (int i = 0; i < S::APT; ++i) {
+            const int pc = tid + i * NTHR;
+            const int row = pc / (CS * 8), c = pc - row * (CS * 8);
+            xv[i] = make_uint4(0, 0, 0, 0);
+            if (row < nrows && c < rowpieces) {
+                int src = rbeg + row;
+                if (MOE && a.gather) src = a.gather[src] / a.topk;
+                xv[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(src) * a.K + size_t(cb) * SB_K + c * 16);
             }
         }
         // 2. this wave's group scales and zero points
@@ -455,68 +430,18 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
             const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
             bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * 1024u));
         }
-        // 5. activations into LDS (int8 as loaded, or quantized here from bfloat16).  Waits
-        //    are per register, so the weight loads stay in flight.
-        if (!FQ) {
+        // 5. activations into LDS.  Waits are per register, so the weight loads stay in flight.
 #pragma unroll
-            for (int i = 0; i < S::APT; ++i) {
-                const int pc = tid + i * NTHR;
-                const int row = pc / (CS * 8), c = pc - row * (CS * 8);
-                if (row < nrows && c < rowpieces) *reinterpret_cast<uint4*>(smem + row * ROWB + c * 16) = xv[i];
-            }
-        } else {
-            uint32_t* rowmax = reinterpret_cast<uint32_t*>(sxs + 16);
-#pragma unroll
-            for (int i = 0; i < S::XPT; ++i) {
-                const int pc = tid + i * NTHR;
-                const int row = pc / (nsb * 16);
-                uint32_t amax = 0;
-                const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    amax = max(amax, (w[j] & 0x7fffu) << 16);
-                    amax = max(amax, w[j] & 0x7fff0000u);
-                }
-                amax = wave_max_u32(amax);
-                if (lane == 0 && row < nrows) atomicMax(rowmax + row, amax);
-            }
-            lds_barrier();
-#pragma unroll
-            for (int i = 0; i < S::XPT; ++i) {
-                __builtin_amdgcn_sched_barrier(0);       // one piece at a time: bounded live range
-                const int pc = tid + i * NTHR;
-                const int row = pc / (nsb * 16), c = pc - row * (nsb * 16);
-                if (row >= MT) continue;
-                const bool rvalid = row < nrows;
-                const RowScale rs = row_scale(rvalid ? rowmax[row] : 0u);
-                const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-                uint32_t out[2] = {0, 0};
-                if (rvalid && rs.finite) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int q0 = quant_one(bf16_to_f32(w[j] & 0xffffu), rs.d, rs.inv, rs.fast);
-                        const int q1 = quant_one(bf16_to_f32(w[j] >> 16), rs.d, rs.inv, rs.fast);
-                        const uint32_t pair = (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8);
-                        out[j >> 1] |= pair << ((j & 1) * 16);
-                    }
-                }
-                *reinterpret_cast<uint2*>(smem + row * ROWB + c * 8) = make_uint2(out[0], out[1]);
-            }
-            if (tid < MT) {
-                const bool rvalid = tid < nrows;
-                const RowScale rs = row_scale<false>(rvalid ? rowmax[tid] : 0u);
-                sxs[tid] = rvalid ? rs.s : 0.0f;
-            }
+        for (int i = 0; i < S::APT; ++i) {
+            const int pc = tid + i * NTHR;
+            const int row = pc / (CS * 8), c = pc - row * (CS * 8);
+            if (row < nrows && c < rowpieces) *reinterpret_cast<uint4*>(smem + row * ROWB + c * 16) = xv[i];
         }
         lds_barrier();
 #pragma unroll
         for (int s = BE; s < SBN; ++s) {
             const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
             bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * 1024u));
-        }
-        if (FQ && MODE != MODE_PARTIALS && q == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sxr[0][i] = sxs[4 * (lane >> 4) + i];
         }
         // 6. MFMA over this wave's superblocks
 #pragma unroll
@@ -569,20 +494,6 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     } else {
         for (int cb = 0; cb < nsb; cb += CS) chunk(cb);
     }
-    if (FQ && blockIdx.x == 0) {
-        // fused path: workgroup x = 0 exports the quantized rows and their scales, after its
-        // last weight load (global stores mixed into the load stream would force full waits)
-        int8_t* xq_out = const_cast<int8_t*>(a.Xq);
-#pragma unroll
-        for (int i = 0; i < S::XPT; ++i) {
-            const int pc = tid + i * NTHR;
-            const int row = pc / (nsb * 16), c = pc - row * (nsb * 16);
-            if (row < nrows)
-                *reinterpret_cast<uint2*>(xq_out + size_t(rbeg + row) * a.K + c * 8) =
-                    *reinterpret_cast<const uint2*>(smem + row * ROWB + c * 8);
-        }
-        if (tid < nrows) const_cast<float*>(a.sx)[rbeg + tid] = sxs[tid];
-    }
     if (MODE == MODE_PARTIALS) return;
 
     // slice-ordered reduction through its own LDS region, row scale, store
@@ -618,6 +529,262 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
             else
                 reinterpret_cast<uint16_t*>(a.Y)[size_t(row) * a.ldy + col] = (uint16_t)f32_to_bf16_rne(y);
         }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// W4A8 GEMM, K-slice decode variant (M <= 32): activations straight into registers
+//
+// A workgroup covers T column tiles (16 columns each) over all of K.  Wave w owns the
+// K-slice of superblocks [w * SW, w * SW + SW): it loads its activation fragments once
+// into registers (no LDS staging, no barrier before the first MFMA) and reuses them for
+// all T tiles, then streams the T x SW weight superblocks of that slice.  Each tile's
+// float32 partial goes to LDS as soon as the tile is done; after one barrier every
+// thread sums the KW slice partials of its outputs in slice order (fixed, so the result
+// does not depend on timing), applies the row scale and stores.
+//
+// Per workgroup: weights T * SW * KW KiB from HBM, activations MT x K from L2, LDS
+// traffic only for the slice reduction (2 * KW * T * 64 * 4 * MS floats).
+// ------------------------------------------------------------------------------------
+template <int MS, int T>
+struct KsliceShape {
+    static constexpr int MT = 16 * MS;
+    static constexpr int NV = 4 * MS;                          // accumulators per lane per tile
+    // slice partials, then 32 row scales and 32 row abs-maxima; the fused path adds its
+    // quantized rows [rows][K + 16] after that
+    static constexpr size_t lds(int kw) { return size_t(kw) * T * 64 * NV * 4 + 64 * 4; }
+};
+
+template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ>
+__global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
+    using S = KsliceShape<MS, T>;
+    static_assert(!FQ || (MS == 1 && !MOE && MODE == MODE_OUT), "fused quantization: dense 16-row tiles");
+    constexpr int NV = S::NV;
+    extern __shared__ __align__(16) uint8_t smem[];
+    float* red = reinterpret_cast<float*>(smem);              // [KW][T][64][NV]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int KW = blockDim.x >> 6;
+    const int ntiles = (a.N + 15) / 16;
+    const int tile0 = blockIdx.x * T;
+    const int nsb = a.K / SB_K;
+    const int sb0 = w * SW;
+
+    int rbeg, rend;
+    const uint8_t* blob = a.blob;
+    if (!MOE) {
+        rbeg = blockIdx.y * S::MT;
+        rend = min(a.M, rbeg + S::MT);
+    } else {
+        const TileRows tr = moe_tile<S::MT>(a, blockIdx.y, lane);
+        if (tr.expert < 0) return;                       // uniform over the workgroup
+        rbeg = tr.rbeg;
+        rend = tr.rend;
+        blob = a.blob + size_t(tr.expert) * a.expert_stride;
+    }
+    const int nrows = rend - rbeg;
+    const uint8_t* codes = blob + a.codes_off;
+    const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
+    const uint8_t* zeros = blob + a.zeros_off;
+
+    // row scales of the tile's rows: fetched first, parked in LDS after the MFMAs
+    float* sxs = red + size_t(KW) * T * 64 * NV;
+    float sxv = 0.0f;
+    if (!FQ && MODE != MODE_PARTIALS && tid < S::MT && tid < nrows)
+        sxv = a.sx[(MOE && a.gather) ? a.gather[rbeg + tid] / a.topk : rbeg + tid];
+
+    // fused path: LDS also holds the row abs-maxima and the quantized rows [nrows][K + 16]
+    uint32_t* rowmax = reinterpret_cast<uint32_t*>(sxs + 32);
+    int8_t* xst = reinterpret_cast<int8_t*>(sxs + 64);
+    const int xstride = a.K + 16;
+    uint4 xv = make_uint4(0, 0, 0, 0);                       // fused: one bf16 piece (8 values)
+    const int xpieces = a.K / 8;                             // pieces per row
+    if (FQ) {
+        if (tid < S::MT) rowmax[tid] = 0u;
+        if (tid < nrows * xpieces) {
+            const int row = tid / xpieces, c = tid - row * xpieces;
+            xv = *reinterpret_cast<const uint4*>(a.X + size_t(rbeg + row) * a.ldx + c * 8);
+        }
+    }
+
+    // 1. activation fragments of this wave's K-slice: lane l holds row ms * 16 + l % 16 and
+    //    the 16 K-values [16 * (l / 16), +16) of each 64-deep half (the MFMA A operand)
+    v4i A[SW][2][MS];
+#pragma unroll
+    for (int ms = 0; ms < MS && !FQ; ++ms) {
+        const int row = ms * 16 + (lane & 15);
+        const bool rv = row < nrows;
+        const int8_t* xrow = a.Xq;
+        if (rv) {
+            const int src = (MOE && a.gather) ? a.gather[rbeg + row] / a.topk : rbeg + row;
+            xrow = a.Xq + size_t(src) * a.K;
+        }
+#pragma unroll
+        for (int s = 0; s < SW; ++s)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                A[s][h][ms] = v4i{0, 0, 0, 0};
+                if (rv && sb0 + s < nsb)
+                    A[s][h][ms] = *reinterpret_cast<const v4i*>(xrow + (sb0 + s) * SB_K + h * 64 + 16 * (lane >> 4));
+            }
+    }
+    // 2. group scales and zero points of the T tiles x SW superblocks
+    float sc[T][SW][GPS];
+    uint32_t zq[T][SW][GPS];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const uint32_t tc = uint32_t(min(tile0 + t, ntiles - 1));
+#pragma unroll
+        for (int s = 0; s < SW; ++s) {
+            const uint32_t sb = uint32_t(min(sb0 + s, nsb - 1));
+#pragma unroll
+            for (int gi = 0; gi < GPS; ++gi) {
+                const uint32_t mi = (tc * uint32_t(a.G) + sb * GPS + gi) * 16u + uint32_t(lane & 15);
+                sc[t][s][gi] = scales[mi];
+                if (ASYM) zq[t][s][gi] = zeros[mi];
+            }
+        }
+    }
+    // issue fence: the small requests of every wave go out before any weight request
+    // (it also publishes the fused path's cleared row maxima)
+    lds_barrier();
+    // 3. weight superblocks, in the order they are consumed (tile-major)
+    uint4 bq[T][SW];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const uint32_t tc = uint32_t(min(tile0 + t, ntiles - 1));
+#pragma unroll
+        for (int s = 0; s < SW; ++s) {
+            const uint32_t sb = uint32_t(min(sb0 + s, nsb - 1));
+            bq[t][s] = *reinterpret_cast<const uint4*>(codes + ((tc * uint32_t(nsb) + sb) * 1024u + uint32_t(lane) * 16u));
+        }
+    }
+    asm volatile("" ::: "memory");                      // keep the whole stream issued here
+    if (FQ) {
+        // per-token quantization of the rows, exactly as quant_act_kernel: a wave's 64
+        // pieces lie in one row (K % 512 == 0), so a wave max and one LDS atomic per wave
+        // give the row abs-max
+        const int row = tid / xpieces, c = tid - row * xpieces;
+        const bool pv = tid < nrows * xpieces;
+        const uint32_t wv[4] = {xv.x, xv.y, xv.z, xv.w};
+        uint32_t amax = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            amax = max(amax, (wv[j] & 0x7fffu) << 16);
+            amax = max(amax, wv[j] & 0x7fff0000u);
+        }
+        amax = wave_max_u32(amax);
+        if (lane == 0 && pv) atomicMax(rowmax + row, amax);
+        lds_barrier();
+        if (pv) {
+            const RowScale rs = row_scale(rowmax[row]);
+            uint32_t out[2] = {0, 0};
+            if (rs.finite) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int q0 = quant_one(bf16_to_f32(wv[j] & 0xffffu), rs.d, rs.inv, rs.fast);
+                    const int q1 = quant_one(bf16_to_f32(wv[j] >> 16), rs.d, rs.inv, rs.fast);
+                    const uint32_t pair = (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8);
+                    out[j >> 1] |= pair << ((j & 1) * 16);
+                }
+            }
+            *reinterpret_cast<uint2*>(xst + row * xstride + c * 8) = make_uint2(out[0], out[1]);
+        }
+        if (tid < nrows) sxv = row_scale<false>(rowmax[tid]).s;
+        lds_barrier();
+        const int row16 = lane & 15;
+#pragma unroll
+        for (int s = 0; s < SW; ++s)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                A[s][h][0] = v4i{0, 0, 0, 0};
+                if (row16 < nrows && sb0 + s < nsb)
+                    A[s][h][0] = *reinterpret_cast<const v4i*>(xst + row16 * xstride + (sb0 + s) * SB_K + h * 64 +
+                                                               16 * (lane >> 4));
+            }
+    }
+    // 4. per tile: MFMAs over the slice, per-group epilogue, partial to LDS
+    const v4i zero4 = {0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        float accf[MS][4];
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accf[ms][i] = 0.0f;
+        const int tile = tile0 + t;
+#pragma unroll
+        for (int s = 0; s < SW; ++s) {
+            if (sb0 + s >= nsb) break;
+            v4i acc[MS];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int gi = (GPS == 2) ? h : 0;
+                const uint32_t w0 = h ? bq[t][s].z : bq[t][s].x;
+                const uint32_t w1 = h ? bq[t][s].w : bq[t][s].y;
+                const uint32_t zc = ASYM ? (128u - zq[t][s][gi]) * 0x01010101u : 0u;
+                const v4i b = unpack_b<ASYM>(w0, w1, zc);
+                const bool first = (GPS == 2) || h == 0;
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+                    acc[ms] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[s][h][ms], b, first ? zero4 : acc[ms], 0, 0, 0);
+                if (GPS == 2 || h == 1) {
+                    if (MODE == MODE_PARTIALS) {
+                        const int col = tile * 16 + (lane & 15);
+#pragma unroll
+                        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int row = ms * 16 + 4 * (lane >> 4) + i;
+                                if (tile < ntiles && row < nrows && col < a.N) {
+                                    const int v = ASYM ? acc[ms][i] : (acc[ms][i] >> 4);
+                                    a.P[(size_t(rbeg + row) * a.N + col) * a.G + size_t(sb0 + s) * GPS + gi] = v;
+                                }
+                            }
+                    } else {
+                        const float scl = ASYM ? sc[t][s][gi] : sc[t][s][gi] * 0.0625f;
+#pragma unroll
+                        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) accf[ms][i] = fmaf((float)acc[ms][i], scl, accf[ms][i]);
+                    }
+                }
+            }
+        }
+        if (MODE != MODE_PARTIALS) {
+            float4* dst = reinterpret_cast<float4*>(red + ((size_t(w) * T + t) * 64 + lane) * NV);
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms) dst[ms] = make_float4(accf[ms][0], accf[ms][1], accf[ms][2], accf[ms][3]);
+        }
+    }
+    if (MODE == MODE_PARTIALS) return;
+    if (tid < S::MT) sxs[tid] = sxv;
+    __syncthreads();
+    // 5. slice-ordered sum, row scale, store.  Output o = (t * 64 + l) * NV + j holds
+    //    C[row = (j / 4) * 16 + 4 * (l / 16) + j % 4][col = 16 * t + l % 16] of the tile grid.
+    for (int o = tid; o < T * 64 * NV; o += int(blockDim.x)) {
+        const int j = o % NV, lo = (o / NV) % 64, t = o / (NV * 64);
+        const int row = (j >> 2) * 16 + 4 * (lo >> 4) + (j & 3);
+        const int col = (tile0 + t) * 16 + (lo & 15);
+        if (row >= nrows || tile0 + t >= ntiles || col >= a.N) continue;
+        float y = red[o];
+        for (int k = 1; k < KW; ++k) y += red[size_t(k) * T * 64 * NV + o];
+        y *= sxs[row];
+        const size_t yi = size_t(rbeg + row) * a.ldy + col;
+        if (a.out_f32)
+            reinterpret_cast<float*>(a.Y)[yi] = y;
+        else
+            reinterpret_cast<uint16_t*>(a.Y)[yi] = (uint16_t)f32_to_bf16_rne(y);
+    }
+    if (FQ && blockIdx.x == 0) {
+        // fused path: workgroup 0 exports the activation codes and scales (after all of its
+        // weight loads, so no store sits inside the load stream)
+        if (tid < nrows * xpieces) {
+            const int row = tid / xpieces, c = tid - row * xpieces;
+            *reinterpret_cast<uint2*>(const_cast<int8_t*>(a.Xq) + size_t(rbeg + row) * a.K + c * 8) =
+                *reinterpret_cast<const uint2*>(xst + row * xstride + c * 8);
+        }
+        if (tid < nrows) const_cast<float*>(a.sx)[rbeg + tid] = sxs[tid];
     }
 }
 
@@ -1012,11 +1179,10 @@ static DecodeCfg decode_cfg(int K, int mt) {
     return c;
 }
 
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool FQ = false,
-          bool MULTI = false>
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI = false>
 static void launch_decode_t(const GemmArgs& a, dim3 grid, hipStream_t s) {
     using S = DecodeShape<MS, NT, KW, SBN>;
-    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, FQ, MULTI>;
+    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, MULTI>;
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(S::LDS));
     (void)attr;
@@ -1027,12 +1193,12 @@ template <int MS, int GPS, bool ASYM, int MODE, bool MOE>
 static void launch_decode_shape(const GemmArgs& a, const DecodeCfg& c, dim3 grid, hipStream_t s) {
     if (c.kw == 8) {
         if constexpr (MS == 1) {
-            if (a.K > 64 * SB_K) launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE, false, true>(a, grid, s);
+            if (a.K > 64 * SB_K) launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE, true>(a, grid, s);
             else launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE>(a, grid, s);
         }
     } else if (c.sbn == 2) launch_decode_t<MS, 4, 4, 2, GPS, ASYM, MODE, MOE>(a, grid, s);
     else if (c.sbn == 4) launch_decode_t<MS, 4, 4, 4, GPS, ASYM, MODE, MOE>(a, grid, s);
-    else if (a.K > 32 * SB_K) launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, false, true>(a, grid, s);
+    else if (a.K > 32 * SB_K) launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, true>(a, grid, s);
     else launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE>(a, grid, s);
 }
 
@@ -1047,6 +1213,74 @@ static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool a
         else { if (asym) W4A8_DEC(2, 2, true); else W4A8_DEC(2, 2, false); }
     }
 #undef W4A8_DEC
+}
+
+// w4a8_linear fuses quantization into the GEMM up to this many activation values.
+constexpr size_t FUSED_MAX_ELEMS = 8192;
+
+// K-slice decode kernel: T tiles per workgroup, SW superblocks per wave, KW waves.
+struct KsliceCfg {
+    int t, sw, kw;
+};
+
+static bool kslice_cfg(int K, int mt, KsliceCfg* c) {
+    const int nsb = K / SB_K;
+    if (nsb <= 16) {
+        c->t = 4;
+        c->sw = 1;
+    } else if (nsb <= 32) {
+        c->t = 4;
+        c->sw = 2;
+    } else if (nsb <= 64 && mt == 16) {   // 32-row tiles at this depth would not fit in registers
+        c->t = 2;
+        c->sw = 4;
+    } else {
+        return false;
+    }
+    c->kw = (nsb + c->sw - 1) / c->sw;
+    return true;
+}
+
+// Dense GEMMs use the K-slice kernel exactly where w4a8_linear can fuse the quantization
+// (so fused and unfused results are bit-identical); above that size the chunked kernel,
+// whose activation tile is staged once per workgroup, streams faster.
+static bool dense_kslice(int M, int K, KsliceCfg* c) {
+    return size_t(M) * K <= FUSED_MAX_ELEMS && kslice_cfg(K, 16, c);
+}
+
+template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ = false>
+static void launch_kslice_t(const GemmArgs& a, int kw, int ytiles, hipStream_t s) {
+    using S = KsliceShape<MS, T>;
+    auto kern = gemm_kslice_kernel<MS, T, SW, GPS, ASYM, MODE, MOE, FQ>;
+    constexpr size_t fq_max = FQ ? FUSED_MAX_ELEMS + 16 * 16 : 0;   // quantized rows, padded
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       int(S::lds(16) + fq_max));
+    (void)attr;
+    const int ntiles = (a.N + 15) / 16;
+    const size_t lds = S::lds(kw) + (FQ ? size_t(a.M) * (a.K + 16) : 0);
+    kern<<<dim3((ntiles + T - 1) / T, ytiles), dim3(64 * kw), lds, s>>>(a);
+}
+
+template <int MS, int GPS, bool ASYM, int MODE, bool MOE>
+static void launch_kslice_shape(const GemmArgs& a, const KsliceCfg& c, int ytiles, hipStream_t s) {
+    if (c.sw == 1) launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+    else if (c.sw == 2) launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+    else if constexpr (MS == 1) launch_kslice_t<MS, 2, 4, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+}
+
+template <int MODE, bool MOE>
+static void launch_kslice(const GemmArgs& a, const KsliceCfg& c, int ms, int gps, bool asym, int ytiles,
+                          hipStream_t s) {
+#define W4A8_KS(MS_, GPS_, ASYM_) launch_kslice_shape<MS_, GPS_, ASYM_, MODE, MOE>(a, c, ytiles, s)
+    if (ms == 1) {
+        if (gps == 1) { if (asym) W4A8_KS(1, 1, true); else W4A8_KS(1, 1, false); }
+        else { if (asym) W4A8_KS(1, 2, true); else W4A8_KS(1, 2, false); }
+    } else {
+        if (gps == 1) { if (asym) W4A8_KS(2, 1, true); else W4A8_KS(2, 1, false); }
+        else { if (asym) W4A8_KS(2, 2, true); else W4A8_KS(2, 2, false); }
+    }
+#undef W4A8_KS
 }
 
 template <bool ASYM, int GPS, int MODE>
@@ -1065,9 +1299,6 @@ static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s)
     if (gps == 1) { if (asym) launch_prefill_t<true, 1, MODE>(a, s); else launch_prefill_t<false, 1, MODE>(a, s); }
     else { if (asym) launch_prefill_t<true, 2, MODE>(a, s); else launch_prefill_t<false, 2, MODE>(a, s); }
 }
-
-// w4a8_linear fuses quantization into the GEMM up to this many activation values.
-constexpr size_t FUSED_MAX_ELEMS = 8192;
 
 // Dense GEMMs with more rows than this use the prefill kernel.
 constexpr int PREFILL_MIN_M = 33;
@@ -1150,6 +1381,12 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
         return launch_status();
     }
     const int mt = dense_mt(M);
+    KsliceCfg kc;
+    if (dense_kslice(M, L.K, &kc)) {
+        launch_kslice<MODE_OUT, false>(a, kc, mt / 16, SB_K / d->group_size, d->asymmetric, (M + mt - 1) / mt,
+                                       static_cast<hipStream_t>(stream));
+        return launch_status();
+    }
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
     launch_decode<MODE_OUT, false>(a, c, SB_K / d->group_size, d->asymmetric, grid, static_cast<hipStream_t>(stream));
@@ -1165,34 +1402,27 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
     if (!X || !blob || !Y || !Xq || !sx || ldy < d->N || ldx < K) return W4A8_EINVAL;
     if (ldx % 8 || !aligned16(X) || !aligned16(Xq) || !aligned16(blob)) return W4A8_EINVAL;
     const Layout L = layout_of(d);
-    // fused path: one chunk, the unfused kernel's workgroup layout (same summation order)
-    // Each workgroup quantizes all M x K activations itself, so the fused kernel pays off
-    // only while that redundant work is small next to the launch it saves.
-    static_assert(FUSED_MAX_ELEMS <= size_t(8) * DecodeShape<1, 4, 4, 8>::XPT * DecodeShape<1, 4, 4, 8>::NTHR,
-                  "fused path: one bfloat16 piece of 8 values per thread");
-    if (size_t(M) * L.K <= FUSED_MAX_ELEMS && L.K % 512 == 0 && L.K / SB_K <= 32 && decode_cfg(L.K, 16).kw == 4) {
+    // Fused path: the unfused K-slice kernel's workgroup layout and summation order, so the
+    // result is bit-identical.  Each workgroup quantizes all M x K activations itself, so
+    // fusing pays off only while that redundant work is small next to the launch it saves.
+    KsliceCfg kc;
+    if (L.K % 512 == 0 && dense_kslice(M, L.K, &kc) && M * (L.K / 8) <= 64 * kc.kw) {
         GemmArgs a = make_args(L, Xq, sx, M, blob);
         a.X = static_cast<const uint16_t*>(X);
         a.ldx = ldx;
         a.Y = Y;
         a.ldy = ldy;
         a.out_f32 = out_dtype == W4A8_OUT_F32;
-        const DecodeCfg c = decode_cfg(L.K, 16);       // same layout as the unfused kernel
-        const dim3 grid = decode_grid(L, c, 1);
         hipStream_t s = static_cast<hipStream_t>(stream);
         const int gps = SB_K / d->group_size;
         const bool asym = d->asymmetric;
-#define W4A8_FQ(SBN_, GPS_, ASYM_) launch_decode_t<1, 4, 4, SBN_, GPS_, ASYM_, MODE_OUT, false, true>(a, grid, s)
-        if (c.sbn == 2) {
-            if (gps == 1) { if (asym) W4A8_FQ(2, 1, true); else W4A8_FQ(2, 1, false); }
-            else { if (asym) W4A8_FQ(2, 2, true); else W4A8_FQ(2, 2, false); }
-        } else if (c.sbn == 4) {
-            if (gps == 1) { if (asym) W4A8_FQ(4, 1, true); else W4A8_FQ(4, 1, false); }
-            else { if (asym) W4A8_FQ(4, 2, true); else W4A8_FQ(4, 2, false); }
-        } else {
-            if (gps == 1) { if (asym) W4A8_FQ(8, 1, true); else W4A8_FQ(8, 1, false); }
-            else { if (asym) W4A8_FQ(8, 2, true); else W4A8_FQ(8, 2, false); }
-        }
+#define W4A8_FQ(T_, SW_, GPS_, ASYM_) launch_kslice_t<1, T_, SW_, GPS_, ASYM_, MODE_OUT, false, true>(a, kc.kw, 1, s)
+#define W4A8_FQS(T_, SW_) do { if (gps == 1) { if (asym) W4A8_FQ(T_, SW_, 1, true); else W4A8_FQ(T_, SW_, 1, false); } \
+                               else { if (asym) W4A8_FQ(T_, SW_, 2, true); else W4A8_FQ(T_, SW_, 2, false); } } while (0)
+        if (kc.sw == 1) W4A8_FQS(4, 1);
+        else if (kc.sw == 2) W4A8_FQS(4, 2);
+        else W4A8_FQS(2, 4);
+#undef W4A8_FQS
 #undef W4A8_FQ
         return launch_status();
     }
@@ -1215,6 +1445,12 @@ int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob, const w4a8_wde
         return launch_status();
     }
     const int mt = dense_mt(M);
+    KsliceCfg kc;
+    if (dense_kslice(M, L.K, &kc)) {
+        launch_kslice<MODE_PARTIALS, false>(a, kc, mt / 16, SB_K / d->group_size, d->asymmetric, (M + mt - 1) / mt,
+                                            static_cast<hipStream_t>(stream));
+        return launch_status();
+    }
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
     launch_decode<MODE_PARTIALS, false>(a, c, SB_K / d->group_size, d->asymmetric, grid,
@@ -1254,6 +1490,11 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
     a.E = E;
     a.expert_stride = stride;
     const int slots = rows / mt + std::min(E, rows) + 1;
+    KsliceCfg kc;
+    if (kslice_cfg(L.K, mt, &kc)) {
+        launch_kslice<MODE_OUT, true>(a, kc, mt / 16, SB_K / d->group_size, d->asymmetric, slots, s);
+        return launch_status();
+    }
     const DecodeCfg c = decode_cfg(L.K, mt);
     launch_decode<MODE_OUT, true>(a, c, SB_K / d->group_size, d->asymmetric, decode_grid(L, c, slots), s);
     return launch_status();
@@ -1377,11 +1618,16 @@ const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
     if (M >= PREFILL_MIN_M)
         return asym ? (g64 ? "w4a8_prefill_asym_g64" : "w4a8_prefill_asym_g128")
                     : (g64 ? "w4a8_prefill_sym_g64" : "w4a8_prefill_sym_g128");
-    if (dense_mt(M) == 16)
-        return asym ? (g64 ? "w4a8_decode_m16_asym_g64" : "w4a8_decode_m16_asym_g128")
-                    : (g64 ? "w4a8_decode_m16_sym_g64" : "w4a8_decode_m16_sym_g128");
-    return asym ? (g64 ? "w4a8_decode_m32_asym_g64" : "w4a8_decode_m32_asym_g128")
-                : (g64 ? "w4a8_decode_m32_sym_g64" : "w4a8_decode_m32_sym_g128");
+    // one name per (kernel family, row tile, format)
+    static const char* const names[2][2][2][2] = {
+        {{{"w4a8_decode_m16_sym_g128", "w4a8_decode_m16_sym_g64"}, {"w4a8_decode_m16_asym_g128", "w4a8_decode_m16_asym_g64"}},
+         {{"w4a8_decode_m32_sym_g128", "w4a8_decode_m32_sym_g64"}, {"w4a8_decode_m32_asym_g128", "w4a8_decode_m32_asym_g64"}}},
+        {{{"w4a8_kslice_m16_sym_g128", "w4a8_kslice_m16_sym_g64"}, {"w4a8_kslice_m16_asym_g128", "w4a8_kslice_m16_asym_g64"}},
+         {{"w4a8_kslice_m32_sym_g128", "w4a8_kslice_m32_sym_g64"}, {"w4a8_kslice_m32_asym_g128", "w4a8_kslice_m32_asym_g64"}}}};
+    const int mt = dense_mt(M);
+    KsliceCfg kc;
+    const int fam = dense_kslice(M, d->K, &kc) ? 1 : 0;
+    return names[fam][mt == 32][asym][g64];
 }
 
 }  // extern "C"
