@@ -546,6 +546,13 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 // Per workgroup: weights T * SW * KW KiB from HBM, activations MT x K from L2, LDS
 // traffic only for the slice reduction (2 * KW * T * 64 * 4 * MS floats).
 // ------------------------------------------------------------------------------------
+// w4a8_linear fuses quantization into the GEMM up to this many activation values, held as
+// up to FQ_PIECES bfloat16 pieces of 8 values per thread.  Every workgroup quantizes all of
+// them, and that redundant work outgrows the launch it saves quickly (measured on the
+// 4096 x 14336 projection: fused beats quantize-then-GEMM at M = 1, loses at M = 8).
+constexpr size_t FUSED_MAX_ELEMS = 8192;
+constexpr int FQ_PIECES = 1;
+
 template <int MS, int T>
 struct KsliceShape {
     static constexpr int MT = 16 * MS;
@@ -597,13 +604,20 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     uint32_t* rowmax = reinterpret_cast<uint32_t*>(sxs + 32);
     int8_t* xst = reinterpret_cast<int8_t*>(sxs + 64);
     const int xstride = a.K + 16;
-    uint4 xv = make_uint4(0, 0, 0, 0);                       // fused: one bf16 piece (8 values)
-    const int xpieces = a.K / 8;                             // pieces per row
+    // fused: piece p = tid + i * blockDim (8 bf16 values); a row holds K / 8 pieces, a
+    // multiple of 64, so each wave's 64 pieces of one iteration lie in one row
+    uint4 xv[FQ ? FQ_PIECES : 1];
+    const int xpieces = a.K / 8;
     if (FQ) {
         if (tid < S::MT) rowmax[tid] = 0u;
-        if (tid < nrows * xpieces) {
-            const int row = tid / xpieces, c = tid - row * xpieces;
-            xv = *reinterpret_cast<const uint4*>(a.X + size_t(rbeg + row) * a.ldx + c * 8);
+#pragma unroll
+        for (int i = 0; i < FQ_PIECES; ++i) {
+            const int pc = tid + i * int(blockDim.x);
+            xv[i] = make_uint4(0, 0, 0, 0);
+            if (pc < nrows * xpieces) {
+                const int row = pc / xpieces, c = pc - row * xpieces;
+                xv[i] = *reinterpret_cast<const uint4*>(a.X + size_t(rbeg + row) * a.ldx + c * 8);
+            }
         }
     }
 
@@ -661,22 +675,29 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     }
     asm volatile("" ::: "memory");                      // keep the whole stream issued here
     if (FQ) {
-        // per-token quantization of the rows, exactly as quant_act_kernel: a wave's 64
-        // pieces lie in one row (K % 512 == 0), so a wave max and one LDS atomic per wave
-        // give the row abs-max
-        const int row = tid / xpieces, c = tid - row * xpieces;
-        const bool pv = tid < nrows * xpieces;
-        const uint32_t wv[4] = {xv.x, xv.y, xv.z, xv.w};
-        uint32_t amax = 0;
+        // per-token quantization of the rows, exactly as quant_act_kernel: a wave max and
+        // one LDS atomic per wave and piece give the row abs-max
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            amax = max(amax, (wv[j] & 0x7fffu) << 16);
-            amax = max(amax, wv[j] & 0x7fff0000u);
+        for (int i = 0; i < FQ_PIECES; ++i) {
+            const int pc = tid + i * int(blockDim.x);
+            const uint32_t wv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+            uint32_t amax = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                amax = max(amax, (wv[j] & 0x7fffu) << 16);
+                amax = max(amax, wv[j] & 0x7fff0000u);
+            }
+            amax = wave_max_u32(amax);
+            if (lane == 0 && pc < nrows * xpieces) atomicMax(rowmax + pc / xpieces, amax);
         }
-        amax = wave_max_u32(amax);
-        if (lane == 0 && pv) atomicMax(rowmax + row, amax);
         lds_barrier();
-        if (pv) {
+#pragma unroll
+        for (int i = 0; i < FQ_PIECES; ++i) {
+            __builtin_amdgcn_sched_barrier(0);           // one piece at a time: bounded live range
+            const int pc = tid + i * int(blockDim.x);
+            if (pc >= nrows * xpieces) continue;
+            const int row = pc / xpieces, c = pc - row * xpieces;
+            const uint32_t wv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
             const RowScale rs = row_scale(rowmax[row]);
             uint32_t out[2] = {0, 0};
             if (rs.finite) {
@@ -779,8 +800,8 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     if (FQ && blockIdx.x == 0) {
         // fused path: workgroup 0 exports the activation codes and scales (after all of its
         // weight loads, so no store sits inside the load stream)
-        if (tid < nrows * xpieces) {
-            const int row = tid / xpieces, c = tid - row * xpieces;
+        for (int pc = tid; pc < nrows * xpieces; pc += int(blockDim.x)) {
+            const int row = pc / xpieces, c = pc - row * xpieces;
             *reinterpret_cast<uint2*>(const_cast<int8_t*>(a.Xq) + size_t(rbeg + row) * a.K + c * 8) =
                 *reinterpret_cast<const uint2*>(xst + row * xstride + c * 8);
         }
@@ -1215,8 +1236,6 @@ static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool a
 #undef W4A8_DEC
 }
 
-// w4a8_linear fuses quantization into the GEMM up to this many activation values.
-constexpr size_t FUSED_MAX_ELEMS = 8192;
 
 // K-slice decode kernel: T tiles per workgroup, SW superblocks per wave, KW waves.
 struct KsliceCfg {
@@ -1406,7 +1425,7 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
     // result is bit-identical.  Each workgroup quantizes all M x K activations itself, so
     // fusing pays off only while that redundant work is small next to the launch it saves.
     KsliceCfg kc;
-    if (L.K % 512 == 0 && dense_kslice(M, L.K, &kc) && M * (L.K / 8) <= 64 * kc.kw) {
+    if (L.K % 512 == 0 && dense_kslice(M, L.K, &kc) && M * (L.K / 8) <= FQ_PIECES * 64 * kc.kw) {
         GemmArgs a = make_args(L, Xq, sx, M, blob);
         a.X = static_cast<const uint16_t*>(X);
         a.ldx = ldx;
