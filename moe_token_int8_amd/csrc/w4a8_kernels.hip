@@ -244,6 +244,7 @@ struct GemmArgs {
     int topk;
     const int32_t* offsets;   // MoE: expert row offsets [E+1]
     int E;
+    int moe_lo, moe_hi;       // MoE: this launch serves the experts with moe_lo <= rows < moe_hi
 };
 
 // Unpack two packed words (16 codes of one column) into one MFMA B operand.
@@ -272,9 +273,10 @@ struct TileRows {
     int rbeg, rend, expert;
 };
 
-// MoE: the slot-th MT-row tile over experts in expert order (each expert's rows split into
-// ceil(rows_e / MT) tiles).  Every wave evaluates this identically, so the workgroup agrees
-// without a barrier.  expert = -1 when the slot is past the last tile.
+// MoE: the slot-th MT-row tile over the experts served by this launch (row count in
+// [moe_lo, moe_hi)), in expert order, each expert's rows split into ceil(rows_e / MT) tiles.
+// Every wave evaluates this identically, so the workgroup agrees without a barrier.
+// expert = -1 when the slot is past the last tile.
 template <int MT>
 __device__ __forceinline__ TileRows moe_tile(const GemmArgs& a, int slot, int lane) {
     TileRows tr{0, 0, -1};
@@ -282,7 +284,7 @@ __device__ __forceinline__ TileRows moe_tile(const GemmArgs& a, int slot, int la
     for (int c = 0; c < a.E; c += 64) {
         const int e = c + lane;
         const int cnt = e < a.E ? a.offsets[e + 1] - a.offsets[e] : 0;
-        const int t = (cnt + MT - 1) / MT;
+        const int t = (cnt >= a.moe_lo && cnt < a.moe_hi) ? (cnt + MT - 1) / MT : 0;
         int incl = t;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -862,34 +864,61 @@ struct PfRegs {
     uint32_t z;     // zero points of this thread's column, one byte per group
 };
 
-template <bool ASYM, int GPS, int MODE>
+// MOE: the grouped form for experts with many rows.  Workgroup (slot, column tile): slot
+// is a PF_BM-row tile of one expert (moe_tile), rows gathered from the token rows when
+// `gather` is set; output row r is the r-th sorted row.
+template <bool ASYM, int GPS, int MODE, bool MOE>
 __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 3, wn = wave >> 2;
-    const int mtiles = (a.M + PF_BM - 1) / PF_BM;
     const int ntl16 = (a.N + 15) / 16;                   // 16-column tiles in the blob
     const int ntiles = (ntl16 + 7) / 8;
-    int mt, nt;
-    prefill_tile(blockIdx.x, mtiles, ntiles, &mt, &nt);
-    const int m0 = mt * PF_BM, t0 = nt * 8;              // first row, first 16-column tile
+    int m0, mend, nt;
+    const uint8_t* blob = a.blob;
+    if (!MOE) {
+        const int mtiles = (a.M + PF_BM - 1) / PF_BM;
+        int mt;
+        prefill_tile(blockIdx.x, mtiles, ntiles, &mt, &nt);
+        m0 = mt * PF_BM;
+        mend = a.M;
+    } else {
+        nt = blockIdx.x % ntiles;
+        const TileRows tr = moe_tile<PF_BM>(a, blockIdx.x / ntiles, lane);
+        if (tr.expert < 0) return;                       // uniform over the workgroup
+        m0 = tr.rbeg;
+        mend = tr.rend;
+        blob = a.blob + size_t(tr.expert) * a.expert_stride;
+    }
+    const int t0 = nt * 8;                               // first 16-column tile
     const int nsb = a.K / SB_K;
-    const uint8_t* codes = a.blob + a.codes_off;
-    const uint8_t* scales_b = a.blob + a.scales_off;
-    const uint8_t* zeros_b = a.blob + a.zeros_off;
+    const uint8_t* codes = blob + a.codes_off;
+    const uint8_t* scales_b = blob + a.scales_off;
+    const uint8_t* zeros_b = blob + a.zeros_off;
+    // source activation row of tile row r (rows past the tile repeat its last row)
+    auto src_row = [&](int r) {
+        const int rr = min(m0 + r, mend - 1);
+        return (MOE && a.gather) ? a.gather[rr] / a.topk : rr;
+    };
 
     // staging: thread tid owns layout lane (tid % 64) of 16-column tile (tid / 64)
     const int b_tile = min(t0 + wave, ntl16 - 1);
     const int st_q4 = lane >> 4, st_c = lane & 15;
     const int nmeta_s = 8 * GPS * 4;                     // 16-byte scale pieces
+    // MOE: the gathered source rows of this thread's activation pieces, looked up once
+    int mrow[MOE ? 4 : 1];
+#pragma unroll
+    for (int i = 0; i < (MOE ? 4 : 1); ++i) mrow[i] = MOE ? src_row((tid + i * PF_THREADS) >> 3) : 0;
     auto gload = [&](PfRegs& r, int sb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int p = tid + i * PF_THREADS;
             const int row = p >> 3, c = p & 7;
             r.a[i] = make_uint4(0, 0, 0, 0);
-            if (m0 + row < a.M)
-                r.a[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(m0 + row) * a.K + size_t(sb) * SB_K + c * 16);
+            if (m0 + row < mend) {
+                const int srow = MOE ? mrow[MOE ? i : 0] : m0 + row;
+                r.a[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(srow) * a.K + size_t(sb) * SB_K + c * 16);
+            }
         }
         r.b = *reinterpret_cast<const uint4*>(codes + (size_t(b_tile) * nsb + sb) * 1024 + lane * 16);
         if (ASYM) {
@@ -982,7 +1011,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                                if (row < a.M && col < a.N) {
+                                if (row < mend && col < a.N) {
                                     const int v = ASYM ? acc[ms][ns][r] : (acc[ms][ns][r] >> 4);
                                     a.P[(size_t(row) * a.N + col) * a.G + size_t(sb) * GPS + gi] = v;
                                 }
@@ -1033,8 +1062,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
         float sxv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            sxv[r] = row < a.M ? a.sx[row] : 0.0f;
+            const int row = wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            sxv[r] = m0 + row < mend ? a.sx[src_row(row)] : 0.0f;
         }
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
@@ -1043,7 +1072,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                if (row >= a.M) continue;
+                if (row >= mend) continue;
                 const float y = accf[ms][ns][r] * sxv[r];
                 if (a.out_f32)
                     reinterpret_cast<float*>(a.Y)[size_t(row) * a.ldy + col] = y;
@@ -1302,22 +1331,30 @@ static void launch_kslice(const GemmArgs& a, const KsliceCfg& c, int ms, int gps
 #undef W4A8_KS
 }
 
-template <bool ASYM, int GPS, int MODE>
-static void launch_prefill_t(const GemmArgs& a, hipStream_t s) {
-    auto kern = gemm_prefill_kernel<ASYM, GPS, MODE>;
+// mtiles: row tiles (dense) or an upper bound on the experts' row tiles (MOE)
+template <bool ASYM, int GPS, int MODE, bool MOE>
+static void launch_prefill_t(const GemmArgs& a, int mtiles, hipStream_t s) {
+    auto kern = gemm_prefill_kernel<ASYM, GPS, MODE, MOE>;
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS);
     (void)attr;
-    const int mtiles = (a.M + PF_BM - 1) / PF_BM;
     const int ntiles = ((a.N + 15) / 16 + 7) / 8;
     kern<<<dim3(mtiles * ntiles), dim3(PF_THREADS), PF_LDS, s>>>(a);
 }
 
-template <int MODE>
-static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s) {
-    if (gps == 1) { if (asym) launch_prefill_t<true, 1, MODE>(a, s); else launch_prefill_t<false, 1, MODE>(a, s); }
-    else { if (asym) launch_prefill_t<true, 2, MODE>(a, s); else launch_prefill_t<false, 2, MODE>(a, s); }
+template <int MODE, bool MOE = false>
+static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s, int mtiles = 0) {
+    if (!MOE) mtiles = (a.M + PF_BM - 1) / PF_BM;
+    if (gps == 1) {
+        if (asym) launch_prefill_t<true, 1, MODE, MOE>(a, mtiles, s); else launch_prefill_t<false, 1, MODE, MOE>(a, mtiles, s);
+    } else {
+        if (asym) launch_prefill_t<true, 2, MODE, MOE>(a, mtiles, s); else launch_prefill_t<false, 2, MODE, MOE>(a, mtiles, s);
+    }
 }
+
+// MoE experts with at least this many rows run on the prefill kernel (256-row tiles: each
+// expert's weights are streamed once per 256 rows instead of once per 16 or 32).
+constexpr int MOE_PREFILL_MIN_ROWS = 128;
 
 // Dense GEMMs with more rows than this use the prefill kernel.
 constexpr int PREFILL_MIN_M = 33;
@@ -1508,6 +1545,17 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
     a.offsets = offsets;
     a.E = E;
     a.expert_stride = stride;
+    a.moe_lo = 0;
+    a.moe_hi = 1 << 30;
+    if (rows >= MOE_PREFILL_MIN_ROWS) {
+        // experts with many rows: prefill tiles; slots bound sum_e ceil(rows_e / 256) over
+        // experts with rows_e >= 128 (surplus workgroups find no tile and exit)
+        a.moe_lo = MOE_PREFILL_MIN_ROWS;
+        launch_prefill<MODE_OUT, true>(a, SB_K / d->group_size, d->asymmetric, s,
+                                       rows / PF_BM + rows / MOE_PREFILL_MIN_ROWS + 1);
+        a.moe_lo = 0;
+        a.moe_hi = MOE_PREFILL_MIN_ROWS;
+    }
     const int slots = rows / mt + std::min(E, rows) + 1;
     KsliceCfg kc;
     if (kslice_cfg(L.K, mt, &kc)) {

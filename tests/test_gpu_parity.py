@@ -100,6 +100,13 @@ def test_quant_act_near_ties_take_the_exact_division():
     (20, 256, 33, 64, False),
     (1, 4096, 256, 128, False),
     (64, 7168, 64, 64, True),                  # MoE decode expert shape (slice of N)
+    # one case per decode kernel variant: chunked 32-row tile (one chunk, several chunks),
+    # chunked 16-row long-K tile (several chunks), K-slice (2 and 4 superblocks per wave)
+    (32, 4096, 512, 128, False),
+    (32, 8192, 64, 128, True),
+    (12, 14336, 48, 128, False),
+    (2, 4096, 64, 64, True),
+    (1, 8192, 80, 128, True),
 ])
 def test_partials_bit_exact(M, K, N, g, asym):
     _print(f"partials M={M} K={K} N={N} g={g} asym={asym}")
