@@ -459,6 +459,54 @@ def test_moe_gemm_grouped_matches_per_expert_oracle():
     _print(check_float_output(Y, Ybf, Y64))
 
 
+@pytest.mark.parametrize("g,asym", [(64, True), (128, False)])
+def test_moe_gemm_hot_expert_paths(g, asym):
+    """Grouped GEMM where expert 0 owns 280 routed rows (two 256-row MFMA tiles, the second
+    ragged), expert 1 about 160 (one tile) and the others fewer than 128 (the streaming
+    kernel); with and without the row gather."""
+    T, k, E, K, N = 300, 2, 5, 256, 96
+    t = np.arange(T)
+    ids = np.stack([np.where(t < 280, 0, 1 + t % 4), np.where(t < 150, 1, 2 + t % 3)], axis=1).astype(np.int32)
+    dup = ids[:, 0] == ids[:, 1]
+    ids[dup, 1] = np.where(ids[dup, 0] == 2, 3, 2)
+    cnt = np.bincount(ids.ravel(), minlength=E)
+    assert cnt[0] > 256 and 128 <= cnt[1] < 256 and cnt[2:].max() < 128 and cnt.min() > 0
+    d = L.desc(K, N, g, asym)
+    host, qw = {}, {}
+    for e in range(E):
+        c = W.random_codes(31 * g + e, K, N, g, asym)
+        host[e] = L.w4a8_pack_codes(d, *c)
+        qw[e] = c
+    dev = L.experts_to_device(d, E, host)
+    Xb = W.random_activations(5, T, K, outlier_cols=2, outlier_scale=20.0)
+    Xq, sx = gpu_quant(Xb)
+    rows = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    inv = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    L.w4a8_moe_align(torch.from_numpy(ids).to(DEV), E, rows, off, inv)
+    q, s = O.quant_act(W.bf16_values(Xb))
+    srt, offs, _ = O.moe_align(ids, E)
+    # gathered rows (gate/up form)
+    Y = torch.empty((T * k, N), dtype=torch.float32, device=DEV)
+    Ybf = torch.empty((T * k, N), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_moe_gemm(Xq, sx, rows, k, off, E, T * k, dev.blob, dev.stride, d, Y, L.W4A8_OUT_F32)
+    L.w4a8_moe_gemm(Xq, sx, rows, k, off, E, T * k, dev.blob, dev.stride, d, Ybf, L.W4A8_OUT_BF16)
+    Y64 = np.zeros((T * k, N))
+    for e in range(E):
+        a, b = offs[e], offs[e + 1]
+        toks = srt[a:b] // k
+        Y64[a:b] = O.gemm(q[toks], s[toks], *qw[e], g)
+    _print(check_float_output(Y.cpu().numpy(), Ybf.float().cpu().numpy(), Y64))
+    # rows already in expert order (down form): the sorted rows' codes and scales
+    tok = rows.long().cpu() // k                          # sorted row -> token
+    assert int(tok.min()) >= 0 and int(tok.max()) < T
+    tok = tok.to(DEV)
+    Xs, ss = Xq[tok].contiguous(), sx[tok].contiguous()
+    L.w4a8_moe_gemm(Xs, ss, None, k, off, E, T * k, dev.blob, dev.stride, d, Y, L.W4A8_OUT_F32)
+    L.w4a8_moe_gemm(Xs, ss, None, k, off, E, T * k, dev.blob, dev.stride, d, Ybf, L.W4A8_OUT_BF16)
+    _print(check_float_output(Y.cpu().numpy(), Ybf.float().cpu().numpy(), Y64))
+
+
 def test_moe_forward_c4_full():
     """The 64-expert top-6 layer at full size (T=512, H=4096, I=1408), random codes."""
     cfg = W.C4
