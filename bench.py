@@ -166,12 +166,26 @@ def decode_leg(args, L, W, torch, dev):
     ms_step = dt * 1e3 / steps
     value = len(Ms) * wbytes * steps / dt / 1e9
     # the dominant kernel (decode GEMM, M = 32): 64 back-to-back launches on rotating weight
-    # copies between two HIP events on the launch stream; per-launch mean
-    kt = Timer(torch)
-    for rep in range(2):
-        s = kt.start()
+    # copies between two HIP events on the launch stream; per-launch mean.  The launches are
+    # replayed from a HIP graph so that the host's launch rate does not pace them.
+    def k_launches():
         for i in range(64):
             L.w4a8_gemm(Xq[32], sx[32], copies[i % args.copies], d, Y[32], L.W4A8_OUT_BF16)
+
+    kgraph = None
+    if not args.no_graph:
+        kgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(kgraph):
+            k_launches()
+        kgraph.replay()
+        torch.cuda.synchronize()
+    kt = Timer(torch)
+    for rep in range(4):
+        s = kt.start()
+        if kgraph is not None:
+            kgraph.replay()
+        else:
+            k_launches()
         kt.stop(s)
     kt.pairs = kt.pairs[1:]
     k_ms = kt.mean_ms() / 64

@@ -445,6 +445,9 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
             const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
             bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * 1024u));
         }
+        // keep these requests issued here: otherwise each is sunk next to its first use
+        // behind a full wait, leaving one weight load in flight per wave
+        asm volatile("" ::: "memory");
         // 6. MFMA over this wave's superblocks
 #pragma unroll
         for (int s = 0; s < SBN; ++s) {
