@@ -558,27 +558,31 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 constexpr size_t FUSED_MAX_ELEMS = 8192;
 constexpr int FQ_PIECES = 1;
 
-template <int MS, int T>
+// TG > 1: the workgroup streams TG groups of T tiles one after another, the loads of two
+// groups in flight (double-buffered registers), so each workgroup's fixed costs (activation
+// fragments, slice reduction, launch) are spread over TG times more weight bytes.
+template <int MS, int T, int TG = 1>
 struct KsliceShape {
     static constexpr int MT = 16 * MS;
     static constexpr int NV = 4 * MS;                          // accumulators per lane per tile
+    static constexpr int TT = T * TG;                          // tiles per workgroup
     // slice partials, then 32 row scales and 32 row abs-maxima; the fused path adds its
     // quantized rows [rows][K + 16] after that
-    static constexpr size_t lds(int kw) { return size_t(kw) * T * 64 * NV * 4 + 64 * 4; }
+    static constexpr size_t lds(int kw) { return size_t(kw) * TT * 64 * NV * 4 + 64 * 4; }
 };
 
-template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ>
+template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ, int TG>
 __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
-    using S = KsliceShape<MS, T>;
-    static_assert(!FQ || (MS == 1 && !MOE && MODE == MODE_OUT), "fused quantization: dense 16-row tiles");
-    constexpr int NV = S::NV;
+    using S = KsliceShape<MS, T, TG>;
+    static_assert(!FQ || (MS == 1 && !MOE && MODE == MODE_OUT && TG == 1), "fused quantization: dense 16-row tiles");
+    constexpr int NV = S::NV, TT = S::TT;
     extern __shared__ __align__(16) uint8_t smem[];
-    float* red = reinterpret_cast<float*>(smem);              // [KW][T][64][NV]
+    float* red = reinterpret_cast<float*>(smem);              // [KW][TT][64][NV]
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int KW = blockDim.x >> 6;
     const int ntiles = (a.N + 15) / 16;
-    const int tile0 = blockIdx.x * T;
+    const int tile0 = blockIdx.x * TT;
     const int nsb = a.K / SB_K;
     const int sb0 = w * SW;
 
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     const uint8_t* zeros = blob + a.zeros_off;
 
     // row scales of the tile's rows: fetched first, parked in LDS after the MFMAs
-    float* sxs = red + size_t(KW) * T * 64 * NV;
+    float* sxs = red + size_t(KW) * TT * 64 * NV;
     float sxv = 0.0f;
     if (!FQ && MODE != MODE_PARTIALS && tid < S::MT && tid < nrows)
         sxv = a.sx[(MOE && a.gather) ? a.gather[rbeg + tid] / a.topk : rbeg + tid];
@@ -647,36 +651,49 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
                     A[s][h][ms] = *reinterpret_cast<const v4i*>(xrow + (sb0 + s) * SB_K + h * 64 + 16 * (lane >> 4));
             }
     }
-    // 2. group scales and zero points of the T tiles x SW superblocks
-    float sc[T][SW][GPS];
-    uint32_t zq[T][SW][GPS];
+    // 2. per tile group (register set g % 2): group scales and zero points of its T tiles x
+    //    SW superblocks, then its weight superblocks in the order they are consumed
+    constexpr int NSET = TG > 1 ? 2 : 1;
+    float sc[NSET][T][SW][GPS];
+    uint32_t zq[NSET][T][SW][GPS];
+    uint4 bq[NSET][T][SW];
+    auto load_meta = [&](const int g) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const uint32_t tc = uint32_t(min(tile0 + t, ntiles - 1));
+        for (int t = 0; t < T; ++t) {
+            const uint32_t tc = uint32_t(min(tile0 + g * T + t, ntiles - 1));
 #pragma unroll
-        for (int s = 0; s < SW; ++s) {
-            const uint32_t sb = uint32_t(min(sb0 + s, nsb - 1));
+            for (int s = 0; s < SW; ++s) {
+                const uint32_t sb = uint32_t(min(sb0 + s, nsb - 1));
 #pragma unroll
-            for (int gi = 0; gi < GPS; ++gi) {
-                const uint32_t mi = (tc * uint32_t(a.G) + sb * GPS + gi) * 16u + uint32_t(lane & 15);
-                sc[t][s][gi] = scales[mi];
-                if (ASYM) zq[t][s][gi] = zeros[mi];
+                for (int gi = 0; gi < GPS; ++gi) {
+                    const uint32_t mi = (tc * uint32_t(a.G) + sb * GPS + gi) * 16u + uint32_t(lane & 15);
+                    sc[g % NSET][t][s][gi] = scales[mi];
+                    if (ASYM) zq[g % NSET][t][s][gi] = zeros[mi];
+                }
             }
         }
-    }
+    };
+    auto load_w = [&](const int g) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const uint32_t tc = uint32_t(min(tile0 + g * T + t, ntiles - 1));
+#pragma unroll
+            for (int s = 0; s < SW; ++s) {
+                const uint32_t sb = uint32_t(min(sb0 + s, nsb - 1));
+                bq[g % NSET][t][s] =
+                    *reinterpret_cast<const uint4*>(codes + ((tc * uint32_t(nsb) + sb) * 1024u + uint32_t(lane) * 16u));
+            }
+        }
+    };
+    load_meta(0);
     // issue fence: the small requests of every wave go out before any weight request
     // (it also publishes the fused path's cleared row maxima)
     lds_barrier();
-    // 3. weight superblocks, in the order they are consumed (tile-major)
-    uint4 bq[T][SW];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const uint32_t tc = uint32_t(min(tile0 + t, ntiles - 1));
-#pragma unroll
-        for (int s = 0; s < SW; ++s) {
-            const uint32_t sb = uint32_t(min(sb0 + s, nsb - 1));
-            bq[t][s] = *reinterpret_cast<const uint4*>(codes + ((tc * uint32_t(nsb) + sb) * 1024u + uint32_t(lane) * 16u));
-        }
+    // 3. the weight stream: group 0, then group 1 (its scales first)
+    load_w(0);
+    if constexpr (TG > 1) {
+        load_meta(1);
+        load_w(1);
     }
     asm volatile("" ::: "memory");                      // keep the whole stream issued here
     if (FQ) {
@@ -729,16 +746,18 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
                                                                16 * (lane >> 4));
             }
     }
-    // 4. per tile: MFMAs over the slice, per-group epilogue, partial to LDS
+    // 4. per tile: MFMAs over the slice, per-group epilogue, partial to LDS; after each tile
+    //    group, the group two ahead is requested into the registers it used
     const v4i zero4 = {0, 0, 0, 0};
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
+    for (int tt = 0; tt < TT; ++tt) {
+        const int g = tt / T, t = tt % T, set = g % NSET;
         float accf[MS][4];
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
             for (int i = 0; i < 4; ++i) accf[ms][i] = 0.0f;
-        const int tile = tile0 + t;
+        const int tile = tile0 + tt;
 #pragma unroll
         for (int s = 0; s < SW; ++s) {
             if (sb0 + s >= nsb) break;
@@ -746,9 +765,9 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int gi = (GPS == 2) ? h : 0;
-                const uint32_t w0 = h ? bq[t][s].z : bq[t][s].x;
-                const uint32_t w1 = h ? bq[t][s].w : bq[t][s].y;
-                const uint32_t zc = ASYM ? (128u - zq[t][s][gi]) * 0x01010101u : 0u;
+                const uint32_t w0 = h ? bq[set][t][s].z : bq[set][t][s].x;
+                const uint32_t w1 = h ? bq[set][t][s].w : bq[set][t][s].y;
+                const uint32_t zc = ASYM ? (128u - zq[set][t][s][gi]) * 0x01010101u : 0u;
                 const v4i b = unpack_b<ASYM>(w0, w1, zc);
                 const bool first = (GPS == 2) || h == 0;
 #pragma unroll
@@ -768,7 +787,7 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
                                 }
                             }
                     } else {
-                        const float scl = ASYM ? sc[t][s][gi] : sc[t][s][gi] * 0.0625f;
+                        const float scl = ASYM ? sc[set][t][s][gi] : sc[set][t][s][gi] * 0.0625f;
 #pragma unroll
                         for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -778,9 +797,16 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
             }
         }
         if (MODE != MODE_PARTIALS) {
-            float4* dst = reinterpret_cast<float4*>(red + ((size_t(w) * T + t) * 64 + lane) * NV);
+            float4* dst = reinterpret_cast<float4*>(red + ((size_t(w) * TT + tt) * 64 + lane) * NV);
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms) dst[ms] = make_float4(accf[ms][0], accf[ms][1], accf[ms][2], accf[ms][3]);
+        }
+        if constexpr (TG > 2) {
+            if (t == T - 1 && g + 2 < TG) {
+                load_meta(g + 2);
+                load_w(g + 2);
+                asm volatile("" ::: "memory");
+            }
         }
     }
     if (MODE == MODE_PARTIALS) return;
@@ -788,13 +814,13 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     __syncthreads();
     // 5. slice-ordered sum, row scale, store.  Output o = (t * 64 + l) * NV + j holds
     //    C[row = (j / 4) * 16 + 4 * (l / 16) + j % 4][col = 16 * t + l % 16] of the tile grid.
-    for (int o = tid; o < T * 64 * NV; o += int(blockDim.x)) {
+    for (int o = tid; o < TT * 64 * NV; o += int(blockDim.x)) {
         const int j = o % NV, lo = (o / NV) % 64, t = o / (NV * 64);
         const int row = (j >> 2) * 16 + 4 * (lo >> 4) + (j & 3);
         const int col = (tile0 + t) * 16 + (lo & 15);
         if (row >= nrows || tile0 + t >= ntiles || col >= a.N) continue;
         float y = red[o];
-        for (int k = 1; k < KW; ++k) y += red[size_t(k) * T * 64 * NV + o];
+        for (int k = 1; k < KW; ++k) y += red[size_t(k) * TT * 64 * NV + o];
         y *= sxs[row];
         const size_t yi = size_t(rbeg + row) * a.ldy + col;
         if (a.out_f32)
@@ -1269,13 +1295,20 @@ static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool a
 }
 
 
-// K-slice decode kernel: T tiles per workgroup, SW superblocks per wave, KW waves.
+// K-slice decode kernel: T tiles per group, TG groups per workgroup, SW superblocks per
+// wave, KW waves.
 struct KsliceCfg {
-    int t, sw, kw;
+    int t, sw, kw, tg;
 };
 
-static bool kslice_cfg(int K, int mt, KsliceCfg* c) {
+// Tile groups per workgroup for the grouped (MoE) form at 16-row tiles and K in (4096, 8192]:
+// there one workgroup fills a compute unit (its registers), and with a single 32-column
+// group it would spend most of its life on fixed costs between short weight streams.
+constexpr int MOE_KSLICE_TG = 8;
+
+static bool kslice_cfg(int K, int mt, KsliceCfg* c, bool moe = false) {
     const int nsb = K / SB_K;
+    c->tg = 1;
     if (nsb <= 16) {
         c->t = 4;
         c->sw = 1;
@@ -1283,8 +1316,9 @@ static bool kslice_cfg(int K, int mt, KsliceCfg* c) {
         c->t = 4;
         c->sw = 2;
     } else if (nsb <= 64 && mt == 16) {   // 32-row tiles at this depth would not fit in registers
-        c->t = 2;
+        c->t = moe ? 1 : 2;
         c->sw = 4;
+        if (moe) c->tg = MOE_KSLICE_TG;
     } else {
         return false;
     }
@@ -1299,10 +1333,11 @@ static bool dense_kslice(int M, int K, KsliceCfg* c) {
     return size_t(M) * K <= FUSED_MAX_ELEMS && kslice_cfg(K, 16, c);
 }
 
-template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ = false>
+template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ = false, int TG = 1>
 static void launch_kslice_t(const GemmArgs& a, int kw, int ytiles, hipStream_t s) {
-    using S = KsliceShape<MS, T>;
-    auto kern = gemm_kslice_kernel<MS, T, SW, GPS, ASYM, MODE, MOE, FQ>;
+    using S = KsliceShape<MS, T, TG>;
+    static_assert(S::lds(16) <= 160 * 1024, "slice partials exceed LDS");
+    auto kern = gemm_kslice_kernel<MS, T, SW, GPS, ASYM, MODE, MOE, FQ, TG>;
     constexpr size_t fq_max = FQ ? FUSED_MAX_ELEMS + 16 * 16 : 0;   // quantized rows, padded
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1310,14 +1345,22 @@ static void launch_kslice_t(const GemmArgs& a, int kw, int ytiles, hipStream_t s
     (void)attr;
     const int ntiles = (a.N + 15) / 16;
     const size_t lds = S::lds(kw) + (FQ ? size_t(a.M) * (a.K + 16) : 0);
-    kern<<<dim3((ntiles + T - 1) / T, ytiles), dim3(64 * kw), lds, s>>>(a);
+    kern<<<dim3((ntiles + S::TT - 1) / S::TT, ytiles), dim3(64 * kw), lds, s>>>(a);
 }
 
 template <int MS, int GPS, bool ASYM, int MODE, bool MOE>
 static void launch_kslice_shape(const GemmArgs& a, const KsliceCfg& c, int ytiles, hipStream_t s) {
     if (c.sw == 1) launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
     else if (c.sw == 2) launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
-    else if constexpr (MS == 1) launch_kslice_t<MS, 2, 4, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+    else if constexpr (MS == 1) {
+        if constexpr (MOE) {
+            if (c.tg == MOE_KSLICE_TG) {
+                launch_kslice_t<MS, 1, 4, GPS, ASYM, MODE, MOE, false, MOE_KSLICE_TG>(a, c.kw, ytiles, s);
+                return;
+            }
+        }
+        launch_kslice_t<MS, 2, 4, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+    }
 }
 
 template <int MODE, bool MOE>
@@ -1561,7 +1604,7 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
     }
     const int slots = rows / mt + std::min(E, rows) + 1;
     KsliceCfg kc;
-    if (kslice_cfg(L.K, mt, &kc)) {
+    if (kslice_cfg(L.K, mt, &kc, true)) {
         launch_kslice<MODE_OUT, true>(a, kc, mt / 16, SB_K / d->group_size, d->asymmetric, slots, s);
         return launch_status();
     }

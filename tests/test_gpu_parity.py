@@ -507,6 +507,48 @@ def test_moe_gemm_hot_expert_paths(g, asym):
     _print(check_float_output(Y.cpu().numpy(), Ybf.float().cpu().numpy(), Y64))
 
 
+@pytest.mark.parametrize("K,N,g,asym", [(7168, 400, 64, True), (4608, 272, 128, False), (5120, 128, 64, False)])
+def test_moe_gemm_tile_groups(K, N, g, asym):
+    """Grouped GEMM at 16-row tiles with K in (4096, 8192], where each workgroup streams
+    several column-tile groups (the last one ragged when N is not a multiple of 128);
+    gathered and already-sorted row forms against the oracle."""
+    T, k, E = 20, 2, 6
+    rng = np.random.default_rng(77 + K)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    d = L.desc(K, N, g, asym)
+    host, qw = {}, {}
+    for e in range(E):
+        c = W.random_codes(K + 7 * e, K, N, g, asym)
+        host[e] = L.w4a8_pack_codes(d, *c)
+        qw[e] = c
+    dev = L.experts_to_device(d, E, host)
+    Xb = W.random_activations(11, T, K, outlier_cols=3, outlier_scale=30.0)
+    Xq, sx = gpu_quant(Xb)
+    rows = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    inv = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    L.w4a8_moe_align(torch.from_numpy(ids).to(DEV), E, rows, off, inv)
+    q, s = O.quant_act(W.bf16_values(Xb))
+    srt, offs, _ = O.moe_align(ids, E)
+    Y64 = np.zeros((T * k, N))
+    for e in range(E):
+        a, b = offs[e], offs[e + 1]
+        toks = srt[a:b] // k
+        Y64[a:b] = O.gemm(q[toks], s[toks], *qw[e], g)
+    Y = torch.empty((T * k, N), dtype=torch.float32, device=DEV)
+    Ybf = torch.empty((T * k, N), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_moe_gemm(Xq, sx, rows, k, off, E, T * k, dev.blob, dev.stride, d, Y, L.W4A8_OUT_F32)
+    L.w4a8_moe_gemm(Xq, sx, rows, k, off, E, T * k, dev.blob, dev.stride, d, Ybf, L.W4A8_OUT_BF16)
+    _print(check_float_output(Y.cpu().numpy(), Ybf.float().cpu().numpy(), Y64))
+    tok = rows.long().cpu() // k
+    assert int(tok.min()) >= 0 and int(tok.max()) < T
+    tok = tok.to(DEV)
+    Xs, ss = Xq[tok].contiguous(), sx[tok].contiguous()
+    L.w4a8_moe_gemm(Xs, ss, None, k, off, E, T * k, dev.blob, dev.stride, d, Y, L.W4A8_OUT_F32)
+    L.w4a8_moe_gemm(Xs, ss, None, k, off, E, T * k, dev.blob, dev.stride, d, Ybf, L.W4A8_OUT_BF16)
+    _print(check_float_output(Y.cpu().numpy(), Ybf.float().cpu().numpy(), Y64))
+
+
 def test_moe_forward_c4_full():
     """The 64-expert top-6 layer at full size (T=512, H=4096, I=1408), random codes."""
     cfg = W.C4
