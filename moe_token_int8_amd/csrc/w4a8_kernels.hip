@@ -571,10 +571,16 @@ struct KsliceShape {
     static constexpr size_t lds(int kw) { return size_t(kw) * TT * 64 * NV * 4 + 64 * 4; }
 };
 
-template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ, int TG>
+// RL (grouped form): a workgroup takes up to MOE_KSLICE_ROWS rows of one expert and runs its
+// MT-row tiles one after another on the weights it holds in registers, so an expert's
+// weights are streamed once per column tile instead of once per row tile.
+constexpr int MOE_KSLICE_ROWS = 128;
+
+template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ, int TG, bool RL>
 __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     using S = KsliceShape<MS, T, TG>;
     static_assert(!FQ || (MS == 1 && !MOE && MODE == MODE_OUT && TG == 1), "fused quantization: dense 16-row tiles");
+    static_assert(!RL || (MOE && MODE == MODE_OUT && TG == 1), "row loop: grouped form, one tile group");
     constexpr int NV = S::NV, TT = S::TT;
     extern __shared__ __align__(16) uint8_t smem[];
     float* red = reinterpret_cast<float*>(smem);              // [KW][TT][64][NV]
@@ -586,19 +592,21 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     const int nsb = a.K / SB_K;
     const int sb0 = w * SW;
 
-    int rbeg, rend;
+    int rbeg, rend, rall;                                // rows of the current tile; of the workgroup
     const uint8_t* blob = a.blob;
     if (!MOE) {
         rbeg = blockIdx.y * S::MT;
         rend = min(a.M, rbeg + S::MT);
+        rall = rend;
     } else {
-        const TileRows tr = moe_tile<S::MT>(a, blockIdx.y, lane);
+        const TileRows tr = moe_tile<RL ? MOE_KSLICE_ROWS : S::MT>(a, blockIdx.y, lane);
         if (tr.expert < 0) return;                       // uniform over the workgroup
         rbeg = tr.rbeg;
-        rend = tr.rend;
+        rall = tr.rend;
+        rend = min(rall, rbeg + S::MT);
         blob = a.blob + size_t(tr.expert) * a.expert_stride;
     }
-    const int nrows = rend - rbeg;
+    int nrows = rend - rbeg;
     const uint8_t* codes = blob + a.codes_off;
     const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
     const uint8_t* zeros = blob + a.zeros_off;
@@ -606,8 +614,12 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     // row scales of the tile's rows: fetched first, parked in LDS after the MFMAs
     float* sxs = red + size_t(KW) * TT * 64 * NV;
     float sxv = 0.0f;
-    if (!FQ && MODE != MODE_PARTIALS && tid < S::MT && tid < nrows)
-        sxv = a.sx[(MOE && a.gather) ? a.gather[rbeg + tid] / a.topk : rbeg + tid];
+    auto load_sx = [&]() __attribute__((always_inline)) {
+        sxv = 0.0f;
+        if (!FQ && MODE != MODE_PARTIALS && tid < S::MT && tid < nrows)
+            sxv = a.sx[(MOE && a.gather) ? a.gather[rbeg + tid] / a.topk : rbeg + tid];
+    };
+    load_sx();
 
     // fused path: LDS also holds the row abs-maxima and the quantized rows [nrows][K + 16]
     uint32_t* rowmax = reinterpret_cast<uint32_t*>(sxs + 32);
@@ -633,24 +645,27 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     // 1. activation fragments of this wave's K-slice: lane l holds row ms * 16 + l % 16 and
     //    the 16 K-values [16 * (l / 16), +16) of each 64-deep half (the MFMA A operand)
     v4i A[SW][2][MS];
+    auto load_a = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int ms = 0; ms < MS && !FQ; ++ms) {
-        const int row = ms * 16 + (lane & 15);
-        const bool rv = row < nrows;
-        const int8_t* xrow = a.Xq;
-        if (rv) {
-            const int src = (MOE && a.gather) ? a.gather[rbeg + row] / a.topk : rbeg + row;
-            xrow = a.Xq + size_t(src) * a.K;
-        }
-#pragma unroll
-        for (int s = 0; s < SW; ++s)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                A[s][h][ms] = v4i{0, 0, 0, 0};
-                if (rv && sb0 + s < nsb)
-                    A[s][h][ms] = *reinterpret_cast<const v4i*>(xrow + (sb0 + s) * SB_K + h * 64 + 16 * (lane >> 4));
+        for (int ms = 0; ms < MS && !FQ; ++ms) {
+            const int row = ms * 16 + (lane & 15);
+            const bool rv = row < nrows;
+            const int8_t* xrow = a.Xq;
+            if (rv) {
+                const int src = (MOE && a.gather) ? a.gather[rbeg + row] / a.topk : rbeg + row;
+                xrow = a.Xq + size_t(src) * a.K;
             }
-    }
+#pragma unroll
+            for (int s = 0; s < SW; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    A[s][h][ms] = v4i{0, 0, 0, 0};
+                    if (rv && sb0 + s < nsb)
+                        A[s][h][ms] = *reinterpret_cast<const v4i*>(xrow + (sb0 + s) * SB_K + h * 64 + 16 * (lane >> 4));
+                }
+        }
+    };
+    load_a();
     // 2. per tile group (register set g % 2): group scales and zero points of its T tiles x
     //    SW superblocks, then its weight superblocks in the order they are consumed
     constexpr int NSET = TG > 1 ? 2 : 1;
@@ -749,6 +764,7 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     // 4. per tile: MFMAs over the slice, per-group epilogue, partial to LDS; after each tile
     //    group, the group two ahead is requested into the registers it used
     const v4i zero4 = {0, 0, 0, 0};
+    auto compute = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
         const int g = tt / T, t = tt % T, set = g % NSET;
@@ -809,11 +825,14 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
             }
         }
     }
+    };
+    compute();
     if (MODE == MODE_PARTIALS) return;
     if (tid < S::MT) sxs[tid] = sxv;
     __syncthreads();
     // 5. slice-ordered sum, row scale, store.  Output o = (t * 64 + l) * NV + j holds
     //    C[row = (j / 4) * 16 + 4 * (l / 16) + j % 4][col = 16 * t + l % 16] of the tile grid.
+    auto reduce_store = [&]() __attribute__((always_inline)) {
     for (int o = tid; o < TT * 64 * NV; o += int(blockDim.x)) {
         const int j = o % NV, lo = (o / NV) % 64, t = o / (NV * 64);
         const int row = (j >> 2) * 16 + 4 * (lo >> 4) + (j & 3);
@@ -827,6 +846,24 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
             reinterpret_cast<float*>(a.Y)[yi] = y;
         else
             reinterpret_cast<uint16_t*>(a.Y)[yi] = (uint16_t)f32_to_bf16_rne(y);
+    }
+    };
+    reduce_store();
+    if constexpr (RL) {
+        // the expert's further row tiles, on the weights, scales and zero points held in
+        // registers (their loads have all completed by now)
+        for (int r0 = rbeg + S::MT; r0 < rall; r0 += S::MT) {
+            rbeg = r0;
+            rend = min(rall, r0 + S::MT);
+            nrows = rend - rbeg;
+            load_sx();
+            load_a();
+            __syncthreads();                             // partials and row scales of the last tile are read
+            compute();
+            if (tid < S::MT) sxs[tid] = sxv;
+            __syncthreads();
+            reduce_store();
+        }
     }
     if (FQ && blockIdx.x == 0) {
         // fused path: workgroup 0 exports the activation codes and scales (after all of its
@@ -1299,6 +1336,7 @@ static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool a
 // wave, KW waves.
 struct KsliceCfg {
     int t, sw, kw, tg;
+    bool rl;        // grouped form: run the expert's row tiles in one workgroup
 };
 
 // Tile groups per workgroup for the grouped (MoE) form at 16-row tiles and K in (4096, 8192]:
@@ -1309,9 +1347,14 @@ constexpr int MOE_KSLICE_TG = 8;
 static bool kslice_cfg(int K, int mt, KsliceCfg* c, bool moe = false) {
     const int nsb = K / SB_K;
     c->tg = 1;
+    c->rl = false;
     if (nsb <= 16) {
         c->t = 4;
         c->sw = 1;
+        // measured: worth it at 32-row tiles (an expert's weights are read once instead of
+        // once per tile); at 16-row tiles the extra registers cost the second resident
+        // workgroup per compute unit, which matters more
+        c->rl = moe && mt == 32;
     } else if (nsb <= 32) {
         c->t = 4;
         c->sw = 2;
@@ -1333,11 +1376,12 @@ static bool dense_kslice(int M, int K, KsliceCfg* c) {
     return size_t(M) * K <= FUSED_MAX_ELEMS && kslice_cfg(K, 16, c);
 }
 
-template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ = false, int TG = 1>
+template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ = false, int TG = 1,
+          bool RL = false>
 static void launch_kslice_t(const GemmArgs& a, int kw, int ytiles, hipStream_t s) {
     using S = KsliceShape<MS, T, TG>;
     static_assert(S::lds(16) <= 160 * 1024, "slice partials exceed LDS");
-    auto kern = gemm_kslice_kernel<MS, T, SW, GPS, ASYM, MODE, MOE, FQ, TG>;
+    auto kern = gemm_kslice_kernel<MS, T, SW, GPS, ASYM, MODE, MOE, FQ, TG, RL>;
     constexpr size_t fq_max = FQ ? FUSED_MAX_ELEMS + 16 * 16 : 0;   // quantized rows, padded
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1350,16 +1394,20 @@ static void launch_kslice_t(const GemmArgs& a, int kw, int ytiles, hipStream_t s
 
 template <int MS, int GPS, bool ASYM, int MODE, bool MOE>
 static void launch_kslice_shape(const GemmArgs& a, const KsliceCfg& c, int ytiles, hipStream_t s) {
-    if (c.sw == 1) launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
-    else if (c.sw == 2) launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
-    else if constexpr (MS == 1) {
-        if constexpr (MOE) {
-            if (c.tg == MOE_KSLICE_TG) {
-                launch_kslice_t<MS, 1, 4, GPS, ASYM, MODE, MOE, false, MOE_KSLICE_TG>(a, c.kw, ytiles, s);
+    // shapes kslice_cfg can return for this form (others are not instantiated)
+    if (c.sw == 1) {
+        if constexpr (MOE && MS == 2 && MODE == MODE_OUT) {
+            if (c.rl) {
+                launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE, false, 1, true>(a, c.kw, ytiles, s);
                 return;
             }
         }
-        launch_kslice_t<MS, 2, 4, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+        launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+    } else if (c.sw == 2) {
+        launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+    } else if constexpr (MS == 1) {
+        if constexpr (MOE) launch_kslice_t<MS, 1, 4, GPS, ASYM, MODE, MOE, false, MOE_KSLICE_TG>(a, c.kw, ytiles, s);
+        else launch_kslice_t<MS, 2, 4, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
     }
 }
 
@@ -1602,10 +1650,13 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
         a.moe_lo = 0;
         a.moe_hi = MOE_PREFILL_MIN_ROWS;
     }
+    // slots bound sum_e ceil(rows_e / per) over the experts; surplus workgroups exit at once
     const int slots = rows / mt + std::min(E, rows) + 1;
     KsliceCfg kc;
     if (kslice_cfg(L.K, mt, &kc, true)) {
-        launch_kslice<MODE_OUT, true>(a, kc, mt / 16, SB_K / d->group_size, d->asymmetric, slots, s);
+        // row loop: a workgroup runs up to MOE_KSLICE_ROWS rows of its expert
+        const int kslots = kc.rl ? rows / MOE_KSLICE_ROWS + std::min(E, rows) + 1 : slots;
+        launch_kslice<MODE_OUT, true>(a, kc, mt / 16, SB_K / d->group_size, d->asymmetric, kslots, s);
         return launch_status();
     }
     const DecodeCfg c = decode_cfg(L.K, mt);

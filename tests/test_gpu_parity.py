@@ -549,6 +549,57 @@ def test_moe_gemm_tile_groups(K, N, g, asym):
     _print(check_float_output(Y.cpu().numpy(), Ybf.float().cpu().numpy(), Y64))
 
 
+@pytest.mark.parametrize("T,k,E,K,N,g,asym", [(60, 2, 16, 2048, 200, 128, False),
+                                                (60, 2, 16, 3072, 200, 64, True),
+                                                (100, 2, 4, 4096, 144, 128, True),
+                                                (100, 2, 4, 1408, 208, 128, False),
+                                                (100, 2, 4, 2048, 144, 64, True)])
+def test_moe_gemm_row_loop(T, k, E, K, N, g, asym):
+    """Grouped GEMM where one expert holds several row tiles below the 128-row cut (about 50
+    rows at 16-row tiles; about 70 at 32-row tiles, where for K <= 2048 one workgroup runs
+    them in turn on the weights it holds); gathered and already-sorted rows against the
+    oracle."""
+    rng = np.random.default_rng(5 + K + E)
+    t = np.arange(T)
+    first = np.where(t < T // 2 if E == 4 else t < 50, 0, 1 + t % (E - 1))
+    second = np.array([rng.choice([e for e in range(E) if e != f]) for f in first])
+    ids = np.stack([first, second], axis=1).astype(np.int32)
+    cnt = np.bincount(ids.ravel(), minlength=E)
+    assert cnt.max() < 128 and cnt[0] >= 50
+    d = L.desc(K, N, g, asym)
+    host, qw = {}, {}
+    for e in range(E):
+        c = W.random_codes(3 * K + e, K, N, g, asym)
+        host[e] = L.w4a8_pack_codes(d, *c)
+        qw[e] = c
+    dev = L.experts_to_device(d, E, host)
+    Xb = W.random_activations(13, T, K, outlier_cols=2, outlier_scale=25.0)
+    Xq, sx = gpu_quant(Xb)
+    rows = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    inv = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    L.w4a8_moe_align(torch.from_numpy(ids).to(DEV), E, rows, off, inv)
+    q, s = O.quant_act(W.bf16_values(Xb))
+    srt, offs, _ = O.moe_align(ids, E)
+    Y64 = np.zeros((T * k, N))
+    for e in range(E):
+        a, b = offs[e], offs[e + 1]
+        toks = srt[a:b] // k
+        Y64[a:b] = O.gemm(q[toks], s[toks], *qw[e], g)
+    Y = torch.empty((T * k, N), dtype=torch.float32, device=DEV)
+    Ybf = torch.empty((T * k, N), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_moe_gemm(Xq, sx, rows, k, off, E, T * k, dev.blob, dev.stride, d, Y, L.W4A8_OUT_F32)
+    L.w4a8_moe_gemm(Xq, sx, rows, k, off, E, T * k, dev.blob, dev.stride, d, Ybf, L.W4A8_OUT_BF16)
+    _print(check_float_output(Y.cpu().numpy(), Ybf.float().cpu().numpy(), Y64))
+    tok = rows.long().cpu() // k
+    assert int(tok.min()) >= 0 and int(tok.max()) < T
+    tok = tok.to(DEV)
+    Xs, ss = Xq[tok].contiguous(), sx[tok].contiguous()
+    L.w4a8_moe_gemm(Xs, ss, None, k, off, E, T * k, dev.blob, dev.stride, d, Y, L.W4A8_OUT_F32)
+    L.w4a8_moe_gemm(Xs, ss, None, k, off, E, T * k, dev.blob, dev.stride, d, Ybf, L.W4A8_OUT_BF16)
+    _print(check_float_output(Y.cpu().numpy(), Ybf.float().cpu().numpy(), Y64))
+
+
 def test_moe_forward_c4_full():
     """The 64-expert top-6 layer at full size (T=512, H=4096, I=1408), random codes."""
     cfg = W.C4
