@@ -1155,20 +1155,27 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
 // per-expert counts live at cnt[e * (B + 1) + b] (padded stride: conflict-free in both
 // passes).  Positions: off[e] + counts of earlier blocks + order inside the block.
 // ------------------------------------------------------------------------------------
+// STAGE: the R expert ids are first copied to LDS with coalesced loads, so both passes over
+// them read LDS instead of issuing one dependent global load per row.
+template <bool STAGE>
 __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restrict__ ids, int R, int E, int L,
                                                          int B, int32_t* __restrict__ sorted_rows,
                                                          int32_t* __restrict__ offsets, int32_t* __restrict__ inv) {
     extern __shared__ __align__(16) uint8_t smem[];
     int* cnt = reinterpret_cast<int*>(smem);   // E * (B + 1)
     int* wsum = cnt + E * (B + 1);             // 16 wave totals
+    int* sid = wsum + 16;                      // STAGE: the R ids
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int stride = B + 1;
     for (int i = tid; i < E * stride; i += 1024) cnt[i] = 0;
+    if (STAGE)
+        for (int i = tid; i < R; i += 1024) sid[i] = ids[i];
     __syncthreads();
+    auto id_of = [&](int r) { return STAGE ? sid[r] : ids[r]; };
     if (tid < B) {
         const int r1 = min(R, (tid + 1) * L);
         for (int r = tid * L; r < r1; ++r) {
-            const int e = ids[r];
+            const int e = id_of(r);
             if (e >= 0 && e < E) cnt[e * stride + tid]++;
         }
     }
@@ -1203,7 +1210,7 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restri
     if (tid < B) {
         const int r1 = min(R, (tid + 1) * L);
         for (int r = tid * L; r < r1; ++r) {
-            const int e = ids[r];
+            const int e = id_of(r);
             if (e >= 0 && e < E) {
                 const int pos = cnt[e * stride + tid]++;
                 sorted_rows[pos] = r;
@@ -1218,25 +1225,46 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restri
 // ------------------------------------------------------------------------------------
 // un-permute + top-k weighted combine (P1 section 4.3): float32, j ascending.
 // ------------------------------------------------------------------------------------
+// KM > 0: k <= KM, all k rows requested at once (their indices and weights first); KM = 0:
+// any k, one row after another.  The sum runs over j ascending either way.
+template <int KM>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const uint16_t* __restrict__ Yd,
                                                           const int32_t* __restrict__ inv,
                                                           const float* __restrict__ w, int k, int H,
                                                           uint16_t* __restrict__ out) {
     const int t = blockIdx.x;
+    int rj[KM > 0 ? KM : 1];
+    float wj[KM > 0 ? KM : 1];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+        rj[j] = j < k ? inv[t * k + j] : -1;
+        wj[j] = j < k ? w[t * k + j] : 0.0f;
+    }
+    auto add_row = [&](float* acc, const uint4 v, const float wgt) __attribute__((always_inline)) {
+        const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(wgt, bf16_to_f32(x[i] & 0xffffu), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(wgt, bf16_to_f32(x[i] >> 16), acc[2 * i + 1]);
+        }
+    };
     for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const int r = inv[t * k + j];
-            if (r < 0) continue;
-            const float wj = w[t * k + j];
-            const uint4 v = *reinterpret_cast<const uint4*>(Yd + size_t(r) * H + c);
-            const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+        if constexpr (KM > 0) {
+            uint4 v[KM];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = fmaf(wj, bf16_to_f32(x[i] & 0xffffu), acc[2 * i]);
-                acc[2 * i + 1] = fmaf(wj, bf16_to_f32(x[i] >> 16), acc[2 * i + 1]);
+            for (int j = 0; j < KM; ++j)
+                v[j] = rj[j] >= 0 ? *reinterpret_cast<const uint4*>(Yd + size_t(rj[j]) * H + c) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < KM; ++j)
+                if (rj[j] >= 0) add_row(acc, v[j], wj[j]);
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const int r = inv[t * k + j];
+                if (r < 0) continue;
+                add_row(acc, *reinterpret_cast<const uint4*>(Yd + size_t(r) * H + c), w[t * k + j]);
             }
         }
         uint4 o;
@@ -1622,7 +1650,17 @@ int w4a8_moe_align(const int32_t* ids, int T, int k, int E, int32_t* sorted_rows
     int B = R > 0 ? int((R + L - 1) / L) : 0;
     size_t lds = (size_t(E) * (B + 1) + 16) * sizeof(int);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    moe_align_kernel<<<dim3(1), dim3(1024), lds, s>>>(ids, int(R), E, L, B, sorted_rows, offsets, inv);
+    constexpr long long STAGE_MAX = 16384;          // 64 KiB of ids next to <= 48 KiB of counts
+    if (R <= STAGE_MAX) {
+        static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(moe_align_kernel<true>),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                           int((LDS_INTS + 16 + STAGE_MAX) * sizeof(int)));
+        (void)attr;
+        moe_align_kernel<true><<<dim3(1), dim3(1024), lds + size_t(R) * sizeof(int), s>>>(
+            ids, int(R), E, L, B, sorted_rows, offsets, inv);
+    } else {
+        moe_align_kernel<false><<<dim3(1), dim3(1024), lds, s>>>(ids, int(R), E, L, B, sorted_rows, offsets, inv);
+    }
     return launch_status();
 }
 
@@ -1705,8 +1743,13 @@ int w4a8_moe_combine(const void* Yd, const int32_t* inv, const float* w, int T, 
     if (T == 0) return W4A8_OK;
     if (!Yd || !inv || !w || !out) return W4A8_EINVAL;
     if (H % 8 || !aligned16(Yd) || !aligned16(out)) return W4A8_EINVAL;
-    moe_combine_kernel<<<dim3(T), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const uint16_t*>(Yd), inv, w, k, H, static_cast<uint16_t*>(out));
+    const uint16_t* yd = static_cast<const uint16_t*>(Yd);
+    uint16_t* o = static_cast<uint16_t*>(out);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (k <= 8)
+        moe_combine_kernel<8><<<dim3(T), dim3(256), 0, s>>>(yd, inv, w, k, H, o);
+    else
+        moe_combine_kernel<0><<<dim3(T), dim3(256), 0, s>>>(yd, inv, w, k, H, o);
     return launch_status();
 }
 

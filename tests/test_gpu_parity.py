@@ -280,8 +280,10 @@ def _routing(seed, T, E, k, zipf=0.0):
 
 
 @pytest.mark.parametrize("T,E,k,zipf", [(512, 64, 6, 1.1), (64, 256, 8, 0.0), (5, 3, 2, 0.0), (1, 8, 1, 0.0),
-                                        (300, 1024, 4, 0.0)])
+                                        (300, 1024, 4, 0.0), (3000, 64, 8, 1.1), (2048, 8, 8, 0.0)])
 def test_moe_align_exact(T, E, k, zipf):
+    """Stable counting sort against the oracle; the last two cases (24000 and 16384 routed
+    rows) are past and at the size where the ids are staged in LDS."""
     ids, _ = _routing(T + E, T, E, k, zipf)
     rows_ref, off_ref, inv_ref = O.moe_align(ids, E)
     ids_d = torch.from_numpy(ids).to(DEV)
