@@ -165,11 +165,11 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob_dev,
  *   Xq, sx   device int8 [M, K] (16-byte aligned) and float32 [M]: always written with the
  *            activation codes and scales (the caller can reuse them)
  *   Y, ldy, out_dtype, blob_dev, d as in w4a8_gemm.
- * For M * K <= 8192 (M <= 2 at K = 4096), K % 512 == 0, K <= 8192, this is one kernel:
- * each workgroup quantizes the activation rows itself (P2 section 3.3 places the
- * per-token quantization node right before the GEMM; P1 section 8 suggests fusing
- * quantization into the GEMM kernel); otherwise it is w4a8_quant_act followed by
- * w4a8_gemm.  Results are bit-identical either way. */
+ * For M <= 16 and M * K <= 8192 (M <= 2 at K = 4096) this is one kernel: each
+ * workgroup of the decode GEMM quantizes the activation rows itself into its staged
+ * activation tile (P2 section 3.3 places the per-token quantization node right before
+ * the GEMM; P1 section 8 suggests fusing quantization into the GEMM kernel); otherwise
+ * it is w4a8_quant_act followed by w4a8_gemm.  Results are bit-identical either way. */
 int w4a8_linear(const void* X_bf16, int M, int K, int ldx, const void* blob_dev, const w4a8_wdesc* d, void* Y,
                 int ldy, int out_dtype, int8_t* Xq, float* sx, void* stream);
 

@@ -320,14 +320,25 @@ struct DecodeShape {
     static constexpr size_t LDS = LDS_A + LDS_RED;
 };
 
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI>
+// w4a8_linear fuses quantization into the GEMM up to this many activation values.  Every
+// workgroup quantizes all of them, and that redundant work outgrows the launch it saves
+// quickly (measured on the 4096 x 14336 projection: fused beats quantize-then-GEMM at
+// M = 1 and 2, loses at M = 8).
+constexpr size_t FUSED_MAX_ELEMS = 8192;
+
+// FQ (w4a8_linear, M * K <= FUSED_MAX_ELEMS): every workgroup quantizes the bf16 rows itself
+// (the per-token rule of quant_act_kernel, the same device routines) straight into its LDS
+// activation tile; workgroup 0 also exports the codes and row scales.
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI, bool FQ>
 __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     using S = DecodeShape<MS, NT, KW, SBN>;
+    static_assert(!FQ || (MS == 1 && !MOE && MODE == MODE_OUT && !MULTI), "fused quantization: dense, one chunk");
     constexpr int MT = S::MT, NTHR = S::NTHR, CS = S::CS, ROWB = S::ROWB, APT = S::APT;
     // weight superblocks requested before the activation hand-off (the rest right after it)
     constexpr int BE = MS == 2 ? (SBN < 2 ? SBN : 2) : (SBN < 4 ? SBN : 4);
     extern __shared__ __align__(16) uint8_t smem[];
     float* red = reinterpret_cast<float*>(smem + S::LDS_A);
+    uint32_t* rowmax = reinterpret_cast<uint32_t*>(smem + S::LDS);   // FQ: row abs-maxima
     // wave-derived indices are made explicitly uniform so per-slice loops branch on scalars
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = wave % NT, q = wave / NT;
@@ -363,7 +374,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i) {
             sxr[ms][i] = 0.0f;
             const int row = rbeg + ms * 16 + 4 * (lane >> 4) + i;
-            if (MODE != MODE_PARTIALS && q == 0 && row < rend) {
+            if (!FQ && MODE != MODE_PARTIALS && q == 0 && row < rend) {
                 const int srow = (MOE && a.gather) ? a.gather[row] / a.topk : row;
                 sxr[ms][i] = a.sx[srow];
             }
@@ -388,16 +399,27 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         // 1. activation pieces into registers: piece p = tid + i * NTHR is row p / (CS * 8),
         //    16 bytes at column p % (CS * 8); rows past the tile's end are neither loaded nor
         //    written (their MFMA outputs are never stored)
+        //    (FQ: the piece's 16 bfloat16 values, 32 bytes; one piece per thread covers the
+        //    M rows, which the launcher checks: (M - 1) * CS * 8 + nsb * 8 <= NTHR)
+        constexpr int APX = FQ ? 1 : S::APT;
         uint4 xv[S::APT];
+        uint4 xb[FQ ? 1 : 1][2];
 #pragma unroll
-        for (int i = 0; i < S::APT; ++i) {
+        for (int i = 0; i < APX; ++i) {
             const int pc = tid + i * NTHR;
             const int row = pc / (CS * 8), c = pc - row * (CS * 8);
             xv[i] = make_uint4(0, 0, 0, 0);
+            if (FQ) xb[0][0] = xb[0][1] = make_uint4(0, 0, 0, 0);
             if (row < nrows && c < rowpieces) {
                 int src = rbeg + row;
                 if (MOE && a.gather) src = a.gather[src] / a.topk;
-                xv[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(src) * a.K + size_t(cb) * SB_K + c * 16);
+                if (FQ) {
+                    const uint4* xp = reinterpret_cast<const uint4*>(a.X + size_t(src) * a.ldx + c * 16);
+                    xb[0][0] = xp[0];
+                    xb[0][1] = xp[1];
+                } else {
+                    xv[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(src) * a.K + size_t(cb) * SB_K + c * 16);
+                }
             }
         }
         // 2. this wave's group scales and zero points
@@ -421,9 +443,15 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
             }
         }
         // 3. issue fence: all small requests of the workgroup are out before any weight request
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
+        //    (FQ: it also publishes the cleared row maxima)
+        if (FQ) {
+            if (tid < MT) rowmax[tid] = 0u;
+            lds_barrier();
+        } else {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
         // 4. this wave's first BE weight superblocks, in the order they are consumed; the rest
         //    follow once the activations are in LDS, which keeps the activation loads from
         //    queueing behind the whole weight stream
@@ -433,11 +461,63 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
             bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * 1024u));
         }
         // 5. activations into LDS.  Waits are per register, so the weight loads stay in flight.
+        if (FQ) {
+            // row abs-max: a row holds CS * 8 pieces, a multiple of 64, so each wave's 64
+            // pieces of one iteration lie in one row: a wave max and one LDS atomic
 #pragma unroll
-        for (int i = 0; i < S::APT; ++i) {
-            const int pc = tid + i * NTHR;
-            const int row = pc / (CS * 8), c = pc - row * (CS * 8);
-            if (row < nrows && c < rowpieces) *reinterpret_cast<uint4*>(smem + row * ROWB + c * 16) = xv[i];
+            for (int i = 0; i < APX; ++i) {
+                const int pc = tid + i * NTHR;
+                const int row = pc / (CS * 8);
+                uint32_t amax = 0;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const uint32_t wv[4] = {xb[0][hh].x, xb[0][hh].y, xb[0][hh].z, xb[0][hh].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        amax = max(amax, (wv[j] & 0x7fffu) << 16);
+                        amax = max(amax, wv[j] & 0x7fff0000u);
+                    }
+                }
+                amax = wave_max_u32(amax);
+                if (lane == 0 && row < nrows) atomicMax(rowmax + row, amax);
+            }
+            lds_barrier();
+#pragma unroll
+            for (int i = 0; i < APX; ++i) {
+                const int pc = tid + i * NTHR;
+                const int row = pc / (CS * 8), c = pc - row * (CS * 8);
+                if (row >= nrows || c >= rowpieces) continue;
+                const RowScale rs = row_scale(rowmax[row]);
+                uint32_t out[4] = {0, 0, 0, 0};
+                if (rs.finite) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const uint32_t wv[4] = {xb[0][hh].x, xb[0][hh].y, xb[0][hh].z, xb[0][hh].w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int q0 = quant_one(bf16_to_f32(wv[j] & 0xffffu), rs.d, rs.inv, rs.fast);
+                            const int q1 = quant_one(bf16_to_f32(wv[j] >> 16), rs.d, rs.inv, rs.fast);
+                            const uint32_t pair = (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8);
+                            out[hh * 2 + (j >> 1)] |= pair << ((j & 1) * 16);
+                        }
+                    }
+                }
+                *reinterpret_cast<uint4*>(smem + row * ROWB + c * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+            }
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = ms * 16 + 4 * (lane >> 4) + i;
+                    sxr[ms][i] = (q == 0 && row < nrows) ? row_scale<false>(rowmax[row]).s : 0.0f;
+                }
+        } else {
+#pragma unroll
+            for (int i = 0; i < S::APT; ++i) {
+                const int pc = tid + i * NTHR;
+                const int row = pc / (CS * 8), c = pc - row * (CS * 8);
+                if (row < nrows && c < rowpieces) *reinterpret_cast<uint4*>(smem + row * ROWB + c * 16) = xv[i];
+            }
         }
         lds_barrier();
 #pragma unroll
@@ -520,6 +600,18 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) accf[ms][i] += red[(((w - 1) * NT + t) * NV + ms * 4 + i) * 64 + lane];
     }
+    if (FQ && blockIdx.x == 0) {
+        // fused path: workgroup 0 exports the activation codes and row scales (after all of
+        // its weight loads, so no store sits inside the load stream); the threads still
+        // running here are 0 .. NT * 64 - 1 (KW > 1) or all of them
+        const int rp = nsb * 8;                          // 16-byte pieces per row
+        for (int pc = tid; pc < nrows * rp; pc += (KW > 1 ? NT * 64 : NTHR)) {
+            const int row = pc / rp, c = pc - row * rp;
+            *reinterpret_cast<uint4*>(const_cast<int8_t*>(a.Xq) + size_t(rbeg + row) * a.K + c * 16) =
+                *reinterpret_cast<const uint4*>(smem + row * ROWB + c * 16);
+        }
+        if (tid < nrows) const_cast<float*>(a.sx)[rbeg + tid] = row_scale<false>(rowmax[tid]).s;
+    }
     const int col = tile * 16 + (lane & 15);
     if (!tvalid || col >= a.N) return;
 #pragma unroll
@@ -538,7 +630,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// W4A8 GEMM, K-slice decode variant (M <= 32): activations straight into registers
+// W4A8 GEMM, K-slice variant for the grouped (MoE) form: activations straight into registers
 //
 // A workgroup covers T column tiles (16 columns each) over all of K.  Wave w owns the
 // K-slice of superblocks [w * SW, w * SW + SW): it loads its activation fragments once
@@ -551,12 +643,6 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 // Per workgroup: weights T * SW * KW KiB from HBM, activations MT x K from L2, LDS
 // traffic only for the slice reduction (2 * KW * T * 64 * 4 * MS floats).
 // ------------------------------------------------------------------------------------
-// w4a8_linear fuses quantization into the GEMM up to this many activation values, held as
-// up to FQ_PIECES bfloat16 pieces of 8 values per thread.  Every workgroup quantizes all of
-// them, and that redundant work outgrows the launch it saves quickly (measured on the
-// 4096 x 14336 projection: fused beats quantize-then-GEMM at M = 1, loses at M = 8).
-constexpr size_t FUSED_MAX_ELEMS = 8192;
-constexpr int FQ_PIECES = 1;
 
 // TG > 1: the workgroup streams TG groups of T tiles one after another, the loads of two
 // groups in flight (double-buffered registers), so each workgroup's fixed costs (activation
@@ -566,8 +652,7 @@ struct KsliceShape {
     static constexpr int MT = 16 * MS;
     static constexpr int NV = 4 * MS;                          // accumulators per lane per tile
     static constexpr int TT = T * TG;                          // tiles per workgroup
-    // slice partials, then 32 row scales and 32 row abs-maxima; the fused path adds its
-    // quantized rows [rows][K + 16] after that
+    // slice partials, then 32 row scales (and 32 floats spare)
     static constexpr size_t lds(int kw) { return size_t(kw) * TT * 64 * NV * 4 + 64 * 4; }
 };
 
@@ -576,10 +661,9 @@ struct KsliceShape {
 // weights are streamed once per column tile instead of once per row tile.
 constexpr int MOE_KSLICE_ROWS = 128;
 
-template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ, int TG, bool RL>
+template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, int TG, bool RL>
 __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     using S = KsliceShape<MS, T, TG>;
-    static_assert(!FQ || (MS == 1 && !MOE && MODE == MODE_OUT && TG == 1), "fused quantization: dense 16-row tiles");
     static_assert(!RL || (MOE && MODE == MODE_OUT && TG == 1), "row loop: grouped form, one tile group");
     constexpr int NV = S::NV, TT = S::TT;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -616,38 +700,17 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     float sxv = 0.0f;
     auto load_sx = [&]() __attribute__((always_inline)) {
         sxv = 0.0f;
-        if (!FQ && MODE != MODE_PARTIALS && tid < S::MT && tid < nrows)
+        if (MODE != MODE_PARTIALS && tid < S::MT && tid < nrows)
             sxv = a.sx[(MOE && a.gather) ? a.gather[rbeg + tid] / a.topk : rbeg + tid];
     };
     load_sx();
-
-    // fused path: LDS also holds the row abs-maxima and the quantized rows [nrows][K + 16]
-    uint32_t* rowmax = reinterpret_cast<uint32_t*>(sxs + 32);
-    int8_t* xst = reinterpret_cast<int8_t*>(sxs + 64);
-    const int xstride = a.K + 16;
-    // fused: piece p = tid + i * blockDim (8 bf16 values); a row holds K / 8 pieces, a
-    // multiple of 64, so each wave's 64 pieces of one iteration lie in one row
-    uint4 xv[FQ ? FQ_PIECES : 1];
-    const int xpieces = a.K / 8;
-    if (FQ) {
-        if (tid < S::MT) rowmax[tid] = 0u;
-#pragma unroll
-        for (int i = 0; i < FQ_PIECES; ++i) {
-            const int pc = tid + i * int(blockDim.x);
-            xv[i] = make_uint4(0, 0, 0, 0);
-            if (pc < nrows * xpieces) {
-                const int row = pc / xpieces, c = pc - row * xpieces;
-                xv[i] = *reinterpret_cast<const uint4*>(a.X + size_t(rbeg + row) * a.ldx + c * 8);
-            }
-        }
-    }
 
     // 1. activation fragments of this wave's K-slice: lane l holds row ms * 16 + l % 16 and
     //    the 16 K-values [16 * (l / 16), +16) of each 64-deep half (the MFMA A operand)
     v4i A[SW][2][MS];
     auto load_a = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int ms = 0; ms < MS && !FQ; ++ms) {
+        for (int ms = 0; ms < MS; ++ms) {
             const int row = ms * 16 + (lane & 15);
             const bool rv = row < nrows;
             const int8_t* xrow = a.Xq;
@@ -702,7 +765,6 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     };
     load_meta(0);
     // issue fence: the small requests of every wave go out before any weight request
-    // (it also publishes the fused path's cleared row maxima)
     lds_barrier();
     // 3. the weight stream: group 0, then group 1 (its scales first)
     load_w(0);
@@ -711,56 +773,6 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
         load_w(1);
     }
     asm volatile("" ::: "memory");                      // keep the whole stream issued here
-    if (FQ) {
-        // per-token quantization of the rows, exactly as quant_act_kernel: a wave max and
-        // one LDS atomic per wave and piece give the row abs-max
-#pragma unroll
-        for (int i = 0; i < FQ_PIECES; ++i) {
-            const int pc = tid + i * int(blockDim.x);
-            const uint32_t wv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-            uint32_t amax = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                amax = max(amax, (wv[j] & 0x7fffu) << 16);
-                amax = max(amax, wv[j] & 0x7fff0000u);
-            }
-            amax = wave_max_u32(amax);
-            if (lane == 0 && pc < nrows * xpieces) atomicMax(rowmax + pc / xpieces, amax);
-        }
-        lds_barrier();
-#pragma unroll
-        for (int i = 0; i < FQ_PIECES; ++i) {
-            __builtin_amdgcn_sched_barrier(0);           // one piece at a time: bounded live range
-            const int pc = tid + i * int(blockDim.x);
-            if (pc >= nrows * xpieces) continue;
-            const int row = pc / xpieces, c = pc - row * xpieces;
-            const uint32_t wv[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-            const RowScale rs = row_scale(rowmax[row]);
-            uint32_t out[2] = {0, 0};
-            if (rs.finite) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int q0 = quant_one(bf16_to_f32(wv[j] & 0xffffu), rs.d, rs.inv, rs.fast);
-                    const int q1 = quant_one(bf16_to_f32(wv[j] >> 16), rs.d, rs.inv, rs.fast);
-                    const uint32_t pair = (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8);
-                    out[j >> 1] |= pair << ((j & 1) * 16);
-                }
-            }
-            *reinterpret_cast<uint2*>(xst + row * xstride + c * 8) = make_uint2(out[0], out[1]);
-        }
-        if (tid < nrows) sxv = row_scale<false>(rowmax[tid]).s;
-        lds_barrier();
-        const int row16 = lane & 15;
-#pragma unroll
-        for (int s = 0; s < SW; ++s)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                A[s][h][0] = v4i{0, 0, 0, 0};
-                if (row16 < nrows && sb0 + s < nsb)
-                    A[s][h][0] = *reinterpret_cast<const v4i*>(xst + row16 * xstride + (sb0 + s) * SB_K + h * 64 +
-                                                               16 * (lane >> 4));
-            }
-    }
     // 4. per tile: MFMAs over the slice, per-group epilogue, partial to LDS; after each tile
     //    group, the group two ahead is requested into the registers it used
     const v4i zero4 = {0, 0, 0, 0};
@@ -864,16 +876,6 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
             __syncthreads();
             reduce_store();
         }
-    }
-    if (FQ && blockIdx.x == 0) {
-        // fused path: workgroup 0 exports the activation codes and scales (after all of its
-        // weight loads, so no store sits inside the load stream)
-        for (int pc = tid; pc < nrows * xpieces; pc += int(blockDim.x)) {
-            const int row = pc / xpieces, c = pc - row * xpieces;
-            *reinterpret_cast<uint2*>(const_cast<int8_t*>(a.Xq) + size_t(rbeg + row) * a.K + c * 8) =
-                *reinterpret_cast<const uint2*>(xst + row * xstride + c * 8);
-        }
-        if (tid < nrows) const_cast<float*>(a.sx)[rbeg + tid] = sxs[tid];
     }
 }
 
@@ -1323,14 +1325,24 @@ static DecodeCfg decode_cfg(int K, int mt) {
     return c;
 }
 
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI = false>
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI = false, bool FQ = false>
 static void launch_decode_t(const GemmArgs& a, dim3 grid, hipStream_t s) {
     using S = DecodeShape<MS, NT, KW, SBN>;
-    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, MULTI>;
+    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, MULTI, FQ>;
+    constexpr size_t lds = S::LDS + (FQ ? 128 : 0);           // FQ: row abs-maxima
     static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(S::LDS));
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     (void)attr;
-    kern<<<grid, dim3(S::NTHR), S::LDS, s>>>(a);
+    kern<<<grid, dim3(S::NTHR), lds, s>>>(a);
+}
+
+// Fused quantization + GEMM on the chunked kernel (dense, 16-row tile, K in one chunk).
+template <int GPS, bool ASYM>
+static void launch_decode_fused(const GemmArgs& a, const DecodeCfg& c, dim3 grid, hipStream_t s) {
+    if (c.kw == 8) launch_decode_t<1, 2, 8, 8, GPS, ASYM, MODE_OUT, false, false, true>(a, grid, s);
+    else if (c.sbn == 2) launch_decode_t<1, 4, 4, 2, GPS, ASYM, MODE_OUT, false, false, true>(a, grid, s);
+    else if (c.sbn == 4) launch_decode_t<1, 4, 4, 4, GPS, ASYM, MODE_OUT, false, false, true>(a, grid, s);
+    else launch_decode_t<1, 4, 4, 8, GPS, ASYM, MODE_OUT, false, false, true>(a, grid, s);
 }
 
 template <int MS, int GPS, bool ASYM, int MODE, bool MOE>
@@ -1397,26 +1409,18 @@ static bool kslice_cfg(int K, int mt, KsliceCfg* c, bool moe = false) {
     return true;
 }
 
-// Dense GEMMs use the K-slice kernel exactly where w4a8_linear can fuse the quantization
-// (so fused and unfused results are bit-identical); above that size the chunked kernel,
-// whose activation tile is staged once per workgroup, streams faster.
-static bool dense_kslice(int M, int K, KsliceCfg* c) {
-    return size_t(M) * K <= FUSED_MAX_ELEMS && kslice_cfg(K, 16, c);
-}
 
-template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, bool FQ = false, int TG = 1,
-          bool RL = false>
+template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, int TG = 1, bool RL = false>
 static void launch_kslice_t(const GemmArgs& a, int kw, int ytiles, hipStream_t s) {
     using S = KsliceShape<MS, T, TG>;
     static_assert(S::lds(16) <= 160 * 1024, "slice partials exceed LDS");
-    auto kern = gemm_kslice_kernel<MS, T, SW, GPS, ASYM, MODE, MOE, FQ, TG, RL>;
-    constexpr size_t fq_max = FQ ? FUSED_MAX_ELEMS + 16 * 16 : 0;   // quantized rows, padded
+    auto kern = gemm_kslice_kernel<MS, T, SW, GPS, ASYM, MODE, MOE, TG, RL>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       int(S::lds(16) + fq_max));
+                                                       int(S::lds(16)));
     (void)attr;
     const int ntiles = (a.N + 15) / 16;
-    const size_t lds = S::lds(kw) + (FQ ? size_t(a.M) * (a.K + 16) : 0);
+    const size_t lds = S::lds(kw);
     kern<<<dim3((ntiles + S::TT - 1) / S::TT, ytiles), dim3(64 * kw), lds, s>>>(a);
 }
 
@@ -1426,7 +1430,7 @@ static void launch_kslice_shape(const GemmArgs& a, const KsliceCfg& c, int ytile
     if (c.sw == 1) {
         if constexpr (MOE && MS == 2 && MODE == MODE_OUT) {
             if (c.rl) {
-                launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE, false, 1, true>(a, c.kw, ytiles, s);
+                launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE, 1, true>(a, c.kw, ytiles, s);
                 return;
             }
         }
@@ -1434,7 +1438,7 @@ static void launch_kslice_shape(const GemmArgs& a, const KsliceCfg& c, int ytile
     } else if (c.sw == 2) {
         launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
     } else if constexpr (MS == 1) {
-        if constexpr (MOE) launch_kslice_t<MS, 1, 4, GPS, ASYM, MODE, MOE, false, MOE_KSLICE_TG>(a, c.kw, ytiles, s);
+        if constexpr (MOE) launch_kslice_t<MS, 1, 4, GPS, ASYM, MODE, MOE, MOE_KSLICE_TG>(a, c.kw, ytiles, s);
         else launch_kslice_t<MS, 2, 4, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
     }
 }
@@ -1559,12 +1563,6 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
         return launch_status();
     }
     const int mt = dense_mt(M);
-    KsliceCfg kc;
-    if (dense_kslice(M, L.K, &kc)) {
-        launch_kslice<MODE_OUT, false>(a, kc, mt / 16, SB_K / d->group_size, d->asymmetric, (M + mt - 1) / mt,
-                                       static_cast<hipStream_t>(stream));
-        return launch_status();
-    }
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
     launch_decode<MODE_OUT, false>(a, c, SB_K / d->group_size, d->asymmetric, grid, static_cast<hipStream_t>(stream));
@@ -1580,11 +1578,13 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
     if (!X || !blob || !Y || !Xq || !sx || ldy < d->N || ldx < K) return W4A8_EINVAL;
     if (ldx % 8 || !aligned16(X) || !aligned16(Xq) || !aligned16(blob)) return W4A8_EINVAL;
     const Layout L = layout_of(d);
-    // Fused path: the unfused K-slice kernel's workgroup layout and summation order, so the
+    // Fused path: the unfused decode kernel's workgroup layout and summation order, so the
     // result is bit-identical.  Each workgroup quantizes all M x K activations itself, so
     // fusing pays off only while that redundant work is small next to the launch it saves.
-    KsliceCfg kc;
-    if (L.K % 512 == 0 && dense_kslice(M, L.K, &kc) && M * (L.K / 8) <= FQ_PIECES * 64 * kc.kw) {
+    const DecodeCfg fc = decode_cfg(L.K, 16);
+    const int fcs = fc.kw * fc.sbn;                      // superblocks per chunk
+    if (M <= 16 && size_t(M) * L.K <= FUSED_MAX_ELEMS && L.K / SB_K <= fcs &&
+        (M - 1) * fcs * 8 + (L.K / SB_K) * 8 <= 64 * fc.nt * fc.kw) {
         GemmArgs a = make_args(L, Xq, sx, M, blob);
         a.X = static_cast<const uint16_t*>(X);
         a.ldx = ldx;
@@ -1592,16 +1592,13 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
         a.ldy = ldy;
         a.out_f32 = out_dtype == W4A8_OUT_F32;
         hipStream_t s = static_cast<hipStream_t>(stream);
+        const dim3 grid = decode_grid(L, fc, 1);
         const int gps = SB_K / d->group_size;
-        const bool asym = d->asymmetric;
-#define W4A8_FQ(T_, SW_, GPS_, ASYM_) launch_kslice_t<1, T_, SW_, GPS_, ASYM_, MODE_OUT, false, true>(a, kc.kw, 1, s)
-#define W4A8_FQS(T_, SW_) do { if (gps == 1) { if (asym) W4A8_FQ(T_, SW_, 1, true); else W4A8_FQ(T_, SW_, 1, false); } \
-                               else { if (asym) W4A8_FQ(T_, SW_, 2, true); else W4A8_FQ(T_, SW_, 2, false); } } while (0)
-        if (kc.sw == 1) W4A8_FQS(4, 1);
-        else if (kc.sw == 2) W4A8_FQS(4, 2);
-        else W4A8_FQS(2, 4);
-#undef W4A8_FQS
-#undef W4A8_FQ
+        if (gps == 1) {
+            if (d->asymmetric) launch_decode_fused<1, true>(a, fc, grid, s); else launch_decode_fused<1, false>(a, fc, grid, s);
+        } else {
+            if (d->asymmetric) launch_decode_fused<2, true>(a, fc, grid, s); else launch_decode_fused<2, false>(a, fc, grid, s);
+        }
         return launch_status();
     }
     if ((st = w4a8_quant_act(X, M, K, ldx, Xq, sx, stream))) return st;
@@ -1623,12 +1620,6 @@ int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob, const w4a8_wde
         return launch_status();
     }
     const int mt = dense_mt(M);
-    KsliceCfg kc;
-    if (dense_kslice(M, L.K, &kc)) {
-        launch_kslice<MODE_PARTIALS, false>(a, kc, mt / 16, SB_K / d->group_size, d->asymmetric, (M + mt - 1) / mt,
-                                            static_cast<hipStream_t>(stream));
-        return launch_status();
-    }
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
     launch_decode<MODE_PARTIALS, false>(a, c, SB_K / d->group_size, d->asymmetric, grid,
@@ -1825,16 +1816,11 @@ const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
     if (M >= PREFILL_MIN_M)
         return asym ? (g64 ? "w4a8_prefill_asym_g64" : "w4a8_prefill_asym_g128")
                     : (g64 ? "w4a8_prefill_sym_g64" : "w4a8_prefill_sym_g128");
-    // one name per (kernel family, row tile, format)
-    static const char* const names[2][2][2][2] = {
-        {{{"w4a8_decode_m16_sym_g128", "w4a8_decode_m16_sym_g64"}, {"w4a8_decode_m16_asym_g128", "w4a8_decode_m16_asym_g64"}},
-         {{"w4a8_decode_m32_sym_g128", "w4a8_decode_m32_sym_g64"}, {"w4a8_decode_m32_asym_g128", "w4a8_decode_m32_asym_g64"}}},
-        {{{"w4a8_kslice_m16_sym_g128", "w4a8_kslice_m16_sym_g64"}, {"w4a8_kslice_m16_asym_g128", "w4a8_kslice_m16_asym_g64"}},
-         {{"w4a8_kslice_m32_sym_g128", "w4a8_kslice_m32_sym_g64"}, {"w4a8_kslice_m32_asym_g128", "w4a8_kslice_m32_asym_g64"}}}};
-    const int mt = dense_mt(M);
-    KsliceCfg kc;
-    const int fam = dense_kslice(M, d->K, &kc) ? 1 : 0;
-    return names[fam][mt == 32][asym][g64];
+    // one name per (row tile, format)
+    static const char* const names[2][2][2] = {
+        {{"w4a8_decode_m16_sym_g128", "w4a8_decode_m16_sym_g64"}, {"w4a8_decode_m16_asym_g128", "w4a8_decode_m16_asym_g64"}},
+        {{"w4a8_decode_m32_sym_g128", "w4a8_decode_m32_sym_g64"}, {"w4a8_decode_m32_asym_g128", "w4a8_decode_m32_asym_g64"}}};
+    return names[dense_mt(M) == 32][asym][g64];
 }
 
 }  // extern "C"

@@ -100,8 +100,9 @@ def test_quant_act_near_ties_take_the_exact_division():
     (20, 256, 33, 64, False),
     (1, 4096, 256, 128, False),
     (64, 7168, 64, 64, True),                  # MoE decode expert shape (slice of N)
-    # one case per decode kernel variant: chunked 32-row tile (one chunk, several chunks),
-    # chunked 16-row long-K tile (several chunks), K-slice (2 and 4 superblocks per wave)
+    # one case per decode kernel shape: 32-row tile (one chunk, several chunks), 16-row
+    # long-K tile (several chunks), 16-row tiles at M * K <= 8192 (one chunk of 8 and 64
+    # superblocks)
     (32, 4096, 512, 128, False),
     (32, 8192, 64, 128, True),
     (12, 14336, 48, 128, False),
@@ -196,10 +197,11 @@ def test_gemm_zero_and_nan_rows():
                                           (16, 4096, 1024, 128, True), (5, 512, 40, 64, True),
                                           (3, 1024, 33, 128, False), (20, 256, 64, 64, True),
                                           (2, 7168, 64, 64, True), (2, 4096, 1024, 64, True),
-                                          (4, 2048, 96, 128, False)])
+                                          (4, 2048, 96, 128, False), (1, 7168, 96, 64, True),
+                                          (1, 8192, 80, 128, False), (16, 512, 72, 128, True)])
 def test_linear_matches_quant_then_gemm(M, K, N, g, asym):
-    """w4a8_linear (one kernel for M * K <= 8192) equals quant_act followed by gemm bit for bit,
-    and writes the same activation codes and scales."""
+    """w4a8_linear (one kernel for M <= 16 and M * K <= 8192) equals quant_act followed by gemm
+    bit for bit, and writes the same activation codes and scales."""
     Xb = W.random_activations(M * 3 + K + N, M, K, outlier_cols=2, outlier_scale=40.0)
     x = W.bf16_values(Xb)
     if M > 2:
