@@ -1398,6 +1398,7 @@ static bool kslice_cfg(int K, int mt, KsliceCfg* c, bool moe = false) {
     } else if (nsb <= 32) {
         c->t = 4;
         c->sw = 2;
+        c->rl = moe && mt == 16;
     } else if (nsb <= 64 && mt == 16) {   // 32-row tiles at this depth would not fit in registers
         c->t = moe ? 1 : 2;
         c->sw = 4;
@@ -1436,6 +1437,12 @@ static void launch_kslice_shape(const GemmArgs& a, const KsliceCfg& c, int ytile
         }
         launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
     } else if (c.sw == 2) {
+        if constexpr (MOE && MS == 1 && MODE == MODE_OUT) {
+            if (c.rl) {
+                launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE, 1, true>(a, c.kw, ytiles, s);
+                return;
+            }
+        }
         launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
     } else if constexpr (MS == 1) {
         if constexpr (MOE) launch_kslice_t<MS, 1, 4, GPS, ASYM, MODE, MOE, MOE_KSLICE_TG>(a, c.kw, ytiles, s);
@@ -1681,11 +1688,15 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
     }
     // slots bound sum_e ceil(rows_e / per) over the experts; surplus workgroups exit at once
     const int slots = rows / mt + std::min(E, rows) + 1;
+    // 2048 < K <= 4096: 16-row tiles run in a row loop (32-row tiles would not leave the
+    // registers for it), so each expert's weights are read once per column tile
+    const int nsb = L.K / SB_K;
+    const int kmt = (nsb > 16 && nsb <= 32) ? 16 : mt;
     KsliceCfg kc;
-    if (kslice_cfg(L.K, mt, &kc, true)) {
+    if (kslice_cfg(L.K, kmt, &kc, true)) {
         // row loop: a workgroup runs up to MOE_KSLICE_ROWS rows of its expert
-        const int kslots = kc.rl ? rows / MOE_KSLICE_ROWS + std::min(E, rows) + 1 : slots;
-        launch_kslice<MODE_OUT, true>(a, kc, mt / 16, SB_K / d->group_size, d->asymmetric, kslots, s);
+        const int kslots = kc.rl ? rows / MOE_KSLICE_ROWS + std::min(E, rows) + 1 : rows / kmt + std::min(E, rows) + 1;
+        launch_kslice<MODE_OUT, true>(a, kc, kmt / 16, SB_K / d->group_size, d->asymmetric, kslots, s);
         return launch_status();
     }
     const DecodeCfg c = decode_cfg(L.K, mt);
