@@ -1383,12 +1383,19 @@ struct KsliceCfg {
 // there one workgroup fills a compute unit (its registers), and with a single 32-column
 // group it would spend most of its life on fixed costs between short weight streams.
 constexpr int MOE_KSLICE_TG = 8;
+// K <= 2048 at 16-row tiles: 8 waves of two superblocks, 4 groups of 2 tiles, so that two
+// workgroups (registers, 64 KiB of slice partials each) share a compute unit
+constexpr int MOE_KSLICE_TG_SHORT = 4;
 
 static bool kslice_cfg(int K, int mt, KsliceCfg* c, bool moe = false) {
     const int nsb = K / SB_K;
     c->tg = 1;
     c->rl = false;
-    if (nsb <= 16) {
+    if (nsb <= 16 && moe && mt == 16 && nsb > 2) {
+        c->t = 2;
+        c->sw = 2;
+        c->tg = MOE_KSLICE_TG_SHORT;
+    } else if (nsb <= 16) {
         c->t = 4;
         c->sw = 1;
         // measured: worth it at 32-row tiles (an expert's weights are read once instead of
@@ -1437,6 +1444,12 @@ static void launch_kslice_shape(const GemmArgs& a, const KsliceCfg& c, int ytile
         }
         launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
     } else if (c.sw == 2) {
+        if constexpr (MOE && MS == 1) {
+            if (c.tg == MOE_KSLICE_TG_SHORT) {
+                launch_kslice_t<MS, 2, 2, GPS, ASYM, MODE, MOE, MOE_KSLICE_TG_SHORT>(a, c.kw, ytiles, s);
+                return;
+            }
+        }
         if constexpr (MOE && MS == 1 && MODE == MODE_OUT) {
             if (c.rl) {
                 launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE, 1, true>(a, c.kw, ytiles, s);
