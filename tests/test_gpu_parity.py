@@ -198,7 +198,8 @@ def test_gemm_zero_and_nan_rows():
                                           (3, 1024, 33, 128, False), (20, 256, 64, 64, True),
                                           (2, 7168, 64, 64, True), (2, 4096, 1024, 64, True),
                                           (4, 2048, 96, 128, False), (1, 7168, 96, 64, True),
-                                          (1, 8192, 80, 128, False), (16, 512, 72, 128, True)])
+                                          (1, 8192, 80, 128, False), (16, 512, 72, 128, True),
+                                          (7, 384, 40, 128, True), (16, 128, 24, 64, False)])
 def test_linear_matches_quant_then_gemm(M, K, N, g, asym):
     """w4a8_linear (one kernel for M <= 16 and M * K <= 8192) equals quant_act followed by gemm
     bit for bit, and writes the same activation codes and scales."""
