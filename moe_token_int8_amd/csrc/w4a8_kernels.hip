@@ -1372,7 +1372,7 @@ static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool a
 }
 
 
-// K-slice decode kernel: T tiles per group, TG groups per workgroup, SW superblocks per
+// K-slice kernel (grouped form): T tiles per group, TG groups per workgroup, SW superblocks per
 // wave, KW waves.
 struct KsliceCfg {
     int t, sw, kw, tg;
