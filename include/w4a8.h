@@ -156,7 +156,8 @@ int w4a8_quant_act(const void* X_bf16, int M, int K, int ldx, int8_t* Xq, float*
  * partial sum is scaled by its float32 weight scale into a float32 accumulator, the
  * row scale is applied last, then the bfloat16 cast rounds to nearest even.  No
  * dequantized weight is ever written to memory (P1 section 4.4 step 4; P5 section 3.2).
- * M == 0 is a no-op. */
+ * M == 0 is a no-op.  EINVAL for M > 32 with 256 * K >= 2^31 (the 256-row activation tile
+ * is addressed with 32-bit offsets). */
 int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob_dev,
               const w4a8_wdesc* d, void* Y, int ldy, int out_dtype, void* stream);
 
@@ -176,7 +177,7 @@ int w4a8_linear(const void* X_bf16, int M, int K, int ldx, const void* blob_dev,
 /* Test export of the same main loop: INT32 per-group partial sums
  * P[m, n, i] = sum_{k in group i} Xq[m, k] (q[k, n] - z[i, n]) written to device
  * int32 [M, N, K/g].  (P3 "Correctness contract" item 3: the accumulator covers the
- * reduction: |P| <= g * 127 * 15 < 2^31.) */
+ * reduction: |P| <= g * 127 * 15 < 2^31.)  Same EINVAL size limit as w4a8_gemm. */
 int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob_dev, const w4a8_wdesc* d,
                        int32_t* P, void* stream);
 
@@ -201,7 +202,9 @@ int w4a8_moe_align(const int32_t* topk_ids, int T, int k, int E, int32_t* sorted
  *   rows           T*k, total rows (= off[E])
  *   blobs_dev      device, E blobs of desc `d`, expert e at blobs_dev + e * expert_stride
  *   Y              device [rows, N] bfloat16 or float32, dense
- * Experts with no rows read no weights. */
+ * Experts with no rows read no weights.  EINVAL when rows >= 128 and the activation rows a
+ * gather may name (ceil(rows / k) with gather, else rows) times K reach 2^31 (32-bit
+ * offsets of the kernel for experts with many rows). */
 int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int k,
                   const int32_t* expert_offsets, int E, int rows, const void* blobs_dev,
                   size_t expert_stride, const w4a8_wdesc* d, void* Y, int out_dtype,

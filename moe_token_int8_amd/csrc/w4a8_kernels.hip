@@ -973,30 +973,46 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     const int b_tile = min(t0 + wave, ntl16 - 1);
     const int st_q4 = lane >> 4, st_c = lane & 15;
     const int nmeta_s = 8 * GPS * 4;                     // 16-byte scale pieces
-    // MOE: the gathered source rows of this thread's activation pieces, looked up once
-    int mrow[MOE ? 4 : 1];
+    // Activation and code loads go through buffer resources.  Each lane's offset is fixed for
+    // the whole K loop and the superblock advances only the scalar offset, so the loop spends
+    // no vector instructions on addresses, and the loads are unconditional, so the compiler
+    // can count them and wait for one register set only.  Rows past the tile's end load the
+    // tile's last row (their outputs are never stored).  Offsets are 32-bit: the dense form's
+    // base is the tile's first row and the codes' base is the wave's column tile; the grouped
+    // form's gathered rows are offsets from Xq (the launcher checks that they fit).
+    const int8_t* xbase = MOE ? a.Xq : a.Xq + size_t(m0) * a.K;
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(xbase), 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(codes + size_t(__builtin_amdgcn_readfirstlane(b_tile)) * nsb * 1024), 0, 0x7fffffff,
+        0x00020000);
+    int aoff[4];
 #pragma unroll
-    for (int i = 0; i < (MOE ? 4 : 1); ++i) mrow[i] = MOE ? src_row((tid + i * PF_THREADS) >> 3) : 0;
+    for (int i = 0; i < 4; ++i) {
+        const int p = tid + i * PF_THREADS;
+        const int row = p >> 3, c = p & 7;
+        aoff[i] = (MOE ? src_row(row) : min(m0 + row, mend - 1) - m0) * a.K + c * 16;
+    }
     auto gload = [&](PfRegs& r, int sb) {
+        sb = __builtin_amdgcn_readfirstlane(sb);         // uniform: the scalar offsets below
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int p = tid + i * PF_THREADS;
-            const int row = p >> 3, c = p & 7;
-            r.a[i] = make_uint4(0, 0, 0, 0);
-            if (m0 + row < mend) {
-                const int srow = MOE ? mrow[MOE ? i : 0] : m0 + row;
-                r.a[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(srow) * a.K + size_t(sb) * SB_K + c * 16);
-            }
+            const v4i t = __builtin_amdgcn_raw_buffer_load_b128(xr, aoff[i], sb * SB_K, 0);
+            r.a[i] = make_uint4(uint32_t(t.x), uint32_t(t.y), uint32_t(t.z), uint32_t(t.w));
         }
-        r.b = *reinterpret_cast<const uint4*>(codes + (size_t(b_tile) * nsb + sb) * 1024 + lane * 16);
+        {
+            const v4i t = __builtin_amdgcn_raw_buffer_load_b128(cr, lane * 16, sb * 1024, 0);
+            r.b = make_uint4(uint32_t(t.x), uint32_t(t.y), uint32_t(t.z), uint32_t(t.w));
+        }
         if (ASYM) {
             r.z = 0;
 #pragma unroll
             for (int gi = 0; gi < GPS; ++gi)
                 r.z |= uint32_t(zeros_b[(size_t(b_tile) * a.G + size_t(sb) * GPS + gi) * 16 + st_c]) << (8 * gi);
         }
-        if (tid < nmeta_s) {
-            const int tl = tid / (GPS * 4), gi = (tid / 4) % GPS, q4 = tid % 4;
+        {   // every thread loads a piece (threads past nmeta_s repeat one and never store it)
+            const int mt = tid % nmeta_s;
+            const int tl = mt / (GPS * 4), gi = (mt / 4) % GPS, q4 = mt % 4;
             const int tile = min(t0 + tl, ntl16 - 1);
             r.m = *reinterpret_cast<const uint4*>(scales_b + ((size_t(tile) * a.G + size_t(sb) * GPS + gi) * 16 + q4 * 4) * 4);
         }
@@ -1103,22 +1119,23 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
 
     // pipeline: register set s%2 holds the loads of superblock s; stage s%2 of LDS holds
     // superblock s while it is computed
+    // (prefetches past the last superblock reload the last one and are never stored)
     PfRegs R0, R1;
     gload(R0, 0);
-    if (nsb > 1) gload(R1, 1);
+    gload(R1, min(1, nsb - 1));
     lstore(R0, 0);
-    if (nsb > 2) gload(R0, 2);
+    gload(R0, min(2, nsb - 1));
     __syncthreads();
     for (int kb = 0; kb < nsb; kb += 2) {
         // even superblock kb: stage 0; R1 holds kb+1, R0 holds kb+2
         if (kb + 1 < nsb) lstore(R1, 1);
-        if (kb + 3 < nsb) gload(R1, kb + 3);
+        gload(R1, min(kb + 3, nsb - 1));
         compute(0, kb);
         __syncthreads();
         if (kb + 1 >= nsb) break;
         // odd superblock kb+1: stage 1; R0 holds kb+2, R1 holds kb+3
         if (kb + 2 < nsb) lstore(R0, 0);
-        if (kb + 4 < nsb) gload(R0, kb + 4);
+        gload(R0, min(kb + 4, nsb - 1));
         compute(1, kb + 1);
         __syncthreads();
     }
@@ -1505,6 +1522,10 @@ constexpr int MOE_PREFILL_MIN_ROWS = 128;
 // Dense GEMMs with more rows than this use the prefill kernel.
 constexpr int PREFILL_MIN_M = 33;
 
+// The prefill kernel reads activations through 32-bit buffer offsets: from the row tile's first
+// row (dense form: PF_BM rows) or from Xq itself (grouped form: every row a gather may name).
+static bool prefill_offsets_fit(int K, size_t rows) { return rows * size_t(K) < (size_t(1) << 31); }
+
 static dim3 decode_grid(const Layout& L, const DecodeCfg& c, int ytiles) {
     const int ntiles = L.Np / 16;
     return dim3((ntiles + c.nt - 1) / c.nt, ytiles);
@@ -1579,6 +1600,7 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
     a.ldy = ldy;
     a.out_f32 = out_dtype == W4A8_OUT_F32;
     if (M >= PREFILL_MIN_M) {
+        if (!prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
         launch_prefill<MODE_OUT>(a, SB_K / d->group_size, d->asymmetric, static_cast<hipStream_t>(stream));
         return launch_status();
     }
@@ -1636,6 +1658,7 @@ int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob, const w4a8_wde
     GemmArgs a = make_args(L, Xq, nullptr, M, blob);
     a.P = P;
     if (M >= PREFILL_MIN_M) {
+        if (!prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
         launch_prefill<MODE_PARTIALS>(a, SB_K / d->group_size, d->asymmetric, static_cast<hipStream_t>(stream));
         return launch_status();
     }
@@ -1693,6 +1716,7 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
     if (rows >= MOE_PREFILL_MIN_ROWS) {
         // experts with many rows: prefill tiles; slots bound sum_e ceil(rows_e / 256) over
         // experts with rows_e >= 128 (surplus workgroups find no tile and exit)
+        if (!prefill_offsets_fit(L.K, gather ? (size_t(rows) + k - 1) / k : size_t(rows))) return W4A8_EINVAL;
         a.moe_lo = MOE_PREFILL_MIN_ROWS;
         launch_prefill<MODE_OUT, true>(a, SB_K / d->group_size, d->asymmetric, s,
                                        rows / PF_BM + rows / MOE_PREFILL_MIN_ROWS + 1);

@@ -215,6 +215,23 @@ def test_gpu_entry_points_validate_before_launch():
     assert L.w4a8_moe_workspace_size(0, 0, 1, 1, 1) == 0
 
 
+def test_prefill_offset_limits_host():
+    """The prefill kernel addresses activations with 32-bit offsets: a 256-row tile of K >= 2^23
+    (dense), or gathered rows times K >= 2^31 (grouped form), is rejected before any launch."""
+    lib = L.lib()
+    fake = 0x10000
+    E = L.W4A8_EINVAL
+    big = L.desc(1 << 23, 16, 128, False)          # 256 * K = 2^31
+    assert L.w4a8_kernel_name(big, 33) == "w4a8_prefill_sym_g128"   # a valid desc otherwise
+    assert lib.w4a8_gemm(fake, fake, 33, fake, ctypes.byref(big), fake, 16, 0, None) == E
+    assert lib.w4a8_gemm_partials(fake, 33, fake, ctypes.byref(big), fake, None) == E
+    d = L.desc(4096, 64, 128, False)
+    rows = (1 << 31) // 4096                       # ceil(rows / k) * K = 2^31 with k = 1
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 1, fake, 1, rows, fake, 0, ctypes.byref(d), fake, 0, None) == E
+    # without gather every row counts
+    assert lib.w4a8_moe_gemm(fake, fake, None, 1, fake, 1, rows, fake, 0, ctypes.byref(d), fake, 0, None) == E
+
+
 def test_kernel_names_resolve():
     for M, g, asym in [(1, 128, False), (32, 128, False), (8, 64, True), (4096, 128, True)]:
         name = L.w4a8_kernel_name(L.desc(4096, 14336, g, asym), M)
