@@ -23,7 +23,9 @@ Pins (each function is checked against something other than itself in
   quant_act         P5 worked INT8 example and outlier example (tests/golden),
                     round-trip bound, zero row, brute-force fp32 per element.
   quant_weight      P3 reference-function invariants and its example, P2 range
-                    example (asymmetric), bounds, zero groups, tiling error.
+                    example (asymmetric), bounds, zero groups, tiling error; 8-bit
+                    codes: the same invariants with qmax = 127 and an exact round
+                    trip of weights on a power-of-two grid.
   gemm_partials     brute-force integer triple loop; zero-point expansion of
                     P5 section 7; integer matmul when K equals the group.
   gemm              brute-force fp64 dequantise-then-matmul; per-token x
@@ -108,12 +110,14 @@ def dequant_act(q, s):
 # --------------------------------------------------------------------------------------
 # offline group-wise INT4 weight quantization (round to nearest)
 # --------------------------------------------------------------------------------------
-def quant_weight(w, group_size: int, asymmetric: bool):
-    """Group-wise 4-bit RTN quantization of W[K, N]; each group is `group_size` consecutive
-    rows k of one output column n (P5 section 8.4: one output channel split along K).
+def quant_weight(w, group_size: int, asymmetric: bool, bits: int = 4):
+    """Group-wise RTN quantization of W[K, N] to `bits`-bit codes (4; 8 for the symmetric
+    W8A8 sibling); each group is `group_size` consecutive rows k of one output column n
+    (P5 section 8.4: one output channel split along K).
 
     Symmetric (P3 "Basic mapping", symmetric form, and the P3 symmetric group-wise
-    reference with bits = 4): s = max|w| / 7, q = clamp(round(w / s), -7, 7), z = 0; an
+    reference, whose qmax is 2^(bits-1) - 1): s = max|w| / qmax,
+    q = clamp(round(w / s), -qmax, qmax), z = 0, with qmax = 7 (4 bits) or 127 (8 bits); an
     all-zero group keeps s = 0 and divides by 1.
 
     Asymmetric (P3 "Basic mapping": s = (x_max - x_min) / (2^b - 1),
@@ -124,9 +128,12 @@ def quant_weight(w, group_size: int, asymmetric: bool):
     q = 0.
 
     Returns (codes int8 [K, N], scales float32 [K/g, N], zeros uint8 [K/g, N] or None).
-    Raises ValueError when the group does not tile K (P3 reference: groups cannot cross rows)
-    or when a weight is not finite.
+    Raises ValueError when the group does not tile K (P3 reference: groups cannot cross rows),
+    when a weight is not finite, or for bits other than 4 and 8 (8: symmetric only).
     """
+    if bits not in (4, 8) or (bits == 8 and asymmetric):
+        raise ValueError("bits must be 4, or 8 with symmetric codes")
+    qmax = (1 << (bits - 1)) - 1
     w = np.asarray(w, dtype=_F32)
     if w.ndim != 2:
         raise ValueError("w must be [K, N]")
@@ -139,9 +146,9 @@ def quant_weight(w, group_size: int, asymmetric: bool):
     wg = w.reshape(G, group_size, N)
     if not asymmetric:
         amax = np.max(np.abs(wg), axis=1)
-        s = (amax / _F32(7.0)).astype(_F32)
+        s = (amax / _F32(qmax)).astype(_F32)
         d = np.where(s > 0, s, _F32(1.0)).astype(_F32)
-        q = np.clip(np.rint((wg / d[:, None, :]).astype(_F32)), -7, 7)
+        q = np.clip(np.rint((wg / d[:, None, :]).astype(_F32)), -qmax, qmax)
         return q.reshape(K, N).astype(np.int8), s, None
     lo = np.minimum(np.min(wg, axis=1), _F32(0.0))
     hi = np.maximum(np.max(wg, axis=1), _F32(0.0))

@@ -173,6 +173,42 @@ def test_weight_properties(g, G, N, seed, asym, shift):
                 assert abs(int(cg[i, j, n])) == 7
 
 
+@settings(max_examples=25, deadline=None)
+@given(st.sampled_from([32, 64, 128]), st.integers(1, 3), st.integers(1, 5), st.integers(0, 2**31 - 1))
+def test_weight_properties_8bit(g, G, N, seed):
+    """bits = 8 of the P3 symmetric group-wise reference: codes in [-127, 127], error at most
+    s / 2, the abs-max element of a nonzero group at +-127, an all-zero group all zero."""
+    rs = np.random.default_rng(seed)
+    w = (rs.standard_normal((g * G, N)) * 0.02).astype(F32)
+    w[:g, 0] = 0.0
+    codes, scales, zeros = O.quant_weight(w, g, False, bits=8)
+    assert zeros is None and codes.min() >= -127 and codes.max() <= 127
+    xhat = O.dequant_weight(codes, scales, None, g)
+    s_full = np.repeat(scales.astype(np.float64), g, axis=0)
+    assert np.all(np.abs(w - xhat) <= s_full / 2 * (1 + 1e-5) + 1e-12)
+    assert scales[0, 0] == 0 and not codes[:g, 0].any()
+    wg, cg = w.reshape(G, g, N), codes.reshape(G, g, N)
+    for i, n in itertools.product(range(G), range(N)):
+        if scales[i, n] > 0:
+            assert abs(int(cg[i, np.argmax(np.abs(wg[i, :, n])), n])) == 127
+
+
+def test_weight_8bit_exact_grid_roundtrip():
+    """Weights on the grid s * q (s a power of two, q integers with |q| = 127 present in
+    every group) quantize back to exactly q and s: a wrong qmax, sign or rounding fails."""
+    rs = np.random.default_rng(5)
+    q = rs.integers(-127, 128, (256, 6)).astype(np.int64)
+    q[0::64, :] = 127                                   # the abs max of every 64-group
+    w = (q * 2.0 ** -9).astype(F32)
+    codes, scales, _ = O.quant_weight(w, 64, False, bits=8)
+    assert np.array_equal(codes.astype(np.int64), q)
+    assert np.all(scales == F32(2.0 ** -9))
+    with pytest.raises(ValueError):
+        O.quant_weight(w, 64, True, bits=8)            # 8-bit codes are symmetric only
+    with pytest.raises(ValueError):
+        O.quant_weight(w, 64, False, bits=3)
+
+
 def test_weight_nonfinite_rejected():
     w = np.zeros((4, 2), F32)
     w[1, 1] = np.nan
@@ -181,11 +217,11 @@ def test_weight_nonfinite_rejected():
 
 
 # ------------------------------------------------------------------ GEMM
-def _tiny_problem(seed, M, K, N, g, asym):
+def _tiny_problem(seed, M, K, N, g, asym, bits=4):
     x = W.bf16_values(W.random_activations(seed, M, K, outlier_cols=1, outlier_scale=10.0))
     w = W.random_weights(seed + 1, K, N)
     xq, sx = O.quant_act(x)
-    codes, scales, zeros = O.quant_weight(w, g, asym)
+    codes, scales, zeros = O.quant_weight(w, g, asym, bits)
     return xq, sx, codes, scales, zeros
 
 
@@ -202,11 +238,12 @@ def test_partials_bruteforce(M, K, N, g, asym):
         assert P[m, n, i] == ref
 
 
-@pytest.mark.parametrize("M,K,N,g,asym", [(3, 64, 5, 32, False), (5, 128, 7, 64, True),
-                                          (6, 512, 9, 128, False), (2, 256, 4, 64, True)])
-def test_gemm_bruteforce_dequant(M, K, N, g, asym):
+@pytest.mark.parametrize("M,K,N,g,asym,bits", [(3, 64, 5, 32, False, 4), (5, 128, 7, 64, True, 4),
+                                               (6, 512, 9, 128, False, 4), (2, 256, 4, 64, True, 4),
+                                               (4, 256, 5, 128, False, 8)])
+def test_gemm_bruteforce_dequant(M, K, N, g, asym, bits):
     """Y equals (s_x * x_q) @ (s_w * (q - z)) evaluated term by term in float64."""
-    xq, sx, codes, scales, zeros = _tiny_problem(23, M, K, N, g, asym)
+    xq, sx, codes, scales, zeros = _tiny_problem(23, M, K, N, g, asym, bits)
     Y = O.gemm(xq, sx, codes, scales, zeros, g)
     for m, n in itertools.product(range(M), range(N)):
         ref = 0.0
