@@ -9,8 +9,9 @@ time, in GB/s.  Each GEMM reads a different one of 16 device copies of the packe
 
 Extra fields (same JSON line): prefill INT8 TOPS of the projection pair at M=4096
 (asymmetric g128), MoE layer tokens/s of the 64-expert top-6 layer (T=512) and the
-256-expert top-8 decode layer (T=64, asymmetric g64), and a bf16 baseline: the decode and
-prefill shapes as bf16 GEMMs through torch.mm, beside W4A8 per-M decode times.
+256-expert top-8 decode layer (T=64, asymmetric g64), and the pages' comparison on the
+decode and prefill shapes: bf16 GEMMs through torch.mm, the W8A8 sibling (8-bit codes) and
+W4A8 per-M decode times.
 
 `roofline` is the decode GEMM at M=32 (the dominant kernel of the step): 64 back-to-back
 launches on rotating weight copies between two HIP events on the launch stream;
@@ -43,7 +44,7 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the prefill and MoE figures")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--only", default="", help="comma list of legs: decode,prefill,moe,bf16")
+    p.add_argument("--only", default="", help="comma list of legs: decode,prefill,moe,compare")
     p.add_argument("--no-graph", action="store_true", help="launch the decode steps eagerly")
     p.add_argument("--calib", action="store_true",
                    help="also run one plain copy kernel (torch.neg over 256 MiB of fp32) so that "
@@ -325,27 +326,34 @@ def moe_leg(args, L, W, torch, dev, steps):
     return out
 
 
-# ------------------------------------------------------------------- bf16 library baseline
-def bf16_leg(args, L, W, torch, dev):
-    """The same shapes as bf16 GEMMs through torch.mm (the platform's library GEMM): the
-    baseline a W4A8 path is meant to beat where weight bytes decide (decode: 4x fewer bytes),
-    set beside W4A8 per-M decode times measured the same way (16 rotating weight copies,
-    launches replayed from a graph, per-GEMM mean)."""
+# ------------------------------------------------------- W8A8 sibling and bf16 library baseline
+def compare_leg(args, L, W, torch, dev):
+    """The pages' comparison (bf16 baseline, W8A8, W4A8) on the same shapes: bf16 GEMMs through
+    torch.mm (the platform's library GEMM), the W8A8 sibling (8-bit symmetric codes, g = 128,
+    the same kernels without the unpack) and W4A8, all measured the same way.  Decode: per-call
+    means of w4a8_linear / torch.mm over 16 rotating weight copies, launches replayed from a
+    graph.  Prefill: the projection pair at M = 4096, GEMM only."""
     out = {"decode": {}, "prefill": {}}
     cfg = W.C2
     K, N = cfg.K, cfg.N
     ncopy = args.copies
     d = L.desc(K, N, cfg.group_size, cfg.asymmetric)
+    d8 = L.desc(K, N, cfg.group_size, False, bits=8)
     _, Wt = W.dense_inputs(cfg, M=1)
-    one = torch.from_numpy(L.w4a8_pack(d, Wt)).to(dev)
-    blobs = torch.empty((ncopy, one.numel()), dtype=torch.uint8, device=dev)
-    for c in range(ncopy):
-        blobs[c].copy_(one)
+
+    def copies(desc):
+        one = torch.from_numpy(L.w4a8_pack(desc, Wt)).to(dev)
+        t = torch.empty((ncopy, one.numel()), dtype=torch.uint8, device=dev)
+        for c in range(ncopy):
+            t[c].copy_(one)
+        return t
+
+    blobs, blobs8 = copies(d), copies(d8)
     wb = torch.from_numpy(Wt).to(dev).to(torch.bfloat16)
     Wb = torch.empty((ncopy, K, N), dtype=torch.bfloat16, device=dev)
     for c in range(ncopy):
         Wb[c].copy_(wb)
-    del one, wb, Wt
+    del wb, Wt
 
     def per_call_us(fn):
         fn()
@@ -374,31 +382,51 @@ def bf16_leg(args, L, W, torch, dev):
             for c in range(ncopy):
                 L.w4a8_linear(X, blobs[c], d, Y, Xq, sx, L.W4A8_OUT_BF16)
 
+        def w8a8():
+            for c in range(ncopy):
+                L.w4a8_linear(X, blobs8[c], d8, Y, Xq, sx, L.W4A8_OUT_BF16)
+
         def bf16():
             for c in range(ncopy):
                 torch.mm(X, Wb[c], out=Y)
 
-        t4, tb = per_call_us(w4a8), per_call_us(bf16)
-        out["decode"][f"m{M}"] = dict(w4a8_linear_us=t4, bf16_mm_us=tb, speedup=tb / t4,
+        t4, t8, tb = per_call_us(w4a8), per_call_us(w8a8), per_call_us(bf16)
+        out["decode"][f"m{M}"] = dict(w4a8_linear_us=t4, w8a8_linear_us=t8, bf16_mm_us=tb,
+                                      w4a8_vs_w8a8=t8 / t4, w4a8_vs_bf16=tb / t4,
+                                      w8a8_weight_gbs=(K * N + K // cfg.group_size * N * 4) / (t8 * 1e-6) / 1e9,
                                       bf16_weight_gbs=K * N * 2 / (tb * 1e-6) / 1e9)
         del X, Xq, sx, Y
-    del blobs, Wb
+    del blobs, blobs8, Wb
     torch.cuda.empty_cache()
     for pc in (W.C3_UP, W.C3_DOWN):
         X = W.random_activations(pc.seed + 7919, pc.M, pc.K).to(dev)
-        Wm = (torch.randn((pc.K, pc.N), generator=torch.Generator().manual_seed(pc.seed), dtype=torch.float32) * 0.02
-              ).to(dev).to(torch.bfloat16)
+        Wf = W.random_weights(pc.seed, pc.K, pc.N)
+        Wm = torch.from_numpy(Wf).to(dev).to(torch.bfloat16)
+        p8 = L.desc(pc.K, pc.N, pc.group_size, False, bits=8)
+        blob8 = torch.from_numpy(L.w4a8_pack(p8, Wf)).to(dev)
+        del Wf
+        Xq = torch.empty((pc.M, pc.K), dtype=torch.int8, device=dev)
+        sx = torch.empty(pc.M, dtype=torch.float32, device=dev)
+        L.w4a8_quant_act(X, Xq, sx)
         Y = torch.empty((pc.M, pc.N), dtype=torch.bfloat16, device=dev)
-        for _ in range(3):
-            torch.mm(X, Wm, out=Y)
-        t = Timer(torch)
-        for _ in range(10):
-            s = t.start()
-            torch.mm(X, Wm, out=Y)
-            t.stop(s)
-        ms = t.mean_ms()
-        out["prefill"][pc.name] = dict(bf16_mm_ms=ms, tflops=2.0 * pc.M * pc.N * pc.K / (ms * 1e-3) / 1e12)
-        del X, Wm, Y
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            t = Timer(torch)
+            for _ in range(10):
+                s = t.start()
+                fn()
+                t.stop(s)
+            return t.mean_ms()
+
+        ms_b = timed(lambda: torch.mm(X, Wm, out=Y))
+        ms_8 = timed(lambda: L.w4a8_gemm(Xq, sx, blob8, p8, Y))
+        ops = 2.0 * pc.M * pc.N * pc.K
+        out["prefill"][pc.name] = dict(bf16_mm_ms=ms_b, bf16_tflops=ops / (ms_b * 1e-3) / 1e12,
+                                       w8a8_gemm_ms=ms_8, w8a8_tops=ops / (ms_8 * 1e-3) / 1e12,
+                                       w8a8_kernel=L.w4a8_kernel_name(p8, pc.M))
+        del X, Wm, Y, Xq, sx, blob8
         torch.cuda.empty_cache()
     return out
 
@@ -420,7 +448,7 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     L.lib()
-    legs = set(args.only.split(",")) if args.only else {"decode", "prefill", "moe", "bf16"}
+    legs = set(args.only.split(",")) if args.only else {"decode", "prefill", "moe", "compare"}
     if args.no_extra:
         legs = {"decode"}
     print(f"[bench] decode leg: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
@@ -432,9 +460,9 @@ def main():
     if "moe" in legs:
         print("[bench] moe leg", file=sys.stderr, flush=True)
         extra["moe"] = moe_leg(args, L, W, torch, dev, steps=20)
-    if "bf16" in legs:
-        print("[bench] bf16 library baseline", file=sys.stderr, flush=True)
-        extra["bf16_library"] = bf16_leg(args, L, W, torch, dev)
+    if "compare" in legs:
+        print("[bench] W8A8 sibling and bf16 library baseline", file=sys.stderr, flush=True)
+        extra["compare"] = compare_leg(args, L, W, torch, dev)
     cpu = None
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)

@@ -60,12 +60,18 @@ typedef enum { W4A8_OUT_BF16 = 0, W4A8_OUT_F32 = 1 } w4a8_out_dtype;
  *   asymmetric  0: signed codes q in [-7, 7], zero point 0 (P3 "Basic mapping",
  *                  symmetric form);
  *               1: unsigned codes q in [0, 15] with a uint8 zero point z per
- *                  group, w ~ s (q - z) (P3 "Basic mapping"; P5 section 6). */
+ *                  group, w ~ s (q - z) (P3 "Basic mapping"; P5 section 6).
+ *   weight_bits 4 (or 0): the INT4 codes above, two per byte;
+ *               8: the W8A8 sibling the pages compare against (P1 section 5): signed
+ *                  codes q in [-127, 127], one per byte, symmetric only (qmax of the
+ *                  P3 symmetric group-wise reference with bits = 8).  Dense GEMMs
+ *                  only: the MoE entry points return EUNSUPPORTED for it. */
 typedef struct {
     int32_t K;
     int32_t N;
     int32_t group_size;
     int32_t asymmetric;
+    int32_t weight_bits;
 } w4a8_wdesc;
 
 /* ------------------------------------------------------------------------------------
@@ -78,6 +84,7 @@ typedef struct {
  *               int32 K, N, group_size, asymmetric; uint32 scale_dtype = 0 (fp32);
  *               uint32 zero_dtype = 0 (uint8); uint64 codes_off, codes_bytes,
  *               scales_off, scales_bytes, zeros_off, zeros_bytes, total_bytes;
+ *               uint32 weight_bits (4 or 8; 0 in older headers reads as 4);
  *               the rest is zero.
  *   codes       Np = N rounded up to 16 (padding columns hold code 0, scale 0).
  *               Superblock = 16 columns x 128 rows = 1024 bytes, stored as 64
@@ -93,6 +100,9 @@ typedef struct {
  *               tile format matched to the MFMA operand; P1 section 7, third pitfall).
  *               Symmetric codes are stored as 4-bit two's complement; asymmetric
  *               codes as unsigned 0..15.  Two codes per byte (P1 section 5.2).
+ *               8-bit codes (weight_bits = 8): superblock = 2048 bytes, 64 lanes x 32
+ *               bytes, one int8 code per byte at lane * 32 + half * 16 + j (lane, half
+ *               and j as above): the values the 4-bit form unpacks, in the same order.
  *   scales      float32 [Np/16][K/g][16]: scale of (group i, column n) at
  *               ((n/16) * (K/g) + i) * 16 + n % 16.
  *   zeros       (asymmetric only) uint8, same index as scales.
@@ -107,7 +117,8 @@ size_t w4a8_packed_size(const w4a8_wdesc* d);
 
 /* Offline RTN quantization + packing on the host (P3 "Basic mapping"; P3 symmetric
  * group-wise reference; P2 section 2.1).  W_host: float32 [K, N] row-major, finite.
- * Per (group, column): symmetric s = fl32(max|w| / 7), q = clamp(rint(fl32(w / s)), -7, 7);
+ * Per (group, column): symmetric s = fl32(max|w| / 7), q = clamp(rint(fl32(w / s)), -7, 7)
+ * (8-bit codes: 127 in place of 7);
  * asymmetric lo = min(0, min w), hi = max(0, max w), s = fl32(fl32(hi - lo) / 15),
  * z = clamp(rint(fl32(-lo / s)), 0, 15), q = clamp(rint(fl32(w / s)) + z, 0, 15); an
  * all-zero group gets s = 0, z = 0, q = 0.  Round half to even, IEEE float32 division.
@@ -116,7 +127,8 @@ size_t w4a8_packed_size(const w4a8_wdesc* d);
 int w4a8_pack(const w4a8_wdesc* d, const float* W_host, void* blob_host, size_t blob_bytes);
 
 /* Pack externally produced codes (e.g. from GPTQ/AWQ, P2 section 3.2) without
- * re-quantizing.  codes: int8 [K, N] in [-7, 7] (symmetric) or [0, 15] (asymmetric);
+ * re-quantizing.  codes: int8 [K, N] in [-7, 7] (symmetric), [0, 15] (asymmetric) or
+ * [-127, 127] (8-bit);
  * scales: float32 [K/g, N]; zeros: uint8 [K/g, N] in [0, 15] (asymmetric) or NULL.
  * EINVAL on out-of-range codes or zero points. */
 int w4a8_pack_codes(const w4a8_wdesc* d, const int8_t* codes, const float* scales,

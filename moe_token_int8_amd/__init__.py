@@ -36,10 +36,11 @@ class W4A8Error(RuntimeError):
 
 class WDesc(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32), ("group_size", ctypes.c_int32),
-                ("asymmetric", ctypes.c_int32)]
+                ("asymmetric", ctypes.c_int32), ("weight_bits", ctypes.c_int32)]
 
     def __repr__(self):
-        return f"WDesc(K={self.K}, N={self.N}, group_size={self.group_size}, asymmetric={self.asymmetric})"
+        return (f"WDesc(K={self.K}, N={self.N}, group_size={self.group_size}, asymmetric={self.asymmetric}, "
+                f"weight_bits={self.weight_bits})")
 
 
 _lib = None
@@ -91,8 +92,9 @@ def _check(status: int, where: str):
         raise W4A8Error(status, where)
 
 
-def desc(K: int, N: int, group_size: int, asymmetric: bool) -> WDesc:
-    return WDesc(int(K), int(N), int(group_size), int(bool(asymmetric)))
+def desc(K: int, N: int, group_size: int, asymmetric: bool, bits: int = 4) -> WDesc:
+    """Weight descriptor; bits = 8 selects the symmetric INT8-weight (W8A8) form."""
+    return WDesc(int(K), int(N), int(group_size), int(bool(asymmetric)), int(bits))
 
 
 def _ptr(x) -> int | None:

@@ -21,6 +21,8 @@ bool desc_valid(const w4a8_wdesc* d) {
     if (!d) return false;
     if (d->K <= 0 || d->N <= 0) return false;
     if (d->asymmetric != 0 && d->asymmetric != 1) return false;
+    if (d->weight_bits != 0 && d->weight_bits != 4 && d->weight_bits != 8) return false;
+    if (d->weight_bits == 8 && d->asymmetric) return false;   // 8-bit codes are symmetric
     const int g = d->group_size;
     if (g != 32 && g != 64 && g != 128 && g != 256) return false;
     if (d->K % g) return false;            // groups cannot cross rows (P3 reference)
@@ -41,8 +43,9 @@ Layout layout_of(const w4a8_wdesc* d) {
     L.g = d->group_size;
     L.G = d->K / d->group_size;
     L.asym = d->asymmetric;
+    L.bits = d->weight_bits == 8 ? 8 : 4;
     L.codes_off = W4A8_HEADER_BYTES;
-    L.codes_bytes = size_t(L.Np) * size_t(L.K) / 2;
+    L.codes_bytes = size_t(L.Np) * size_t(L.K) * size_t(L.bits) / 8;
     L.scales_off = align256(L.codes_off + L.codes_bytes);
     L.scales_bytes = size_t(L.Np) * size_t(L.G) * 4;
     L.zeros_off = align256(L.scales_off + L.scales_bytes);
@@ -61,6 +64,17 @@ static inline void code_pos(const Layout& L, int k, int n, size_t* byte, int* ni
     *nib = (j % 8) / 4;
 }
 
+// 8-bit codes: superblock (16 columns x 128 k) = 2 KiB, 32 bytes per layout lane: byte
+// 16 * half + j of lane (r / 16) * 16 + c holds k = 128 sb + 64 half + r with r % 16 = j, i.e.
+// the 16 values the 4-bit form unpacks for that lane and half, in the same order.
+static inline size_t code_pos8(const Layout& L, int k, int n) {
+    const int sb = k / SB_K, kk = k % SB_K, c = n % 16;
+    const int half = kk / 64, r = kk % 64;
+    const int lane = (r / 16) * 16 + c, j = r % 16;
+    const size_t sbi = size_t(n / 16) * size_t(L.K / SB_K) + size_t(sb);
+    return sbi * 2048 + size_t(lane) * 32 + size_t(half) * 16 + size_t(j);
+}
+
 static inline size_t meta_index(const Layout& L, int i, int n) {
     return (size_t(n / 16) * size_t(L.G) + size_t(i)) * 16 + size_t(n % 16);
 }
@@ -71,6 +85,7 @@ struct Header {
     int32_t K, N, group_size, asymmetric;
     uint32_t scale_dtype, zero_dtype;
     uint64_t codes_off, codes_bytes, scales_off, scales_bytes, zeros_off, zeros_bytes, total;
+    uint32_t weight_bits;   // 4 or 8
 };
 static_assert(sizeof(Header) <= W4A8_HEADER_BYTES, "header too large");
 
@@ -91,6 +106,7 @@ static void write_header(const w4a8_wdesc* d, const Layout& L, uint8_t* blob) {
     h.zeros_off = L.zeros_off;
     h.zeros_bytes = L.zeros_bytes;
     h.total = L.total;
+    h.weight_bits = uint32_t(L.bits);
     std::memset(blob, 0, W4A8_HEADER_BYTES);
     std::memcpy(blob, &h, sizeof(h));
 }
@@ -100,7 +116,9 @@ static int read_header(const void* blob, size_t bytes, w4a8_wdesc* d, Layout* L)
     Header h;
     std::memcpy(&h, blob, sizeof(h));
     if (std::memcmp(h.magic, "W4A8BLB1", 8) || h.version != 1 || h.layout != 1) return W4A8_EINVAL;
-    w4a8_wdesc dd{h.K, h.N, h.group_size, h.asymmetric};
+    if (h.weight_bits == 0) h.weight_bits = 4;          // headers written before the field existed
+    if (h.weight_bits != 4 && h.weight_bits != 8) return W4A8_EINVAL;
+    w4a8_wdesc dd{h.K, h.N, h.group_size, h.asymmetric, int32_t(h.weight_bits)};
     int st = desc_status(&dd);
     if (st) return st == W4A8_EUNSUPPORTED ? W4A8_EINVAL : st;
     Layout l = layout_of(&dd);
@@ -138,16 +156,17 @@ static void parallel_tiles(int Np, F f) {
 // Quantize one group (g values of column n, stride N) -- P3 "Basic mapping" and the P3
 // symmetric group-wise reference; IEEE float32 division and round-half-to-even (rint under
 // the default rounding mode), matching the per-group rule stated in w4a8.h.
-static void rtn_group(const float* w, size_t stride, int g, int asym, int8_t* q, float* s_out,
+static void rtn_group(const float* w, size_t stride, int g, int asym, int bits, int8_t* q, float* s_out,
                       uint8_t* z_out) {
     if (!asym) {
+        const float qmax = bits == 8 ? 127.0f : 7.0f;    // 2^(bits-1) - 1
         float amax = 0.0f;
         for (int t = 0; t < g; ++t) amax = std::max(amax, std::fabs(w[size_t(t) * stride]));
-        const float s = amax / 7.0f;
+        const float s = amax / qmax;
         const float d = s > 0.0f ? s : 1.0f;
         for (int t = 0; t < g; ++t) {
             float r = std::rint(w[size_t(t) * stride] / d);
-            r = std::min(7.0f, std::max(-7.0f, r));
+            r = std::min(qmax, std::max(-qmax, r));
             q[t] = int8_t(r);
         }
         *s_out = s;
@@ -180,6 +199,10 @@ static void rtn_group(const float* w, size_t stride, int g, int asym, int8_t* q,
 }
 
 static void store_code(const Layout& L, uint8_t* codes, int k, int n, int q) {
+    if (L.bits == 8) {
+        codes[code_pos8(L, k, n)] = uint8_t(int8_t(q));
+        return;
+    }
     size_t byte;
     int nib;
     code_pos(L, k, n, &byte, &nib);
@@ -220,7 +243,7 @@ int w4a8_pack(const w4a8_wdesc* d, const float* W, void* blob_host, size_t blob_
             for (int i = 0; i < L.G; ++i) {
                 float s;
                 uint8_t z;
-                rtn_group(W + size_t(i) * g * N + n, size_t(N), g, L.asym, q.data(), &s, &z);
+                rtn_group(W + size_t(i) * g * N + n, size_t(N), g, L.asym, L.bits, q.data(), &s, &z);
                 scales[meta_index(L, i, n)] = s;
                 if (L.asym) zeros[meta_index(L, i, n)] = z;
                 for (int t = 0; t < g; ++t) store_code(L, codes, i * g + t, n, q[size_t(t)]);
@@ -239,7 +262,8 @@ int w4a8_pack_codes(const w4a8_wdesc* d, const int8_t* codesIn, const float* sca
     const Layout L = layout_of(d);
     if (blob_bytes < L.total) return W4A8_ESIZE;
     const size_t KN = size_t(d->K) * size_t(d->N);
-    const int lo = d->asymmetric ? 0 : -7, hi = d->asymmetric ? 15 : 7;
+    const int qmax = L.bits == 8 ? 127 : 7;
+    const int lo = d->asymmetric ? 0 : -qmax, hi = d->asymmetric ? 15 : qmax;
     for (size_t i = 0; i < KN; ++i)
         if (codesIn[i] < lo || codesIn[i] > hi) return W4A8_EINVAL;
     if (d->asymmetric)
@@ -280,7 +304,9 @@ int w4a8_unpack_codes(const void* blob_host, size_t blob_bytes, w4a8_wdesc* d_ou
             if (scalesOut) scalesOut[size_t(i) * L.N + n] = scales[meta_index(L, i, n)];
             if (zerosOut && L.asym) zerosOut[size_t(i) * L.N + n] = zeros[meta_index(L, i, n)];
         }
-        if (codesOut)
+        if (codesOut && L.bits == 8)
+            for (int k = 0; k < L.K; ++k) codesOut[size_t(k) * L.N + n] = int8_t(codes[code_pos8(L, k, n)]);
+        else if (codesOut)
             for (int k = 0; k < L.K; ++k) {
                 size_t byte;
                 int nib;
@@ -300,7 +326,8 @@ int w4a8_blob_check(const void* blob_host, size_t blob_bytes, const w4a8_wdesc* 
     Layout L;
     st = read_header(blob_host, blob_bytes, &h, &L);
     if (st) return st;
-    if (h.K != d->K || h.N != d->N || h.group_size != d->group_size || h.asymmetric != d->asymmetric)
+    if (h.K != d->K || h.N != d->N || h.group_size != d->group_size || h.asymmetric != d->asymmetric ||
+        layout_of(&h).bits != layout_of(d).bits)
         return W4A8_EINVAL;
     return W4A8_OK;
 }

@@ -9,9 +9,11 @@
 namespace w4a8 {
 
 constexpr int SB_K = 128;   // superblock depth: 16 columns x 128 k = 1 KiB of packed codes
+                            // (2 KiB with 8-bit codes)
 
 struct Layout {
     int K, N, Np, g, G, asym;
+    int bits;               // 4 or 8 (desc weight_bits, 0 read as 4)
     size_t codes_off, codes_bytes, scales_off, scales_bytes, zeros_off, zeros_bytes, total;
 };
 

@@ -329,10 +329,15 @@ constexpr size_t FUSED_MAX_ELEMS = 8192;
 // FQ (w4a8_linear, M * K <= FUSED_MAX_ELEMS): every workgroup quantizes the bf16 rows itself
 // (the per-token rule of quant_act_kernel, the same device routines) straight into its LDS
 // activation tile; workgroup 0 also exports the codes and row scales.
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI, bool FQ>
+// W8: 8-bit weight codes (2 KiB superblocks, 32 bytes per layout lane), used as MFMA operands
+// as loaded; otherwise 4-bit codes unpacked in registers.
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI, bool FQ, bool W8>
 __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     using S = DecodeShape<MS, NT, KW, SBN>;
     static_assert(!FQ || (MS == 1 && !MOE && MODE == MODE_OUT && !MULTI), "fused quantization: dense, one chunk");
+    static_assert(!W8 || (!ASYM && !MOE), "8-bit codes: symmetric, dense");
+    constexpr uint32_t SBB = W8 ? 2048u : 1024u;         // bytes per superblock
+    constexpr uint32_t LB = W8 ? 32u : 16u;              // bytes per layout lane
     constexpr int MT = S::MT, NTHR = S::NTHR, CS = S::CS, ROWB = S::ROWB, APT = S::APT;
     // weight superblocks requested before the activation hand-off (the rest right after it)
     constexpr int BE = MS == 2 ? (SBN < 2 ? SBN : 2) : (SBN < 4 ? SBN : 4);
@@ -426,11 +431,12 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         const int s0 = cb + q * SBN;
         const int s_end = min(cb + clen, s0 + SBN);
         uint4 bq[SBN];
+        uint4 bq2[W8 ? SBN : 1];                         // W8: the lane's second 16 bytes
         float sc[SBN][GPS];
         uint32_t zq[SBN][GPS];
         // 32-bit offsets from wave-uniform bases (a blob is far below 4 GiB): saddr-form loads,
         // no 64-bit per-lane addresses to keep alive
-        const uint32_t boff = (uint32_t(tile_c) * uint32_t(nsb)) * 1024u + uint32_t(lane) * 16u;
+        const uint32_t boff = (uint32_t(tile_c) * uint32_t(nsb)) * SBB + uint32_t(lane) * LB;
         const uint32_t moff = uint32_t(tile_c) * uint32_t(a.G) * 16u + uint32_t(lane & 15);
 #pragma unroll
         for (int s = 0; s < SBN; ++s) {
@@ -458,7 +464,8 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
         for (int s = 0; s < BE; ++s) {
             const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
-            bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * 1024u));
+            bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * SBB));
+            if constexpr (W8) bq2[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * SBB + 16u));
         }
         // 5. activations into LDS.  Waits are per register, so the weight loads stay in flight.
         if (FQ) {
@@ -523,7 +530,8 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
         for (int s = BE; s < SBN; ++s) {
             const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
-            bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * 1024u));
+            bq[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * SBB));
+            if constexpr (W8) bq2[s] = *reinterpret_cast<const uint4*>(codes + (boff + sb * SBB + 16u));
         }
         // keep these requests issued here: otherwise each is sunk next to its first use
         // behind a full wait, leaving one weight load in flight per wave
@@ -537,10 +545,16 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int gi = (GPS == 2) ? h : 0;
-                const uint32_t w0 = h ? bq[s].z : bq[s].x;
-                const uint32_t w1 = h ? bq[s].w : bq[s].y;
-                const uint32_t zc = ASYM ? (128u - zq[s][gi]) * 0x01010101u : 0u;
-                const v4i b = unpack_b<ASYM>(w0, w1, zc);
+                v4i b;
+                if constexpr (W8) {
+                    const uint4 u = h ? bq2[s] : bq[s];
+                    b = v4i{int(u.x), int(u.y), int(u.z), int(u.w)};
+                } else {
+                    const uint32_t w0 = h ? bq[s].z : bq[s].x;
+                    const uint32_t w1 = h ? bq[s].w : bq[s].y;
+                    const uint32_t zc = ASYM ? (128u - zq[s][gi]) * 0x01010101u : 0u;
+                    b = unpack_b<ASYM>(w0, w1, zc);
+                }
                 const bool first = (GPS == 2) || h == 0;
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms) {
@@ -558,12 +572,12 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                             for (int i = 0; i < 4; ++i) {
                                 const int row = rbeg + ms * 16 + 4 * (lane >> 4) + i;
                                 if (tvalid && row < rend && col < a.N) {
-                                    const int v = ASYM ? acc[ms][i] : (acc[ms][i] >> 4);
+                                    const int v = (ASYM || W8) ? acc[ms][i] : (acc[ms][i] >> 4);
                                     a.P[(size_t(row) * a.N + col) * a.G + size_t(sb) * GPS + gi] = v;
                                 }
                             }
                     } else {
-                        const float scl = ASYM ? sc[s][gi] : sc[s][gi] * 0.0625f;
+                        const float scl = (ASYM || W8) ? sc[s][gi] : sc[s][gi] * 0.0625f;
 #pragma unroll
                         for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -928,6 +942,7 @@ __device__ __forceinline__ void prefill_tile(int b, int mtiles, int ntiles, int*
 struct PfRegs {
     uint4 a[4];     // activation pieces
     uint4 b;        // 16 bytes of packed codes (one layout lane of one 16-column tile)
+    uint4 b2;       // W8: the lane's second 16 bytes
     uint4 m;        // scales piece (threads that stage metadata)
     uint32_t z;     // zero points of this thread's column, one byte per group
 };
@@ -935,8 +950,11 @@ struct PfRegs {
 // MOE: the grouped form for experts with many rows.  Workgroup (slot, column tile): slot
 // is a PF_BM-row tile of one expert (moe_tile), rows gathered from the token rows when
 // `gather` is set; output row r is the r-th sorted row.
-template <bool ASYM, int GPS, int MODE, bool MOE>
+// W8: 8-bit weight codes, copied to the LDS operand layout as loaded (no unpack).
+template <bool ASYM, int GPS, int MODE, bool MOE, bool W8>
 __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a) {
+    static_assert(!W8 || (!ASYM && !MOE), "8-bit codes: symmetric, dense");
+    constexpr int SBB = W8 ? 2048 : 1024;                // code bytes per superblock
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 3, wn = wave >> 2;
@@ -984,7 +1002,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(xbase), 0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(codes + size_t(__builtin_amdgcn_readfirstlane(b_tile)) * nsb * 1024), 0, 0x7fffffff,
+        const_cast<uint8_t*>(codes + size_t(__builtin_amdgcn_readfirstlane(b_tile)) * nsb * SBB), 0, 0x7fffffff,
         0x00020000);
     int aoff[4];
 #pragma unroll
@@ -1001,8 +1019,12 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
             r.a[i] = make_uint4(uint32_t(t.x), uint32_t(t.y), uint32_t(t.z), uint32_t(t.w));
         }
         {
-            const v4i t = __builtin_amdgcn_raw_buffer_load_b128(cr, lane * 16, sb * 1024, 0);
+            const v4i t = __builtin_amdgcn_raw_buffer_load_b128(cr, lane * (SBB / 64), sb * SBB, 0);
             r.b = make_uint4(uint32_t(t.x), uint32_t(t.y), uint32_t(t.z), uint32_t(t.w));
+        }
+        if constexpr (W8) {
+            const v4i t = __builtin_amdgcn_raw_buffer_load_b128(cr, lane * 32 + 16, sb * SBB, 0);
+            r.b2 = make_uint4(uint32_t(t.x), uint32_t(t.y), uint32_t(t.z), uint32_t(t.w));
         }
         if (ASYM) {
             r.z = 0;
@@ -1030,8 +1052,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int gi = (GPS == 2) ? h : 0;
-            const uint32_t zc = ASYM ? (128u - ((r.z >> (8 * gi)) & 0xffu)) * 0x01010101u : 0u;
-            const v4i u = unpack_b<ASYM>(h ? r.b.z : r.b.x, h ? r.b.w : r.b.y, zc);
+            v4i u;
+            if constexpr (W8) {
+                const uint4 v = h ? r.b2 : r.b;
+                u = v4i{int(v.x), int(v.y), int(v.z), int(v.w)};
+            } else {
+                const uint32_t zc = ASYM ? (128u - ((r.z >> (8 * gi)) & 0xffu)) * 0x01010101u : 0u;
+                u = unpack_b<ASYM>(h ? r.b.z : r.b.x, h ? r.b.w : r.b.y, zc);
+            }
             const int j = 2 * h + (st_q4 >> 1), hl = st_q4 & 1;
             *reinterpret_cast<v4i*>(st + PF_A_BYTES + ((j * 2 + hl) * PF_BN + col) * 16) = u;
         }
@@ -1096,7 +1124,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
                             for (int r = 0; r < 16; ++r) {
                                 const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
                                 if (row < mend && col < a.N) {
-                                    const int v = ASYM ? acc[ms][ns][r] : (acc[ms][ns][r] >> 4);
+                                    const int v = (ASYM || W8) ? acc[ms][ns][r] : (acc[ms][ns][r] >> 4);
                                     a.P[(size_t(row) * a.N + col) * a.G + size_t(sb) * GPS + gi] = v;
                                 }
                             }
@@ -1105,7 +1133,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
 #pragma unroll
                     for (int ns = 0; ns < 2; ++ns) {
                         float scl = *reinterpret_cast<const float*>(st + s_off[ns] + gi * 64);
-                        if (!ASYM) scl *= 0.0625f;
+                        if (!ASYM && !W8) scl *= 0.0625f;
 #pragma unroll
                         for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
@@ -1342,10 +1370,11 @@ static DecodeCfg decode_cfg(int K, int mt) {
     return c;
 }
 
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI = false, bool FQ = false>
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI = false, bool FQ = false,
+          bool W8 = false>
 static void launch_decode_t(const GemmArgs& a, dim3 grid, hipStream_t s) {
     using S = DecodeShape<MS, NT, KW, SBN>;
-    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, MULTI, FQ>;
+    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, MULTI, FQ, W8>;
     constexpr size_t lds = S::LDS + (FQ ? 128 : 0);           // FQ: row abs-maxima
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -1354,30 +1383,41 @@ static void launch_decode_t(const GemmArgs& a, dim3 grid, hipStream_t s) {
 }
 
 // Fused quantization + GEMM on the chunked kernel (dense, 16-row tile, K in one chunk).
-template <int GPS, bool ASYM>
+template <int GPS, bool ASYM, bool W8 = false>
 static void launch_decode_fused(const GemmArgs& a, const DecodeCfg& c, dim3 grid, hipStream_t s) {
-    if (c.kw == 8) launch_decode_t<1, 2, 8, 8, GPS, ASYM, MODE_OUT, false, false, true>(a, grid, s);
-    else if (c.sbn == 2) launch_decode_t<1, 4, 4, 2, GPS, ASYM, MODE_OUT, false, false, true>(a, grid, s);
-    else if (c.sbn == 4) launch_decode_t<1, 4, 4, 4, GPS, ASYM, MODE_OUT, false, false, true>(a, grid, s);
-    else launch_decode_t<1, 4, 4, 8, GPS, ASYM, MODE_OUT, false, false, true>(a, grid, s);
+    if (c.kw == 8) launch_decode_t<1, 2, 8, 8, GPS, ASYM, MODE_OUT, false, false, true, W8>(a, grid, s);
+    else if (c.sbn == 2) launch_decode_t<1, 4, 4, 2, GPS, ASYM, MODE_OUT, false, false, true, W8>(a, grid, s);
+    else if (c.sbn == 4) launch_decode_t<1, 4, 4, 4, GPS, ASYM, MODE_OUT, false, false, true, W8>(a, grid, s);
+    else launch_decode_t<1, 4, 4, 8, GPS, ASYM, MODE_OUT, false, false, true, W8>(a, grid, s);
 }
 
-template <int MS, int GPS, bool ASYM, int MODE, bool MOE>
+template <int MS, int GPS, bool ASYM, int MODE, bool MOE, bool W8 = false>
 static void launch_decode_shape(const GemmArgs& a, const DecodeCfg& c, dim3 grid, hipStream_t s) {
     if (c.kw == 8) {
         if constexpr (MS == 1) {
-            if (a.K > 64 * SB_K) launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE, true>(a, grid, s);
-            else launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE>(a, grid, s);
+            if (a.K > 64 * SB_K) launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE, true, false, W8>(a, grid, s);
+            else launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE, false, false, W8>(a, grid, s);
         }
-    } else if (c.sbn == 2) launch_decode_t<MS, 4, 4, 2, GPS, ASYM, MODE, MOE>(a, grid, s);
-    else if (c.sbn == 4) launch_decode_t<MS, 4, 4, 4, GPS, ASYM, MODE, MOE>(a, grid, s);
-    else if (a.K > 32 * SB_K) launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, true>(a, grid, s);
-    else launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE>(a, grid, s);
+    } else if (c.sbn == 2) launch_decode_t<MS, 4, 4, 2, GPS, ASYM, MODE, MOE, false, false, W8>(a, grid, s);
+    else if (c.sbn == 4) launch_decode_t<MS, 4, 4, 4, GPS, ASYM, MODE, MOE, false, false, W8>(a, grid, s);
+    else if (a.K > 32 * SB_K) launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, true, false, W8>(a, grid, s);
+    else launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, false, false, W8>(a, grid, s);
 }
 
+// w8: 8-bit codes (symmetric, dense form only; the entry points check)
 template <int MODE, bool MOE>
-static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool asym, dim3 grid, hipStream_t s) {
+static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool asym, dim3 grid, hipStream_t s,
+                          bool w8 = false) {
 #define W4A8_DEC(MS_, GPS_, ASYM_) launch_decode_shape<MS_, GPS_, ASYM_, MODE, MOE>(a, c, grid, s)
+    if constexpr (!MOE) {
+        if (w8) {
+            if (c.ms == 1) { if (gps == 1) launch_decode_shape<1, 1, false, MODE, false, true>(a, c, grid, s);
+                             else launch_decode_shape<1, 2, false, MODE, false, true>(a, c, grid, s); }
+            else { if (gps == 1) launch_decode_shape<2, 1, false, MODE, false, true>(a, c, grid, s);
+                   else launch_decode_shape<2, 2, false, MODE, false, true>(a, c, grid, s); }
+            return;
+        }
+    }
     if (c.ms == 1) {
         if (gps == 1) { if (asym) W4A8_DEC(1, 1, true); else W4A8_DEC(1, 1, false); }
         else { if (asym) W4A8_DEC(1, 2, true); else W4A8_DEC(1, 2, false); }
@@ -1495,9 +1535,9 @@ static void launch_kslice(const GemmArgs& a, const KsliceCfg& c, int ms, int gps
 }
 
 // mtiles: row tiles (dense) or an upper bound on the experts' row tiles (MOE)
-template <bool ASYM, int GPS, int MODE, bool MOE>
+template <bool ASYM, int GPS, int MODE, bool MOE, bool W8 = false>
 static void launch_prefill_t(const GemmArgs& a, int mtiles, hipStream_t s) {
-    auto kern = gemm_prefill_kernel<ASYM, GPS, MODE, MOE>;
+    auto kern = gemm_prefill_kernel<ASYM, GPS, MODE, MOE, W8>;
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS);
     (void)attr;
@@ -1505,9 +1545,17 @@ static void launch_prefill_t(const GemmArgs& a, int mtiles, hipStream_t s) {
     kern<<<dim3(mtiles * ntiles), dim3(PF_THREADS), PF_LDS, s>>>(a);
 }
 
+// w8: 8-bit codes (symmetric, dense form only; the entry points check)
 template <int MODE, bool MOE = false>
-static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s, int mtiles = 0) {
+static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s, int mtiles = 0, bool w8 = false) {
     if (!MOE) mtiles = (a.M + PF_BM - 1) / PF_BM;
+    if constexpr (!MOE) {
+        if (w8) {
+            if (gps == 1) launch_prefill_t<false, 1, MODE, false, true>(a, mtiles, s);
+            else launch_prefill_t<false, 2, MODE, false, true>(a, mtiles, s);
+            return;
+        }
+    }
     if (gps == 1) {
         if (asym) launch_prefill_t<true, 1, MODE, MOE>(a, mtiles, s); else launch_prefill_t<false, 1, MODE, MOE>(a, mtiles, s);
     } else {
@@ -1601,13 +1649,15 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
     a.out_f32 = out_dtype == W4A8_OUT_F32;
     if (M >= PREFILL_MIN_M) {
         if (!prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
-        launch_prefill<MODE_OUT>(a, SB_K / d->group_size, d->asymmetric, static_cast<hipStream_t>(stream));
+        launch_prefill<MODE_OUT>(a, SB_K / d->group_size, d->asymmetric, static_cast<hipStream_t>(stream), 0,
+                                 L.bits == 8);
         return launch_status();
     }
     const int mt = dense_mt(M);
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
-    launch_decode<MODE_OUT, false>(a, c, SB_K / d->group_size, d->asymmetric, grid, static_cast<hipStream_t>(stream));
+    launch_decode<MODE_OUT, false>(a, c, SB_K / d->group_size, d->asymmetric, grid, static_cast<hipStream_t>(stream),
+                                   L.bits == 8);
     return launch_status();
 }
 
@@ -1636,7 +1686,9 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
         hipStream_t s = static_cast<hipStream_t>(stream);
         const dim3 grid = decode_grid(L, fc, 1);
         const int gps = SB_K / d->group_size;
-        if (gps == 1) {
+        if (L.bits == 8) {
+            if (gps == 1) launch_decode_fused<1, false, true>(a, fc, grid, s); else launch_decode_fused<2, false, true>(a, fc, grid, s);
+        } else if (gps == 1) {
             if (d->asymmetric) launch_decode_fused<1, true>(a, fc, grid, s); else launch_decode_fused<1, false>(a, fc, grid, s);
         } else {
             if (d->asymmetric) launch_decode_fused<2, true>(a, fc, grid, s); else launch_decode_fused<2, false>(a, fc, grid, s);
@@ -1659,14 +1711,15 @@ int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob, const w4a8_wde
     a.P = P;
     if (M >= PREFILL_MIN_M) {
         if (!prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
-        launch_prefill<MODE_PARTIALS>(a, SB_K / d->group_size, d->asymmetric, static_cast<hipStream_t>(stream));
+        launch_prefill<MODE_PARTIALS>(a, SB_K / d->group_size, d->asymmetric, static_cast<hipStream_t>(stream), 0,
+                                      L.bits == 8);
         return launch_status();
     }
     const int mt = dense_mt(M);
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
     launch_decode<MODE_PARTIALS, false>(a, c, SB_K / d->group_size, d->asymmetric, grid,
-                                        static_cast<hipStream_t>(stream));
+                                        static_cast<hipStream_t>(stream), L.bits == 8);
     return launch_status();
 }
 
@@ -1746,6 +1799,7 @@ int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int 
                   void* stream) {
     int st = check_gemm_desc(d);
     if (st) return st;
+    if (layout_of(d).bits != 4) return W4A8_EUNSUPPORTED;   // the grouped kernels take 4-bit codes
     if (rows < 0 || E <= 0 || (out_dtype != W4A8_OUT_BF16 && out_dtype != W4A8_OUT_F32)) return W4A8_EINVAL;
     if (rows == 0) return W4A8_OK;
     if (!Xq || !sx || !offsets || !blobs || !Y) return W4A8_EINVAL;
@@ -1827,6 +1881,7 @@ int w4a8_moe_forward(const void* X, const int32_t* ids, const float* w, int T, i
     if (st) return st;
     st = check_gemm_desc(d_desc);
     if (st) return st;
+    if (layout_of(gu_desc).bits != 4 || layout_of(d_desc).bits != 4) return W4A8_EUNSUPPORTED;
     if (T < 0 || k <= 0 || E <= 0) return W4A8_EINVAL;
     const int H = gu_desc->K, I2 = gu_desc->N;
     if (I2 % 2 || d_desc->K != I2 / 2 || d_desc->N != H) return W4A8_EINVAL;
@@ -1861,6 +1916,12 @@ const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
     if (check_gemm_desc(d) != W4A8_OK || M < 0) return "unsupported";
     const bool asym = d->asymmetric;
     const bool g64 = d->group_size == 64;
+    if (layout_of(d).bits == 8) {
+        if (M >= PREFILL_MIN_M) return g64 ? "w8a8_prefill_sym_g64" : "w8a8_prefill_sym_g128";
+        static const char* const n8[2][2] = {{"w8a8_decode_m16_sym_g128", "w8a8_decode_m16_sym_g64"},
+                                             {"w8a8_decode_m32_sym_g128", "w8a8_decode_m32_sym_g64"}};
+        return n8[dense_mt(M) == 32][g64];
+    }
     if (M >= PREFILL_MIN_M)
         return asym ? (g64 ? "w4a8_prefill_asym_g64" : "w4a8_prefill_asym_g128")
                     : (g64 ? "w4a8_prefill_sym_g64" : "w4a8_prefill_sym_g128");

@@ -37,9 +37,11 @@ def decode_blob(blob: np.ndarray):
     version, layout, K, N, g, asym, sdt, zdt = struct.unpack_from("<IIiiiiII", blob, 8)
     assert (version, layout, sdt, zdt) == (1, 1, 0, 0)
     co, cb, so, sb_, zo, zb, total = struct.unpack_from("<7Q", blob, 40)
+    (bits,) = struct.unpack_from("<I", blob, 96)
+    assert bits in (4, 8)
     Np = (N + 15) // 16 * 16
     G = K // g
-    assert cb == Np * K // 2 and sb_ == Np * G * 4 and zb == (Np * G if asym else 0)
+    assert cb == Np * K * bits // 8 and sb_ == Np * G * 4 and zb == (Np * G if asym else 0)
     assert co == 256 and so % 256 == 0 and zo % 256 == 0 and total % 256 == 0
     raw = blob[co:co + cb]
     codes = np.zeros((K, N), np.int8)
@@ -49,6 +51,9 @@ def decode_blob(blob: np.ndarray):
             half, r = kk // 64, kk % 64
             lane, j = (r // 16) * 16 + c, r % 16
             sbi = (n // 16) * (K // 128) + k // 128
+            if bits == 8:                             # 2 KiB superblocks, 32 bytes per lane
+                codes[k, n] = np.int8(np.uint8(raw[sbi * 2048 + lane * 32 + half * 16 + j]).view(np.int8))
+                continue
             byte = sbi * 1024 + lane * 16 + half * 8 + (j // 8) * 4 + (j % 4)
             nib = (j % 8) // 4
             v = (int(raw[byte]) >> (4 * nib)) & 0xF
@@ -66,7 +71,7 @@ def decode_blob(blob: np.ndarray):
     for n in range(N, Np):
         for i in range(G):
             assert sc[((n // 16) * G + i) * 16 + n % 16] == 0
-    return dict(K=K, N=N, g=g, asym=bool(asym), codes=codes, scales=scales, zeros=zeros, total=total)
+    return dict(K=K, N=N, g=g, asym=bool(asym), bits=bits, codes=codes, scales=scales, zeros=zeros, total=total)
 
 
 @pytest.mark.parametrize("K,N,g,asym", [(128, 16, 32, False), (256, 40, 64, True), (384, 19, 128, False),
@@ -92,6 +97,55 @@ def test_pack_matches_oracle_via_independent_decoder(K, N, g, asym):
     # packing the oracle's codes reproduces the blob byte for byte
     assert np.array_equal(L.w4a8_pack_codes(d, codes, scales, zeros), blob)
     L.w4a8_blob_check(blob, d)
+
+
+@pytest.mark.parametrize("K,N,g", [(128, 16, 64), (256, 40, 128), (384, 19, 128), (512, 33, 64)])
+def test_pack_8bit_matches_oracle_via_independent_decoder(K, N, g):
+    """8-bit codes (the W8A8 sibling): the blob decoded from the layout text equals the
+    oracle's bits = 8 quantization; the library's inverse and pack_codes agree."""
+    Wt = W.random_weights(2000 + K + N, K, N)
+    Wt[:g, 0] = 0.0
+    d = L.desc(K, N, g, False, bits=8)
+    blob = L.w4a8_pack(d, Wt)
+    dec = decode_blob(blob)
+    codes, scales, _ = O.quant_weight(Wt, g, False, bits=8)
+    assert dec["bits"] == 8 and np.abs(codes).max() == 127
+    assert np.array_equal(dec["codes"], codes)
+    assert np.array_equal(dec["scales"].view(np.uint32), scales.view(np.uint32))
+    d2, c2, s2, _ = L.w4a8_unpack_codes(blob)
+    assert (d2.K, d2.N, d2.group_size, d2.asymmetric, d2.weight_bits) == (K, N, g, 0, 8)
+    assert np.array_equal(c2, codes) and np.array_equal(s2.view(np.uint32), scales.view(np.uint32))
+    assert np.array_equal(L.w4a8_pack_codes(d, codes, scales, None), blob)
+    L.w4a8_blob_check(blob, d)
+    with pytest.raises(L.W4A8Error):                  # a 4-bit desc does not match the blob
+        L.w4a8_blob_check(blob, L.desc(K, N, g, False))
+
+
+def test_8bit_validation_host():
+    lib = L.lib()
+    E, U = L.W4A8_EINVAL, L.W4A8_EUNSUPPORTED
+    assert L.w4a8_packed_size(L.desc(256, 16, 128, True, bits=8)) == 0      # 8-bit is symmetric only
+    assert L.w4a8_packed_size(L.desc(256, 16, 128, False, bits=5)) == 0
+    d = L.desc(256, 16, 128, False, bits=8)
+    codes = np.zeros((256, 16), np.int8)
+    codes[3, 2] = -128                                                    # outside [-127, 127]
+    blob = np.zeros(L.w4a8_packed_size(d), np.uint8)
+    assert lib.w4a8_pack_codes(ctypes.byref(d), codes.ctypes.data, np.ones((2, 16), np.float32).ctypes.data,
+                               None, blob.ctypes.data, blob.nbytes) == E
+    assert L.w4a8_kernel_name(d, 1) == "w8a8_decode_m16_sym_g128"
+    assert L.w4a8_kernel_name(d, 32) == "w8a8_decode_m32_sym_g128"
+    assert L.w4a8_kernel_name(d, 4096) == "w8a8_prefill_sym_g128"
+    # the grouped (MoE) entry points take 4-bit codes only; rejected before any HIP call
+    fake = 0x10000
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0, None) == U
+    gu = L.desc(256, 64, 128, False)
+    ws = L.w4a8_moe_workspace_size(4, 2, 256, 32, 8)
+    assert lib.w4a8_moe_forward(fake, fake, fake, 4, 2, 8, fake, 1 << 20, ctypes.byref(gu), fake, 1 << 20,
+                                ctypes.byref(L.desc(32, 256, 128, False, bits=8)), fake, ws, fake, None) in (E, U)
+    g8 = L.desc(256, 64, 128, False, bits=8)
+    d4 = L.desc(32, 256, 128, False)
+    assert lib.w4a8_moe_forward(fake, fake, fake, 4, 2, 8, fake, 1 << 20, ctypes.byref(g8), fake, 1 << 20,
+                                ctypes.byref(d4), fake, ws, fake, None) in (E, U)
 
 
 def test_pack_page_examples_through_library():
@@ -124,6 +178,16 @@ def test_packed_size_formula(K, N, g, asym):
     assert expect - 256 - body < 3 * 256                 # only alignment on top of the formula
     # effective bits per weight without padding/header (P3 b_eff)
     assert abs(body * 8 / (Np * K) - O.effective_bits(4, 32, 8 if asym else 0, g)) < 1e-12
+
+
+@pytest.mark.parametrize("K,N,g", [(4096, 14336, 128), (1408, 4096, 64), (128, 5, 64)])
+def test_packed_size_formula_8bit(K, N, g):
+    """The same memory formula with b = 8: one byte per code, fp32 scales, no zeros."""
+    Np = (N + 15) // 16 * 16
+    a = lambda v: (v + 255) // 256 * 256
+    expect = a(a(256 + Np * K) + Np * (K // g) * 4)
+    assert L.w4a8_packed_size(L.desc(K, N, g, False, bits=8)) == expect
+    assert abs(O.memory_bytes(Np * K, 8, Np * (K // g), 4) * 8 / (Np * K) - O.effective_bits(8, 32, 0, g)) < 1e-12
 
 
 def test_validation_errors_host():
