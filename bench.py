@@ -257,8 +257,12 @@ def cpu_baseline(args, leg, W):
 
 # ---------------------------------------------------------------------------------- prefill
 def prefill_leg(args, L, W, torch, dev, steps):
+    """The projection pair at M = 4096 (asymmetric g128), and the up projection again with
+    g = 256: half the per-group epilogues, the same weights otherwise."""
     out = {}
-    for cfg in (W.C3_UP, W.C3_DOWN):
+    import dataclasses
+    g256 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "g256"), group_size=256)
+    for cfg in (W.C3_UP, W.C3_DOWN, g256):
         d = L.desc(cfg.K, cfg.N, cfg.group_size, cfg.asymmetric)
         _, Wt = W.dense_inputs(cfg, M=1)
         blob = torch.from_numpy(L.w4a8_pack(d, Wt)).to(dev)

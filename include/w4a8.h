@@ -55,7 +55,8 @@ typedef enum { W4A8_OUT_BF16 = 0, W4A8_OUT_F32 = 1 } w4a8_out_dtype;
  * granularity, execution types must each be stated).
  *   K, N        weight matrix W[K, N]
  *   group_size  g: consecutive k sharing one scale per column (P5 section 8.4);
- *               must divide K.  Kernels implement g in {64, 128}; pack accepts
+ *               must divide K.  Kernels implement g in {64, 128, 256} (256: dense
+ *               GEMMs only; the MoE entry points return EUNSUPPORTED); pack accepts
  *               g in {32, 64, 128, 256}.
  *   asymmetric  0: signed codes q in [-7, 7], zero point 0 (P3 "Basic mapping",
  *                  symmetric form);

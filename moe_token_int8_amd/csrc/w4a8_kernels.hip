@@ -336,6 +336,11 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     using S = DecodeShape<MS, NT, KW, SBN>;
     static_assert(!FQ || (MS == 1 && !MOE && MODE == MODE_OUT && !MULTI), "fused quantization: dense, one chunk");
     static_assert(!W8 || (!ASYM && !MOE), "8-bit codes: symmetric, dense");
+    // GPS: groups per superblock, 2 (g = 64) or 1 (g = 128); 0 is g = 256, one group per two
+    // superblocks (a wave's superblocks come in aligned pairs, so a group never straddles waves)
+    static_assert(GPS != 0 || !MOE, "g = 256: dense");
+    constexpr int NG = GPS == 0 ? 1 : GPS;              // scale entries per superblock
+    auto gidx = [](int sb, int gi) { return GPS == 0 ? sb / 2 : sb * GPS + gi; };
     constexpr uint32_t SBB = W8 ? 2048u : 1024u;         // bytes per superblock
     constexpr uint32_t LB = W8 ? 32u : 16u;              // bytes per layout lane
     constexpr int MT = S::MT, NTHR = S::NTHR, CS = S::CS, ROWB = S::ROWB, APT = S::APT;
@@ -432,8 +437,8 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         const int s_end = min(cb + clen, s0 + SBN);
         uint4 bq[SBN];
         uint4 bq2[W8 ? SBN : 1];                         // W8: the lane's second 16 bytes
-        float sc[SBN][GPS];
-        uint32_t zq[SBN][GPS];
+        float sc[SBN][NG];
+        uint32_t zq[SBN][NG];
         // 32-bit offsets from wave-uniform bases (a blob is far below 4 GiB): saddr-form loads,
         // no 64-bit per-lane addresses to keep alive
         const uint32_t boff = (uint32_t(tile_c) * uint32_t(nsb)) * SBB + uint32_t(lane) * LB;
@@ -442,8 +447,8 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         for (int s = 0; s < SBN; ++s) {
             const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
 #pragma unroll
-            for (int gi = 0; gi < GPS; ++gi) {
-                const uint32_t mi = moff + (sb * GPS + gi) * 16u;
+            for (int gi = 0; gi < NG; ++gi) {
+                const uint32_t mi = moff + uint32_t(gidx(int(sb), gi)) * 16u;
                 sc[s][gi] = scales[mi];
                 if (ASYM) zq[s][gi] = zeros[mi];
             }
@@ -537,11 +542,11 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         // behind a full wait, leaving one weight load in flight per wave
         asm volatile("" ::: "memory");
         // 6. MFMA over this wave's superblocks
+        v4i acc[MS];
 #pragma unroll
         for (int s = 0; s < SBN; ++s) {
             const int sb = s0 + s;
             if (sb >= s_end) break;
-            v4i acc[MS];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int gi = (GPS == 2) ? h : 0;
@@ -555,7 +560,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                     const uint32_t zc = ASYM ? (128u - zq[s][gi]) * 0x01010101u : 0u;
                     b = unpack_b<ASYM>(w0, w1, zc);
                 }
-                const bool first = (GPS == 2) || h == 0;
+                const bool first = GPS == 0 ? (h == 0 && s % 2 == 0) : ((GPS == 2) || h == 0);
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms) {
                     const uint4 av = *reinterpret_cast<const uint4*>(
@@ -563,7 +568,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                     const v4i A = {int(av.x), int(av.y), int(av.z), int(av.w)};
                     acc[ms] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, b, first ? zero4 : acc[ms], 0, 0, 0);
                 }
-                if (GPS == 2 || h == 1) {
+                if (GPS == 0 ? (h == 1 && s % 2 == 1) : (GPS == 2 || h == 1)) {
                     if (MODE == MODE_PARTIALS) {
                         const int col = tile * 16 + (lane & 15);
 #pragma unroll
@@ -573,7 +578,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                                 const int row = rbeg + ms * 16 + 4 * (lane >> 4) + i;
                                 if (tvalid && row < rend && col < a.N) {
                                     const int v = (ASYM || W8) ? acc[ms][i] : (acc[ms][i] >> 4);
-                                    a.P[(size_t(row) * a.N + col) * a.G + size_t(sb) * GPS + gi] = v;
+                                    a.P[(size_t(row) * a.N + col) * a.G + size_t(gidx(sb, gi))] = v;
                                 }
                             }
                     } else {
@@ -954,6 +959,10 @@ struct PfRegs {
 template <bool ASYM, int GPS, int MODE, bool MOE, bool W8>
 __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a) {
     static_assert(!W8 || (!ASYM && !MOE), "8-bit codes: symmetric, dense");
+    // GPS 0: g = 256, one group per superblock pair (even, odd), which the loop runs back to back
+    static_assert(GPS != 0 || !MOE, "g = 256: dense");
+    constexpr int NG = GPS == 0 ? 1 : GPS;              // scale entries per superblock
+    auto gidx = [](int sb, int gi) { return GPS == 0 ? sb / 2 : sb * GPS + gi; };
     constexpr int SBB = W8 ? 2048 : 1024;                // code bytes per superblock
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -990,7 +999,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     // staging: thread tid owns layout lane (tid % 64) of 16-column tile (tid / 64)
     const int b_tile = min(t0 + wave, ntl16 - 1);
     const int st_q4 = lane >> 4, st_c = lane & 15;
-    const int nmeta_s = 8 * GPS * 4;                     // 16-byte scale pieces
+    const int nmeta_s = 8 * NG * 4;                      // 16-byte scale pieces
     // Activation and code loads go through buffer resources.  Each lane's offset is fixed for
     // the whole K loop and the superblock advances only the scalar offset, so the loop spends
     // no vector instructions on addresses, and the loads are unconditional, so the compiler
@@ -1004,6 +1013,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(codes + size_t(__builtin_amdgcn_readfirstlane(b_tile)) * nsb * SBB), 0, 0x7fffffff,
         0x00020000);
+    const __amdgpu_buffer_rsrc_t sr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(scales_b), 0, 0x7fffffff, 0x00020000);
     int aoff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1029,14 +1040,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
         if (ASYM) {
             r.z = 0;
 #pragma unroll
-            for (int gi = 0; gi < GPS; ++gi)
-                r.z |= uint32_t(zeros_b[(size_t(b_tile) * a.G + size_t(sb) * GPS + gi) * 16 + st_c]) << (8 * gi);
+            for (int gi = 0; gi < NG; ++gi)
+                r.z |= uint32_t(zeros_b[(size_t(b_tile) * a.G + size_t(gidx(sb, gi))) * 16 + st_c]) << (8 * gi);
         }
         {   // every thread loads a piece (threads past nmeta_s repeat one and never store it)
             const int mt = tid % nmeta_s;
-            const int tl = mt / (GPS * 4), gi = (mt / 4) % GPS, q4 = mt % 4;
+            const int tl = mt / (NG * 4), gi = (mt / 4) % NG, q4 = mt % 4;
             const int tile = min(t0 + tl, ntl16 - 1);
-            r.m = *reinterpret_cast<const uint4*>(scales_b + ((size_t(tile) * a.G + size_t(sb) * GPS + gi) * 16 + q4 * 4) * 4);
+            const v4i t = __builtin_amdgcn_raw_buffer_load_b128(sr, ((tile * a.G + gidx(sb, gi)) * 16 + q4 * 4) * 4, 0, 0);
+            r.m = make_uint4(uint32_t(t.x), uint32_t(t.y), uint32_t(t.z), uint32_t(t.w));
         }
     };
     auto lstore = [&](const PfRegs& r, int stage) {
@@ -1064,8 +1076,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
             *reinterpret_cast<v4i*>(st + PF_A_BYTES + ((j * 2 + hl) * PF_BN + col) * 16) = u;
         }
         if (tid < nmeta_s) {
-            const int tl = tid / (GPS * 4), gi = (tid / 4) % GPS, q4 = tid % 4;
-            *reinterpret_cast<uint4*>(st + PF_A_BYTES + PF_B_BYTES + ((tl * GPS + gi) * 16 + q4 * 4) * 4) = r.m;
+            const int tl = tid / (NG * 4), gi = (tid / 4) % NG, q4 = tid % 4;
+            *reinterpret_cast<uint4*>(st + PF_A_BYTES + PF_B_BYTES + ((tl * NG + gi) * 16 + q4 * 4) * 4) = r.m;
         }
     };
 
@@ -1089,7 +1101,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     for (int ns = 0; ns < 2; ++ns) {
         const int colw = wn * 64 + ns * 32 + l32;       // column inside the workgroup tile
         b_off[ns] = PF_A_BYTES + (hi * PF_BN + colw) * 16;
-        s_off[ns] = PF_A_BYTES + PF_B_BYTES + (((colw >> 4) * GPS) * 16 + (colw & 15)) * 4;
+        s_off[ns] = PF_A_BYTES + PF_B_BYTES + (((colw >> 4) * NG) * 16 + (colw & 15)) * 4;
         col_g[ns] = t0 * 16 + colw;
     }
 
@@ -1106,13 +1118,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
             }
 #pragma unroll
             for (int ns = 0; ns < 2; ++ns) B[ns] = *reinterpret_cast<const v4i*>(st + b_off[ns] + j * 2 * PF_BN * 16);
-            const bool first = (GPS == 2) ? ((j & 1) == 0) : (j == 0);
+            const bool first = GPS == 0 ? (j == 0 && sb % 2 == 0) : (GPS == 2) ? ((j & 1) == 0) : (j == 0);
 #pragma unroll
             for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
                 for (int ns = 0; ns < 2; ++ns)
                     acc[ms][ns] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ms], B[ns], first ? zero16 : acc[ms][ns], 0, 0, 0);
-            const bool last = (GPS == 2) ? ((j & 1) == 1) : (j == 3);
+            const bool last = GPS == 0 ? (j == 3 && sb % 2 == 1) : (GPS == 2) ? ((j & 1) == 1) : (j == 3);
             if (last) {
                 if (MODE == MODE_PARTIALS) {
 #pragma unroll
@@ -1125,7 +1137,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
                                 const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
                                 if (row < mend && col < a.N) {
                                     const int v = (ASYM || W8) ? acc[ms][ns][r] : (acc[ms][ns][r] >> 4);
-                                    a.P[(size_t(row) * a.N + col) * a.G + size_t(sb) * GPS + gi] = v;
+                                    a.P[(size_t(row) * a.N + col) * a.G + size_t(gidx(sb, gi))] = v;
                                 }
                             }
                         }
@@ -1404,7 +1416,8 @@ static void launch_decode_shape(const GemmArgs& a, const DecodeCfg& c, dim3 grid
     else launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, false, false, W8>(a, grid, s);
 }
 
-// w8: 8-bit codes (symmetric, dense form only; the entry points check)
+// gps: groups per superblock (2, 1, or 0 for g = 256); w8: 8-bit codes.  g = 256 and 8-bit
+// codes are dense-form only (the entry points check).
 template <int MODE, bool MOE>
 static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool asym, dim3 grid, hipStream_t s,
                           bool w8 = false) {
@@ -1412,9 +1425,16 @@ static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool a
     if constexpr (!MOE) {
         if (w8) {
             if (c.ms == 1) { if (gps == 1) launch_decode_shape<1, 1, false, MODE, false, true>(a, c, grid, s);
-                             else launch_decode_shape<1, 2, false, MODE, false, true>(a, c, grid, s); }
+                             else if (gps == 2) launch_decode_shape<1, 2, false, MODE, false, true>(a, c, grid, s);
+                             else launch_decode_shape<1, 0, false, MODE, false, true>(a, c, grid, s); }
             else { if (gps == 1) launch_decode_shape<2, 1, false, MODE, false, true>(a, c, grid, s);
-                   else launch_decode_shape<2, 2, false, MODE, false, true>(a, c, grid, s); }
+                   else if (gps == 2) launch_decode_shape<2, 2, false, MODE, false, true>(a, c, grid, s);
+                   else launch_decode_shape<2, 0, false, MODE, false, true>(a, c, grid, s); }
+            return;
+        }
+        if (gps == 0) {                                   // g = 256 (dense form only)
+            if (c.ms == 1) { if (asym) W4A8_DEC(1, 0, true); else W4A8_DEC(1, 0, false); }
+            else { if (asym) W4A8_DEC(2, 0, true); else W4A8_DEC(2, 0, false); }
             return;
         }
     }
@@ -1545,14 +1565,20 @@ static void launch_prefill_t(const GemmArgs& a, int mtiles, hipStream_t s) {
     kern<<<dim3(mtiles * ntiles), dim3(PF_THREADS), PF_LDS, s>>>(a);
 }
 
-// w8: 8-bit codes (symmetric, dense form only; the entry points check)
+// gps: groups per superblock (2, 1, or 0 for g = 256); w8: 8-bit codes.  g = 256 and 8-bit
+// codes are dense-form only (the entry points check).
 template <int MODE, bool MOE = false>
 static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s, int mtiles = 0, bool w8 = false) {
     if (!MOE) mtiles = (a.M + PF_BM - 1) / PF_BM;
     if constexpr (!MOE) {
         if (w8) {
             if (gps == 1) launch_prefill_t<false, 1, MODE, false, true>(a, mtiles, s);
-            else launch_prefill_t<false, 2, MODE, false, true>(a, mtiles, s);
+            else if (gps == 2) launch_prefill_t<false, 2, MODE, false, true>(a, mtiles, s);
+            else launch_prefill_t<false, 0, MODE, false, true>(a, mtiles, s);
+            return;
+        }
+        if (gps == 0) {                                   // g = 256
+            if (asym) launch_prefill_t<true, 0, MODE, false>(a, mtiles, s); else launch_prefill_t<false, 0, MODE, false>(a, mtiles, s);
             return;
         }
     }
@@ -1579,8 +1605,9 @@ static dim3 decode_grid(const Layout& L, const DecodeCfg& c, int ytiles) {
     return dim3((ntiles + c.nt - 1) / c.nt, ytiles);
 }
 
+// g = 256 runs on the dense kernels only; the grouped (MoE) entry points reject it
 static bool kernel_format_ok(const w4a8_wdesc* d) {
-    return d->group_size == 64 || d->group_size == 128;
+    return d->group_size == 64 || d->group_size == 128 || d->group_size == 256;
 }
 
 static int dense_mt(int M) { return M <= 16 ? 16 : 32; }
@@ -1687,7 +1714,11 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
         const dim3 grid = decode_grid(L, fc, 1);
         const int gps = SB_K / d->group_size;
         if (L.bits == 8) {
-            if (gps == 1) launch_decode_fused<1, false, true>(a, fc, grid, s); else launch_decode_fused<2, false, true>(a, fc, grid, s);
+            if (gps == 1) launch_decode_fused<1, false, true>(a, fc, grid, s);
+            else if (gps == 2) launch_decode_fused<2, false, true>(a, fc, grid, s);
+            else launch_decode_fused<0, false, true>(a, fc, grid, s);
+        } else if (gps == 0) {
+            if (d->asymmetric) launch_decode_fused<0, true>(a, fc, grid, s); else launch_decode_fused<0, false>(a, fc, grid, s);
         } else if (gps == 1) {
             if (d->asymmetric) launch_decode_fused<1, true>(a, fc, grid, s); else launch_decode_fused<1, false>(a, fc, grid, s);
         } else {
@@ -1799,7 +1830,8 @@ int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int 
                   void* stream) {
     int st = check_gemm_desc(d);
     if (st) return st;
-    if (layout_of(d).bits != 4) return W4A8_EUNSUPPORTED;   // the grouped kernels take 4-bit codes
+    // the grouped kernels take 4-bit codes with g in {64, 128}
+    if (layout_of(d).bits != 4 || d->group_size == 256) return W4A8_EUNSUPPORTED;
     if (rows < 0 || E <= 0 || (out_dtype != W4A8_OUT_BF16 && out_dtype != W4A8_OUT_F32)) return W4A8_EINVAL;
     if (rows == 0) return W4A8_OK;
     if (!Xq || !sx || !offsets || !blobs || !Y) return W4A8_EINVAL;
@@ -1881,7 +1913,9 @@ int w4a8_moe_forward(const void* X, const int32_t* ids, const float* w, int T, i
     if (st) return st;
     st = check_gemm_desc(d_desc);
     if (st) return st;
-    if (layout_of(gu_desc).bits != 4 || layout_of(d_desc).bits != 4) return W4A8_EUNSUPPORTED;
+    if (layout_of(gu_desc).bits != 4 || layout_of(d_desc).bits != 4 || gu_desc->group_size == 256 ||
+        d_desc->group_size == 256)
+        return W4A8_EUNSUPPORTED;
     if (T < 0 || k <= 0 || E <= 0) return W4A8_EINVAL;
     const int H = gu_desc->K, I2 = gu_desc->N;
     if (I2 % 2 || d_desc->K != I2 / 2 || d_desc->N != H) return W4A8_EINVAL;
@@ -1914,22 +1948,20 @@ int w4a8_moe_forward(const void* X, const int32_t* ids, const float* w, int T, i
 
 const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
     if (check_gemm_desc(d) != W4A8_OK || M < 0) return "unsupported";
-    const bool asym = d->asymmetric;
-    const bool g64 = d->group_size == 64;
-    if (layout_of(d).bits == 8) {
-        if (M >= PREFILL_MIN_M) return g64 ? "w8a8_prefill_sym_g64" : "w8a8_prefill_sym_g128";
-        static const char* const n8[2][2] = {{"w8a8_decode_m16_sym_g128", "w8a8_decode_m16_sym_g64"},
-                                             {"w8a8_decode_m32_sym_g128", "w8a8_decode_m32_sym_g64"}};
-        return n8[dense_mt(M) == 32][g64];
-    }
-    if (M >= PREFILL_MIN_M)
-        return asym ? (g64 ? "w4a8_prefill_asym_g64" : "w4a8_prefill_asym_g128")
-                    : (g64 ? "w4a8_prefill_sym_g64" : "w4a8_prefill_sym_g128");
-    // one name per (row tile, format)
-    static const char* const names[2][2][2] = {
-        {{"w4a8_decode_m16_sym_g128", "w4a8_decode_m16_sym_g64"}, {"w4a8_decode_m16_asym_g128", "w4a8_decode_m16_asym_g64"}},
-        {{"w4a8_decode_m32_sym_g128", "w4a8_decode_m32_sym_g64"}, {"w4a8_decode_m32_asym_g128", "w4a8_decode_m32_asym_g64"}}};
-    return names[dense_mt(M) == 32][asym][g64];
+    // one name per (form, row tile, format): [w8][kind: decode m16, decode m32, prefill][asym][g]
+    static const char* const names[2][3][2][3] = {
+        {{{"w4a8_decode_m16_sym_g64", "w4a8_decode_m16_sym_g128", "w4a8_decode_m16_sym_g256"},
+          {"w4a8_decode_m16_asym_g64", "w4a8_decode_m16_asym_g128", "w4a8_decode_m16_asym_g256"}},
+         {{"w4a8_decode_m32_sym_g64", "w4a8_decode_m32_sym_g128", "w4a8_decode_m32_sym_g256"},
+          {"w4a8_decode_m32_asym_g64", "w4a8_decode_m32_asym_g128", "w4a8_decode_m32_asym_g256"}},
+         {{"w4a8_prefill_sym_g64", "w4a8_prefill_sym_g128", "w4a8_prefill_sym_g256"},
+          {"w4a8_prefill_asym_g64", "w4a8_prefill_asym_g128", "w4a8_prefill_asym_g256"}}},
+        {{{"w8a8_decode_m16_sym_g64", "w8a8_decode_m16_sym_g128", "w8a8_decode_m16_sym_g256"}, {}},
+         {{"w8a8_decode_m32_sym_g64", "w8a8_decode_m32_sym_g128", "w8a8_decode_m32_sym_g256"}, {}},
+         {{"w8a8_prefill_sym_g64", "w8a8_prefill_sym_g128", "w8a8_prefill_sym_g256"}, {}}}};
+    const int kind = M >= PREFILL_MIN_M ? 2 : (dense_mt(M) == 32 ? 1 : 0);
+    const int gi = d->group_size == 64 ? 0 : (d->group_size == 128 ? 1 : 2);
+    return names[layout_of(d).bits == 8][kind][d->asymmetric][gi];
 }
 
 }  // extern "C"

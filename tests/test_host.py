@@ -148,6 +148,22 @@ def test_8bit_validation_host():
                                 ctypes.byref(d4), fake, ws, fake, None) in (E, U)
 
 
+def test_g256_names_and_grouped_form_rejected_host():
+    """g = 256 runs on the dense kernels (one group per two superblocks); the grouped (MoE)
+    entry points reject it before any HIP call."""
+    lib = L.lib()
+    d = L.desc(1024, 64, 256, True)
+    assert L.w4a8_kernel_name(d, 1) == "w4a8_decode_m16_asym_g256"
+    assert L.w4a8_kernel_name(d, 20) == "w4a8_decode_m32_asym_g256"
+    assert L.w4a8_kernel_name(d, 40) == "w4a8_prefill_asym_g256"
+    assert L.w4a8_kernel_name(L.desc(1024, 64, 256, False, bits=8), 40) == "w8a8_prefill_sym_g256"
+    assert L.w4a8_kernel_name(L.desc(1024, 64, 64, False), 8) == "w4a8_decode_m16_sym_g64"
+    assert L.w4a8_kernel_name(L.desc(1024, 64, 32, False), 8) == "unsupported"
+    fake = 0x10000
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
+                             None) == L.W4A8_EUNSUPPORTED
+
+
 def test_pack_page_examples_through_library():
     # P3 symmetric group-wise reference example (transposed: groups along K)
     x = np.array([[0.0, -1.0, 0.5, 0.25], [3.0, -2.0, 1.0, 0.0]], np.float32)
