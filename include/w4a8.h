@@ -160,6 +160,18 @@ int w4a8_blob_check(const void* blob_host, size_t blob_bytes, const w4a8_wdesc* 
 int w4a8_quant_act(const void* X_bf16, int M, int K, int ldx, int8_t* Xq, float* sx,
                    void* stream);
 
+/* The same quantization of X diag(alpha)^-1, the activation side of the equivalent
+ * per-channel rescaling Y = (X diag(alpha)^-1) (diag(alpha) W) of P3 "Weight-Activation"
+ * (SmoothQuant: quantization difficulty moved from activations to weights offline).  The
+ * page asks for the scaling to be fused into an adjacent operator; here it is: each
+ * x[m, k] is multiplied by inv_alpha[k] (one float32 product, round to nearest even) and
+ * the per-token rule above applies to the products.  The weight side, diag(alpha) W, is
+ * applied before packing by the caller.
+ *   inv_alpha  device float32 [K], 16-byte aligned (1 / alpha per input channel)
+ * Other arguments, layouts and errors as w4a8_quant_act; EINVAL if inv_alpha is NULL. */
+int w4a8_quant_act_smooth(const void* X_bf16, int M, int K, int ldx, const float* inv_alpha, int8_t* Xq,
+                          float* sx, void* stream);
+
 /* W4A8 GEMM Y = (s_x * Xq) (s_w * (q - z)) (P5 section 4 ideal path; P5 section 8.3
  * epilogue Y[i, j] = s_x[i] s_w[j] acc[i, j], applied per K-group of P5 section 8.4).
  *   Xq, sx    device, from w4a8_quant_act ([M, K] int8 dense, [M] float32)

@@ -22,7 +22,8 @@ HEADER_BYTES = 256
 
 EXPORTED = [
     "w4a8_packed_size", "w4a8_pack", "w4a8_pack_codes", "w4a8_unpack_codes", "w4a8_blob_check",
-    "w4a8_quant_act", "w4a8_gemm", "w4a8_linear", "w4a8_gemm_partials", "w4a8_moe_align", "w4a8_moe_gemm",
+    "w4a8_quant_act", "w4a8_quant_act_smooth", "w4a8_gemm", "w4a8_linear", "w4a8_gemm_partials", "w4a8_moe_align",
+    "w4a8_moe_gemm",
     "w4a8_silu_mul_quant", "w4a8_moe_combine", "w4a8_moe_workspace_size", "w4a8_moe_forward",
     "w4a8_kernel_name", "w4a8_status_string", "w4a8_version",
 ]
@@ -62,6 +63,7 @@ def lib() -> ctypes.CDLL:
             "w4a8_unpack_codes": (I, [P, SZ, DP, P, P, P]),
             "w4a8_blob_check": (I, [P, SZ, DP]),
             "w4a8_quant_act": (I, [P, I, I, I, P, P, VP]),
+            "w4a8_quant_act_smooth": (I, [P, I, I, I, P, P, P, VP]),
             "w4a8_gemm": (I, [P, P, I, P, DP, P, I, I, VP]),
             "w4a8_linear": (I, [P, I, I, I, P, DP, P, I, I, P, P, VP]),
             "w4a8_gemm_partials": (I, [P, I, P, DP, P, VP]),
@@ -189,6 +191,14 @@ def w4a8_quant_act(X, Xq, sx, stream=None) -> None:
     M, K = X.shape
     _check(lib().w4a8_quant_act(_ptr(X), M, K, X.stride(0), _ptr(Xq), _ptr(sx), _stream(stream)),
            "w4a8_quant_act")
+
+
+def w4a8_quant_act_smooth(X, inv_alpha, Xq, sx, stream=None) -> None:
+    """w4a8_quant_act of X diag(alpha)^-1; inv_alpha: float32 [K] on the device."""
+    _require_cuda(X, inv_alpha, Xq, sx)
+    M, K = X.shape
+    _check(lib().w4a8_quant_act_smooth(_ptr(X), M, K, X.stride(0), _ptr(inv_alpha), _ptr(Xq), _ptr(sx),
+                                       _stream(stream)), "w4a8_quant_act_smooth")
 
 
 def w4a8_gemm(Xq, sx, blob_dev, d: WDesc, Y, out_dtype: int = W4A8_OUT_BF16, stream=None) -> None:

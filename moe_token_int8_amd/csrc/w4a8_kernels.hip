@@ -114,25 +114,48 @@ __device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
 // per-token INT8 activation quantization (P1 section 3.3, P5 section 8.3)
 // One 256-thread workgroup per row; each thread holds IT x 8 bf16 values in registers
 // so the row is read from HBM once.
+// SMOOTH: every value is first multiplied by inv_alpha[k] (one float32 product), the
+// activation side of the equivalent rescaling Y = (X diag(alpha)^-1)(diag(alpha) W) (P3
+// "Weight-Activation"), fused here so that it adds no kernel; the product is recomputed,
+// identically, in the quantization pass instead of being held in registers.
 // ------------------------------------------------------------------------------------
-template <int IT>
+template <int IT, bool SMOOTH = false>
 __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ X, int K, int ldx,
-                                                        int8_t* __restrict__ Xq, float* __restrict__ sx) {
+                                                        int8_t* __restrict__ Xq, float* __restrict__ sx,
+                                                        const float* __restrict__ inv_alpha = nullptr) {
     __shared__ uint32_t red[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     const uint16_t* xr = X + size_t(row) * size_t(ldx);
     uint4 v[IT];
     uint32_t amax = 0;
+    // the 8 factors of the values at k (SMOOTH)
+    auto factors = [&](int k, float (&f)[8]) {
+        const float4 a = *reinterpret_cast<const float4*>(inv_alpha + k);
+        const float4 b = *reinterpret_cast<const float4*>(inv_alpha + k + 4);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    };
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int k = (it * 256 + tid) * 8;
         v[it] = make_uint4(0, 0, 0, 0);
         if (k < K) v[it] = *reinterpret_cast<const uint4*>(xr + k);
         const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+        if constexpr (SMOOTH) {
+            if (k < K) {
+                float f[8];
+                factors(k, f);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            amax = max(amax, (w[j] & 0x7fffu) << 16);
-            amax = max(amax, w[j] & 0x7fff0000u);
+                for (int j = 0; j < 4; ++j) {
+                    amax = max(amax, __float_as_uint(bf16_to_f32(w[j] & 0xffffu) * f[2 * j]) & 0x7fffffffu);
+                    amax = max(amax, __float_as_uint(bf16_to_f32(w[j] >> 16) * f[2 * j + 1]) & 0x7fffffffu);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                amax = max(amax, (w[j] & 0x7fffu) << 16);
+                amax = max(amax, w[j] & 0x7fff0000u);
+            }
         }
     }
     amax = block_max_u32(amax, red, 4);
@@ -145,10 +168,17 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
         const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
         uint32_t out[2] = {0, 0};
         if (rs.finite) {
+            float f[8] = {1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (SMOOTH) factors(k, f);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int q0 = quant_one(bf16_to_f32(w[j] & 0xffffu), rs.d, rs.inv, rs.fast);
-                const int q1 = quant_one(bf16_to_f32(w[j] >> 16), rs.d, rs.inv, rs.fast);
+                float x0 = bf16_to_f32(w[j] & 0xffffu), x1 = bf16_to_f32(w[j] >> 16);
+                if constexpr (SMOOTH) {
+                    x0 *= f[2 * j];
+                    x1 *= f[2 * j + 1];
+                }
+                const int q0 = quant_one(x0, rs.d, rs.inv, rs.fast);
+                const int q1 = quant_one(x1, rs.d, rs.inv, rs.fast);
                 const uint32_t pair = (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8);
                 out[j >> 1] |= pair << ((j & 1) * 16);
             }
@@ -1353,8 +1383,10 @@ static int row_iters(int K) {
 }
 
 template <int IT>
-static void launch_quant(const uint16_t* X, int M, int K, int ldx, int8_t* Xq, float* sx, hipStream_t s) {
-    quant_act_kernel<IT><<<dim3(M), dim3(256), 0, s>>>(X, K, ldx, Xq, sx);
+static void launch_quant(const uint16_t* X, int M, int K, int ldx, int8_t* Xq, float* sx, hipStream_t s,
+                         const float* inv_alpha = nullptr) {
+    if (inv_alpha) quant_act_kernel<IT, true><<<dim3(M), dim3(256), 0, s>>>(X, K, ldx, Xq, sx, inv_alpha);
+    else quant_act_kernel<IT><<<dim3(M), dim3(256), 0, s>>>(X, K, ldx, Xq, sx);
 }
 
 template <int IT>
@@ -1641,24 +1673,35 @@ using namespace w4a8;
 
 extern "C" {
 
-int w4a8_quant_act(const void* X, int M, int K, int ldx, int8_t* Xq, float* sx, void* stream) {
+static int quant_act_impl(const void* X, int M, int K, int ldx, const float* inv_alpha, int8_t* Xq, float* sx,
+                          void* stream) {
     if (M < 0 || K <= 0 || ldx < K) return W4A8_EINVAL;
     if (M == 0) return W4A8_OK;
     if (!X || !Xq || !sx) return W4A8_EINVAL;
-    if (K % 16 || ldx % 8 || !aligned16(X) || !aligned16(Xq)) return W4A8_EINVAL;
+    if (K % 16 || ldx % 8 || !aligned16(X) || !aligned16(Xq) || !aligned16(inv_alpha)) return W4A8_EINVAL;
     if (K > 65536) return W4A8_EUNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint16_t* x = static_cast<const uint16_t*>(X);
     switch (row_iters(K)) {
-        case 1: launch_quant<1>(x, M, K, ldx, Xq, sx, s); break;
-        case 2: launch_quant<2>(x, M, K, ldx, Xq, sx, s); break;
-        case 4: launch_quant<4>(x, M, K, ldx, Xq, sx, s); break;
-        case 8: launch_quant<8>(x, M, K, ldx, Xq, sx, s); break;
-        case 16: launch_quant<16>(x, M, K, ldx, Xq, sx, s); break;
-        case 32: launch_quant<32>(x, M, K, ldx, Xq, sx, s); break;
+        case 1: launch_quant<1>(x, M, K, ldx, Xq, sx, s, inv_alpha); break;
+        case 2: launch_quant<2>(x, M, K, ldx, Xq, sx, s, inv_alpha); break;
+        case 4: launch_quant<4>(x, M, K, ldx, Xq, sx, s, inv_alpha); break;
+        case 8: launch_quant<8>(x, M, K, ldx, Xq, sx, s, inv_alpha); break;
+        case 16: launch_quant<16>(x, M, K, ldx, Xq, sx, s, inv_alpha); break;
+        case 32: launch_quant<32>(x, M, K, ldx, Xq, sx, s, inv_alpha); break;
         default: return W4A8_EUNSUPPORTED;
     }
     return launch_status();
+}
+
+int w4a8_quant_act(const void* X, int M, int K, int ldx, int8_t* Xq, float* sx, void* stream) {
+    return quant_act_impl(X, M, K, ldx, nullptr, Xq, sx, stream);
+}
+
+int w4a8_quant_act_smooth(const void* X, int M, int K, int ldx, const float* inv_alpha, int8_t* Xq, float* sx,
+                          void* stream) {
+    if (M > 0 && !inv_alpha) return W4A8_EINVAL;
+    return quant_act_impl(X, M, K, ldx, inv_alpha, Xq, sx, stream);
 }
 
 int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const w4a8_wdesc* d, void* Y,

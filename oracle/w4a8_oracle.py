@@ -37,13 +37,18 @@ Pins (each function is checked against something other than itself in
   effective_bits,
   memory_bytes      P3 closed forms; P5 section 8.4 compression ratios.
   bf16_rne          torch's float32->bfloat16 conversion (library routine).
+  smooth_factors,
+  smooth_weights,
+  quant_act_smooth  the rescaling is exactly equivalent when alpha is a power of two
+                    (products exact: codes equal quant_act of x 2^-e, GEMM unchanged);
+                    inv_alpha = 1 reduces to quant_act; the factor rule's closed form.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = [
-    "bf16_rne", "quant_act", "dequant_act", "quant_weight", "dequant_weight", "gemm_partials",
+    "bf16_rne", "quant_act", "quant_act_smooth", "smooth_factors", "smooth_weights", "dequant_act", "quant_weight", "dequant_weight", "gemm_partials",
     "gemm", "silu_mul", "silu_mul_quant", "moe_align", "moe_layer", "effective_bits",
     "memory_bytes", "compression_vs_fp16",
 ]
@@ -100,6 +105,36 @@ def quant_act(x):
     q = np.where(finite[:, None], q, 0).astype(np.int8)
     s = np.where(finite, s, _F32(np.nan)).astype(_F32)
     return q, s
+
+
+def smooth_factors(x_absmax, w, strength: float = 0.5):
+    """Per-input-channel factors alpha of the equivalent rescaling
+    Y = (X diag(alpha)^-1) (diag(alpha) W) (P3 "Weight-Activation", the SmoothQuant form:
+    offline, moving quantization difficulty from activations to weights).  The page leaves
+    alpha open beyond "per channel, positive"; reading: SmoothQuant's rule
+    alpha_j = max|X_j|^a / max|W_j|^(1-a) with migration strength a, computed in float64
+    and rounded to float32; a channel with a zero maximum on either side keeps alpha = 1.
+    x_absmax: [K] calibration abs-max of each input channel; w: [K, N].  Returns float32 [K]."""
+    xa = np.asarray(x_absmax, np.float64)
+    wa = np.max(np.abs(np.asarray(w, np.float64)), axis=1)
+    ok = (xa > 0) & (wa > 0) & np.isfinite(xa) & np.isfinite(wa)
+    alpha = np.ones_like(xa)
+    alpha[ok] = xa[ok] ** strength / wa[ok] ** (1.0 - strength)
+    return alpha.astype(_F32)
+
+
+def smooth_weights(w, alpha):
+    """diag(alpha) W: row k of W[K, N] times alpha_k, each product rounded to float32."""
+    return (np.asarray(w, _F32) * np.asarray(alpha, _F32)[:, None]).astype(_F32)
+
+
+def quant_act_smooth(x, inv_alpha):
+    """Per-token INT8 quantization of X diag(alpha)^-1: every x[m, k] is first multiplied by
+    inv_alpha[k] (one float32 product, round to nearest even), then quant_act's per-token rule
+    applies to the products (P3 "Weight-Activation": the scaling fused into the adjacent
+    operator, here the activation quantization)."""
+    xs = (np.asarray(x, _F32) * np.asarray(inv_alpha, _F32)[None, :]).astype(_F32)
+    return quant_act(xs)
 
 
 def dequant_act(q, s):

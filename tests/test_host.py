@@ -258,6 +258,9 @@ def test_gpu_entry_points_validate_before_launch():
     assert lib.w4a8_quant_act(mis, 4, 256, 256, fake, fake, None) == E
     assert lib.w4a8_quant_act(None, 4, 256, 256, fake, fake, None) == E
     assert lib.w4a8_quant_act(fake, 4, 131072, 131072, fake, fake, None) == L.W4A8_EUNSUPPORTED
+    assert lib.w4a8_quant_act_smooth(fake, 4, 256, 256, None, fake, fake, None) == E          # no factors
+    assert lib.w4a8_quant_act_smooth(fake, 4, 256, 256, mis, fake, fake, None) == E           # misaligned
+    assert lib.w4a8_quant_act_smooth(fake, 0, 256, 256, None, fake, fake, None) == L.W4A8_OK
     assert lib.w4a8_gemm(fake, fake, 0, fake, ctypes.byref(d), fake, 32, 0, None) == L.W4A8_OK
     assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(d), fake, 32, 7, None) == E
     assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(d), fake, 16, 0, None) == E   # ldy < N

@@ -396,3 +396,45 @@ def test_bf16_rne_matches_torch():
     ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(O.bf16_rne(v), ref)
     assert np.isinf(O.bf16_rne(np.array([3.5e38]))[0])
+
+
+# ------------------------------------------------------------------ SmoothQuant rescaling
+def test_smooth_identity_and_power_of_two_exactness():
+    """inv_alpha = 1 reduces to quant_act; with alpha a power of two every product is exact, so
+    the codes equal quant_act of x * 2^-e and the dequantized GEMM of the rescaled pair equals
+    the plain one on the same grid (P3 "Weight-Activation": the two forms are equal in real
+    arithmetic)."""
+    x = W.bf16_values(W.random_activations(31, 6, 256, outlier_cols=3, outlier_scale=20.0))
+    q0, s0 = O.quant_act(x)
+    q1, s1 = O.quant_act_smooth(x, np.ones(256, F32))
+    assert np.array_equal(q0, q1) and np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
+    e = np.random.default_rng(2).integers(-3, 4, 256)
+    alpha = (2.0 ** e).astype(F32)
+    q2, s2 = O.quant_act_smooth(x, (1.0 / alpha).astype(F32))
+    q3, s3 = O.quant_act((x * (2.0 ** -e)).astype(F32))
+    assert np.array_equal(q2, q3) and np.array_equal(s2.view(np.uint32), s3.view(np.uint32))
+    w = W.random_weights(5, 256, 7)
+    ws = O.smooth_weights(w, alpha)
+    assert np.array_equal(ws, (w * alpha[:, None]).astype(F32))
+    lhs = (x.astype(np.float64) / alpha.astype(np.float64)) @ ws.astype(np.float64)
+    assert np.allclose(lhs, x.astype(np.float64) @ w.astype(np.float64), rtol=0, atol=1e-12)
+
+
+def test_smooth_factor_rule():
+    """alpha_j = max|X_j|^a / max|W_j|^(1-a), zero channels keep 1; a = 1 moves all of the
+    activation range into the weights (every rescaled channel max becomes 1)."""
+    rs = np.random.default_rng(4)
+    xa = np.abs(rs.standard_normal(64)) * 5
+    xa[3] = 0.0
+    w = rs.standard_normal((64, 9)).astype(F32) * 0.02
+    w[7] = 0.0
+    a = O.smooth_factors(xa, w, 0.5)
+    wa = np.max(np.abs(w.astype(np.float64)), axis=1)
+    for j in range(64):
+        if j in (3, 7):
+            assert a[j] == 1.0
+        else:
+            assert a[j] == np.float32(np.sqrt(xa[j]) / np.sqrt(wa[j]))
+    a1 = O.smooth_factors(xa, w, 1.0)
+    ok = (xa > 0) & (wa > 0)
+    assert np.allclose((xa / a1.astype(np.float64))[ok], 1.0, rtol=1e-6)
