@@ -57,7 +57,8 @@ typedef enum { W4A8_OUT_BF16 = 0, W4A8_OUT_F32 = 1 } w4a8_out_dtype;
  *   group_size  g: consecutive k sharing one scale per column (P5 section 8.4);
  *               must divide K.  Kernels implement g in {64, 128, 256} (256: dense
  *               GEMMs only; the MoE entry points return EUNSUPPORTED); pack accepts
- *               g in {32, 64, 128, 256}.
+ *               g in {32, 64, 128, 256}.  The GPU entry points also return
+ *               EUNSUPPORTED for a blob whose codes reach 2 GiB (32-bit offsets).
  *   asymmetric  0: signed codes q in [-7, 7], zero point 0 (P3 "Basic mapping",
  *                  symmetric form);
  *               1: unsigned codes q in [0, 15] with a uint8 zero point z per

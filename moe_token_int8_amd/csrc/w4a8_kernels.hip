@@ -1664,6 +1664,9 @@ static int check_gemm_desc(const w4a8_wdesc* d) {
     int st = desc_status(d);
     if (st) return st;
     if (!kernel_format_ok(d)) return W4A8_EUNSUPPORTED;
+    // the kernels address one blob's codes and scales with 32-bit offsets
+    const Layout L = layout_of(d);
+    if (L.codes_bytes >= (size_t(1) << 31) || L.scales_bytes >= (size_t(1) << 31)) return W4A8_EUNSUPPORTED;
     return W4A8_OK;
 }
 

@@ -298,6 +298,18 @@ def test_gpu_entry_points_validate_before_launch():
     assert L.w4a8_moe_workspace_size(0, 0, 1, 1, 1) == 0
 
 
+def test_codes_beyond_two_gib_unsupported_host():
+    """Blobs whose codes reach 2 GiB are rejected by the GPU entry points (32-bit offsets)."""
+    lib = L.lib()
+    fake = 0x10000
+    d = L.desc(65536, 65536, 128, False)               # 2 GiB of 4-bit codes
+    assert L.w4a8_packed_size(d) > (1 << 31)
+    assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(d), fake, 65536, 0, None) == L.W4A8_EUNSUPPORTED
+    assert L.w4a8_kernel_name(d, 4) == "unsupported"
+    d_ok = L.desc(65536, 32768, 128, False)            # 1 GiB
+    assert L.w4a8_kernel_name(d_ok, 4) == "w4a8_decode_m16_sym_g128"
+
+
 def test_prefill_offset_limits_host():
     """The prefill kernel addresses activations with 32-bit offsets: a 256-row tile of K >= 2^23
     (dense), or gathered rows times K >= 2^31 (grouped form), is rejected before any launch."""
