@@ -258,11 +258,13 @@ def cpu_baseline(args, leg, W):
 # ---------------------------------------------------------------------------------- prefill
 def prefill_leg(args, L, W, torch, dev, steps):
     """The projection pair at M = 4096 (asymmetric g128), and the up projection again with
-    g = 256: half the per-group epilogues, the same weights otherwise."""
+    g = 256 (half the per-group epilogues) and with per-channel scales (g = K: one epilogue),
+    the same weights otherwise."""
     out = {}
     import dataclasses
     g256 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "g256"), group_size=256)
-    for cfg in (W.C3_UP, W.C3_DOWN, g256):
+    gk = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "gK"), group_size=W.C3_UP.K)
+    for cfg in (W.C3_UP, W.C3_DOWN, g256, gk):
         d = L.desc(cfg.K, cfg.N, cfg.group_size, cfg.asymmetric)
         _, Wt = W.dense_inputs(cfg, M=1)
         blob = torch.from_numpy(L.w4a8_pack(d, Wt)).to(dev)

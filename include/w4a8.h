@@ -55,9 +55,13 @@ typedef enum { W4A8_OUT_BF16 = 0, W4A8_OUT_F32 = 1 } w4a8_out_dtype;
  * granularity, execution types must each be stated).
  *   K, N        weight matrix W[K, N]
  *   group_size  g: consecutive k sharing one scale per column (P5 section 8.4);
- *               must divide K.  Kernels implement g in {64, 128, 256} (256: dense
- *               GEMMs only; the MoE entry points return EUNSUPPORTED); pack accepts
- *               g in {32, 64, 128, 256}.  The GPU entry points also return
+ *               must divide K.  pack accepts g in {32, 64, 128, 256} and g = K (one
+ *               scale, and zero point, per output column: the per-channel granularity
+ *               of P5 section 8.3).  Kernels implement g in {64, 128, 256} and g = K;
+ *               256 and K run on the dense GEMMs only (the MoE entry points return
+ *               EUNSUPPORTED), and g = K needs g * 127 * 15 < 2^31 (4-bit codes) or
+ *               g * 127 * 127 < 2^31 (8-bit codes), the reach of the int32 group sum;
+ *               otherwise EUNSUPPORTED.  The GPU entry points also return
  *               EUNSUPPORTED for a blob whose codes reach 2 GiB (32-bit offsets).
  *   asymmetric  0: signed codes q in [-7, 7], zero point 0 (P3 "Basic mapping",
  *                  symmetric form);
@@ -203,7 +207,9 @@ int w4a8_linear(const void* X_bf16, int M, int K, int ldx, const void* blob_dev,
 /* Test export of the same main loop: INT32 per-group partial sums
  * P[m, n, i] = sum_{k in group i} Xq[m, k] (q[k, n] - z[i, n]) written to device
  * int32 [M, N, K/g].  (P3 "Correctness contract" item 3: the accumulator covers the
- * reduction: |P| <= g * 127 * 15 < 2^31.)  Same EINVAL size limit as w4a8_gemm. */
+ * reduction: |P| <= g * 127 * 15, or g * 127 * 127 with 8-bit codes, < 2^31.)  Same
+ * EINVAL size limit as w4a8_gemm.  With g = K and M <= 32 (the decode kernels, which split
+ * K across waves) it returns EUNSUPPORTED. */
 int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob_dev, const w4a8_wdesc* d,
                        int32_t* P, void* stream);
 

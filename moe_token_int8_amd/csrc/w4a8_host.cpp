@@ -24,7 +24,7 @@ bool desc_valid(const w4a8_wdesc* d) {
     if (d->weight_bits != 0 && d->weight_bits != 4 && d->weight_bits != 8) return false;
     if (d->weight_bits == 8 && d->asymmetric) return false;   // 8-bit codes are symmetric
     const int g = d->group_size;
-    if (g != 32 && g != 64 && g != 128 && g != 256) return false;
+    if (g != 32 && g != 64 && g != 128 && g != 256 && g != d->K) return false;   // g = K: per channel
     if (d->K % g) return false;            // groups cannot cross rows (P3 reference)
     return true;
 }

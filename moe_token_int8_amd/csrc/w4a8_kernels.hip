@@ -368,9 +368,12 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     static_assert(!W8 || (!ASYM && !MOE), "8-bit codes: symmetric, dense");
     // GPS: groups per superblock, 2 (g = 64) or 1 (g = 128); 0 is g = 256, one group per two
     // superblocks (a wave's superblocks come in aligned pairs, so a group never straddles waves)
-    static_assert(GPS != 0 || !MOE, "g = 256: dense");
-    constexpr int NG = GPS == 0 ? 1 : GPS;              // scale entries per superblock
-    auto gidx = [](int sb, int gi) { return GPS == 0 ? sb / 2 : sb * GPS + gi; };
+    // GPS -1: per-channel scales (g = K): each wave converts its slice's int32 sum once, and
+    // the slices add in the fixed float32 reduction below
+    static_assert(GPS > 0 || !MOE, "g = 256 and per-channel: dense");
+    static_assert(GPS >= 0 || MODE == MODE_OUT, "per-channel partials: the prefill kernel only");
+    constexpr int NG = GPS <= 0 ? 1 : GPS;              // scale entries per superblock
+    auto gidx = [](int sb, int gi) { return GPS < 0 ? 0 : GPS == 0 ? sb / 2 : sb * GPS + gi; };
     constexpr uint32_t SBB = W8 ? 2048u : 1024u;         // bytes per superblock
     constexpr uint32_t LB = W8 ? 32u : 16u;              // bytes per layout lane
     constexpr int MT = S::MT, NTHR = S::NTHR, CS = S::CS, ROWB = S::ROWB, APT = S::APT;
@@ -590,7 +593,9 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                     const uint32_t zc = ASYM ? (128u - zq[s][gi]) * 0x01010101u : 0u;
                     b = unpack_b<ASYM>(w0, w1, zc);
                 }
-                const bool first = GPS == 0 ? (h == 0 && s % 2 == 0) : ((GPS == 2) || h == 0);
+                const bool first = GPS < 0    ? (h == 0 && s == 0)
+                                   : GPS == 0 ? (h == 0 && s % 2 == 0)
+                                              : ((GPS == 2) || h == 0);
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms) {
                     const uint4 av = *reinterpret_cast<const uint4*>(
@@ -598,7 +603,9 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                     const v4i A = {int(av.x), int(av.y), int(av.z), int(av.w)};
                     acc[ms] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, b, first ? zero4 : acc[ms], 0, 0, 0);
                 }
-                if (GPS == 0 ? (h == 1 && s % 2 == 1) : (GPS == 2 || h == 1)) {
+                if (GPS < 0    ? (h == 1 && sb == s_end - 1)
+                    : GPS == 0 ? (h == 1 && s % 2 == 1)
+                               : (GPS == 2 || h == 1)) {
                     if (MODE == MODE_PARTIALS) {
                         const int col = tile * 16 + (lane & 15);
 #pragma unroll
@@ -990,9 +997,10 @@ template <bool ASYM, int GPS, int MODE, bool MOE, bool W8>
 __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a) {
     static_assert(!W8 || (!ASYM && !MOE), "8-bit codes: symmetric, dense");
     // GPS 0: g = 256, one group per superblock pair (even, odd), which the loop runs back to back
-    static_assert(GPS != 0 || !MOE, "g = 256: dense");
-    constexpr int NG = GPS == 0 ? 1 : GPS;              // scale entries per superblock
-    auto gidx = [](int sb, int gi) { return GPS == 0 ? sb / 2 : sb * GPS + gi; };
+    // GPS -1: per-channel scales (g = K), one int32 sum over all of K and one epilogue
+    static_assert(GPS > 0 || !MOE, "g = 256 and per-channel: dense");
+    constexpr int NG = GPS <= 0 ? 1 : GPS;              // scale entries per superblock
+    auto gidx = [](int sb, int gi) { return GPS < 0 ? 0 : GPS == 0 ? sb / 2 : sb * GPS + gi; };
     constexpr int SBB = W8 ? 2048 : 1024;                // code bytes per superblock
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1148,13 +1156,17 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
             }
 #pragma unroll
             for (int ns = 0; ns < 2; ++ns) B[ns] = *reinterpret_cast<const v4i*>(st + b_off[ns] + j * 2 * PF_BN * 16);
-            const bool first = GPS == 0 ? (j == 0 && sb % 2 == 0) : (GPS == 2) ? ((j & 1) == 0) : (j == 0);
+            const bool first = GPS < 0    ? (j == 0 && sb == 0)
+                             : GPS == 0 ? (j == 0 && sb % 2 == 0)
+                             : GPS == 2 ? ((j & 1) == 0) : (j == 0);
 #pragma unroll
             for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
                 for (int ns = 0; ns < 2; ++ns)
                     acc[ms][ns] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ms], B[ns], first ? zero16 : acc[ms][ns], 0, 0, 0);
-            const bool last = GPS == 0 ? (j == 3 && sb % 2 == 1) : (GPS == 2) ? ((j & 1) == 1) : (j == 3);
+            const bool last = GPS < 0    ? (j == 3 && sb == nsb - 1)
+                            : GPS == 0 ? (j == 3 && sb % 2 == 1)
+                            : GPS == 2 ? ((j & 1) == 1) : (j == 3);
             if (last) {
                 if (MODE == MODE_PARTIALS) {
 #pragma unroll
@@ -1448,8 +1460,8 @@ static void launch_decode_shape(const GemmArgs& a, const DecodeCfg& c, dim3 grid
     else launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, false, false, W8>(a, grid, s);
 }
 
-// gps: groups per superblock (2, 1, or 0 for g = 256); w8: 8-bit codes.  g = 256 and 8-bit
-// codes are dense-form only (the entry points check).
+// gps: groups per superblock (2, 1, 0 for g = 256, -1 per-channel); w8: 8-bit codes.  g = 256,
+// per-channel and 8-bit codes are dense-form only (the entry points check).
 template <int MODE, bool MOE>
 static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool asym, dim3 grid, hipStream_t s,
                           bool w8 = false) {
@@ -1458,16 +1470,25 @@ static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool a
         if (w8) {
             if (c.ms == 1) { if (gps == 1) launch_decode_shape<1, 1, false, MODE, false, true>(a, c, grid, s);
                              else if (gps == 2) launch_decode_shape<1, 2, false, MODE, false, true>(a, c, grid, s);
-                             else launch_decode_shape<1, 0, false, MODE, false, true>(a, c, grid, s); }
+                             else if (gps == 0) launch_decode_shape<1, 0, false, MODE, false, true>(a, c, grid, s);
+                             else if constexpr (MODE == MODE_OUT) launch_decode_shape<1, -1, false, MODE, false, true>(a, c, grid, s); }
             else { if (gps == 1) launch_decode_shape<2, 1, false, MODE, false, true>(a, c, grid, s);
                    else if (gps == 2) launch_decode_shape<2, 2, false, MODE, false, true>(a, c, grid, s);
-                   else launch_decode_shape<2, 0, false, MODE, false, true>(a, c, grid, s); }
+                   else if (gps == 0) launch_decode_shape<2, 0, false, MODE, false, true>(a, c, grid, s);
+                   else if constexpr (MODE == MODE_OUT) launch_decode_shape<2, -1, false, MODE, false, true>(a, c, grid, s); }
             return;
         }
         if (gps == 0) {                                   // g = 256 (dense form only)
             if (c.ms == 1) { if (asym) W4A8_DEC(1, 0, true); else W4A8_DEC(1, 0, false); }
             else { if (asym) W4A8_DEC(2, 0, true); else W4A8_DEC(2, 0, false); }
             return;
+        }
+        if constexpr (MODE == MODE_OUT) {
+            if (gps < 0) {                                // per-channel (dense form, outputs only)
+                if (c.ms == 1) { if (asym) W4A8_DEC(1, -1, true); else W4A8_DEC(1, -1, false); }
+                else { if (asym) W4A8_DEC(2, -1, true); else W4A8_DEC(2, -1, false); }
+                return;
+            }
         }
     }
     if (c.ms == 1) {
@@ -1597,8 +1618,8 @@ static void launch_prefill_t(const GemmArgs& a, int mtiles, hipStream_t s) {
     kern<<<dim3(mtiles * ntiles), dim3(PF_THREADS), PF_LDS, s>>>(a);
 }
 
-// gps: groups per superblock (2, 1, or 0 for g = 256); w8: 8-bit codes.  g = 256 and 8-bit
-// codes are dense-form only (the entry points check).
+// gps: groups per superblock (2, 1, 0 for g = 256, -1 per-channel); w8: 8-bit codes.  g = 256,
+// per-channel and 8-bit codes are dense-form only (the entry points check).
 template <int MODE, bool MOE = false>
 static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s, int mtiles = 0, bool w8 = false) {
     if (!MOE) mtiles = (a.M + PF_BM - 1) / PF_BM;
@@ -1606,11 +1627,16 @@ static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s,
         if (w8) {
             if (gps == 1) launch_prefill_t<false, 1, MODE, false, true>(a, mtiles, s);
             else if (gps == 2) launch_prefill_t<false, 2, MODE, false, true>(a, mtiles, s);
-            else launch_prefill_t<false, 0, MODE, false, true>(a, mtiles, s);
+            else if (gps == 0) launch_prefill_t<false, 0, MODE, false, true>(a, mtiles, s);
+            else launch_prefill_t<false, -1, MODE, false, true>(a, mtiles, s);
             return;
         }
         if (gps == 0) {                                   // g = 256
             if (asym) launch_prefill_t<true, 0, MODE, false>(a, mtiles, s); else launch_prefill_t<false, 0, MODE, false>(a, mtiles, s);
+            return;
+        }
+        if (gps < 0) {                                    // per-channel
+            if (asym) launch_prefill_t<true, -1, MODE, false>(a, mtiles, s); else launch_prefill_t<false, -1, MODE, false>(a, mtiles, s);
             return;
         }
     }
@@ -1637,9 +1663,27 @@ static dim3 decode_grid(const Layout& L, const DecodeCfg& c, int ytiles) {
     return dim3((ntiles + c.nt - 1) / c.nt, ytiles);
 }
 
-// g = 256 runs on the dense kernels only; the grouped (MoE) entry points reject it
+// g = 256 and per-channel scales (g = K) run on the dense kernels only; the grouped (MoE)
+// entry points reject them.  One group's sum stays in an int32 accumulator, so g * 127 *
+// max|q - z| must stay below 2^31: this bounds K for per-channel scales (K < 1127304 with
+// 4-bit codes, K < 133144 with 8-bit codes).
 static bool kernel_format_ok(const w4a8_wdesc* d) {
-    return d->group_size == 64 || d->group_size == 128 || d->group_size == 256;
+    const int g = d->group_size;
+    if (g != 64 && g != 128 && g != 256 && g != d->K) return false;
+    const int64_t qr = d->weight_bits == 8 ? 127 : 15;
+    return int64_t(g) * 127 * qr < (int64_t(1) << 31);
+}
+
+// Groups per 128-deep superblock as the kernels' GPS: 2 (g = 64), 1 (g = 128), 0 (g = 256:
+// one group per two superblocks), -1 (per-channel: g = K > 256, one group over all of K).
+static int gps_of(const w4a8_wdesc* d) {
+    if (d->group_size == d->K && d->K > 256) return -1;
+    return SB_K / d->group_size;
+}
+
+// The grouped (MoE) kernels take 4-bit codes with g in {64, 128}.
+static bool grouped_format_ok(const w4a8_wdesc* d) {
+    return layout_of(d).bits == 4 && gps_of(d) > 0;
 }
 
 static int dense_mt(int M) { return M <= 16 ? 16 : 32; }
@@ -1722,14 +1766,14 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
     a.out_f32 = out_dtype == W4A8_OUT_F32;
     if (M >= PREFILL_MIN_M) {
         if (!prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
-        launch_prefill<MODE_OUT>(a, SB_K / d->group_size, d->asymmetric, static_cast<hipStream_t>(stream), 0,
+        launch_prefill<MODE_OUT>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), 0,
                                  L.bits == 8);
         return launch_status();
     }
     const int mt = dense_mt(M);
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
-    launch_decode<MODE_OUT, false>(a, c, SB_K / d->group_size, d->asymmetric, grid, static_cast<hipStream_t>(stream),
+    launch_decode<MODE_OUT, false>(a, c, gps_of(d), d->asymmetric, grid, static_cast<hipStream_t>(stream),
                                    L.bits == 8);
     return launch_status();
 }
@@ -1758,13 +1802,16 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
         a.out_f32 = out_dtype == W4A8_OUT_F32;
         hipStream_t s = static_cast<hipStream_t>(stream);
         const dim3 grid = decode_grid(L, fc, 1);
-        const int gps = SB_K / d->group_size;
+        const int gps = gps_of(d);
         if (L.bits == 8) {
             if (gps == 1) launch_decode_fused<1, false, true>(a, fc, grid, s);
             else if (gps == 2) launch_decode_fused<2, false, true>(a, fc, grid, s);
-            else launch_decode_fused<0, false, true>(a, fc, grid, s);
+            else if (gps == 0) launch_decode_fused<0, false, true>(a, fc, grid, s);
+            else launch_decode_fused<-1, false, true>(a, fc, grid, s);
         } else if (gps == 0) {
             if (d->asymmetric) launch_decode_fused<0, true>(a, fc, grid, s); else launch_decode_fused<0, false>(a, fc, grid, s);
+        } else if (gps < 0) {
+            if (d->asymmetric) launch_decode_fused<-1, true>(a, fc, grid, s); else launch_decode_fused<-1, false>(a, fc, grid, s);
         } else if (gps == 1) {
             if (d->asymmetric) launch_decode_fused<1, true>(a, fc, grid, s); else launch_decode_fused<1, false>(a, fc, grid, s);
         } else {
@@ -1788,14 +1835,16 @@ int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob, const w4a8_wde
     a.P = P;
     if (M >= PREFILL_MIN_M) {
         if (!prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
-        launch_prefill<MODE_PARTIALS>(a, SB_K / d->group_size, d->asymmetric, static_cast<hipStream_t>(stream), 0,
+        launch_prefill<MODE_PARTIALS>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), 0,
                                       L.bits == 8);
         return launch_status();
     }
+    // per-channel partials span all of K, which the decode kernels split across waves
+    if (gps_of(d) < 0) return W4A8_EUNSUPPORTED;
     const int mt = dense_mt(M);
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
-    launch_decode<MODE_PARTIALS, false>(a, c, SB_K / d->group_size, d->asymmetric, grid,
+    launch_decode<MODE_PARTIALS, false>(a, c, gps_of(d), d->asymmetric, grid,
                                         static_cast<hipStream_t>(stream), L.bits == 8);
     return launch_status();
 }
@@ -1848,7 +1897,7 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
         // experts with rows_e >= 128 (surplus workgroups find no tile and exit)
         if (!prefill_offsets_fit(L.K, gather ? (size_t(rows) + k - 1) / k : size_t(rows))) return W4A8_EINVAL;
         a.moe_lo = MOE_PREFILL_MIN_ROWS;
-        launch_prefill<MODE_OUT, true>(a, SB_K / d->group_size, d->asymmetric, s,
+        launch_prefill<MODE_OUT, true>(a, gps_of(d), d->asymmetric, s,
                                        rows / PF_BM + rows / MOE_PREFILL_MIN_ROWS + 1);
         a.moe_lo = 0;
         a.moe_hi = MOE_PREFILL_MIN_ROWS;
@@ -1863,11 +1912,11 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
     if (kslice_cfg(L.K, kmt, &kc, true)) {
         // row loop: a workgroup runs up to MOE_KSLICE_ROWS rows of its expert
         const int kslots = kc.rl ? rows / MOE_KSLICE_ROWS + std::min(E, rows) + 1 : rows / kmt + std::min(E, rows) + 1;
-        launch_kslice<MODE_OUT, true>(a, kc, kmt / 16, SB_K / d->group_size, d->asymmetric, kslots, s);
+        launch_kslice<MODE_OUT, true>(a, kc, kmt / 16, gps_of(d), d->asymmetric, kslots, s);
         return launch_status();
     }
     const DecodeCfg c = decode_cfg(L.K, mt);
-    launch_decode<MODE_OUT, true>(a, c, SB_K / d->group_size, d->asymmetric, decode_grid(L, c, slots), s);
+    launch_decode<MODE_OUT, true>(a, c, gps_of(d), d->asymmetric, decode_grid(L, c, slots), s);
     return launch_status();
 }
 
@@ -1876,8 +1925,7 @@ int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int 
                   void* stream) {
     int st = check_gemm_desc(d);
     if (st) return st;
-    // the grouped kernels take 4-bit codes with g in {64, 128}
-    if (layout_of(d).bits != 4 || d->group_size == 256) return W4A8_EUNSUPPORTED;
+    if (!grouped_format_ok(d)) return W4A8_EUNSUPPORTED;
     if (rows < 0 || E <= 0 || (out_dtype != W4A8_OUT_BF16 && out_dtype != W4A8_OUT_F32)) return W4A8_EINVAL;
     if (rows == 0) return W4A8_OK;
     if (!Xq || !sx || !offsets || !blobs || !Y) return W4A8_EINVAL;
@@ -1959,9 +2007,7 @@ int w4a8_moe_forward(const void* X, const int32_t* ids, const float* w, int T, i
     if (st) return st;
     st = check_gemm_desc(d_desc);
     if (st) return st;
-    if (layout_of(gu_desc).bits != 4 || layout_of(d_desc).bits != 4 || gu_desc->group_size == 256 ||
-        d_desc->group_size == 256)
-        return W4A8_EUNSUPPORTED;
+    if (!grouped_format_ok(gu_desc) || !grouped_format_ok(d_desc)) return W4A8_EUNSUPPORTED;
     if (T < 0 || k <= 0 || E <= 0) return W4A8_EINVAL;
     const int H = gu_desc->K, I2 = gu_desc->N;
     if (I2 % 2 || d_desc->K != I2 / 2 || d_desc->N != H) return W4A8_EINVAL;
@@ -1995,18 +2041,18 @@ int w4a8_moe_forward(const void* X, const int32_t* ids, const float* w, int T, i
 const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
     if (check_gemm_desc(d) != W4A8_OK || M < 0) return "unsupported";
     // one name per (form, row tile, format): [w8][kind: decode m16, decode m32, prefill][asym][g]
-    static const char* const names[2][3][2][3] = {
-        {{{"w4a8_decode_m16_sym_g64", "w4a8_decode_m16_sym_g128", "w4a8_decode_m16_sym_g256"},
-          {"w4a8_decode_m16_asym_g64", "w4a8_decode_m16_asym_g128", "w4a8_decode_m16_asym_g256"}},
-         {{"w4a8_decode_m32_sym_g64", "w4a8_decode_m32_sym_g128", "w4a8_decode_m32_sym_g256"},
-          {"w4a8_decode_m32_asym_g64", "w4a8_decode_m32_asym_g128", "w4a8_decode_m32_asym_g256"}},
-         {{"w4a8_prefill_sym_g64", "w4a8_prefill_sym_g128", "w4a8_prefill_sym_g256"},
-          {"w4a8_prefill_asym_g64", "w4a8_prefill_asym_g128", "w4a8_prefill_asym_g256"}}},
-        {{{"w8a8_decode_m16_sym_g64", "w8a8_decode_m16_sym_g128", "w8a8_decode_m16_sym_g256"}, {}},
-         {{"w8a8_decode_m32_sym_g64", "w8a8_decode_m32_sym_g128", "w8a8_decode_m32_sym_g256"}, {}},
-         {{"w8a8_prefill_sym_g64", "w8a8_prefill_sym_g128", "w8a8_prefill_sym_g256"}, {}}}};
+#define W4A8_NAMES(P, K, S) {P K S "_g64", P K S "_g128", P K S "_g256", P K S "_gK"}
+    static const char* const names[2][3][2][4] = {
+        {{W4A8_NAMES("w4a8", "_decode_m16", "_sym"), W4A8_NAMES("w4a8", "_decode_m16", "_asym")},
+         {W4A8_NAMES("w4a8", "_decode_m32", "_sym"), W4A8_NAMES("w4a8", "_decode_m32", "_asym")},
+         {W4A8_NAMES("w4a8", "_prefill", "_sym"), W4A8_NAMES("w4a8", "_prefill", "_asym")}},
+        {{W4A8_NAMES("w8a8", "_decode_m16", "_sym"), {}},
+         {W4A8_NAMES("w8a8", "_decode_m32", "_sym"), {}},
+         {W4A8_NAMES("w8a8", "_prefill", "_sym"), {}}}};
+#undef W4A8_NAMES
     const int kind = M >= PREFILL_MIN_M ? 2 : (dense_mt(M) == 32 ? 1 : 0);
-    const int gi = d->group_size == 64 ? 0 : (d->group_size == 128 ? 1 : 2);
+    const int gps = gps_of(d);
+    const int gi = gps == 2 ? 0 : gps == 1 ? 1 : gps == 0 ? 2 : 3;
     return names[layout_of(d).bits == 8][kind][d->asymmetric][gi];
 }
 

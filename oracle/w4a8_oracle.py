@@ -216,8 +216,8 @@ def gemm_partials(xq, codes, zeros, group_size: int):
     This is the INT8 x INT8 -> INT32 accumulation of P5 section 4 (acc_int32) restricted to one
     K-group, with the weight zero point subtracted from the code (P5 section 7 expansion with
     zp_x = 0).  Each group is one float64 matrix product of small integers: every product and
-    every partial sum is an integer below 2**18, so the result is exact in any summation
-    order.  Returns int64 [M, N, K/g].
+    every partial sum is an integer of magnitude at most 127 * 255 * g, far below 2**53, so the
+    result is exact in any summation order.  Returns int64 [M, N, K/g].
     """
     xq = np.asarray(xq)
     codes = np.asarray(codes)

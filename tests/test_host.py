@@ -164,6 +164,27 @@ def test_g256_names_and_grouped_form_rejected_host():
                              None) == L.W4A8_EUNSUPPORTED
 
 
+def test_perchannel_names_and_limits_host():
+    """g = K is the per-channel form: dense kernels only; the decode kernels' partial-sum export
+    and the grouped entry points return EUNSUPPORTED before any HIP call."""
+    lib = L.lib()
+    fake = 0x10000
+    d = L.desc(4096, 64, 4096, True)
+    assert L.w4a8_packed_size(d) > 0
+    assert L.w4a8_kernel_name(d, 1) == "w4a8_decode_m16_asym_gK"
+    assert L.w4a8_kernel_name(d, 64) == "w4a8_prefill_asym_gK"
+    assert lib.w4a8_gemm_partials(fake, 4, fake, ctypes.byref(d), fake, None) == L.W4A8_EUNSUPPORTED
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
+                             None) == L.W4A8_EUNSUPPORTED
+    assert L.w4a8_packed_size(L.desc(4096, 64, 2048, True)) == 0          # neither a listed g nor K
+    # one group's int32 sum must hold g * 127 * max|q - z|: K = 133248 with 8-bit codes does not
+    # (133248 * 127 * 127 > 2^31) and is rejected; K = 133120 still fits
+    big = L.desc(133248, 16, 133248, False, bits=8)
+    assert L.w4a8_packed_size(big) > 0
+    assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(big), fake, 16, 0, None) == L.W4A8_EUNSUPPORTED
+    assert 133120 * 127 * 127 < 2 ** 31 < 133248 * 127 * 127
+
+
 def test_pack_page_examples_through_library():
     # P3 symmetric group-wise reference example (transposed: groups along K)
     x = np.array([[0.0, -1.0, 0.5, 0.25], [3.0, -2.0, 1.0, 0.0]], np.float32)
