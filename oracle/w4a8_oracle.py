@@ -42,13 +42,22 @@ Pins (each function is checked against something other than itself in
   quant_act_smooth  the rescaling is exactly equivalent when alpha is a power of two
                     (products exact: codes equal quant_act of x 2^-e, GEMM unchanged);
                     inv_alpha = 1 reduces to quant_act; the factor rule's closed form.
+  calibrate_act_scale,
+  quant_act_static  with each row's own dynamic scale it reduces to quant_act; exact
+                    quotients on a power-of-two scale (ties to even, saturation, NaN,
+                    infinities); the calibrated scale of a batch is the largest per-token
+                    scale of its rows.
+  moe_layer (static scales)
+                    one routed row per expert, through a non-trivial expert permutation,
+                    with each expert's scales set to its row's dynamic scales: identical to
+                    the dynamic layer.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = [
-    "bf16_rne", "quant_act", "quant_act_smooth", "smooth_factors", "smooth_weights", "dequant_act", "quant_weight", "dequant_weight", "gemm_partials",
+    "bf16_rne", "quant_act", "quant_act_static", "calibrate_act_scale", "quant_act_smooth", "smooth_factors", "smooth_weights", "dequant_act", "quant_weight", "dequant_weight", "gemm_partials",
     "gemm", "silu_mul", "silu_mul_quant", "moe_align", "moe_layer", "effective_bits",
     "memory_bytes", "compression_vs_fp16",
 ]
@@ -135,6 +144,37 @@ def quant_act_smooth(x, inv_alpha):
     operator, here the activation quantization)."""
     xs = (np.asarray(x, _F32) * np.asarray(inv_alpha, _F32)[None, :]).astype(_F32)
     return quant_act(xs)
+
+
+def calibrate_act_scale(x_calib):
+    """Static (calibrated) activation scale: one per-tensor scale fixed offline from a
+    calibration batch (P1 section 3.2: static quantization measures the activation range on a
+    calibration set ahead of time and serves with the fixed scale; the page recommends it for
+    decode).  Reading: the per-token rule applied to the whole batch, s = fl32(max|x| / 127)
+    over every value of x_calib[R, K].  Returns a float32 scalar."""
+    x = np.asarray(x_calib, dtype=_F32)
+    return _F32(np.max(np.abs(x)) / _F32(127.0))
+
+
+def quant_act_static(x, s):
+    """INT8 quantization of X[M, K] with one fixed scale s for every row (P1 section 3.2, static
+    mode): q = clamp(rint(fl32(x / s)), -127, 127), the per-token rule of quant_act with the
+    scale given instead of measured.  Values outside the calibrated range saturate at +-127
+    (the long-tail loss the page warns about).  Readings: a NaN value gets code 0; a scale
+    that is not finite and positive gives all-zero codes.  Returns (q int8 [M, K], s float32
+    [M], every entry the given s)."""
+    x = np.asarray(x, dtype=_F32)
+    if x.ndim != 2 or x.shape[1] == 0:
+        raise ValueError("x must be [M, K] with K >= 1")
+    s = _F32(s)
+    sx = np.full(x.shape[0], s, dtype=_F32)
+    if not (np.isfinite(s) and s > 0):
+        return np.zeros(x.shape, np.int8), sx
+    with np.errstate(invalid="ignore", over="ignore"):
+        quot = (x / s).astype(_F32)                # IEEE float32 division (may overflow to inf)
+        q = np.clip(np.rint(quot), -127, 127)      # round half to even, saturate
+    q = np.where(np.isnan(x), 0, q).astype(np.int8)
+    return q, sx
 
 
 def dequant_act(q, s):
@@ -302,7 +342,7 @@ def moe_align(topk_ids, E: int):
     return order.astype(np.int32), offsets, inv.reshape(T, k).astype(np.int32)
 
 
-def moe_layer(x, topk_ids, topk_w, expert, E: int, I: int, group_size: int):
+def moe_layer(x, topk_ids, topk_w, expert, E: int, I: int, group_size: int, s_gu=None, s_dn=None):
     """One MoE expert layer in the W4A8 flow of P1 section 4.4.
 
     1. per-token INT8 quantization of the input, once per token, before dispatch;
@@ -317,6 +357,12 @@ def moe_layer(x, topk_ids, topk_w, expert, E: int, I: int, group_size: int):
 
     `expert(e)` returns (codes_gu [H, 2I], scales_gu, zeros_gu, codes_d [I, H], scales_d,
     zeros_d) for expert e; it is called only for experts that received rows.
+
+    Static per-expert activation scales (P1 section 3.1: each expert keeps its own activation
+    scale; section 3.2: calibrated static scales for decode): with s_gu [E] given, step 1
+    moves after dispatch and each routed row quantizes its token with quant_act_static and the
+    scale s_gu[e] of its expert e; with s_dn [E] given, step 4 quantizes each routed row's
+    silu(gate) * up (rounded once to float32) with s_dn[e].
     Returns dict(out=bf16 values [T, H], out64=float64 [T, H], and the intermediates).
     """
     x = np.asarray(x, _F32)
@@ -324,7 +370,7 @@ def moe_layer(x, topk_ids, topk_w, expert, E: int, I: int, group_size: int):
     w = np.asarray(topk_w, np.float64)
     T, k = ids.shape
     H = x.shape[1]
-    xq, sx = quant_act(x)
+    xq, sx = quant_act(x) if s_gu is None else (None, None)
     sorted_rows, offsets, inv = moe_align(ids, E)
     R = T * k
     gu = np.zeros((R, 2 * I), dtype=_F32)
@@ -337,8 +383,15 @@ def moe_layer(x, topk_ids, topk_w, expert, E: int, I: int, group_size: int):
         weights[e] = expert(e)
         cg, sg, zg = weights[e][:3]
         toks = sorted_rows[a:b] // k
-        gu[a:b] = bf16_rne(gemm(xq[toks], sx[toks], cg, sg, zg, group_size))
-    hq, sh = silu_mul_quant(gu)
+        qa, sa = (xq[toks], sx[toks]) if s_gu is None else quant_act_static(x[toks], s_gu[e])
+        gu[a:b] = bf16_rne(gemm(qa, sa, cg, sg, zg, group_size))
+    if s_dn is None:
+        hq, sh = silu_mul_quant(gu)
+    else:
+        hq, sh = np.zeros((R, I), np.int8), np.zeros(R, _F32)
+        for e in weights:
+            a, b = int(offsets[e]), int(offsets[e + 1])
+            hq[a:b], sh[a:b] = quant_act_static(silu_mul(gu[a:b]).astype(_F32), s_dn[e])
     for e, wts in weights.items():
         a, b = int(offsets[e]), int(offsets[e + 1])
         cd, sd, zd = wts[3:]

@@ -438,3 +438,66 @@ def test_smooth_factor_rule():
     a1 = O.smooth_factors(xa, w, 1.0)
     ok = (xa > 0) & (wa > 0)
     assert np.allclose((xa / a1.astype(np.float64))[ok], 1.0, rtol=1e-6)
+
+
+# ------------------------------------------------------------------ static activation scales
+def test_static_with_each_rows_own_scale_is_dynamic():
+    """P1 section 3.2: static mode only fixes the scale in advance; given the row's own
+    measured scale it must produce quant_act's codes."""
+    rs = np.random.default_rng(5)
+    x = (rs.standard_normal((6, 96)) * rs.uniform(0.01, 30, (6, 1))).astype(F32)
+    x[2, 7] = 500.0
+    q, s = O.quant_act(x)
+    for m in range(6):
+        qs, ss = O.quant_act_static(x[m:m + 1], s[m])
+        assert np.array_equal(qs[0], q[m]) and ss[0] == s[m]
+
+
+def test_static_exact_quotients_power_of_two_scale():
+    """x = j/8 with s = 1/4: every quotient x/s = j/2 is exact, so the code is Python's
+    round-half-to-even of j/2, saturated at +-127 outside the calibrated range."""
+    j = np.arange(-300, 301)
+    x = (j.astype(np.float64) / 8).astype(F32)
+    q, sx = O.quant_act_static(x[None, :], F32(0.25))
+    assert q[0].tolist() == [max(-127, min(127, round(v / 2))) for v in j.tolist()]
+    assert sx.tolist() == [0.25]
+    # non-finite and overflowing quotients saturate; NaN gets code 0
+    sp, _ = O.quant_act_static(np.array([[np.nan, np.inf, -np.inf, 3e38, -3e38, 0.0]], F32), F32(1e-3))
+    assert sp[0].tolist() == [0, 127, -127, 127, -127, 0]
+    # a scale that is not finite and positive gives zero codes and is passed through
+    for bad in (0.0, -1.0, np.inf):
+        qb, sb = O.quant_act_static(x[None, :], F32(bad))
+        assert not qb.any() and sb[0] == F32(bad)
+
+
+def test_calibrated_scale_is_largest_row_scale():
+    """The batch's max|x| is the largest row abs-max, and division by 127 is monotone, so the
+    calibrated scale is the largest per-token scale; the tiny case is exact: 127 / 127 = 1."""
+    rs = np.random.default_rng(6)
+    x = (rs.standard_normal((9, 40)) * rs.uniform(0.1, 10, (9, 1))).astype(F32)
+    assert O.calibrate_act_scale(x) == O.quant_act(x)[1].max()
+    assert O.calibrate_act_scale(np.array([[1.0, -127.0], [3.0, 0.5]], F32)) == F32(1.0)
+
+
+def test_moe_static_scales_reduce_to_dynamic_layer():
+    """One routed row per expert through a permuted routing: giving each expert the dynamic
+    scales of its one row reproduces the dynamic layer exactly; handing the gate/up scales to
+    the neighbouring experts does not (the scale is looked up by expert, not by token)."""
+    T, E, H, I, g = 5, 5, 64, 32, 32
+    ids = np.array([[3], [0], [4], [1], [2]], np.int32)
+    w = np.array([[0.7], [1.0], [0.3], [0.9], [0.5]], F32)
+    rs = np.random.default_rng(8)
+    x = W.bf16_values(W.to_bf16((rs.standard_normal((T, H)) * rs.uniform(0.5, 8, (T, 1))).astype(F32)))
+    qw = {e: O.quant_weight(W.random_weights(40 + e, H, 2 * I, 0.2), g, True) +
+          O.quant_weight(W.random_weights(60 + e, I, H, 0.2), g, False) for e in range(E)}
+    dyn = O.moe_layer(x, ids, w, lambda e: qw[e], E, I, g)
+    s_gu, s_dn = np.empty(E, F32), np.empty(E, F32)
+    for t in range(T):
+        e = ids[t, 0]
+        s_gu[e] = dyn["sx"][t]
+        s_dn[e] = dyn["sh"][dyn["inv"][t, 0]]
+    st = O.moe_layer(x, ids, w, lambda e: qw[e], E, I, g, s_gu=s_gu, s_dn=s_dn)
+    assert np.array_equal(st["gu"], dyn["gu"]) and np.array_equal(st["hq"], dyn["hq"])
+    assert np.array_equal(st["sh"], dyn["sh"]) and np.array_equal(st["out64"], dyn["out64"])
+    off = O.moe_layer(x, ids, w, lambda e: qw[e], E, I, g, s_gu=np.roll(s_gu, 1), s_dn=s_dn)
+    assert not np.array_equal(off["gu"], dyn["gu"])
