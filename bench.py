@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the prefill and MoE figures")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--only", default="", help="comma list of legs: decode,prefill,moe,compare")
+    p.add_argument("--only", default="", help="comma list of legs: decode,prefill,moe,quant,compare")
     p.add_argument("--no-graph", action="store_true", help="launch the decode steps eagerly")
     p.add_argument("--calib", action="store_true",
                    help="also run one plain copy kernel (torch.neg over 256 MiB of fp32) so that "
@@ -311,24 +311,73 @@ def moe_leg(args, L, W, torch, dev, steps):
                          device=dev)
         o = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
 
+        # static per-expert activation scales (values do not change the work)
+        ws_st = torch.empty(L.w4a8_moe_static_workspace_size(cfg.T, cfg.topk, cfg.H, cfg.I, cfg.E),
+                            dtype=torch.uint8, device=dev)
+        s_gu = torch.full((cfg.E,), 0.05, dtype=torch.float32, device=dev)
+        s_dn = torch.full((cfg.E,), 0.02, dtype=torch.float32, device=dev)
+
         def run():
             L.w4a8_moe_forward(X, ids_d, w_d, cfg.E, gu, gstride, gud, dn, dstride, dd, ws, o)
 
-        for _ in range(3):
-            run()
-        t = Timer(torch)
-        for _ in range(steps):
-            s = t.start()
-            run()
-            t.stop(s)
-        ms = t.mean_ms()
+        def run_static():
+            L.w4a8_moe_forward_static(X, ids_d, w_d, cfg.E, gu, gstride, gud, dn, dstride, dd, s_gu, s_dn, ws_st, o)
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            t = Timer(torch)
+            for _ in range(steps):
+                s = t.start()
+                fn()
+                t.stop(s)
+            return t.mean_ms()
+
+        ms = timed(run)
+        ms_static = timed(run_static)
         touched = len(set(ids.ravel().tolist()))
         wbytes = touched * (gstride + dstride)
         out[cfg.name] = dict(layer_ms=ms, tokens_per_s=cfg.T / (ms * 1e-3), experts_touched=touched,
                              weight_gbs=wbytes / (ms * 1e-3) / 1e9,
-                             frac_hbm=wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)
-        del gu, dn, ws
+                             frac_hbm=wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             static_scales_layer_ms=ms_static)
+        del gu, dn, ws, ws_st
         torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------- static vs dynamic activation scales
+def quant_leg(args, L, W, torch, dev, steps):
+    """Per-token dynamic quantization (row abs-max reduction, then the codes) against static
+    quantization with a calibrated scale (one pass), at the decode rows of the 4096-wide
+    projection and at M = 4096.  Per-call means over 32 back-to-back launches replayed from a
+    graph (a single launch timed alone measures the event overhead, not the kernel)."""
+    out = {}
+    s = torch.tensor([0.05], dtype=torch.float32, device=dev)
+    per_graph = 32
+    for M in (1, 8, 32, 4096):
+        K = 4096
+        X = W.random_activations(M, M, K).to(dev)
+        Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+        res = {}
+        for name, fn in (("dynamic_us", lambda: L.w4a8_quant_act(X, Xq, sx)),
+                         ("static_us", lambda: L.w4a8_quant_act_static(X, s, Xq, sx))):
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(per_graph):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            t = Timer(torch)
+            for _ in range(max(2, steps // per_graph)):
+                st = t.start()
+                g.replay()
+                t.stop(st)
+            res[name] = t.mean_ms() * 1e3 / per_graph
+        out[f"m{M}_k{K}"] = res
     return out
 
 
@@ -440,7 +489,7 @@ def compare_leg(args, L, W, torch, dev):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
@@ -454,7 +503,7 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     L.lib()
-    legs = set(args.only.split(",")) if args.only else {"decode", "prefill", "moe", "compare"}
+    legs = set(args.only.split(",")) if args.only else {"decode", "prefill", "moe", "quant", "compare"}
     if args.no_extra:
         legs = {"decode"}
     print(f"[bench] decode leg: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
@@ -466,6 +515,9 @@ def main():
     if "moe" in legs:
         print("[bench] moe leg", file=sys.stderr, flush=True)
         extra["moe"] = moe_leg(args, L, W, torch, dev, steps=20)
+    if "quant" in legs:
+        print("[bench] quant leg", file=sys.stderr, flush=True)
+        extra["quant"] = quant_leg(args, L, W, torch, dev, steps=256)
     if "compare" in legs:
         print("[bench] W8A8 sibling and bf16 library baseline", file=sys.stderr, flush=True)
         extra["compare"] = compare_leg(args, L, W, torch, dev)

@@ -177,6 +177,32 @@ int w4a8_quant_act(const void* X_bf16, int M, int K, int ldx, int8_t* Xq, float*
 int w4a8_quant_act_smooth(const void* X_bf16, int M, int K, int ldx, const float* inv_alpha, int8_t* Xq,
                           float* sx, void* stream);
 
+/* Static (calibrated) activation quantization (P1 section 3.2: a scale measured on a
+ * calibration set ahead of time replaces the per-batch reduction; the page recommends it for
+ * decode).  Every row uses the one given scale:
+ *   s       device float32 [1] (a device value, so a captured graph can be recalibrated)
+ *   Xq, sx  as w4a8_quant_act; sx[m] = s for every row
+ * q = clamp(rint(fl32(x / s)), -127, 127): values beyond the calibrated range saturate at
+ * +-127, NaN gives 0, +-Inf gives +-127.  A scale that is not finite and positive gives
+ * all-zero codes.  No limit on K besides K % 16 == 0 (one pass, nothing held per row).
+ * M == 0 is a no-op; EINVAL for NULL pointers, K % 16, ldx % 8 or misaligned X / Xq. */
+int w4a8_quant_act_static(const void* X_bf16, int M, int K, int ldx, const float* s, int8_t* Xq,
+                          float* sx, void* stream);
+
+/* Static per-expert quantization of the routed rows (P1 section 3.1: one activation scale
+ * per expert; section 3.2: static scales).  Row r of the expert-sorted order (from
+ * w4a8_moe_align) quantizes token sorted_rows[r] / k of X with the scale s[e] of the
+ * expert e that owns row r (expert_offsets[e] <= r < expert_offsets[e + 1]), by the rule of
+ * w4a8_quant_act_static.
+ *   X_bf16          device bfloat16 [T, H], row stride ldx
+ *   sorted_rows     device int32 [T*k]; expert_offsets device int32 [E+1]; s device float32 [E]
+ *   Xq, sx          device int8 [T*k, H] (16-byte aligned), float32 [T*k], sorted order
+ * Rows at or past expert_offsets[E] (routing ids outside [0, E)) get zero codes and scale 0.
+ * E <= 1024 (EINVAL), T*k <= 2^24 (EUNSUPPORTED). */
+int w4a8_moe_quant_static(const void* X_bf16, int T, int H, int ldx, const int32_t* sorted_rows,
+                          int k, const int32_t* expert_offsets, int E, const float* s, int8_t* Xq,
+                          float* sx, void* stream);
+
 /* W4A8 GEMM Y = (s_x * Xq) (s_w * (q - z)) (P5 section 4 ideal path; P5 section 8.3
  * epilogue Y[i, j] = s_x[i] s_w[j] acc[i, j], applied per K-group of P5 section 8.4).
  *   Xq, sx    device, from w4a8_quant_act ([M, K] int8 dense, [M] float32)
@@ -250,6 +276,13 @@ int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int 
 int w4a8_silu_mul_quant(const void* GU_bf16, int R, int I, int8_t* Hq, float* sh,
                         void* stream);
 
+/* The same with static per-expert scales: row r (expert-sorted order) is quantized by the
+ * rule of w4a8_quant_act_static with the scale s[e] of the expert that owns it.
+ *   expert_offsets  device int32 [E+1] from w4a8_moe_align; s device float32 [E]
+ * Rows at or past expert_offsets[E] get zero codes and scale 0.  E <= 1024 (EINVAL). */
+int w4a8_silu_mul_quant_static(const void* GU_bf16, int R, int I, const int32_t* expert_offsets,
+                               int E, const float* s, int8_t* Hq, float* sh, void* stream);
+
 /* Un-permute and top-k weighted combine (P1 section 4.3: dequantize to 16-bit, multiply
  * by the gate weight, accumulate; kept out of the integer domain).
  *   Yd_bf16  device bfloat16 [T*k, H] in sorted order
@@ -276,6 +309,23 @@ int w4a8_moe_forward(const void* X_bf16, const int32_t* topk_ids, const float* t
                      const w4a8_wdesc* gu_desc, const void* d_blobs, size_t d_stride,
                      const w4a8_wdesc* d_desc, void* workspace, size_t workspace_bytes,
                      void* out_bf16, void* stream);
+
+/* Workspace bytes needed by w4a8_moe_forward_static (0 if invalid): the routed rows are
+ * quantized one by one, so the activation codes take T*k rows instead of T. */
+size_t w4a8_moe_static_workspace_size(int T, int k, int H, int I, int E);
+
+/* One MoE expert layer with static per-expert activation scales (P1 section 3.1 and 3.2:
+ * calibrated scales, one per expert, for decode).  The steps of w4a8_moe_forward, with the
+ * two quantizations replaced: moe_align -> moe_quant_static(X, s_gu) -> moe_gemm(gate/up,
+ * rows already sorted) -> silu_mul_quant_static(s_dn) -> moe_gemm(down) -> moe_combine.
+ *   s_gu, s_dn  device float32 [E]: scale of each expert's gate/up and down inputs
+ *   workspace   device, >= w4a8_moe_static_workspace_size(T, k, H, I, E) bytes, 256-aligned
+ * Other arguments and errors as w4a8_moe_forward. */
+int w4a8_moe_forward_static(const void* X_bf16, const int32_t* topk_ids, const float* topk_w, int T,
+                            int k, int E, const void* gu_blobs, size_t gu_stride,
+                            const w4a8_wdesc* gu_desc, const void* d_blobs, size_t d_stride,
+                            const w4a8_wdesc* d_desc, const float* s_gu, const float* s_dn,
+                            void* workspace, size_t workspace_bytes, void* out_bf16, void* stream);
 
 /* Name of the kernel variant w4a8_gemm resolves to for (d, M), or "unsupported"
  * (P4: record target and resolved backend so a silent fallback is visible). */

@@ -25,6 +25,8 @@ EXPORTED = [
     "w4a8_quant_act", "w4a8_quant_act_smooth", "w4a8_gemm", "w4a8_linear", "w4a8_gemm_partials", "w4a8_moe_align",
     "w4a8_moe_gemm",
     "w4a8_silu_mul_quant", "w4a8_moe_combine", "w4a8_moe_workspace_size", "w4a8_moe_forward",
+    "w4a8_quant_act_static", "w4a8_moe_quant_static", "w4a8_silu_mul_quant_static",
+    "w4a8_moe_static_workspace_size", "w4a8_moe_forward_static",
     "w4a8_kernel_name", "w4a8_status_string", "w4a8_version",
 ]
 
@@ -73,6 +75,11 @@ def lib() -> ctypes.CDLL:
             "w4a8_moe_combine": (I, [P, P, P, I, I, I, P, VP]),
             "w4a8_moe_workspace_size": (SZ, [I, I, I, I, I]),
             "w4a8_moe_forward": (I, [P, P, P, I, I, I, P, SZ, DP, P, SZ, DP, P, SZ, P, VP]),
+            "w4a8_quant_act_static": (I, [P, I, I, I, P, P, P, VP]),
+            "w4a8_moe_quant_static": (I, [P, I, I, I, P, I, P, I, P, P, P, VP]),
+            "w4a8_silu_mul_quant_static": (I, [P, I, I, P, I, P, P, P, VP]),
+            "w4a8_moe_static_workspace_size": (SZ, [I, I, I, I, I]),
+            "w4a8_moe_forward_static": (I, [P, P, P, I, I, I, P, SZ, DP, P, SZ, DP, P, P, P, SZ, P, VP]),
             "w4a8_kernel_name": (ctypes.c_char_p, [DP, I]),
             "w4a8_status_string": (ctypes.c_char_p, [I]),
             "w4a8_version": (I, []),
@@ -180,6 +187,10 @@ def w4a8_moe_workspace_size(T: int, k: int, H: int, I: int, E: int) -> int:
     return int(lib().w4a8_moe_workspace_size(T, k, H, I, E))
 
 
+def w4a8_moe_static_workspace_size(T: int, k: int, H: int, I: int, E: int) -> int:
+    return int(lib().w4a8_moe_static_workspace_size(T, k, H, I, E))
+
+
 def w4a8_version() -> int:
     return int(lib().w4a8_version())
 
@@ -199,6 +210,24 @@ def w4a8_quant_act_smooth(X, inv_alpha, Xq, sx, stream=None) -> None:
     M, K = X.shape
     _check(lib().w4a8_quant_act_smooth(_ptr(X), M, K, X.stride(0), _ptr(inv_alpha), _ptr(Xq), _ptr(sx),
                                        _stream(stream)), "w4a8_quant_act_smooth")
+
+
+def w4a8_quant_act_static(X, s, Xq, sx, stream=None) -> None:
+    """Quantize every row of X (bf16 [M, K]) with the one calibrated scale s (float32 [1] on
+    the device); sx[m] receives s."""
+    _require_cuda(X, s, Xq, sx)
+    M, K = X.shape
+    _check(lib().w4a8_quant_act_static(_ptr(X), M, K, X.stride(0), _ptr(s), _ptr(Xq), _ptr(sx), _stream(stream)),
+           "w4a8_quant_act_static")
+
+
+def w4a8_moe_quant_static(X, k: int, sorted_rows, expert_offsets, E: int, s, Xq, sx, stream=None) -> None:
+    """Routed rows in expert-sorted order: row r quantizes token sorted_rows[r] // k of X with the
+    scale s[e] of its expert; Xq int8 [T*k, H], sx float32 [T*k]."""
+    _require_cuda(X, sorted_rows, expert_offsets, s, Xq, sx)
+    T, H = X.shape
+    _check(lib().w4a8_moe_quant_static(_ptr(X), T, H, X.stride(0), _ptr(sorted_rows), int(k), _ptr(expert_offsets),
+                                       int(E), _ptr(s), _ptr(Xq), _ptr(sx), _stream(stream)), "w4a8_moe_quant_static")
 
 
 def w4a8_gemm(Xq, sx, blob_dev, d: WDesc, Y, out_dtype: int = W4A8_OUT_BF16, stream=None) -> None:
@@ -244,6 +273,13 @@ def w4a8_silu_mul_quant(GU, Hq, sh, stream=None) -> None:
            "w4a8_silu_mul_quant")
 
 
+def w4a8_silu_mul_quant_static(GU, expert_offsets, E: int, s, Hq, sh, stream=None) -> None:
+    _require_cuda(GU, expert_offsets, s, Hq, sh)
+    R, I2 = GU.shape
+    _check(lib().w4a8_silu_mul_quant_static(_ptr(GU), R, I2 // 2, _ptr(expert_offsets), int(E), _ptr(s), _ptr(Hq),
+                                            _ptr(sh), _stream(stream)), "w4a8_silu_mul_quant_static")
+
+
 def w4a8_moe_combine(Yd, inv, topk_w, out, stream=None) -> None:
     _require_cuda(Yd, inv, topk_w, out)
     T, k = inv.shape
@@ -260,6 +296,19 @@ def w4a8_moe_forward(X, topk_ids, topk_w, E: int, gu_blobs, gu_stride: int, gu_d
                                   int(gu_stride), ctypes.byref(gu_desc), _ptr(d_blobs), int(d_stride),
                                   ctypes.byref(d_desc), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _ptr(out), _stream(stream)), "w4a8_moe_forward")
+
+
+def w4a8_moe_forward_static(X, topk_ids, topk_w, E: int, gu_blobs, gu_stride: int, gu_desc: WDesc, d_blobs,
+                            d_stride: int, d_desc: WDesc, s_gu, s_dn, workspace, out, stream=None) -> None:
+    """w4a8_moe_forward with static per-expert activation scales s_gu, s_dn (float32 [E] on the
+    device); workspace of w4a8_moe_static_workspace_size bytes."""
+    _require_cuda(X, topk_ids, topk_w, gu_blobs, d_blobs, s_gu, s_dn, workspace, out)
+    T, k = topk_ids.shape
+    _check(lib().w4a8_moe_forward_static(_ptr(X), _ptr(topk_ids), _ptr(topk_w), T, k, int(E), _ptr(gu_blobs),
+                                         int(gu_stride), ctypes.byref(gu_desc), _ptr(d_blobs), int(d_stride),
+                                         ctypes.byref(d_desc), _ptr(s_gu), _ptr(s_dn), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)),
+           "w4a8_moe_forward_static")
 
 
 # ------------------------------------------------------------------------------ helpers

@@ -191,9 +191,94 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
 // ------------------------------------------------------------------------------------
 // SiLU-gated activation + per-row requantization (P1 section 1 and section 3.1)
 // ------------------------------------------------------------------------------------
-template <int IT>
+// Static (calibrated) activation scales (P1 section 3.2: the scale is measured on a
+// calibration set ahead of time, so serving needs no row reduction; section 3.1: each expert
+// keeps its own scale).  The rule is the per-token one with the scale given.
+
+// Expert that owns sorted row r: the e with offs[e] <= r < offs[e + 1], for offs
+// non-decreasing with offs[0] = 0 and r < offs[E] (binary search; uniform per workgroup).
+__device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offs, int E, int r) {
+    int lo = 0, hi = E;                        // offs[lo] <= r < offs[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offs[mid] <= r) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// A given scale s: codes are produced only for a finite, positive s (otherwise all zero).
+__device__ __forceinline__ RowScale static_row_scale(float s) {
+    RowScale r;
+    r.s = s;
+    r.finite = s > 0.0f && s <= 3.40282347e38f;
+    r.d = r.finite ? s : 1.0f;
+    r.inv = 1.0f / r.d;
+    r.fast = r.d >= 1e-30f;
+    return r;
+}
+
+// clamp(rint(fl32(x / d)), -127, 127) for any x.  Values are first limited to +-128 d (a
+// power-of-two multiple, exact unless it overflows, hence the FLT_MAX cap): every such value
+// still saturates, and quant_one's quotient stays finite.  NaN gives 0; +-Inf gives +-127.
+__device__ __forceinline__ int quant_static_one(float x, const RowScale& r) {
+    const float lim = fminf(128.0f * r.d, 3.40282347e38f);
+    int q = quant_one(fminf(fmaxf(x, -lim), lim), r.d, r.inv, r.fast);
+    if (x != x) q = 0;
+    else if (fabsf(x) > 3.40282347e38f) q = x > 0.0f ? 127 : -127;
+    return q;
+}
+
+// Row r of Xq quantizes source row src of X with the scale s[e]: src = r (gather == NULL) or
+// gather[r] / k; e = 0 (offs == NULL) or the expert that owns sorted row r.  Rows no expert
+// owns (r >= offs[E]: routing ids outside [0, E)) and gathered rows outside [0, T) get zero
+// codes and scale 0.  One 256-thread workgroup per row, one pass: each value is quantized as
+// it is read.
+__global__ __launch_bounds__(256) void quant_static_kernel(const uint16_t* __restrict__ X, int K, int ldx, int T,
+                                                           const float* __restrict__ s,
+                                                           const int32_t* __restrict__ gather, int k,
+                                                           const int32_t* __restrict__ offs, int E,
+                                                           int8_t* __restrict__ Xq, float* __restrict__ sx) {
+    const int row = blockIdx.x, tid = threadIdx.x;
+    int e = 0, src = row;
+    bool live = true;
+    if (offs) {
+        live = row < offs[E];
+        if (live) e = expert_of_row(offs, E, row);
+    }
+    if (gather && live) {
+        const int gr = gather[row];
+        src = gr >= 0 ? gr / k : -1;
+        live = src >= 0 && src < T;
+    }
+    const RowScale rs = static_row_scale(live ? s[e] : 0.0f);
+    const uint16_t* xr = X + size_t(live ? src : 0) * size_t(ldx);
+    int8_t* qr = Xq + size_t(row) * size_t(K);
+    for (int kk = tid * 8; kk < K; kk += 256 * 8) {
+        uint32_t out[2] = {0, 0};
+        if (rs.finite) {
+            const uint4 v = *reinterpret_cast<const uint4*>(xr + kk);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int q0 = quant_static_one(bf16_to_f32(w[j] & 0xffffu), rs);
+                const int q1 = quant_static_one(bf16_to_f32(w[j] >> 16), rs);
+                const uint32_t pair = (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8);
+                out[j >> 1] |= pair << ((j & 1) * 16);
+            }
+        }
+        *reinterpret_cast<uint2*>(qr + kk) = make_uint2(out[0], out[1]);
+    }
+    if (tid == 0) sx[row] = rs.s;
+}
+
+// STATIC: row r (in expert-sorted order) takes the scale s[e] of the expert that owns it
+// (zero codes and scale 0 past offs[E]) instead of its own abs-max.
+template <int IT, bool STATIC = false>
 __global__ __launch_bounds__(256) void silu_quant_kernel(const uint16_t* __restrict__ GU, int I,
-                                                         int8_t* __restrict__ Hq, float* __restrict__ sh) {
+                                                         int8_t* __restrict__ Hq, float* __restrict__ sh,
+                                                         const float* __restrict__ s = nullptr,
+                                                         const int32_t* __restrict__ offs = nullptr, int E = 0) {
     __shared__ uint32_t red[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     const uint16_t* gp = GU + size_t(row) * size_t(2 * I);
@@ -219,8 +304,13 @@ __global__ __launch_bounds__(256) void silu_quant_kernel(const uint16_t* __restr
             amax = max(amax, __float_as_uint(h[it][j]) & 0x7fffffffu);
         }
     }
-    amax = block_max_u32(amax, red, 4);
-    const RowScale rs = row_scale(amax);
+    RowScale rs;
+    if constexpr (STATIC) {
+        rs = static_row_scale(row < offs[E] ? s[expert_of_row(offs, E, row)] : 0.0f);
+    } else {
+        amax = block_max_u32(amax, red, 4);
+        rs = row_scale(amax);
+    }
     int8_t* qr = Hq + size_t(row) * size_t(I);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -230,7 +320,7 @@ __global__ __launch_bounds__(256) void silu_quant_kernel(const uint16_t* __restr
         if (rs.finite) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int q = quant_one(h[it][j], rs.d, rs.inv, rs.fast);
+                const int q = STATIC ? quant_static_one(h[it][j], rs) : quant_one(h[it][j], rs.d, rs.inv, rs.fast);
                 out[j >> 2] |= (uint32_t(q) & 0xffu) << ((j & 3) * 8);
             }
         }
@@ -1402,8 +1492,10 @@ static void launch_quant(const uint16_t* X, int M, int K, int ldx, int8_t* Xq, f
 }
 
 template <int IT>
-static void launch_silu(const uint16_t* GU, int R, int I, int8_t* Hq, float* sh, hipStream_t s) {
-    silu_quant_kernel<IT><<<dim3(R), dim3(256), 0, s>>>(GU, I, Hq, sh);
+static void launch_silu(const uint16_t* GU, int R, int I, int8_t* Hq, float* sh, hipStream_t s,
+                        const float* sstat = nullptr, const int32_t* offs = nullptr, int E = 0) {
+    if (sstat) silu_quant_kernel<IT, true><<<dim3(R), dim3(256), 0, s>>>(GU, I, Hq, sh, sstat, offs, E);
+    else silu_quant_kernel<IT><<<dim3(R), dim3(256), 0, s>>>(GU, I, Hq, sh);
 }
 
 // Variant table of the decode GEMM.  (NT, KW, SBN): column tiles per workgroup, K slices,
@@ -1751,6 +1843,30 @@ int w4a8_quant_act_smooth(const void* X, int M, int K, int ldx, const float* inv
     return quant_act_impl(X, M, K, ldx, inv_alpha, Xq, sx, stream);
 }
 
+static int quant_static_impl(const void* X, int rows, int K, int ldx, int T, const float* s, const int32_t* gather,
+                             int k, const int32_t* offs, int E, int8_t* Xq, float* sx, void* stream) {
+    if (rows < 0 || K <= 0 || ldx < K) return W4A8_EINVAL;
+    if (rows == 0) return W4A8_OK;
+    if (!X || !s || !Xq || !sx) return W4A8_EINVAL;
+    if (K % 16 || ldx % 8 || !aligned16(X) || !aligned16(Xq)) return W4A8_EINVAL;
+    quant_static_kernel<<<dim3(rows), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        static_cast<const uint16_t*>(X), K, ldx, T, s, gather, k, offs, E, Xq, sx);
+    return launch_status();
+}
+
+int w4a8_quant_act_static(const void* X, int M, int K, int ldx, const float* s, int8_t* Xq, float* sx,
+                          void* stream) {
+    return quant_static_impl(X, M, K, ldx, M, s, nullptr, 1, nullptr, 0, Xq, sx, stream);
+}
+
+int w4a8_moe_quant_static(const void* X, int T, int H, int ldx, const int32_t* sorted_rows, int k,
+                          const int32_t* offsets, int E, const float* s, int8_t* Xq, float* sx, void* stream) {
+    if (T < 0 || k <= 0 || E <= 0 || E > 1024) return W4A8_EINVAL;
+    if ((long long)T * k > (1 << 24)) return W4A8_EUNSUPPORTED;
+    if (T > 0 && (!sorted_rows || !offsets)) return W4A8_EINVAL;
+    return quant_static_impl(X, T * k, H, ldx, T, s, sorted_rows, k, offsets, E, Xq, sx, stream);
+}
+
 int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const w4a8_wdesc* d, void* Y,
               int ldy, int out_dtype, void* stream) {
     int st = check_gemm_desc(d);
@@ -1938,7 +2054,8 @@ int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int 
                          static_cast<hipStream_t>(stream));
 }
 
-int w4a8_silu_mul_quant(const void* GU, int R, int I, int8_t* Hq, float* sh, void* stream) {
+static int silu_impl(const void* GU, int R, int I, int8_t* Hq, float* sh, const float* sstat, const int32_t* offs,
+                     int E, void* stream) {
     if (R < 0 || I <= 0) return W4A8_EINVAL;
     if (R == 0) return W4A8_OK;
     if (!GU || !Hq || !sh) return W4A8_EINVAL;
@@ -1947,13 +2064,24 @@ int w4a8_silu_mul_quant(const void* GU, int R, int I, int8_t* Hq, float* sh, voi
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint16_t* g = static_cast<const uint16_t*>(GU);
     switch (row_iters(I)) {
-        case 1: launch_silu<1>(g, R, I, Hq, sh, s); break;
-        case 2: launch_silu<2>(g, R, I, Hq, sh, s); break;
-        case 4: launch_silu<4>(g, R, I, Hq, sh, s); break;
-        case 8: launch_silu<8>(g, R, I, Hq, sh, s); break;
+        case 1: launch_silu<1>(g, R, I, Hq, sh, s, sstat, offs, E); break;
+        case 2: launch_silu<2>(g, R, I, Hq, sh, s, sstat, offs, E); break;
+        case 4: launch_silu<4>(g, R, I, Hq, sh, s, sstat, offs, E); break;
+        case 8: launch_silu<8>(g, R, I, Hq, sh, s, sstat, offs, E); break;
         default: return W4A8_EUNSUPPORTED;
     }
     return launch_status();
+}
+
+int w4a8_silu_mul_quant(const void* GU, int R, int I, int8_t* Hq, float* sh, void* stream) {
+    return silu_impl(GU, R, I, Hq, sh, nullptr, nullptr, 0, stream);
+}
+
+int w4a8_silu_mul_quant_static(const void* GU, int R, int I, const int32_t* offsets, int E, const float* s,
+                               int8_t* Hq, float* sh, void* stream) {
+    if (E <= 0 || E > 1024) return W4A8_EINVAL;
+    if (R > 0 && (!offsets || !s)) return W4A8_EINVAL;
+    return silu_impl(GU, R, I, Hq, sh, s, offsets, E, stream);
 }
 
 int w4a8_moe_combine(const void* Yd, const int32_t* inv, const float* w, int T, int k, int H, void* out,
@@ -1977,13 +2105,15 @@ struct MoeWs {
     size_t xq, sx, rows, offs, inv, gu, hq, sh, yd, total;
 };
 
-static MoeWs moe_ws(int T, int k, int H, int I, int E) {
+// per_row: the static-scale form quantizes each routed row (T * k rows) instead of each token
+static MoeWs moe_ws(int T, int k, int H, int I, int E, bool per_row = false) {
     auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
     const size_t R = size_t(T) * size_t(k);
+    const size_t QR = per_row ? R : size_t(T);
     MoeWs w;
     size_t o = 0;
-    w.xq = o; o = al(o + size_t(T) * H);
-    w.sx = o; o = al(o + size_t(T) * 4);
+    w.xq = o; o = al(o + QR * H);
+    w.sx = o; o = al(o + QR * 4);
     w.rows = o; o = al(o + R * 4);
     w.offs = o; o = al(o + size_t(E + 1) * 4);
     w.inv = o; o = al(o + R * 4);
@@ -2033,6 +2163,52 @@ int w4a8_moe_forward(const void* X, const int32_t* ids, const float* w, int T, i
     if ((st = w4a8_moe_gemm(xq, sx, rows, k, offs, E, R, gu_blobs, gu_stride, gu_desc, gu, W4A8_OUT_BF16, stream)))
         return st;
     if ((st = w4a8_silu_mul_quant(gu, R, I, hq, sh, stream))) return st;
+    if ((st = w4a8_moe_gemm(hq, sh, nullptr, k, offs, E, R, d_blobs, d_stride, d_desc, yd, W4A8_OUT_BF16, stream)))
+        return st;
+    return w4a8_moe_combine(yd, inv, w, T, k, H, out, stream);
+}
+
+size_t w4a8_moe_static_workspace_size(int T, int k, int H, int I, int E) {
+    if (T < 0 || k <= 0 || H <= 0 || I <= 0 || E <= 0) return 0;
+    return moe_ws(T, k, H, I, E, true).total;
+}
+
+int w4a8_moe_forward_static(const void* X, const int32_t* ids, const float* w, int T, int k, int E,
+                            const void* gu_blobs, size_t gu_stride, const w4a8_wdesc* gu_desc, const void* d_blobs,
+                            size_t d_stride, const w4a8_wdesc* d_desc, const float* s_gu, const float* s_dn,
+                            void* ws, size_t ws_bytes, void* out, void* stream) {
+    int st = check_gemm_desc(gu_desc);
+    if (st) return st;
+    st = check_gemm_desc(d_desc);
+    if (st) return st;
+    if (!grouped_format_ok(gu_desc) || !grouped_format_ok(d_desc)) return W4A8_EUNSUPPORTED;
+    if (T < 0 || k <= 0 || E <= 0) return W4A8_EINVAL;
+    const int H = gu_desc->K, I2 = gu_desc->N;
+    if (I2 % 2 || d_desc->K != I2 / 2 || d_desc->N != H) return W4A8_EINVAL;
+    const int I = I2 / 2;
+    if (T == 0) return W4A8_OK;
+    if (!X || !ids || !w || !gu_blobs || !d_blobs || !s_gu || !s_dn || !ws || !out) return W4A8_EINVAL;
+    const MoeWs L = moe_ws(T, k, H, I, E, true);
+    if (ws_bytes < L.total) return W4A8_ESIZE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return W4A8_EINVAL;
+    uint8_t* b = static_cast<uint8_t*>(ws);
+    int8_t* xq = reinterpret_cast<int8_t*>(b + L.xq);
+    float* sx = reinterpret_cast<float*>(b + L.sx);
+    int32_t* rows = reinterpret_cast<int32_t*>(b + L.rows);
+    int32_t* offs = reinterpret_cast<int32_t*>(b + L.offs);
+    int32_t* inv = reinterpret_cast<int32_t*>(b + L.inv);
+    void* gu = b + L.gu;
+    int8_t* hq = reinterpret_cast<int8_t*>(b + L.hq);
+    float* sh = reinterpret_cast<float*>(b + L.sh);
+    void* yd = b + L.yd;
+    const int R = T * k;
+    if ((st = w4a8_moe_align(ids, T, k, E, rows, offs, inv, stream))) return st;
+    // each routed row quantizes its token with the scale of its expert, already in sorted order
+    if ((st = w4a8_moe_quant_static(X, T, H, H, rows, k, offs, E, s_gu, xq, sx, stream))) return st;
+    if ((st = w4a8_moe_gemm(xq, sx, nullptr, k, offs, E, R, gu_blobs, gu_stride, gu_desc, gu, W4A8_OUT_BF16,
+                            stream)))
+        return st;
+    if ((st = w4a8_silu_mul_quant_static(gu, R, I, offs, E, s_dn, hq, sh, stream))) return st;
     if ((st = w4a8_moe_gemm(hq, sh, nullptr, k, offs, E, R, d_blobs, d_stride, d_desc, yd, W4A8_OUT_BF16, stream)))
         return st;
     return w4a8_moe_combine(yd, inv, w, T, k, H, out, stream);

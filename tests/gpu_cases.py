@@ -63,3 +63,84 @@ def random_expert_set(seed, E, K, N, g, asym):
     def make(e):
         return W.random_codes(seed * 1009 + e, K, N, g, asym)
     return make
+
+
+# ---------------------------------------------------------------- MoE layer helpers
+def moe_experts_rtn(cfg, experts_touched):
+    """Float weights quantized by the oracle (for the oracle) and packed by the library."""
+    dgu = L.desc(cfg.H, 2 * cfg.I, cfg.group_size, cfg.asymmetric)
+    dd = L.desc(cfg.I, cfg.H, cfg.group_size, cfg.asymmetric)
+    host_gu, host_d, qw = {}, {}, {}
+    for e in sorted(experts_touched):
+        Wgu, Wd = W.expert_weights(cfg, e)
+        host_gu[e] = L.w4a8_pack(dgu, Wgu)
+        host_d[e] = L.w4a8_pack(dd, Wd)
+        qw[e] = O.quant_weight(Wgu, cfg.group_size, cfg.asymmetric) + \
+            O.quant_weight(Wd, cfg.group_size, cfg.asymmetric)
+    return (dgu, dd, L.experts_to_device(dgu, cfg.E, host_gu), L.experts_to_device(dd, cfg.E, host_d), qw)
+
+
+def moe_experts_codes(cfg, experts_touched, seed):
+    """Random well-formed codes per expert (sizes whose float weights are too slow to draw)."""
+    dgu = L.desc(cfg.H, 2 * cfg.I, cfg.group_size, cfg.asymmetric)
+    dd = L.desc(cfg.I, cfg.H, cfg.group_size, cfg.asymmetric)
+    host_gu, host_d, qw = {}, {}, {}
+    for e in sorted(experts_touched):
+        cg = W.random_codes(seed * 1009 + e, cfg.H, 2 * cfg.I, cfg.group_size, cfg.asymmetric)
+        cd = W.random_codes(seed * 2003 + e, cfg.I, cfg.H, cfg.group_size, cfg.asymmetric)
+        host_gu[e] = L.w4a8_pack_codes(dgu, *cg)
+        host_d[e] = L.w4a8_pack_codes(dd, *cd)
+        qw[e] = cg + cd
+    return (dgu, dd, L.experts_to_device(dgu, cfg.E, host_gu), L.experts_to_device(dd, cfg.E, host_d), qw)
+
+
+def run_moe_forward(cfg, Xb, ids, w, gud, dd_):
+    T, k = ids.shape
+    ws = torch.empty(L.w4a8_moe_workspace_size(T, k, cfg.H, cfg.I, cfg.E), dtype=torch.uint8, device=DEV)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_moe_forward(Xb.to(DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), cfg.E,
+                       gud.blob, gud.stride, gud.desc, dd_.blob, dd_.stride, dd_.desc, ws, out)
+    return out, ws
+
+
+def check_moe(out, ref, qw, group_size, flips_per_row=2):
+    """End-to-end gate against the oracle's own bf16 output.
+
+    The stages are pinned one by one above; end to end, two things may legitimately differ:
+    bf16 roundings of intermediate outputs (one step when a value sits on a rounding
+    boundary), and the requantization of silu(gate)*up, where a near-tie code can move by
+    +-1 (the GPU's expf and the oracle's float64 exp differ by ulps).  One such flip in
+    routed row r moves out[t, n] by at most w[t, j] * sh[r] * max_k |s_d (q - z)|[k, n].
+    Bound per element: 2 bf16 steps + flips_per_row of those for each routed row; normwise
+    1e-3 against the float64 output."""
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref_bf = ref["out"].astype(np.float64)
+    o64 = ref["out64"]
+    inv, sh = ref["inv"], ref["sh"].astype(np.float64)
+    T, k = inv.shape
+    srt, offs = ref["sorted_rows"], ref["offsets"]
+    flip = np.zeros_like(o64)
+    colmax = {}
+    for e, wts in qw.items():
+        cd, sd, zd = wts[3:]
+        deq = O.dequant_weight(cd, sd, zd, group_size)
+        colmax[e] = np.max(np.abs(deq), axis=0)
+    ids = np.empty(T * k, np.int64)
+    for e in range(len(offs) - 1):
+        ids[srt[offs[e]:offs[e + 1]]] = e
+    for t in range(T):
+        for j in range(k):
+            r = inv[t, j]
+            e = ids[t * k + j]
+            flip[t] += abs(ref["topk_w"][t, j]) * sh[r] * colmax[e]
+    rms = np.sqrt(np.mean(o64 ** 2))
+    nw = np.linalg.norm(got - ref_bf) / np.linalg.norm(o64)
+    err = np.abs(got - ref_bf)
+    allow = 2 * bf16_ulp(ref_bf) + flips_per_row * flip
+    stats = dict(normwise=float(nw), frac_bitexact=float(np.mean(got == ref_bf)),
+                 frac_within_1ulp=float(np.mean(err <= bf16_ulp(ref_bf))),
+                 max_err_over_rms=float(np.max(err) / rms), max_err_over_allow=float(np.max(err / allow)))
+    print(stats, flush=True)
+    assert nw < 1e-3, stats
+    assert np.all(err <= allow), stats
+    return stats
