@@ -25,7 +25,10 @@ Pins (each function is checked against something other than itself in
   quant_weight      P3 reference-function invariants and its example, P2 range
                     example (asymmetric), bounds, zero groups, tiling error; 8-bit
                     codes: the same invariants with qmax = 127 and an exact round
-                    trip of weights on a power-of-two grid.
+                    trip of weights on a power-of-two grid; binary16 scales: torch's
+                    float32 -> float16 cast, half-spacing bound, identity when every
+                    float32 scale is already a binary16 value, the rounding invariants
+                    against the stored scale, and the range error.
   gemm_partials     brute-force integer triple loop; zero-point expansion of
                     P5 section 7; integer matmul when K equals the group.
   gemm              brute-force fp64 dequantise-then-matmul; per-token x
@@ -185,7 +188,7 @@ def dequant_act(q, s):
 # --------------------------------------------------------------------------------------
 # offline group-wise INT4 weight quantization (round to nearest)
 # --------------------------------------------------------------------------------------
-def quant_weight(w, group_size: int, asymmetric: bool, bits: int = 4):
+def quant_weight(w, group_size: int, asymmetric: bool, bits: int = 4, scale_bits: int = 32):
     """Group-wise RTN quantization of W[K, N] to `bits`-bit codes (4; 8 for the symmetric
     W8A8 sibling); each group is `group_size` consecutive rows k of one output column n
     (P5 section 8.4: one output channel split along K).
@@ -202,12 +205,28 @@ def quant_weight(w, group_size: int, asymmetric: bool, bits: int = 4):
     exact; z = clamp(round(-lo / s), 0, 15) is an integer; an all-zero group has s = 0, z = 0,
     q = 0.
 
+    scale_bits = 16 stores the scales in binary16, as P1 section 4.1 does for expert weights.
+    Reading: the float32 scale above is rounded to the nearest binary16 (ties to even, numpy's
+    float32 -> float16 cast) before any code is computed, so the codes are those of the stored
+    scale and w_hat = s16 (q - z) exactly; a scale past the binary16 range is an error.
+
     Returns (codes int8 [K, N], scales float32 [K/g, N], zeros uint8 [K/g, N] or None).
     Raises ValueError when the group does not tile K (P3 reference: groups cannot cross rows),
     when a weight is not finite, or for bits other than 4 and 8 (8: symmetric only).
     """
     if bits not in (4, 8) or (bits == 8 and asymmetric):
         raise ValueError("bits must be 4, or 8 with symmetric codes")
+    if scale_bits not in (16, 32):
+        raise ValueError("scale_bits must be 16 or 32")
+
+    def stored(scale):
+        if scale_bits == 32:
+            return scale
+        with np.errstate(over="ignore"):
+            h = scale.astype(np.float16)
+        if not np.all(np.isfinite(h)):
+            raise ValueError("a scale exceeds the binary16 range")
+        return h.astype(_F32)
     qmax = (1 << (bits - 1)) - 1
     w = np.asarray(w, dtype=_F32)
     if w.ndim != 2:
@@ -221,13 +240,13 @@ def quant_weight(w, group_size: int, asymmetric: bool, bits: int = 4):
     wg = w.reshape(G, group_size, N)
     if not asymmetric:
         amax = np.max(np.abs(wg), axis=1)
-        s = (amax / _F32(qmax)).astype(_F32)
+        s = stored((amax / _F32(qmax)).astype(_F32))
         d = np.where(s > 0, s, _F32(1.0)).astype(_F32)
         q = np.clip(np.rint((wg / d[:, None, :]).astype(_F32)), -qmax, qmax)
         return q.reshape(K, N).astype(np.int8), s, None
     lo = np.minimum(np.min(wg, axis=1), _F32(0.0))
     hi = np.maximum(np.max(wg, axis=1), _F32(0.0))
-    s = ((hi - lo).astype(_F32) / _F32(15.0)).astype(_F32)
+    s = stored(((hi - lo).astype(_F32) / _F32(15.0)).astype(_F32))
     nz = s > 0
     d = np.where(nz, s, _F32(1.0)).astype(_F32)
     z = np.where(nz, np.clip(np.rint((-lo / d).astype(_F32)), 0, 15), 0)

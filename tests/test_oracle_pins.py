@@ -501,3 +501,56 @@ def test_moe_static_scales_reduce_to_dynamic_layer():
     assert np.array_equal(st["sh"], dyn["sh"]) and np.array_equal(st["out64"], dyn["out64"])
     off = O.moe_layer(x, ids, w, lambda e: qw[e], E, I, g, s_gu=np.roll(s_gu, 1), s_dn=s_dn)
     assert not np.array_equal(off["gu"], dyn["gu"])
+
+
+# ------------------------------------------------------------------ binary16 weight scales
+def _f16_spacing(x):
+    """Spacing of the binary16 grid at |x|: 2^(e - 10) for |x| in [2^e, 2^(e+1)), 2^-24 below 2^-14."""
+    x = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+@pytest.mark.parametrize("g,asym", [(64, False), (128, True), (32, True)])
+def test_weight_fp16_scales(g, asym):
+    """The stored scale is torch's float32 -> float16 rounding of the float32 scale (within half
+    a binary16 step of it), and the codes obey the RTN invariants against the stored scale."""
+    rs = np.random.default_rng(g)
+    K, N = 4 * g, 24
+    w = (rs.standard_normal((K, N)) * rs.uniform(1e-4, 3.0, (1, N))).astype(F32)
+    w[:g, 3] = 0.0                                              # a zero group
+    w[g:2 * g, 5] = 1e-5                                        # a scale in the subnormal range
+    w[2 * g:3 * g, 7] = 1e-9                                    # a scale that rounds to 0
+    c32, s32, z32 = O.quant_weight(w, g, asym)
+    c16, s16, z16 = O.quant_weight(w, g, asym, scale_bits=16)
+    ref = torch.from_numpy(s32).to(torch.float16).to(torch.float32).numpy()
+    assert np.array_equal(s16, ref)
+    assert np.all(np.abs(s16.astype(np.float64) - s32) <= 0.5 * _f16_spacing(s32))
+    G = K // g
+    sk = np.repeat(s16.astype(np.float64), g, axis=0)
+    dk = np.where(sk > 0, sk, 1.0)
+    zk = np.repeat(z16.astype(np.float64), g, axis=0) if asym else 0.0
+    t = w / dk + zk                                             # the code before rounding
+    lo, hi = (0, 15) if asym else (-7, 7)
+    assert c16.min() >= lo and c16.max() <= hi
+    inside = (sk > 0) & (t >= lo) & (t <= hi)
+    err = np.abs(sk * (c16 - zk) - w)
+    assert np.all(err[inside] <= 0.5 * sk[inside] * (1 + 1e-6))   # round to nearest on the stored scale
+    assert np.all(c16[(sk > 0) & (t >= hi + 0.5)] == hi) and np.all(c16[(sk > 0) & (t <= lo - 0.5)] == lo)
+    assert s16[0, 3] == 0 and not c16[:g, 3].any()              # the zero group
+    assert s16.shape == (G, N) and 0 < s16[1, 5] < 2.0 ** -14   # the subnormal binary16 scale
+    assert s32[2, 7] > 0 and s16[2, 7] == 0 and not c16[2 * g:3 * g, 7].any()   # underflow: zero codes
+
+
+def test_weight_fp16_scales_identity_and_range():
+    """Weights whose float32 scales are binary16 values (max|w| / 7 a power of two) give the same
+    codes and scales either way; a scale past 65504 is an error."""
+    rs = np.random.default_rng(3)
+    top = 7.0 * 2.0 ** rs.integers(-12, 4, 8)                    # column maxima: max|w| / 7 exact
+    w = (rs.uniform(-1, 1, (128, 8)) * top).astype(F32)
+    w[0] = top
+    c32, s32, _ = O.quant_weight(w, 128, False)
+    c16, s16, _ = O.quant_weight(w, 128, False, scale_bits=16)
+    assert np.array_equal(c32, c16) and np.array_equal(s32, s16)
+    with pytest.raises(ValueError):
+        O.quant_weight(np.full((64, 1), 7.0 * 70000.0, F32), 64, False, scale_bits=16)
