@@ -68,9 +68,10 @@ def random_device_blobs(L, d, E, seed, dev):
     codes_b = Np * d.K // 2
     al = lambda v: (v + 255) // 256 * 256
     so = al(256 + codes_b)
-    zo = al(so + Np * G * 4)
-    struct.pack_into("<iiii", hdr, 16, d.K, d.N, d.group_size, d.asymmetric)
-    struct.pack_into("<7Q", hdr, 40, 256, codes_b, so, Np * G * 4, zo, Np * G if d.asymmetric else 0, n)
+    ssz = 2 if d.scale_bits == 16 else 4                 # binary16 or float32 scales
+    zo = al(so + Np * G * ssz)
+    struct.pack_into("<iiiiI", hdr, 16, d.K, d.N, d.group_size, d.asymmetric, 1 if ssz == 2 else 0)
+    struct.pack_into("<7Q", hdr, 40, 256, codes_b, so, Np * G * ssz, zo, Np * G if d.asymmetric else 0, n)
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
     buf = torch.empty(E * n, dtype=torch.uint8, device=dev)
@@ -83,7 +84,9 @@ def random_device_blobs(L, d, E, seed, dev):
             nib = torch.randint(-7, 8, (codes_b, 2), device=dev, generator=g, dtype=torch.int16) & 0xF
         b[256:256 + codes_b].copy_((nib[:, 0] | (nib[:, 1] << 4)).to(torch.uint8))
         sc = (torch.randn(Np * G, device=dev, generator=g).abs() * (0.02 / 7) + 1e-4).float()
-        b[so:so + Np * G * 4].copy_(sc.view(torch.uint8))
+        if ssz == 2:
+            sc = sc.half()
+        b[so:so + Np * G * ssz].copy_(sc.view(torch.uint8))
         if d.asymmetric:
             b[zo:zo + Np * G].copy_(torch.randint(4, 12, (Np * G,), device=dev, generator=g).to(torch.uint8))
     return buf, n
@@ -258,14 +261,15 @@ def cpu_baseline(args, leg, W):
 # ---------------------------------------------------------------------------------- prefill
 def prefill_leg(args, L, W, torch, dev, steps):
     """The projection pair at M = 4096 (asymmetric g128), and the up projection again with
-    g = 256 (half the per-group epilogues) and with per-channel scales (g = K: one epilogue),
-    the same weights otherwise."""
+    g = 256 (half the per-group epilogues), with per-channel scales (g = K: one epilogue) and
+    with binary16 group scales, the same weights otherwise."""
     out = {}
     import dataclasses
     g256 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "g256"), group_size=256)
     gk = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "gK"), group_size=W.C3_UP.K)
-    for cfg in (W.C3_UP, W.C3_DOWN, g256, gk):
-        d = L.desc(cfg.K, cfg.N, cfg.group_size, cfg.asymmetric)
+    h16 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name + "_fp16_scales")
+    for cfg in (W.C3_UP, W.C3_DOWN, g256, gk, h16):
+        d = L.desc(cfg.K, cfg.N, cfg.group_size, cfg.asymmetric, scale_bits=16 if cfg is h16 else 32)
         _, Wt = W.dense_inputs(cfg, M=1)
         blob = torch.from_numpy(L.w4a8_pack(d, Wt)).to(dev)
         del Wt
@@ -335,12 +339,21 @@ def moe_leg(args, L, W, torch, dev, steps):
 
         ms = timed(run)
         ms_static = timed(run_static)
+        # binary16 group scales: the same codes, the scales rounded to binary16 on packing
+        gud16 = L.desc(cfg.H, 2 * cfg.I, cfg.group_size, cfg.asymmetric, scale_bits=16)
+        dd16 = L.desc(cfg.I, cfg.H, cfg.group_size, cfg.asymmetric, scale_bits=16)
+        del gu, dn
+        torch.cuda.empty_cache()
+        gu, gstride16 = random_device_blobs(L, gud16, cfg.E, seed * 7, dev)
+        dn, dstride16 = random_device_blobs(L, dd16, cfg.E, seed * 11, dev)
+        ms_h16 = timed(lambda: L.w4a8_moe_forward(X, ids_d, w_d, cfg.E, gu, gstride16, gud16, dn, dstride16, dd16,
+                                                  ws, o))
         touched = len(set(ids.ravel().tolist()))
         wbytes = touched * (gstride + dstride)
         out[cfg.name] = dict(layer_ms=ms, tokens_per_s=cfg.T / (ms * 1e-3), experts_touched=touched,
                              weight_gbs=wbytes / (ms * 1e-3) / 1e9,
                              frac_hbm=wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             static_scales_layer_ms=ms_static)
+                             static_scales_layer_ms=ms_static, fp16_scales_layer_ms=ms_h16)
         del gu, dn, ws, ws_st
         torch.cuda.empty_cache()
     return out
@@ -394,6 +407,7 @@ def compare_leg(args, L, W, torch, dev):
     ncopy = args.copies
     d = L.desc(K, N, cfg.group_size, cfg.asymmetric)
     d8 = L.desc(K, N, cfg.group_size, False, bits=8)
+    d16 = L.desc(K, N, cfg.group_size, cfg.asymmetric, scale_bits=16)
     _, Wt = W.dense_inputs(cfg, M=1)
 
     def copies(desc):
@@ -403,7 +417,7 @@ def compare_leg(args, L, W, torch, dev):
             t[c].copy_(one)
         return t
 
-    blobs, blobs8 = copies(d), copies(d8)
+    blobs, blobs8, blobs16 = copies(d), copies(d8), copies(d16)
     wb = torch.from_numpy(Wt).to(dev).to(torch.bfloat16)
     Wb = torch.empty((ncopy, K, N), dtype=torch.bfloat16, device=dev)
     for c in range(ncopy):
@@ -445,13 +459,18 @@ def compare_leg(args, L, W, torch, dev):
             for c in range(ncopy):
                 torch.mm(X, Wb[c], out=Y)
 
-        t4, t8, tb = per_call_us(w4a8), per_call_us(w8a8), per_call_us(bf16)
+        def w4a8_h16():
+            for c in range(ncopy):
+                L.w4a8_linear(X, blobs16[c], d16, Y, Xq, sx, L.W4A8_OUT_BF16)
+
+        t4, t8, tb, t16 = per_call_us(w4a8), per_call_us(w8a8), per_call_us(bf16), per_call_us(w4a8_h16)
         out["decode"][f"m{M}"] = dict(w4a8_linear_us=t4, w8a8_linear_us=t8, bf16_mm_us=tb,
+                                      w4a8_fp16_scales_linear_us=t16,
                                       w4a8_vs_w8a8=t8 / t4, w4a8_vs_bf16=tb / t4,
                                       w8a8_weight_gbs=(K * N + K // cfg.group_size * N * 4) / (t8 * 1e-6) / 1e9,
                                       bf16_weight_gbs=K * N * 2 / (tb * 1e-6) / 1e9)
         del X, Xq, sx, Y
-    del blobs, blobs8, Wb
+    del blobs, blobs8, blobs16, Wb
     torch.cuda.empty_cache()
     for pc in (W.C3_UP, W.C3_DOWN):
         X = W.random_activations(pc.seed + 7919, pc.M, pc.K).to(dev)

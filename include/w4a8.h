@@ -71,13 +71,22 @@ typedef enum { W4A8_OUT_BF16 = 0, W4A8_OUT_F32 = 1 } w4a8_out_dtype;
  *               8: the W8A8 sibling the pages compare against (P1 section 5): signed
  *                  codes q in [-127, 127], one per byte, symmetric only (qmax of the
  *                  P3 symmetric group-wise reference with bits = 8).  Dense GEMMs
- *                  only: the MoE entry points return EUNSUPPORTED for it. */
+ *                  only: the MoE entry points return EUNSUPPORTED for it.
+ *   scale_bits  32 (or 0): float32 group scales;
+ *               16: binary16 group scales, the storage P1 section 4.1 names for expert
+ *                  weights.  The packer rounds each float32 scale to the nearest binary16
+ *                  (ties to even) and computes the codes with the rounded scale, so
+ *                  dequantization uses exactly the stored value; a scale past the binary16
+ *                  range (65504) makes w4a8_pack return EINVAL.  Kernels take binary16
+ *                  scales with 4-bit codes and g in {64, 128} (dense and MoE); other
+ *                  combinations return EUNSUPPORTED. */
 typedef struct {
     int32_t K;
     int32_t N;
     int32_t group_size;
     int32_t asymmetric;
     int32_t weight_bits;
+    int32_t scale_bits;
 } w4a8_wdesc;
 
 /* ------------------------------------------------------------------------------------
@@ -87,7 +96,8 @@ typedef struct {
  *
  *   offset 0    header, W4A8_HEADER_BYTES bytes, little endian:
  *               char magic[8] = "W4A8BLB1"; uint32 version = 1; uint32 layout = 1;
- *               int32 K, N, group_size, asymmetric; uint32 scale_dtype = 0 (fp32);
+ *               int32 K, N, group_size, asymmetric; uint32 scale_dtype (0 float32,
+ *               1 binary16);
  *               uint32 zero_dtype = 0 (uint8); uint64 codes_off, codes_bytes,
  *               scales_off, scales_bytes, zeros_off, zeros_bytes, total_bytes;
  *               uint32 weight_bits (4 or 8; 0 in older headers reads as 4);

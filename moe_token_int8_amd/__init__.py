@@ -39,11 +39,11 @@ class W4A8Error(RuntimeError):
 
 class WDesc(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32), ("group_size", ctypes.c_int32),
-                ("asymmetric", ctypes.c_int32), ("weight_bits", ctypes.c_int32)]
+                ("asymmetric", ctypes.c_int32), ("weight_bits", ctypes.c_int32), ("scale_bits", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"WDesc(K={self.K}, N={self.N}, group_size={self.group_size}, asymmetric={self.asymmetric}, "
-                f"weight_bits={self.weight_bits})")
+                f"weight_bits={self.weight_bits}, scale_bits={self.scale_bits})")
 
 
 _lib = None
@@ -101,9 +101,10 @@ def _check(status: int, where: str):
         raise W4A8Error(status, where)
 
 
-def desc(K: int, N: int, group_size: int, asymmetric: bool, bits: int = 4) -> WDesc:
-    """Weight descriptor; bits = 8 selects the symmetric INT8-weight (W8A8) form."""
-    return WDesc(int(K), int(N), int(group_size), int(bool(asymmetric)), int(bits))
+def desc(K: int, N: int, group_size: int, asymmetric: bool, bits: int = 4, scale_bits: int = 32) -> WDesc:
+    """Weight descriptor; bits = 8 selects the symmetric INT8-weight (W8A8) form, scale_bits = 16
+    binary16 group scales."""
+    return WDesc(int(K), int(N), int(group_size), int(bool(asymmetric)), int(bits), int(scale_bits))
 
 
 def _ptr(x) -> int | None:

@@ -8,6 +8,7 @@
 #include "w4a8_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <thread>
@@ -23,6 +24,7 @@ bool desc_valid(const w4a8_wdesc* d) {
     if (d->asymmetric != 0 && d->asymmetric != 1) return false;
     if (d->weight_bits != 0 && d->weight_bits != 4 && d->weight_bits != 8) return false;
     if (d->weight_bits == 8 && d->asymmetric) return false;   // 8-bit codes are symmetric
+    if (d->scale_bits != 0 && d->scale_bits != 16 && d->scale_bits != 32) return false;
     const int g = d->group_size;
     if (g != 32 && g != 64 && g != 128 && g != 256 && g != d->K) return false;   // g = K: per channel
     if (d->K % g) return false;            // groups cannot cross rows (P3 reference)
@@ -44,10 +46,11 @@ Layout layout_of(const w4a8_wdesc* d) {
     L.G = d->K / d->group_size;
     L.asym = d->asymmetric;
     L.bits = d->weight_bits == 8 ? 8 : 4;
+    L.sbytes = d->scale_bits == 16 ? 2 : 4;
     L.codes_off = W4A8_HEADER_BYTES;
     L.codes_bytes = size_t(L.Np) * size_t(L.K) * size_t(L.bits) / 8;
     L.scales_off = align256(L.codes_off + L.codes_bytes);
-    L.scales_bytes = size_t(L.Np) * size_t(L.G) * 4;
+    L.scales_bytes = size_t(L.Np) * size_t(L.G) * size_t(L.sbytes);
     L.zeros_off = align256(L.scales_off + L.scales_bytes);
     L.zeros_bytes = L.asym ? size_t(L.Np) * size_t(L.G) : 0;
     L.total = align256(L.zeros_off + L.zeros_bytes);
@@ -107,6 +110,7 @@ static void write_header(const w4a8_wdesc* d, const Layout& L, uint8_t* blob) {
     h.zeros_bytes = L.zeros_bytes;
     h.total = L.total;
     h.weight_bits = uint32_t(L.bits);
+    h.scale_dtype = L.sbytes == 2 ? 1u : 0u;
     std::memset(blob, 0, W4A8_HEADER_BYTES);
     std::memcpy(blob, &h, sizeof(h));
 }
@@ -118,7 +122,8 @@ static int read_header(const void* blob, size_t bytes, w4a8_wdesc* d, Layout* L)
     if (std::memcmp(h.magic, "W4A8BLB1", 8) || h.version != 1 || h.layout != 1) return W4A8_EINVAL;
     if (h.weight_bits == 0) h.weight_bits = 4;          // headers written before the field existed
     if (h.weight_bits != 4 && h.weight_bits != 8) return W4A8_EINVAL;
-    w4a8_wdesc dd{h.K, h.N, h.group_size, h.asymmetric, int32_t(h.weight_bits)};
+    if (h.scale_dtype > 1) return W4A8_EINVAL;
+    w4a8_wdesc dd{h.K, h.N, h.group_size, h.asymmetric, int32_t(h.weight_bits), h.scale_dtype ? 16 : 32};
     int st = desc_status(&dd);
     if (st) return st == W4A8_EUNSUPPORTED ? W4A8_EINVAL : st;
     Layout l = layout_of(&dd);
@@ -153,16 +158,62 @@ static void parallel_tiles(int Np, F f) {
     for (auto& x : th) x.join();
 }
 
+// Nearest binary16 value of a finite float (ties to even), returned as a float; +-infinity
+// past the binary16 range.  Binary16 has 11 significant bits down to 2^-14 and a fixed
+// spacing of 2^-24 below it (subnormals).
+static float round_f16(float f) {
+    const double v = std::fabs(double(f));
+    if (v == 0.0 || !std::isfinite(v)) return f;
+    int e;
+    std::frexp(v, &e);                                   // v in [2^(e-1), 2^e)
+    const int qe = std::max(e - 11, -24);                // spacing of the binary16 grid at v
+    double r = std::ldexp(std::nearbyint(std::ldexp(v, -qe)), qe);
+    if (r > 65504.0) r = HUGE_VAL;
+    return float(std::copysign(r, double(f)));
+}
+
+// Bit pattern of a binary16 value held exactly in a float (an output of round_f16).
+static uint16_t f16_bits(float h) {
+    const uint16_t sign = std::signbit(h) ? 0x8000u : 0u;
+    const double v = std::fabs(double(h));
+    if (std::isinf(v)) return sign | 0x7c00u;
+    if (v < std::ldexp(1.0, -14)) return uint16_t(sign | uint16_t(std::ldexp(v, 24)));   // subnormal or 0
+    int e;
+    const double m = std::frexp(v, &e);                  // v = (1 + f / 1024) 2^(e - 1)
+    return uint16_t(sign | uint16_t((e - 1 + 15) << 10) | uint16_t(std::ldexp(m, 11) - 1024.0));
+}
+
+static float f16_value(uint16_t b) {
+    const int ex = (b >> 10) & 31, fr = b & 1023;
+    double v;
+    if (ex == 31) v = fr ? NAN : HUGE_VAL;
+    else if (ex == 0) v = std::ldexp(double(fr), -24);
+    else v = std::ldexp(double(1024 + fr), ex - 25);
+    return float((b & 0x8000u) ? -v : v);
+}
+
+static void store_scale(const Layout& L, uint8_t* scales, size_t idx, float s) {
+    if (L.sbytes == 2) reinterpret_cast<uint16_t*>(scales)[idx] = f16_bits(s);
+    else reinterpret_cast<float*>(scales)[idx] = s;
+}
+
+static float load_scale(const Layout& L, const uint8_t* scales, size_t idx) {
+    return L.sbytes == 2 ? f16_value(reinterpret_cast<const uint16_t*>(scales)[idx])
+                         : reinterpret_cast<const float*>(scales)[idx];
+}
+
 // Quantize one group (g values of column n, stride N) -- P3 "Basic mapping" and the P3
 // symmetric group-wise reference; IEEE float32 division and round-half-to-even (rint under
 // the default rounding mode), matching the per-group rule stated in w4a8.h.
-static void rtn_group(const float* w, size_t stride, int g, int asym, int bits, int8_t* q, float* s_out,
+// h16: the float32 scale is first rounded to binary16, and the codes use the rounded value.
+static void rtn_group(const float* w, size_t stride, int g, int asym, int bits, bool h16, int8_t* q, float* s_out,
                       uint8_t* z_out) {
     if (!asym) {
         const float qmax = bits == 8 ? 127.0f : 7.0f;    // 2^(bits-1) - 1
         float amax = 0.0f;
         for (int t = 0; t < g; ++t) amax = std::max(amax, std::fabs(w[size_t(t) * stride]));
-        const float s = amax / qmax;
+        float s = amax / qmax;
+        if (h16) s = round_f16(s);
         const float d = s > 0.0f ? s : 1.0f;
         for (int t = 0; t < g; ++t) {
             float r = std::rint(w[size_t(t) * stride] / d);
@@ -180,7 +231,8 @@ static void rtn_group(const float* w, size_t stride, int g, int asym, int bits, 
         hi = std::max(hi, v);
     }
     const float range = hi - lo;
-    const float s = range / 15.0f;
+    float s = range / 15.0f;
+    if (h16) s = round_f16(s);
     if (!(s > 0.0f)) {
         for (int t = 0; t < g; ++t) q[t] = 0;
         *s_out = s;
@@ -234,23 +286,25 @@ int w4a8_pack(const w4a8_wdesc* d, const float* W, void* blob_host, size_t blob_
     std::memset(blob, 0, L.total);
     write_header(d, L, blob);
     uint8_t* codes = blob + L.codes_off;
-    float* scales = reinterpret_cast<float*>(blob + L.scales_off);
+    uint8_t* scales = blob + L.scales_off;
     uint8_t* zeros = blob + L.zeros_off;
     const int g = L.g, N = L.N;
+    std::atomic<bool> overflow(false);
     parallel_tiles(L.Np, [&](int t0, int t1) {
         std::vector<int8_t> q(static_cast<size_t>(g));
         for (int n = t0 * 16; n < std::min(N, t1 * 16); ++n) {
             for (int i = 0; i < L.G; ++i) {
                 float s;
                 uint8_t z;
-                rtn_group(W + size_t(i) * g * N + n, size_t(N), g, L.asym, L.bits, q.data(), &s, &z);
-                scales[meta_index(L, i, n)] = s;
+                rtn_group(W + size_t(i) * g * N + n, size_t(N), g, L.asym, L.bits, L.sbytes == 2, q.data(), &s, &z);
+                if (!std::isfinite(s)) overflow = true;
+                store_scale(L, scales, meta_index(L, i, n), s);
                 if (L.asym) zeros[meta_index(L, i, n)] = z;
                 for (int t = 0; t < g; ++t) store_code(L, codes, i * g + t, n, q[size_t(t)]);
             }
         }
     });
-    return W4A8_OK;
+    return overflow ? W4A8_EINVAL : W4A8_OK;     // a scale past the binary16 range
 }
 
 int w4a8_pack_codes(const w4a8_wdesc* d, const int8_t* codesIn, const float* scalesIn,
@@ -273,13 +327,17 @@ int w4a8_pack_codes(const w4a8_wdesc* d, const int8_t* codesIn, const float* sca
     std::memset(blob, 0, L.total);
     write_header(d, L, blob);
     uint8_t* codes = blob + L.codes_off;
-    float* scales = reinterpret_cast<float*>(blob + L.scales_off);
+    uint8_t* scales = blob + L.scales_off;
     uint8_t* zeros = blob + L.zeros_off;
     const int N = L.N;
+    if (L.sbytes == 2)
+        for (size_t i = 0; i < size_t(L.G) * size_t(N); ++i)
+            if (std::isfinite(scalesIn[i]) && !std::isfinite(round_f16(scalesIn[i]))) return W4A8_EINVAL;
     parallel_tiles(L.Np, [&](int t0, int t1) {
         for (int n = t0 * 16; n < std::min(N, t1 * 16); ++n) {
             for (int i = 0; i < L.G; ++i) {
-                scales[meta_index(L, i, n)] = scalesIn[size_t(i) * N + n];
+                const float sv = scalesIn[size_t(i) * N + n];
+                store_scale(L, scales, meta_index(L, i, n), L.sbytes == 2 ? round_f16(sv) : sv);
                 if (L.asym) zeros[meta_index(L, i, n)] = zerosIn[size_t(i) * N + n];
             }
             for (int k = 0; k < L.K; ++k) store_code(L, codes, k, n, codesIn[size_t(k) * N + n]);
@@ -297,11 +355,11 @@ int w4a8_unpack_codes(const void* blob_host, size_t blob_bytes, w4a8_wdesc* d_ou
     if (d_out) *d_out = d;
     const uint8_t* blob = static_cast<const uint8_t*>(blob_host);
     const uint8_t* codes = blob + L.codes_off;
-    const float* scales = reinterpret_cast<const float*>(blob + L.scales_off);
+    const uint8_t* scales = blob + L.scales_off;
     const uint8_t* zeros = blob + L.zeros_off;
     for (int n = 0; n < L.N; ++n) {
         for (int i = 0; i < L.G; ++i) {
-            if (scalesOut) scalesOut[size_t(i) * L.N + n] = scales[meta_index(L, i, n)];
+            if (scalesOut) scalesOut[size_t(i) * L.N + n] = load_scale(L, scales, meta_index(L, i, n));
             if (zerosOut && L.asym) zerosOut[size_t(i) * L.N + n] = zeros[meta_index(L, i, n)];
         }
         if (codesOut && L.bits == 8)
@@ -327,7 +385,7 @@ int w4a8_blob_check(const void* blob_host, size_t blob_bytes, const w4a8_wdesc* 
     st = read_header(blob_host, blob_bytes, &h, &L);
     if (st) return st;
     if (h.K != d->K || h.N != d->N || h.group_size != d->group_size || h.asymmetric != d->asymmetric ||
-        layout_of(&h).bits != layout_of(d).bits)
+        layout_of(&h).bits != layout_of(d).bits || layout_of(&h).sbytes != layout_of(d).sbytes)
         return W4A8_EINVAL;
     return W4A8_OK;
 }

@@ -14,6 +14,7 @@ constexpr int SB_K = 128;   // superblock depth: 16 columns x 128 k = 1 KiB of p
 struct Layout {
     int K, N, Np, g, G, asym;
     int bits;               // 4 or 8 (desc weight_bits, 0 read as 4)
+    int sbytes;             // bytes per scale: 4 (float32) or 2 (binary16, desc scale_bits 16)
     size_t codes_off, codes_bytes, scales_off, scales_bytes, zeros_off, zeros_bytes, total;
 };
 

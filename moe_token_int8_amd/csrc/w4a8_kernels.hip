@@ -20,6 +20,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "w4a8_internal.h"
 
@@ -31,6 +32,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // small device helpers
 // ------------------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// binary16 bit pattern -> float32 (exact)
+__device__ __forceinline__ float f16_to_f32(uint16_t bits) { return static_cast<float>(__builtin_bit_cast(_Float16, bits)); }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -92,6 +96,8 @@ __device__ __forceinline__ int quant_one(float x, float d, float inv, bool fast)
 struct RowScale {
     float s, d, inv;
     bool finite, fast;
+    float lim;      // static scales: values are clamped to +-lim = 128 d before the division
+    bool huge;      // static scales: 128 d overflows (d > 2^120), lim is FLT_MAX
 };
 
 // Scale of a row from the bit pattern of its abs-max.  With UNIFORM (the default) amax_bits
@@ -215,25 +221,30 @@ __device__ __forceinline__ RowScale static_row_scale(float s) {
     r.d = r.finite ? s : 1.0f;
     r.inv = 1.0f / r.d;
     r.fast = r.d >= 1e-30f;
+    r.huge = r.d > 1.329228e36f;                         // 2^120
+    r.lim = r.huge ? 3.40282347e38f : 128.0f * r.d;
     return r;
 }
 
-// clamp(rint(fl32(x / d)), -127, 127) for any x.  Values are first limited to +-128 d (a
-// power-of-two multiple, exact unless it overflows, hence the FLT_MAX cap): every such value
-// still saturates, and quant_one's quotient stays finite.  NaN gives 0; +-Inf gives +-127.
+// clamp(rint(fl32(x / d)), -127, 127) for any x.  Values are first limited to +-lim = 128 d
+// (one med3; exact, a power-of-two multiple): every such value still saturates, +-Inf
+// included, and quant_one's quotient stays finite.  NaN gives 0.  With d > 2^120 (lim is
+// FLT_MAX there) +-Inf is set to +-127 explicitly.
+template <bool HUGE = true>
 __device__ __forceinline__ int quant_static_one(float x, const RowScale& r) {
-    const float lim = fminf(128.0f * r.d, 3.40282347e38f);
-    int q = quant_one(fminf(fmaxf(x, -lim), lim), r.d, r.inv, r.fast);
+    int q = quant_one(__builtin_amdgcn_fmed3f(x, -r.lim, r.lim), r.d, r.inv, r.fast);
     if (x != x) q = 0;
-    else if (fabsf(x) > 3.40282347e38f) q = x > 0.0f ? 127 : -127;
+    if (HUGE && r.huge && fabsf(x) > 3.40282347e38f) q = x > 0.0f ? 127 : -127;
     return q;
 }
 
 // Row r of Xq quantizes source row src of X with the scale s[e]: src = r (gather == NULL) or
 // gather[r] / k; e = 0 (offs == NULL) or the expert that owns sorted row r.  Rows no expert
 // owns (r >= offs[E]: routing ids outside [0, E)) and gathered rows outside [0, T) get zero
-// codes and scale 0.  One 256-thread workgroup per row, one pass: each value is quantized as
-// it is read.
+// codes and scale 0.  One 256-thread workgroup per row, one pass: each thread issues the loads
+// of its IT pieces of 8 values at once, then quantizes and stores them (rows longer than
+// IT * 2048 values take several such passes).
+template <int IT>
 __global__ __launch_bounds__(256) void quant_static_kernel(const uint16_t* __restrict__ X, int K, int ldx, int T,
                                                            const float* __restrict__ s,
                                                            const int32_t* __restrict__ gather, int k,
@@ -251,25 +262,42 @@ __global__ __launch_bounds__(256) void quant_static_kernel(const uint16_t* __res
         src = gr >= 0 ? gr / k : -1;
         live = src >= 0 && src < T;
     }
-    const RowScale rs = static_row_scale(live ? s[e] : 0.0f);
+    const float sv = live ? s[e] : 0.0f;
     const uint16_t* xr = X + size_t(live ? src : 0) * size_t(ldx);
     int8_t* qr = Xq + size_t(row) * size_t(K);
-    for (int kk = tid * 8; kk < K; kk += 256 * 8) {
-        uint32_t out[2] = {0, 0};
-        if (rs.finite) {
-            const uint4 v = *reinterpret_cast<const uint4*>(xr + kk);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int base = 0; base < K; base += IT * 256 * 8) {
+        uint4 v[IT];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int q0 = quant_static_one(bf16_to_f32(w[j] & 0xffffu), rs);
-                const int q1 = quant_static_one(bf16_to_f32(w[j] >> 16), rs);
-                const uint32_t pair = (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8);
-                out[j >> 1] |= pair << ((j & 1) * 16);
-            }
+        for (int it = 0; it < IT; ++it) {
+            const int kk = base + (it * 256 + tid) * 8;
+            v[it] = make_uint4(0, 0, 0, 0);
+            if (live && kk < K) v[it] = *reinterpret_cast<const uint4*>(xr + kk);
         }
-        *reinterpret_cast<uint2*>(qr + kk) = make_uint2(out[0], out[1]);
+        const RowScale rs = static_row_scale(sv);
+        // the scale is uniform per row: the d > 2^120 handling is one branch, not a select per value
+        auto quantize = [&](auto huge) __attribute__((always_inline)) {
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int kk = base + (it * 256 + tid) * 8;
+                if (kk >= K) continue;
+                uint32_t out[2] = {0, 0};
+                if (rs.finite) {
+                    const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int q0 = quant_static_one<decltype(huge)::value>(bf16_to_f32(w[j] & 0xffffu), rs);
+                        const int q1 = quant_static_one<decltype(huge)::value>(bf16_to_f32(w[j] >> 16), rs);
+                        const uint32_t pair = (uint32_t(q0) & 0xffu) | ((uint32_t(q1) & 0xffu) << 8);
+                        out[j >> 1] |= pair << ((j & 1) * 16);
+                    }
+                }
+                *reinterpret_cast<uint2*>(qr + kk) = make_uint2(out[0], out[1]);
+            }
+        };
+        if (__builtin_amdgcn_readfirstlane(int(rs.huge))) quantize(std::true_type{});
+        else quantize(std::false_type{});
     }
-    if (tid == 0) sx[row] = rs.s;
+    if (tid == 0) sx[row] = sv;
 }
 
 // STATIC: row r (in expert-sorted order) takes the scale s[e] of the expert that owns it
@@ -365,6 +393,7 @@ struct GemmArgs {
     const int32_t* offsets;   // MoE: expert row offsets [E+1]
     int E;
     int moe_lo, moe_hi;       // MoE: this launch serves the experts with moe_lo <= rows < moe_hi
+    int h16;                  // binary16 group scales (selects the H16 kernels)
 };
 
 // Unpack two packed words (16 codes of one column) into one MFMA B operand.
@@ -451,7 +480,9 @@ constexpr size_t FUSED_MAX_ELEMS = 8192;
 // activation tile; workgroup 0 also exports the codes and row scales.
 // W8: 8-bit weight codes (2 KiB superblocks, 32 bytes per layout lane), used as MFMA operands
 // as loaded; otherwise 4-bit codes unpacked in registers.
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI, bool FQ, bool W8>
+// H16: binary16 group scales (converted to float32 as loaded).
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI, bool FQ, bool W8,
+          bool H16 = false>
 __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     using S = DecodeShape<MS, NT, KW, SBN>;
     static_assert(!FQ || (MS == 1 && !MOE && MODE == MODE_OUT && !MULTI), "fused quantization: dense, one chunk");
@@ -496,6 +527,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     const int nrows = rend - rbeg;
     const uint8_t* codes = blob + a.codes_off;
     const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
+    const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(blob + a.scales_off);
     const uint8_t* zeros = blob + a.zeros_off;
 
     // row scales of the rows this lane stores, fetched before anything else so the
@@ -572,7 +604,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const uint32_t mi = moff + uint32_t(gidx(int(sb), gi)) * 16u;
-                sc[s][gi] = scales[mi];
+                sc[s][gi] = H16 ? f16_to_f32(scales16[mi]) : scales[mi];
                 if (ASYM) zq[s][gi] = zeros[mi];
             }
         }
@@ -807,7 +839,7 @@ struct KsliceShape {
 // weights are streamed once per column tile instead of once per row tile.
 constexpr int MOE_KSLICE_ROWS = 128;
 
-template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, int TG, bool RL>
+template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, int TG, bool RL, bool H16 = false>
 __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     using S = KsliceShape<MS, T, TG>;
     static_assert(!RL || (MOE && MODE == MODE_OUT && TG == 1), "row loop: grouped form, one tile group");
@@ -839,6 +871,7 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     int nrows = rend - rbeg;
     const uint8_t* codes = blob + a.codes_off;
     const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
+    const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(blob + a.scales_off);
     const uint8_t* zeros = blob + a.zeros_off;
 
     // row scales of the tile's rows: fetched first, parked in LDS after the MFMAs
@@ -891,7 +924,7 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
 #pragma unroll
                 for (int gi = 0; gi < GPS; ++gi) {
                     const uint32_t mi = (tc * uint32_t(a.G) + sb * GPS + gi) * 16u + uint32_t(lane & 15);
-                    sc[g % NSET][t][s][gi] = scales[mi];
+                    sc[g % NSET][t][s][gi] = H16 ? f16_to_f32(scales16[mi]) : scales[mi];
                     if (ASYM) zq[g % NSET][t][s][gi] = zeros[mi];
                 }
             }
@@ -1083,7 +1116,8 @@ struct PfRegs {
 // is a PF_BM-row tile of one expert (moe_tile), rows gathered from the token rows when
 // `gather` is set; output row r is the r-th sorted row.
 // W8: 8-bit weight codes, copied to the LDS operand layout as loaded (no unpack).
-template <bool ASYM, int GPS, int MODE, bool MOE, bool W8>
+// H16: binary16 group scales, converted to float32 before they are staged in LDS.
+template <bool ASYM, int GPS, int MODE, bool MOE, bool W8, bool H16 = false>
 __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a) {
     static_assert(!W8 || (!ASYM && !MOE), "8-bit codes: symmetric, dense");
     // GPS 0: g = 256, one group per superblock pair (even, odd), which the loop runs back to back
@@ -1175,8 +1209,18 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
             const int mt = tid % nmeta_s;
             const int tl = mt / (NG * 4), gi = (mt / 4) % NG, q4 = mt % 4;
             const int tile = min(t0 + tl, ntl16 - 1);
-            const v4i t = __builtin_amdgcn_raw_buffer_load_b128(sr, ((tile * a.G + gidx(sb, gi)) * 16 + q4 * 4) * 4, 0, 0);
-            r.m = make_uint4(uint32_t(t.x), uint32_t(t.y), uint32_t(t.z), uint32_t(t.w));
+            const int mo = (tile * a.G + gidx(sb, gi)) * 16 + q4 * 4;
+            if constexpr (H16) {
+                const auto t = __builtin_amdgcn_raw_buffer_load_b64(sr, mo * 2, 0, 0);
+                const uint32_t h0 = uint32_t(t[0]), h1 = uint32_t(t[1]);
+                r.m = make_uint4(__float_as_uint(f16_to_f32(uint16_t(h0 & 0xffffu))),
+                                 __float_as_uint(f16_to_f32(uint16_t(h0 >> 16))),
+                                 __float_as_uint(f16_to_f32(uint16_t(h1 & 0xffffu))),
+                                 __float_as_uint(f16_to_f32(uint16_t(h1 >> 16))));
+            } else {
+                const v4i t = __builtin_amdgcn_raw_buffer_load_b128(sr, mo * 4, 0, 0);
+                r.m = make_uint4(uint32_t(t.x), uint32_t(t.y), uint32_t(t.z), uint32_t(t.w));
+            }
         }
     };
     auto lstore = [&](const PfRegs& r, int stage) {
@@ -1519,10 +1563,10 @@ static DecodeCfg decode_cfg(int K, int mt) {
 }
 
 template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, int MODE, bool MOE, bool MULTI = false, bool FQ = false,
-          bool W8 = false>
+          bool W8 = false, bool H16 = false>
 static void launch_decode_t(const GemmArgs& a, dim3 grid, hipStream_t s) {
     using S = DecodeShape<MS, NT, KW, SBN>;
-    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, MULTI, FQ, W8>;
+    auto kern = gemm_decode_kernel<MS, NT, KW, SBN, GPS, ASYM, MODE, MOE, MULTI, FQ, W8, H16>;
     constexpr size_t lds = S::LDS + (FQ ? 128 : 0);           // FQ: row abs-maxima
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -1531,25 +1575,25 @@ static void launch_decode_t(const GemmArgs& a, dim3 grid, hipStream_t s) {
 }
 
 // Fused quantization + GEMM on the chunked kernel (dense, 16-row tile, K in one chunk).
-template <int GPS, bool ASYM, bool W8 = false>
+template <int GPS, bool ASYM, bool W8 = false, bool H16 = false>
 static void launch_decode_fused(const GemmArgs& a, const DecodeCfg& c, dim3 grid, hipStream_t s) {
-    if (c.kw == 8) launch_decode_t<1, 2, 8, 8, GPS, ASYM, MODE_OUT, false, false, true, W8>(a, grid, s);
-    else if (c.sbn == 2) launch_decode_t<1, 4, 4, 2, GPS, ASYM, MODE_OUT, false, false, true, W8>(a, grid, s);
-    else if (c.sbn == 4) launch_decode_t<1, 4, 4, 4, GPS, ASYM, MODE_OUT, false, false, true, W8>(a, grid, s);
-    else launch_decode_t<1, 4, 4, 8, GPS, ASYM, MODE_OUT, false, false, true, W8>(a, grid, s);
+    if (c.kw == 8) launch_decode_t<1, 2, 8, 8, GPS, ASYM, MODE_OUT, false, false, true, W8, H16>(a, grid, s);
+    else if (c.sbn == 2) launch_decode_t<1, 4, 4, 2, GPS, ASYM, MODE_OUT, false, false, true, W8, H16>(a, grid, s);
+    else if (c.sbn == 4) launch_decode_t<1, 4, 4, 4, GPS, ASYM, MODE_OUT, false, false, true, W8, H16>(a, grid, s);
+    else launch_decode_t<1, 4, 4, 8, GPS, ASYM, MODE_OUT, false, false, true, W8, H16>(a, grid, s);
 }
 
-template <int MS, int GPS, bool ASYM, int MODE, bool MOE, bool W8 = false>
+template <int MS, int GPS, bool ASYM, int MODE, bool MOE, bool W8 = false, bool H16 = false>
 static void launch_decode_shape(const GemmArgs& a, const DecodeCfg& c, dim3 grid, hipStream_t s) {
     if (c.kw == 8) {
         if constexpr (MS == 1) {
-            if (a.K > 64 * SB_K) launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE, true, false, W8>(a, grid, s);
-            else launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE, false, false, W8>(a, grid, s);
+            if (a.K > 64 * SB_K) launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE, true, false, W8, H16>(a, grid, s);
+            else launch_decode_t<MS, 2, 8, 8, GPS, ASYM, MODE, MOE, false, false, W8, H16>(a, grid, s);
         }
-    } else if (c.sbn == 2) launch_decode_t<MS, 4, 4, 2, GPS, ASYM, MODE, MOE, false, false, W8>(a, grid, s);
-    else if (c.sbn == 4) launch_decode_t<MS, 4, 4, 4, GPS, ASYM, MODE, MOE, false, false, W8>(a, grid, s);
-    else if (a.K > 32 * SB_K) launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, true, false, W8>(a, grid, s);
-    else launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, false, false, W8>(a, grid, s);
+    } else if (c.sbn == 2) launch_decode_t<MS, 4, 4, 2, GPS, ASYM, MODE, MOE, false, false, W8, H16>(a, grid, s);
+    else if (c.sbn == 4) launch_decode_t<MS, 4, 4, 4, GPS, ASYM, MODE, MOE, false, false, W8, H16>(a, grid, s);
+    else if (a.K > 32 * SB_K) launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, true, false, W8, H16>(a, grid, s);
+    else launch_decode_t<MS, 4, 4, 8, GPS, ASYM, MODE, MOE, false, false, W8, H16>(a, grid, s);
 }
 
 // gps: groups per superblock (2, 1, 0 for g = 256, -1 per-channel); w8: 8-bit codes.  g = 256,
@@ -1583,6 +1627,13 @@ static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool a
             }
         }
     }
+#undef W4A8_DEC
+    // 4-bit codes, g in {64, 128}: float32 or binary16 scales
+#define W4A8_DEC(MS_, GPS_, ASYM_)                                                              \
+    do {                                                                                        \
+        if (a.h16) launch_decode_shape<MS_, GPS_, ASYM_, MODE, MOE, false, true>(a, c, grid, s); \
+        else launch_decode_shape<MS_, GPS_, ASYM_, MODE, MOE>(a, c, grid, s);                  \
+    } while (0)
     if (c.ms == 1) {
         if (gps == 1) { if (asym) W4A8_DEC(1, 1, true); else W4A8_DEC(1, 1, false); }
         else { if (asym) W4A8_DEC(1, 2, true); else W4A8_DEC(1, 2, false); }
@@ -1640,11 +1691,11 @@ static bool kslice_cfg(int K, int mt, KsliceCfg* c, bool moe = false) {
 }
 
 
-template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, int TG = 1, bool RL = false>
+template <int MS, int T, int SW, int GPS, bool ASYM, int MODE, bool MOE, int TG = 1, bool RL = false, bool H16 = false>
 static void launch_kslice_t(const GemmArgs& a, int kw, int ytiles, hipStream_t s) {
     using S = KsliceShape<MS, T, TG>;
     static_assert(S::lds(16) <= 160 * 1024, "slice partials exceed LDS");
-    auto kern = gemm_kslice_kernel<MS, T, SW, GPS, ASYM, MODE, MOE, TG, RL>;
+    auto kern = gemm_kslice_kernel<MS, T, SW, GPS, ASYM, MODE, MOE, TG, RL, H16>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        int(S::lds(16)));
@@ -1654,41 +1705,45 @@ static void launch_kslice_t(const GemmArgs& a, int kw, int ytiles, hipStream_t s
     kern<<<dim3((ntiles + S::TT - 1) / S::TT, ytiles), dim3(64 * kw), lds, s>>>(a);
 }
 
-template <int MS, int GPS, bool ASYM, int MODE, bool MOE>
+template <int MS, int GPS, bool ASYM, int MODE, bool MOE, bool H16 = false>
 static void launch_kslice_shape(const GemmArgs& a, const KsliceCfg& c, int ytiles, hipStream_t s) {
     // shapes kslice_cfg can return for this form (others are not instantiated)
     if (c.sw == 1) {
         if constexpr (MOE && MS == 2 && MODE == MODE_OUT) {
             if (c.rl) {
-                launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE, 1, true>(a, c.kw, ytiles, s);
+                launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE, 1, true, H16>(a, c.kw, ytiles, s);
                 return;
             }
         }
-        launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+        launch_kslice_t<MS, 4, 1, GPS, ASYM, MODE, MOE, 1, false, H16>(a, c.kw, ytiles, s);
     } else if (c.sw == 2) {
         if constexpr (MOE && MS == 1) {
             if (c.tg == MOE_KSLICE_TG_SHORT) {
-                launch_kslice_t<MS, 2, 2, GPS, ASYM, MODE, MOE, MOE_KSLICE_TG_SHORT>(a, c.kw, ytiles, s);
+                launch_kslice_t<MS, 2, 2, GPS, ASYM, MODE, MOE, MOE_KSLICE_TG_SHORT, false, H16>(a, c.kw, ytiles, s);
                 return;
             }
         }
         if constexpr (MOE && MS == 1 && MODE == MODE_OUT) {
             if (c.rl) {
-                launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE, 1, true>(a, c.kw, ytiles, s);
+                launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE, 1, true, H16>(a, c.kw, ytiles, s);
                 return;
             }
         }
-        launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+        launch_kslice_t<MS, 4, 2, GPS, ASYM, MODE, MOE, 1, false, H16>(a, c.kw, ytiles, s);
     } else if constexpr (MS == 1) {
-        if constexpr (MOE) launch_kslice_t<MS, 1, 4, GPS, ASYM, MODE, MOE, MOE_KSLICE_TG>(a, c.kw, ytiles, s);
-        else launch_kslice_t<MS, 2, 4, GPS, ASYM, MODE, MOE>(a, c.kw, ytiles, s);
+        if constexpr (MOE) launch_kslice_t<MS, 1, 4, GPS, ASYM, MODE, MOE, MOE_KSLICE_TG, false, H16>(a, c.kw, ytiles, s);
+        else launch_kslice_t<MS, 2, 4, GPS, ASYM, MODE, MOE, 1, false, H16>(a, c.kw, ytiles, s);
     }
 }
 
 template <int MODE, bool MOE>
 static void launch_kslice(const GemmArgs& a, const KsliceCfg& c, int ms, int gps, bool asym, int ytiles,
                           hipStream_t s) {
-#define W4A8_KS(MS_, GPS_, ASYM_) launch_kslice_shape<MS_, GPS_, ASYM_, MODE, MOE>(a, c, ytiles, s)
+#define W4A8_KS(MS_, GPS_, ASYM_)                                                           \
+    do {                                                                                    \
+        if (a.h16) launch_kslice_shape<MS_, GPS_, ASYM_, MODE, MOE, true>(a, c, ytiles, s); \
+        else launch_kslice_shape<MS_, GPS_, ASYM_, MODE, MOE>(a, c, ytiles, s);            \
+    } while (0)
     if (ms == 1) {
         if (gps == 1) { if (asym) W4A8_KS(1, 1, true); else W4A8_KS(1, 1, false); }
         else { if (asym) W4A8_KS(1, 2, true); else W4A8_KS(1, 2, false); }
@@ -1700,9 +1755,9 @@ static void launch_kslice(const GemmArgs& a, const KsliceCfg& c, int ms, int gps
 }
 
 // mtiles: row tiles (dense) or an upper bound on the experts' row tiles (MOE)
-template <bool ASYM, int GPS, int MODE, bool MOE, bool W8 = false>
+template <bool ASYM, int GPS, int MODE, bool MOE, bool W8 = false, bool H16 = false>
 static void launch_prefill_t(const GemmArgs& a, int mtiles, hipStream_t s) {
-    auto kern = gemm_prefill_kernel<ASYM, GPS, MODE, MOE, W8>;
+    auto kern = gemm_prefill_kernel<ASYM, GPS, MODE, MOE, W8, H16>;
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS);
     (void)attr;
@@ -1732,11 +1787,18 @@ static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s,
             return;
         }
     }
+    // 4-bit codes, g in {64, 128}: float32 or binary16 scales
+#define W4A8_PF(ASYM_, GPS_)                                                            \
+    do {                                                                                \
+        if (a.h16) launch_prefill_t<ASYM_, GPS_, MODE, MOE, false, true>(a, mtiles, s); \
+        else launch_prefill_t<ASYM_, GPS_, MODE, MOE>(a, mtiles, s);                    \
+    } while (0)
     if (gps == 1) {
-        if (asym) launch_prefill_t<true, 1, MODE, MOE>(a, mtiles, s); else launch_prefill_t<false, 1, MODE, MOE>(a, mtiles, s);
+        if (asym) W4A8_PF(true, 1); else W4A8_PF(false, 1);
     } else {
-        if (asym) launch_prefill_t<true, 2, MODE, MOE>(a, mtiles, s); else launch_prefill_t<false, 2, MODE, MOE>(a, mtiles, s);
+        if (asym) W4A8_PF(true, 2); else W4A8_PF(false, 2);
     }
+#undef W4A8_PF
 }
 
 // MoE experts with at least this many rows run on the prefill kernel (256-row tiles: each
@@ -1762,6 +1824,8 @@ static dim3 decode_grid(const Layout& L, const DecodeCfg& c, int ytiles) {
 static bool kernel_format_ok(const w4a8_wdesc* d) {
     const int g = d->group_size;
     if (g != 64 && g != 128 && g != 256 && g != d->K) return false;
+    // binary16 scales: 4-bit codes with g in {64, 128}
+    if (d->scale_bits == 16 && (d->weight_bits == 8 || (g != 64 && g != 128))) return false;
     const int64_t qr = d->weight_bits == 8 ? 127 : 15;
     return int64_t(g) * 127 * qr < (int64_t(1) << 31);
 }
@@ -1793,6 +1857,7 @@ static GemmArgs make_args(const Layout& L, const int8_t* Xq, const float* sx, in
     a.codes_off = L.codes_off;
     a.scales_off = L.scales_off;
     a.zeros_off = L.zeros_off;
+    a.h16 = L.sbytes == 2;
     return a;
 }
 
@@ -1849,8 +1914,15 @@ static int quant_static_impl(const void* X, int rows, int K, int ldx, int T, con
     if (rows == 0) return W4A8_OK;
     if (!X || !s || !Xq || !sx) return W4A8_EINVAL;
     if (K % 16 || ldx % 8 || !aligned16(X) || !aligned16(Xq)) return W4A8_EINVAL;
-    quant_static_kernel<<<dim3(rows), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-        static_cast<const uint16_t*>(X), K, ldx, T, s, gather, k, offs, E, Xq, sx);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint16_t* x = static_cast<const uint16_t*>(X);
+    const dim3 grid(rows), block(256);
+    switch (std::min(row_iters(K), 8)) {      // longer rows: several passes of 8 pieces per thread
+        case 1: quant_static_kernel<1><<<grid, block, 0, st>>>(x, K, ldx, T, s, gather, k, offs, E, Xq, sx); break;
+        case 2: quant_static_kernel<2><<<grid, block, 0, st>>>(x, K, ldx, T, s, gather, k, offs, E, Xq, sx); break;
+        case 4: quant_static_kernel<4><<<grid, block, 0, st>>>(x, K, ldx, T, s, gather, k, offs, E, Xq, sx); break;
+        default: quant_static_kernel<8><<<grid, block, 0, st>>>(x, K, ldx, T, s, gather, k, offs, E, Xq, sx); break;
+    }
     return launch_status();
 }
 
@@ -1929,9 +2001,11 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
         } else if (gps < 0) {
             if (d->asymmetric) launch_decode_fused<-1, true>(a, fc, grid, s); else launch_decode_fused<-1, false>(a, fc, grid, s);
         } else if (gps == 1) {
-            if (d->asymmetric) launch_decode_fused<1, true>(a, fc, grid, s); else launch_decode_fused<1, false>(a, fc, grid, s);
+            if (a.h16) { if (d->asymmetric) launch_decode_fused<1, true, false, true>(a, fc, grid, s); else launch_decode_fused<1, false, false, true>(a, fc, grid, s); }
+            else if (d->asymmetric) launch_decode_fused<1, true>(a, fc, grid, s); else launch_decode_fused<1, false>(a, fc, grid, s);
         } else {
-            if (d->asymmetric) launch_decode_fused<2, true>(a, fc, grid, s); else launch_decode_fused<2, false>(a, fc, grid, s);
+            if (a.h16) { if (d->asymmetric) launch_decode_fused<2, true, false, true>(a, fc, grid, s); else launch_decode_fused<2, false, false, true>(a, fc, grid, s); }
+            else if (d->asymmetric) launch_decode_fused<2, true>(a, fc, grid, s); else launch_decode_fused<2, false>(a, fc, grid, s);
         }
         return launch_status();
     }
@@ -2226,9 +2300,18 @@ const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
          {W4A8_NAMES("w8a8", "_decode_m32", "_sym"), {}},
          {W4A8_NAMES("w8a8", "_prefill", "_sym"), {}}}};
 #undef W4A8_NAMES
+    // binary16 scales (4-bit codes, g in {64, 128})
+    static const char* const names16[3][2][2] = {
+        {{"w4a8_decode_m16_sym_g64_h16", "w4a8_decode_m16_sym_g128_h16"},
+         {"w4a8_decode_m16_asym_g64_h16", "w4a8_decode_m16_asym_g128_h16"}},
+        {{"w4a8_decode_m32_sym_g64_h16", "w4a8_decode_m32_sym_g128_h16"},
+         {"w4a8_decode_m32_asym_g64_h16", "w4a8_decode_m32_asym_g128_h16"}},
+        {{"w4a8_prefill_sym_g64_h16", "w4a8_prefill_sym_g128_h16"},
+         {"w4a8_prefill_asym_g64_h16", "w4a8_prefill_asym_g128_h16"}}};
     const int kind = M >= PREFILL_MIN_M ? 2 : (dense_mt(M) == 32 ? 1 : 0);
     const int gps = gps_of(d);
     const int gi = gps == 2 ? 0 : gps == 1 ? 1 : gps == 0 ? 2 : 3;
+    if (layout_of(d).sbytes == 2) return names16[kind][d->asymmetric][gi];
     return names[layout_of(d).bits == 8][kind][d->asymmetric][gi];
 }
 

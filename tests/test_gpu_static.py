@@ -70,6 +70,20 @@ def test_quant_act_static_edge_values_and_strides():
     assert qr[1, :6].tolist() == [0, 127, -127, 127, -127, 0]
 
 
+def test_quant_act_static_huge_scale():
+    """A scale above 2^120 (128 s overflows): infinities still saturate, huge finite values
+    still divide exactly."""
+    x = np.zeros((2, 16), np.float32)
+    x[0, :7] = [np.inf, -np.inf, 3.3e38, -3.3e38, 1e38, np.nan, 0.0]
+    x[1, :] = np.linspace(-3e38, 3e38, 16)
+    Xb = W.to_bf16(x)
+    s = np.float32(2.0 ** 126)
+    q, sx = _static_quant(Xb, s)
+    qr, sr = O.quant_act_static(W.bf16_values(Xb), s)
+    assert np.array_equal(q, qr) and np.array_equal(sx, sr)
+    assert qr[0, :2].tolist() == [127, -127] and qr[0, 5] == 0
+
+
 @pytest.mark.parametrize("s", [0.0, -1.0, float("inf"), float("nan"), 1e-38])
 def test_quant_act_static_degenerate_scales(s):
     Xb = W.random_activations(3, 5, 256)

@@ -35,13 +35,14 @@ def decode_blob(blob: np.ndarray):
     magic = bytes(blob[:8])
     assert magic == b"W4A8BLB1"
     version, layout, K, N, g, asym, sdt, zdt = struct.unpack_from("<IIiiiiII", blob, 8)
-    assert (version, layout, sdt, zdt) == (1, 1, 0, 0)
+    assert (version, layout, zdt) == (1, 1, 0) and sdt in (0, 1)
     co, cb, so, sb_, zo, zb, total = struct.unpack_from("<7Q", blob, 40)
     (bits,) = struct.unpack_from("<I", blob, 96)
     assert bits in (4, 8)
     Np = (N + 15) // 16 * 16
     G = K // g
-    assert cb == Np * K * bits // 8 and sb_ == Np * G * 4 and zb == (Np * G if asym else 0)
+    ssz = 2 if sdt == 1 else 4                        # binary16 or float32 scales
+    assert cb == Np * K * bits // 8 and sb_ == Np * G * ssz and zb == (Np * G if asym else 0)
     assert co == 256 and so % 256 == 0 and zo % 256 == 0 and total % 256 == 0
     raw = blob[co:co + cb]
     codes = np.zeros((K, N), np.int8)
@@ -58,7 +59,7 @@ def decode_blob(blob: np.ndarray):
             nib = (j % 8) // 4
             v = (int(raw[byte]) >> (4 * nib)) & 0xF
             codes[k, n] = v - 16 if (not asym and v >= 8) else v
-    sc = np.frombuffer(blob[so:so + sb_].tobytes(), np.float32)
+    sc = np.frombuffer(blob[so:so + sb_].tobytes(), np.float16 if sdt == 1 else np.float32).astype(np.float32)
     scales = np.zeros((G, N), np.float32)
     zeros = np.zeros((G, N), np.uint8) if asym else None
     for n in range(N):
@@ -71,7 +72,8 @@ def decode_blob(blob: np.ndarray):
     for n in range(N, Np):
         for i in range(G):
             assert sc[((n // 16) * G + i) * 16 + n % 16] == 0
-    return dict(K=K, N=N, g=g, asym=bool(asym), bits=bits, codes=codes, scales=scales, zeros=zeros, total=total)
+    return dict(K=K, N=N, g=g, asym=bool(asym), bits=bits, codes=codes, scales=scales, zeros=zeros, total=total,
+                scale_bits=16 if sdt == 1 else 32)
 
 
 @pytest.mark.parametrize("K,N,g,asym", [(128, 16, 32, False), (256, 40, 64, True), (384, 19, 128, False),
@@ -119,6 +121,52 @@ def test_pack_8bit_matches_oracle_via_independent_decoder(K, N, g):
     L.w4a8_blob_check(blob, d)
     with pytest.raises(L.W4A8Error):                  # a 4-bit desc does not match the blob
         L.w4a8_blob_check(blob, L.desc(K, N, g, False))
+
+
+@pytest.mark.parametrize("K,N,g,asym", [(128, 16, 64, False), (256, 40, 128, True), (384, 19, 128, False),
+                                        (256, 33, 64, True), (128, 16, 32, True)])
+def test_pack_fp16_scales_matches_oracle_via_independent_decoder(K, N, g, asym):
+    """binary16 scales: the blob decoded from the layout text (scales read as binary16) equals
+    the oracle's scale_bits = 16 quantization; the library's inverse and pack_codes agree."""
+    rs = np.random.default_rng(K + N)
+    Wt = (W.random_weights(3000 + K + N, K, N) * rs.uniform(1e-3, 50, (1, N))).astype(np.float32)
+    Wt[:g, 0] = 0.0
+    Wt[:g, 1] = 1e-5                                  # a subnormal binary16 scale
+    d = L.desc(K, N, g, asym, scale_bits=16)
+    blob = L.w4a8_pack(d, Wt)
+    dec = decode_blob(blob)
+    codes, scales, zeros = O.quant_weight(Wt, g, asym, scale_bits=16)
+    assert dec["scale_bits"] == 16
+    assert np.array_equal(dec["codes"], codes)
+    assert np.array_equal(dec["scales"].view(np.uint32), scales.view(np.uint32))
+    if asym:
+        assert np.array_equal(dec["zeros"], zeros)
+    d2, c2, s2, z2 = L.w4a8_unpack_codes(blob)
+    assert (d2.K, d2.N, d2.group_size, d2.asymmetric, d2.scale_bits) == (K, N, g, int(asym), 16)
+    assert np.array_equal(c2, codes) and np.array_equal(s2.view(np.uint32), scales.view(np.uint32))
+    assert np.array_equal(L.w4a8_pack_codes(d, codes, scales, zeros), blob)
+    L.w4a8_blob_check(blob, d)
+    with pytest.raises(L.W4A8Error):                  # a float32-scale desc does not match the blob
+        L.w4a8_blob_check(blob, L.desc(K, N, g, asym))
+    assert L.w4a8_packed_size(d) <= L.w4a8_packed_size(L.desc(K, N, g, asym))   # sections are 256-aligned
+
+
+def test_fp16_scales_validation_and_names_host():
+    """Scale range, the kernel formats that take binary16 scales, and the resolved names."""
+    lib = L.lib()
+    fake = 0x10000
+    with pytest.raises(L.W4A8Error):                  # max|w| / 7 = 70000 > 65504
+        L.w4a8_pack(L.desc(128, 16, 64, False, scale_bits=16), np.full((128, 16), 490000.0, np.float32))
+    assert L.w4a8_packed_size(L.desc(128, 16, 64, False, scale_bits=24)) == 0
+    d = L.desc(4096, 64, 128, True, scale_bits=16)
+    assert L.w4a8_kernel_name(d, 1) == "w4a8_decode_m16_asym_g128_h16"
+    assert L.w4a8_kernel_name(d, 32) == "w4a8_decode_m32_asym_g128_h16"
+    assert L.w4a8_kernel_name(L.desc(4096, 64, 64, False, scale_bits=16), 64) == "w4a8_prefill_sym_g64_h16"
+    for bad in (L.desc(4096, 64, 256, False, scale_bits=16), L.desc(4096, 64, 4096, False, scale_bits=16),
+                L.desc(4096, 64, 128, False, bits=8, scale_bits=16)):
+        assert L.w4a8_packed_size(bad) > 0                    # the packer takes them
+        assert L.w4a8_kernel_name(bad, 1) == "unsupported"
+        assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(bad), fake, 64, 0, None) == L.W4A8_EUNSUPPORTED
 
 
 def test_8bit_validation_host():
