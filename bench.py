@@ -261,14 +261,16 @@ def cpu_baseline(args, leg, W):
 # ---------------------------------------------------------------------------------- prefill
 def prefill_leg(args, L, W, torch, dev, steps):
     """The projection pair at M = 4096 (asymmetric g128), and the up projection again with
-    g = 256 (half the per-group epilogues), with per-channel scales (g = K: one epilogue) and
-    with binary16 group scales, the same weights otherwise."""
+    g = 256 (half the per-group epilogues), with per-channel scales (g = K: one epilogue), with
+    binary16 group scales and with g = 32 (four epilogues per superblock), the same weights
+    otherwise."""
     out = {}
     import dataclasses
     g256 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "g256"), group_size=256)
     gk = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "gK"), group_size=W.C3_UP.K)
     h16 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name + "_fp16_scales")
-    for cfg in (W.C3_UP, W.C3_DOWN, g256, gk, h16):
+    g32 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "g32"), group_size=32)
+    for cfg in (W.C3_UP, W.C3_DOWN, g256, gk, h16, g32):
         d = L.desc(cfg.K, cfg.N, cfg.group_size, cfg.asymmetric, scale_bits=16 if cfg is h16 else 32)
         _, Wt = W.dense_inputs(cfg, M=1)
         blob = torch.from_numpy(L.w4a8_pack(d, Wt)).to(dev)
@@ -408,6 +410,7 @@ def compare_leg(args, L, W, torch, dev):
     d = L.desc(K, N, cfg.group_size, cfg.asymmetric)
     d8 = L.desc(K, N, cfg.group_size, False, bits=8)
     d16 = L.desc(K, N, cfg.group_size, cfg.asymmetric, scale_bits=16)
+    d32 = L.desc(K, N, 32, cfg.asymmetric)
     _, Wt = W.dense_inputs(cfg, M=1)
 
     def copies(desc):
@@ -417,7 +420,7 @@ def compare_leg(args, L, W, torch, dev):
             t[c].copy_(one)
         return t
 
-    blobs, blobs8, blobs16 = copies(d), copies(d8), copies(d16)
+    blobs, blobs8, blobs16, blobs32 = copies(d), copies(d8), copies(d16), copies(d32)
     wb = torch.from_numpy(Wt).to(dev).to(torch.bfloat16)
     Wb = torch.empty((ncopy, K, N), dtype=torch.bfloat16, device=dev)
     for c in range(ncopy):
@@ -463,14 +466,19 @@ def compare_leg(args, L, W, torch, dev):
             for c in range(ncopy):
                 L.w4a8_linear(X, blobs16[c], d16, Y, Xq, sx, L.W4A8_OUT_BF16)
 
+        def w4a8_g32():
+            for c in range(ncopy):
+                L.w4a8_linear(X, blobs32[c], d32, Y, Xq, sx, L.W4A8_OUT_BF16)
+
         t4, t8, tb, t16 = per_call_us(w4a8), per_call_us(w8a8), per_call_us(bf16), per_call_us(w4a8_h16)
+        t32 = per_call_us(w4a8_g32)
         out["decode"][f"m{M}"] = dict(w4a8_linear_us=t4, w8a8_linear_us=t8, bf16_mm_us=tb,
-                                      w4a8_fp16_scales_linear_us=t16,
+                                      w4a8_fp16_scales_linear_us=t16, w4a8_g32_linear_us=t32,
                                       w4a8_vs_w8a8=t8 / t4, w4a8_vs_bf16=tb / t4,
                                       w8a8_weight_gbs=(K * N + K // cfg.group_size * N * 4) / (t8 * 1e-6) / 1e9,
                                       bf16_weight_gbs=K * N * 2 / (tb * 1e-6) / 1e9)
         del X, Xq, sx, Y
-    del blobs, blobs8, blobs16, Wb
+    del blobs, blobs8, blobs16, blobs32, Wb
     torch.cuda.empty_cache()
     for pc in (W.C3_UP, W.C3_DOWN):
         X = W.random_activations(pc.seed + 7919, pc.M, pc.K).to(dev)

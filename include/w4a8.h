@@ -57,9 +57,9 @@ typedef enum { W4A8_OUT_BF16 = 0, W4A8_OUT_F32 = 1 } w4a8_out_dtype;
  *   group_size  g: consecutive k sharing one scale per column (P5 section 8.4);
  *               must divide K.  pack accepts g in {32, 64, 128, 256} and g = K (one
  *               scale, and zero point, per output column: the per-channel granularity
- *               of P5 section 8.3).  Kernels implement g in {64, 128, 256} and g = K;
- *               256 and K run on the dense GEMMs only (the MoE entry points return
- *               EUNSUPPORTED), and g = K needs g * 127 * 15 < 2^31 (4-bit codes) or
+ *               of P5 section 8.3).  Kernels implement all of them; 32, 256 and K run on
+ *               the dense GEMMs only (the MoE entry points return EUNSUPPORTED), and
+ *               g = K needs g * 127 * 15 < 2^31 (4-bit codes) or
  *               g * 127 * 127 < 2^31 (8-bit codes), the reach of the int32 group sum;
  *               otherwise EUNSUPPORTED.  The GPU entry points also return
  *               EUNSUPPORTED for a blob whose codes reach 2 GiB (32-bit offsets).

@@ -487,11 +487,12 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     using S = DecodeShape<MS, NT, KW, SBN>;
     static_assert(!FQ || (MS == 1 && !MOE && MODE == MODE_OUT && !MULTI), "fused quantization: dense, one chunk");
     static_assert(!W8 || (!ASYM && !MOE), "8-bit codes: symmetric, dense");
-    // GPS: groups per superblock, 2 (g = 64) or 1 (g = 128); 0 is g = 256, one group per two
+    // GPS: groups per superblock, 4 (g = 32), 2 (g = 64) or 1 (g = 128); 0 is g = 256, one group per two
     // superblocks (a wave's superblocks come in aligned pairs, so a group never straddles waves)
     // GPS -1: per-channel scales (g = K): each wave converts its slice's int32 sum once, and
     // the slices add in the fixed float32 reduction below
     static_assert(GPS > 0 || !MOE, "g = 256 and per-channel: dense");
+    static_assert(GPS != 4 || !MOE, "g = 32: dense");
     static_assert(GPS >= 0 || MODE == MODE_OUT, "per-channel partials: the prefill kernel only");
     constexpr int NG = GPS <= 0 ? 1 : GPS;              // scale entries per superblock
     auto gidx = [](int sb, int gi) { return GPS < 0 ? 0 : GPS == 0 ? sb / 2 : sb * GPS + gi; };
@@ -704,7 +705,8 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
             if (sb >= s_end) break;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int gi = (GPS == 2) ? h : 0;
+                // GPS 4 (g = 32): the half's 64 k hold groups 2h (lanes 0-31) and 2h + 1
+                // (lanes 32-63); each group runs its own MFMA with the other lanes' B zeroed
                 v4i b;
                 if constexpr (W8) {
                     const uint4 u = h ? bq2[s] : bq[s];
@@ -712,22 +714,34 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                 } else {
                     const uint32_t w0 = h ? bq[s].z : bq[s].x;
                     const uint32_t w1 = h ? bq[s].w : bq[s].y;
-                    const uint32_t zc = ASYM ? (128u - zq[s][gi]) * 0x01010101u : 0u;
+                    const uint32_t zl = GPS == 4 ? ((lane >> 5) ? zq[s][NG > 1 ? 2 * h + 1 : 0] : zq[s][NG > 1 ? 2 * h : 0])
+                                                 : zq[s][GPS == 2 ? h : 0];
+                    const uint32_t zc = ASYM ? (128u - zl) * 0x01010101u : 0u;
                     b = unpack_b<ASYM>(w0, w1, zc);
                 }
-                const bool first = GPS < 0    ? (h == 0 && s == 0)
-                                   : GPS == 0 ? (h == 0 && s % 2 == 0)
-                                              : ((GPS == 2) || h == 0);
+                v4i A[MS];
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms) {
                     const uint4 av = *reinterpret_cast<const uint4*>(
                         smem + (ms * 16 + (lane & 15)) * ROWB + (sb - cb) * SB_K + h * 64 + 16 * (lane >> 4));
-                    const v4i A = {int(av.x), int(av.y), int(av.z), int(av.w)};
-                    acc[ms] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, b, first ? zero4 : acc[ms], 0, 0, 0);
+                    A[ms] = v4i{int(av.x), int(av.y), int(av.z), int(av.w)};
                 }
+#pragma unroll
+              for (int u = 0; u < (GPS == 4 ? 2 : 1); ++u) {
+                const int gi = GPS == 4 ? 2 * h + u : (GPS == 2) ? h : 0;
+                v4i bu = b;
+                if constexpr (GPS == 4) {
+                    if ((lane >> 5) != u) bu = zero4;
+                }
+                const bool first = GPS < 0    ? (h == 0 && s == 0)
+                                   : GPS == 0 ? (h == 0 && s % 2 == 0)
+                                              : ((GPS >= 2) || h == 0);
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+                    acc[ms] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[ms], bu, first ? zero4 : acc[ms], 0, 0, 0);
                 if (GPS < 0    ? (h == 1 && sb == s_end - 1)
                     : GPS == 0 ? (h == 1 && s % 2 == 1)
-                               : (GPS == 2 || h == 1)) {
+                               : (GPS >= 2 || h == 1)) {
                     if (MODE == MODE_PARTIALS) {
                         const int col = tile * 16 + (lane & 15);
 #pragma unroll
@@ -748,6 +762,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
                             for (int i = 0; i < 4; ++i) accf[ms][i] = fmaf((float)acc[ms][i], scl, accf[ms][i]);
                     }
                 }
+              }
             }
         }
         if (cb + CS < nsb) lds_barrier();                // LDS is rewritten by the next chunk
@@ -1082,7 +1097,7 @@ constexpr int PF_BM = 256, PF_BN = 128, PF_THREADS = 512;
 constexpr int PF_AROW = SB_K + 16;                       // padded activation row (bytes)
 constexpr int PF_A_BYTES = PF_BM * PF_AROW;              // 36864
 constexpr int PF_B_BYTES = PF_BN * SB_K;                 // unpacked int8 weights: 16384
-constexpr int PF_S_BYTES = (PF_BN / 16) * 2 * 64;        // scales of up to 2 groups: 1024
+constexpr int PF_S_BYTES = (PF_BN / 16) * 4 * 64;        // scales of up to 4 groups: 2048
 constexpr int PF_STAGE = PF_A_BYTES + PF_B_BYTES + PF_S_BYTES;
 constexpr int PF_LDS = 2 * PF_STAGE;
 
@@ -1123,6 +1138,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     // GPS 0: g = 256, one group per superblock pair (even, odd), which the loop runs back to back
     // GPS -1: per-channel scales (g = K), one int32 sum over all of K and one epilogue
     static_assert(GPS > 0 || !MOE, "g = 256 and per-channel: dense");
+    static_assert(GPS != 4 || !MOE, "g = 32: dense");
     constexpr int NG = GPS <= 0 ? 1 : GPS;              // scale entries per superblock
     auto gidx = [](int sb, int gi) { return GPS < 0 ? 0 : GPS == 0 ? sb / 2 : sb * GPS + gi; };
     constexpr int SBB = W8 ? 2048 : 1024;                // code bytes per superblock
@@ -1235,7 +1251,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
         const int col = wave * 16 + st_c;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int gi = (GPS == 2) ? h : 0;
+            // g = 32: the staging thread's 16 k (q4) lie in group 2h + q4 / 2
+            const int gi = GPS == 4 ? 2 * h + (st_q4 >> 1) : (GPS == 2) ? h : 0;
             v4i u;
             if constexpr (W8) {
                 const uint4 v = h ? r.b2 : r.b;
@@ -1281,7 +1298,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
         const uint8_t* st = smem + stage * PF_STAGE;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int gi = (GPS == 2) ? (j >> 1) : 0;
+            const int gi = GPS == 4 ? j : (GPS == 2) ? (j >> 1) : 0;   // MFMA step j is k in [32j, 32j + 32)
             v4i A[2], B[2];
 #pragma unroll
             for (int ms = 0; ms < 2; ++ms) {
@@ -1292,7 +1309,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
             for (int ns = 0; ns < 2; ++ns) B[ns] = *reinterpret_cast<const v4i*>(st + b_off[ns] + j * 2 * PF_BN * 16);
             const bool first = GPS < 0    ? (j == 0 && sb == 0)
                              : GPS == 0 ? (j == 0 && sb % 2 == 0)
-                             : GPS == 2 ? ((j & 1) == 0) : (j == 0);
+                             : GPS == 4 ? true : GPS == 2 ? ((j & 1) == 0) : (j == 0);
 #pragma unroll
             for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
@@ -1300,7 +1317,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
                     acc[ms][ns] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ms], B[ns], first ? zero16 : acc[ms][ns], 0, 0, 0);
             const bool last = GPS < 0    ? (j == 3 && sb == nsb - 1)
                             : GPS == 0 ? (j == 3 && sb % 2 == 1)
-                            : GPS == 2 ? ((j & 1) == 1) : (j == 3);
+                            : GPS == 4 ? true : GPS == 2 ? ((j & 1) == 1) : (j == 3);
             if (last) {
                 if (MODE == MODE_PARTIALS) {
 #pragma unroll
@@ -1603,6 +1620,13 @@ static void launch_decode(const GemmArgs& a, const DecodeCfg& c, int gps, bool a
                           bool w8 = false) {
 #define W4A8_DEC(MS_, GPS_, ASYM_) launch_decode_shape<MS_, GPS_, ASYM_, MODE, MOE>(a, c, grid, s)
     if constexpr (!MOE) {
+        if (gps == 4) {                                   // g = 32 (dense form only)
+            if (w8) { if (c.ms == 1) launch_decode_shape<1, 4, false, MODE, false, true>(a, c, grid, s);
+                      else launch_decode_shape<2, 4, false, MODE, false, true>(a, c, grid, s); }
+            else if (c.ms == 1) { if (asym) W4A8_DEC(1, 4, true); else W4A8_DEC(1, 4, false); }
+            else { if (asym) W4A8_DEC(2, 4, true); else W4A8_DEC(2, 4, false); }
+            return;
+        }
         if (w8) {
             if (c.ms == 1) { if (gps == 1) launch_decode_shape<1, 1, false, MODE, false, true>(a, c, grid, s);
                              else if (gps == 2) launch_decode_shape<1, 2, false, MODE, false, true>(a, c, grid, s);
@@ -1771,6 +1795,12 @@ template <int MODE, bool MOE = false>
 static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s, int mtiles = 0, bool w8 = false) {
     if (!MOE) mtiles = (a.M + PF_BM - 1) / PF_BM;
     if constexpr (!MOE) {
+        if (gps == 4) {                                   // g = 32
+            if (w8) launch_prefill_t<false, 4, MODE, false, true>(a, mtiles, s);
+            else if (asym) launch_prefill_t<true, 4, MODE, false>(a, mtiles, s);
+            else launch_prefill_t<false, 4, MODE, false>(a, mtiles, s);
+            return;
+        }
         if (w8) {
             if (gps == 1) launch_prefill_t<false, 1, MODE, false, true>(a, mtiles, s);
             else if (gps == 2) launch_prefill_t<false, 2, MODE, false, true>(a, mtiles, s);
@@ -1817,21 +1847,22 @@ static dim3 decode_grid(const Layout& L, const DecodeCfg& c, int ytiles) {
     return dim3((ntiles + c.nt - 1) / c.nt, ytiles);
 }
 
-// g = 256 and per-channel scales (g = K) run on the dense kernels only; the grouped (MoE)
-// entry points reject them.  One group's sum stays in an int32 accumulator, so g * 127 *
+// g = 32, g = 256 and per-channel scales (g = K) run on the dense kernels only; the grouped
+// (MoE) entry points reject them.  One group's sum stays in an int32 accumulator, so g * 127 *
 // max|q - z| must stay below 2^31: this bounds K for per-channel scales (K < 1127304 with
 // 4-bit codes, K < 133144 with 8-bit codes).
 static bool kernel_format_ok(const w4a8_wdesc* d) {
     const int g = d->group_size;
-    if (g != 64 && g != 128 && g != 256 && g != d->K) return false;
+    if (g != 32 && g != 64 && g != 128 && g != 256 && g != d->K) return false;
     // binary16 scales: 4-bit codes with g in {64, 128}
     if (d->scale_bits == 16 && (d->weight_bits == 8 || (g != 64 && g != 128))) return false;
     const int64_t qr = d->weight_bits == 8 ? 127 : 15;
     return int64_t(g) * 127 * qr < (int64_t(1) << 31);
 }
 
-// Groups per 128-deep superblock as the kernels' GPS: 2 (g = 64), 1 (g = 128), 0 (g = 256:
-// one group per two superblocks), -1 (per-channel: g = K > 256, one group over all of K).
+// Groups per 128-deep superblock as the kernels' GPS: 4 (g = 32), 2 (g = 64), 1 (g = 128), 0
+// (g = 256: one group per two superblocks), -1 (per-channel: g = K > 256, one group over all
+// of K).
 static int gps_of(const w4a8_wdesc* d) {
     if (d->group_size == d->K && d->K > 256) return -1;
     return SB_K / d->group_size;
@@ -1839,7 +1870,7 @@ static int gps_of(const w4a8_wdesc* d) {
 
 // The grouped (MoE) kernels take 4-bit codes with g in {64, 128}.
 static bool grouped_format_ok(const w4a8_wdesc* d) {
-    return layout_of(d).bits == 4 && gps_of(d) > 0;
+    return layout_of(d).bits == 4 && (gps_of(d) == 1 || gps_of(d) == 2);
 }
 
 static int dense_mt(int M) { return M <= 16 ? 16 : 32; }
@@ -1992,7 +2023,8 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
         const dim3 grid = decode_grid(L, fc, 1);
         const int gps = gps_of(d);
         if (L.bits == 8) {
-            if (gps == 1) launch_decode_fused<1, false, true>(a, fc, grid, s);
+            if (gps == 4) launch_decode_fused<4, false, true>(a, fc, grid, s);
+            else if (gps == 1) launch_decode_fused<1, false, true>(a, fc, grid, s);
             else if (gps == 2) launch_decode_fused<2, false, true>(a, fc, grid, s);
             else if (gps == 0) launch_decode_fused<0, false, true>(a, fc, grid, s);
             else launch_decode_fused<-1, false, true>(a, fc, grid, s);
@@ -2000,6 +2032,8 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
             if (d->asymmetric) launch_decode_fused<0, true>(a, fc, grid, s); else launch_decode_fused<0, false>(a, fc, grid, s);
         } else if (gps < 0) {
             if (d->asymmetric) launch_decode_fused<-1, true>(a, fc, grid, s); else launch_decode_fused<-1, false>(a, fc, grid, s);
+        } else if (gps == 4) {
+            if (d->asymmetric) launch_decode_fused<4, true>(a, fc, grid, s); else launch_decode_fused<4, false>(a, fc, grid, s);
         } else if (gps == 1) {
             if (a.h16) { if (d->asymmetric) launch_decode_fused<1, true, false, true>(a, fc, grid, s); else launch_decode_fused<1, false, false, true>(a, fc, grid, s); }
             else if (d->asymmetric) launch_decode_fused<1, true>(a, fc, grid, s); else launch_decode_fused<1, false>(a, fc, grid, s);
@@ -2291,8 +2325,8 @@ int w4a8_moe_forward_static(const void* X, const int32_t* ids, const float* w, i
 const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
     if (check_gemm_desc(d) != W4A8_OK || M < 0) return "unsupported";
     // one name per (form, row tile, format): [w8][kind: decode m16, decode m32, prefill][asym][g]
-#define W4A8_NAMES(P, K, S) {P K S "_g64", P K S "_g128", P K S "_g256", P K S "_gK"}
-    static const char* const names[2][3][2][4] = {
+#define W4A8_NAMES(P, K, S) {P K S "_g64", P K S "_g128", P K S "_g256", P K S "_gK", P K S "_g32"}
+    static const char* const names[2][3][2][5] = {
         {{W4A8_NAMES("w4a8", "_decode_m16", "_sym"), W4A8_NAMES("w4a8", "_decode_m16", "_asym")},
          {W4A8_NAMES("w4a8", "_decode_m32", "_sym"), W4A8_NAMES("w4a8", "_decode_m32", "_asym")},
          {W4A8_NAMES("w4a8", "_prefill", "_sym"), W4A8_NAMES("w4a8", "_prefill", "_asym")}},
@@ -2310,7 +2344,7 @@ const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
          {"w4a8_prefill_asym_g64_h16", "w4a8_prefill_asym_g128_h16"}}};
     const int kind = M >= PREFILL_MIN_M ? 2 : (dense_mt(M) == 32 ? 1 : 0);
     const int gps = gps_of(d);
-    const int gi = gps == 2 ? 0 : gps == 1 ? 1 : gps == 0 ? 2 : 3;
+    const int gi = gps == 2 ? 0 : gps == 1 ? 1 : gps == 0 ? 2 : gps == 4 ? 4 : 3;
     if (layout_of(d).sbytes == 2) return names16[kind][d->asymmetric][gi];
     return names[layout_of(d).bits == 8][kind][d->asymmetric][gi];
 }

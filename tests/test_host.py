@@ -206,10 +206,24 @@ def test_g256_names_and_grouped_form_rejected_host():
     assert L.w4a8_kernel_name(d, 40) == "w4a8_prefill_asym_g256"
     assert L.w4a8_kernel_name(L.desc(1024, 64, 256, False, bits=8), 40) == "w8a8_prefill_sym_g256"
     assert L.w4a8_kernel_name(L.desc(1024, 64, 64, False), 8) == "w4a8_decode_m16_sym_g64"
-    assert L.w4a8_kernel_name(L.desc(1024, 64, 32, False), 8) == "unsupported"
+    assert L.w4a8_kernel_name(L.desc(1024, 64, 32, False), 8) == "w4a8_decode_m16_sym_g32"
     fake = 0x10000
     assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
                              None) == L.W4A8_EUNSUPPORTED
+
+
+def test_g32_names_and_grouped_form_rejected_host():
+    """g = 32 runs on the dense kernels only: names end in _g32, the grouped entry points
+    return EUNSUPPORTED before any HIP call."""
+    lib = L.lib()
+    fake = 0x10000
+    d = L.desc(4096, 64, 32, True)
+    assert L.w4a8_kernel_name(d, 1) == "w4a8_decode_m16_asym_g32"
+    assert L.w4a8_kernel_name(d, 32) == "w4a8_decode_m32_asym_g32"
+    assert L.w4a8_kernel_name(L.desc(4096, 64, 32, False, bits=8), 64) == "w8a8_prefill_sym_g32"
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
+                             None) == L.W4A8_EUNSUPPORTED
+    assert L.w4a8_kernel_name(L.desc(4096, 64, 32, True, scale_bits=16), 1) == "unsupported"
 
 
 def test_perchannel_names_and_limits_host():
@@ -335,9 +349,10 @@ def test_gpu_entry_points_validate_before_launch():
     assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(d), fake, 16, 0, None) == E   # ldy < N
     assert lib.w4a8_gemm(mis, fake, 4, fake, ctypes.byref(d), fake, 32, 0, None) == E
     assert lib.w4a8_gemm(fake, None, 4, fake, ctypes.byref(d), fake, 32, 0, None) == E
-    d32 = L.desc(256, 32, 32, False)         # packs, but no kernel implements g = 32
-    assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(d32), fake, 32, 0, None) == L.W4A8_EUNSUPPORTED
-    assert L.w4a8_kernel_name(d32, 4) == "unsupported"
+    dnk = L.desc(256, 32, 256, False, scale_bits=16)   # packs, but no kernel takes binary16 scales at g = 256
+    assert L.w4a8_packed_size(dnk) > 0
+    assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(dnk), fake, 32, 0, None) == L.W4A8_EUNSUPPORTED
+    assert L.w4a8_kernel_name(dnk, 4) == "unsupported"
     dbad = L.desc(250, 32, 125, False)
     assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(dbad), fake, 32, 0, None) == E
     assert lib.w4a8_gemm_partials(fake, 4, fake, ctypes.byref(d), None, None) == E
