@@ -350,12 +350,29 @@ def moe_leg(args, L, W, torch, dev, steps):
         dn, dstride16 = random_device_blobs(L, dd16, cfg.E, seed * 11, dev)
         ms_h16 = timed(lambda: L.w4a8_moe_forward(X, ids_d, w_d, cfg.E, gu, gstride16, gud16, dn, dstride16, dd16,
                                                   ws, o))
+        # two format classes: the first half of the experts as above (binary16 scales), the
+        # second half at the other grouped-kernel group size (64 <-> 128) with float32 scales
+        del gu, dn
+        torch.cuda.empty_cache()
+        h = cfg.E // 2
+        g2 = 64 if cfg.group_size == 128 else 128
+        cls = [(h, gud16, dd16), (cfg.E - h, L.desc(cfg.H, 2 * cfg.I, g2, cfg.asymmetric),
+                                  L.desc(cfg.I, cfg.H, g2, cfg.asymmetric))]
+        dev_sets = []
+        for i, (n, gdesc, ddesc) in enumerate(cls):
+            gb, gs_ = random_device_blobs(L, gdesc, n, seed * 13 + i, dev)
+            db, ds_ = random_device_blobs(L, ddesc, n, seed * 17 + i, dev)
+            dev_sets.append((L.DeviceWeights(gdesc, gb, gs_, n), L.DeviceWeights(ddesc, db, ds_, n)))
+        ms_sets = timed(lambda: L.w4a8_moe_forward_sets(X, ids_d, w_d, dev_sets, ws, o))
+        gu = dn = None
+        del dev_sets
         touched = len(set(ids.ravel().tolist()))
         wbytes = touched * (gstride + dstride)
         out[cfg.name] = dict(layer_ms=ms, tokens_per_s=cfg.T / (ms * 1e-3), experts_touched=touched,
                              weight_gbs=wbytes / (ms * 1e-3) / 1e9,
                              frac_hbm=wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             static_scales_layer_ms=ms_static, fp16_scales_layer_ms=ms_h16)
+                             static_scales_layer_ms=ms_static, fp16_scales_layer_ms=ms_h16,
+                             two_format_classes_layer_ms=ms_sets)
         del gu, dn, ws, ws_st
         torch.cuda.empty_cache()
     return out

@@ -320,6 +320,32 @@ int w4a8_moe_forward(const void* X_bf16, const int32_t* topk_ids, const float* t
                      const w4a8_wdesc* d_desc, void* workspace, size_t workspace_bytes,
                      void* out_bf16, void* stream);
 
+/* One format class of experts for w4a8_moe_forward_sets: n_experts consecutive experts
+ * whose gate/up blobs (desc gu_desc, stride gu_stride) and down blobs (d_desc, d_stride)
+ * share one format.  Experts are numbered set by set: set 0 holds experts [0, n_0), set 1
+ * [n_0, n_0 + n_1), and so on. */
+typedef struct {
+    int32_t n_experts;
+    const void* gu_blobs;
+    size_t gu_stride;
+    const w4a8_wdesc* gu_desc;
+    const void* d_blobs;
+    size_t d_stride;
+    const w4a8_wdesc* d_desc;
+} w4a8_expert_set;
+
+/* One MoE expert layer whose experts use different weight formats (P1 section 8: quantize at
+ * expert granularity, with a group size and format per expert, so that sensitive experts can
+ * be kept at a finer format).  The steps of w4a8_moe_forward; each grouped GEMM runs
+ * once per set, over that set's experts.  The group size, zero points and scale width may
+ * differ between sets; the shapes (gate/up [H, 2I], down [I, H]) may not (EINVAL).
+ *   sets, nsets  host array of the format classes; E = sum of n_experts <= 1024
+ *   workspace    device, >= w4a8_moe_workspace_size(T, k, H, I, E) bytes, 256-aligned
+ * Other arguments and errors as w4a8_moe_forward. */
+int w4a8_moe_forward_sets(const void* X_bf16, const int32_t* topk_ids, const float* topk_w, int T,
+                          int k, const w4a8_expert_set* sets, int nsets, void* workspace,
+                          size_t workspace_bytes, void* out_bf16, void* stream);
+
 /* Workspace bytes needed by w4a8_moe_forward_static (0 if invalid): the routed rows are
  * quantized one by one, so the activation codes take T*k rows instead of T. */
 size_t w4a8_moe_static_workspace_size(int T, int k, int H, int I, int E);

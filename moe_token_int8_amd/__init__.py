@@ -26,7 +26,7 @@ EXPORTED = [
     "w4a8_moe_gemm",
     "w4a8_silu_mul_quant", "w4a8_moe_combine", "w4a8_moe_workspace_size", "w4a8_moe_forward",
     "w4a8_quant_act_static", "w4a8_moe_quant_static", "w4a8_silu_mul_quant_static",
-    "w4a8_moe_static_workspace_size", "w4a8_moe_forward_static",
+    "w4a8_moe_static_workspace_size", "w4a8_moe_forward_static", "w4a8_moe_forward_sets",
     "w4a8_kernel_name", "w4a8_status_string", "w4a8_version",
 ]
 
@@ -44,6 +44,12 @@ class WDesc(ctypes.Structure):
     def __repr__(self):
         return (f"WDesc(K={self.K}, N={self.N}, group_size={self.group_size}, asymmetric={self.asymmetric}, "
                 f"weight_bits={self.weight_bits}, scale_bits={self.scale_bits})")
+
+
+class ExpertSet(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("gu_blobs", ctypes.c_void_p), ("gu_stride", ctypes.c_size_t),
+                ("gu_desc", ctypes.POINTER(WDesc)), ("d_blobs", ctypes.c_void_p), ("d_stride", ctypes.c_size_t),
+                ("d_desc", ctypes.POINTER(WDesc))]
 
 
 _lib = None
@@ -80,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "w4a8_silu_mul_quant_static": (I, [P, I, I, P, I, P, P, P, VP]),
             "w4a8_moe_static_workspace_size": (SZ, [I, I, I, I, I]),
             "w4a8_moe_forward_static": (I, [P, P, P, I, I, I, P, SZ, DP, P, SZ, DP, P, P, P, SZ, P, VP]),
+            "w4a8_moe_forward_sets": (I, [P, P, P, I, I, ctypes.POINTER(ExpertSet), I, P, SZ, P, VP]),
             "w4a8_kernel_name": (ctypes.c_char_p, [DP, I]),
             "w4a8_status_string": (ctypes.c_char_p, [I]),
             "w4a8_version": (I, []),
@@ -310,6 +317,26 @@ def w4a8_moe_forward_static(X, topk_ids, topk_w, E: int, gu_blobs, gu_stride: in
                                          ctypes.byref(d_desc), _ptr(s_gu), _ptr(s_dn), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)),
            "w4a8_moe_forward_static")
+
+
+def w4a8_moe_forward_sets(X, topk_ids, topk_w, sets, workspace, out, stream=None) -> None:
+    """One MoE layer whose experts come in format classes: `sets` is a list of
+    (DeviceWeights gate/up, DeviceWeights down) pairs, experts numbered set by set."""
+    _require_cuda(X, topk_ids, topk_w, workspace, out)
+    T, k = topk_ids.shape
+    arr = (ExpertSet * len(sets))()
+    keep = []
+    for i, (gu, dn) in enumerate(sets):
+        if gu.experts != dn.experts:
+            raise ValueError("gate/up and down sets must hold the same experts")
+        gd, dd = WDesc(*[getattr(gu.desc, f) for f, _ in WDesc._fields_]), \
+            WDesc(*[getattr(dn.desc, f) for f, _ in WDesc._fields_])
+        keep += [gd, dd]
+        arr[i] = ExpertSet(gu.experts, _ptr(gu.blob), gu.stride, ctypes.pointer(gd), _ptr(dn.blob), dn.stride,
+                           ctypes.pointer(dd))
+    _check(lib().w4a8_moe_forward_sets(_ptr(X), _ptr(topk_ids), _ptr(topk_w), T, k, arr, len(sets), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)),
+           "w4a8_moe_forward_sets")
 
 
 # ------------------------------------------------------------------------------ helpers

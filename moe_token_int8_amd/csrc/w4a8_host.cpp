@@ -176,6 +176,7 @@ static float round_f16(float f) {
 static uint16_t f16_bits(float h) {
     const uint16_t sign = std::signbit(h) ? 0x8000u : 0u;
     const double v = std::fabs(double(h));
+    if (std::isnan(v)) return sign | 0x7e00u;
     if (std::isinf(v)) return sign | 0x7c00u;
     if (v < std::ldexp(1.0, -14)) return uint16_t(sign | uint16_t(std::ldexp(v, 24)));   // subnormal or 0
     int e;

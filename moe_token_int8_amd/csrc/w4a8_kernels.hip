@@ -2276,6 +2276,62 @@ int w4a8_moe_forward(const void* X, const int32_t* ids, const float* w, int T, i
     return w4a8_moe_combine(yd, inv, w, T, k, H, out, stream);
 }
 
+int w4a8_moe_forward_sets(const void* X, const int32_t* ids, const float* w, int T, int k, const w4a8_expert_set* sets,
+                          int nsets, void* ws, size_t ws_bytes, void* out, void* stream) {
+    if (!sets || nsets <= 0 || T < 0 || k <= 0) return W4A8_EINVAL;
+    int E = 0;
+    for (int i = 0; i < nsets; ++i) {
+        const w4a8_expert_set& st = sets[i];
+        if (st.n_experts <= 0 || !st.gu_desc || !st.d_desc) return W4A8_EINVAL;
+        int c = check_gemm_desc(st.gu_desc);
+        if (c) return c;
+        if ((c = check_gemm_desc(st.d_desc))) return c;
+        if (!grouped_format_ok(st.gu_desc) || !grouped_format_ok(st.d_desc)) return W4A8_EUNSUPPORTED;
+        // every set has the layer's shapes: gate/up [H, 2I], down [I, H]
+        if (st.gu_desc->K != sets[0].gu_desc->K || st.gu_desc->N != sets[0].gu_desc->N ||
+            st.d_desc->K != sets[0].d_desc->K || st.d_desc->N != sets[0].d_desc->N)
+            return W4A8_EINVAL;
+        E += st.n_experts;
+    }
+    const int H = sets[0].gu_desc->K, I2 = sets[0].gu_desc->N;
+    if (I2 % 2 || sets[0].d_desc->K != I2 / 2 || sets[0].d_desc->N != H) return W4A8_EINVAL;
+    const int I = I2 / 2;
+    if (E > 1024) return W4A8_EINVAL;
+    if (T == 0) return W4A8_OK;
+    if (!X || !ids || !w || !ws || !out) return W4A8_EINVAL;
+    for (int i = 0; i < nsets; ++i)
+        if (!sets[i].gu_blobs || !sets[i].d_blobs) return W4A8_EINVAL;
+    const MoeWs L = moe_ws(T, k, H, I, E);
+    if (ws_bytes < L.total) return W4A8_ESIZE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return W4A8_EINVAL;
+    uint8_t* b = static_cast<uint8_t*>(ws);
+    int8_t* xq = reinterpret_cast<int8_t*>(b + L.xq);
+    float* sx = reinterpret_cast<float*>(b + L.sx);
+    int32_t* rows = reinterpret_cast<int32_t*>(b + L.rows);
+    int32_t* offs = reinterpret_cast<int32_t*>(b + L.offs);
+    int32_t* inv = reinterpret_cast<int32_t*>(b + L.inv);
+    void* gu = b + L.gu;
+    int8_t* hq = reinterpret_cast<int8_t*>(b + L.hq);
+    float* sh = reinterpret_cast<float*>(b + L.sh);
+    void* yd = b + L.yd;
+    const int R = T * k;
+    int st;
+    if ((st = w4a8_quant_act(X, T, H, H, xq, sx, stream))) return st;
+    if ((st = w4a8_moe_align(ids, T, k, E, rows, offs, inv, stream))) return st;
+    // each set is one grouped launch over its expert range: offs + e0 holds the absolute row
+    // ranges of those experts, so the sets write disjoint output rows
+    for (int i = 0, e0 = 0; i < nsets; e0 += sets[i].n_experts, ++i)
+        if ((st = w4a8_moe_gemm(xq, sx, rows, k, offs + e0, sets[i].n_experts, R, sets[i].gu_blobs,
+                                sets[i].gu_stride, sets[i].gu_desc, gu, W4A8_OUT_BF16, stream)))
+            return st;
+    if ((st = w4a8_silu_mul_quant(gu, R, I, hq, sh, stream))) return st;
+    for (int i = 0, e0 = 0; i < nsets; e0 += sets[i].n_experts, ++i)
+        if ((st = w4a8_moe_gemm(hq, sh, nullptr, k, offs + e0, sets[i].n_experts, R, sets[i].d_blobs,
+                                sets[i].d_stride, sets[i].d_desc, yd, W4A8_OUT_BF16, stream)))
+            return st;
+    return w4a8_moe_combine(yd, inv, w, T, k, H, out, stream);
+}
+
 size_t w4a8_moe_static_workspace_size(int T, int k, int H, int I, int E) {
     if (T < 0 || k <= 0 || H <= 0 || I <= 0 || E <= 0) return 0;
     return moe_ws(T, k, H, I, E, true).total;

@@ -50,6 +50,10 @@ Pins (each function is checked against something other than itself in
                     quotients on a power-of-two scale (ties to even, saturation, NaN,
                     infinities); the calibrated scale of a batch is the largest per-token
                     scale of its rows.
+  moe_layer (per-expert group sizes)
+                    one routed row per expert with each expert at its own group size:
+                    every output row equals the dense chain of quant_act, gemm, silu_mul_quant
+                    and gemm at that expert's group size.
   moe_layer (static scales)
                     one routed row per expert, through a non-trivial expert permutation,
                     with each expert's scales set to its row's dynamic scales: identical to
@@ -375,7 +379,8 @@ def moe_layer(x, topk_ids, topk_w, expert, E: int, I: int, group_size: int, s_gu
        float64 over j ascending, then rounded to bf16.
 
     `expert(e)` returns (codes_gu [H, 2I], scales_gu, zeros_gu, codes_d [I, H], scales_d,
-    zeros_d) for expert e; it is called only for experts that received rows.
+    zeros_d) for expert e; it is called only for experts that received rows.  `group_size` is
+    one group size, or a sequence of E, one per expert (P1 section 8: expert-granular formats).
 
     Static per-expert activation scales (P1 section 3.1: each expert keeps its own activation
     scale; section 3.2: calibrated static scales for decode): with s_gu [E] given, step 1
@@ -389,6 +394,7 @@ def moe_layer(x, topk_ids, topk_w, expert, E: int, I: int, group_size: int, s_gu
     w = np.asarray(topk_w, np.float64)
     T, k = ids.shape
     H = x.shape[1]
+    g_of = (lambda e: int(group_size)) if np.ndim(group_size) == 0 else (lambda e: int(group_size[e]))
     xq, sx = quant_act(x) if s_gu is None else (None, None)
     sorted_rows, offsets, inv = moe_align(ids, E)
     R = T * k
@@ -403,7 +409,7 @@ def moe_layer(x, topk_ids, topk_w, expert, E: int, I: int, group_size: int, s_gu
         cg, sg, zg = weights[e][:3]
         toks = sorted_rows[a:b] // k
         qa, sa = (xq[toks], sx[toks]) if s_gu is None else quant_act_static(x[toks], s_gu[e])
-        gu[a:b] = bf16_rne(gemm(qa, sa, cg, sg, zg, group_size))
+        gu[a:b] = bf16_rne(gemm(qa, sa, cg, sg, zg, g_of(e)))
     if s_dn is None:
         hq, sh = silu_mul_quant(gu)
     else:
@@ -414,7 +420,7 @@ def moe_layer(x, topk_ids, topk_w, expert, E: int, I: int, group_size: int, s_gu
     for e, wts in weights.items():
         a, b = int(offsets[e]), int(offsets[e + 1])
         cd, sd, zd = wts[3:]
-        yd[a:b] = bf16_rne(gemm(hq[a:b], sh[a:b], cd, sd, zd, group_size))
+        yd[a:b] = bf16_rne(gemm(hq[a:b], sh[a:b], cd, sd, zd, g_of(e)))
     out64 = np.zeros((T, H), dtype=np.float64)
     for j in range(k):
         out64 += w[:, j:j + 1] * yd[inv[:, j]].astype(np.float64)

@@ -123,7 +123,7 @@ def check_moe(out, ref, qw, group_size, flips_per_row=2):
     colmax = {}
     for e, wts in qw.items():
         cd, sd, zd = wts[3:]
-        deq = O.dequant_weight(cd, sd, zd, group_size)
+        deq = O.dequant_weight(cd, sd, zd, group_size if np.ndim(group_size) == 0 else group_size[e])
         colmax[e] = np.max(np.abs(deq), axis=0)
     ids = np.empty(T * k, np.int64)
     for e in range(len(offs) - 1):

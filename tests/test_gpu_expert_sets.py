@@ -1,0 +1,96 @@
+"""GPU parity of a MoE layer whose experts come in format classes (P1 section 8: a group size
+and format per expert), through w4a8_moe_forward_sets: each class is one grouped launch over
+its expert range, against the oracle layer with per-expert group sizes."""
+import numpy as np
+import pytest
+import torch
+
+import moe_token_int8_amd as L
+import oracle as O
+import workloads as W
+from gpu_cases import DEV, check_moe
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.lib()
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _sets(cfg, touched, classes, seed, rtn):
+    """classes: list of (n_experts, group_size, asymmetric, scale_bits).  Returns the device
+    sets, the oracle's per-expert weights and group sizes."""
+    sets, qw, gs = [], {}, []
+    e0 = 0
+    for n, g, asym, sbits in classes:
+        dgu = L.desc(cfg.H, 2 * cfg.I, g, asym, scale_bits=sbits)
+        dd = L.desc(cfg.I, cfg.H, g, asym, scale_bits=sbits)
+        host_gu, host_d = {}, {}
+        for e in range(e0, e0 + n):
+            gs.append(g)
+            if e not in touched:
+                continue
+            if rtn:
+                Wgu, Wd = W.expert_weights(cfg, e)
+                host_gu[e - e0], host_d[e - e0] = L.w4a8_pack(dgu, Wgu), L.w4a8_pack(dd, Wd)
+                qw[e] = O.quant_weight(Wgu, g, asym, scale_bits=sbits) + O.quant_weight(Wd, g, asym, scale_bits=sbits)
+            else:
+                cg = W.random_codes(seed * 1009 + e, cfg.H, 2 * cfg.I, g, asym)
+                cd = W.random_codes(seed * 2003 + e, cfg.I, cfg.H, g, asym)
+                host_gu[e - e0], host_d[e - e0] = L.w4a8_pack_codes(dgu, *cg), L.w4a8_pack_codes(dd, *cd)
+                r = (lambda c: (c[0], c[1].astype(np.float16).astype(np.float32), c[2])) if sbits == 16 else (lambda c: c)
+                qw[e] = r(cg) + r(cd)
+        sets.append((L.experts_to_device(dgu, n, host_gu), L.experts_to_device(dd, n, host_d)))
+        e0 += n
+    return sets, qw, gs
+
+
+def _run(cfg, Xb, ids, w, sets):
+    T, k = ids.shape
+    ws = torch.empty(L.w4a8_moe_workspace_size(T, k, cfg.H, cfg.I, cfg.E), dtype=torch.uint8, device=DEV)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_moe_forward_sets(Xb.to(DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), sets, ws, out)
+    return out
+
+
+@pytest.mark.parametrize("name", ["small_rtn", "c4_two_classes", "c5_4tok_two_classes"])
+def test_moe_forward_expert_sets(name):
+    if name == "small_rtn":
+        cfg, T, rtn = W.MoEConfig("small", 40, 512, 256, 8, 2, 64, True, 51), None, True
+        classes = [(4, 64, True, 32), (2, 128, False, 16), (2, 128, True, 32)]
+    elif name == "c4_two_classes":                     # hot experts take the prefill tiles
+        cfg, T, rtn = W.C4, None, False
+        classes = [(32, 128, False, 32), (32, 64, True, 16)]
+    else:
+        cfg, T, rtn = W.C5, 4, False
+        classes = [(128, 64, True, 32), (128, 128, True, 16)]
+    _print(f"expert sets {name}: {classes}")
+    ids, w = W.moe_routing(cfg, T=T) if T else W.moe_routing(cfg)
+    Xb = W.moe_activations(cfg, T=T) if T else W.moe_activations(cfg)
+    sets, qw, gs = _sets(cfg, set(ids.ravel().tolist()), classes, 9, rtn)
+    out = _run(cfg, Xb, ids, w, sets)
+    ref = O.moe_layer(W.bf16_values(Xb), ids, w, lambda e: qw[e], cfg.E, cfg.I, gs)
+    check_moe(out, ref, qw, gs)
+
+
+def test_one_set_equals_moe_forward():
+    """A single class is the plain layer: bit-identical to w4a8_moe_forward."""
+    cfg = W.MoEConfig("one", 33, 256, 128, 16, 4, 128, True, 52)
+    ids, w = W.moe_routing(cfg)
+    Xb = W.moe_activations(cfg)
+    sets, _, _ = _sets(cfg, set(ids.ravel().tolist()), [(16, 128, True, 32)], 3, True)
+    out = _run(cfg, Xb, ids, w, sets)
+    T, k = ids.shape
+    ws = torch.empty(L.w4a8_moe_workspace_size(T, k, cfg.H, cfg.I, cfg.E), dtype=torch.uint8, device=DEV)
+    ref = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    gu, dn = sets[0]
+    L.w4a8_moe_forward(Xb.to(DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), cfg.E,
+                       gu.blob, gu.stride, gu.desc, dn.blob, dn.stride, dn.desc, ws, ref)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

@@ -226,6 +226,25 @@ def test_g32_names_and_grouped_form_rejected_host():
     assert L.w4a8_kernel_name(L.desc(4096, 64, 32, True, scale_bits=16), 1) == "unsupported"
 
 
+def test_expert_sets_validation_host():
+    """w4a8_moe_forward_sets checks every set before any HIP call: shapes must agree, formats
+    must be grouped-kernel formats, and there must be at least one set."""
+    lib = L.lib()
+    fake = 0x10000
+    a_gu, a_d = L.desc(256, 256, 64, True), L.desc(128, 256, 64, True)
+    b_gu, b_d = L.desc(256, 256, 128, False, scale_bits=16), L.desc(128, 256, 128, False, scale_bits=16)
+    mk = lambda n, g, d: L.ExpertSet(n, fake, 1 << 20, ctypes.pointer(g), fake, 1 << 20, ctypes.pointer(d))
+    sets = (L.ExpertSet * 2)(mk(4, a_gu, a_d), mk(4, b_gu, b_d))
+    call = lambda arr, n: lib.w4a8_moe_forward_sets(fake, fake, fake, 8, 2, arr, n, fake, 1 << 30, fake, None)
+    assert call(sets, 0) == L.W4A8_EINVAL
+    bad_shape = L.desc(256, 512, 64, True)
+    assert call((L.ExpertSet * 2)(mk(4, a_gu, a_d), mk(4, bad_shape, b_d)), 2) == L.W4A8_EINVAL
+    g256 = L.desc(256, 256, 256, True)
+    assert call((L.ExpertSet * 2)(mk(4, a_gu, a_d), mk(4, g256, b_d)), 2) == L.W4A8_EUNSUPPORTED
+    assert call((L.ExpertSet * 2)(mk(4, a_gu, a_d), mk(0, b_gu, b_d)), 2) == L.W4A8_EINVAL
+    assert lib.w4a8_moe_forward_sets(fake, fake, fake, 0, 2, sets, 2, fake, 1 << 30, fake, None) == L.W4A8_OK
+
+
 def test_perchannel_names_and_limits_host():
     """g = K is the per-channel form: dense kernels only; the decode kernels' partial-sum export
     and the grouped entry points return EUNSUPPORTED before any HIP call."""

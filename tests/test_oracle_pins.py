@@ -554,3 +554,26 @@ def test_weight_fp16_scales_identity_and_range():
     assert np.array_equal(c32, c16) and np.array_equal(s32, s16)
     with pytest.raises(ValueError):
         O.quant_weight(np.full((64, 1), 7.0 * 70000.0, F32), 64, False, scale_bits=16)
+
+
+def test_moe_per_expert_group_size_is_the_dense_chain_per_expert():
+    """One routed row per expert (weight 1), experts at group sizes 32, 64 and 128: each output
+    row is the dense chain quant_act -> gemm -> bf16 -> silu_mul_quant -> gemm -> bf16 at its
+    own expert's group size."""
+    T, E, H, I = 3, 3, 128, 128
+    gs = [64, 128, 32]
+    ids = np.array([[2], [0], [1]], np.int32)
+    w = np.ones((T, 1), F32)
+    rs = np.random.default_rng(12)
+    x = W.bf16_values(W.to_bf16((rs.standard_normal((T, H)) * 3).astype(F32)))
+    qw = {e: O.quant_weight(W.random_weights(70 + e, H, 2 * I, 0.2), gs[e], e == 0) +
+          O.quant_weight(W.random_weights(80 + e, I, H, 0.2), gs[e], e == 0) for e in range(E)}
+    out = O.moe_layer(x, ids, w, lambda e: qw[e], E, I, gs)
+    for t in range(T):
+        e = int(ids[t, 0])
+        cg, sg, zg, cd, sd, zd = qw[e]
+        q, s = O.quant_act(x[t:t + 1])
+        gu = O.bf16_rne(O.gemm(q, s, cg, sg, zg, gs[e]))
+        hq, sh = O.silu_mul_quant(gu)
+        y = O.bf16_rne(O.gemm(hq, sh, cd, sd, zd, gs[e]))
+        assert np.array_equal(out["out"][t], O.bf16_rne(y[0].astype(np.float64)))
