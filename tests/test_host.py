@@ -434,3 +434,42 @@ def test_kernel_names_resolve():
     for M, g, asym in [(1, 128, False), (32, 128, False), (8, 64, True), (4096, 128, True)]:
         name = L.w4a8_kernel_name(L.desc(4096, 14336, g, asym), M)
         assert name.startswith("w4a8_") and ("asym" in name) == asym and f"g{g}" in name
+
+
+def test_static_entry_points_validate_before_launch():
+    """Static-scale entry points return their errors before any HIP call."""
+    lib = L.lib()
+    fake, mis = 0x10000, 0x10004
+    E, U = L.W4A8_EINVAL, L.W4A8_EUNSUPPORTED
+    assert lib.w4a8_quant_act_static(fake, 0, 256, 256, fake, fake, fake, None) == L.W4A8_OK
+    assert lib.w4a8_quant_act_static(fake, 4, 256, 256, None, fake, fake, None) == E     # no scale
+    assert lib.w4a8_quant_act_static(mis, 4, 256, 256, fake, fake, fake, None) == E      # misaligned X
+    assert lib.w4a8_quant_act_static(fake, 4, 250, 256, fake, fake, fake, None) == E     # K % 16
+    assert lib.w4a8_quant_act_static(fake, 4, 256, 128, fake, fake, fake, None) == E     # ldx < K
+    assert lib.w4a8_moe_quant_static(fake, 4, 256, 256, None, 2, fake, 8, fake, fake, fake, None) == E
+    assert lib.w4a8_moe_quant_static(fake, 4, 256, 256, fake, 2, fake, 2000, fake, fake, fake, None) == E
+    assert lib.w4a8_moe_quant_static(fake, 1 << 23, 256, 256, fake, 4, fake, 8, fake, fake, fake, None) == U
+    assert lib.w4a8_silu_mul_quant_static(fake, 8, 128, None, 4, fake, fake, fake, None) == E
+    assert lib.w4a8_silu_mul_quant_static(fake, 8, 128, fake, 0, fake, fake, fake, None) == E
+    gu, dn = L.desc(256, 256, 64, True), L.desc(128, 256, 64, True)
+    need = L.w4a8_moe_static_workspace_size(8, 2, 256, 128, 4)
+    assert need > L.w4a8_moe_workspace_size(8, 2, 256, 128, 4)       # codes of T*k routed rows
+    args = lambda sg, sd, nbytes: (fake, fake, fake, 8, 2, 4, fake, 1 << 20, ctypes.byref(gu), fake, 1 << 20,
+                                   ctypes.byref(dn), sg, sd, fake, nbytes, fake, None)
+    assert lib.w4a8_moe_forward_static(*args(None, fake, need)) == E
+    assert lib.w4a8_moe_forward_static(*args(fake, None, need)) == E
+    assert lib.w4a8_moe_forward_static(*args(fake, fake, need - 256)) == L.W4A8_ESIZE
+
+
+def test_fp16_pack_codes_nan_and_range():
+    """pack_codes with binary16 scales: a NaN scale is stored as a NaN and read back as one; a
+    finite scale past the binary16 range is rejected."""
+    d = L.desc(128, 16, 64, False, scale_bits=16)
+    codes = np.zeros((128, 16), np.int8)
+    sc = np.full((2, 16), 0.5, np.float32)
+    sc[1, 3] = np.nan
+    _, _, s2, _ = L.w4a8_unpack_codes(L.w4a8_pack_codes(d, codes, sc, None))
+    assert np.isnan(s2[1, 3]) and np.all(s2[~np.isnan(s2)] == 0.5)
+    sc[1, 3] = 70000.0
+    with pytest.raises(L.W4A8Error):
+        L.w4a8_pack_codes(d, codes, sc, None)
