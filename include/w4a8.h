@@ -59,9 +59,10 @@ typedef enum { W4A8_OUT_BF16 = 0, W4A8_OUT_F32 = 1 } w4a8_out_dtype;
  *               scale, and zero point, per output column: the per-channel granularity
  *               of P5 section 8.3).  Kernels implement all of them; 32, 256 and K run on
  *               the dense GEMMs only (the MoE entry points return EUNSUPPORTED), and
- *               g = K needs g * 127 * 15 < 2^31 (4-bit codes) or
- *               g * 127 * 127 < 2^31 (8-bit codes), the reach of the int32 group sum;
- *               otherwise EUNSUPPORTED.  The GPU entry points also return
+ *               g = K needs g * 127 * m < 2^31, the reach of the int32 group sum, where
+ *               m is the largest weight operand the kernels feed: 15 (asymmetric), 112
+ *               (symmetric 4-bit codes enter as 16 q) or 127 (8-bit codes); so K <= 150912
+ *               for symmetric 4-bit per-channel weights; otherwise EUNSUPPORTED.  The GPU entry points also return
  *               EUNSUPPORTED for a blob whose codes reach 2 GiB (32-bit offsets).
  *   asymmetric  0: signed codes q in [-7, 7], zero point 0 (P3 "Basic mapping",
  *                  symmetric form);
@@ -243,7 +244,8 @@ int w4a8_linear(const void* X_bf16, int M, int K, int ldx, const void* blob_dev,
 /* Test export of the same main loop: INT32 per-group partial sums
  * P[m, n, i] = sum_{k in group i} Xq[m, k] (q[k, n] - z[i, n]) written to device
  * int32 [M, N, K/g].  (P3 "Correctness contract" item 3: the accumulator covers the
- * reduction: |P| <= g * 127 * 15, or g * 127 * 127 with 8-bit codes, < 2^31.)  Same
+ * reduction: |P| <= g * 127 * 15, or g * 127 * 127 with 8-bit codes, < 2^31; symmetric
+ * 4-bit sums are formed as 16 P, |16 P| <= g * 127 * 112 < 2^31.)  Same
  * EINVAL size limit as w4a8_gemm.  With g = K and M <= 32 (the decode kernels, which split
  * K across waves) it returns EUNSUPPORTED. */
 int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob_dev, const w4a8_wdesc* d,
@@ -261,20 +263,25 @@ int w4a8_moe_align(const int32_t* topk_ids, int T, int k, int E, int32_t* sorted
                    int32_t* expert_offsets, int32_t* inv, void* stream);
 
 /* Expert-grouped W4A8 GEMM (P1 section 4.4 step 4, "the performance key").
- *   Xq, sx         device activations; if `gather` is non-NULL, output row r (in sorted
- *                  order) reads Xq/sx row gather[r] / k (token of the routed row);
- *                  if NULL, row r reads row r (rows already permuted)
+ *   Xq, sx         device activations [src_rows, K] and [src_rows]; if `gather` is non-NULL,
+ *                  output row r (in sorted order) reads Xq/sx row gather[r] / k (token of
+ *                  the routed row); if NULL, row r reads row r (rows already permuted)
  *   gather         device int32 [rows] or NULL (pass sorted_rows from w4a8_moe_align)
  *   k              top-k (divisor for gather; ignored when gather is NULL)
  *   expert_offsets device int32 [E+1]; rows [off[e], off[e+1]) use expert e
- *   rows           T*k, total rows (= off[E])
+ *   rows           T*k, total rows (= off[E]); rows of Y
+ *   src_rows       rows of Xq and sx: T with a gather, >= rows without one (EINVAL otherwise)
  *   blobs_dev      device, E blobs of desc `d`, expert e at blobs_dev + e * expert_stride
  *   Y              device [rows, N] bfloat16 or float32, dense
- * Experts with no rows read no weights.  EINVAL when rows >= 128 and the activation rows a
- * gather may name (ceil(rows / k) with gather, else rows) times K reach 2^31 (32-bit
- * offsets of the kernel for experts with many rows). */
+ * The kernels bound what the device arrays may name: a gather entry that is negative or
+ * names a token at or past src_rows reads no activations and gives an output row of zeros,
+ * and expert row ranges are clamped to [0, rows).  Experts with no rows read no weights.
+ * All experts of a call share one allocation at a fixed stride: the kernels find an expert's
+ * weights by one multiply of ids they already hold, with no further dependent load in front of
+ * the weight stream.  EINVAL when rows >= 128 and src_rows * K reaches 2^31 (32-bit offsets of
+ * the kernel for experts with many rows). */
 int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int k,
-                  const int32_t* expert_offsets, int E, int rows, const void* blobs_dev,
+                  const int32_t* expert_offsets, int E, int rows, int src_rows, const void* blobs_dev,
                   size_t expert_stride, const w4a8_wdesc* d, void* Y, int out_dtype,
                   void* stream);
 
@@ -282,7 +289,8 @@ int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int 
  * (P1 section 1 names SiLU; P1 section 3.1: per-expert activation scales).
  *   GU_bf16  device bfloat16 [R, 2I]: gate = columns [0, I), up = [I, 2I)
  *   Hq, sh   device int8 [R, I] (16-byte aligned, I % 16 == 0), float32 [R]
- * h = fl32(g / (1 + exp(-g)) * u) in float32, then the per-token rule of w4a8_quant_act. */
+ * h = fl32(g / (1 + exp(-g)) * u) in float32, then the per-token rule of w4a8_quant_act.
+ * I <= 16384 (EUNSUPPORTED beyond). */
 int w4a8_silu_mul_quant(const void* GU_bf16, int R, int I, int8_t* Hq, float* sh,
                         void* stream);
 
@@ -313,7 +321,10 @@ size_t w4a8_moe_workspace_size(int T, int k, int H, int I, int E);
  *   gu_blobs    E blobs of desc gu_desc (K = H, N = 2I), stride gu_stride
  *   d_blobs     E blobs of desc d_desc (K = I, N = H), stride d_stride
  *   workspace   device, >= w4a8_moe_workspace_size(T, k, H, I, E) bytes, 256-aligned
- *   out_bf16    device [T, H] */
+ *   out_bf16    device [T, H], 16-byte aligned
+ * Limits: E <= 1024 (EINVAL), T*k <= 2^24, H <= 65536, I <= 16384 (EUNSUPPORTED); H and I
+ * multiples of 16, X 16-byte aligned (EINVAL).  Every argument check of the chained steps
+ * runs before the first launch: an error return means that nothing was enqueued. */
 int w4a8_moe_forward(const void* X_bf16, const int32_t* topk_ids, const float* topk_w, int T,
                      int k, int E, const void* gu_blobs, size_t gu_stride,
                      const w4a8_wdesc* gu_desc, const void* d_blobs, size_t d_stride,

@@ -76,7 +76,7 @@ def lib() -> ctypes.CDLL:
             "w4a8_linear": (I, [P, I, I, I, P, DP, P, I, I, P, P, VP]),
             "w4a8_gemm_partials": (I, [P, I, P, DP, P, VP]),
             "w4a8_moe_align": (I, [P, I, I, I, P, P, P, VP]),
-            "w4a8_moe_gemm": (I, [P, P, P, I, P, I, I, P, SZ, DP, P, I, VP]),
+            "w4a8_moe_gemm": (I, [P, P, P, I, P, I, I, I, P, SZ, DP, P, I, VP]),
             "w4a8_silu_mul_quant": (I, [P, I, I, P, P, VP]),
             "w4a8_moe_combine": (I, [P, P, P, I, I, I, P, VP]),
             "w4a8_moe_workspace_size": (SZ, [I, I, I, I, I]),
@@ -269,9 +269,12 @@ def w4a8_moe_align(topk_ids, E: int, sorted_rows, expert_offsets, inv, stream=No
 def w4a8_moe_gemm(Xq, sx, gather, k: int, expert_offsets, E: int, rows: int, blobs_dev, expert_stride: int,
                   d: WDesc, Y, out_dtype: int = W4A8_OUT_BF16, stream=None) -> None:
     _require_cuda(Xq, sx, gather, expert_offsets, blobs_dev, Y)
+    src_rows = int(Xq.shape[0])
+    if sx.numel() < src_rows:
+        raise ValueError("sx must hold one scale per row of Xq")
     _check(lib().w4a8_moe_gemm(_ptr(Xq), _ptr(sx), _ptr(gather), int(k), _ptr(expert_offsets), int(E), int(rows),
-                               _ptr(blobs_dev), int(expert_stride), ctypes.byref(d), _ptr(Y), int(out_dtype),
-                               _stream(stream)), "w4a8_moe_gemm")
+                               src_rows, _ptr(blobs_dev), int(expert_stride), ctypes.byref(d), _ptr(Y),
+                               int(out_dtype), _stream(stream)), "w4a8_moe_gemm")
 
 
 def w4a8_silu_mul_quant(GU, Hq, sh, stream=None) -> None:

@@ -16,6 +16,17 @@ def bf16_ulp(x):
     return 2.0 ** (e - 7)
 
 
+# Near-tie window of the SiLU requantization, in units of the code t = h / s.
+# The kernel computes h = RN(RN(g / RN(1 + expf(-g))) * u) in float32 from exact bfloat16 g, u.
+# With expf within 1 ulp, the relative error of h against the exact value is at most
+# 2^-23 (exp through 1 + e) + 3 * 2^-24 (three roundings) = 2.5 * 2^-23 ~ 3.0e-7.  At
+# |t| <= 127 that moves t by <= 3.8e-5; the dynamic scale s = fl32(max|h| / 127) carries the same
+# relative error (another 3.8e-5), and the oracle's own float32 rounding of h adds 127 * 2^-24 ~
+# 7.6e-6.  Total < 8.4e-5, so a code may differ by one only where the float64 t lies within
+# 1e-4 of a .5 boundary.
+SILU_TIE_WINDOW = 1e-4
+
+
 def gpu_quant(Xb: torch.Tensor):
     X = Xb.to(DEV)
     M, K = X.shape
@@ -144,3 +155,12 @@ def check_moe(out, ref, qw, group_size, flips_per_row=2):
     assert nw < 1e-3, stats
     assert np.all(err <= allow), stats
     return stats
+
+
+def sample_tokens(T, n, seed):
+    """n distinct token indices of a T-token batch, always including the first and the last
+    (sorted).  The MoE layer is independent per token once the routing is fixed, so the
+    oracle runs on these tokens only while the GPU runs the whole batch."""
+    rs = np.random.default_rng(seed)
+    mid = rs.choice(np.arange(1, T - 1), size=max(0, n - 2), replace=False)
+    return np.unique(np.concatenate([[0, T - 1], mid])).astype(np.int64)

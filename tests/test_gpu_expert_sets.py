@@ -8,7 +8,7 @@ import torch
 import moe_token_int8_amd as L
 import oracle as O
 import workloads as W
-from gpu_cases import DEV, check_moe
+from gpu_cases import DEV, check_moe, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,8 @@ def _run(cfg, Xb, ids, w, sets):
     return out
 
 
-@pytest.mark.parametrize("name", ["small_rtn", "c4_two_classes", "c5_4tok_two_classes"])
+@pytest.mark.parametrize("name", ["small_rtn", "c4_two_classes", "c5_4tok_two_classes",
+                                  "c5_full_two_classes_sampled"])
 def test_moe_forward_expert_sets(name):
     if name == "small_rtn":
         cfg, T, rtn = W.MoEConfig("small", 40, 512, 256, 8, 2, 64, True, 51), None, True
@@ -68,16 +69,20 @@ def test_moe_forward_expert_sets(name):
     elif name == "c4_two_classes":                     # hot experts take the prefill tiles
         cfg, T, rtn = W.C4, None, False
         classes = [(32, 128, False, 32), (32, 64, True, 16)]
-    else:
+    elif name == "c5_4tok_two_classes":
         cfg, T, rtn = W.C5, 4, False
+        classes = [(128, 64, True, 32), (128, 128, True, 16)]
+    else:                                              # full T = 64; the oracle checks 6 tokens
+        cfg, T, rtn = W.C5, None, False
         classes = [(128, 64, True, 32), (128, 128, True, 16)]
     _print(f"expert sets {name}: {classes}")
     ids, w = W.moe_routing(cfg, T=T) if T else W.moe_routing(cfg)
     Xb = W.moe_activations(cfg, T=T) if T else W.moe_activations(cfg)
-    sets, qw, gs = _sets(cfg, set(ids.ravel().tolist()), classes, 9, rtn)
+    tok = sample_tokens(ids.shape[0], 6, 55) if name.endswith("_sampled") else np.arange(ids.shape[0])
+    sets, qw, gs = _sets(cfg, set(ids[tok].ravel().tolist()), classes, 9, rtn)
     out = _run(cfg, Xb, ids, w, sets)
-    ref = O.moe_layer(W.bf16_values(Xb), ids, w, lambda e: qw[e], cfg.E, cfg.I, gs)
-    check_moe(out, ref, qw, gs)
+    ref = O.moe_layer(W.bf16_values(Xb)[tok], ids[tok], w[tok], lambda e: qw[e], cfg.E, cfg.I, gs)
+    check_moe(out[torch.from_numpy(tok).to(DEV)], ref, qw, gs)
 
 
 def test_one_set_equals_moe_forward():

@@ -12,7 +12,7 @@ import torch
 import moe_token_int8_amd as L
 import oracle as O
 import workloads as W
-from gpu_cases import DEV, check_moe, moe_experts_codes, moe_experts_rtn
+from gpu_cases import DEV, SILU_TIE_WINDOW, check_moe, moe_experts_codes, moe_experts_rtn
 
 pytestmark = pytest.mark.gpu
 
@@ -173,7 +173,7 @@ def test_silu_mul_quant_static_vs_oracle(T, E, k, I):
         diff = np.abs(qg[a:b] - qr.astype(np.int64))
         assert diff.max() <= 1
         t = h[a:b] / np.float64(s_e[e])
-        near = (np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-3) & (np.abs(t) < 127.5)
+        near = (np.abs(np.abs(t - np.floor(t)) - 0.5) < SILU_TIE_WINDOW) & (np.abs(t) < 127.5)
         assert np.all(near[diff > 0])
         nflip += int((diff > 0).sum())
     _print(f"silu static R={R} I={I}: {nflip} near-tie code differences")

@@ -185,7 +185,7 @@ def test_8bit_validation_host():
     assert L.w4a8_kernel_name(d, 4096) == "w8a8_prefill_sym_g128"
     # the grouped (MoE) entry points take 4-bit codes only; rejected before any HIP call
     fake = 0x10000
-    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0, None) == U
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, 8, fake, 1 << 20, ctypes.byref(d), fake, 0, None) == U
     gu = L.desc(256, 64, 128, False)
     ws = L.w4a8_moe_workspace_size(4, 2, 256, 32, 8)
     assert lib.w4a8_moe_forward(fake, fake, fake, 4, 2, 8, fake, 1 << 20, ctypes.byref(gu), fake, 1 << 20,
@@ -208,7 +208,7 @@ def test_g256_names_and_grouped_form_rejected_host():
     assert L.w4a8_kernel_name(L.desc(1024, 64, 64, False), 8) == "w4a8_decode_m16_sym_g64"
     assert L.w4a8_kernel_name(L.desc(1024, 64, 32, False), 8) == "w4a8_decode_m16_sym_g32"
     fake = 0x10000
-    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
                              None) == L.W4A8_EUNSUPPORTED
 
 
@@ -221,7 +221,7 @@ def test_g32_names_and_grouped_form_rejected_host():
     assert L.w4a8_kernel_name(d, 1) == "w4a8_decode_m16_asym_g32"
     assert L.w4a8_kernel_name(d, 32) == "w4a8_decode_m32_asym_g32"
     assert L.w4a8_kernel_name(L.desc(4096, 64, 32, False, bits=8), 64) == "w8a8_prefill_sym_g32"
-    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
                              None) == L.W4A8_EUNSUPPORTED
     assert L.w4a8_kernel_name(L.desc(4096, 64, 32, True, scale_bits=16), 1) == "unsupported"
 
@@ -255,7 +255,7 @@ def test_perchannel_names_and_limits_host():
     assert L.w4a8_kernel_name(d, 1) == "w4a8_decode_m16_asym_gK"
     assert L.w4a8_kernel_name(d, 64) == "w4a8_prefill_asym_gK"
     assert lib.w4a8_gemm_partials(fake, 4, fake, ctypes.byref(d), fake, None) == L.W4A8_EUNSUPPORTED
-    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
                              None) == L.W4A8_EUNSUPPORTED
     assert L.w4a8_packed_size(L.desc(4096, 64, 2048, True)) == 0          # neither a listed g nor K
     # one group's int32 sum must hold g * 127 * max|q - z|: K = 133248 with 8-bit codes does not
@@ -378,9 +378,9 @@ def test_gpu_entry_points_validate_before_launch():
     assert lib.w4a8_moe_align(fake, 4, 2, 0, fake, fake, fake, None) == E
     assert lib.w4a8_moe_align(fake, 4, 2, 2000, fake, fake, fake, None) == E
     assert lib.w4a8_moe_align(fake, 4, 0, 8, fake, fake, fake, None) == E
-    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 0, fake, 4096, ctypes.byref(d), fake, 0, None) == L.W4A8_OK
-    assert lib.w4a8_moe_gemm(fake, fake, fake, 0, fake, 4, 8, fake, 1 << 20, ctypes.byref(d), fake, 0, None) == E
-    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, fake, 64, ctypes.byref(d), fake, 0, None) == E  # stride
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 0, 0, fake, 4096, ctypes.byref(d), fake, 0, None) == L.W4A8_OK
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 0, fake, 4, 8, 8, fake, 1 << 20, ctypes.byref(d), fake, 0, None) == E
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, 8, fake, 64, ctypes.byref(d), fake, 0, None) == E  # stride
     assert lib.w4a8_silu_mul_quant(fake, 4, 24, fake, fake, None) == E                # I % 16
     assert lib.w4a8_silu_mul_quant(fake, 0, 32, fake, fake, None) == L.W4A8_OK
     assert lib.w4a8_moe_combine(fake, fake, fake, 4, 2, 12, fake, None) == E          # H % 8
@@ -425,9 +425,9 @@ def test_prefill_offset_limits_host():
     assert lib.w4a8_gemm_partials(fake, 33, fake, ctypes.byref(big), fake, None) == E
     d = L.desc(4096, 64, 128, False)
     rows = (1 << 31) // 4096                       # ceil(rows / k) * K = 2^31 with k = 1
-    assert lib.w4a8_moe_gemm(fake, fake, fake, 1, fake, 1, rows, fake, 0, ctypes.byref(d), fake, 0, None) == E
+    assert lib.w4a8_moe_gemm(fake, fake, fake, 1, fake, 1, rows, rows, fake, 0, ctypes.byref(d), fake, 0, None) == E
     # without gather every row counts
-    assert lib.w4a8_moe_gemm(fake, fake, None, 1, fake, 1, rows, fake, 0, ctypes.byref(d), fake, 0, None) == E
+    assert lib.w4a8_moe_gemm(fake, fake, None, 1, fake, 1, rows, rows, fake, 0, ctypes.byref(d), fake, 0, None) == E
 
 
 def test_kernel_names_resolve():
@@ -473,3 +473,69 @@ def test_fp16_pack_codes_nan_and_range():
     sc[1, 3] = 70000.0
     with pytest.raises(L.W4A8Error):
         L.w4a8_pack_codes(d, codes, sc, None)
+
+
+def test_moe_gemm_source_rows_checked():
+    """w4a8_moe_gemm takes the row count of Xq / sx: with a gather it must be positive (the
+    kernels bound gathered tokens by it), without one it must cover the output rows."""
+    lib = L.lib()
+    fake = 0x10000
+    E = L.W4A8_EINVAL
+    d = L.desc(256, 64, 128, False)
+    call = lambda gather, rows, src: lib.w4a8_moe_gemm(fake, fake, gather, 2, fake, 4, rows, src, fake, 1 << 20,
+                                                       ctypes.byref(d), fake, 0, None)
+    assert call(fake, 8, 0) == E                   # gather, no source rows
+    assert call(fake, 8, -1) == E
+    assert call(None, 8, 7) == E                   # no gather: Xq must hold every output row
+    assert call(None, 0, 0) == L.W4A8_OK
+
+
+def test_symmetric_per_channel_accumulator_bound():
+    """Symmetric 4-bit codes enter the int32 sum as 16 q (|16 q| <= 112): per-channel scales
+    (g = K) are accepted up to K = 150912, since 150912 * 127 * 112 < 2^31 <= 151040 * 127 * 112;
+    asymmetric codes (|q - z| <= 15) reach much further."""
+    lib = L.lib()
+    fake = 0x10000
+    assert 150912 * 127 * 112 < 2 ** 31 <= 151040 * 127 * 112
+    ok = L.desc(150912, 16, 150912, False)
+    bad = L.desc(151040, 16, 151040, False)
+    assert L.w4a8_kernel_name(ok, 1) == "w4a8_decode_m16_sym_gK"
+    assert L.w4a8_kernel_name(bad, 1) == "unsupported"
+    assert L.w4a8_kernel_name(L.desc(151040, 16, 151040, True), 1) == "w4a8_decode_m16_asym_gK"
+    assert lib.w4a8_gemm(fake, fake, 4, fake, ctypes.byref(bad), fake, 16, 0, None) == L.W4A8_EUNSUPPORTED
+    assert lib.w4a8_gemm_partials(fake, 64, fake, ctypes.byref(bad), fake, None) == L.W4A8_EUNSUPPORTED
+
+
+def test_moe_layer_checks_run_before_any_launch():
+    """The MoE layer entry points check every step's arguments before the first launch.  On a
+    host without a GPU any launch fails with EHIP, so receiving the argument error itself shows
+    that nothing was launched first (quantization and align used to be enqueued before the
+    expert count, the output alignment or the SiLU row length were checked)."""
+    lib = L.lib()
+    fake = 0x10000
+    ws = 1 << 40
+    H, I = 256, 128
+
+    def descs(I_):
+        return L.desc(H, 2 * I_, 128, False), L.desc(I_, H, 128, False)
+
+    def fwd(E, out=fake, I_=I):
+        gu, dn = descs(I_)
+        return lib.w4a8_moe_forward(fake, fake, fake, 8, 2, E, fake, 1 << 24, ctypes.byref(gu), fake, 1 << 24,
+                                    ctypes.byref(dn), fake, ws, out, None)
+
+    def fwd_static(E, out=fake, I_=I):
+        gu, dn = descs(I_)
+        return lib.w4a8_moe_forward_static(fake, fake, fake, 8, 2, E, fake, 1 << 24, ctypes.byref(gu), fake,
+                                           1 << 24, ctypes.byref(dn), fake, fake, fake, ws, out, None)
+
+    def fwd_sets(E, out=fake, I_=I):
+        gu, dn = descs(I_)
+        sets = (L.ExpertSet * 1)(L.ExpertSet(E, fake, 1 << 24, ctypes.pointer(gu), fake, 1 << 24, ctypes.pointer(dn)))
+        return lib.w4a8_moe_forward_sets(fake, fake, fake, 8, 2, sets, 1, fake, ws, out, None)
+
+    for f in (fwd, fwd_static, fwd_sets):
+        assert f(2000) == L.W4A8_EINVAL                       # E > 1024 (align's limit)
+        assert f(8, out=0x10002) == L.W4A8_EINVAL             # combine needs a 16-byte aligned output
+        assert f(8, I_=16512) == L.W4A8_EUNSUPPORTED          # SiLU rows up to 16384
+        assert f(8) == L.W4A8_EHIP                            # valid: the first launch fails here
