@@ -331,6 +331,19 @@ int w4a8_moe_forward(const void* X_bf16, const int32_t* topk_ids, const float* t
                      const w4a8_wdesc* d_desc, void* workspace, size_t workspace_bytes,
                      void* out_bf16, void* stream);
 
+/* w4a8_moe_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The workspace is a 64 MiB
+ * device array that the library holds on each GPU it runs on until the process ends; the call
+ * itself allocates nothing.  Layers whose w4a8_moe_workspace_size exceeds 64 MiB return
+ * W4A8_ESIZE (the T = 512, E = 64, top-6 layer with H = 4096, I = 1408 needs about 49 MB).
+ * Every call on one GPU shares that array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialized by the caller.  Arguments, results and other errors as
+ * w4a8_moe_forward (W4A8_EHIP also if the array's address cannot be obtained). */
+int w4a8_moe_forward_noalloc(const void* X_bf16, const int32_t* topk_ids, const float* topk_w, int T,
+                             int k, int E, const void* gu_blobs, size_t gu_stride,
+                             const w4a8_wdesc* gu_desc, const void* d_blobs, size_t d_stride,
+                             const w4a8_wdesc* d_desc, void* out_bf16, void* stream);
+
 /* One format class of experts for w4a8_moe_forward_sets: n_experts consecutive experts
  * whose gate/up blobs (desc gu_desc, stride gu_stride) and down blobs (d_desc, d_stride)
  * share one format.  Experts are numbered set by set: set 0 holds experts [0, n_0), set 1

@@ -26,7 +26,7 @@ EXPORTED = [
     "w4a8_moe_gemm",
     "w4a8_silu_mul_quant", "w4a8_moe_combine", "w4a8_moe_workspace_size", "w4a8_moe_forward",
     "w4a8_quant_act_static", "w4a8_moe_quant_static", "w4a8_silu_mul_quant_static",
-    "w4a8_moe_static_workspace_size", "w4a8_moe_forward_static", "w4a8_moe_forward_sets",
+    "w4a8_moe_static_workspace_size", "w4a8_moe_forward_static", "w4a8_moe_forward_sets", "w4a8_moe_forward_noalloc",
     "w4a8_kernel_name", "w4a8_status_string", "w4a8_version",
 ]
 
@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
             "w4a8_moe_static_workspace_size": (SZ, [I, I, I, I, I]),
             "w4a8_moe_forward_static": (I, [P, P, P, I, I, I, P, SZ, DP, P, SZ, DP, P, P, P, SZ, P, VP]),
             "w4a8_moe_forward_sets": (I, [P, P, P, I, I, ctypes.POINTER(ExpertSet), I, P, SZ, P, VP]),
+            "w4a8_moe_forward_noalloc": (I, [P, P, P, I, I, I, P, SZ, DP, P, SZ, DP, P, VP]),
             "w4a8_kernel_name": (ctypes.c_char_p, [DP, I]),
             "w4a8_status_string": (ctypes.c_char_p, [I]),
             "w4a8_version": (I, []),
@@ -307,6 +308,18 @@ def w4a8_moe_forward(X, topk_ids, topk_w, E: int, gu_blobs, gu_stride: int, gu_d
                                   int(gu_stride), ctypes.byref(gu_desc), _ptr(d_blobs), int(d_stride),
                                   ctypes.byref(d_desc), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _ptr(out), _stream(stream)), "w4a8_moe_forward")
+
+
+def w4a8_moe_forward_noalloc(X, topk_ids, topk_w, E: int, gu_blobs, gu_stride: int, gu_desc: WDesc, d_blobs,
+                             d_stride: int, d_desc: WDesc, out, stream=None) -> None:
+    """w4a8_moe_forward on the library's own device scratch (no workspace argument; the call
+    allocates nothing).  Calls that overlap on one GPU race: serialize them."""
+    _require_cuda(X, topk_ids, topk_w, gu_blobs, d_blobs, out)
+    T, k = topk_ids.shape
+    _check(lib().w4a8_moe_forward_noalloc(_ptr(X), _ptr(topk_ids), _ptr(topk_w), T, k, int(E), _ptr(gu_blobs),
+                                          int(gu_stride), ctypes.byref(gu_desc), _ptr(d_blobs), int(d_stride),
+                                          ctypes.byref(d_desc), _ptr(out), _stream(stream)),
+           "w4a8_moe_forward_noalloc")
 
 
 def w4a8_moe_forward_static(X, topk_ids, topk_w, E: int, gu_blobs, gu_stride: int, gu_desc: WDesc, d_blobs,

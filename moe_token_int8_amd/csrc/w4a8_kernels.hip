@@ -20,6 +20,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "w4a8_internal.h"
@@ -2350,6 +2351,52 @@ int w4a8_moe_forward(const void* X, const int32_t* ids, const float* w, int T, i
                             W4A8_OUT_BF16, stream)))
         return st;
     return w4a8_moe_combine(B.yd, B.inv, w, T, k, H, out, stream);
+}
+
+// Scratch of w4a8_moe_forward_noalloc: the workspace of w4a8_moe_forward, held in device memory
+// for the life of the process (one copy on each GPU the library runs on).  Host code never
+// uses the name `scratch` as an address: each device's copy is reached through the pointer
+// that hipGetSymbolAddress returns with that device current.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static std::mutex scratch_mu;
+static void* scratch_dev[NOALLOC_MAX_DEVICES];
+
+// Address of the current device's scratch, looked up once per device.
+static int scratch_of_current_device(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return W4A8_EHIP;
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return W4A8_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return W4A8_EHIP;
+        scratch_dev[dev] = p;
+    }
+    *ptr = scratch_dev[dev];
+    return W4A8_OK;
+}
+
+int w4a8_moe_forward_noalloc(const void* X, const int32_t* ids, const float* w, int T, int k, int E,
+                             const void* gu_blobs, size_t gu_stride, const w4a8_wdesc* gu_desc, const void* d_blobs,
+                             size_t d_stride, const w4a8_wdesc* d_desc, void* out, void* stream) {
+    int st = check_gemm_desc(gu_desc);
+    if (st) return st;
+    if ((st = check_gemm_desc(d_desc))) return st;
+    if (T < 0 || k <= 0 || E <= 0) return W4A8_EINVAL;
+    const int H = gu_desc->K, I2 = gu_desc->N;
+    if (I2 % 2 || d_desc->K != I2 / 2 || d_desc->N != H) return W4A8_EINVAL;
+    if (T == 0) return W4A8_OK;
+    // the layer's workspace must fit the scratch (checked before the device is touched)
+    if (moe_ws(T, k, H, I2 / 2, E).total > NOALLOC_SCRATCH_BYTES) return W4A8_ESIZE;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws))) return st;
+    // the layer writes every workspace byte it reads before reading it, so nothing left by an
+    // earlier call needs clearing
+    return w4a8_moe_forward(X, ids, w, T, k, E, gu_blobs, gu_stride, gu_desc, d_blobs, d_stride, d_desc, ws,
+                            NOALLOC_SCRATCH_BYTES, out, stream);
 }
 
 int w4a8_moe_forward_sets(const void* X, const int32_t* ids, const float* w, int T, int k, const w4a8_expert_set* sets,

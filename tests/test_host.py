@@ -539,3 +539,17 @@ def test_moe_layer_checks_run_before_any_launch():
         assert f(8, out=0x10002) == L.W4A8_EINVAL             # combine needs a 16-byte aligned output
         assert f(8, I_=16512) == L.W4A8_EUNSUPPORTED          # SiLU rows up to 16384
         assert f(8) == L.W4A8_EHIP                            # valid: the first launch fails here
+
+
+def test_noalloc_forward_rejects_layers_past_its_scratch():
+    """w4a8_moe_forward_noalloc holds a 64 MiB workspace: a layer needing more returns ESIZE
+    before the device is touched."""
+    lib = L.lib()
+    fake = 0x10000
+    gu, dn = L.desc(4096, 2 * 1408, 128, False), L.desc(1408, 4096, 128, False)
+    call = lambda T: lib.w4a8_moe_forward_noalloc(fake, fake, fake, T, 6, 64, fake, 1 << 24, ctypes.byref(gu),
+                                                  fake, 1 << 24, ctypes.byref(dn), fake, None)
+    assert L.w4a8_moe_workspace_size(512, 6, 4096, 1408, 64) <= 64 << 20
+    assert L.w4a8_moe_workspace_size(1024, 6, 4096, 1408, 64) > 64 << 20
+    assert call(1024) == L.W4A8_ESIZE
+    assert call(0) == L.W4A8_OK
