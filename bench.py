@@ -38,7 +38,7 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--steps", type=int, default=200, help="timed steps (exactly this many)")
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--copies", type=int, default=16, help="device copies of the decode weights")
     p.add_argument("--no-extra", action="store_true", help="skip the prefill and MoE figures")
@@ -145,24 +145,21 @@ def decode_leg(args, L, W, torch, dev):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # One graph holds `per_graph` steps, a whole period of the weight-copy rotation, so
-    # replaying it keeps every GEMM on a copy that was not read for 15 launches.
-    per_graph = args.copies
-    counter[0] = 0
+    # The timed region is exactly `steps` steps.  With graphs (the default) they are captured
+    # once into one HIP graph (the weight-copy rotation continues through it, so consecutive
+    # GEMMs read different copies), the graph is replayed once untimed, then once timed.
+    steps = args.steps
     graph = None
     if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for _ in range(per_graph):
+            for _ in range(steps):
                 step()
         graph.replay()
         torch.cuda.synchronize()
-    reps = max(1, (args.steps + per_graph - 1) // per_graph)
-    steps = reps * per_graph
     t0 = time.perf_counter()
     if graph is not None:
-        for _ in range(reps):
-            graph.replay()
+        graph.replay()
     else:
         for _ in range(steps):
             step()
@@ -170,6 +167,16 @@ def decode_leg(args, L, W, torch, dev):
     dt = time.perf_counter() - t0
     ms_step = dt * 1e3 / steps
     value = len(Ms) * wbytes * steps / dt / 1e9
+    # the same region timed again with HIP events on the launch stream, 5 repeats: median and
+    # spread of the step time (reported beside `value`)
+    ev_ms = []
+    if graph is not None:
+        for _ in range(5):
+            t = Timer(torch)
+            s_ = t.start()
+            graph.replay()
+            t.stop(s_)
+            ev_ms.append(t.mean_ms() / steps)
     # the dominant kernel (decode GEMM, M = 32): 64 back-to-back launches on rotating weight
     # copies between two HIP events on the launch stream; per-launch mean.  The launches are
     # replayed from a HIP graph so that the host's launch rate does not pace them.
@@ -206,7 +213,7 @@ def decode_leg(args, L, W, torch, dev):
     achieved = kbytes / (k_ms * 1e-3) / 1e9
     return dict(value=value, ms_per_step=ms_step, steps=steps, weight_bytes=wbytes, kernel_ms=k_ms,
                 kernel_bytes=kbytes, achieved=achieved, kernel=L.w4a8_kernel_name(d, 32), host_blob=host, Wt=Wt,
-                graph=graph is not None)
+                graph=graph is not None, event_ms=ev_ms)
 
 
 def measured_traffic(kernel):
@@ -227,14 +234,26 @@ def measured_traffic(kernel):
     return int(rec["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(args, leg, W):
-    """The oracle on the same decode step (weights quantized once, outside the timing)."""
-    import oracle as O
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline(args, leg, W):
+    """The oracle on the same decode step (weights quantized once, outside the timing), with BLAS
+    limited to the cores this process may run on."""
+    import oracle as O
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads)
     except Exception:
-        threads = 1
+        limiter = None
     cfg = W.C2
     codes, scales, zeros = O.quant_weight(leg["Wt"], cfg.group_size, cfg.asymmetric)
     xs = {M: W.bf16_values(W.dense_inputs(W.with_decode_m(cfg, M))[0]) for M in W.C2_M}
@@ -252,10 +271,12 @@ def cpu_baseline(args, leg, W):
         if time.perf_counter() - t0 >= args.cpu_seconds or n >= 50:
             break
     dt = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.restore_original_limits()
     return {"value": len(W.C2_M) * leg["weight_bytes"] * n / dt / 1e9, "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n} full decode steps (quant + GEMM for M=1,8,32; K=4096, N=14336) in {dt:.1f} s; "
-                      f"numpy/BLAS, weights quantized once beforehand"}
+                      f"numpy/BLAS on {threads} threads of {cpu_model()}, weights quantized once beforehand"}
 
 
 # ---------------------------------------------------------------------------------- prefill
@@ -586,6 +607,9 @@ def main():
                    "group_size": W.C2.group_size, "asymmetric": False, "weight_copies": args.copies,
                    "hip_graph": leg["graph"],
                    "parallelism": "single_gpu"},
+        "step_event_ms": {"median": round(float(np.median(leg["event_ms"])), 5),
+                          "min": round(float(np.min(leg["event_ms"])), 5),
+                          "max": round(float(np.max(leg["event_ms"])), 5)} if leg["event_ms"] else None,
         "roofline": {"bound": "hbm", "achieved": round(leg["achieved"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(leg["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(leg["kernel"]),

@@ -33,6 +33,8 @@ Pins (each function is checked against something other than itself in
                     P5 section 7; integer matmul when K equals the group.
   gemm              brute-force fp64 dequantise-then-matmul; per-token x
                     per-channel closed form of P5 section 8.3 when g = K.
+  gemm_a16          brute-force fp64 x @ dequantised weights; equals gemm on activations
+                    that are exactly s_x x_q; per-channel closed form when g = K.
   silu_mul          x*sigmoid(x) via scipy.special.expit; odd-part identity.
   moe_align         bincount/prefix-sum and permutation invariants.
   moe_layer         E=1,k=1,w=1 reduces to the dense chain; token permutation
@@ -65,7 +67,7 @@ import numpy as np
 
 __all__ = [
     "bf16_rne", "quant_act", "quant_act_static", "calibrate_act_scale", "quant_act_smooth", "smooth_factors", "smooth_weights", "dequant_act", "quant_weight", "dequant_weight", "gemm_partials",
-    "gemm", "silu_mul", "silu_mul_quant", "moe_align", "moe_layer", "effective_bits",
+    "gemm", "gemm_a16", "silu_mul", "silu_mul_quant", "moe_align", "moe_layer", "effective_bits",
     "memory_bytes", "compression_vs_fp16",
 ]
 
@@ -318,6 +320,29 @@ def gemm(xq, sx, codes, scales, zeros, group_size: int):
         Pi = xq[:, ks].astype(np.float64) @ b                 # exact integers
         acc += Pi * np.asarray(scales[i], np.float64)[None, :]
     return acc * np.asarray(sx, np.float64)[:, None]
+
+
+def gemm_a16(x, codes, scales, zeros, group_size: int):
+    """W4A16 sibling: Y[m, n] = sum_i s_w[i, n] * sum_{k in group i} x[m, k] * (q[k, n] - z[i, n])
+    in float64, with the activations x kept in 16 bits (no activation quantization) and the
+    4-bit weights dequantized inside the kernel.  P1 section 5.3 lists W4A16 beside W8A8 and W4A8;
+    P5 section 3.2 describes the weight-only path as a dequantization fused into the GEMM.  The
+    weight dequantization is the same s (q - z) as for W4A8 (P3 "Basic mapping"); the reading
+    taken is that the scale multiplies each group's sum, as in the W4A8 epilogue.  x: the float
+    values of the bfloat16 activations.  Every product x * (q - z) is exact in float64, and the
+    sums round at 2^-53, far below any tolerance used against them."""
+    x = np.asarray(x, np.float64)
+    M, K = x.shape
+    N = np.asarray(codes).shape[1]
+    G = K // group_size
+    acc = np.zeros((M, N), dtype=np.float64)
+    for i in range(G):
+        ks = slice(i * group_size, (i + 1) * group_size)
+        b = np.asarray(codes[ks], np.float64)
+        if zeros is not None:
+            b = b - np.asarray(zeros[i], np.float64)[None, :]
+        acc += (x[:, ks] @ b) * np.asarray(scales[i], np.float64)[None, :]
+    return acc
 
 
 # --------------------------------------------------------------------------------------

@@ -292,6 +292,44 @@ def test_gemm_linear_in_scales_and_rows():
     assert np.array_equal(O.gemm(xq[perm], sx[perm], codes, scales, zeros, 128), Y[perm])
 
 
+@pytest.mark.parametrize("M,K,N,g,asym", [(3, 64, 5, 32, False), (5, 128, 7, 64, True), (4, 256, 6, 128, False),
+                                          (2, 256, 3, 128, True)])
+def test_gemm_a16_bruteforce_dequant(M, K, N, g, asym):
+    """W4A16: Y equals x @ (s_w * (q - z)) evaluated term by term in float64, x the bfloat16
+    activations themselves (no quantization)."""
+    _, _, codes, scales, zeros = _tiny_problem(31, M, K, N, g, asym)
+    rs = np.random.default_rng(M * K + N)
+    x = W.bf16_values(W.to_bf16(rs.standard_normal((M, K)).astype(F32) * 3))
+    Y = O.gemm_a16(x, codes, scales, zeros, g)
+    for m, n in itertools.product(range(M), range(N)):
+        ref = 0.0
+        for kk in range(K):
+            i = kk // g
+            z = float(zeros[i, n]) if asym else 0.0
+            ref += float(x[m, kk]) * (float(scales[i, n]) * (float(codes[kk, n]) - z))
+        assert abs(Y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref)) + 1e-15
+
+
+def test_gemm_a16_reduces_to_w4a8_on_quantized_activations():
+    """When the 16-bit activations are exactly s_x * x_q (a power-of-two row scale times int8
+    codes), W4A16 and W4A8 compute the same product: gemm_a16(s_x x_q) = gemm(x_q, s_x)."""
+    xq, _, codes, scales, zeros = _tiny_problem(37, 5, 256, 7, 64, True)
+    sx = np.array([2.0 ** -5, 2.0 ** -7, 1.0, 2.0 ** 3, 2.0 ** -10], F32)
+    x = sx.astype(np.float64)[:, None] * xq.astype(np.float64)
+    assert np.array_equal(W.bf16_values(W.to_bf16(x.astype(F32))), x.astype(F32))      # exact in bf16
+    ya16 = O.gemm_a16(x, codes, scales, zeros, 64)
+    y8 = O.gemm(xq, sx, codes, scales, zeros, 64)
+    assert np.allclose(ya16, y8, rtol=1e-14, atol=0)
+
+
+def test_gemm_a16_per_channel_closed_form():
+    """g = K: one scale per column, Y = (x @ q) * s_w[n] (the weight-only form of P5 section 8.3)."""
+    _, _, codes, scales, _ = _tiny_problem(41, 3, 128, 4, 128, False)
+    x = W.bf16_values(W.to_bf16(np.random.default_rng(5).standard_normal((3, 128)).astype(F32)))
+    ref = (x.astype(np.float64) @ codes.astype(np.float64)) * scales[0].astype(np.float64)[None, :]
+    assert np.allclose(O.gemm_a16(x, codes, scales, None, 128), ref, rtol=1e-14, atol=0)
+
+
 # ------------------------------------------------------------------ silu / requant
 def test_silu_mul_library_and_identity():
     rs = np.random.default_rng(0)
