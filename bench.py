@@ -436,9 +436,10 @@ def quant_leg(args, L, W, torch, dev, steps):
 
 # ------------------------------------------------------- W8A8 sibling and bf16 library baseline
 def compare_leg(args, L, W, torch, dev):
-    """The pages' comparison (bf16 baseline, W8A8, W4A8) on the same shapes: bf16 GEMMs through
-    torch.mm (the platform's library GEMM), the W8A8 sibling (8-bit symmetric codes, g = 128,
-    the same kernels without the unpack) and W4A8, all measured the same way.  Decode: per-call
+    """The pages' comparison (bf16 baseline, W8A8, W4A16, W4A8) on the same shapes: bf16 GEMMs
+    through torch.mm (the platform's library GEMM), the W8A8 sibling (8-bit symmetric codes,
+    g = 128, the same kernels without the unpack), the W4A16 sibling (bfloat16 activations, the
+    same 4-bit blob, bfloat16 MFMA) and W4A8, all measured the same way.  Decode: per-call
     means of w4a8_linear / torch.mm over 16 rotating weight copies, launches replayed from a
     graph.  Prefill: the projection pair at M = 4096, GEMM only."""
     out = {"decode": {}, "prefill": {}}
@@ -508,10 +509,16 @@ def compare_leg(args, L, W, torch, dev):
             for c in range(ncopy):
                 L.w4a8_linear(X, blobs32[c], d32, Y, Xq, sx, L.W4A8_OUT_BF16)
 
+        def w4a16():
+            for c in range(ncopy):
+                L.w4a16_gemm(X, blobs[c], d, Y, L.W4A8_OUT_BF16)
+
         t4, t8, tb, t16 = per_call_us(w4a8), per_call_us(w8a8), per_call_us(bf16), per_call_us(w4a8_h16)
         t32 = per_call_us(w4a8_g32)
-        out["decode"][f"m{M}"] = dict(w4a8_linear_us=t4, w8a8_linear_us=t8, bf16_mm_us=tb,
+        ta16 = per_call_us(w4a16)
+        out["decode"][f"m{M}"] = dict(w4a8_linear_us=t4, w8a8_linear_us=t8, bf16_mm_us=tb, w4a16_gemm_us=ta16,
                                       w4a8_fp16_scales_linear_us=t16, w4a8_g32_linear_us=t32,
+                                      w4a16_kernel=L.w4a16_kernel_name(d, M),
                                       w4a8_vs_w8a8=t8 / t4, w4a8_vs_bf16=tb / t4,
                                       w8a8_weight_gbs=(K * N + K // cfg.group_size * N * 4) / (t8 * 1e-6) / 1e9,
                                       bf16_weight_gbs=K * N * 2 / (tb * 1e-6) / 1e9)
@@ -524,6 +531,8 @@ def compare_leg(args, L, W, torch, dev):
         Wm = torch.from_numpy(Wf).to(dev).to(torch.bfloat16)
         p8 = L.desc(pc.K, pc.N, pc.group_size, False, bits=8)
         blob8 = torch.from_numpy(L.w4a8_pack(p8, Wf)).to(dev)
+        p4 = L.desc(pc.K, pc.N, pc.group_size, pc.asymmetric)
+        blob4 = torch.from_numpy(L.w4a8_pack(p4, Wf)).to(dev)
         del Wf
         Xq = torch.empty((pc.M, pc.K), dtype=torch.int8, device=dev)
         sx = torch.empty(pc.M, dtype=torch.float32, device=dev)
@@ -542,11 +551,14 @@ def compare_leg(args, L, W, torch, dev):
 
         ms_b = timed(lambda: torch.mm(X, Wm, out=Y))
         ms_8 = timed(lambda: L.w4a8_gemm(Xq, sx, blob8, p8, Y))
+        ms_a16 = timed(lambda: L.w4a16_gemm(X, blob4, p4, Y))
         ops = 2.0 * pc.M * pc.N * pc.K
         out["prefill"][pc.name] = dict(bf16_mm_ms=ms_b, bf16_tflops=ops / (ms_b * 1e-3) / 1e12,
                                        w8a8_gemm_ms=ms_8, w8a8_tops=ops / (ms_8 * 1e-3) / 1e12,
-                                       w8a8_kernel=L.w4a8_kernel_name(p8, pc.M))
-        del X, Wm, Y, Xq, sx, blob8
+                                       w8a8_kernel=L.w4a8_kernel_name(p8, pc.M),
+                                       w4a16_gemm_ms=ms_a16, w4a16_tflops=ops / (ms_a16 * 1e-3) / 1e12,
+                                       w4a16_kernel=L.w4a16_kernel_name(p4, pc.M))
+        del X, Wm, Y, Xq, sx, blob8, blob4
         torch.cuda.empty_cache()
     return out
 

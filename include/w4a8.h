@@ -241,6 +241,23 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob_dev,
 int w4a8_linear(const void* X_bf16, int M, int K, int ldx, const void* blob_dev, const w4a8_wdesc* d, void* Y,
                 int ldy, int out_dtype, int8_t* Xq, float* sx, void* stream);
 
+/* W4A16 sibling (P1 section 5.3 compares W4A16 with W8A8 and W4A8; P5 section 3.2: the
+ * weight-only path dequantizes inside the GEMM): Y = X W with the activations kept in bfloat16
+ * (no activation quantization) and the 4-bit codes of a W4A8 blob dequantized in registers,
+ *   Y[m, n] = sum_i s[i, n] * sum_{k in group i} X[m, k] * (q[k, n] - z[i, n]),
+ * accumulated in float32 on bfloat16 MFMA.
+ *   X_bf16   device bfloat16 [M, ldx], 16-byte aligned, ldx % 8 == 0, ldx >= K
+ *   blob_dev the same blob as w4a8_gemm: 4-bit codes, g in {64, 128}, float32 scales
+ *            (other formats: EUNSUPPORTED)
+ *   Y        device [M, ldy] bfloat16 or float32
+ * M <= 32 runs the streaming (decode) kernel, larger M the 128 x 128-tile kernel; M == 0 is a
+ * no-op.  EINVAL for M > 32 when 128 * ldx * 2 reaches 2^31 (32-bit activation offsets). */
+int w4a16_gemm(const void* X_bf16, int M, int ldx, const void* blob_dev, const w4a8_wdesc* d, void* Y,
+               int ldy, int out_dtype, void* stream);
+
+/* Name of the kernel variant w4a16_gemm resolves to for (d, M), or "unsupported". */
+const char* w4a16_kernel_name(const w4a8_wdesc* d, int M);
+
 /* Test export of the same main loop: INT32 per-group partial sums
  * P[m, n, i] = sum_{k in group i} Xq[m, k] (q[k, n] - z[i, n]) written to device
  * int32 [M, N, K/g].  (P3 "Correctness contract" item 3: the accumulator covers the

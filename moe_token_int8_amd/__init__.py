@@ -27,6 +27,7 @@ EXPORTED = [
     "w4a8_silu_mul_quant", "w4a8_moe_combine", "w4a8_moe_workspace_size", "w4a8_moe_forward",
     "w4a8_quant_act_static", "w4a8_moe_quant_static", "w4a8_silu_mul_quant_static",
     "w4a8_moe_static_workspace_size", "w4a8_moe_forward_static", "w4a8_moe_forward_sets", "w4a8_moe_forward_noalloc",
+    "w4a16_gemm", "w4a16_kernel_name",
     "w4a8_kernel_name", "w4a8_status_string", "w4a8_version",
 ]
 
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
             "w4a8_moe_forward_sets": (I, [P, P, P, I, I, ctypes.POINTER(ExpertSet), I, P, SZ, P, VP]),
             "w4a8_moe_forward_noalloc": (I, [P, P, P, I, I, I, P, SZ, DP, P, SZ, DP, P, VP]),
             "w4a8_kernel_name": (ctypes.c_char_p, [DP, I]),
+            "w4a16_gemm": (I, [P, I, I, P, DP, P, I, I, VP]),
+            "w4a16_kernel_name": (ctypes.c_char_p, [DP, I]),
             "w4a8_status_string": (ctypes.c_char_p, [I]),
             "w4a8_version": (I, []),
         }
@@ -252,6 +255,19 @@ def w4a8_linear(X, blob_dev, d: WDesc, Y, Xq, sx, out_dtype: int = W4A8_OUT_BF16
     M, K = X.shape
     _check(lib().w4a8_linear(_ptr(X), M, K, X.stride(0), _ptr(blob_dev), ctypes.byref(d), _ptr(Y), Y.stride(0),
                              int(out_dtype), _ptr(Xq), _ptr(sx), _stream(stream)), "w4a8_linear")
+
+
+def w4a16_gemm(X, blob_dev, d: WDesc, Y, out_dtype: int = W4A8_OUT_BF16, stream=None) -> None:
+    """W4A16 sibling: Y = X W with bfloat16 activations and the blob's 4-bit weights dequantized in
+    the kernel (no activation quantization)."""
+    _require_cuda(X, blob_dev, Y)
+    M = X.shape[0]
+    _check(lib().w4a16_gemm(_ptr(X), int(M), int(X.stride(0)), _ptr(blob_dev), ctypes.byref(d), _ptr(Y),
+                            int(Y.stride(0)), int(out_dtype), _stream(stream)), "w4a16_gemm")
+
+
+def w4a16_kernel_name(d: WDesc, M: int) -> str:
+    return lib().w4a16_kernel_name(ctypes.byref(d), int(M)).decode()
 
 
 def w4a8_gemm_partials(Xq, blob_dev, d: WDesc, P, stream=None) -> None:

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_library_exports_every_declared_symbol():
     hdr = open(os.path.join(ROOT, "include", "w4a8.h")).read()
     hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
-    declared = set(re.findall(r"\b(w4a8_[a-z0-9_]+)\s*\(", hdr))
+    declared = set(re.findall(r"\b(w4a(?:8|16)_[a-z0-9_]+)\s*\(", hdr))
     assert declared, "no declarations parsed"
     lib = ctypes.CDLL(L.LIB_PATH)
     for name in sorted(declared):
@@ -553,3 +553,25 @@ def test_noalloc_forward_rejects_layers_past_its_scratch():
     assert L.w4a8_moe_workspace_size(1024, 6, 4096, 1408, 64) > 64 << 20
     assert call(1024) == L.W4A8_ESIZE
     assert call(0) == L.W4A8_OK
+
+
+def test_w4a16_checks_and_names():
+    """The W4A16 entry point takes the W4A8 blob's 4-bit formats with g in {64, 128} and float32
+    scales; other formats are EUNSUPPORTED, bad arguments EINVAL, all before any launch."""
+    lib = L.lib()
+    fake = 0x10000
+    d = L.desc(4096, 14336, 128, False)
+    assert L.w4a16_kernel_name(d, 1) == "w4a16_decode_m16_sym_g128"
+    assert L.w4a16_kernel_name(L.desc(4096, 64, 64, True), 32) == "w4a16_decode_m32_asym_g64"
+    assert L.w4a16_kernel_name(d, 33) == "w4a16_prefill_sym_g128"
+    for bad in (L.desc(4096, 64, 32, False), L.desc(4096, 64, 256, False), L.desc(4096, 64, 128, False, bits=8),
+                L.desc(4096, 64, 128, False, scale_bits=16)):
+        assert L.w4a16_kernel_name(bad, 4) == "unsupported"
+        assert lib.w4a16_gemm(fake, 4, 4096, fake, ctypes.byref(bad), fake, 64, 0, None) == L.W4A8_EUNSUPPORTED
+    E = L.W4A8_EINVAL
+    assert lib.w4a16_gemm(fake, 0, 4096, fake, ctypes.byref(d), fake, 14336, 0, None) == L.W4A8_OK
+    assert lib.w4a16_gemm(fake, 4, 4000, fake, ctypes.byref(d), fake, 14336, 0, None) == E       # ldx < K
+    assert lib.w4a16_gemm(fake, 4, 4100, fake, ctypes.byref(d), fake, 14336, 0, None) == E       # ldx % 8
+    assert lib.w4a16_gemm(0x10002, 4, 4096, fake, ctypes.byref(d), fake, 14336, 0, None) == E    # alignment
+    assert lib.w4a16_gemm(fake, 4, 4096, fake, ctypes.byref(d), fake, 14000, 0, None) == E       # ldy < N
+    assert lib.w4a16_gemm(fake, 4, 4096, fake, ctypes.byref(d), fake, 14336, 7, None) == E       # out dtype
