@@ -1,0 +1,246 @@
+// Grouped (MoE) W4A8 GEMM for K <= 4096: every expert, hot or cold, in one streaming launch.
+//
+// Sources (cited with the page's own section names):
+//   P1 "Kimi 2.7 MoE: from 4-bit storage to INT8 (W4A8)" (pwwt.cn), section 4.4 step 4: the grouped
+//      expert GEMM over router-sorted tokens, "the performance key"; section 5.2: the 4-bit layout
+//      matches the MFMA operand layout.
+//   P2 "Kimi 2.7 MoE W4A8 ... deployment notes" (xdnf.cn), section 4.2: MoE layers are bound by
+//      weight movement, not arithmetic.
+//
+// A workgroup owns one row tile of one expert (up to 32 sorted rows, gathered from the token rows
+// when `gather` is set) and 16 column tiles (256 columns).  It stages the tile's activation rows
+// in LDS once, with coalesced 16-byte loads, and then streams its columns in CG groups of NT tiles:
+// wave (t, q) owns tile t of the group over the K-slice q (SBN superblocks), the weights, scales
+// and zero points of two groups are in flight at a time (double-buffered registers, fully
+// unrolled so every wait is per register), and each group's KW slice sums are added in slice
+// order through LDS before the row scale and the store.  An expert's weights are therefore read
+// once per row tile and its activations once per 256 columns; experts with no rows launch nothing
+// that reads their weights.
+#include <hip/hip_runtime.h>
+
+#include "w4a8_device.h"
+#include "w4a8_internal.h"
+
+namespace w4a8 {
+
+constexpr int MST_TILES = 16;            // column tiles per workgroup
+
+template <int MS, int NT, int KW>
+struct MoeStreamShape {
+    static constexpr int MT = 16 * MS;
+    static constexpr int NTHR = 64 * NT * KW;                  // 512
+    static constexpr int CG = MST_TILES / NT;                  // column groups
+    static constexpr size_t LDS_RED = size_t(KW - 1) * NT * MS * 4 * 64 * 4;
+    static size_t lds(int K) { return size_t(MT) * size_t(K + 16) + LDS_RED; }
+    static_assert(NTHR == 512, "8 waves: two per SIMD, so each has 256 registers");
+};
+
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16>
+__global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
+    using S = MoeStreamShape<MS, NT, KW>;
+    constexpr int MT = S::MT, NTHR = S::NTHR, CG = S::CG, NV = MS * 4;
+    // activation pieces (16 bytes) per thread: the K <= KW * SBN * 128 rows of a full tile
+    constexpr int APT = (MT * KW * SBN * 8 + NTHR - 1) / NTHR;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int K = a.K, ROWB = K + 16;
+    float* red = reinterpret_cast<float*>(smem + size_t(MT) * ROWB);
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t = wave % NT, q = wave / NT;
+    const int ntiles = (a.N + 15) / 16;
+    const int nsb = K / SB_K;
+
+    const TileRows tr = moe_tile<MT>(a, blockIdx.y, lane);
+    if (tr.expert < 0) return;                                   // uniform over the workgroup
+    const int rbeg = tr.rbeg, nrows = tr.rend - tr.rbeg;
+    const uint8_t* blob = a.blob + size_t(tr.expert) * a.expert_stride;
+    const uint8_t* codes = blob + a.codes_off;
+    const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
+    const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(blob + a.scales_off);
+    const uint8_t* zeros = blob + a.zeros_off;
+
+    // 1. the tile's activation rows, requested first (they gate the first MFMA)
+    const int ppr = nsb * 8;                                     // pieces per row
+    uint4 xv[APT];
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+        const int p = tid + i * NTHR, row = p / ppr, c = p - row * ppr;
+        xv[i] = make_uint4(0, 0, 0, 0);
+        if (row < nrows) {
+            const int src = a.gather ? gather_src(a, rbeg + row) : rbeg + row;
+            if (src >= 0) xv[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(src) * K + c * 16);
+        }
+    }
+    // row scales of the rows this lane stores (slice-0 waves store)
+    float sxr[MS][4];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = ms * 16 + 4 * (lane >> 4) + i;
+            sxr[ms][i] = 0.0f;
+            if (q == 0 && row < nrows) {
+                const int src = a.gather ? gather_src(a, rbeg + row) : rbeg + row;
+                sxr[ms][i] = src >= 0 ? a.sx[src] : 0.0f;
+            }
+        }
+
+    // 2. per column group g (register set g % 2): scales, zero points and weight superblocks
+    const int s0 = q * SBN;
+    float sc[2][SBN][GPS];
+    uint32_t zq[2][SBN][GPS];
+    uint4 bq[2][SBN];
+    auto tile_of = [&](int g) { return (int(blockIdx.x) * CG + g) * NT + t; };
+    auto load_group = [&](const int g, const int set) __attribute__((always_inline)) {
+        const uint32_t tc = uint32_t(min(tile_of(g), ntiles - 1));
+#pragma unroll
+        for (int s = 0; s < SBN; ++s) {
+            const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
+#pragma unroll
+            for (int gi = 0; gi < GPS; ++gi) {
+                const uint32_t mi = (tc * uint32_t(a.G) + sb * GPS + gi) * 16u + uint32_t(lane & 15);
+                sc[set][s][gi] = H16 ? f16_to_f32(scales16[mi]) : scales[mi];
+                zq[set][s][gi] = ASYM ? uint32_t(zeros[mi]) : 0u;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < SBN; ++s) {
+            const uint32_t sb = uint32_t(min(s0 + s, nsb - 1));
+            bq[set][s] = stream_load(codes + ((tc * uint32_t(nsb) + sb) * 1024u + uint32_t(lane) * 16u));
+        }
+    };
+    load_group(0, 0);
+    asm volatile("" ::: "memory");                               // keep the stream issued here
+
+    // 3. activations to LDS (rows past the tile are not written; their outputs are never stored);
+    //    the second group is requested once the activation registers are free
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+        const int p = tid + i * NTHR, row = p / ppr, c = p - row * ppr;
+        if (row < nrows) *reinterpret_cast<uint4*>(smem + row * ROWB + c * 16) = xv[i];
+    }
+    if (CG > 1) load_group(1, 1);
+    asm volatile("" ::: "memory");
+    lds_barrier();
+
+    // 4. column groups, two at a time (register sets 0 and 1); the pair loop is not unrolled, so
+    //    only one copy of each set's code exists
+    const v4i zero4 = {0, 0, 0, 0};
+    auto group = [&](const int g, const int set) __attribute__((always_inline)) {
+        float accf[MS][4];
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accf[ms][i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < SBN; ++s) {
+            const int sb = s0 + s;
+            if (sb >= nsb) break;                                // uniform per wave
+            v4i acc[MS];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int gi = GPS == 2 ? h : 0;
+                const uint32_t zc = ASYM ? (128u - zq[set][s][gi]) * 0x01010101u : 0u;
+                const v4i b = unpack_b<ASYM>(h ? bq[set][s].z : bq[set][s].x, h ? bq[set][s].w : bq[set][s].y, zc);
+                const bool first = GPS == 2 || h == 0;
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) {
+                    const uint4 av = *reinterpret_cast<const uint4*>(
+                        smem + (ms * 16 + (lane & 15)) * ROWB + sb * SB_K + h * 64 + 16 * (lane >> 4));
+                    const v4i A = v4i{int(av.x), int(av.y), int(av.z), int(av.w)};
+                    acc[ms] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, b, first ? zero4 : acc[ms], 0, 0, 0);
+                }
+                if (GPS == 2 || h == 1) {
+                    const float scl = ASYM ? sc[set][s][gi] : sc[set][s][gi] * 0.0625f;
+#pragma unroll
+                    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) accf[ms][i] = fmaf(float(acc[ms][i]), scl, accf[ms][i]);
+                }
+            }
+        }
+        // the register set of this group is free: request group g + 2 into it
+        if (g + 2 < CG) {
+            load_group(g + 2, set);
+            asm volatile("" ::: "memory");
+        }
+        // slice-ordered reduction through LDS, row scale, store
+        if (q > 0) {
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) red[(((q - 1) * NT + t) * NV + ms * 4 + i) * 64 + lane] = accf[ms][i];
+        }
+        lds_barrier();
+        if (q == 0) {
+#pragma unroll
+            for (int w = 1; w < KW; ++w)
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) accf[ms][i] += red[(((w - 1) * NT + t) * NV + ms * 4 + i) * 64 + lane];
+            const int tile = tile_of(g);
+            const int col = tile * 16 + (lane & 15);
+            if (tile < ntiles && col < a.N) {
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = ms * 16 + 4 * (lane >> 4) + i;
+                        if (row >= nrows) continue;
+                        const float y = accf[ms][i] * sxr[ms][i];
+                        const size_t yi = size_t(rbeg + row) * a.ldy + col;
+                        if (a.out_f32)
+                            reinterpret_cast<float*>(a.Y)[yi] = y;
+                        else
+                            reinterpret_cast<uint16_t*>(a.Y)[yi] = uint16_t(f32_to_bf16_rne(y));
+                    }
+            }
+        }
+        if (g + 1 < CG) lds_barrier();                           // the reduction area is reused
+    };
+#pragma unroll
+    for (int g = 0; g < CG; ++g) group(g, g & 1);
+}
+
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16>
+static void launch_moe_stream_t(const GemmArgs& a, int slots, hipStream_t s) {
+    using S = MoeStreamShape<MS, NT, KW>;
+    auto kern = gemm_moe_stream_kernel<MS, NT, KW, SBN, GPS, ASYM, H16>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       int(S::lds(KW * SBN * SB_K)));
+    (void)attr;
+    const int ntiles = (a.N + 15) / 16;
+    kern<<<dim3((ntiles + MST_TILES - 1) / MST_TILES, slots), dim3(S::NTHR), S::lds(a.K), s>>>(a);
+}
+
+template <int MS, int GPS, bool ASYM, bool H16>
+static void launch_moe_stream_k(const GemmArgs& a, int slots, hipStream_t s) {
+    const int nsb = a.K / SB_K;
+    // 4 slices of SBN superblocks cover K (up to 32 superblocks)
+    if (nsb <= 8) launch_moe_stream_t<MS, 2, 4, 2, GPS, ASYM, H16>(a, slots, s);
+    else if (nsb <= 12) launch_moe_stream_t<MS, 2, 4, 3, GPS, ASYM, H16>(a, slots, s);
+    else if (nsb <= 16) launch_moe_stream_t<MS, 2, 4, 4, GPS, ASYM, H16>(a, slots, s);
+    else if (nsb <= 24) launch_moe_stream_t<MS, 2, 4, 6, GPS, ASYM, H16>(a, slots, s);
+    else launch_moe_stream_t<MS, 2, 4, 8, GPS, ASYM, H16>(a, slots, s);
+}
+
+bool moe_stream_fits(int K, int gps) { return K <= 32 * SB_K && (gps == 1 || gps == 2); }
+
+void launch_moe_stream(const GemmArgs& a, int mt, int gps, bool asym, int slots, hipStream_t s) {
+#define W4A8_MST(MS_, GPS_, ASYM_)                                                     \
+    do {                                                                               \
+        if (a.h16) launch_moe_stream_k<MS_, GPS_, ASYM_, true>(a, slots, s);           \
+        else launch_moe_stream_k<MS_, GPS_, ASYM_, false>(a, slots, s);                \
+    } while (0)
+    if (mt == 16) {
+        if (gps == 1) { if (asym) W4A8_MST(1, 1, true); else W4A8_MST(1, 1, false); }
+        else { if (asym) W4A8_MST(1, 2, true); else W4A8_MST(1, 2, false); }
+    } else {
+        if (gps == 1) { if (asym) W4A8_MST(2, 1, true); else W4A8_MST(2, 1, false); }
+        else { if (asym) W4A8_MST(2, 2, true); else W4A8_MST(2, 2, false); }
+    }
+#undef W4A8_MST
+}
+
+}  // namespace w4a8

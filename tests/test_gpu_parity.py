@@ -394,12 +394,13 @@ def test_moe_gemm_grouped_matches_per_expert_oracle():
     _print(check_float_output(Y, Ybf, Y64))
 
 
-@pytest.mark.parametrize("g,asym", [(64, True), (128, False)])
-def test_moe_gemm_hot_expert_paths(g, asym):
+@pytest.mark.parametrize("g,asym,K", [(64, True, 256), (128, False, 256), (64, True, 4608), (128, False, 4608)])
+def test_moe_gemm_hot_expert_paths(g, asym, K):
     """Grouped GEMM where expert 0 owns 280 routed rows (two 256-row MFMA tiles, the second
-    ragged), expert 1 about 160 (one tile) and the others fewer than 128 (the streaming
-    kernel); with and without the row gather."""
-    T, k, E, K, N = 300, 2, 5, 256, 96
+    ragged), expert 1 about 160 (one tile) and the others fewer than 128; with and without the row
+    gather.  The others run on the grouped streaming kernel (K = 256) or on the streaming decode
+    kernel (K = 4608)."""
+    T, k, E, N = 300, 2, 5, 96
     t = np.arange(T)
     ids = np.stack([np.where(t < 280, 0, 1 + t % 4), np.where(t < 150, 1, 2 + t % 3)], axis=1).astype(np.int32)
     dup = ids[:, 0] == ids[:, 1]
