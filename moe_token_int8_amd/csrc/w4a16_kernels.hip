@@ -271,26 +271,27 @@ static void launch_a16_decode(const A16Args& a, int Np, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------------------------
-// Prefill form (M > 32).  Workgroup tile 128 rows x 128 columns, 4 waves of 64 x 64 (4 x 4 MFMA
-// tiles of 16 x 16).  Per 128-deep superblock the workgroup stages the activation tile in LDS
+// Prefill form (M > 32).  Workgroup tile 128 rows x 128 columns, 8 waves (2 x 4) of 64 x 32 (4 x 2
+// MFMA tiles of 16 x 16).  Per 128-deep superblock the workgroup stages the activation tile in LDS
 // (bfloat16, operand order, double buffered, loads one superblock ahead) with each row's group
-// sums; each wave loads the packed codes of its 4 column tiles itself (16 bytes per lane each, the
+// sums; each wave loads the packed codes of its 2 column tiles itself (16 bytes per lane each, the
 // two waves of a column block share them through L1) and turns them into operands in registers.
 // ------------------------------------------------------------------------------------
-constexpr int A16P_BM = 128, A16P_BN = 128, A16P_THREADS = 256;
+constexpr int A16P_BM = 128, A16P_BN = 128, A16P_THREADS = 512;
 constexpr int A16P_ROWB = SB_K * 2 + 16;                       // LDS row stride in bytes
 constexpr int A16P_ABYTES = A16P_BM * A16P_ROWB;               // 34816
 constexpr int A16P_SBYTES = 2 * A16P_BM * 4;                   // group sums, up to 2 groups
 constexpr int A16P_STAGE = A16P_ABYTES + A16P_SBYTES;
 constexpr int A16P_LDS = 2 * A16P_STAGE;
-constexpr int A16P_APT = A16P_BM * 16 / A16P_THREADS;          // 16-byte pieces per thread: 8
+constexpr int A16P_APT = A16P_BM * 16 / A16P_THREADS;          // 16-byte pieces per thread: 4
+constexpr int A16P_WC = 2;                                     // column tiles per wave
 
 template <int GPS, bool ASYM>
 __global__ __launch_bounds__(A16P_THREADS) void gemm_a16_prefill_kernel(A16Args a) {
     constexpr int PPG = (GPS == 2 ? 64 : 128) / 8;
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int mtiles = (a.M + A16P_BM - 1) / A16P_BM;
     const int mt = blockIdx.x % mtiles, nt = blockIdx.x / mtiles;   // consecutive workgroups share weights
     const int m0 = mt * A16P_BM;
@@ -299,11 +300,11 @@ __global__ __launch_bounds__(A16P_THREADS) void gemm_a16_prefill_kernel(A16Args 
     const uint8_t* codes = a.blob + a.codes_off;
     const float* scales = reinterpret_cast<const float*>(a.blob + a.scales_off);
     const uint8_t* zeros = a.blob + a.zeros_off;
-    // this wave's 4 column tiles (clamped to the last one; their outputs are not stored)
-    uint32_t boff[4], moff[4];
+    // this wave's column tiles (clamped to the last one; their outputs are not stored)
+    uint32_t boff[A16P_WC], moff[A16P_WC];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint32_t tl = uint32_t(min(nt * 8 + wn * 4 + c, ntl16 - 1));
+    for (int c = 0; c < A16P_WC; ++c) {
+        const uint32_t tl = uint32_t(min(nt * 8 + wn * A16P_WC + c, ntl16 - 1));
         boff[c] = tl * uint32_t(nsb) * 1024u + uint32_t(lane) * 16u;
         moff[c] = tl * uint32_t(a.G) * 16u + uint32_t(lane & 15);
     }
@@ -336,13 +337,13 @@ __global__ __launch_bounds__(A16P_THREADS) void gemm_a16_prefill_kernel(A16Args 
         }
     };
     struct Meta {
-        uint4 b[4];
-        float s[4][GPS];
-        uint32_t z[4][GPS];
+        uint4 b[A16P_WC];
+        float s[A16P_WC][GPS];
+        uint32_t z[A16P_WC][GPS];
     };
     auto load_w = [&](Meta& m, int sb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < A16P_WC; ++c) {
             m.b[c] = *reinterpret_cast<const uint4*>(codes + (boff[c] + uint32_t(sb) * 1024u));
 #pragma unroll
             for (int gi = 0; gi < GPS; ++gi) {
@@ -353,11 +354,11 @@ __global__ __launch_bounds__(A16P_THREADS) void gemm_a16_prefill_kernel(A16Args 
         }
     };
 
-    float accf[4][4][4];
+    float accf[4][A16P_WC][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < A16P_WC; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) accf[r][c][i] = 0.0f;
 
@@ -377,12 +378,12 @@ __global__ __launch_bounds__(A16P_THREADS) void gemm_a16_prefill_kernel(A16Args 
         const float* gs = reinterpret_cast<const float*>(st + A16P_ABYTES);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            v4f acc[4][4];
+            v4f acc[4][A16P_WC];
 #pragma unroll
             for (int set = 0; set < 2; ++set) {
-                v8bf b[4];
+                v8bf b[A16P_WC];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                for (int c = 0; c < A16P_WC; ++c) {
                     const uint32_t w = set ? (h ? cur.b[c].w : cur.b[c].y) : (h ? cur.b[c].z : cur.b[c].x);
                     b[c] = b_operand<ASYM>(w);
                 }
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(A16P_THREADS) void gemm_a16_prefill_kernel(A16Args 
                     const v8bf av = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(ap));
                     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
+                    for (int c = 0; c < A16P_WC; ++c)
                         acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b[c], first ? zero : acc[r][c], 0, 0, 0);
                 }
             }
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(A16P_THREADS) void gemm_a16_prefill_kernel(A16Args 
                     const float4 g4 = *reinterpret_cast<const float4*>(gs + gi * A16P_BM + wm * 64 + r * 16 + 4 * (lane >> 4));
                     const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
+                    for (int c = 0; c < A16P_WC; ++c) {
                         const float C = ASYM ? float(16u + cur.z[c][gi]) : 24.0f;
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
@@ -417,11 +418,11 @@ __global__ __launch_bounds__(A16P_THREADS) void gemm_a16_prefill_kernel(A16Args 
             store_a(xv, stage ^ 1);                      // the other stage was last read before the barrier below
             cur = nxt;
         }
-        __syncthreads();
+        lds_barrier();                                   // LDS hand-off only: global loads may stay in flight
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int col = (nt * 8 + wn * 4 + c) * 16 + (lane & 15);
+    for (int c = 0; c < A16P_WC; ++c) {
+        const int col = (nt * 8 + wn * A16P_WC + c) * 16 + (lane & 15);
         if (col >= a.N) continue;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
