@@ -302,6 +302,26 @@ int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int 
                   size_t expert_stride, const w4a8_wdesc* d, void* Y, int out_dtype,
                   void* stream);
 
+/* Expert-grouped gate/up GEMM with the static SiLU-requant folded into its epilogue (P1
+ * section 8: fold the activation quantization into the GEMM; P1 section 3.2: static, calibrated
+ * activation scales, so the requantization needs no reduction over a row).  The blob holds the
+ * gate columns [0, I) and the up columns [I, 2I) of each expert (d->N = 2I, I % 16 == 0,
+ * EINVAL otherwise).  A workgroup computes gate column c and up column I + c side by side; each
+ * output is rounded to bfloat16 as w4a8_moe_gemm stores it, h = silu(g) * u is formed in float32
+ * and quantized with the scale s[e] of the row's expert (the rule of w4a8_quant_act_static),
+ * so Hq and sh equal those of w4a8_moe_gemm followed by w4a8_silu_mul_quant_static, bit for
+ * bit, without the [rows, 2I] bfloat16 intermediate.
+ *   Xq, sx, gather, k, expert_offsets, E, rows, src_rows, blobs_dev, expert_stride, d
+ *                  as for w4a8_moe_gemm
+ *   s              device float32 [E], static scales of h
+ *   Hq, sh         device int8 [rows, I], float32 [rows]
+ * Rows at or past expert_offsets[E] (no expert owns them) are not written.  Same checks and
+ * limits as w4a8_moe_gemm. */
+int w4a8_moe_gemm_silu_static(const int8_t* Xq, const float* sx, const int32_t* gather, int k,
+                              const int32_t* expert_offsets, int E, int rows, int src_rows,
+                              const void* blobs_dev, size_t expert_stride, const w4a8_wdesc* d,
+                              const float* s, int8_t* Hq, float* sh, void* stream);
+
 /* SiLU-gated expert activation + per-row INT8 requantization for the down projection
  * (P1 section 1 names SiLU; P1 section 3.1: per-expert activation scales).
  *   GU_bf16  device bfloat16 [R, 2I]: gate = columns [0, I), up = [I, 2I)
@@ -393,8 +413,9 @@ size_t w4a8_moe_static_workspace_size(int T, int k, int H, int I, int E);
 
 /* One MoE expert layer with static per-expert activation scales (P1 section 3.1 and 3.2:
  * calibrated scales, one per expert, for decode).  The steps of w4a8_moe_forward, with the
- * two quantizations replaced: moe_align -> moe_quant_static(X, s_gu) -> moe_gemm(gate/up,
- * rows already sorted) -> silu_mul_quant_static(s_dn) -> moe_gemm(down) -> moe_combine.
+ * two quantizations replaced: moe_align -> moe_quant_static(X, s_gu) -> moe_gemm_silu_static
+ * (gate/up GEMM, rows already sorted, with the SiLU-requant by s_dn in its epilogue) ->
+ * moe_gemm(down) -> moe_combine.
  *   s_gu, s_dn  device float32 [E]: scale of each expert's gate/up and down inputs
  *   workspace   device, >= w4a8_moe_static_workspace_size(T, k, H, I, E) bytes, 256-aligned
  * Other arguments and errors as w4a8_moe_forward. */

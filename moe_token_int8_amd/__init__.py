@@ -24,6 +24,7 @@ EXPORTED = [
     "w4a8_packed_size", "w4a8_pack", "w4a8_pack_codes", "w4a8_unpack_codes", "w4a8_blob_check",
     "w4a8_quant_act", "w4a8_quant_act_smooth", "w4a8_gemm", "w4a8_linear", "w4a8_gemm_partials", "w4a8_moe_align",
     "w4a8_moe_gemm",
+    "w4a8_moe_gemm_silu_static",
     "w4a8_silu_mul_quant", "w4a8_moe_combine", "w4a8_moe_workspace_size", "w4a8_moe_forward",
     "w4a8_quant_act_static", "w4a8_moe_quant_static", "w4a8_silu_mul_quant_static",
     "w4a8_moe_static_workspace_size", "w4a8_moe_forward_static", "w4a8_moe_forward_sets", "w4a8_moe_forward_noalloc",
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "w4a8_gemm_partials": (I, [P, I, P, DP, P, VP]),
             "w4a8_moe_align": (I, [P, I, I, I, P, P, P, VP]),
             "w4a8_moe_gemm": (I, [P, P, P, I, P, I, I, I, P, SZ, DP, P, I, VP]),
+            "w4a8_moe_gemm_silu_static": (I, [P, P, P, I, P, I, I, I, P, SZ, DP, P, P, P, VP]),
             "w4a8_silu_mul_quant": (I, [P, I, I, P, P, VP]),
             "w4a8_moe_combine": (I, [P, P, P, I, I, I, P, VP]),
             "w4a8_moe_workspace_size": (SZ, [I, I, I, I, I]),
@@ -292,6 +294,19 @@ def w4a8_moe_gemm(Xq, sx, gather, k: int, expert_offsets, E: int, rows: int, blo
     _check(lib().w4a8_moe_gemm(_ptr(Xq), _ptr(sx), _ptr(gather), int(k), _ptr(expert_offsets), int(E), int(rows),
                                src_rows, _ptr(blobs_dev), int(expert_stride), ctypes.byref(d), _ptr(Y),
                                int(out_dtype), _stream(stream)), "w4a8_moe_gemm")
+
+
+def w4a8_moe_gemm_silu_static(Xq, sx, gather, k: int, expert_offsets, E: int, rows: int, blobs_dev,
+                              expert_stride: int, d: WDesc, s, Hq, sh, stream=None) -> None:
+    """Grouped gate/up GEMM with the static SiLU-requant in its epilogue: Hq [rows, N/2], sh [rows]."""
+    _require_cuda(Xq, sx, gather, expert_offsets, blobs_dev, s, Hq, sh)
+    src_rows = int(Xq.shape[0])
+    if sx.numel() < src_rows:
+        raise ValueError("sx must hold one scale per row of Xq")
+    _check(lib().w4a8_moe_gemm_silu_static(_ptr(Xq), _ptr(sx), _ptr(gather), int(k), _ptr(expert_offsets), int(E),
+                                           int(rows), src_rows, _ptr(blobs_dev), int(expert_stride), ctypes.byref(d),
+                                           _ptr(s), _ptr(Hq), _ptr(sh), _stream(stream)),
+           "w4a8_moe_gemm_silu_static")
 
 
 def w4a8_silu_mul_quant(GU, Hq, sh, stream=None) -> None:

@@ -25,8 +25,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unus
 
 
 def build(verbose: bool = False) -> str:
-    objs = []
+    objs, procs = [], []
     os.makedirs(os.path.join(PKG, "_build"), exist_ok=True)
+    # the translation units compile concurrently (one process each)
     for src in HIP_SOURCES + HOST_SOURCES:
         obj = os.path.join(PKG, "_build", src + ".o")
         if src in HIP_SOURCES:
@@ -35,8 +36,11 @@ def build(verbose: bool = False) -> str:
             cmd = [CXX, *COMMON, "-pthread", "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((subprocess.Popen(cmd), cmd))
         objs.append(obj)
+    failed = [cmd for p, cmd in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "-pthread", *DEVICE_FLAGS, *objs, "-o", tmp]
     if verbose:

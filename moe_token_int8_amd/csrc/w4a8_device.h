@@ -47,6 +47,90 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ------------------------------------------------------------------------------------
+// per-row INT8 quantization rule (P1 section 3.3; P5 section 8.3) and the SiLU-gated product
+// ------------------------------------------------------------------------------------
+// One element of the per-token rule q = clamp(rint(fl32(x / d)), -127, 127), branch free.
+// inv = RN(1/d) comes from one IEEE division per row.  q0 = RN(x * inv) is within 1.5 ulp of
+// x/d; one Newton correction q1 = RN(q0 + inv * (x - d * q0)) (residual through fma) has an
+// error far below 1 ulp before rounding, so q1 is faithful; by Markstein's theorem a second
+// correction from a faithful q1 with the correctly rounded reciprocal inv gives exactly
+// RN(x / d), the IEEE float32 quotient.  Rows with a tiny divisor (fast == false, uniform per
+// row) use the IEEE division directly.
+__device__ __forceinline__ int quant_one(float x, float d, float inv, bool fast) {
+    float q;
+    if (fast) {
+        const float q0 = x * inv;
+        const float q1 = fmaf(fmaf(-d, q0, x), inv, q0);
+        q = rintf(fmaf(fmaf(-d, q1, x), inv, q1));
+    } else {
+        q = rintf(x / d);
+    }
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return (int)q;
+}
+
+struct RowScale {
+    float s, d, inv;
+    bool finite, fast;
+    float lim;      // static scales: values are clamped to +-lim = 128 d before the division
+    bool huge;      // static scales: 128 d overflows (d > 2^120), lim is FLT_MAX
+};
+
+// Scale of a row from the bit pattern of its abs-max.  With UNIFORM (the default) amax_bits
+// must be the same in every lane of the wave: it is broadcast from lane 0 so that the scale,
+// and the branch on `fast`, are wave-uniform.
+template <bool UNIFORM = true>
+__device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
+    if (UNIFORM) amax_bits = __builtin_amdgcn_readfirstlane(amax_bits);
+    RowScale r;
+    r.finite = amax_bits < 0x7f800000u;
+    const float amax = __uint_as_float(amax_bits);
+    r.s = r.finite ? amax / 127.0f : __uint_as_float(0x7fc00000u);
+    r.d = (r.finite && r.s > 0.0f) ? r.s : 1.0f;
+    r.inv = 1.0f / r.d;
+    r.fast = r.d >= 1e-30f;
+    return r;
+}
+
+// A given scale s: codes are produced only for a finite, positive s (otherwise all zero).
+__device__ __forceinline__ RowScale static_row_scale(float s) {
+    RowScale r;
+    r.s = s;
+    r.finite = s > 0.0f && s <= 3.40282347e38f;
+    r.d = r.finite ? s : 1.0f;
+    r.inv = 1.0f / r.d;
+    r.fast = r.d >= 1e-30f;
+    r.huge = r.d > 1.329228e36f;                         // 2^120
+    r.lim = r.huge ? 3.40282347e38f : 128.0f * r.d;
+    return r;
+}
+
+// clamp(rint(fl32(x / d)), -127, 127) for any x.  Values are first limited to +-lim = 128 d
+// (one med3; exact, a power-of-two multiple): every such value still saturates, +-Inf
+// included, and quant_one's quotient stays finite.  NaN gives 0.  With d > 2^120 (lim is
+// FLT_MAX there) +-Inf is set to +-127 explicitly.
+template <bool HUGE = true>
+__device__ __forceinline__ int quant_static_one(float x, const RowScale& r) {
+    int q = quant_one(__builtin_amdgcn_fmed3f(x, -r.lim, r.lim), r.d, r.inv, r.fast);
+    if (x != x) q = 0;
+    if (HUGE && r.huge && fabsf(x) > 3.40282347e38f) q = x > 0.0f ? 127 : -127;
+    return q;
+}
+
+// silu(g) * u in float32 (P1 section 1: the expert MLP's gated activation).  Every path that
+// forms h calls this one definition, so fused and unfused paths agree bit for bit.
+__device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
+
+// One code of the static SiLU-requant (P1 section 3.2: a calibrated scale per expert, so no row
+// reduction): the gate and up GEMM outputs are first rounded to bfloat16, the precision in which
+// the unfused chain stores them, then h = silu(g) * u is quantized with the expert's scale.
+__device__ __forceinline__ int silu_static_code(float yg, float yu, const RowScale& rs) {
+    if (!rs.finite) return 0;
+    const float h = silu_mul(bf16_to_f32(f32_to_bf16_rne(yg)), bf16_to_f32(f32_to_bf16_rne(yu)));
+    return quant_static_one(h, rs);
+}
+
+// ------------------------------------------------------------------------------------
 // GEMM arguments, operand unpacking and the grouped (MoE) tile mapping
 // ------------------------------------------------------------------------------------
 enum { MODE_OUT = 0, MODE_PARTIALS = 1 };
@@ -70,7 +154,24 @@ struct GemmArgs {
     int E;
     int moe_lo, moe_hi;       // MoE: this launch serves the experts with moe_lo <= rows < moe_hi
     int h16;                  // binary16 group scales (selects the H16 kernels)
+    // MoE gate/up with the static SiLU-requant epilogue (when Hq is set): blob columns c and
+    // pair_n + c are the gate and up outputs of column c of h.  A workgroup computes both side
+    // by side, and instead of Y it writes the codes Hq [M, pair_n] and the row scales sh [M]
+    // (= s_dn[e] for every row of expert e).
+    int8_t* Hq;
+    float* sh;
+    const float* s_dn;
+    int pair_n;
 };
+
+// Blob column tile of tile slot l (0 <= l < n) of a workgroup whose slots start at tile `first`.
+// Unpaired: first + l.  Paired (a.Hq set): the first n / 2 slots are the gate tiles
+// first / 2 + l, the rest the matching up tiles pair_n / 16 + first / 2 + l - n / 2.
+__device__ __forceinline__ int pair_tile(const GemmArgs& a, int first, int l, int n) {
+    if (!a.Hq) return first + l;
+    const int g0 = first / 2;
+    return l < n / 2 ? g0 + l : a.pair_n / 16 + g0 + l - n / 2;
+}
 
 // Unpack two packed words (16 codes of one column) into one MFMA B operand.
 // Symmetric: two's-complement nibbles moved to the high half of each byte -> 16 * q

@@ -46,49 +46,6 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red, int
     return r;
 }
 
-// One element of the per-token rule q = clamp(rint(fl32(x / d)), -127, 127), branch free.
-// inv = RN(1/d) comes from one IEEE division per row.  q0 = RN(x * inv) is within 1.5 ulp of
-// x/d; one Newton correction q1 = RN(q0 + inv * (x - d * q0)) (residual through fma) has an
-// error far below 1 ulp before rounding, so q1 is faithful; by Markstein's theorem a second
-// correction from a faithful q1 with the correctly rounded reciprocal inv gives exactly
-// RN(x / d), the IEEE float32 quotient.  Rows with a tiny divisor (fast == false, uniform per
-// row) use the IEEE division directly.
-__device__ __forceinline__ int quant_one(float x, float d, float inv, bool fast) {
-    float q;
-    if (fast) {
-        const float q0 = x * inv;
-        const float q1 = fmaf(fmaf(-d, q0, x), inv, q0);
-        q = rintf(fmaf(fmaf(-d, q1, x), inv, q1));
-    } else {
-        q = rintf(x / d);
-    }
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (int)q;
-}
-
-struct RowScale {
-    float s, d, inv;
-    bool finite, fast;
-    float lim;      // static scales: values are clamped to +-lim = 128 d before the division
-    bool huge;      // static scales: 128 d overflows (d > 2^120), lim is FLT_MAX
-};
-
-// Scale of a row from the bit pattern of its abs-max.  With UNIFORM (the default) amax_bits
-// must be the same in every lane of the wave: it is broadcast from lane 0 so that the scale,
-// and the branch on `fast`, are wave-uniform.
-template <bool UNIFORM = true>
-__device__ __forceinline__ RowScale row_scale(uint32_t amax_bits) {
-    if (UNIFORM) amax_bits = __builtin_amdgcn_readfirstlane(amax_bits);
-    RowScale r;
-    r.finite = amax_bits < 0x7f800000u;
-    const float amax = __uint_as_float(amax_bits);
-    r.s = r.finite ? amax / 127.0f : __uint_as_float(0x7fc00000u);
-    r.d = (r.finite && r.s > 0.0f) ? r.s : 1.0f;
-    r.inv = 1.0f / r.d;
-    r.fast = r.d >= 1e-30f;
-    return r;
-}
-
 // ------------------------------------------------------------------------------------
 // per-token INT8 activation quantization (P1 section 3.3, P5 section 8.3)
 // One 256-thread workgroup per row; each thread holds IT x 8 bf16 values in registers
@@ -186,31 +143,6 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offs, i
     return lo;
 }
 
-// A given scale s: codes are produced only for a finite, positive s (otherwise all zero).
-__device__ __forceinline__ RowScale static_row_scale(float s) {
-    RowScale r;
-    r.s = s;
-    r.finite = s > 0.0f && s <= 3.40282347e38f;
-    r.d = r.finite ? s : 1.0f;
-    r.inv = 1.0f / r.d;
-    r.fast = r.d >= 1e-30f;
-    r.huge = r.d > 1.329228e36f;                         // 2^120
-    r.lim = r.huge ? 3.40282347e38f : 128.0f * r.d;
-    return r;
-}
-
-// clamp(rint(fl32(x / d)), -127, 127) for any x.  Values are first limited to +-lim = 128 d
-// (one med3; exact, a power-of-two multiple): every such value still saturates, +-Inf
-// included, and quant_one's quotient stays finite.  NaN gives 0.  With d > 2^120 (lim is
-// FLT_MAX there) +-Inf is set to +-127 explicitly.
-template <bool HUGE = true>
-__device__ __forceinline__ int quant_static_one(float x, const RowScale& r) {
-    int q = quant_one(__builtin_amdgcn_fmed3f(x, -r.lim, r.lim), r.d, r.inv, r.fast);
-    if (x != x) q = 0;
-    if (HUGE && r.huge && fabsf(x) > 3.40282347e38f) q = x > 0.0f ? 127 : -127;
-    return q;
-}
-
 // Row r of Xq quantizes source row src of X with the scale s[e]: src = r (gather == NULL) or
 // gather[r] / k; e = 0 (offs == NULL) or the expert that owns sorted row r.  Rows no expert
 // owns (r >= offs[E]: routing ids outside [0, E)) and gathered rows outside [0, T) get zero
@@ -299,9 +231,7 @@ __global__ __launch_bounds__(256) void silu_quant_kernel(const uint16_t* __restr
         for (int j = 0; j < 8; ++j) {
             const uint32_t gb = (j & 1) ? (g4[j >> 1] >> 16) : (g4[j >> 1] & 0xffffu);
             const uint32_t ub = (j & 1) ? (u4[j >> 1] >> 16) : (u4[j >> 1] & 0xffffu);
-            const float g = bf16_to_f32(gb), u = bf16_to_f32(ub);
-            const float sg = g / (1.0f + expf(-g));
-            h[it][j] = sg * u;
+            h[it][j] = silu_mul(bf16_to_f32(gb), bf16_to_f32(ub));
             amax = max(amax, __float_as_uint(h[it][j]) & 0x7fffffffu);
         }
     }
@@ -398,12 +328,14 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = wave % NT, q = wave / NT;
     const int ntiles = (a.N + 15) / 16;
-    const int tile = blockIdx.x * NT + t;
+    // paired form (grouped, static SiLU-requant epilogue): tiles t < NT / 2 are gate tiles, the
+    // others their up tiles
+    const int tile = MOE ? pair_tile(a, blockIdx.x * NT, t, NT) : blockIdx.x * NT + t;
     const bool tvalid = tile < ntiles;
     const int tile_c = tvalid ? tile : ntiles - 1;
     const int nsb = a.K / SB_K;
 
-    int rbeg, rend;
+    int rbeg, rend, expert = 0;
     const uint8_t* blob = a.blob;
     if (!MOE) {
         rbeg = blockIdx.y * MT;
@@ -413,6 +345,7 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         if (tr.expert < 0) return;                       // uniform over the workgroup
         rbeg = tr.rbeg;
         rend = tr.rend;
+        expert = tr.expert;
         blob = a.blob + size_t(tr.expert) * a.expert_stride;
     }
     const int nrows = rend - rbeg;
@@ -695,6 +628,39 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
         }
         if (tid < nrows) const_cast<float*>(a.sx)[rbeg + tid] = row_scale<false>(rowmax[tid]).s;
     }
+    if constexpr (MOE && MODE == MODE_OUT) {
+        if (a.Hq) {
+            // paired form: the up waves hand their outputs to the gate waves through the
+            // activation area of LDS (every wave's MFMAs are done); only the slice-0 waves are
+            // still running (s_barrier waits for the waves that have not ended)
+            static_assert(NT % 2 == 0, "paired form: gate and up tiles in equal numbers");
+            float* pb = reinterpret_cast<float*>(smem);
+            const RowScale prs = static_row_scale(a.s_dn[expert]);
+            if (t >= NT / 2) {
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        pb[((t - NT / 2) * NV + ms * 4 + i) * 64 + lane] = accf[ms][i] * sxr[ms][i];
+            }
+            lds_barrier();
+            const int gt = int(blockIdx.x) * (NT / 2) + t;
+            if (t < NT / 2 && gt < a.pair_n / 16) {
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = ms * 16 + 4 * (lane >> 4) + i;
+                        if (rbeg + row >= rend) continue;
+                        const float yu = pb[(t * NV + ms * 4 + i) * 64 + lane];
+                        a.Hq[size_t(rbeg + row) * a.pair_n + gt * 16 + (lane & 15)] =
+                            int8_t(silu_static_code(accf[ms][i] * sxr[ms][i], yu, prs));
+                    }
+            }
+            if (blockIdx.x == 0 && tid < nrows) a.sh[rbeg + tid] = prs.s;
+            return;
+        }
+    }
     const int col = tile * 16 + (lane & 15);
     if (!tvalid || col >= a.N) return;
 #pragma unroll
@@ -760,6 +726,7 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     const int sb0 = w * SW;
 
     int rbeg, rend, rall;                                // rows of the current tile; of the workgroup
+    int expert = 0;
     const uint8_t* blob = a.blob;
     if (!MOE) {
         rbeg = blockIdx.y * S::MT;
@@ -771,6 +738,7 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
         rbeg = tr.rbeg;
         rall = tr.rend;
         rend = min(rall, rbeg + S::MT);
+        expert = tr.expert;
         blob = a.blob + size_t(tr.expert) * a.expert_stride;
     }
     int nrows = rend - rbeg;
@@ -822,7 +790,7 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     auto load_meta = [&](const int g) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const uint32_t tc = uint32_t(min(tile0 + g * T + t, ntiles - 1));
+            const uint32_t tc = uint32_t(min(MOE ? pair_tile(a, tile0, g * T + t, TT) : tile0 + g * T + t, ntiles - 1));
 #pragma unroll
             for (int s = 0; s < SW; ++s) {
                 const uint32_t sb = uint32_t(min(sb0 + s, nsb - 1));
@@ -838,7 +806,7 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     auto load_w = [&](const int g) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const uint32_t tc = uint32_t(min(tile0 + g * T + t, ntiles - 1));
+            const uint32_t tc = uint32_t(min(MOE ? pair_tile(a, tile0, g * T + t, TT) : tile0 + g * T + t, ntiles - 1));
 #pragma unroll
             for (int s = 0; s < SW; ++s) {
                 const uint32_t sb = uint32_t(min(sb0 + s, nsb - 1));
@@ -928,6 +896,28 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
     // 5. slice-ordered sum, row scale, store.  Output o = (t * 64 + l) * NV + j holds
     //    C[row = (j / 4) * 16 + 4 * (l / 16) + j % 4][col = 16 * t + l % 16] of the tile grid.
     auto reduce_store = [&]() __attribute__((always_inline)) {
+    if (MOE && MODE == MODE_OUT && a.Hq) {
+        // paired form: tile slots [0, TT/2) are gate tiles, [TT/2, TT) their up tiles; output o
+        // of a gate slot and output o + half of its up slot are the same row and h column
+        static_assert(TT % 2 == 0, "paired form: gate and up tiles in equal numbers");
+        constexpr int half = TT / 2 * 64 * NV;
+        const RowScale prs = static_row_scale(a.s_dn[expert]);
+        for (int o = tid; o < half; o += int(blockDim.x)) {
+            const int j = o % NV, lo = (o / NV) % 64, t = o / (NV * 64);
+            const int row = (j >> 2) * 16 + 4 * (lo >> 4) + (j & 3);
+            const int gt = tile0 / 2 + t;
+            if (row >= nrows || gt >= a.pair_n / 16) continue;
+            float yg = red[o], yu = red[o + half];
+            for (int k = 1; k < KW; ++k) {
+                yg += red[size_t(k) * TT * 64 * NV + o];
+                yu += red[size_t(k) * TT * 64 * NV + o + half];
+            }
+            const int code = silu_static_code(yg * sxs[row], yu * sxs[row], prs);
+            a.Hq[size_t(rbeg + row) * a.pair_n + gt * 16 + (lo & 15)] = int8_t(code);
+        }
+        if (blockIdx.x == 0 && tid < nrows) a.sh[rbeg + tid] = prs.s;
+        return;
+    }
     for (int o = tid; o < TT * 64 * NV; o += int(blockDim.x)) {
         const int j = o % NV, lo = (o / NV) % 64, t = o / (NV * 64);
         const int row = (j >> 2) * 16 + 4 * (lo >> 4) + (j & 3);
@@ -1036,7 +1026,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     const int wm = wave & 3, wn = wave >> 2;
     const int ntl16 = (a.N + 15) / 16;                   // 16-column tiles in the blob
     const int ntiles = (ntl16 + 7) / 8;
-    int m0, mend, nt;
+    int m0, mend, nt, expert = 0;
     const uint8_t* blob = a.blob;
     if (!MOE) {
         const int mtiles = (a.M + PF_BM - 1) / PF_BM;
@@ -1050,9 +1040,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
         if (tr.expert < 0) return;                       // uniform over the workgroup
         m0 = tr.rbeg;
         mend = tr.rend;
+        expert = tr.expert;
         blob = a.blob + size_t(tr.expert) * a.expert_stride;
     }
     const int t0 = nt * 8;                               // first 16-column tile
+    // blob tile of the workgroup's l-th 16-column tile (paired form: 4 gate tiles, then their
+    // 4 up tiles)
+    auto tile_l = [&](int l) { return MOE ? pair_tile(a, t0, l, 8) : t0 + l; };
     const int nsb = a.K / SB_K;
     const uint8_t* codes = blob + a.codes_off;
     const uint8_t* scales_b = blob + a.scales_off;
@@ -1065,7 +1059,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     };
 
     // staging: thread tid owns layout lane (tid % 64) of 16-column tile (tid / 64)
-    const int b_tile = min(t0 + wave, ntl16 - 1);
+    const int b_tile = min(tile_l(wave), ntl16 - 1);
     const int st_q4 = lane >> 4, st_c = lane & 15;
     const int nmeta_s = 8 * NG * 4;                      // 16-byte scale pieces
     // Activation and code loads go through buffer resources.  Each lane's offset is fixed for
@@ -1114,7 +1108,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
         {   // every thread loads a piece (threads past nmeta_s repeat one and never store it)
             const int mt = tid % nmeta_s;
             const int tl = mt / (NG * 4), gi = (mt / 4) % NG, q4 = mt % 4;
-            const int tile = min(t0 + tl, ntl16 - 1);
+            const int tile = min(tile_l(tl), ntl16 - 1);
             const int mo = (tile * a.G + gidx(sb, gi)) * 16 + q4 * 4;
             if constexpr (H16) {
                 const auto t = __builtin_amdgcn_raw_buffer_load_b64(sr, mo * 2, 0, 0);
@@ -1181,7 +1175,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
         const int colw = wn * 64 + ns * 32 + l32;       // column inside the workgroup tile
         b_off[ns] = PF_A_BYTES + (hi * PF_BN + colw) * 16;
         s_off[ns] = PF_A_BYTES + PF_B_BYTES + (((colw >> 4) * NG) * 16 + (colw & 15)) * 4;
-        col_g[ns] = t0 * 16 + colw;
+        col_g[ns] = tile_l(colw >> 4) * 16 + (colw & 15);
     }
 
     auto compute = [&](int stage, int sb) {
@@ -1263,6 +1257,52 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
         __syncthreads();
     }
     if (MODE == MODE_PARTIALS) return;
+
+    if (MOE && MODE == MODE_OUT && a.Hq) {
+        // paired form: waves wn = 1 hold the up outputs of the same rows, lanes and registers as
+        // the gate outputs of waves wn = 0; they pass them through LDS (free after the K loop)
+        float* pb = reinterpret_cast<float*>(smem);
+        const RowScale prs = static_row_scale(a.s_dn[expert]);
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+            float sxv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const int sr = m0 + row < mend ? src_row(row) : -1;
+                sxv[r] = sr >= 0 ? a.sx[sr] : 0.0f;
+            }
+            if (wn == 1) {
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        pb[((wm * 4 + ms * 2 + ns) * 16 + r) * 64 + lane] = accf[ms][ns][r] * sxv[r];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) accf[ms][0][r] *= sxv[r], accf[ms][1][r] *= sxv[r];
+            }
+        }
+        __syncthreads();
+        if (wn == 0) {
+#pragma unroll
+            for (int ms = 0; ms < 2; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns) {
+                    const int gc = nt * 64 + ns * 32 + l32;          // column of h
+                    if (gc >= a.pair_n) continue;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        if (row >= mend) continue;
+                        const float yu = pb[((wm * 4 + ms * 2 + ns) * 16 + r) * 64 + lane];
+                        a.Hq[size_t(row) * a.pair_n + gc] = int8_t(silu_static_code(accf[ms][ns][r], yu, prs));
+                    }
+                }
+        }
+        if (nt == 0 && tid < mend - m0) a.sh[m0 + tid] = prs.s;
+        return;
+    }
 
     // row scales, then store
 #pragma unroll
@@ -1994,11 +2034,17 @@ int w4a8_moe_align(const int32_t* ids, int T, int k, int E, int32_t* sorted_rows
     return launch_status();
 }
 
+// Hq set: the paired form (gate/up blob, static SiLU-requant epilogue into Hq, sh with scales s_dn).
 static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gather, int k, const int32_t* offsets,
                          int E, int rows, int src_rows, const void* blobs, size_t stride, const w4a8_wdesc* d,
-                         void* Y, int out_dtype, int mt, hipStream_t s) {
+                         void* Y, int out_dtype, int mt, hipStream_t s, int8_t* Hq = nullptr, float* sh = nullptr,
+                         const float* s_dn = nullptr) {
     const Layout L = layout_of(d);
     GemmArgs a = make_args(L, Xq, sx, rows, blobs);
+    a.Hq = Hq;
+    a.sh = sh;
+    a.s_dn = s_dn;
+    a.pair_n = L.N / 2;
     a.Y = Y;
     a.ldy = L.N;
     a.out_f32 = out_dtype == W4A8_OUT_F32;
@@ -2075,6 +2121,28 @@ int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int 
                          static_cast<hipStream_t>(stream));
 }
 
+// Checks of the paired form on top of moe_gemm_check: the blob holds gate and up columns in
+// equal numbers that split into whole 16-column tiles, and the outputs are given.
+static int moe_gemm_silu_check(const int8_t* Xq, const float* sx, const int32_t* gather, int k,
+                               const int32_t* offsets, int E, int rows, int src_rows, const void* blobs, size_t stride,
+                               const w4a8_wdesc* d, const float* s, const int8_t* Hq, const float* sh) {
+    const int st = moe_gemm_check(Xq, sx, gather, k, offsets, E, rows, src_rows, blobs, stride, d, Hq, W4A8_OUT_BF16);
+    if (st || rows == 0) return st;
+    if (d->N % 32) return W4A8_EINVAL;
+    if (!s || !sh) return W4A8_EINVAL;
+    return W4A8_OK;
+}
+
+int w4a8_moe_gemm_silu_static(const int8_t* Xq, const float* sx, const int32_t* gather, int k,
+                              const int32_t* offsets, int E, int rows, int src_rows, const void* blobs, size_t stride,
+                              const w4a8_wdesc* d, const float* s, int8_t* Hq, float* sh, void* stream) {
+    const int st = moe_gemm_silu_check(Xq, sx, gather, k, offsets, E, rows, src_rows, blobs, stride, d, s, Hq, sh);
+    if (st || rows == 0) return st;
+    const int mt = rows / E >= 16 ? 32 : 16;
+    return moe_gemm_impl(Xq, sx, gather, k, offsets, E, rows, src_rows, blobs, stride, d, nullptr, W4A8_OUT_BF16, mt,
+                         static_cast<hipStream_t>(stream), Hq, sh, s);
+}
+
 // Longest row of the SiLU step: 8 passes of 2048 values per 256-thread workgroup.
 constexpr int SILU_MAX_I = 16384;
 
@@ -2141,7 +2209,7 @@ static MoeWs moe_ws(int T, int k, int H, int I, int E, bool per_row = false) {
     w.rows = o; o = al(o + R * 4);
     w.offs = o; o = al(o + size_t(E + 1) * 4);
     w.inv = o; o = al(o + R * 4);
-    w.gu = o; o = al(o + R * size_t(2 * I) * 2);
+    w.gu = o; o = al(o + (per_row ? 0 : R * size_t(2 * I) * 2));   // the static form needs no gate/up buffer
     w.hq = o; o = al(o + R * size_t(I));
     w.sh = o; o = al(o + R * 4);
     w.yd = o; o = al(o + R * size_t(H) * 2);
@@ -2344,8 +2412,8 @@ int w4a8_moe_forward_static(const void* X, const int32_t* ids, const float* w, i
     if (!s_gu || !s_dn) return W4A8_EINVAL;
     const MoeBufs B = moe_bufs(ws, L);
     const int R = T * k;
-    if ((st = moe_gemm_check(B.xq, B.sx, nullptr, k, B.offs, E, R, R, gu_blobs, gu_stride, gu_desc, B.gu,
-                             W4A8_OUT_BF16)))
+    if ((st = moe_gemm_silu_check(B.xq, B.sx, nullptr, k, B.offs, E, R, R, gu_blobs, gu_stride, gu_desc, s_dn,
+                                  B.hq, B.sh)))
         return st;
     if ((st = moe_gemm_check(B.hq, B.sh, nullptr, k, B.offs, E, R, R, d_blobs, d_stride, d_desc, B.yd,
                              W4A8_OUT_BF16)))
@@ -2353,10 +2421,10 @@ int w4a8_moe_forward_static(const void* X, const int32_t* ids, const float* w, i
     if ((st = w4a8_moe_align(ids, T, k, E, B.rows, B.offs, B.inv, stream))) return st;
     // each routed row quantizes its token with the scale of its expert, already in sorted order
     if ((st = w4a8_moe_quant_static(X, T, H, H, B.rows, k, B.offs, E, s_gu, B.xq, B.sx, stream))) return st;
-    if ((st = w4a8_moe_gemm(B.xq, B.sx, nullptr, k, B.offs, E, R, R, gu_blobs, gu_stride, gu_desc, B.gu,
-                            W4A8_OUT_BF16, stream)))
+    // gate/up GEMM with the SiLU-requant folded into its epilogue: h's codes, no gate/up buffer
+    if ((st = w4a8_moe_gemm_silu_static(B.xq, B.sx, nullptr, k, B.offs, E, R, R, gu_blobs, gu_stride, gu_desc, s_dn,
+                                        B.hq, B.sh, stream)))
         return st;
-    if ((st = w4a8_silu_mul_quant_static(B.gu, R, I, B.offs, E, s_dn, B.hq, B.sh, stream))) return st;
     if ((st = w4a8_moe_gemm(B.hq, B.sh, nullptr, k, B.offs, E, R, R, d_blobs, d_stride, d_desc, B.yd,
                             W4A8_OUT_BF16, stream)))
         return st;

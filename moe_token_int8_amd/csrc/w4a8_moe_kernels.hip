@@ -31,7 +31,8 @@ struct MoeStreamShape {
     static constexpr int NTHR = 64 * NT * KW;                  // 512
     static constexpr int CG = MST_TILES / NT;                  // column groups
     static constexpr size_t LDS_RED = size_t(KW - 1) * NT * MS * 4 * 64 * 4;
-    static size_t lds(int K) { return size_t(MT) * size_t(K + 16) + LDS_RED; }
+    static constexpr size_t LDS_PAIR = size_t(MS) * 4 * 64 * 4;   // paired form: the up outputs of a group
+    static size_t lds(int K) { return size_t(MT) * size_t(K + 16) + LDS_RED + LDS_PAIR; }
     static_assert(NTHR == 512, "8 waves: two per SIMD, so each has 256 registers");
 };
 
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int K = a.K, ROWB = K + 16;
     float* red = reinterpret_cast<float*>(smem + size_t(MT) * ROWB);
+    float* pbuf = reinterpret_cast<float*>(smem + size_t(MT) * ROWB + S::LDS_RED);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = wave % NT, q = wave / NT;
     const int ntiles = (a.N + 15) / 16;
@@ -57,6 +59,14 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
     const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
     const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(blob + a.scales_off);
     const uint8_t* zeros = blob + a.zeros_off;
+    // paired form (static SiLU-requant epilogue): group g holds gate tile bx * CG + g (t = 0) and
+    // its up tile (t = 1); the workgroup of the first column block writes the row scales
+    const bool pair = a.Hq != nullptr;
+    RowScale prs{};
+    if (pair) {
+        prs = static_row_scale(a.s_dn[tr.expert]);
+        if (blockIdx.x == 0 && tid < nrows) a.sh[rbeg + tid] = prs.s;
+    }
 
     // 1. the tile's activation rows, requested first (they gate the first MFMA)
     const int ppr = nsb * 8;                                     // pieces per row
@@ -89,7 +99,7 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
     float sc[2][SBN][GPS];
     uint32_t zq[2][SBN][GPS];
     uint4 bq[2][SBN];
-    auto tile_of = [&](int g) { return (int(blockIdx.x) * CG + g) * NT + t; };
+    auto tile_of = [&](int g) { return pair_tile(a, (int(blockIdx.x) * CG + g) * NT, t, NT); };
     auto load_group = [&](const int g, const int set) __attribute__((always_inline)) {
         const uint32_t tc = uint32_t(min(tile_of(g), ntiles - 1));
 #pragma unroll
@@ -180,7 +190,7 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
                     for (int i = 0; i < 4; ++i) accf[ms][i] += red[(((w - 1) * NT + t) * NV + ms * 4 + i) * 64 + lane];
             const int tile = tile_of(g);
             const int col = tile * 16 + (lane & 15);
-            if (tile < ntiles && col < a.N) {
+            if (!pair && tile < ntiles && col < a.N) {
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
@@ -193,6 +203,30 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
                             reinterpret_cast<float*>(a.Y)[yi] = y;
                         else
                             reinterpret_cast<uint16_t*>(a.Y)[yi] = uint16_t(f32_to_bf16_rne(y));
+                    }
+            }
+        }
+        if (pair) {
+            // the up wave hands its outputs to the gate wave of the same lanes and rows, which
+            // forms h and stores its codes
+            if (q == 0 && t == 1) {
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pbuf[(ms * 4 + i) * 64 + lane] = accf[ms][i] * sxr[ms][i];
+            }
+            lds_barrier();
+            const int gt = int(blockIdx.x) * CG + g;
+            if (q == 0 && t == 0 && gt < a.pair_n / 16) {
+                const int col = gt * 16 + (lane & 15);
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = ms * 16 + 4 * (lane >> 4) + i;
+                        if (row >= nrows) continue;
+                        const int code = silu_static_code(accf[ms][i] * sxr[ms][i], pbuf[(ms * 4 + i) * 64 + lane], prs);
+                        a.Hq[size_t(rbeg + row) * a.pair_n + col] = int8_t(code);
                     }
             }
         }

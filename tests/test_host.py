@@ -453,12 +453,23 @@ def test_static_entry_points_validate_before_launch():
     assert lib.w4a8_silu_mul_quant_static(fake, 8, 128, fake, 0, fake, fake, fake, None) == E
     gu, dn = L.desc(256, 256, 64, True), L.desc(128, 256, 64, True)
     need = L.w4a8_moe_static_workspace_size(8, 2, 256, 128, 4)
-    assert need > L.w4a8_moe_workspace_size(8, 2, 256, 128, 4)       # codes of T*k routed rows
+    # codes of T*k routed rows, but no gate/up buffer (the SiLU-requant is in the GEMM's epilogue)
+    al = lambda v: (v + 255) // 256 * 256
+    R, T = 16, 8
+    assert need - L.w4a8_moe_workspace_size(8, 2, 256, 128, 4) == \
+        (al(R * 256) - al(T * 256)) + (al(R * 4) - al(T * 4)) - al(R * 256 * 2)
     args = lambda sg, sd, nbytes: (fake, fake, fake, 8, 2, 4, fake, 1 << 20, ctypes.byref(gu), fake, 1 << 20,
                                    ctypes.byref(dn), sg, sd, fake, nbytes, fake, None)
     assert lib.w4a8_moe_forward_static(*args(None, fake, need)) == E
     assert lib.w4a8_moe_forward_static(*args(fake, None, need)) == E
     assert lib.w4a8_moe_forward_static(*args(fake, fake, need - 256)) == L.W4A8_ESIZE
+    # the grouped gate/up GEMM with the static SiLU-requant epilogue
+    fz = lambda d, rows=8, s=fake, hq=fake, sh=fake: lib.w4a8_moe_gemm_silu_static(
+        fake, fake, fake, 2, fake, 4, rows, 8, fake, 1 << 20, ctypes.byref(d), s, hq, sh, None)
+    assert fz(gu, rows=0) == L.W4A8_OK
+    assert fz(L.desc(256, 48, 64, True)) == E                 # 2I = 48: I is not a whole tile
+    assert fz(gu, s=None) == E and fz(gu, hq=None) == E and fz(gu, sh=None) == E
+    assert fz(L.desc(256, 256, 32, True)) == U                # g = 32: dense kernels only
 
 
 def test_fp16_pack_codes_nan_and_range():
