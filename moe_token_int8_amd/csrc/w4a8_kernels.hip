@@ -1259,45 +1259,40 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     if (MODE == MODE_PARTIALS) return;
 
     if (MOE && MODE == MODE_OUT && a.Hq) {
-        // paired form: waves wn = 1 hold the up outputs of the same rows, lanes and registers as
-        // the gate outputs of waves wn = 0; they pass them through LDS (free after the K loop)
-        float* pb = reinterpret_cast<float*>(smem);
+        // paired form: waves wn = 0 hold the gate outputs and waves wn = 1 the up outputs of the
+        // same rows, lanes and registers.  Each side hands the other half of its outputs over
+        // through LDS (free after the K loop): wn = 1 passes its ns = 0 outputs, wn = 0 its ns = 1
+        // outputs; then wn = 0 forms the codes of h columns ns = 0 and wn = 1 those of ns = 1, so
+        // the SiLU-requant is split evenly over the 8 waves.
+        float* pb = reinterpret_cast<float*>(smem);          // [ns][wm][ms][r][64]
         const RowScale prs = static_row_scale(a.s_dn[expert]);
+        const int own = wn == 0 ? 0 : 1;                     // ns of the h columns this wave forms
+        float y[2][16];                                      // this wave's outputs at ns = own
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms) {
-            float sxv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
                 const int sr = m0 + row < mend ? src_row(row) : -1;
-                sxv[r] = sr >= 0 ? a.sx[sr] : 0.0f;
-            }
-            if (wn == 1) {
-#pragma unroll
-                for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        pb[((wm * 4 + ms * 2 + ns) * 16 + r) * 64 + lane] = accf[ms][ns][r] * sxv[r];
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) accf[ms][0][r] *= sxv[r], accf[ms][1][r] *= sxv[r];
+                const float sxv = sr >= 0 ? a.sx[sr] : 0.0f;
+                const float mine = (own == 0 ? accf[ms][0][r] : accf[ms][1][r]) * sxv;
+                const float other = (own == 0 ? accf[ms][1][r] : accf[ms][0][r]) * sxv;
+                y[ms][r] = mine;
+                pb[(((1 - own) * 4 + wm) * 2 * 16 + ms * 16 + r) * 64 + lane] = other;
             }
         }
         __syncthreads();
-        if (wn == 0) {
+        const int gc = nt * 64 + own * 32 + l32;             // column of h
+        if (gc < a.pair_n) {
 #pragma unroll
             for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
-                for (int ns = 0; ns < 2; ++ns) {
-                    const int gc = nt * 64 + ns * 32 + l32;          // column of h
-                    if (gc >= a.pair_n) continue;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                        if (row >= mend) continue;
-                        const float yu = pb[((wm * 4 + ms * 2 + ns) * 16 + r) * 64 + lane];
-                        a.Hq[size_t(row) * a.pair_n + gc] = int8_t(silu_static_code(accf[ms][ns][r], yu, prs));
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    if (row >= mend) continue;
+                    const float v = pb[((own * 4 + wm) * 2 * 16 + ms * 16 + r) * 64 + lane];
+                    const float yg = own == 0 ? y[ms][r] : v, yu = own == 0 ? v : y[ms][r];
+                    a.Hq[size_t(row) * a.pair_n + gc] = int8_t(silu_static_code(yg, yu, prs));
                 }
         }
         if (nt == 0 && tid < mend - m0) a.sh[m0 + tid] = prs.s;

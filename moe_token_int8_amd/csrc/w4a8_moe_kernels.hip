@@ -31,7 +31,7 @@ struct MoeStreamShape {
     static constexpr int NTHR = 64 * NT * KW;                  // 512
     static constexpr int CG = MST_TILES / NT;                  // column groups
     static constexpr size_t LDS_RED = size_t(KW - 1) * NT * MS * 4 * 64 * 4;
-    static constexpr size_t LDS_PAIR = size_t(MS) * 4 * 64 * 4;   // paired form: the up outputs of a group
+    static constexpr size_t LDS_PAIR = size_t(NT) * MS * 4 * 64 * 4;   // paired form: a group's final sums
     static size_t lds(int K) { return size_t(MT) * size_t(K + 16) + LDS_RED + LDS_PAIR; }
     static_assert(NTHR == 512, "8 waves: two per SIMD, so each has 256 registers");
 };
@@ -60,13 +60,9 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
     const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(blob + a.scales_off);
     const uint8_t* zeros = blob + a.zeros_off;
     // paired form (static SiLU-requant epilogue): group g holds gate tile bx * CG + g (t = 0) and
-    // its up tile (t = 1); the workgroup of the first column block writes the row scales
+    // its up tile (t = 1)
     const bool pair = a.Hq != nullptr;
-    RowScale prs{};
-    if (pair) {
-        prs = static_row_scale(a.s_dn[tr.expert]);
-        if (blockIdx.x == 0 && tid < nrows) a.sh[rbeg + tid] = prs.s;
-    }
+    static_assert(NT == 2 && NT * KW >= NV, "paired form: one gate and one up tile per group");
 
     // 1. the tile's activation rows, requested first (they gate the first MFMA)
     const int ppr = nsb * 8;                                     // pieces per row
@@ -93,6 +89,9 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
                 sxr[ms][i] = src >= 0 ? a.sx[src] : 0.0f;
             }
         }
+
+    // paired form: the expert's static scale of h (first needed in the first group's epilogue)
+    const float s_e = pair ? a.s_dn[tr.expert] : 0.0f;
 
     // 2. per column group g (register set g % 2): scales, zero points and weight superblocks
     const int s0 = q * SBN;
@@ -207,33 +206,30 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
             }
         }
         if (pair) {
-            // the up wave hands its outputs to the gate wave of the same lanes and rows, which
-            // forms h and stores its codes
-            if (q == 0 && t == 1) {
+            // the two slice-0 waves put the group's final gate and up outputs in LDS; then wave w
+            // forms the codes of accumulator slot w (one value per lane), so the SiLU-requant
+            // is spread over the workgroup instead of lengthening one wave's path
+            if (q == 0) {
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) pbuf[(ms * 4 + i) * 64 + lane] = accf[ms][i] * sxr[ms][i];
+                    for (int i = 0; i < 4; ++i) pbuf[(t * NV + ms * 4 + i) * 64 + lane] = accf[ms][i] * sxr[ms][i];
             }
             lds_barrier();
             const int gt = int(blockIdx.x) * CG + g;
-            if (q == 0 && t == 0 && gt < a.pair_n / 16) {
-                const int col = gt * 16 + (lane & 15);
-#pragma unroll
-                for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = ms * 16 + 4 * (lane >> 4) + i;
-                        if (row >= nrows) continue;
-                        const int code = silu_static_code(accf[ms][i] * sxr[ms][i], pbuf[(ms * 4 + i) * 64 + lane], prs);
-                        a.Hq[size_t(rbeg + row) * a.pair_n + col] = int8_t(code);
-                    }
+            const int row = (wave / 4) * 16 + 4 * (lane >> 4) + (wave & 3);
+            if (wave < NV && gt < a.pair_n / 16 && row < nrows) {
+                const float yg = pbuf[wave * 64 + lane], yu = pbuf[(NV + wave) * 64 + lane];
+                a.Hq[size_t(rbeg + row) * a.pair_n + gt * 16 + (lane & 15)] =
+                    int8_t(silu_static_code(yg, yu, static_row_scale(s_e)));
             }
         }
         if (g + 1 < CG) lds_barrier();                           // the reduction area is reused
     };
 #pragma unroll
     for (int g = 0; g < CG; ++g) group(g, g & 1);
+    // paired form: the workgroup of the first column block writes the row scales of h
+    if (pair && blockIdx.x == 0 && tid < nrows) a.sh[rbeg + tid] = s_e;
 }
 
 template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16>
