@@ -354,6 +354,14 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
     const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(blob + a.scales_off);
     const uint8_t* zeros = blob + a.zeros_off;
 
+    // grouped form: source row (of Xq and sx) of tile row r, held by lane r and shared by
+    // cross-lane reads, so no activation piece waits on a dependent gather load of its own
+    int srcl = -1;
+    if constexpr (MOE) {
+        if (lane < nrows) srcl = a.gather ? gather_src(a, rbeg + lane) : rbeg + lane;
+    }
+    auto src_of = [&](int r) { return MOE ? __shfl(srcl, r & 63, 64) : rbeg + r; };
+
     // row scales of the rows this lane stores, fetched before anything else so the
     // epilogue never waits on a load
     float sxr[MS][4];
@@ -362,11 +370,9 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             sxr[ms][i] = 0.0f;
-            const int row = rbeg + ms * 16 + 4 * (lane >> 4) + i;
-            if (!FQ && MODE != MODE_PARTIALS && q == 0 && row < rend) {
-                const int srow = (MOE && a.gather) ? gather_src(a, row) : row;
-                sxr[ms][i] = srow >= 0 ? a.sx[srow] : 0.0f;
-            }
+            const int r = ms * 16 + 4 * (lane >> 4) + i;
+            const int srow = src_of(r);
+            if (!FQ && MODE != MODE_PARTIALS && q == 0 && r < nrows) sxr[ms][i] = srow >= 0 ? a.sx[srow] : 0.0f;
         }
 
     float accf[MS][4];
@@ -399,8 +405,8 @@ __global__ __launch_bounds__(64 * NT * KW) void gemm_decode_kernel(GemmArgs a) {
             const int row = pc / (CS * 8), c = pc - row * (CS * 8);
             xv[i] = make_uint4(0, 0, 0, 0);
             if (FQ) xb[0][0] = xb[0][1] = make_uint4(0, 0, 0, 0);
-            int src = -1;
-            if (row < nrows && c < rowpieces) src = (MOE && a.gather) ? gather_src(a, rbeg + row) : rbeg + row;
+            const int srow = src_of(row);
+            const int src = (row < nrows && c < rowpieces) ? srow : -1;
             if (src >= 0) {
                 if (FQ) {
                     const uint4* xp = reinterpret_cast<const uint4*>(a.X + size_t(src) * a.ldx + c * 16);
@@ -1258,6 +1264,17 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     }
     if (MODE == MODE_PARTIALS) return;
 
+    // row scale of tile row wm * 64 + lane, loaded once per lane (the gather of a grouped tile
+    // and the scale are two dependent loads); each output register takes its row's by a
+    // cross-lane read
+    float sxl = 0.0f;
+    {
+        const int row = wm * 64 + lane;
+        const int sr = m0 + row < mend ? src_row(row) : -1;
+        if (sr >= 0) sxl = a.sx[sr];
+    }
+    auto row_sx = [&](int ms, int r) { return __shfl(sxl, ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3), 64); };
+
     if (MOE && MODE == MODE_OUT && a.Hq) {
         // paired form: waves wn = 0 hold the gate outputs and waves wn = 1 the up outputs of the
         // same rows, lanes and registers.  Each side hands the other half of its outputs over
@@ -1272,9 +1289,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
         for (int ms = 0; ms < 2; ++ms) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                const int sr = m0 + row < mend ? src_row(row) : -1;
-                const float sxv = sr >= 0 ? a.sx[sr] : 0.0f;
+                const float sxv = row_sx(ms, r);
                 const float mine = (own == 0 ? accf[ms][0][r] : accf[ms][1][r]) * sxv;
                 const float other = (own == 0 ? accf[ms][1][r] : accf[ms][0][r]) * sxv;
                 y[ms][r] = mine;
@@ -1304,11 +1319,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     for (int ms = 0; ms < 2; ++ms) {
         float sxv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const int sr = m0 + row < mend ? src_row(row) : -1;
-            sxv[r] = sr >= 0 ? a.sx[sr] : 0.0f;
-        }
+        for (int r = 0; r < 16; ++r) sxv[r] = row_sx(ms, r);
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
             const int col = col_g[ns];

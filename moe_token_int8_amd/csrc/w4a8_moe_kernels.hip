@@ -64,17 +64,20 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
     const bool pair = a.Hq != nullptr;
     static_assert(NT == 2 && NT * KW >= NV, "paired form: one gate and one up tile per group");
 
+    // source row (of Xq and sx) of tile row r, held by lane r: one gather load per lane, shared
+    // by cross-lane reads, so no activation piece waits on a dependent load of its own
+    int srcl = -1;
+    if (lane < nrows) srcl = a.gather ? gather_src(a, rbeg + lane) : rbeg + lane;
+
     // 1. the tile's activation rows, requested first (they gate the first MFMA)
     const int ppr = nsb * 8;                                     // pieces per row
     uint4 xv[APT];
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
         const int p = tid + i * NTHR, row = p / ppr, c = p - row * ppr;
+        const int src = __shfl(srcl, row & 63, 64);
         xv[i] = make_uint4(0, 0, 0, 0);
-        if (row < nrows) {
-            const int src = a.gather ? gather_src(a, rbeg + row) : rbeg + row;
-            if (src >= 0) xv[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(src) * K + c * 16);
-        }
+        if (row < nrows && src >= 0) xv[i] = *reinterpret_cast<const uint4*>(a.Xq + size_t(src) * K + c * 16);
     }
     // row scales of the rows this lane stores (slice-0 waves store)
     float sxr[MS][4];
@@ -83,11 +86,9 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = ms * 16 + 4 * (lane >> 4) + i;
+            const int src = __shfl(srcl, row, 64);
             sxr[ms][i] = 0.0f;
-            if (q == 0 && row < nrows) {
-                const int src = a.gather ? gather_src(a, rbeg + row) : rbeg + row;
-                sxr[ms][i] = src >= 0 ? a.sx[src] : 0.0f;
-            }
+            if (q == 0 && row < nrows && src >= 0) sxr[ms][i] = a.sx[src];
         }
 
     // paired form: the expert's static scale of h (first needed in the first group's epilogue)
