@@ -400,6 +400,13 @@ typedef struct {
  * be kept at a finer format).  The steps of w4a8_moe_forward; each grouped GEMM runs
  * once per set, over that set's experts.  The group size, zero points and scale width may
  * differ between sets; the shapes (gate/up [H, 2I], down [I, H]) may not (EINVAL).
+ * The sets' grouped GEMMs are independent (disjoint experts, disjoint rows): set 0 runs on
+ * `stream`, the others on up to four helper streams of the current device, forked from `stream`
+ * and joined back into it with events, so the call completes in `stream` order and can be
+ * captured into a graph.  The helpers (default priority) are created by the first call with
+ * two or more sets that is not made under graph capture, and kept until the process ends; a
+ * call made before they exist, or where they cannot be created, runs the sets one after
+ * another on `stream`.  Calls from several host threads enqueue one at a time.
  *   sets, nsets  host array of the format classes; E = sum of n_experts <= 1024
  *   workspace    device, >= w4a8_moe_workspace_size(T, k, H, I, E) bytes, 256-aligned
  * Other arguments and errors as w4a8_moe_forward. */
