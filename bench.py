@@ -44,7 +44,8 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="skip the prefill and MoE figures")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--only", default="", help="comma list of legs: decode,prefill,moe,quant,compare")
+    p.add_argument("--only", default="",
+                   help="comma list of legs: decode,prefill,moe,quant,compare (default), moe_sparse (byte check)")
     p.add_argument("--no-graph", action="store_true", help="launch the decode steps eagerly")
     p.add_argument("--calib", action="store_true",
                    help="also run one plain copy kernel (torch.neg over 256 MiB of fp32) so that "
@@ -323,6 +324,34 @@ def prefill_leg(args, L, W, torch, dev, steps):
 
 
 # ---------------------------------------------------------------------------------- MoE
+def moe_sparse_leg(args, L, W, torch, dev, steps=3):
+    """The 64-expert top-6 layer (H = 4096, I = 1408) on 16 tokens routed among experts 0..7
+    only: 56 experts receive no rows, the 8 others 12 rows each (one 16-row tile, so each
+    touched expert's weights are streamed exactly once per GEMM).  Run under rocprofv3 --pmc FETCH_SIZE,
+    the grouped launches must read about 8 experts' weights, not 64.  Reports the bytes of the
+    touched and of all experts for that comparison."""
+    cfg = W.C4
+    T, E8 = 16, 8
+    # token t takes the 6 experts other than (t % 8) and ((t + 4) % 8): every expert gets 12 rows
+    ids = np.array([[e for e in range(E8) if e not in (t % E8, (t + 4) % E8)] for t in range(T)], np.int32)
+    w = np.full(ids.shape, 1.0 / cfg.topk, np.float32)
+    gud = L.desc(cfg.H, 2 * cfg.I, cfg.group_size, cfg.asymmetric)
+    dd = L.desc(cfg.I, cfg.H, cfg.group_size, cfg.asymmetric)
+    gu, gstride = random_device_blobs(L, gud, cfg.E, 41, dev)
+    dn, dstride = random_device_blobs(L, dd, cfg.E, 43, dev)
+    X = W.moe_activations(cfg, T=T).to(dev)
+    ids_d, w_d = torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)
+    ws = torch.empty(L.w4a8_moe_workspace_size(T, cfg.topk, cfg.H, cfg.I, cfg.E), dtype=torch.uint8, device=dev)
+    o = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+    for _ in range(steps):
+        L.w4a8_moe_forward(X, ids_d, w_d, cfg.E, gu, gstride, gud, dn, dstride, dd, ws, o)
+    torch.cuda.synchronize()
+    touched = len(set(ids.ravel().tolist()))
+    return dict(layers=steps, tokens=T, experts=cfg.E, experts_touched=touched,
+                gate_up_bytes_touched=touched * gstride, down_bytes_touched=touched * dstride,
+                gate_up_bytes_all=cfg.E * gstride, down_bytes_all=cfg.E * dstride)
+
+
 def moe_leg(args, L, W, torch, dev, steps):
     out = {}
     for cfg, seed in ((W.C4, 4), (W.C5, 5)):
@@ -621,6 +650,9 @@ def main():
     if "moe" in legs:
         print("[bench] moe leg", file=sys.stderr, flush=True)
         extra["moe"] = moe_leg(args, L, W, torch, dev, steps=20)
+    if "moe_sparse" in legs:
+        print("[bench] moe leg, 16 tokens over 8 of 64 experts", file=sys.stderr, flush=True)
+        extra["moe_sparse"] = moe_sparse_leg(args, L, W, torch, dev)
     if "quant" in legs:
         print("[bench] quant leg", file=sys.stderr, flush=True)
         extra["quant"] = quant_leg(args, L, W, torch, dev, steps=256)

@@ -282,7 +282,11 @@ struct DecodeShape {
     static constexpr int MT = 16 * MS;
     static constexpr int NTHR = 64 * NT * KW;
     static constexpr int CS = KW * SBN;                        // superblocks per chunk
-    static constexpr int ROWB = CS * SB_K + 16;                // padded LDS row stride
+    // padded LDS row stride: 32 bytes past a multiple of 128, so the 16 rows x 4 k-chunks that a
+    // 16x16x64 operand read spreads over lanes land in distinct banks (with 16 bytes of padding,
+    // chunk c + 1 of row r and chunk c of row r + 1 shared banks: SQ_LDS_BANK_CONFLICT counted
+    // about 2.8 conflict cycles per LDS instruction)
+    static constexpr int ROWB = CS * SB_K + 32;
     static constexpr int APT = (MT * CS * 8 + NTHR - 1) / NTHR;  // 16-byte A pieces / thread
     static constexpr size_t LDS_A = size_t(MT) * ROWB;
     static constexpr size_t LDS_RED = size_t(KW > 1 ? KW - 1 : 1) * NT * MS * 4 * 64 * 4;

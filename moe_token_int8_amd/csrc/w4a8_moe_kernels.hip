@@ -32,7 +32,9 @@ struct MoeStreamShape {
     static constexpr int CG = MST_TILES / NT;                  // column groups
     static constexpr size_t LDS_RED = size_t(KW - 1) * NT * MS * 4 * 64 * 4;
     static constexpr size_t LDS_PAIR = size_t(NT) * MS * 4 * 64 * 4;   // paired form: a group's final sums
-    static size_t lds(int K) { return size_t(MT) * size_t(K + 16) + LDS_RED + LDS_PAIR; }
+    // activation rows padded by 32 bytes (a multiple of 128 plus 32: the 16 rows x 4 k-chunks of
+    // a 16x16x64 operand read fall in distinct LDS banks)
+    static size_t lds(int K) { return size_t(MT) * size_t(K + 32) + LDS_RED + LDS_PAIR; }
     static_assert(NTHR == 512, "8 waves: two per SIMD, so each has 256 registers");
 };
 
@@ -43,7 +45,7 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
     // activation pieces (16 bytes) per thread: the K <= KW * SBN * 128 rows of a full tile
     constexpr int APT = (MT * KW * SBN * 8 + NTHR - 1) / NTHR;
     extern __shared__ __align__(16) uint8_t smem[];
-    const int K = a.K, ROWB = K + 16;
+    const int K = a.K, ROWB = K + 32;
     float* red = reinterpret_cast<float*>(smem + size_t(MT) * ROWB);
     float* pbuf = reinterpret_cast<float*>(smem + size_t(MT) * ROWB + S::LDS_RED);
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
