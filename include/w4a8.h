@@ -19,8 +19,9 @@
  *     M = batch * seq_len, K = hidden, N = out features).
  *   - The caller owns every buffer, host and device.  GPU entry points only
  *     enqueue work on `stream` (a hipStream_t, NULL = the null stream) and never
- *     allocate, free or synchronize.  Device pointers must stay valid until the
- *     enqueued work completes.
+ *     allocate device memory, free or synchronize (w4a8_moe_forward_sets creates
+ *     helper streams and events once per device; see there).  Device pointers must
+ *     stay valid until the enqueued work completes.
  *   - Return value: W4A8_OK (0) or a negative w4a8_status.  All argument checks
  *     run on the host before anything is enqueued, so an error return means
  *     nothing was launched.  W4A8_EHIP reports a launch failure seen right after
@@ -29,7 +30,12 @@
  *     and P4: a fallback must be explicit and observable).
  *   - Device buffers read with 128-bit loads (Xq, Hq, blobs) must be 16-byte
  *     aligned; the library checks this and returns W4A8_EINVAL otherwise.
- *   - Calls are thread-safe; the library keeps no mutable global state.
+ *   - Calls are thread-safe.  The only state the library keeps is created once per
+ *     device and kept until the process ends: the helper streams of
+ *     w4a8_moe_forward_sets and the scratch array of w4a8_moe_forward_noalloc.
+ *   - Environment: W4A8_LOG set to anything but "0" makes every GEMM and MoE entry
+ *     point print one line to stderr before it launches: the call, its shape and the
+ *     kernel variant it resolved to (P4: a kernel hit must be observable).
  */
 #ifndef W4A8_H
 #define W4A8_H

@@ -33,6 +33,7 @@
 // (k = 64 h + 16 (l / 16) + j) feed two such steps: j in [0, 8) and j in [8, 16).
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
 #include <cstring>
 
 #include "w4a8_device.h"
@@ -490,6 +491,7 @@ int w4a16_gemm(const void* X, int M, int ldx, const void* blob, const w4a8_wdesc
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool asym = d->asymmetric != 0;
     const int gps = SB_K / L.g;
+    if (log_on()) std::fprintf(stderr, "w4a8: w4a16_gemm M=%d K=%d N=%d -> %s\n", M, L.K, L.N, w4a16_kernel_name(d, M));
     if (M > 32) {
         if (gps == 1) { if (asym) launch_a16_prefill<1, true>(a, s); else launch_a16_prefill<1, false>(a, s); }
         else { if (asym) launch_a16_prefill<2, true>(a, s); else launch_a16_prefill<2, false>(a, s); }

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <thread>
 #include <vector>
@@ -29,6 +30,14 @@ bool desc_valid(const w4a8_wdesc* d) {
     if (g != 32 && g != 64 && g != 128 && g != 256 && g != d->K) return false;   // g = K: per channel
     if (d->K % g) return false;            // groups cannot cross rows (P3 reference)
     return true;
+}
+
+bool log_on() {
+    static const bool on = [] {
+        const char* e = std::getenv("W4A8_LOG");
+        return e && *e && std::strcmp(e, "0") != 0;
+    }();
+    return on;
 }
 
 int desc_status(const w4a8_wdesc* d) {

@@ -22,4 +22,8 @@ bool desc_valid(const w4a8_wdesc* d);
 int desc_status(const w4a8_wdesc* d);   // OK, EINVAL (bad desc) or EUNSUPPORTED (layout)
 Layout layout_of(const w4a8_wdesc* d);
 
+// W4A8_LOG set in the environment (to anything but "0"): the GEMM and MoE entry points print one
+// line each to stderr, naming the call, its shape and the kernel variant it resolved to.
+bool log_on();
+
 }  // namespace w4a8

@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 #include <type_traits>
@@ -1247,23 +1248,37 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     // pipeline: register set s%2 holds the loads of superblock s; stage s%2 of LDS holds
     // superblock s while it is computed
     // (prefetches past the last superblock reload the last one and are never stored)
+    // The pair loop is straight-line code: the wait before each LDS store then names exactly the
+    // register set it stores (the other set's loads stay in flight).  With conditional stores
+    // and an exit in the middle of the body the compiler merged the paths pessimistically and
+    // waited for every outstanding load, which collapsed the two-superblock prefetch.  The
+    // empty asm statements keep each set's loads issued where they are written.
     PfRegs R0, R1;
     gload(R0, 0);
     gload(R1, min(1, nsb - 1));
+    asm volatile("" ::: "memory");
     lstore(R0, 0);
     gload(R0, min(2, nsb - 1));
+    asm volatile("" ::: "memory");
     __syncthreads();
-    for (int kb = 0; kb < nsb; kb += 2) {
-        // even superblock kb: stage 0; R1 holds kb+1, R0 holds kb+2
-        if (kb + 1 < nsb) lstore(R1, 1);
+    int kb = 0;
+    for (; kb + 1 < nsb; kb += 2) {
+        // even superblock kb: stage 0; R1 holds kb+1, R0 holds kb+2 (clamped past the end)
+        lstore(R1, 1);
         gload(R1, min(kb + 3, nsb - 1));
+        asm volatile("" ::: "memory");
         compute(0, kb);
         __syncthreads();
-        if (kb + 1 >= nsb) break;
-        // odd superblock kb+1: stage 1; R0 holds kb+2, R1 holds kb+3
-        if (kb + 2 < nsb) lstore(R0, 0);
+        // odd superblock kb+1: stage 1; R0 holds kb+2, R1 holds kb+3 (stage 0 written past the
+        // end is never computed)
+        lstore(R0, 0);
         gload(R0, min(kb + 4, nsb - 1));
+        asm volatile("" ::: "memory");
         compute(1, kb + 1);
+        __syncthreads();
+    }
+    if (kb < nsb) {                                      // odd nsb: the last superblock, in stage 0
+        compute(0, kb);
         __syncthreads();
     }
     if (MODE == MODE_PARTIALS) return;
@@ -1926,8 +1941,9 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
     a.Y = Y;
     a.ldy = ldy;
     a.out_f32 = out_dtype == W4A8_OUT_F32;
+    if (M >= PREFILL_MIN_M && !prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
+    if (log_on()) std::fprintf(stderr, "w4a8: w4a8_gemm M=%d K=%d N=%d -> %s\n", M, L.K, L.N, w4a8_kernel_name(d, M));
     if (M >= PREFILL_MIN_M) {
-        if (!prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
         launch_prefill<MODE_OUT>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), 0,
                                  L.bits == 8);
         return launch_status();
@@ -1956,6 +1972,9 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
     const int fcs = fc.kw * fc.sbn;                      // superblocks per chunk
     if (M <= 16 && size_t(M) * L.K <= FUSED_MAX_ELEMS && L.K / SB_K <= fcs &&
         (M - 1) * fcs * 8 + (L.K / SB_K) * 8 <= 64 * fc.nt * fc.kw) {
+        if (log_on())
+            std::fprintf(stderr, "w4a8: w4a8_linear M=%d K=%d N=%d -> %s, quantization fused\n", M, L.K, L.N,
+                         w4a8_kernel_name(d, M));
         GemmArgs a = make_args(L, Xq, sx, M, blob);
         a.X = static_cast<const uint16_t*>(X);
         a.ldx = ldx;
@@ -1986,6 +2005,7 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
         }
         return launch_status();
     }
+    if (log_on()) std::fprintf(stderr, "w4a8: w4a8_linear M=%d K=%d N=%d -> quant_act + w4a8_gemm\n", M, L.K, L.N);
     if ((st = w4a8_quant_act(X, M, K, ldx, Xq, sx, stream))) return st;
     return w4a8_gemm(Xq, sx, M, blob, d, Y, ldy, out_dtype, stream);
 }
@@ -2118,6 +2138,16 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
                          void* Y, int out_dtype, int mt, hipStream_t s, int8_t* Hq = nullptr, float* sh = nullptr,
                          const float* s_dn = nullptr) {
     const Layout L = layout_of(d);
+    if (log_on()) {
+        const int nsb = L.K / SB_K;
+        const char* cold = moe_stream_fits(L.K, gps_of(d)) ? "gemm_moe_stream_kernel"
+                           : (nsb <= 64 && (mt == 16 || (nsb > 16 && nsb <= 32))) ? "gemm_kslice_kernel"
+                                                                                  : "gemm_decode_kernel (grouped)";
+        std::fprintf(stderr, "w4a8: %s E=%d rows=%d K=%d N=%d g=%d %s -> %s%s, %d-row tiles\n",
+                     Hq ? "w4a8_moe_gemm_silu_static" : "w4a8_moe_gemm", E, rows, L.K, L.N, L.g,
+                     d->asymmetric ? "asym" : "sym",
+                     rows >= MOE_PREFILL_MIN_ROWS ? "gemm_prefill_kernel (experts with >= 128 rows) + " : "", cold, mt);
+    }
     GemmArgs a = make_args(L, Xq, sx, rows, blobs);
     a.Hq = Hq;
     a.sh = sh;

@@ -586,3 +586,30 @@ def test_w4a16_checks_and_names():
     assert lib.w4a16_gemm(0x10002, 4, 4096, fake, ctypes.byref(d), fake, 14336, 0, None) == E    # alignment
     assert lib.w4a16_gemm(fake, 4, 4096, fake, ctypes.byref(d), fake, 14000, 0, None) == E       # ldy < N
     assert lib.w4a16_gemm(fake, 4, 4096, fake, ctypes.byref(d), fake, 14336, 7, None) == E       # out dtype
+
+
+def test_log_names_the_resolved_kernel():
+    """W4A8_LOG=1: each GEMM entry point prints the kernel variant it resolved to before its
+    launch.  Run in a child process (the flag is read once); on a host without a GPU the launch
+    itself then fails with EHIP, after the line was printed."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes, moe_token_int8_amd as L\n"
+        "lib = L.lib(); f = 0x10000\n"
+        "d = L.desc(4096, 14336, 128, False)\n"
+        "print(lib.w4a8_gemm(f, f, 32, f, ctypes.byref(d), f, 14336, 0, None))\n"
+        "print(lib.w4a8_gemm(f, f, 4096, f, ctypes.byref(L.desc(4096, 14336, 128, True)), f, 14336, 0, None))\n"
+        "print(lib.w4a16_gemm(f, 8, 4096, f, ctypes.byref(d), f, 14336, 0, None))\n"
+    )
+    env = dict(os.environ, W4A8_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr
+    assert "w4a8: w4a8_gemm M=32 K=4096 N=14336 -> w4a8_decode_m32_sym_g128" in r.stderr
+    assert "w4a8: w4a8_gemm M=4096 K=4096 N=14336 -> w4a8_prefill_asym_g128" in r.stderr
+    assert "w4a8: w4a16_gemm M=8 K=4096 N=14336 -> w4a16_decode_m16_sym_g128" in r.stderr
+    env["W4A8_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert "w4a8:" not in r.stderr
