@@ -284,15 +284,16 @@ def cpu_baseline(args, leg, W):
 def prefill_leg(args, L, W, torch, dev, steps):
     """The projection pair at M = 4096 (asymmetric g128), and the up projection again with
     g = 256 (half the per-group epilogues), with per-channel scales (g = K: one epilogue), with
-    binary16 group scales and with g = 32 (four epilogues per superblock), the same weights
-    otherwise."""
+    binary16 group scales, with g = 64 (two epilogues per superblock) and with g = 32 (four),
+    the same weights otherwise."""
     out = {}
     import dataclasses
     g256 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "g256"), group_size=256)
     gk = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "gK"), group_size=W.C3_UP.K)
     h16 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name + "_fp16_scales")
+    g64 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "g64"), group_size=64)
     g32 = dataclasses.replace(W.C3_UP, name=W.C3_UP.name.replace("g128", "g32"), group_size=32)
-    for cfg in (W.C3_UP, W.C3_DOWN, g256, gk, h16, g32):
+    for cfg in (W.C3_UP, W.C3_DOWN, g256, gk, h16, g64, g32):
         d = L.desc(cfg.K, cfg.N, cfg.group_size, cfg.asymmetric, scale_bits=16 if cfg is h16 else 32)
         _, Wt = W.dense_inputs(cfg, M=1)
         blob = torch.from_numpy(L.w4a8_pack(d, Wt)).to(dev)

@@ -991,24 +991,6 @@ constexpr int PF_S_BYTES = (PF_BN / 16) * 4 * 64;        // scales of up to 4 gr
 constexpr int PF_STAGE = PF_A_BYTES + PF_B_BYTES + PF_S_BYTES;
 constexpr int PF_LDS = 2 * PF_STAGE;
 
-// Workgroup id -> (M tile, N tile).  Consecutive ids are dealt round robin to the 8 XCDs,
-// so each XCD is given a contiguous range of tile indices; inside it, tiles are walked in
-// groups of 4 M tiles so that workgroups running together on one XCD share activation and
-// weight tiles in its L2.
-__device__ __forceinline__ void prefill_tile(int b, int mtiles, int ntiles, int* mt, int* nt) {
-    const int T = mtiles * ntiles;
-    const int per = T / 8, rem = T % 8;
-    const int x = b % 8, j = b / 8;
-    const int t = x * per + min(x, rem) + j;
-    constexpr int GM = 4;
-    const int group = t / (GM * ntiles);
-    const int first = group * GM;
-    const int gsz = min(GM, mtiles - first);
-    const int in = t - group * GM * ntiles;
-    *mt = first + in % gsz;
-    *nt = in / gsz;
-}
-
 struct PfRegs {
     uint4 a[4];     // activation pieces
     uint4 b;        // 16 bytes of packed codes (one layout lane of one 16-column tile)
@@ -1944,8 +1926,11 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
     if (M >= PREFILL_MIN_M && !prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
     if (log_on()) std::fprintf(stderr, "w4a8: w4a8_gemm M=%d K=%d N=%d -> %s\n", M, L.K, L.N, w4a8_kernel_name(d, M));
     if (M >= PREFILL_MIN_M) {
-        launch_prefill<MODE_OUT>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), 0,
-                                 L.bits == 8);
+        if (prefill2_fits(a, gps_of(d), L.bits))
+            launch_prefill2(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream));
+        else
+            launch_prefill<MODE_OUT>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), 0,
+                                     L.bits == 8);
         return launch_status();
     }
     const int mt = dense_mt(M);

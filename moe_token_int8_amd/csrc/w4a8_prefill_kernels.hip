@@ -1,0 +1,250 @@
+// Dense W4A8 GEMM for large M with small groups (g = 64 and g = 32) on 16x16x64 INT8 MFMAs, weights
+// straight from the blob into registers.
+//
+// Sources (cited with the page's own section names):
+//   P5 "Inference quantization, chapter 1: the Linear layer" (sgdbs.github.io), section 4: the INT8
+//      "ideal path" (integer GEMM, then the scales in a float epilogue); sections 8.3 and 8.4: per-token
+//      activation scales times per-group weight scales.
+//   P1 "Kimi 2.7 MoE: from 4-bit storage to INT8 (W4A8)" (pwwt.cn), section 5.2: the 4-bit layout
+//      matches the MFMA operand layout, so the nibbles unpack in registers.
+//
+// A workgroup (512 threads, 8 waves) owns a 128 x 128 output tile.  Wave (wm, wn) computes rows
+// [64 wm, +64) and the two 16-column tiles 2 wn, 2 wn + 1 of the workgroup's 8.  Per 128-deep
+// superblock:
+//   - the activation rows [128 x 128] are staged in LDS (double buffered, rows padded by 32 bytes so
+//     a 16x16x64 operand read touches distinct banks); every thread loads 2 pieces of 16 bytes for
+//     the next superblock while the current one is computed;
+//   - each lane loads the 16 bytes of the blob that are its B operand for both 64-deep halves of
+//     each of its 2 column tiles (the blob layout is the 16x16x64 operand layout) and unpacks them
+//     in registers: no LDS traffic for the weights.  The next superblock's codes and zero points are
+//     requested as soon as the current ones are unpacked (half a superblock ahead), its scales a
+//     superblock ahead;
+//   - 4 row blocks x 2 column tiles x 2 halves = 16 MFMAs per wave (32 at g = 32); after each group the int32
+//     sums are scaled into the float32 accumulators (acc = fma(float(P_g), s_g, acc)).
+// At 40 KiB of LDS and <= 128 registers per lane, two workgroups share a compute unit: four waves
+// per SIMD to hide the load and LDS latencies.
+//
+// Why a second prefill kernel: the 256 x 128 kernel (32x32x32 MFMAs, 64 x 64 per wave) closes a
+// group every 64 or 32 k; with two or four epilogues per superblock its live registers pass the
+// 256 per lane it may hold and it spills (10x slower at g = 32).  This one carries a 64 x 32 wave
+// tile and half the accumulators.  At g = 128 and above the 256 x 128 kernel is as fast or faster
+// and stays in use.
+//
+// g = 32: a 64-deep half holds two groups, lanes 0-31 one, lanes 32-63 the other; each group takes
+// its own MFMA with the other lanes' B operand zeroed (twice the MFMA work, which is not the bound
+// here: the per-group epilogue's VALU work is).
+#include <hip/hip_runtime.h>
+
+#include "w4a8_device.h"
+#include "w4a8_internal.h"
+
+namespace w4a8 {
+
+constexpr int P2_BM = 128, P2_THREADS = 512;
+constexpr int P2_ROWB = SB_K + 32;                      // padded activation row (bytes)
+constexpr int P2_STAGE = P2_BM * P2_ROWB;               // 20 KiB
+constexpr int P2_LDS = 2 * P2_STAGE;
+
+template <int GPS, bool ASYM, bool H16>
+__global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int mtiles = (a.M + P2_BM - 1) / P2_BM;
+    const int ntl16 = (a.N + 15) / 16;
+    const int ntiles = (ntl16 + 7) / 8;
+    int mt, nt;
+    prefill_tile(blockIdx.x, mtiles, ntiles, &mt, &nt);
+    const int m0 = mt * P2_BM;
+    const int nsb = a.K / SB_K;
+    const uint8_t* codes = a.blob + a.codes_off;
+    const float* scales = reinterpret_cast<const float*>(a.blob + a.scales_off);
+    const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(a.blob + a.scales_off);
+    const uint8_t* zeros = a.blob + a.zeros_off;
+
+    // this wave's two column tiles (clamped to the last one; their outputs are not stored)
+    uint32_t boff[2], moff[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const uint32_t tl = uint32_t(min(nt * 8 + wn * 2 + c, ntl16 - 1));
+        boff[c] = tl * uint32_t(nsb) * 1024u + uint32_t(lane) * 16u;
+        moff[c] = tl * uint32_t(a.G) * 16u + uint32_t(lane & 15);
+    }
+    // activation pieces: piece p (of 1024) is row p / 8, bytes [16 (p % 8), +16) of the superblock;
+    // thread t stages pieces t and t + 512 (rows past M repeat the last row; never stored)
+    const int8_t* xrow[2];
+    int lofs[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int p = tid + i * P2_THREADS, row = p >> 3, c = p & 7;
+        xrow[i] = a.Xq + size_t(min(m0 + row, a.M - 1)) * a.K + c * 16;
+        lofs[i] = row * P2_ROWB + c * 16;
+    }
+    // row scale of tile row 64 wm + lane, shared by cross-lane reads in the epilogue
+    const float sxl = (m0 + wm * 64 + lane < a.M) ? a.sx[m0 + wm * 64 + lane] : 0.0f;
+
+    auto load_a = [&](uint4 (&xv)[2], int sb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) xv[i] = *reinterpret_cast<const uint4*>(xrow[i] + size_t(sb) * SB_K);
+    };
+    auto store_a = [&](const uint4 (&xv)[2], int stage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(smem + stage * P2_STAGE + lofs[i]) = xv[i];
+    };
+    // weight registers: codes and zero points of the superblock being computed (b0, z0), requested
+    // for the next superblock as soon as the current ones are unpacked; group scales of the current
+    // superblock (s0) and of the next one (s1)
+    uint4 b0[2];
+    float s0[2][GPS], s1[2][GPS != 4 ? GPS : 1];
+    uint32_t z0[2];                                      // zero points, one byte per group
+    auto load_codes = [&](int sb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            b0[c] = *reinterpret_cast<const uint4*>(codes + (boff[c] + uint32_t(sb) * 1024u));
+#pragma unroll
+            for (int gi = 0; gi < GPS; ++gi) {
+                const uint32_t z = ASYM ? uint32_t(zeros[moff[c] + (uint32_t(sb) * GPS + gi) * 16u]) : 0u;
+                z0[c] = gi ? z0[c] | (z << (8 * gi)) : z;
+            }
+        }
+    };
+    auto load_scales = [&](auto& sv, int sb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int gi = 0; gi < GPS; ++gi) {
+                const uint32_t mi = moff[c] + (uint32_t(sb) * GPS + gi) * 16u;
+                sv[c][gi] = H16 ? __uint_as_float(uint32_t(scales16[mi])) : scales[mi];   // binary16: converted at use
+            }
+    };
+
+    float accf[4][2][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accf[r][c][i] = 0.0f;
+    const v4i zero4 = {0, 0, 0, 0};
+
+    // g = 32: lanes 0-31 carry k [0, 32) of a 64-deep half (group 2h), lanes 32-63 k [32, 64)
+    // (group 2h + 1).  Each group takes its own MFMA, with the other lane half's B operand zeroed.
+    constexpr int NSUB = GPS == 4 ? 2 : 1;
+    const bool upper = lane >= 32;
+    auto compute = [&](int stage, int nx) __attribute__((always_inline)) {
+        const uint8_t* st = smem + stage * P2_STAGE + (wm * 64 + (lane & 15)) * P2_ROWB + 16 * (lane >> 4);
+        v4i acc[4][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v4i b[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int zg = GPS == 4 ? 2 * h + int(upper) : GPS == 2 ? h : 0;
+                const uint32_t z = (z0[c] >> (8 * zg)) & 0xffu;
+                const uint32_t zc = ASYM ? (128u - z) * 0x01010101u : 0u;
+                b[c] = unpack_b<ASYM>(h ? b0[c].z : b0[c].x, h ? b0[c].w : b0[c].y, zc);
+            }
+            if (h == 1) load_codes(nx);                  // this superblock's codes are unpacked
+#pragma unroll
+            for (int sub = 0; sub < NSUB; ++sub) {
+                const int gi = GPS == 4 ? 2 * h + sub : GPS == 2 ? h : 0;
+                const bool first = GPS >= 2 || h == 0;
+                v4i bm[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) bm[c] = (GPS != 4 || upper == (sub == 1)) ? b[c] : zero4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint4 av = *reinterpret_cast<const uint4*>(st + r * 16 * P2_ROWB + h * 64);
+                    const v4i A = v4i{int(av.x), int(av.y), int(av.z), int(av.w)};
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        acc[r][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bm[c], first ? zero4 : acc[r][c], 0, 0, 0);
+                }
+                if (GPS >= 2 || h == 1) {
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const float sg = H16 ? f16_to_f32(uint16_t(__float_as_uint(s0[c][gi]))) : s0[c][gi];
+                        const float scl = ASYM ? sg : sg * 0.0625f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) accf[r][c][i] = fmaf(float(acc[r][c][i]), scl, accf[r][c][i]);
+                    }
+                }
+            }
+        }
+    };
+
+    // One superblock ahead through registers, two LDS stages.  Straight-line loop (every
+    // iteration loads, clamped at the end, and stores to the stage not being read), so each wait
+    // names exactly the registers it needs.  With g = 32 the four groups' scales are requested at
+    // the start of their own superblock (a second set would not fit the register budget).
+    constexpr bool SCALES_AHEAD = GPS != 4;
+    uint4 xv[2];
+    load_a(xv, 0);
+    load_codes(0);
+    if (SCALES_AHEAD) load_scales(s0, 0);
+    store_a(xv, 0);
+    __syncthreads();
+    for (int sb = 0; sb < nsb; ++sb) {
+        const int nx = min(sb + 1, nsb - 1);
+        load_a(xv, nx);
+        if (SCALES_AHEAD) load_scales(s1, nx);
+        else load_scales(s0, sb);
+        compute(sb & 1, nx);
+        store_a(xv, (sb & 1) ^ 1);                       // that stage was last read before the barrier below
+        if (SCALES_AHEAD) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int gi = 0; gi < GPS; ++gi) s0[c][gi] = s1[c][gi];
+        }
+        lds_barrier();                                   // LDS hand-off only: global loads may stay in flight
+    }
+
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int tile = nt * 8 + wn * 2 + c;
+        const int col = tile * 16 + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rl = r * 16 + 4 * (lane >> 4) + i;                // row inside the wave's 64
+                const float sxv = __shfl(sxl, rl, 64);
+                const int row = m0 + wm * 64 + rl;
+                if (tile >= ntl16 || col >= a.N || row >= a.M) continue;
+                const float y = accf[r][c][i] * sxv;
+                const size_t yi = size_t(row) * a.ldy + col;
+                if (a.out_f32)
+                    reinterpret_cast<float*>(a.Y)[yi] = y;
+                else
+                    reinterpret_cast<uint16_t*>(a.Y)[yi] = uint16_t(f32_to_bf16_rne(y));
+            }
+    }
+}
+
+template <int GPS, bool ASYM, bool H16>
+static void launch_prefill2_t(const GemmArgs& a, hipStream_t s) {
+    auto kern = gemm_prefill2_kernel<GPS, ASYM, H16>;
+    const int mtiles = (a.M + P2_BM - 1) / P2_BM;
+    const int ntiles = ((a.N + 15) / 16 + 7) / 8;
+    kern<<<dim3(mtiles * ntiles), dim3(P2_THREADS), P2_LDS, s>>>(a);
+}
+
+// 4-bit codes, g in {32, 64}
+bool prefill2_fits(const GemmArgs& a, int gps, int bits) { return bits == 4 && (gps == 2 || gps == 4); }
+
+void launch_prefill2(const GemmArgs& a, int gps, bool asym, hipStream_t s) {
+#define W4A8_P2(GPS_, ASYM_)                                                  \
+    do {                                                                      \
+        if (a.h16) launch_prefill2_t<GPS_, ASYM_, true>(a, s);                \
+        else launch_prefill2_t<GPS_, ASYM_, false>(a, s);                     \
+    } while (0)
+    if (gps == 2) { if (asym) W4A8_P2(2, true); else W4A8_P2(2, false); }
+    else if (asym) launch_prefill2_t<4, true, false>(a, s);   // binary16 scales: g in {64, 128} only
+    else launch_prefill2_t<4, false, false>(a, s);
+#undef W4A8_P2
+}
+
+}  // namespace w4a8
