@@ -301,8 +301,7 @@ int w4a8_moe_align(const int32_t* topk_ids, int T, int k, int E, int32_t* sorted
  * and expert row ranges are clamped to [0, rows).  Experts with no rows read no weights.
  * All experts of a call share one allocation at a fixed stride: the kernels find an expert's
  * weights by one multiply of ids they already hold, with no further dependent load in front of
- * the weight stream.  EINVAL when rows >= 128 and src_rows * K reaches 2^31 (32-bit offsets of
- * the kernel for experts with many rows). */
+ * the weight stream. */
 int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int k,
                   const int32_t* expert_offsets, int E, int rows, int src_rows, const void* blobs_dev,
                   size_t expert_stride, const w4a8_wdesc* d, void* Y, int out_dtype,

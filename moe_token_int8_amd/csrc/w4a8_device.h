@@ -272,5 +272,8 @@ void launch_moe_stream(const GemmArgs& a, int mt, int gps, bool asym, int slots,
 // g in {32, 64}, float32 or binary16 scales, outputs only.
 bool prefill2_fits(const GemmArgs& a, int gps, int bits);
 void launch_prefill2(const GemmArgs& a, int gps, bool asym, hipStream_t s);
+// Its grouped (MoE) form over the experts with moe_lo <= rows < moe_hi, 128-row tiles, g in {64, 128};
+// slots bounds the sum over those experts of ceil(rows_e / 128).
+void launch_prefill2_moe(const GemmArgs& a, int gps, bool asym, int slots, hipStream_t s);
 
 }  // namespace w4a8

@@ -999,18 +999,13 @@ struct PfRegs {
     uint32_t z;     // zero points of this thread's column, one byte per group
 };
 
-// MOE: the grouped form for experts with many rows.  Workgroup (slot, column tile): slot
-// is a PF_BM-row tile of one expert (moe_tile), rows gathered from the token rows when
-// `gather` is set; output row r is the r-th sorted row.
 // W8: 8-bit weight codes, copied to the LDS operand layout as loaded (no unpack).
 // H16: binary16 group scales, converted to float32 before they are staged in LDS.
-template <bool ASYM, int GPS, int MODE, bool MOE, bool W8, bool H16 = false>
+template <bool ASYM, int GPS, int MODE, bool W8, bool H16 = false>
 __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a) {
-    static_assert(!W8 || (!ASYM && !MOE), "8-bit codes: symmetric, dense");
+    static_assert(!W8 || !ASYM, "8-bit codes: symmetric");
     // GPS 0: g = 256, one group per superblock pair (even, odd), which the loop runs back to back
     // GPS -1: per-channel scales (g = K), one int32 sum over all of K and one epilogue
-    static_assert(GPS > 0 || !MOE, "g = 256 and per-channel: dense");
-    static_assert(GPS != 4 || !MOE, "g = 32: dense");
     constexpr int NG = GPS <= 0 ? 1 : GPS;              // scale entries per superblock
     auto gidx = [](int sb, int gi) { return GPS < 0 ? 0 : GPS == 0 ? sb / 2 : sb * GPS + gi; };
     constexpr int SBB = W8 ? 2048 : 1024;                // code bytes per superblock
@@ -1019,37 +1014,16 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     const int wm = wave & 3, wn = wave >> 2;
     const int ntl16 = (a.N + 15) / 16;                   // 16-column tiles in the blob
     const int ntiles = (ntl16 + 7) / 8;
-    int m0, mend, nt, expert = 0;
-    const uint8_t* blob = a.blob;
-    if (!MOE) {
-        const int mtiles = (a.M + PF_BM - 1) / PF_BM;
-        int mt;
-        prefill_tile(blockIdx.x, mtiles, ntiles, &mt, &nt);
-        m0 = mt * PF_BM;
-        mend = a.M;
-    } else {
-        nt = blockIdx.x % ntiles;
-        const TileRows tr = moe_tile<PF_BM>(a, blockIdx.x / ntiles, lane);
-        if (tr.expert < 0) return;                       // uniform over the workgroup
-        m0 = tr.rbeg;
-        mend = tr.rend;
-        expert = tr.expert;
-        blob = a.blob + size_t(tr.expert) * a.expert_stride;
-    }
+    const int mtiles = (a.M + PF_BM - 1) / PF_BM;
+    int mt, nt;
+    prefill_tile(blockIdx.x, mtiles, ntiles, &mt, &nt);
+    const int m0 = mt * PF_BM, mend = a.M;
     const int t0 = nt * 8;                               // first 16-column tile
-    // blob tile of the workgroup's l-th 16-column tile (paired form: 4 gate tiles, then their
-    // 4 up tiles)
-    auto tile_l = [&](int l) { return MOE ? pair_tile(a, t0, l, 8) : t0 + l; };
+    auto tile_l = [&](int l) { return t0 + l; };         // blob tile of the workgroup's l-th tile
     const int nsb = a.K / SB_K;
-    const uint8_t* codes = blob + a.codes_off;
-    const uint8_t* scales_b = blob + a.scales_off;
-    const uint8_t* zeros_b = blob + a.zeros_off;
-    // source activation row of tile row r (rows past the tile repeat its last row); -1 for a
-    // gathered row that names no activation row (it loads row 0 and gets a zero scale)
-    auto src_row = [&](int r) {
-        const int rr = min(m0 + r, mend - 1);
-        return (MOE && a.gather) ? gather_src(a, rr) : rr;
-    };
+    const uint8_t* codes = a.blob + a.codes_off;
+    const uint8_t* scales_b = a.blob + a.scales_off;
+    const uint8_t* zeros_b = a.blob + a.zeros_off;
 
     // staging: thread tid owns layout lane (tid % 64) of 16-column tile (tid / 64)
     const int b_tile = min(tile_l(wave), ntl16 - 1);
@@ -1059,10 +1033,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     // the whole K loop and the superblock advances only the scalar offset, so the loop spends
     // no vector instructions on addresses, and the loads are unconditional, so the compiler
     // can count them and wait for one register set only.  Rows past the tile's end load the
-    // tile's last row (their outputs are never stored).  Offsets are 32-bit: the dense form's
-    // base is the tile's first row and the codes' base is the wave's column tile; the grouped
-    // form's gathered rows are offsets from Xq (the launcher checks that they fit).
-    const int8_t* xbase = MOE ? a.Xq : a.Xq + size_t(m0) * a.K;
+    // tile's last row (their outputs are never stored).  Offsets are 32-bit: the activations'
+    // base is the tile's first row and the codes' base is the wave's column tile (the launcher
+    // checks that PF_BM rows fit).
+    const int8_t* xbase = a.Xq + size_t(m0) * a.K;
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(xbase), 0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
@@ -1075,7 +1049,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     for (int i = 0; i < 4; ++i) {
         const int p = tid + i * PF_THREADS;
         const int row = p >> 3, c = p & 7;
-        aoff[i] = (MOE ? max(src_row(row), 0) : min(m0 + row, mend - 1) - m0) * a.K + c * 16;
+        aoff[i] = (min(m0 + row, mend - 1) - m0) * a.K + c * 16;
     }
     auto gload = [&](PfRegs& r, int sb) {
         sb = __builtin_amdgcn_readfirstlane(sb);         // uniform: the scalar offsets below
@@ -1265,55 +1239,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     }
     if (MODE == MODE_PARTIALS) return;
 
-    // row scale of tile row wm * 64 + lane, loaded once per lane (the gather of a grouped tile
-    // and the scale are two dependent loads); each output register takes its row's by a
-    // cross-lane read
-    float sxl = 0.0f;
-    {
-        const int row = wm * 64 + lane;
-        const int sr = m0 + row < mend ? src_row(row) : -1;
-        if (sr >= 0) sxl = a.sx[sr];
-    }
+    // row scale of tile row wm * 64 + lane, loaded once per lane; each output register takes its
+    // row's by a cross-lane read
+    const float sxl = m0 + wm * 64 + lane < mend ? a.sx[m0 + wm * 64 + lane] : 0.0f;
     auto row_sx = [&](int ms, int r) { return __shfl(sxl, ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3), 64); };
-
-    if (MOE && MODE == MODE_OUT && a.Hq) {
-        // paired form: waves wn = 0 hold the gate outputs and waves wn = 1 the up outputs of the
-        // same rows, lanes and registers.  Each side hands the other half of its outputs over
-        // through LDS (free after the K loop): wn = 1 passes its ns = 0 outputs, wn = 0 its ns = 1
-        // outputs; then wn = 0 forms the codes of h columns ns = 0 and wn = 1 those of ns = 1, so
-        // the SiLU-requant is split evenly over the 8 waves.
-        float* pb = reinterpret_cast<float*>(smem);          // [ns][wm][ms][r][64]
-        const RowScale prs = static_row_scale(a.s_dn[expert]);
-        const int own = wn == 0 ? 0 : 1;                     // ns of the h columns this wave forms
-        float y[2][16];                                      // this wave's outputs at ns = own
-#pragma unroll
-        for (int ms = 0; ms < 2; ++ms) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float sxv = row_sx(ms, r);
-                const float mine = (own == 0 ? accf[ms][0][r] : accf[ms][1][r]) * sxv;
-                const float other = (own == 0 ? accf[ms][1][r] : accf[ms][0][r]) * sxv;
-                y[ms][r] = mine;
-                pb[(((1 - own) * 4 + wm) * 2 * 16 + ms * 16 + r) * 64 + lane] = other;
-            }
-        }
-        __syncthreads();
-        const int gc = nt * 64 + own * 32 + l32;             // column of h
-        if (gc < a.pair_n) {
-#pragma unroll
-            for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 64 + ms * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    if (row >= mend) continue;
-                    const float v = pb[((own * 4 + wm) * 2 * 16 + ms * 16 + r) * 64 + lane];
-                    const float yg = own == 0 ? y[ms][r] : v, yu = own == 0 ? v : y[ms][r];
-                    a.Hq[size_t(row) * a.pair_n + gc] = int8_t(silu_static_code(yg, yu, prs));
-                }
-        }
-        if (nt == 0 && tid < mend - m0) a.sh[m0 + tid] = prs.s;
-        return;
-    }
 
     // row scales, then store
 #pragma unroll
@@ -1716,50 +1645,46 @@ static void launch_kslice(const GemmArgs& a, const KsliceCfg& c, int ms, int gps
 #undef W4A8_KS
 }
 
-// mtiles: row tiles (dense) or an upper bound on the experts' row tiles (MOE)
-template <bool ASYM, int GPS, int MODE, bool MOE, bool W8 = false, bool H16 = false>
-static void launch_prefill_t(const GemmArgs& a, int mtiles, hipStream_t s) {
-    auto kern = gemm_prefill_kernel<ASYM, GPS, MODE, MOE, W8, H16>;
+template <bool ASYM, int GPS, int MODE, bool W8 = false, bool H16 = false>
+static void launch_prefill_t(const GemmArgs& a, hipStream_t s) {
+    auto kern = gemm_prefill_kernel<ASYM, GPS, MODE, W8, H16>;
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS);
     (void)attr;
+    const int mtiles = (a.M + PF_BM - 1) / PF_BM;
     const int ntiles = ((a.N + 15) / 16 + 7) / 8;
     kern<<<dim3(mtiles * ntiles), dim3(PF_THREADS), PF_LDS, s>>>(a);
 }
 
-// gps: groups per superblock (2, 1, 0 for g = 256, -1 per-channel); w8: 8-bit codes.  g = 256,
-// per-channel and 8-bit codes are dense-form only (the entry points check).
-template <int MODE, bool MOE = false>
-static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s, int mtiles = 0, bool w8 = false) {
-    if (!MOE) mtiles = (a.M + PF_BM - 1) / PF_BM;
-    if constexpr (!MOE) {
-        if (gps == 4) {                                   // g = 32
-            if (w8) launch_prefill_t<false, 4, MODE, false, true>(a, mtiles, s);
-            else if (asym) launch_prefill_t<true, 4, MODE, false>(a, mtiles, s);
-            else launch_prefill_t<false, 4, MODE, false>(a, mtiles, s);
-            return;
-        }
-        if (w8) {
-            if (gps == 1) launch_prefill_t<false, 1, MODE, false, true>(a, mtiles, s);
-            else if (gps == 2) launch_prefill_t<false, 2, MODE, false, true>(a, mtiles, s);
-            else if (gps == 0) launch_prefill_t<false, 0, MODE, false, true>(a, mtiles, s);
-            else launch_prefill_t<false, -1, MODE, false, true>(a, mtiles, s);
-            return;
-        }
-        if (gps == 0) {                                   // g = 256
-            if (asym) launch_prefill_t<true, 0, MODE, false>(a, mtiles, s); else launch_prefill_t<false, 0, MODE, false>(a, mtiles, s);
-            return;
-        }
-        if (gps < 0) {                                    // per-channel
-            if (asym) launch_prefill_t<true, -1, MODE, false>(a, mtiles, s); else launch_prefill_t<false, -1, MODE, false>(a, mtiles, s);
-            return;
-        }
+// gps: groups per superblock (4 for g = 32, 2, 1, 0 for g = 256, -1 per-channel); w8: 8-bit codes
+template <int MODE>
+static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s, bool w8 = false) {
+    if (gps == 4) {                                       // g = 32
+        if (w8) launch_prefill_t<false, 4, MODE, true>(a, s);
+        else if (asym) launch_prefill_t<true, 4, MODE>(a, s);
+        else launch_prefill_t<false, 4, MODE>(a, s);
+        return;
+    }
+    if (w8) {
+        if (gps == 1) launch_prefill_t<false, 1, MODE, true>(a, s);
+        else if (gps == 2) launch_prefill_t<false, 2, MODE, true>(a, s);
+        else if (gps == 0) launch_prefill_t<false, 0, MODE, true>(a, s);
+        else launch_prefill_t<false, -1, MODE, true>(a, s);
+        return;
+    }
+    if (gps == 0) {                                       // g = 256
+        if (asym) launch_prefill_t<true, 0, MODE>(a, s); else launch_prefill_t<false, 0, MODE>(a, s);
+        return;
+    }
+    if (gps < 0) {                                        // per-channel
+        if (asym) launch_prefill_t<true, -1, MODE>(a, s); else launch_prefill_t<false, -1, MODE>(a, s);
+        return;
     }
     // 4-bit codes, g in {64, 128}: float32 or binary16 scales
-#define W4A8_PF(ASYM_, GPS_)                                                            \
-    do {                                                                                \
-        if (a.h16) launch_prefill_t<ASYM_, GPS_, MODE, MOE, false, true>(a, mtiles, s); \
-        else launch_prefill_t<ASYM_, GPS_, MODE, MOE>(a, mtiles, s);                    \
+#define W4A8_PF(ASYM_, GPS_)                                                     \
+    do {                                                                         \
+        if (a.h16) launch_prefill_t<ASYM_, GPS_, MODE, false, true>(a, s);       \
+        else launch_prefill_t<ASYM_, GPS_, MODE>(a, s);                          \
     } while (0)
     if (gps == 1) {
         if (asym) W4A8_PF(true, 1); else W4A8_PF(false, 1);
@@ -1769,15 +1694,15 @@ static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s,
 #undef W4A8_PF
 }
 
-// MoE experts with at least this many rows run on the prefill kernel (256-row tiles: each
-// expert's weights are streamed once per 256 rows instead of once per 16 or 32).
+// MoE experts with at least this many rows run on the 128 x 128 tile prefill kernel (each
+// expert's weights are streamed once per 128 rows instead of once per 16 or 32).
 constexpr int MOE_PREFILL_MIN_ROWS = 128;
 
 // Dense GEMMs with more rows than this use the prefill kernel.
 constexpr int PREFILL_MIN_M = 33;
 
-// The prefill kernel reads activations through 32-bit buffer offsets: from the row tile's first
-// row (dense form: PF_BM rows) or from Xq itself (grouped form: every row a gather may name).
+// The 256 x 128 prefill kernel reads activations through 32-bit buffer offsets from the row
+// tile's first row (PF_BM rows).
 static bool prefill_offsets_fit(int K, size_t rows) { return rows * size_t(K) < (size_t(1) << 31); }
 
 static dim3 decode_grid(const Layout& L, const DecodeCfg& c, int ytiles) {
@@ -1929,8 +1854,7 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
         if (prefill2_fits(a, gps_of(d), L.bits))
             launch_prefill2(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream));
         else
-            launch_prefill<MODE_OUT>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), 0,
-                                     L.bits == 8);
+            launch_prefill<MODE_OUT>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), L.bits == 8);
         return launch_status();
     }
     const int mt = dense_mt(M);
@@ -2007,7 +1931,7 @@ int w4a8_gemm_partials(const int8_t* Xq, int M, const void* blob, const w4a8_wde
     a.P = P;
     if (M >= PREFILL_MIN_M) {
         if (!prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
-        launch_prefill<MODE_PARTIALS>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), 0,
+        launch_prefill<MODE_PARTIALS>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream),
                                       L.bits == 8);
         return launch_status();
     }
@@ -2131,7 +2055,8 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
         std::fprintf(stderr, "w4a8: %s E=%d rows=%d K=%d N=%d g=%d %s -> %s%s, %d-row tiles\n",
                      Hq ? "w4a8_moe_gemm_silu_static" : "w4a8_moe_gemm", E, rows, L.K, L.N, L.g,
                      d->asymmetric ? "asym" : "sym",
-                     rows >= MOE_PREFILL_MIN_ROWS ? "gemm_prefill_kernel (experts with >= 128 rows) + " : "", cold, mt);
+                     rows >= MOE_PREFILL_MIN_ROWS ? "gemm_prefill2_kernel (experts with >= 128 rows) + " : "",
+                     cold, mt);
     }
     GemmArgs a = make_args(L, Xq, sx, rows, blobs);
     a.Hq = Hq;
@@ -2150,11 +2075,10 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
     a.moe_lo = 0;
     a.moe_hi = 1 << 30;
     if (rows >= MOE_PREFILL_MIN_ROWS) {
-        // experts with many rows: prefill tiles; slots bound sum_e ceil(rows_e / 256) over
+        // experts with many rows: prefill tiles; slots bound sum_e ceil(rows_e / tile rows) over
         // experts with rows_e >= 128 (surplus workgroups find no tile and exit)
         a.moe_lo = MOE_PREFILL_MIN_ROWS;
-        launch_prefill<MODE_OUT, true>(a, gps_of(d), d->asymmetric, s,
-                                       rows / PF_BM + rows / MOE_PREFILL_MIN_ROWS + 1);
+        launch_prefill2_moe(a, gps_of(d), d->asymmetric, rows / 128 + rows / MOE_PREFILL_MIN_ROWS + 1, s);
         a.moe_lo = 0;
         a.moe_hi = MOE_PREFILL_MIN_ROWS;
     }
@@ -2198,9 +2122,6 @@ static int moe_gemm_check(const int8_t* Xq, const float* sx, const int32_t* gath
     const Layout L = layout_of(d);
     if (E > 1 && stride < L.total) return W4A8_EINVAL;
     if (!aligned16(Xq) || !aligned16(blobs) || (stride & 15)) return W4A8_EINVAL;
-    // the tiles for experts with many rows address every row a gather may name through 32-bit
-    // offsets from Xq
-    if (rows >= MOE_PREFILL_MIN_ROWS && !prefill_offsets_fit(L.K, size_t(src_rows))) return W4A8_EINVAL;
     return W4A8_OK;
 }
 

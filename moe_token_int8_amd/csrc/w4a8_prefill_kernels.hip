@@ -27,8 +27,9 @@
 // Why a second prefill kernel: the 256 x 128 kernel (32x32x32 MFMAs, 64 x 64 per wave) closes a
 // group every 64 or 32 k; with two or four epilogues per superblock its live registers pass the
 // 256 per lane it may hold and it spills (10x slower at g = 32).  This one carries a 64 x 32 wave
-// tile and half the accumulators.  At g = 128 and above the 256 x 128 kernel is as fast or faster
-// and stays in use.
+// tile and half the accumulators.  Dense GEMMs at g >= 128 stay on the 256 x 128 kernel (as fast
+// or faster there); the grouped (MoE) form of experts with many rows runs here at g = 64 and
+// g = 128 (128-row tiles waste fewer rows of an expert's last tile than 256-row ones).
 //
 // g = 32: a 64-deep half holds two groups, lanes 0-31 one, lanes 32-63 the other; each group takes
 // its own MFMA with the other lanes' B operand zeroed (twice the MFMA work, which is not the bound
@@ -45,43 +46,72 @@ constexpr int P2_ROWB = SB_K + 32;                      // padded activation row
 constexpr int P2_STAGE = P2_BM * P2_ROWB;               // 20 KiB
 constexpr int P2_LDS = 2 * P2_STAGE;
 
-template <int GPS, bool ASYM, bool H16>
+// MOE: the grouped form for experts with many rows.  Workgroup (slot, column tile): slot is a
+// 128-row tile of one expert (moe_tile), rows gathered from the token rows when `gather` is set;
+// output row r is the r-th sorted row.  With a.Hq set (paired gate/up blob) waves wn = 0, 1 hold
+// gate tiles and waves wn = 2, 3 the matching up tiles, and the epilogue writes SiLU-requant codes.
+template <int GPS, bool ASYM, bool H16, bool MOE>
 __global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
-    const int mtiles = (a.M + P2_BM - 1) / P2_BM;
     const int ntl16 = (a.N + 15) / 16;
     const int ntiles = (ntl16 + 7) / 8;
-    int mt, nt;
-    prefill_tile(blockIdx.x, mtiles, ntiles, &mt, &nt);
-    const int m0 = mt * P2_BM;
+    int m0, mend, nt, expert = 0;
+    const uint8_t* blob = a.blob;
+    if (!MOE) {
+        const int mtiles = (a.M + P2_BM - 1) / P2_BM;
+        int mt;
+        prefill_tile(blockIdx.x, mtiles, ntiles, &mt, &nt);
+        m0 = mt * P2_BM;
+        mend = a.M;
+    } else {
+        nt = blockIdx.x % ntiles;
+        const TileRows tr = moe_tile<P2_BM>(a, blockIdx.x / ntiles, lane);
+        if (tr.expert < 0) return;                       // uniform over the workgroup
+        m0 = tr.rbeg;
+        mend = tr.rend;
+        expert = tr.expert;
+        blob = a.blob + size_t(tr.expert) * a.expert_stride;
+    }
     const int nsb = a.K / SB_K;
-    const uint8_t* codes = a.blob + a.codes_off;
-    const float* scales = reinterpret_cast<const float*>(a.blob + a.scales_off);
-    const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(a.blob + a.scales_off);
-    const uint8_t* zeros = a.blob + a.zeros_off;
+    const uint8_t* codes = blob + a.codes_off;
+    const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
+    const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(blob + a.scales_off);
+    const uint8_t* zeros = blob + a.zeros_off;
+    // blob tile of the workgroup's l-th 16-column tile (paired form: 4 gate tiles, then their up tiles)
+    auto tile_l = [&](int l) { return MOE ? pair_tile(a, nt * 8, l, 8) : nt * 8 + l; };
+    // source activation row of tile row r (rows past the tile repeat its last row); -1 for a
+    // gathered row that names no activation row (it loads row 0 and gets a zero scale)
+    auto src_row = [&](int r) {
+        const int rr = min(m0 + r, mend - 1);
+        return (MOE && a.gather) ? gather_src(a, rr) : rr;
+    };
 
     // this wave's two column tiles (clamped to the last one; their outputs are not stored)
     uint32_t boff[2], moff[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        const uint32_t tl = uint32_t(min(nt * 8 + wn * 2 + c, ntl16 - 1));
+        const uint32_t tl = uint32_t(min(tile_l(wn * 2 + c), ntl16 - 1));
         boff[c] = tl * uint32_t(nsb) * 1024u + uint32_t(lane) * 16u;
         moff[c] = tl * uint32_t(a.G) * 16u + uint32_t(lane & 15);
     }
     // activation pieces: piece p (of 1024) is row p / 8, bytes [16 (p % 8), +16) of the superblock;
-    // thread t stages pieces t and t + 512 (rows past M repeat the last row; never stored)
+    // thread t stages pieces t and t + 512 (rows past the tile's end repeat its last row; never stored)
     const int8_t* xrow[2];
     int lofs[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int p = tid + i * P2_THREADS, row = p >> 3, c = p & 7;
-        xrow[i] = a.Xq + size_t(min(m0 + row, a.M - 1)) * a.K + c * 16;
+        xrow[i] = a.Xq + size_t(max(src_row(row), 0)) * a.K + c * 16;
         lofs[i] = row * P2_ROWB + c * 16;
     }
     // row scale of tile row 64 wm + lane, shared by cross-lane reads in the epilogue
-    const float sxl = (m0 + wm * 64 + lane < a.M) ? a.sx[m0 + wm * 64 + lane] : 0.0f;
+    float sxl = 0.0f;
+    {
+        const int sr = m0 + wm * 64 + lane < mend ? src_row(wm * 64 + lane) : -1;
+        if (sr >= 0) sxl = a.sx[sr];
+    }
 
     auto load_a = [&](uint4 (&xv)[2], int sb) __attribute__((always_inline)) {
 #pragma unroll
@@ -202,9 +232,46 @@ __global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a
         lds_barrier();                                   // LDS hand-off only: global loads may stay in flight
     }
 
+    if (MOE && a.Hq) {
+        // paired form: gate wave wn (0, 1) and up wave wn + 2 hold the two outputs of the same h
+        // columns in the same lanes and registers.  Each hands one of its column tiles to the
+        // other through LDS (free after the K loop): the gate wave forms the codes of its tile
+        // c = 0, the up wave those of c = 1.
+        float* pb = reinterpret_cast<float*>(smem);      // [to gate, to up][pair][wm][r][i][64]
+        const bool gate = wn < 2;
+        const int pair = gate ? wn : wn - 2;
+        const int own = gate ? 0 : 1;                    // column tile whose codes this wave forms
+        const RowScale prs = static_row_scale(a.s_dn[expert]);
+        float y[4][4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float sxv = __shfl(sxl, r * 16 + 4 * (lane >> 4) + i, 64);
+                y[r][i] = accf[r][own][i] * sxv;
+                pb[((((gate ? 1 : 0) * 2 + pair) * 2 + wm) * 16 + r * 4 + i) * 64 + lane] = accf[r][1 - own][i] * sxv;
+            }
+        __syncthreads();
+        const int hc = (nt * 4 + pair * 2 + own) * 16 + (lane & 15);   // column of h
+        if (hc < a.pair_n) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = m0 + wm * 64 + r * 16 + 4 * (lane >> 4) + i;
+                    if (row >= mend) continue;
+                    const float v = pb[((((gate ? 0 : 1) * 2 + pair) * 2 + wm) * 16 + r * 4 + i) * 64 + lane];
+                    const float yg = gate ? y[r][i] : v, yu = gate ? v : y[r][i];
+                    a.Hq[size_t(row) * a.pair_n + hc] = int8_t(silu_static_code(yg, yu, prs));
+                }
+        }
+        if (nt == 0 && tid < mend - m0) a.sh[m0 + tid] = prs.s;
+        return;
+    }
+
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        const int tile = nt * 8 + wn * 2 + c;
+        const int tile = tile_l(wn * 2 + c);
         const int col = tile * 16 + (lane & 15);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -213,7 +280,7 @@ __global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a
                 const int rl = r * 16 + 4 * (lane >> 4) + i;                // row inside the wave's 64
                 const float sxv = __shfl(sxl, rl, 64);
                 const int row = m0 + wm * 64 + rl;
-                if (tile >= ntl16 || col >= a.N || row >= a.M) continue;
+                if (tile >= ntl16 || col >= a.N || row >= mend) continue;
                 const float y = accf[r][c][i] * sxv;
                 const size_t yi = size_t(row) * a.ldy + col;
                 if (a.out_f32)
@@ -224,10 +291,11 @@ __global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a
     }
 }
 
-template <int GPS, bool ASYM, bool H16>
-static void launch_prefill2_t(const GemmArgs& a, hipStream_t s) {
-    auto kern = gemm_prefill2_kernel<GPS, ASYM, H16>;
-    const int mtiles = (a.M + P2_BM - 1) / P2_BM;
+// slots: row tiles (dense form: 0, derived from M) or an upper bound on the experts' row tiles
+template <int GPS, bool ASYM, bool H16, bool MOE>
+static void launch_prefill2_t(const GemmArgs& a, int slots, hipStream_t s) {
+    auto kern = gemm_prefill2_kernel<GPS, ASYM, H16, MOE>;
+    const int mtiles = MOE ? slots : (a.M + P2_BM - 1) / P2_BM;
     const int ntiles = ((a.N + 15) / 16 + 7) / 8;
     kern<<<dim3(mtiles * ntiles), dim3(P2_THREADS), P2_LDS, s>>>(a);
 }
@@ -238,13 +306,24 @@ bool prefill2_fits(const GemmArgs& a, int gps, int bits) { return bits == 4 && (
 void launch_prefill2(const GemmArgs& a, int gps, bool asym, hipStream_t s) {
 #define W4A8_P2(GPS_, ASYM_)                                                  \
     do {                                                                      \
-        if (a.h16) launch_prefill2_t<GPS_, ASYM_, true>(a, s);                \
-        else launch_prefill2_t<GPS_, ASYM_, false>(a, s);                     \
+        if (a.h16) launch_prefill2_t<GPS_, ASYM_, true, false>(a, 0, s);      \
+        else launch_prefill2_t<GPS_, ASYM_, false, false>(a, 0, s);           \
     } while (0)
     if (gps == 2) { if (asym) W4A8_P2(2, true); else W4A8_P2(2, false); }
-    else if (asym) launch_prefill2_t<4, true, false>(a, s);   // binary16 scales: g in {64, 128} only
-    else launch_prefill2_t<4, false, false>(a, s);
+    else if (asym) launch_prefill2_t<4, true, false, false>(a, 0, s);   // binary16 scales: g in {64, 128} only
+    else launch_prefill2_t<4, false, false, false>(a, 0, s);
 #undef W4A8_P2
+}
+
+void launch_prefill2_moe(const GemmArgs& a, int gps, bool asym, int slots, hipStream_t s) {
+#define W4A8_P2M(GPS_, ASYM_)                                                 \
+    do {                                                                      \
+        if (a.h16) launch_prefill2_t<GPS_, ASYM_, true, true>(a, slots, s);   \
+        else launch_prefill2_t<GPS_, ASYM_, false, true>(a, slots, s);        \
+    } while (0)
+    if (gps == 1) { if (asym) W4A8_P2M(1, true); else W4A8_P2M(1, false); }
+    else { if (asym) W4A8_P2M(2, true); else W4A8_P2M(2, false); }
+#undef W4A8_P2M
 }
 
 }  // namespace w4a8

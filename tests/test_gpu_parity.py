@@ -394,12 +394,15 @@ def test_moe_gemm_grouped_matches_per_expert_oracle():
     _print(check_float_output(Y, Ybf, Y64))
 
 
-@pytest.mark.parametrize("g,asym,K", [(64, True, 256), (128, False, 256), (64, True, 4608), (128, False, 4608)])
-def test_moe_gemm_hot_expert_paths(g, asym, K):
-    """Grouped GEMM where expert 0 owns 280 routed rows (two 256-row MFMA tiles, the second
-    ragged), expert 1 about 160 (one tile) and the others fewer than 128; with and without the row
-    gather.  The others run on the grouped streaming kernel (K = 256) or on the streaming decode
-    kernel (K = 4608)."""
+@pytest.mark.parametrize("g,asym,K,sbits", [(64, True, 256, 32), (128, False, 256, 32), (64, True, 4608, 32),
+                                            (128, False, 4608, 32), (64, False, 1024, 32), (64, True, 768, 16),
+                                            (128, True, 512, 16)])
+def test_moe_gemm_hot_expert_paths(g, asym, K, sbits):
+    """Grouped GEMM where expert 0 owns 280 routed rows (g = 128: two 256-row MFMA tiles, the
+    second ragged; g = 64: three 128-row tiles), expert 1 about 160 (one or two tiles) and the
+    others fewer than 128; with and without the row gather; float32 and binary16 scales.  The
+    others run on the grouped streaming kernel (K <= 4096) or on the streaming decode kernel
+    (K = 4608)."""
     T, k, E, N = 300, 2, 5, 96
     t = np.arange(T)
     ids = np.stack([np.where(t < 280, 0, 1 + t % 4), np.where(t < 150, 1, 2 + t % 3)], axis=1).astype(np.int32)
@@ -407,10 +410,12 @@ def test_moe_gemm_hot_expert_paths(g, asym, K):
     ids[dup, 1] = np.where(ids[dup, 0] == 2, 3, 2)
     cnt = np.bincount(ids.ravel(), minlength=E)
     assert cnt[0] > 256 and 128 <= cnt[1] < 256 and cnt[2:].max() < 128 and cnt.min() > 0
-    d = L.desc(K, N, g, asym)
+    d = L.desc(K, N, g, asym, scale_bits=sbits)
     host, qw = {}, {}
     for e in range(E):
         c = W.random_codes(31 * g + e, K, N, g, asym)
+        if sbits == 16:                                 # scales the binary16 field holds exactly
+            c = (c[0], c[1].astype(np.float16).astype(np.float32), c[2])
         host[e] = L.w4a8_pack_codes(d, *c)
         qw[e] = c
     dev = L.experts_to_device(d, E, host)
