@@ -246,34 +246,12 @@ __device__ __forceinline__ TileRows moe_tile(const GemmArgs& a, int slot, int la
     return tr;
 }
 
-// Workgroup id -> (M tile, N tile).  Consecutive ids are dealt round robin to the 8 XCDs,
-// so each XCD is given a contiguous range of tile indices; inside it, tiles are walked in
-// groups of 4 M tiles so that workgroups running together on one XCD share activation and
-// weight tiles in its L2.
-__device__ __forceinline__ void prefill_tile(int b, int mtiles, int ntiles, int* mt, int* nt) {
-    const int T = mtiles * ntiles;
-    const int per = T / 8, rem = T % 8;
-    const int x = b % 8, j = b / 8;
-    const int t = x * per + min(x, rem) + j;
-    constexpr int GM = 4;
-    const int group = t / (GM * ntiles);
-    const int first = group * GM;
-    const int gsz = min(GM, mtiles - first);
-    const int in = t - group * GM * ntiles;
-    *mt = first + in % gsz;
-    *nt = in / gsz;
-}
-
 // Grouped streaming GEMM (w4a8_moe_kernels.hip): every expert of a launch, K <= 4096, g in {64, 128}.
 bool moe_stream_fits(int K, int gps);
 void launch_moe_stream(const GemmArgs& a, int mt, int gps, bool asym, int slots, hipStream_t s);
 
-// Dense prefill GEMM on 128 x 128 tiles of 16x16x64 MFMAs (w4a8_prefill_kernels.hip): 4-bit codes,
-// g in {32, 64}, float32 or binary16 scales, outputs only.
-bool prefill2_fits(const GemmArgs& a, int gps, int bits);
-void launch_prefill2(const GemmArgs& a, int gps, bool asym, hipStream_t s);
-// Its grouped (MoE) form over the experts with moe_lo <= rows < moe_hi, 128-row tiles, g in {64, 128};
-// slots bounds the sum over those experts of ceil(rows_e / 128).
-void launch_prefill2_moe(const GemmArgs& a, int gps, bool asym, int slots, hipStream_t s);
+// Grouped GEMM on 128 x 128 MFMA tiles (w4a8_moe_tile_kernels.hip) over the experts with
+// moe_lo <= rows < moe_hi, g in {64, 128}; slots bounds the sum over those experts of ceil(rows_e / 128).
+void launch_moe_tile(const GemmArgs& a, int gps, bool asym, int slots, hipStream_t s);
 
 }  // namespace w4a8

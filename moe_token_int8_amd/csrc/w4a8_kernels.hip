@@ -983,6 +983,24 @@ __global__ __launch_bounds__(1024) void gemm_kslice_kernel(GemmArgs a) {
 // ------------------------------------------------------------------------------------
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+// Workgroup id -> (M tile, N tile).  Consecutive ids are dealt round robin to the 8 XCDs,
+// so each XCD is given a contiguous range of tile indices; inside it, tiles are walked in
+// groups of 4 M tiles so that workgroups running together on one XCD share activation and
+// weight tiles in its L2.
+__device__ __forceinline__ void prefill_tile(int b, int mtiles, int ntiles, int* mt, int* nt) {
+    const int T = mtiles * ntiles;
+    const int per = T / 8, rem = T % 8;
+    const int x = b % 8, j = b / 8;
+    const int t = x * per + min(x, rem) + j;
+    constexpr int GM = 4;
+    const int group = t / (GM * ntiles);
+    const int first = group * GM;
+    const int gsz = min(GM, mtiles - first);
+    const int in = t - group * GM * ntiles;
+    *mt = first + in % gsz;
+    *nt = in / gsz;
+}
+
 constexpr int PF_BM = 256, PF_BN = 128, PF_THREADS = 512;
 constexpr int PF_AROW = SB_K + 16;                       // padded activation row (bytes)
 constexpr int PF_A_BYTES = PF_BM * PF_AROW;              // 36864
@@ -1202,39 +1220,28 @@ __global__ __launch_bounds__(PF_THREADS, 1) void gemm_prefill_kernel(GemmArgs a)
     };
 
     // pipeline: register set s%2 holds the loads of superblock s; stage s%2 of LDS holds
-    // superblock s while it is computed
-    // (prefetches past the last superblock reload the last one and are never stored)
-    // The pair loop is straight-line code: the wait before each LDS store then names exactly the
-    // register set it stores (the other set's loads stay in flight).  With conditional stores
-    // and an exit in the middle of the body the compiler merged the paths pessimistically and
-    // waited for every outstanding load, which collapsed the two-superblock prefetch.  The
-    // empty asm statements keep each set's loads issued where they are written.
+    // superblock s while it is computed (prefetches past the last superblock reload the last one
+    // and are never stored).  A straight-line pair loop without the conditional stores and the
+    // mid-loop exit gave per-register waits in the assembly but no measurable speed at g >= 128,
+    // and with two or four group epilogues per superblock its register pressure spilled
+    // (g = 32: 720 -> 140 TOPS), so the loop keeps this form.
     PfRegs R0, R1;
     gload(R0, 0);
     gload(R1, min(1, nsb - 1));
-    asm volatile("" ::: "memory");
     lstore(R0, 0);
     gload(R0, min(2, nsb - 1));
-    asm volatile("" ::: "memory");
     __syncthreads();
-    int kb = 0;
-    for (; kb + 1 < nsb; kb += 2) {
-        // even superblock kb: stage 0; R1 holds kb+1, R0 holds kb+2 (clamped past the end)
-        lstore(R1, 1);
+    for (int kb = 0; kb < nsb; kb += 2) {
+        // even superblock kb: stage 0; R1 holds kb+1, R0 holds kb+2
+        if (kb + 1 < nsb) lstore(R1, 1);
         gload(R1, min(kb + 3, nsb - 1));
-        asm volatile("" ::: "memory");
         compute(0, kb);
         __syncthreads();
-        // odd superblock kb+1: stage 1; R0 holds kb+2, R1 holds kb+3 (stage 0 written past the
-        // end is never computed)
-        lstore(R0, 0);
+        if (kb + 1 >= nsb) break;
+        // odd superblock kb+1: stage 1; R0 holds kb+2, R1 holds kb+3
+        if (kb + 2 < nsb) lstore(R0, 0);
         gload(R0, min(kb + 4, nsb - 1));
-        asm volatile("" ::: "memory");
         compute(1, kb + 1);
-        __syncthreads();
-    }
-    if (kb < nsb) {                                      // odd nsb: the last superblock, in stage 0
-        compute(0, kb);
         __syncthreads();
     }
     if (MODE == MODE_PARTIALS) return;
@@ -1694,8 +1701,8 @@ static void launch_prefill(const GemmArgs& a, int gps, bool asym, hipStream_t s,
 #undef W4A8_PF
 }
 
-// MoE experts with at least this many rows run on the 128 x 128 tile prefill kernel (each
-// expert's weights are streamed once per 128 rows instead of once per 16 or 32).
+// MoE experts with at least this many rows run on 128 x 128 MFMA tiles (gemm_moe_tile_kernel:
+// each expert's weights are streamed once per 128 rows instead of once per 16 or 32).
 constexpr int MOE_PREFILL_MIN_ROWS = 128;
 
 // Dense GEMMs with more rows than this use the prefill kernel.
@@ -1851,10 +1858,7 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
     if (M >= PREFILL_MIN_M && !prefill_offsets_fit(L.K, PF_BM)) return W4A8_EINVAL;
     if (log_on()) std::fprintf(stderr, "w4a8: w4a8_gemm M=%d K=%d N=%d -> %s\n", M, L.K, L.N, w4a8_kernel_name(d, M));
     if (M >= PREFILL_MIN_M) {
-        if (prefill2_fits(a, gps_of(d), L.bits))
-            launch_prefill2(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream));
-        else
-            launch_prefill<MODE_OUT>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), L.bits == 8);
+        launch_prefill<MODE_OUT>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), L.bits == 8);
         return launch_status();
     }
     const int mt = dense_mt(M);
@@ -2055,7 +2059,7 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
         std::fprintf(stderr, "w4a8: %s E=%d rows=%d K=%d N=%d g=%d %s -> %s%s, %d-row tiles\n",
                      Hq ? "w4a8_moe_gemm_silu_static" : "w4a8_moe_gemm", E, rows, L.K, L.N, L.g,
                      d->asymmetric ? "asym" : "sym",
-                     rows >= MOE_PREFILL_MIN_ROWS ? "gemm_prefill2_kernel (experts with >= 128 rows) + " : "",
+                     rows >= MOE_PREFILL_MIN_ROWS ? "gemm_moe_tile_kernel (experts with >= 128 rows) + " : "",
                      cold, mt);
     }
     GemmArgs a = make_args(L, Xq, sx, rows, blobs);
@@ -2078,7 +2082,7 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
         // experts with many rows: prefill tiles; slots bound sum_e ceil(rows_e / tile rows) over
         // experts with rows_e >= 128 (surplus workgroups find no tile and exit)
         a.moe_lo = MOE_PREFILL_MIN_ROWS;
-        launch_prefill2_moe(a, gps_of(d), d->asymmetric, rows / 128 + rows / MOE_PREFILL_MIN_ROWS + 1, s);
+        launch_moe_tile(a, gps_of(d), d->asymmetric, rows / 128 + rows / MOE_PREFILL_MIN_ROWS + 1, s);
         a.moe_lo = 0;
         a.moe_hi = MOE_PREFILL_MIN_ROWS;
     }

@@ -1,15 +1,19 @@
-// Dense W4A8 GEMM for large M with small groups (g = 64 and g = 32) on 16x16x64 INT8 MFMAs, weights
-// straight from the blob into registers.
+// Grouped (MoE) W4A8 GEMM for the experts with many rows: 128 x 128 tiles of 16x16x64 INT8 MFMAs,
+// weights straight from the blob into registers.
 //
 // Sources (cited with the page's own section names):
-//   P5 "Inference quantization, chapter 1: the Linear layer" (sgdbs.github.io), section 4: the INT8
-//      "ideal path" (integer GEMM, then the scales in a float epilogue); sections 8.3 and 8.4: per-token
-//      activation scales times per-group weight scales.
-//   P1 "Kimi 2.7 MoE: from 4-bit storage to INT8 (W4A8)" (pwwt.cn), section 5.2: the 4-bit layout
-//      matches the MFMA operand layout, so the nibbles unpack in registers.
+//   P1 "Kimi 2.7 MoE: from 4-bit storage to INT8 (W4A8)" (pwwt.cn), section 4.4 step 4: the grouped
+//      expert GEMM over router-sorted tokens; section 5.2: the 4-bit layout matches the MFMA operand
+//      layout, so the nibbles unpack in registers; section 8: the activation quantization folded
+//      into the GEMM (the paired gate/up epilogue below).
+//   P5 "Inference quantization, chapter 1: the Linear layer" (sgdbs.github.io), section 4: integer
+//      GEMM, then the scales in a float epilogue; sections 8.3 and 8.4: per-token activation scales
+//      times per-group weight scales.
 //
-// A workgroup (512 threads, 8 waves) owns a 128 x 128 output tile.  Wave (wm, wn) computes rows
-// [64 wm, +64) and the two 16-column tiles 2 wn, 2 wn + 1 of the workgroup's 8.  Per 128-deep
+// Workgroup (slot, column tile): slot is a 128-row tile of one expert (moe_tile; each expert with
+// rows_e in [moe_lo, moe_hi) has ceil(rows_e / 128) of them), rows gathered from the token rows when
+// `gather` is set; output row r is the r-th sorted row.  512 threads, 8 waves: wave (wm, wn) computes
+// tile rows [64 wm, +64) and the 16-column tiles 2 wn, 2 wn + 1 of the workgroup's 8.  Per 128-deep
 // superblock:
 //   - the activation rows [128 x 128] are staged in LDS (double buffered, rows padded by 32 bytes so
 //     a 16x16x64 operand read touches distinct banks); every thread loads 2 pieces of 16 bytes for
@@ -19,21 +23,18 @@
 //     in registers: no LDS traffic for the weights.  The next superblock's codes and zero points are
 //     requested as soon as the current ones are unpacked (half a superblock ahead), its scales a
 //     superblock ahead;
-//   - 4 row blocks x 2 column tiles x 2 halves = 16 MFMAs per wave (32 at g = 32); after each group the int32
+//   - 4 row blocks x 2 column tiles x 2 halves = 16 MFMAs per wave; after each group the int32
 //     sums are scaled into the float32 accumulators (acc = fma(float(P_g), s_g, acc)).
 // At 40 KiB of LDS and <= 128 registers per lane, two workgroups share a compute unit: four waves
 // per SIMD to hide the load and LDS latencies.
 //
-// Why a second prefill kernel: the 256 x 128 kernel (32x32x32 MFMAs, 64 x 64 per wave) closes a
-// group every 64 or 32 k; with two or four epilogues per superblock its live registers pass the
-// 256 per lane it may hold and it spills (10x slower at g = 32).  This one carries a 64 x 32 wave
-// tile and half the accumulators.  Dense GEMMs at g >= 128 stay on the 256 x 128 kernel (as fast
-// or faster there); the grouped (MoE) form of experts with many rows runs here at g = 64 and
-// g = 128 (128-row tiles waste fewer rows of an expert's last tile than 256-row ones).
+// Why not the dense prefill kernel's 256 x 128 tiles: an expert's last tile is partly empty, and
+// 128-row tiles waste fewer of its MFMA rows; with 64 x 32 per wave the accumulators leave the
+// registers for two resident workgroups at g = 64 as well as g = 128.
 //
-// g = 32: a 64-deep half holds two groups, lanes 0-31 one, lanes 32-63 the other; each group takes
-// its own MFMA with the other lanes' B operand zeroed (twice the MFMA work, which is not the bound
-// here: the per-group epilogue's VALU work is).
+// Paired form (a.Hq set, gate/up blob): the workgroup's tiles 0-3 are gate tiles and 4-7 the
+// matching up tiles, so gate wave wn (0, 1) and up wave wn + 2 hold the two outputs of the same h
+// columns in the same lanes and registers; the epilogue writes SiLU-requant codes instead of Y.
 #include <hip/hip_runtime.h>
 
 #include "w4a8_device.h"
@@ -41,51 +42,37 @@
 
 namespace w4a8 {
 
-constexpr int P2_BM = 128, P2_THREADS = 512;
-constexpr int P2_ROWB = SB_K + 32;                      // padded activation row (bytes)
-constexpr int P2_STAGE = P2_BM * P2_ROWB;               // 20 KiB
-constexpr int P2_LDS = 2 * P2_STAGE;
+constexpr int MTL_BM = 128, MTL_THREADS = 512;
+constexpr int MTL_ROWB = SB_K + 32;                     // padded activation row (bytes)
+constexpr int MTL_STAGE = MTL_BM * MTL_ROWB;            // 20 KiB
+constexpr int MTL_LDS = 2 * MTL_STAGE;
 
-// MOE: the grouped form for experts with many rows.  Workgroup (slot, column tile): slot is a
-// 128-row tile of one expert (moe_tile), rows gathered from the token rows when `gather` is set;
-// output row r is the r-th sorted row.  With a.Hq set (paired gate/up blob) waves wn = 0, 1 hold
-// gate tiles and waves wn = 2, 3 the matching up tiles, and the epilogue writes SiLU-requant codes.
-template <int GPS, bool ASYM, bool H16, bool MOE>
-__global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a) {
+// GPS: groups per superblock, 2 (g = 64) or 1 (g = 128).  H16: binary16 group scales.
+template <int GPS, bool ASYM, bool H16>
+__global__ __launch_bounds__(MTL_THREADS, 4) void gemm_moe_tile_kernel(GemmArgs a) {
+    static_assert(GPS == 1 || GPS == 2, "grouped formats: g in {64, 128}");
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int ntl16 = (a.N + 15) / 16;
     const int ntiles = (ntl16 + 7) / 8;
-    int m0, mend, nt, expert = 0;
-    const uint8_t* blob = a.blob;
-    if (!MOE) {
-        const int mtiles = (a.M + P2_BM - 1) / P2_BM;
-        int mt;
-        prefill_tile(blockIdx.x, mtiles, ntiles, &mt, &nt);
-        m0 = mt * P2_BM;
-        mend = a.M;
-    } else {
-        nt = blockIdx.x % ntiles;
-        const TileRows tr = moe_tile<P2_BM>(a, blockIdx.x / ntiles, lane);
-        if (tr.expert < 0) return;                       // uniform over the workgroup
-        m0 = tr.rbeg;
-        mend = tr.rend;
-        expert = tr.expert;
-        blob = a.blob + size_t(tr.expert) * a.expert_stride;
-    }
+    const int nt = blockIdx.x % ntiles;
+    const TileRows tr = moe_tile<MTL_BM>(a, blockIdx.x / ntiles, lane);
+    if (tr.expert < 0) return;                           // uniform over the workgroup
+    const int m0 = tr.rbeg, mend = tr.rend, expert = tr.expert;
+    const uint8_t* blob = a.blob + size_t(expert) * a.expert_stride;
     const int nsb = a.K / SB_K;
     const uint8_t* codes = blob + a.codes_off;
     const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
     const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(blob + a.scales_off);
     const uint8_t* zeros = blob + a.zeros_off;
     // blob tile of the workgroup's l-th 16-column tile (paired form: 4 gate tiles, then their up tiles)
-    auto tile_l = [&](int l) { return MOE ? pair_tile(a, nt * 8, l, 8) : nt * 8 + l; };
+    auto tile_l = [&](int l) { return pair_tile(a, nt * 8, l, 8); };
     // source activation row of tile row r (rows past the tile repeat its last row); -1 for a
     // gathered row that names no activation row (it loads row 0 and gets a zero scale)
     auto src_row = [&](int r) {
         const int rr = min(m0 + r, mend - 1);
-        return (MOE && a.gather) ? gather_src(a, rr) : rr;
+        return a.gather ? gather_src(a, rr) : rr;
     };
 
     // this wave's two column tiles (clamped to the last one; their outputs are not stored)
@@ -102,9 +89,9 @@ __global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a
     int lofs[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int p = tid + i * P2_THREADS, row = p >> 3, c = p & 7;
+        const int p = tid + i * MTL_THREADS, row = p >> 3, c = p & 7;
         xrow[i] = a.Xq + size_t(max(src_row(row), 0)) * a.K + c * 16;
-        lofs[i] = row * P2_ROWB + c * 16;
+        lofs[i] = row * MTL_ROWB + c * 16;
     }
     // row scale of tile row 64 wm + lane, shared by cross-lane reads in the epilogue
     float sxl = 0.0f;
@@ -119,13 +106,13 @@ __global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a
     };
     auto store_a = [&](const uint4 (&xv)[2], int stage) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(smem + stage * P2_STAGE + lofs[i]) = xv[i];
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(smem + stage * MTL_STAGE + lofs[i]) = xv[i];
     };
     // weight registers: codes and zero points of the superblock being computed (b0, z0), requested
     // for the next superblock as soon as the current ones are unpacked; group scales of the current
-    // superblock (s0) and of the next one (s1)
+    // superblock (s0) and of the next one (s1), binary16 ones as their bits (converted at use)
     uint4 b0[2];
-    float s0[2][GPS], s1[2][GPS != 4 ? GPS : 1];
+    float s0[2][GPS], s1[2][GPS];
     uint32_t z0[2];                                      // zero points, one byte per group
     auto load_codes = [&](int sb) __attribute__((always_inline)) {
 #pragma unroll
@@ -138,13 +125,13 @@ __global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a
             }
         }
     };
-    auto load_scales = [&](auto& sv, int sb) __attribute__((always_inline)) {
+    auto load_scales = [&](float (&sv)[2][GPS], int sb) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int gi = 0; gi < GPS; ++gi) {
                 const uint32_t mi = moff[c] + (uint32_t(sb) * GPS + gi) * 16u;
-                sv[c][gi] = H16 ? __uint_as_float(uint32_t(scales16[mi])) : scales[mi];   // binary16: converted at use
+                sv[c][gi] = H16 ? __uint_as_float(uint32_t(scales16[mi])) : scales[mi];
             }
     };
 
@@ -157,49 +144,37 @@ __global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a
             for (int i = 0; i < 4; ++i) accf[r][c][i] = 0.0f;
     const v4i zero4 = {0, 0, 0, 0};
 
-    // g = 32: lanes 0-31 carry k [0, 32) of a 64-deep half (group 2h), lanes 32-63 k [32, 64)
-    // (group 2h + 1).  Each group takes its own MFMA, with the other lane half's B operand zeroed.
-    constexpr int NSUB = GPS == 4 ? 2 : 1;
-    const bool upper = lane >= 32;
     auto compute = [&](int stage, int nx) __attribute__((always_inline)) {
-        const uint8_t* st = smem + stage * P2_STAGE + (wm * 64 + (lane & 15)) * P2_ROWB + 16 * (lane >> 4);
+        const uint8_t* st = smem + stage * MTL_STAGE + (wm * 64 + (lane & 15)) * MTL_ROWB + 16 * (lane >> 4);
         v4i acc[4][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            const int gi = GPS == 2 ? h : 0;
             v4i b[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const int zg = GPS == 4 ? 2 * h + int(upper) : GPS == 2 ? h : 0;
-                const uint32_t z = (z0[c] >> (8 * zg)) & 0xffu;
-                const uint32_t zc = ASYM ? (128u - z) * 0x01010101u : 0u;
+                const uint32_t zc = ASYM ? (128u - ((z0[c] >> (8 * gi)) & 0xffu)) * 0x01010101u : 0u;
                 b[c] = unpack_b<ASYM>(h ? b0[c].z : b0[c].x, h ? b0[c].w : b0[c].y, zc);
             }
             if (h == 1) load_codes(nx);                  // this superblock's codes are unpacked
+            const bool first = GPS == 2 || h == 0;
 #pragma unroll
-            for (int sub = 0; sub < NSUB; ++sub) {
-                const int gi = GPS == 4 ? 2 * h + sub : GPS == 2 ? h : 0;
-                const bool first = GPS >= 2 || h == 0;
-                v4i bm[2];
+            for (int r = 0; r < 4; ++r) {
+                const uint4 av = *reinterpret_cast<const uint4*>(st + r * 16 * MTL_ROWB + h * 64);
+                const v4i A = v4i{int(av.x), int(av.y), int(av.z), int(av.w)};
 #pragma unroll
-                for (int c = 0; c < 2; ++c) bm[c] = (GPS != 4 || upper == (sub == 1)) ? b[c] : zero4;
+                for (int c = 0; c < 2; ++c)
+                    acc[r][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, b[c], first ? zero4 : acc[r][c], 0, 0, 0);
+            }
+            if (GPS == 2 || h == 1) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint4 av = *reinterpret_cast<const uint4*>(st + r * 16 * P2_ROWB + h * 64);
-                    const v4i A = v4i{int(av.x), int(av.y), int(av.z), int(av.w)};
+                for (int c = 0; c < 2; ++c) {
+                    const float sg = H16 ? f16_to_f32(uint16_t(__float_as_uint(s0[c][gi]))) : s0[c][gi];
+                    const float scl = ASYM ? sg : sg * 0.0625f;
 #pragma unroll
-                    for (int c = 0; c < 2; ++c)
-                        acc[r][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bm[c], first ? zero4 : acc[r][c], 0, 0, 0);
-                }
-                if (GPS >= 2 || h == 1) {
+                    for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        const float sg = H16 ? f16_to_f32(uint16_t(__float_as_uint(s0[c][gi]))) : s0[c][gi];
-                        const float scl = ASYM ? sg : sg * 0.0625f;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) accf[r][c][i] = fmaf(float(acc[r][c][i]), scl, accf[r][c][i]);
-                    }
+                        for (int i = 0; i < 4; ++i) accf[r][c][i] = fmaf(float(acc[r][c][i]), scl, accf[r][c][i]);
                 }
             }
         }
@@ -207,32 +182,27 @@ __global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a
 
     // One superblock ahead through registers, two LDS stages.  Straight-line loop (every
     // iteration loads, clamped at the end, and stores to the stage not being read), so each wait
-    // names exactly the registers it needs.  With g = 32 the four groups' scales are requested at
-    // the start of their own superblock (a second set would not fit the register budget).
-    constexpr bool SCALES_AHEAD = GPS != 4;
+    // names exactly the registers it needs.
     uint4 xv[2];
     load_a(xv, 0);
     load_codes(0);
-    if (SCALES_AHEAD) load_scales(s0, 0);
+    load_scales(s0, 0);
     store_a(xv, 0);
     __syncthreads();
     for (int sb = 0; sb < nsb; ++sb) {
         const int nx = min(sb + 1, nsb - 1);
         load_a(xv, nx);
-        if (SCALES_AHEAD) load_scales(s1, nx);
-        else load_scales(s0, sb);
+        load_scales(s1, nx);
         compute(sb & 1, nx);
         store_a(xv, (sb & 1) ^ 1);                       // that stage was last read before the barrier below
-        if (SCALES_AHEAD) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int gi = 0; gi < GPS; ++gi) s0[c][gi] = s1[c][gi];
-        }
+            for (int gi = 0; gi < GPS; ++gi) s0[c][gi] = s1[c][gi];
         lds_barrier();                                   // LDS hand-off only: global loads may stay in flight
     }
 
-    if (MOE && a.Hq) {
+    if (a.Hq) {
         // paired form: gate wave wn (0, 1) and up wave wn + 2 hold the two outputs of the same h
         // columns in the same lanes and registers.  Each hands one of its column tiles to the
         // other through LDS (free after the K loop): the gate wave forms the codes of its tile
@@ -291,39 +261,21 @@ __global__ __launch_bounds__(P2_THREADS, 4) void gemm_prefill2_kernel(GemmArgs a
     }
 }
 
-// slots: row tiles (dense form: 0, derived from M) or an upper bound on the experts' row tiles
-template <int GPS, bool ASYM, bool H16, bool MOE>
-static void launch_prefill2_t(const GemmArgs& a, int slots, hipStream_t s) {
-    auto kern = gemm_prefill2_kernel<GPS, ASYM, H16, MOE>;
-    const int mtiles = MOE ? slots : (a.M + P2_BM - 1) / P2_BM;
+template <int GPS, bool ASYM, bool H16>
+static void launch_moe_tile_t(const GemmArgs& a, int slots, hipStream_t s) {
     const int ntiles = ((a.N + 15) / 16 + 7) / 8;
-    kern<<<dim3(mtiles * ntiles), dim3(P2_THREADS), P2_LDS, s>>>(a);
+    gemm_moe_tile_kernel<GPS, ASYM, H16><<<dim3(slots * ntiles), dim3(MTL_THREADS), MTL_LDS, s>>>(a);
 }
 
-// 4-bit codes, g in {32, 64}
-bool prefill2_fits(const GemmArgs& a, int gps, int bits) { return bits == 4 && (gps == 2 || gps == 4); }
-
-void launch_prefill2(const GemmArgs& a, int gps, bool asym, hipStream_t s) {
-#define W4A8_P2(GPS_, ASYM_)                                                  \
+void launch_moe_tile(const GemmArgs& a, int gps, bool asym, int slots, hipStream_t s) {
+#define W4A8_MTL(GPS_, ASYM_)                                                 \
     do {                                                                      \
-        if (a.h16) launch_prefill2_t<GPS_, ASYM_, true, false>(a, 0, s);      \
-        else launch_prefill2_t<GPS_, ASYM_, false, false>(a, 0, s);           \
+        if (a.h16) launch_moe_tile_t<GPS_, ASYM_, true>(a, slots, s);         \
+        else launch_moe_tile_t<GPS_, ASYM_, false>(a, slots, s);              \
     } while (0)
-    if (gps == 2) { if (asym) W4A8_P2(2, true); else W4A8_P2(2, false); }
-    else if (asym) launch_prefill2_t<4, true, false, false>(a, 0, s);   // binary16 scales: g in {64, 128} only
-    else launch_prefill2_t<4, false, false, false>(a, 0, s);
-#undef W4A8_P2
-}
-
-void launch_prefill2_moe(const GemmArgs& a, int gps, bool asym, int slots, hipStream_t s) {
-#define W4A8_P2M(GPS_, ASYM_)                                                 \
-    do {                                                                      \
-        if (a.h16) launch_prefill2_t<GPS_, ASYM_, true, true>(a, slots, s);   \
-        else launch_prefill2_t<GPS_, ASYM_, false, true>(a, slots, s);        \
-    } while (0)
-    if (gps == 1) { if (asym) W4A8_P2M(1, true); else W4A8_P2M(1, false); }
-    else { if (asym) W4A8_P2M(2, true); else W4A8_P2M(2, false); }
-#undef W4A8_P2M
+    if (gps == 1) { if (asym) W4A8_MTL(1, true); else W4A8_MTL(1, false); }
+    else { if (asym) W4A8_MTL(2, true); else W4A8_MTL(2, false); }
+#undef W4A8_MTL
 }
 
 }  // namespace w4a8

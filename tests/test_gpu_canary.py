@@ -106,7 +106,7 @@ def _experts(seed, E, K, N, g, asym):
 @pytest.mark.parametrize("T,E,k,H,I,g,asym,zipf", [(300, 6, 2, 512, 256, 128, False, 1.1),
                                                    (9, 16, 4, 256, 128, 64, True, 0.0)])
 def test_moe_outputs_guarded_and_deterministic(T, E, k, H, I, g, asym, zipf):
-    """The dynamic layer (experts with many rows on the 256-row tiles when T = 300), its workspace
+    """The dynamic layer (experts with many rows on the 128-row MFMA tiles when T = 300), its workspace
     guarded too; the static layer with the fused SiLU-requant; two format classes side by side."""
     _print(f"guards: moe layers T={T} E={E} k={k} H={H} I={I} g={g} asym={asym}")
     cfg, ids, w, X = _moe_case(T, E, k, H, I, g, asym, 50 + T, zipf)

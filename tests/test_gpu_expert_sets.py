@@ -66,7 +66,7 @@ def test_moe_forward_expert_sets(name):
     if name == "small_rtn":
         cfg, T, rtn = W.MoEConfig("small", 40, 512, 256, 8, 2, 64, True, 51), None, True
         classes = [(4, 64, True, 32), (2, 128, False, 16), (2, 128, True, 32)]
-    elif name == "c4_two_classes":                     # hot experts take the prefill tiles
+    elif name == "c4_two_classes":                     # hot experts take the 128-row MFMA tiles
         cfg, T, rtn = W.C4, None, False
         classes = [(32, 128, False, 32), (32, 64, True, 16)]
     elif name == "c5_4tok_two_classes":

@@ -116,7 +116,7 @@ def _experts(cfg, touched, seed, rtn):
 
 @pytest.mark.parametrize("name", ["small_asym_g64", "small_sym_g128", "c4", "c5_4tok"])
 def test_fp16_scales_moe_forward(name):
-    """The grouped kernels (decode tiles, K-slice groups, prefill tiles for hot experts) with
+    """The grouped kernels (decode tiles, K-slice groups, 128-row MFMA tiles for hot experts) with
     binary16 scales, through the whole layer."""
     if name == "c4":
         cfg, T, rtn = W.C4, None, False

@@ -10,7 +10,7 @@ Two gates per case:
      expf and numpy's exp differ by ulps), and the row scales equal.
 The grouped GEMM itself is pinned against the oracle in test_gpu_parity.py.  The cases reach
 every kernel that serves a grouped launch: the streaming kernel (K <= 4096, 16- and 32-row
-tiles), the 256-row (g = 128) and 128-row (g = 64) tiles of experts with many rows, the K-slice kernel (4096 < K <= 8192,
+tiles), the 128-row MFMA tiles of experts with many rows, the K-slice kernel (4096 < K <= 8192,
 16-row tiles) and the chunked decode kernel (32-row tiles past K = 4096, and K > 8192)."""
 import numpy as np
 import pytest
@@ -108,10 +108,10 @@ def _fused_vs_chain(T, E, k, K, I, g, asym, seed, gather, zipf=0.0, bad_scales=F
 @pytest.mark.parametrize("T,E,k,K,I,g,asym,gather,route", [
     (40, 8, 2, 1024, 256, 128, False, True, "streaming, 16-row tiles, gathered rows"),
     (40, 8, 2, 1024, 256, 64, True, False, "streaming, 16-row tiles, sorted rows"),
-    (300, 4, 2, 512, 80, 64, True, True, "128-row tiles (g = 64) and streaming, 32-row tiles; I % 64 != 0"),
-    (600, 4, 2, 1024, 144, 64, False, True, "128-row tiles (g = 64), symmetric, gathered rows"),
-    (600, 4, 2, 512, 80, 64, True, False, "128-row tiles (g = 64), sorted rows"),
-    (600, 4, 2, 512, 208, 128, False, True, "256-row tiles (g = 128), gathered rows"),
+    (300, 4, 2, 512, 80, 64, True, True, "128-row tiles and streaming, 32-row tiles; I % 64 != 0"),
+    (600, 4, 2, 1024, 144, 64, False, True, "128-row tiles, g = 64, symmetric, gathered rows"),
+    (600, 4, 2, 512, 80, 64, True, False, "128-row tiles, g = 64, sorted rows"),
+    (600, 4, 2, 512, 208, 128, False, True, "128-row tiles, g = 128, gathered rows"),
     (20, 16, 4, 6144, 128, 128, True, False, "K-slice, 16-row tiles"),
     (64, 4, 2, 6144, 96, 64, False, True, "chunked decode kernel, 32-row tiles"),
     (20, 16, 4, 9216, 64, 128, False, False, "chunked decode kernel, 16-row tiles, K > 8192"),
@@ -131,7 +131,7 @@ def test_moe_gemm_silu_static_degenerate_scales():
 @pytest.mark.parametrize("name", ["c4", "c5_8tok"])
 def test_moe_gemm_silu_static_full_shapes(name):
     """The 64-expert top-6 gate/up at full size (Zipf routing: experts with many rows run on
-    256-row tiles) and the 256-expert gate/up (K = 7168, I = 2048) on 8 tokens."""
+    128-row MFMA tiles) and the 256-expert gate/up (K = 7168, I = 2048) on 8 tokens."""
     if name == "c4":
         c = W.C4
         _print(f"fused gate/up + static SiLU-requant: {c.name} full")

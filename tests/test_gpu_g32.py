@@ -1,9 +1,8 @@
 """GPU parity of the group size 32 format (one fp32 scale, and zero point, per 32 rows of a
 column; P3 lists g among the format choices) through the dense decode and prefill kernels.
-A 128-deep superblock holds four groups: the prefill kernel's partials form closes a group
-after every 32-deep MFMA step; the prefill outputs (128 x 128 tile kernel) and the decode
-kernels run each 64-deep MFMA twice, once per group, with the other group's lanes of the
-weight operand zeroed.
+A 128-deep superblock holds four groups: the prefill kernel closes a group after every
+32-deep MFMA step; the decode kernels run each 64-deep MFMA twice, once per group, with the
+other group's lanes of the weight operand zeroed.
 
 Same gates as the other formats: INT32 per-group partials bit for bit against the oracle,
 float outputs through gpu_cases.check_float_output, w4a8_linear bit-identical to quant_act

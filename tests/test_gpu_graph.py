@@ -63,7 +63,7 @@ def _replays_match(fn, out, n=4):
 
 
 def test_moe_forward_graph_with_hot_experts():
-    """300 tokens over 4 experts, top-2: every expert has >= 128 rows (the 256-row tiles)."""
+    """300 tokens over 4 experts, top-2: every expert has >= 128 rows (the 128-row MFMA tiles)."""
     _print("graph: moe_forward, experts with many rows")
     cfg, ids, w, X = _layer(300, 4, 2, 512, 256, 11)
     gud, gdev = _experts(3, cfg.E, cfg.H, 2 * cfg.I, 128, False)

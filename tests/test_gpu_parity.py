@@ -398,9 +398,8 @@ def test_moe_gemm_grouped_matches_per_expert_oracle():
                                             (128, False, 4608, 32), (64, False, 1024, 32), (64, True, 768, 16),
                                             (128, True, 512, 16)])
 def test_moe_gemm_hot_expert_paths(g, asym, K, sbits):
-    """Grouped GEMM where expert 0 owns 280 routed rows (g = 128: two 256-row MFMA tiles, the
-    second ragged; g = 64: three 128-row tiles), expert 1 about 160 (one or two tiles) and the
-    others fewer than 128; with and without the row gather; float32 and binary16 scales.  The
+    """Grouped GEMM where expert 0 owns 280 routed rows (three 128-row MFMA tiles, the third
+    ragged), expert 1 about 160 (two tiles) and the others fewer than 128; with and without the row gather; float32 and binary16 scales.  The
     others run on the grouped streaming kernel (K <= 4096) or on the streaming decode kernel
     (K = 4608)."""
     T, k, E, N = 300, 2, 5, 96

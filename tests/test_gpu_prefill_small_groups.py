@@ -1,7 +1,7 @@
-"""GPU parity of the prefill GEMM for small groups (g = 64 and g = 32; P3 lists g among the format
-choices): at M >= 33 with 4-bit codes these formats run on the 128 x 128 tile kernel of
-16x16x64 MFMAs (at g = 32 each 64-deep half holds two groups, one per lane half, and takes two
-MFMAs with the other half's weight operand zeroed).
+"""GPU parity of the prefill GEMM's float outputs for small groups (g = 64 and g = 32; P3 lists g
+among the format choices): two and four group epilogues per superblock, which set the prefill
+kernel's register budget (each 32-deep MFMA step closes a group at g = 32, every second one at
+g = 64).
 
 Gates: float outputs through gpu_cases.check_float_output against the float64 oracle, on ragged
 shapes (M and N not multiples of the 128 x 128 tile, N not a multiple of 16, one superblock, an
