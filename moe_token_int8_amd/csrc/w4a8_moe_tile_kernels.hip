@@ -1,5 +1,5 @@
-// Grouped (MoE) W4A8 GEMM for the experts with many rows: 128 x 128 tiles of 16x16x64 INT8 MFMAs,
-// weights straight from the blob into registers.
+// Grouped (MoE) W4A8 GEMM for the experts with many rows (>= 96): 128 x 128 tiles of 16x16x64
+// INT8 MFMAs, weights straight from the blob into registers.
 //
 // Sources (cited with the page's own section names):
 //   P1 "Kimi 2.7 MoE: from 4-bit storage to INT8 (W4A8)" (pwwt.cn), section 4.4 step 4: the grouped
