@@ -620,6 +620,26 @@ def test_moe_gemm_gather_out_of_range(T, E, K, N, g):
     _grouped_vs_oracle(ids, E, K, N, g, True, seed=T + N, bad=bad)
 
 
+@pytest.mark.parametrize("K,g,asym,bad", [(256, 64, True, False), (4608, 128, False, False), (1024, 128, True, True)])
+def test_moe_gemm_tile_cut_boundaries(K, g, asym, bad):
+    """Experts at the edges of the 96-row MFMA-tile cut and of the 128-row tiles: 95 rows (the
+    streaming or K-slice kernel), 96, 127, 128, 129 and 256 rows (one tile, one full tile, a
+    one-row second tile, two full tiles), plus a 3-row and an empty expert; N ends mid 16-column
+    tile.  One token per routed row (k = 1), gathered and sorted rows; with `bad`, gather entries
+    that name no token inside the 96- and 256-row experts."""
+    counts = [95, 96, 127, 128, 129, 256, 3, 0]
+    E, N = len(counts), 200
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    ids = np.random.default_rng(K + g).permutation(ids).reshape(-1, 1)
+    T = ids.shape[0]
+    positions = []
+    if bad:                                             # sorted-order rows inside experts 1 and 5
+        off = np.concatenate([[0], np.cumsum(counts)])
+        positions = [int(off[1]) + 3, int(off[1]) + 95, int(off[5]), int(off[5]) + 200, int(off[6]) - 1]
+    _print(f"tile cut boundaries K={K} g={g} asym={asym} bad={bad}")
+    _grouped_vs_oracle(ids, E, K, N, g, asym, seed=K + g, bad=positions)
+
+
 def test_moe_forward_c4_full():
     """The 64-expert top-6 layer at full size (T=512, H=4096, I=1408), random codes."""
     cfg = W.C4
