@@ -222,7 +222,6 @@ def measured_traffic(kernel):
     when there is none or it was taken on a different kernel source."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.txt")
-    src = os.path.join(ROOT, "moe_token_int8_amd", "csrc", "w4a8_kernels.hip")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -230,7 +229,10 @@ def measured_traffic(kernel):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip().split()[0] if v.strip() else ""
-    if rec.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    # the source file that holds the kernel (named in the summary) must be the one the counters
+    # were taken on
+    src = os.path.join(ROOT, "moe_token_int8_amd", "csrc", rec.get("kernel_source_file", "w4a8_kernels.hip"))
+    if not os.path.exists(src) or rec.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
         return None
     return int(rec["traffic_bytes_per_launch"])
 

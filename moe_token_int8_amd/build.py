@@ -13,7 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libw4a8.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-HIP_SOURCES = ["w4a8_kernels.hip", "w4a16_kernels.hip", "w4a8_moe_kernels.hip", "w4a8_moe_tile_kernels.hip"]
+HIP_SOURCES = ["w4a8_kernels.hip", "w4a16_kernels.hip", "w4a8_moe_kernels.hip", "w4a8_moe_tile_kernels.hip",
+               "w4a8_decode_kernels.hip"]
 HOST_SOURCES = ["w4a8_host.cpp"]     # plain C++ (no device code): built with the host compiler
 CXX = os.environ.get("CXX", "g++")
 

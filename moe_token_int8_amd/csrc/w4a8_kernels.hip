@@ -1776,6 +1776,15 @@ static int check_gemm_desc(const w4a8_wdesc* d) {
     return W4A8_OK;
 }
 
+// w4a8_linear quantizes these rows inside the GEMM (the chunked kernel's fused form: a 16-row
+// tile, K in one chunk, one 16-value piece per thread)
+static bool linear_fuses(const Layout& L, int M) {
+    const DecodeCfg fc = decode_cfg(L.K, 16);
+    const int fcs = fc.kw * fc.sbn;                      // superblocks per chunk
+    return M <= 16 && size_t(M) * L.K <= FUSED_MAX_ELEMS && L.K / SB_K <= fcs &&
+           (M - 1) * fcs * 8 + (L.K / SB_K) * 8 <= 64 * fc.nt * fc.kw;
+}
+
 }  // namespace w4a8
 
 using namespace w4a8;
@@ -1863,6 +1872,12 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
         launch_prefill<MODE_OUT>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), L.bits == 8);
         return launch_status();
     }
+    // rows that w4a8_linear quantizes inside the GEMM stay on the chunked kernel, whose fused form
+    // shares its summation order (fused and unfused results are bit-identical)
+    if (!linear_fuses(L, M) && decode_split_fits(L.K, M, gps_of(d), L.bits)) {
+        launch_decode_split(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream));
+        return launch_status();
+    }
     const int mt = dense_mt(M);
     const DecodeCfg c = decode_cfg(L.K, mt);
     const dim3 grid = decode_grid(L, c, (M + mt - 1) / mt);
@@ -1884,9 +1899,7 @@ int w4a8_linear(const void* X, int M, int K, int ldx, const void* blob, const w4
     // result is bit-identical.  Each workgroup quantizes all M x K activations itself, so
     // fusing pays off only while that redundant work is small next to the launch it saves.
     const DecodeCfg fc = decode_cfg(L.K, 16);
-    const int fcs = fc.kw * fc.sbn;                      // superblocks per chunk
-    if (M <= 16 && size_t(M) * L.K <= FUSED_MAX_ELEMS && L.K / SB_K <= fcs &&
-        (M - 1) * fcs * 8 + (L.K / SB_K) * 8 <= 64 * fc.nt * fc.kw) {
+    if (linear_fuses(L, M)) {
         if (log_on())
             std::fprintf(stderr, "w4a8: w4a8_linear M=%d K=%d N=%d -> %s, quantization fused\n", M, L.K, L.N,
                          w4a8_kernel_name(d, M));
