@@ -447,6 +447,15 @@ def moe_leg(args, L, W, torch, dev, steps):
         ms_sets = timed(lambda: L.w4a8_moe_forward_sets(X, ids_d, w_d, dev_sets, ws, o))
         gu = dn = None
         del dev_sets
+        # every expert at the second class's format (group size g2, float32 scales): with the
+        # binary16-scale layer above, the two single-format layers the two-class layer mixes
+        torch.cuda.empty_cache()
+        gud2, dd2 = cls[1][1], cls[1][2]
+        gu, gs2 = random_device_blobs(L, gud2, cfg.E, seed * 19, dev)
+        dn, ds2 = random_device_blobs(L, dd2, cfg.E, seed * 23, dev)
+        ms_g2 = timed(lambda: L.w4a8_moe_forward(X, ids_d, w_d, cfg.E, gu, gs2, gud2, dn, ds2, dd2, ws, o))
+        del gu, dn
+        gu = dn = None
         touched = len(set(ids.ravel().tolist()))
         wbytes = touched * (gstride + dstride)
         out[cfg.name] = dict(layer_ms=ms, tokens_per_s=cfg.T / (ms * 1e-3), experts_touched=touched,
@@ -454,7 +463,8 @@ def moe_leg(args, L, W, torch, dev, steps):
                              frac_hbm=wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              static_scales_layer_ms=ms_static, static_scales_unfused_chain_ms=ms_static_unfused,
                              fp16_scales_layer_ms=ms_h16,
-                             two_format_classes_layer_ms=ms_sets)
+                             two_format_classes_layer_ms=ms_sets,
+                             **{f"g{g2}_scales_f32_layer_ms": ms_g2})
         del gu, dn, ws, ws_st
         torch.cuda.empty_cache()
     return out

@@ -1306,10 +1306,22 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restri
         }
     }
     __syncthreads();
-    // per-expert totals (E <= 1024: one thread per expert), then a block exclusive scan
+    // Output position of chunk b's first row of expert e: the exclusive prefix sum of the count
+    // matrix read in (expert, chunk) order, i.e. over experts first and over the chunks of one
+    // expert second.  Thread tid scans the NS consecutive entries [tid * NS, tid * NS + NS) of
+    // that order, the threads' totals are scanned across the block, and the entries are
+    // replaced by their positions.
+    // (the whole launch is one workgroup on one compute unit, so the walk steps through
+    // (expert, chunk) without a division per entry)
+    const int n = E * B;
+    const int NS = (n + 1023) / 1024;
+    const int i0 = min(n, tid * NS), cntn = min(n, i0 + NS) - i0;
+    const int e0 = B > 0 ? i0 / B : 0, b0 = B > 0 ? i0 - e0 * B : 0;
     int tot = 0;
-    if (tid < E)
-        for (int b = 0; b < B; ++b) tot += cnt[tid * stride + b];
+    for (int j = 0, e = e0, b = b0; j < cntn; ++j) {
+        tot += cnt[e * stride + b];
+        if (++b == B) { b = 0; ++e; }
+    }
     int incl = tot;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -1320,19 +1332,21 @@ __global__ __launch_bounds__(1024) void moe_align_kernel(const int32_t* __restri
     __syncthreads();
     int wbase = 0;
     for (int w = 0; w < wave; ++w) wbase += wsum[w];
-    const int off = wbase + incl - tot;
-    if (tid < E) {
-        offsets[tid] = off;
-        if (tid == E - 1) offsets[E] = off + tot;
-        int run = off;
-        for (int b = 0; b < B; ++b) {
-            const int c = cnt[tid * stride + b];
-            cnt[tid * stride + b] = run;
-            run += c;
-        }
+    int run = wbase + incl - tot;
+    for (int j = 0, e = e0, b = b0; j < cntn; ++j) {
+        const int c = cnt[e * stride + b];
+        cnt[e * stride + b] = run;
+        run += c;
+        if (++b == B) { b = 0; ++e; }
     }
-    if (E == 0 && tid == 0) offsets[0] = 0;
     __syncthreads();
+    // expert e's rows start at chunk 0's position; the last expert's end is the total
+    if (tid < E) offsets[tid] = B > 0 ? cnt[tid * stride] : 0;
+    if (tid == 0) {
+        int total = 0;
+        for (int w = 0; w < 16; ++w) total += wsum[w];
+        offsets[E] = total;
+    }
     if (tid < B) {
         const int r1 = min(R, (tid + 1) * L);
         for (int r = tid * L; r < r1; ++r) {
