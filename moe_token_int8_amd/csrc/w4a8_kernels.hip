@@ -2075,10 +2075,15 @@ static int join_from(ForkSet* f, hipStream_t s, int i0, int i1) {
 }
 
 // Hq set: the paired form (gate/up blob, static SiLU-requant epilogue into Hq, sh with scales s_dn).
+// rows_cap: a bound on any expert's row count that the caller expects (the layer entry points pass
+// T: a token routes to k distinct experts).  Below the MFMA-tile cut the 128-row tile launch is
+// left out and the streaming kernels serve every expert; they take any row count, so an expert
+// with more rows than the bound (duplicate routing ids) is still computed, only not on the tiles.
 static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gather, int k, const int32_t* offsets,
                          int E, int rows, int src_rows, const void* blobs, size_t stride, const w4a8_wdesc* d,
                          void* Y, int out_dtype, int mt, hipStream_t s, int8_t* Hq = nullptr, float* sh = nullptr,
-                         const float* s_dn = nullptr) {
+                         const float* s_dn = nullptr, int rows_cap = 1 << 30) {
+    const bool tiles = rows >= MOE_TILE_MIN_ROWS && rows_cap >= MOE_TILE_MIN_ROWS;
     const Layout L = layout_of(d);
     if (log_on()) {
         const int nsb = L.K / SB_K;
@@ -2088,7 +2093,7 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
         std::fprintf(stderr, "w4a8: %s E=%d rows=%d K=%d N=%d g=%d %s -> %s%s, %d-row tiles\n",
                      Hq ? "w4a8_moe_gemm_silu_static" : "w4a8_moe_gemm", E, rows, L.K, L.N, L.g,
                      d->asymmetric ? "asym" : "sym",
-                     rows >= MOE_TILE_MIN_ROWS ? "gemm_moe_tile_kernel (experts with >= 96 rows) + " : "",
+                     tiles ? "gemm_moe_tile_kernel (experts with >= 96 rows) + " : "",
                      cold, mt);
     }
     GemmArgs a = make_args(L, Xq, sx, rows, blobs);
@@ -2107,7 +2112,7 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
     a.expert_stride = stride;
     a.moe_lo = 0;
     a.moe_hi = 1 << 30;
-    if (rows >= MOE_TILE_MIN_ROWS) {
+    if (tiles) {
         // experts with many rows: prefill tiles; slots bound sum_e ceil(rows_e / tile rows) over
         // experts with rows_e >= MOE_TILE_MIN_ROWS (surplus workgroups find no tile and exit)
         a.moe_lo = MOE_TILE_MIN_ROWS;
@@ -2158,14 +2163,22 @@ static int moe_gemm_check(const int8_t* Xq, const float* sx, const int32_t* gath
     return W4A8_OK;
 }
 
-int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int k, const int32_t* offsets, int E,
-                  int rows, int src_rows, const void* blobs, size_t stride, const w4a8_wdesc* d, void* Y,
-                  int out_dtype, void* stream) {
+// w4a8_moe_gemm with a bound on the rows of any expert (see moe_gemm_impl)
+static int moe_gemm_capped(const int8_t* Xq, const float* sx, const int32_t* gather, int k, const int32_t* offsets,
+                           int E, int rows, int src_rows, const void* blobs, size_t stride, const w4a8_wdesc* d,
+                           void* Y, int out_dtype, void* stream, int rows_cap) {
     const int st = moe_gemm_check(Xq, sx, gather, k, offsets, E, rows, src_rows, blobs, stride, d, Y, out_dtype);
     if (st || rows == 0) return st;
     const int mt = rows / E >= 16 ? 32 : 16;
     return moe_gemm_impl(Xq, sx, gather, k, offsets, E, rows, src_rows, blobs, stride, d, Y, out_dtype, mt,
-                         static_cast<hipStream_t>(stream));
+                         static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, rows_cap);
+}
+
+int w4a8_moe_gemm(const int8_t* Xq, const float* sx, const int32_t* gather, int k, const int32_t* offsets, int E,
+                  int rows, int src_rows, const void* blobs, size_t stride, const w4a8_wdesc* d, void* Y,
+                  int out_dtype, void* stream) {
+    return moe_gemm_capped(Xq, sx, gather, k, offsets, E, rows, src_rows, blobs, stride, d, Y, out_dtype, stream,
+                           1 << 30);
 }
 
 // Checks of the paired form on top of moe_gemm_check: the blob holds gate and up columns in
@@ -2180,14 +2193,22 @@ static int moe_gemm_silu_check(const int8_t* Xq, const float* sx, const int32_t*
     return W4A8_OK;
 }
 
-int w4a8_moe_gemm_silu_static(const int8_t* Xq, const float* sx, const int32_t* gather, int k,
-                              const int32_t* offsets, int E, int rows, int src_rows, const void* blobs, size_t stride,
-                              const w4a8_wdesc* d, const float* s, int8_t* Hq, float* sh, void* stream) {
+static int moe_gemm_silu_capped(const int8_t* Xq, const float* sx, const int32_t* gather, int k,
+                                const int32_t* offsets, int E, int rows, int src_rows, const void* blobs,
+                                size_t stride, const w4a8_wdesc* d, const float* s, int8_t* Hq, float* sh,
+                                void* stream, int rows_cap) {
     const int st = moe_gemm_silu_check(Xq, sx, gather, k, offsets, E, rows, src_rows, blobs, stride, d, s, Hq, sh);
     if (st || rows == 0) return st;
     const int mt = rows / E >= 16 ? 32 : 16;
     return moe_gemm_impl(Xq, sx, gather, k, offsets, E, rows, src_rows, blobs, stride, d, nullptr, W4A8_OUT_BF16, mt,
-                         static_cast<hipStream_t>(stream), Hq, sh, s);
+                         static_cast<hipStream_t>(stream), Hq, sh, s, rows_cap);
+}
+
+int w4a8_moe_gemm_silu_static(const int8_t* Xq, const float* sx, const int32_t* gather, int k,
+                              const int32_t* offsets, int E, int rows, int src_rows, const void* blobs, size_t stride,
+                              const w4a8_wdesc* d, const float* s, int8_t* Hq, float* sh, void* stream) {
+    return moe_gemm_silu_capped(Xq, sx, gather, k, offsets, E, rows, src_rows, blobs, stride, d, s, Hq, sh, stream,
+                                1 << 30);
 }
 
 // Longest row of the SiLU step: 8 passes of 2048 values per 256-thread workgroup.
@@ -2331,12 +2352,14 @@ int w4a8_moe_forward(const void* X, const int32_t* ids, const float* w, int T, i
     // every step's checks have passed: from here on only a launch error can stop the chain
     if ((st = w4a8_quant_act(X, T, H, H, B.xq, B.sx, stream))) return st;
     if ((st = w4a8_moe_align(ids, T, k, E, B.rows, B.offs, B.inv, stream))) return st;
-    if ((st = w4a8_moe_gemm(B.xq, B.sx, B.rows, k, B.offs, E, R, T, gu_blobs, gu_stride, gu_desc, B.gu,
-                            W4A8_OUT_BF16, stream)))
+    // a token's k rows go to k distinct experts, so no expert has more than T rows (T bounds
+    // the tile launch; duplicate ids stay correct, see moe_gemm_impl)
+    if ((st = moe_gemm_capped(B.xq, B.sx, B.rows, k, B.offs, E, R, T, gu_blobs, gu_stride, gu_desc, B.gu,
+                              W4A8_OUT_BF16, stream, T)))
         return st;
     if ((st = w4a8_silu_mul_quant(B.gu, R, I, B.hq, B.sh, stream))) return st;
-    if ((st = w4a8_moe_gemm(B.hq, B.sh, nullptr, k, B.offs, E, R, R, d_blobs, d_stride, d_desc, B.yd,
-                            W4A8_OUT_BF16, stream)))
+    if ((st = moe_gemm_capped(B.hq, B.sh, nullptr, k, B.offs, E, R, R, d_blobs, d_stride, d_desc, B.yd,
+                              W4A8_OUT_BF16, stream, T)))
         return st;
     return w4a8_moe_combine(B.yd, B.inv, w, T, k, H, out, stream);
 }
@@ -2435,10 +2458,10 @@ int w4a8_moe_forward_sets(const void* X, const int32_t* ids, const float* w, int
         for (int i = 0, e0 = 0; i < nsets; e0 += sets[i].n_experts, ++i) {
             const w4a8_expert_set& c = sets[i];
             void* cs = (i == 0 || !nh) ? stream : static_cast<void*>(f->st[(i - 1) % nh]);
-            r = gate_up ? w4a8_moe_gemm(B.xq, B.sx, B.rows, k, B.offs + e0, c.n_experts, R, T, c.gu_blobs, c.gu_stride,
-                                        c.gu_desc, B.gu, W4A8_OUT_BF16, cs)
-                        : w4a8_moe_gemm(B.hq, B.sh, nullptr, k, B.offs + e0, c.n_experts, R, R, c.d_blobs, c.d_stride,
-                                        c.d_desc, B.yd, W4A8_OUT_BF16, cs);
+            r = gate_up ? moe_gemm_capped(B.xq, B.sx, B.rows, k, B.offs + e0, c.n_experts, R, T, c.gu_blobs,
+                                          c.gu_stride, c.gu_desc, B.gu, W4A8_OUT_BF16, cs, T)
+                        : moe_gemm_capped(B.hq, B.sh, nullptr, k, B.offs + e0, c.n_experts, R, R, c.d_blobs,
+                                          c.d_stride, c.d_desc, B.yd, W4A8_OUT_BF16, cs, T);
             if (r) return r;
         }
         return nh ? join_from(f, s, 0, nh) : W4A8_OK;
@@ -2482,11 +2505,11 @@ int w4a8_moe_forward_static(const void* X, const int32_t* ids, const float* w, i
     // each routed row quantizes its token with the scale of its expert, already in sorted order
     if ((st = w4a8_moe_quant_static(X, T, H, H, B.rows, k, B.offs, E, s_gu, B.xq, B.sx, stream))) return st;
     // gate/up GEMM with the SiLU-requant folded into its epilogue: h's codes, no gate/up buffer
-    if ((st = w4a8_moe_gemm_silu_static(B.xq, B.sx, nullptr, k, B.offs, E, R, R, gu_blobs, gu_stride, gu_desc, s_dn,
-                                        B.hq, B.sh, stream)))
+    if ((st = moe_gemm_silu_capped(B.xq, B.sx, nullptr, k, B.offs, E, R, R, gu_blobs, gu_stride, gu_desc, s_dn,
+                                   B.hq, B.sh, stream, T)))
         return st;
-    if ((st = w4a8_moe_gemm(B.hq, B.sh, nullptr, k, B.offs, E, R, R, d_blobs, d_stride, d_desc, B.yd,
-                            W4A8_OUT_BF16, stream)))
+    if ((st = moe_gemm_capped(B.hq, B.sh, nullptr, k, B.offs, E, R, R, d_blobs, d_stride, d_desc, B.yd,
+                              W4A8_OUT_BF16, stream, T)))
         return st;
     return w4a8_moe_combine(B.yd, B.inv, w, T, k, H, out, stream);
 }

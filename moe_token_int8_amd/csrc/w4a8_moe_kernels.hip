@@ -8,14 +8,14 @@
 //      weight movement, not arithmetic.
 //
 // A workgroup owns one row tile of one expert (up to 32 sorted rows, gathered from the token rows
-// when `gather` is set) and 16 column tiles (256 columns).  It stages the tile's activation rows
-// in LDS once, with coalesced 16-byte loads, and then streams its columns in CG groups of NT tiles:
-// wave (t, q) owns tile t of the group over the K-slice q (SBN superblocks), the weights, scales
-// and zero points of two groups are in flight at a time (double-buffered registers, fully
-// unrolled so every wait is per register), and each group's KW slice sums are added in slice
-// order through LDS before the row scale and the store.  An expert's weights are therefore read
-// once per row tile and its activations once per 256 columns; experts with no rows launch nothing
-// that reads their weights.
+// when `gather` is set) and 16 column tiles (256 columns; 32 tiles on large launches of 16-row
+// tiles).  It stages the tile's activation rows in LDS once, with coalesced 16-byte loads, and
+// then streams its columns in CG groups of NT tiles: wave (t, q) owns tile t of the group over the
+// K-slice q (SBN superblocks), the weights, scales and zero points of two groups are in flight at
+// a time (double-buffered registers, fully unrolled so every wait is per register), and each
+// group's KW slice sums are added in slice order through LDS before the row scale and the store.
+// An expert's weights are therefore read once per row tile and its activations once per 256 (or
+// 512) columns; experts with no rows launch nothing that reads their weights.
 #include <hip/hip_runtime.h>
 
 #include "w4a8_device.h"
@@ -23,13 +23,20 @@
 
 namespace w4a8 {
 
-constexpr int MST_TILES = 16;            // column tiles per workgroup
+// Column tiles per workgroup: 16, or 32 for 16-row tiles on launches of many workgroups.  Measured
+// on the 256-expert down GEMM (K = 2048, 7168 columns, about 215 one-tile experts): 32 tiles per
+// workgroup halve the activation staging per column and the workgroup count, layer 0.964-0.967 ->
+// 0.953-0.958 ms; on the 64-expert layer's cold experts (61 row tiles) 32 tiles leave 1.4 rounds
+// of workgroups, and that layer went from 0.25 to 0.39 ms.
+constexpr int MST_TILES = 16;
+constexpr int MST_TILES_WIDE = 32;
+constexpr long long MST_WIDE_MIN_WG = 4096;   // 16-tile workgroups (upper bound) from which 32 are used
 
-template <int MS, int NT, int KW>
+template <int MS, int NT, int KW, int TILES = MST_TILES>
 struct MoeStreamShape {
     static constexpr int MT = 16 * MS;
     static constexpr int NTHR = 64 * NT * KW;                  // 512
-    static constexpr int CG = MST_TILES / NT;                  // column groups
+    static constexpr int CG = TILES / NT;                      // column groups
     static constexpr size_t LDS_RED = size_t(KW - 1) * NT * MS * 4 * 64 * 4;
     static constexpr size_t LDS_PAIR = size_t(NT) * MS * 4 * 64 * 4;   // paired form: a group's final sums
     // activation rows padded by 32 bytes (a multiple of 128 plus 32: the 16 rows x 4 k-chunks of
@@ -38,9 +45,9 @@ struct MoeStreamShape {
     static_assert(NTHR == 512, "8 waves: two per SIMD, so each has 256 registers");
 };
 
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16>
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16, int TILES = MST_TILES>
 __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
-    using S = MoeStreamShape<MS, NT, KW>;
+    using S = MoeStreamShape<MS, NT, KW, TILES>;
     constexpr int MT = S::MT, NTHR = S::NTHR, CG = S::CG, NV = MS * 4;
     // activation pieces (16 bytes) per thread: the K <= KW * SBN * 128 rows of a full tile
     constexpr int APT = (MT * KW * SBN * 8 + NTHR - 1) / NTHR;
@@ -235,27 +242,27 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
     if (pair && blockIdx.x == 0 && tid < nrows) a.sh[rbeg + tid] = s_e;
 }
 
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16>
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16, int TILES>
 static void launch_moe_stream_t(const GemmArgs& a, int slots, hipStream_t s) {
-    using S = MoeStreamShape<MS, NT, KW>;
-    auto kern = gemm_moe_stream_kernel<MS, NT, KW, SBN, GPS, ASYM, H16>;
+    using S = MoeStreamShape<MS, NT, KW, TILES>;
+    auto kern = gemm_moe_stream_kernel<MS, NT, KW, SBN, GPS, ASYM, H16, TILES>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        int(S::lds(KW * SBN * SB_K)));
     (void)attr;
     const int ntiles = (a.N + 15) / 16;
-    kern<<<dim3((ntiles + MST_TILES - 1) / MST_TILES, slots), dim3(S::NTHR), S::lds(a.K), s>>>(a);
+    kern<<<dim3((ntiles + TILES - 1) / TILES, slots), dim3(S::NTHR), S::lds(a.K), s>>>(a);
 }
 
-template <int MS, int GPS, bool ASYM, bool H16>
+template <int MS, int GPS, bool ASYM, bool H16, int TILES = MST_TILES>
 static void launch_moe_stream_k(const GemmArgs& a, int slots, hipStream_t s) {
     const int nsb = a.K / SB_K;
     // 4 slices of SBN superblocks cover K (up to 32 superblocks)
-    if (nsb <= 8) launch_moe_stream_t<MS, 2, 4, 2, GPS, ASYM, H16>(a, slots, s);
-    else if (nsb <= 12) launch_moe_stream_t<MS, 2, 4, 3, GPS, ASYM, H16>(a, slots, s);
-    else if (nsb <= 16) launch_moe_stream_t<MS, 2, 4, 4, GPS, ASYM, H16>(a, slots, s);
-    else if (nsb <= 24) launch_moe_stream_t<MS, 2, 4, 6, GPS, ASYM, H16>(a, slots, s);
-    else launch_moe_stream_t<MS, 2, 4, 8, GPS, ASYM, H16>(a, slots, s);
+    if (nsb <= 8) launch_moe_stream_t<MS, 2, 4, 2, GPS, ASYM, H16, TILES>(a, slots, s);
+    else if (nsb <= 12) launch_moe_stream_t<MS, 2, 4, 3, GPS, ASYM, H16, TILES>(a, slots, s);
+    else if (nsb <= 16) launch_moe_stream_t<MS, 2, 4, 4, GPS, ASYM, H16, TILES>(a, slots, s);
+    else if (nsb <= 24) launch_moe_stream_t<MS, 2, 4, 6, GPS, ASYM, H16, TILES>(a, slots, s);
+    else launch_moe_stream_t<MS, 2, 4, 8, GPS, ASYM, H16, TILES>(a, slots, s);
 }
 
 bool moe_stream_fits(int K, int gps) { return K <= 32 * SB_K && (gps == 1 || gps == 2); }
@@ -266,7 +273,18 @@ void launch_moe_stream(const GemmArgs& a, int mt, int gps, bool asym, int slots,
         if (a.h16) launch_moe_stream_k<MS_, GPS_, ASYM_, true>(a, slots, s);           \
         else launch_moe_stream_k<MS_, GPS_, ASYM_, false>(a, slots, s);                \
     } while (0)
-    if (mt == 16) {
+    const long long ntiles = (a.N + 15) / 16;
+    const bool wide = (long long)slots * ((ntiles + MST_TILES - 1) / MST_TILES) >= MST_WIDE_MIN_WG;
+    if (mt == 16 && wide) {
+#define W4A8_MSTW(GPS_, ASYM_)                                                              \
+    do {                                                                                    \
+        if (a.h16) launch_moe_stream_k<1, GPS_, ASYM_, true, MST_TILES_WIDE>(a, slots, s);  \
+        else launch_moe_stream_k<1, GPS_, ASYM_, false, MST_TILES_WIDE>(a, slots, s);       \
+    } while (0)
+        if (gps == 1) { if (asym) W4A8_MSTW(1, true); else W4A8_MSTW(1, false); }
+        else { if (asym) W4A8_MSTW(2, true); else W4A8_MSTW(2, false); }
+#undef W4A8_MSTW
+    } else if (mt == 16) {
         if (gps == 1) { if (asym) W4A8_MST(1, 1, true); else W4A8_MST(1, 1, false); }
         else { if (asym) W4A8_MST(1, 2, true); else W4A8_MST(1, 2, false); }
     } else {
