@@ -86,3 +86,19 @@ def test_moe_forward_sets_graph_two_classes():
     ws = torch.empty(L.w4a8_moe_workspace_size(cfg.T, cfg.topk, cfg.H, cfg.I, cfg.E), dtype=torch.uint8, device=DEV)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=DEV)
     _replays_match(lambda: L.w4a8_moe_forward_sets(X, ids, w, sets, ws, out), out)
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_decode_linear_graph(M):
+    """The decode Linear (quantization + GEMM; at 32 rows the split-K-slice kernel, at 1 row the
+    fused quantization) on the 4096 x 14336 projection, captured and replayed."""
+    _print(f"graph: w4a8_linear M={M}")
+    K, N = 4096, 14336
+    d = L.desc(K, N, 128, False)
+    host = L.w4a8_pack_codes(d, *W.random_codes(40 + M, K, N, 128, False))
+    blob = torch.from_numpy(host).to(DEV)
+    X = W.random_activations(50 + M, M, K, outlier_cols=4, outlier_scale=50.0).to(DEV)
+    Xq = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    sx = torch.empty(M, dtype=torch.float32, device=DEV)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    _replays_match(lambda: L.w4a8_linear(X, blob, d, out, Xq, sx), out)
