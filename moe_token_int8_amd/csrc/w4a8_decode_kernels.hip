@@ -198,20 +198,30 @@ __global__ __launch_bounds__(1024) void gemm_decode_split_kernel(GemmArgs a) {
 
     // 6. slice partials into this wave's region (its activations are no longer read), then the
     //    fixed-order sum over the 16 slices
+    //    Layout: each tile row block's 4 accumulators per lane are split into 4 / MS planes of MS
+    //    consecutive values, lane-contiguous, so that both the writes and the reducers' reads (MS
+    //    values per lane) cover contiguous bytes across a wave: no LDS bank conflicts (a float4 per
+    //    lane, read 8 bytes at a time, conflicted two ways).
+    constexpr int NPL = 4 / MS;                                  // planes per tile row block
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms)
-            *reinterpret_cast<float4*>(reg + ((t * MS + ms) * 64 + lane) * 16) =
-                make_float4(accf[t][ms][0], accf[t][ms][1], accf[t][ms][2], accf[t][ms][3]);
+#pragma unroll
+            for (int pl = 0; pl < NPL; ++pl) {
+                float* dst = reinterpret_cast<float*>(reg + (((t * MS + ms) * NPL + pl) * 64 + lane) * (4 * MS));
+#pragma unroll
+                for (int j = 0; j < MS; ++j) dst[j] = accf[t][ms][pl * MS + j];
+            }
     __syncthreads();
     float y[MS];
 #pragma unroll
     for (int j = 0; j < MS; ++j) y[j] = 0.0f;
 #pragma unroll
     for (int w2 = 0; w2 < KW; ++w2) {
-        const float* p = reinterpret_cast<const float*>(smem + w2 * S::REG + ((rt * MS + rms) * 64 + lane) * 16) + ri0;
+        const float* p = reinterpret_cast<const float*>(
+            smem + w2 * S::REG + (((rt * MS + rms) * NPL + ri0 / MS) * 64 + lane) * (4 * MS));
 #pragma unroll
         for (int j = 0; j < MS; ++j) y[j] += p[j];
     }
