@@ -1,4 +1,4 @@
-// Dense W4A8 decode GEMM with one K-slice per wave (17-32 rows, 2048 < K <= 4096).
+// Dense W4A8 decode GEMM with one K-slice per wave (up to 32 rows, 2048 < K <= 4096).
 //
 // Sources (cited with the page's own section names):
 //   P1 "Kimi 2.7 MoE: from 4-bit storage to INT8 (W4A8)" (pwwt.cn), section 5.1-5.2: the INT8
@@ -24,12 +24,11 @@
 // activations land, and the LDS operand reads drop fourfold (one read per operand instead of one
 // per tile).
 //
-// The kernel serves 17-32 rows (32-row tiles).  Measured against the chunked kernel on the 4096 x
-// 14336 projection: 32 rows 9.4-9.6 -> 9.1-9.3 us; at 16-row tiles it was 2 % slower (the 16
-// slice partials per output cost more LDS traffic than the shared activation tile saves there).
-// Folding the per-token quantization into it (every wave quantizing its slice of the bfloat16
-// rows after a workgroup abs-max) was measured and dropped: 8 rows 10.7 -> 14.4 us, since every
-// workgroup repeats the whole quantization.
+// The kernel serves 16-row tiles (1-16 rows) and 32-row tiles (17-32 rows).  Measured against the
+// chunked kernel on the 4096 x 14336 projection: 32 rows 9.4-9.6 -> 8.9-9.0 us, 16 rows 8.0 -> 7.7-7.8
+// us, 8 rows 7.9-8.1 -> 7.8 us.  Folding the per-token quantization into it (every wave
+// quantizing its slice of the bfloat16 rows after a workgroup abs-max) was measured and dropped:
+// 8 rows 10.7 -> 14.4 us, since every workgroup repeats the whole quantization.
 #include <hip/hip_runtime.h>
 
 #include "w4a8_device.h"
@@ -242,13 +241,13 @@ __global__ __launch_bounds__(1024) void gemm_decode_split_kernel(GemmArgs a) {
 
 bool decode_split_fits(int K, int M, int gps, int bits) {
     const int nsb = K / SB_K;
-    return bits == 4 && (gps == 1 || gps == 2) && M > 16 && M <= 32 && nsb > 16 && nsb <= 32;
+    return bits == 4 && (gps == 1 || gps == 2) && M >= 1 && M <= 32 && nsb > 16 && nsb <= 32;
 }
 
-template <int GPS, bool ASYM, bool H16>
+template <int MS, int GPS, bool ASYM, bool H16>
 static void launch_split_t(const GemmArgs& a, hipStream_t s) {
-    using S = DecodeSplitShape<2, 2>;
-    auto kern = gemm_decode_split_kernel<2, 2, GPS, ASYM, H16>;
+    using S = DecodeSplitShape<MS, 2>;
+    auto kern = gemm_decode_split_kernel<MS, 2, GPS, ASYM, H16>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(S::LDS));
     (void)attr;
@@ -257,14 +256,20 @@ static void launch_split_t(const GemmArgs& a, hipStream_t s) {
     kern<<<grid, dim3(S::NTHR), S::LDS, s>>>(a);
 }
 
-void launch_decode_split(const GemmArgs& a, int gps, bool asym, hipStream_t s) {
+template <int MS>
+static void launch_split_ms(const GemmArgs& a, int gps, bool asym, hipStream_t s) {
     if (gps == 1) {
-        if (a.h16) { if (asym) launch_split_t<1, true, true>(a, s); else launch_split_t<1, false, true>(a, s); }
-        else if (asym) launch_split_t<1, true, false>(a, s); else launch_split_t<1, false, false>(a, s);
+        if (a.h16) { if (asym) launch_split_t<MS, 1, true, true>(a, s); else launch_split_t<MS, 1, false, true>(a, s); }
+        else if (asym) launch_split_t<MS, 1, true, false>(a, s); else launch_split_t<MS, 1, false, false>(a, s);
     } else {
-        if (a.h16) { if (asym) launch_split_t<2, true, true>(a, s); else launch_split_t<2, false, true>(a, s); }
-        else if (asym) launch_split_t<2, true, false>(a, s); else launch_split_t<2, false, false>(a, s);
+        if (a.h16) { if (asym) launch_split_t<MS, 2, true, true>(a, s); else launch_split_t<MS, 2, false, true>(a, s); }
+        else if (asym) launch_split_t<MS, 2, true, false>(a, s); else launch_split_t<MS, 2, false, false>(a, s);
     }
+}
+
+void launch_decode_split(const GemmArgs& a, int gps, bool asym, hipStream_t s) {
+    if (a.M <= 16) launch_split_ms<1>(a, gps, asym, s);
+    else launch_split_ms<2>(a, gps, asym, s);
 }
 
 }  // namespace w4a8

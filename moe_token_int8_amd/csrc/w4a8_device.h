@@ -255,7 +255,7 @@ void launch_moe_stream(const GemmArgs& a, int mt, int gps, bool asym, int slots,
 void launch_moe_tile(const GemmArgs& a, int gps, bool asym, int slots, hipStream_t s);
 
 // Dense decode GEMM with one K-slice per wave (w4a8_decode_kernels.hip): 4-bit codes, g in {64, 128},
-// 17 <= M <= 32, 2048 < K <= 4096.
+// M <= 32, 2048 < K <= 4096.
 bool decode_split_fits(int K, int M, int gps, int bits);
 void launch_decode_split(const GemmArgs& a, int gps, bool asym, hipStream_t s);
 

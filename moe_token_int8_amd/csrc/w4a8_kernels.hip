@@ -1886,7 +1886,8 @@ int w4a8_gemm(const int8_t* Xq, const float* sx, int M, const void* blob, const 
         launch_prefill<MODE_OUT>(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream), L.bits == 8);
         return launch_status();
     }
-    // rows that w4a8_linear quantizes inside the GEMM stay on the chunked kernel, whose fused form
+    // the split kernel (one K-slice per wave) serves the decode rows, except those that
+    // w4a8_linear quantizes inside the GEMM: they stay on the chunked kernel, whose fused form
     // shares its summation order (fused and unfused results are bit-identical)
     if (!linear_fuses(L, M) && decode_split_fits(L.K, M, gps_of(d), L.bits)) {
         launch_decode_split(a, gps_of(d), d->asymmetric, static_cast<hipStream_t>(stream));

@@ -1,11 +1,11 @@
 """GPU parity of the dense decode GEMM with one K-slice per wave (4-bit codes, g in {64, 128},
-17-32 rows, 2048 < K <= 4096; P1 section 5.2, P5 section 7).
+up to 32 rows in 16- or 32-row tiles, 2048 < K <= 4096; P1 section 5.2, P5 section 7).
 
 Each case runs w4a8_gemm through the C-ABI and checks the float32 and bfloat16 outputs against the
 oracle (gpu_cases.check_float_output: float32 within 1e-3 of the float64 product, bfloat16 equal to
 the round-to-nearest-even of the float32 output).  The shapes reach the kernel's edges: ragged N
 (a workgroup's last column tiles past N), ragged K (waves whose slice is partly or wholly past K),
-row counts that leave part of the 32-row tile empty, asymmetric codes, binary16 scales, and a
+row counts that leave part of the 16- or 32-row tile empty, asymmetric codes, binary16 scales, and a
 strided output whose columns past N must stay untouched."""
 import numpy as np
 import pytest
@@ -39,6 +39,13 @@ def _print(*a):
     (20, 4096, 64, 64, True, True),
     (32, 4096, 14336, 128, False, False),  # the decode projection at 32 rows
     (18, 3968, 200, 128, True, False),    # 31 superblocks, ragged N inside a tile
+    # 16-row tiles (rows that w4a8_linear does not quantize inside the chunked kernel)
+    (3, 4096, 40, 128, False, False),     # 3 of 4 tile slots, 3 of 16 rows
+    (8, 4096, 14336, 128, False, False),  # the decode projection at 8 rows
+    (16, 3072, 1024, 64, True, False),
+    (4, 2176, 72, 128, True, False),      # 17 superblocks
+    (9, 2560, 48, 64, False, True),       # binary16 scales
+    (11, 3968, 200, 128, False, False),
 ])
 def test_decode_split_vs_oracle(M, K, N, g, asym, h16):
     _print(f"decode split M={M} K={K} N={N} g={g} asym={asym} h16={h16}")
