@@ -42,18 +42,19 @@ def build(verbose: bool = False) -> str:
     failed = [cmd for p, cmd in procs if p.wait() != 0]
     if failed:
         raise subprocess.CalledProcessError(1, failed[0])
-    # the INT8 MFMA peak microbenchmark (a standalone program; not part of the library)
-    mb_src = os.path.join(PKG, "microbench", "mfma_peak.hip")
-    mb = subprocess.Popen([HIPCC, "-O3", "-std=c++17", *DEVICE_FLAGS, mb_src, "-o",
-                           os.path.join(PKG, "_build", "mfma_peak")])
+    # the INT8 MFMA peak and HBM streaming-read microbenchmarks (standalone programs; not part of
+    # the library)
+    mbs = [subprocess.Popen([HIPCC, "-O3", "-std=c++17", *DEVICE_FLAGS, os.path.join(PKG, "microbench", name + ".hip"),
+                             "-o", os.path.join(PKG, "_build", name)]) for name in ("mfma_peak", "hbm_read")]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "-pthread", *DEVICE_FLAGS, *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
-    if mb.wait() != 0:
-        raise subprocess.CalledProcessError(mb.returncode, mb_src)
+    for mb in mbs:
+        if mb.wait() != 0:
+            raise subprocess.CalledProcessError(mb.returncode, mb.args)
     return LIB
 
 
