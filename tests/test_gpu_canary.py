@@ -52,7 +52,10 @@ def _weights(K, N, g, asym, seed):
 
 
 @pytest.mark.parametrize("M,K,N,g,asym", [(5, 1024, 80, 128, False), (23, 512, 200, 64, True),
-                                          (300, 512, 200, 128, True), (1, 4096, 48, 128, False)])
+                                          (300, 512, 200, 128, True), (1, 4096, 48, 128, False),
+                                          # the split decode kernel: 16- and 32-row tiles, ragged N and K
+                                          (9, 3072, 200, 64, True), (29, 4096, 72, 128, False),
+                                          (20, 2176, 40, 64, False)])
 def test_gemm_outputs_guarded_and_deterministic(M, K, N, g, asym):
     _print(f"guards: quant + gemm + linear + w4a16 M={M} K={K} N={N} g={g} asym={asym}")
     d, blob = _weights(K, N, g, asym, M + K + N)
