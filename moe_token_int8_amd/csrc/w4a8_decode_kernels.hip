@@ -25,8 +25,8 @@
 // per tile).
 //
 // The kernel serves 16-row tiles (1-16 rows) and 32-row tiles (17-32 rows).  Measured against the
-// chunked kernel on the 4096 x 14336 projection: 32 rows 9.4-9.6 -> 8.9-9.0 us, 16 rows 8.0 -> 7.7-7.8
-// us, 8 rows 7.9-8.1 -> 7.8 us.  Folding the per-token quantization into it (every wave
+// chunked kernel on the 4096 x 14336 projection: 32 rows 9.4-9.6 -> 8.9-9.0 us, 16 rows 8.0 ->
+// 7.7-7.8 us, 8 rows 7.9-8.1 -> 7.8 us.  Folding the per-token quantization into it (every wave
 // quantizing its slice of the bfloat16 rows after a workgroup abs-max) was measured and dropped:
 // 8 rows 10.7 -> 14.4 us, since every workgroup repeats the whole quantization.
 #include <hip/hip_runtime.h>
@@ -41,7 +41,7 @@ struct DecodeSplitShape {
     static constexpr int NT = 4, KW = 16, MT = 16 * MS, NTHR = 64 * KW;
     static constexpr int ROWB = SW * SB_K + 32;                 // padded row of a wave's slice
     static constexpr int ACT = MT * ROWB;                       // activation bytes of a wave region
-    static constexpr int PART = NT * MS * 64 * 16;              // slice partials: a float4 per lane and tile row block
+    static constexpr int PART = NT * MS * 64 * 16;              // slice partials: 4 floats per lane and tile row block
     static constexpr int REG = ACT > PART ? ACT : PART;
     static constexpr size_t LDS = size_t(KW) * REG;
 };
