@@ -438,7 +438,11 @@ int w4a8_moe_forward_static(const void* X_bf16, const int32_t* topk_ids, const f
                             void* workspace, size_t workspace_bytes, void* out_bf16, void* stream);
 
 /* Name of the kernel variant w4a8_gemm resolves to for (d, M), or "unsupported"
- * (P4: record target and resolved backend so a silent fallback is visible). */
+ * (P4: record target and resolved backend so a silent fallback is visible):
+ * {w4a8,w8a8}_{decode_m16,decode_m32,prefill}_{sym,asym}_g{64,128,256,K,32}[_h16], and
+ * w4a8_decode_split_m{16,32}_... for the decode GEMMs served by the kernel with one K-slice per
+ * wave (4-bit codes, g in {64, 128}, 2048 < K <= 4096, rows w4a8_linear does not quantize
+ * inside the GEMM). */
 const char* w4a8_kernel_name(const w4a8_wdesc* d, int M);
 
 /* Human-readable text of a w4a8_status. */

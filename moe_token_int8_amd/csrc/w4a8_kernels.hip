@@ -2538,6 +2538,20 @@ const char* w4a8_kernel_name(const w4a8_wdesc* d, int M) {
     const int kind = M >= PREFILL_MIN_M ? 2 : (dense_mt(M) == 32 ? 1 : 0);
     const int gps = gps_of(d);
     const int gi = gps == 2 ? 0 : gps == 1 ? 1 : gps == 0 ? 2 : gps == 4 ? 4 : 3;
+    // the decode GEMMs that w4a8_gemm routes to the split kernel (one K-slice per wave):
+    // [row tile][asym][g128][binary16 scales]
+    static const char* const split_names[2][2][2][2] = {
+        {{{"w4a8_decode_split_m16_sym_g64", "w4a8_decode_split_m16_sym_g64_h16"},
+          {"w4a8_decode_split_m16_sym_g128", "w4a8_decode_split_m16_sym_g128_h16"}},
+         {{"w4a8_decode_split_m16_asym_g64", "w4a8_decode_split_m16_asym_g64_h16"},
+          {"w4a8_decode_split_m16_asym_g128", "w4a8_decode_split_m16_asym_g128_h16"}}},
+        {{{"w4a8_decode_split_m32_sym_g64", "w4a8_decode_split_m32_sym_g64_h16"},
+          {"w4a8_decode_split_m32_sym_g128", "w4a8_decode_split_m32_sym_g128_h16"}},
+         {{"w4a8_decode_split_m32_asym_g64", "w4a8_decode_split_m32_asym_g64_h16"},
+          {"w4a8_decode_split_m32_asym_g128", "w4a8_decode_split_m32_asym_g128_h16"}}}};
+    const Layout L = layout_of(d);
+    if (kind < 2 && M > 0 && !linear_fuses(L, M) && decode_split_fits(L.K, M, gps, L.bits))
+        return split_names[kind][d->asymmetric ? 1 : 0][gps == 1 ? 1 : 0][L.sbytes == 2 ? 1 : 0];
     if (layout_of(d).sbytes == 2) return names16[kind][d->asymmetric][gi];
     return names[layout_of(d).bits == 8][kind][d->asymmetric][gi];
 }

@@ -160,7 +160,7 @@ def test_fp16_scales_validation_and_names_host():
     assert L.w4a8_packed_size(L.desc(128, 16, 64, False, scale_bits=24)) == 0
     d = L.desc(4096, 64, 128, True, scale_bits=16)
     assert L.w4a8_kernel_name(d, 1) == "w4a8_decode_m16_asym_g128_h16"
-    assert L.w4a8_kernel_name(d, 32) == "w4a8_decode_m32_asym_g128_h16"
+    assert L.w4a8_kernel_name(d, 32) == "w4a8_decode_split_m32_asym_g128_h16"
     assert L.w4a8_kernel_name(L.desc(4096, 64, 64, False, scale_bits=16), 64) == "w4a8_prefill_sym_g64_h16"
     for bad in (L.desc(4096, 64, 256, False, scale_bits=16), L.desc(4096, 64, 4096, False, scale_bits=16),
                 L.desc(4096, 64, 128, False, bits=8, scale_bits=16)):
@@ -206,6 +206,14 @@ def test_g256_names_and_grouped_form_rejected_host():
     assert L.w4a8_kernel_name(d, 40) == "w4a8_prefill_asym_g256"
     assert L.w4a8_kernel_name(L.desc(1024, 64, 256, False, bits=8), 40) == "w8a8_prefill_sym_g256"
     assert L.w4a8_kernel_name(L.desc(1024, 64, 64, False), 8) == "w4a8_decode_m16_sym_g64"
+    # the split decode kernel (one K-slice per wave): 4-bit codes, g in {64, 128}, 2048 < K <= 4096,
+    # rows that w4a8_linear does not quantize inside the chunked kernel
+    assert L.w4a8_kernel_name(L.desc(4096, 64, 64, False), 8) == "w4a8_decode_split_m16_sym_g64"
+    assert L.w4a8_kernel_name(L.desc(4096, 64, 64, False), 2) == "w4a8_decode_m16_sym_g64"
+    assert L.w4a8_kernel_name(L.desc(2048, 64, 64, False), 8) == "w4a8_decode_m16_sym_g64"
+    assert L.w4a8_kernel_name(L.desc(3072, 64, 128, True), 17) == "w4a8_decode_split_m32_asym_g128"
+    assert L.w4a8_kernel_name(L.desc(4096, 64, 128, False, bits=8), 32) == "w8a8_decode_m32_sym_g128"
+    assert L.w4a8_kernel_name(L.desc(4096, 64, 32, False), 32) == "w4a8_decode_m32_sym_g32"
     assert L.w4a8_kernel_name(L.desc(1024, 64, 32, False), 8) == "w4a8_decode_m16_sym_g32"
     fake = 0x10000
     assert lib.w4a8_moe_gemm(fake, fake, fake, 2, fake, 4, 8, 8, fake, 1 << 20, ctypes.byref(d), fake, 0,
@@ -602,7 +610,7 @@ def test_log_names_the_resolved_kernel():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120,
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert r.returncode == 0, r.stderr
-    assert "w4a8: w4a8_gemm M=32 K=4096 N=14336 -> w4a8_decode_m32_sym_g128" in r.stderr
+    assert "w4a8: w4a8_gemm M=32 K=4096 N=14336 -> w4a8_decode_split_m32_sym_g128" in r.stderr
     assert "w4a8: w4a8_gemm M=4096 K=4096 N=14336 -> w4a8_prefill_asym_g128" in r.stderr
     assert "w4a8: w4a16_gemm M=8 K=4096 N=14336 -> w4a16_decode_m16_sym_g128" in r.stderr
     env["W4A8_LOG"] = "0"
