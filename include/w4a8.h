@@ -402,15 +402,17 @@ typedef struct {
 
 /* One MoE expert layer whose experts use different weight formats (P1 section 8: quantize at
  * expert granularity, with a group size and format per expert, so that sensitive experts can
- * be kept at a finer format).  The steps of w4a8_moe_forward; each grouped GEMM runs
- * once per set, over that set's experts.  The group size, zero points and scale width may
- * differ between sets; the shapes (gate/up [H, 2I], down [I, H]) may not (EINVAL).
- * The sets' grouped GEMMs are independent (disjoint experts, disjoint rows): set 0 runs on
- * `stream`, the others on up to four helper streams of the current device, forked from `stream`
- * and joined back into it with events, so the call completes in `stream` order and can be
- * captured into a graph.  The helpers (default priority) are created by the first call with
- * two or more sets that is not made under graph capture, and kept until the process ends; a
- * call made before they exist, or where they cannot be created, runs the sets one after
+ * be kept at a finer format).  The steps of w4a8_moe_forward.  The group size, zero points and
+ * scale width may differ between sets; the shapes (gate/up [H, 2I], down [I, H]) may not (EINVAL).
+ * A grouped GEMM whose K (H for gate/up, I for down) is at most 4096 runs every set in one
+ * launch pair on `stream` when there are at most four sets: each workgroup takes the format of
+ * its expert's set, so the result is that of one launch per set.  Otherwise the GEMM runs once
+ * per set, over that set's experts; these launches are independent (disjoint experts, disjoint
+ * rows): set 0 runs on `stream`, the others on up to four helper streams of the current device,
+ * forked from `stream` and joined back into it with events, so the call completes in `stream`
+ * order and can be captured into a graph.  The helpers (default priority) are created by the
+ * first call that needs them and is not made under graph capture, and kept until the process
+ * ends; a call made before they exist, or where they cannot be created, runs the sets one after
  * another on `stream`.  Calls from several host threads enqueue one at a time.
  *   sets, nsets  host array of the format classes; E = sum of n_experts <= 1024
  *   workspace    device, >= w4a8_moe_workspace_size(T, k, H, I, E) bytes, 256-aligned

@@ -246,13 +246,47 @@ __device__ __forceinline__ TileRows moe_tile(const GemmArgs& a, int slot, int la
     return tr;
 }
 
+// Format classes of one grouped launch (experts of different weight formats, P1 section 8).
+// Class c holds the experts [first, e_end[c]) with first = e_end[c - 1] (0 for c = 0); expert e
+// of class c has its blob at blob[c] + (e - first) * stride[c], G[c] groups along K and the
+// blob sections at codes_off[c], scales_off[c], zeros_off[c].  fmt[c] = (gps - 1) | asym << 1 |
+// h16 << 2 selects the code a workgroup of that class runs.  Every class has the launch's K and N.
+constexpr int MOE_MAX_CLASSES = 4;
+struct MoeClasses {
+    int n;
+    int e_end[MOE_MAX_CLASSES];
+    int fmt[MOE_MAX_CLASSES];
+    int G[MOE_MAX_CLASSES];
+    const uint8_t* blob[MOE_MAX_CLASSES];
+    size_t stride[MOE_MAX_CLASSES];
+    size_t codes_off[MOE_MAX_CLASSES], scales_off[MOE_MAX_CLASSES], zeros_off[MOE_MAX_CLASSES];
+};
+
+// The class of expert e (uniform over the workgroup): a's group count and blob sections become
+// the class's, blob is the expert's blob; returns the class's fmt.  An expert past the last
+// class's end (malformed e_end) takes the last class.
+__device__ __forceinline__ int moe_class_resolve(const MoeClasses& mc, int e, GemmArgs& a, const uint8_t*& blob) {
+    int c = 0;
+    while (c + 1 < mc.n && e >= mc.e_end[c]) ++c;
+    const int first = c ? mc.e_end[c - 1] : 0;
+    a.G = mc.G[c];
+    a.codes_off = mc.codes_off[c];
+    a.scales_off = mc.scales_off[c];
+    a.zeros_off = mc.zeros_off[c];
+    blob = mc.blob[c] + size_t(e - first) * mc.stride[c];
+    return mc.fmt[c];
+}
+
 // Grouped streaming GEMM (w4a8_moe_kernels.hip): every expert of a launch, K <= 4096, g in {64, 128}.
 bool moe_stream_fits(int K, int gps);
 void launch_moe_stream(const GemmArgs& a, int mt, int gps, bool asym, int slots, hipStream_t s);
+// the same over format classes: each workgroup runs the code of its expert's class
+void launch_moe_stream_classes(const GemmArgs& a, const MoeClasses& mc, int mt, int slots, hipStream_t s);
 
 // Grouped GEMM on 128 x 128 MFMA tiles (w4a8_moe_tile_kernels.hip) over the experts with
 // moe_lo <= rows < moe_hi, g in {64, 128}; slots bounds the sum over those experts of ceil(rows_e / 128).
 void launch_moe_tile(const GemmArgs& a, int gps, bool asym, int slots, hipStream_t s);
+void launch_moe_tile_classes(const GemmArgs& a, const MoeClasses& mc, int slots, hipStream_t s);
 
 // Dense decode GEMM with one K-slice per wave (w4a8_decode_kernels.hip): 4-bit codes, g in {64, 128},
 // M <= 32, 2048 < K <= 4096.

@@ -2083,7 +2083,7 @@ static int join_from(ForkSet* f, hipStream_t s, int i0, int i1) {
 static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gather, int k, const int32_t* offsets,
                          int E, int rows, int src_rows, const void* blobs, size_t stride, const w4a8_wdesc* d,
                          void* Y, int out_dtype, int mt, hipStream_t s, int8_t* Hq = nullptr, float* sh = nullptr,
-                         const float* s_dn = nullptr, int rows_cap = 1 << 30) {
+                         const float* s_dn = nullptr, int rows_cap = 1 << 30, const MoeClasses* mc = nullptr) {
     const bool tiles = rows >= MOE_TILE_MIN_ROWS && rows_cap >= MOE_TILE_MIN_ROWS;
     const Layout L = layout_of(d);
     if (log_on()) {
@@ -2117,7 +2117,9 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
         // experts with many rows: prefill tiles; slots bound sum_e ceil(rows_e / tile rows) over
         // experts with rows_e >= MOE_TILE_MIN_ROWS (surplus workgroups find no tile and exit)
         a.moe_lo = MOE_TILE_MIN_ROWS;
-        launch_moe_tile(a, gps_of(d), d->asymmetric, rows / 128 + rows / MOE_TILE_MIN_ROWS + 1, s);
+        const int tslots = rows / 128 + rows / MOE_TILE_MIN_ROWS + 1;
+        if (mc) launch_moe_tile_classes(a, *mc, tslots, s);
+        else launch_moe_tile(a, gps_of(d), d->asymmetric, tslots, s);
         a.moe_lo = 0;
         a.moe_hi = MOE_TILE_MIN_ROWS;
     }
@@ -2126,9 +2128,11 @@ static int moe_gemm_impl(const int8_t* Xq, const float* sx, const int32_t* gathe
     if (moe_stream_fits(L.K, gps_of(d))) {
         // the experts below the MFMA-tile cut in one streaming launch: each workgroup stages one
         // row tile of one expert and streams 256 of its columns
-        launch_moe_stream(a, mt, gps_of(d), d->asymmetric, slots, s);
+        if (mc) launch_moe_stream_classes(a, *mc, mt, slots, s);
+        else launch_moe_stream(a, mt, gps_of(d), d->asymmetric, slots, s);
         return launch_status();
     }
+    if (mc) return W4A8_EUNSUPPORTED;                // format classes: streaming kernels only
     // 2048 < K <= 4096: 16-row tiles run in a row loop (32-row tiles would not leave the
     // registers for it), so each expert's weights are read once per column tile
     const int nsb = L.K / SB_K;
@@ -2450,11 +2454,43 @@ int w4a8_moe_forward_sets(const void* X, const int32_t* ids, const float* w, int
     // of those experts, so the sets write disjoint output rows.  Set 0 runs on the caller's stream,
     // set i > 0 on helper (i - 1) % FORK_STREAMS, side by side.
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // a GEMM whose K fits the streaming kernels runs every set in one launch pair (tiles, then
+    // streaming), each workgroup taking the format of its expert's set
+    const bool one_gu = nsets > 1 && nsets <= MOE_MAX_CLASSES && moe_stream_fits(H, 1);
+    const bool one_dn = nsets > 1 && nsets <= MOE_MAX_CLASSES && moe_stream_fits(I, 1);
+    const int mt = R / E >= 16 ? 32 : 16;
+    auto classes = [&](bool gate_up) {
+        MoeClasses mc{};
+        mc.n = nsets;
+        for (int i = 0, e0 = 0; i < nsets; ++i) {
+            const w4a8_wdesc* d = gate_up ? sets[i].gu_desc : sets[i].d_desc;
+            const Layout Lc = layout_of(d);
+            e0 += sets[i].n_experts;
+            mc.e_end[i] = e0;
+            mc.fmt[i] = (gps_of(d) - 1) | (Lc.asym ? 2 : 0) | (Lc.sbytes == 2 ? 4 : 0);
+            mc.G[i] = Lc.G;
+            mc.blob[i] = static_cast<const uint8_t*>(gate_up ? sets[i].gu_blobs : sets[i].d_blobs);
+            mc.stride[i] = gate_up ? sets[i].gu_stride : sets[i].d_stride;
+            mc.codes_off[i] = Lc.codes_off;
+            mc.scales_off[i] = Lc.scales_off;
+            mc.zeros_off[i] = Lc.zeros_off;
+        }
+        return mc;
+    };
     std::lock_guard<std::mutex> lock(fork_mu);
-    ForkSet* f = nsets > 1 ? fork_set(s) : nullptr;
+    ForkSet* f = nsets > 1 && !(one_gu && one_dn) ? fork_set(s) : nullptr;
     const int nh = f ? std::min(nsets - 1, FORK_STREAMS) : 0;
     auto stage = [&](bool gate_up) -> int {
         int r;
+        if (gate_up ? one_gu : one_dn) {
+            const MoeClasses mc = classes(gate_up);
+            return gate_up ? moe_gemm_impl(B.xq, B.sx, B.rows, k, B.offs, E, R, T, sets[0].gu_blobs,
+                                           sets[0].gu_stride, sets[0].gu_desc, B.gu, W4A8_OUT_BF16, mt, s,
+                                           nullptr, nullptr, nullptr, T, &mc)
+                           : moe_gemm_impl(B.hq, B.sh, nullptr, k, B.offs, E, R, R, sets[0].d_blobs,
+                                           sets[0].d_stride, sets[0].d_desc, B.yd, W4A8_OUT_BF16, mt, s,
+                                           nullptr, nullptr, nullptr, T, &mc);
+        }
         if (nh && (r = fork_to(f, s, 0, nh))) return r;
         for (int i = 0, e0 = 0; i < nsets; e0 += sets[i].n_experts, ++i) {
             const w4a8_expert_set& c = sets[i];

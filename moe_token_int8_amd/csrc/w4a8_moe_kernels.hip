@@ -45,8 +45,9 @@ struct MoeStreamShape {
     static_assert(NTHR == 512, "8 waves: two per SIMD, so each has 256 registers");
 };
 
-template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16, int TILES = MST_TILES>
-__global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
+// One workgroup's row tile tr of one expert, whose blob is `blob` (the format is the template's).
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16, int TILES>
+__device__ __forceinline__ void moe_stream_body(const GemmArgs& a, const TileRows tr, const uint8_t* blob) {
     using S = MoeStreamShape<MS, NT, KW, TILES>;
     constexpr int MT = S::MT, NTHR = S::NTHR, CG = S::CG, NV = MS * 4;
     // activation pieces (16 bytes) per thread: the K <= KW * SBN * 128 rows of a full tile
@@ -60,10 +61,7 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
     const int ntiles = (a.N + 15) / 16;
     const int nsb = K / SB_K;
 
-    const TileRows tr = moe_tile<MT>(a, blockIdx.y, lane);
-    if (tr.expert < 0) return;                                   // uniform over the workgroup
     const int rbeg = tr.rbeg, nrows = tr.rend - tr.rbeg;
-    const uint8_t* blob = a.blob + size_t(tr.expert) * a.expert_stride;
     const uint8_t* codes = blob + a.codes_off;
     const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
     const uint16_t* scales16 = reinterpret_cast<const uint16_t*>(blob + a.scales_off);
@@ -242,6 +240,37 @@ __global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
     if (pair && blockIdx.x == 0 && tid < nrows) a.sh[rbeg + tid] = s_e;
 }
 
+template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16, int TILES = MST_TILES>
+__global__ __launch_bounds__(512) void gemm_moe_stream_kernel(GemmArgs a) {
+    const TileRows tr = moe_tile<16 * MS>(a, blockIdx.y, int(threadIdx.x) & 63);
+    if (tr.expert < 0) return;                                   // uniform over the workgroup
+    moe_stream_body<MS, NT, KW, SBN, GPS, ASYM, H16, TILES>(a, tr, a.blob + size_t(tr.expert) * a.expert_stride);
+}
+
+// Format classes in one launch: the workgroup resolves its expert's class, then runs the code of
+// that class's format (every branch is uniform over the workgroup; only one is taken).
+template <int MS, int NT, int KW, int SBN, int TILES>
+__global__ __launch_bounds__(512) void gemm_moe_stream_classes_kernel(GemmArgs a, MoeClasses mc) {
+    const TileRows tr = moe_tile<16 * MS>(a, blockIdx.y, int(threadIdx.x) & 63);
+    if (tr.expert < 0) return;
+    const uint8_t* blob;
+    const int fmt = __builtin_amdgcn_readfirstlane(moe_class_resolve(mc, __builtin_amdgcn_readfirstlane(tr.expert), a, blob));
+#define W4A8_MSC(F_, GPS_, ASYM_, H16_) \
+    case F_: moe_stream_body<MS, NT, KW, SBN, GPS_, ASYM_, H16_, TILES>(a, tr, blob); break;
+    switch (fmt) {
+        W4A8_MSC(0, 1, false, false)
+        W4A8_MSC(1, 2, false, false)
+        W4A8_MSC(2, 1, true, false)
+        W4A8_MSC(3, 2, true, false)
+        W4A8_MSC(4, 1, false, true)
+        W4A8_MSC(5, 2, false, true)
+        W4A8_MSC(6, 1, true, true)
+        W4A8_MSC(7, 2, true, true)
+        default: break;
+    }
+#undef W4A8_MSC
+}
+
 template <int MS, int NT, int KW, int SBN, int GPS, bool ASYM, bool H16, int TILES>
 static void launch_moe_stream_t(const GemmArgs& a, int slots, hipStream_t s) {
     using S = MoeStreamShape<MS, NT, KW, TILES>;
@@ -292,6 +321,36 @@ void launch_moe_stream(const GemmArgs& a, int mt, int gps, bool asym, int slots,
         else { if (asym) W4A8_MST(2, 2, true); else W4A8_MST(2, 2, false); }
     }
 #undef W4A8_MST
+}
+
+template <int MS, int NT, int KW, int SBN, int TILES>
+static void launch_moe_stream_classes_t(const GemmArgs& a, const MoeClasses& mc, int slots, hipStream_t s) {
+    using S = MoeStreamShape<MS, NT, KW, TILES>;
+    auto kern = gemm_moe_stream_classes_kernel<MS, NT, KW, SBN, TILES>;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       int(S::lds(KW * SBN * SB_K)));
+    (void)attr;
+    const int ntiles = (a.N + 15) / 16;
+    kern<<<dim3((ntiles + TILES - 1) / TILES, slots), dim3(S::NTHR), S::lds(a.K), s>>>(a, mc);
+}
+
+template <int MS, int TILES = MST_TILES>
+static void launch_moe_stream_classes_k(const GemmArgs& a, const MoeClasses& mc, int slots, hipStream_t s) {
+    const int nsb = a.K / SB_K;
+    if (nsb <= 8) launch_moe_stream_classes_t<MS, 2, 4, 2, TILES>(a, mc, slots, s);
+    else if (nsb <= 12) launch_moe_stream_classes_t<MS, 2, 4, 3, TILES>(a, mc, slots, s);
+    else if (nsb <= 16) launch_moe_stream_classes_t<MS, 2, 4, 4, TILES>(a, mc, slots, s);
+    else if (nsb <= 24) launch_moe_stream_classes_t<MS, 2, 4, 6, TILES>(a, mc, slots, s);
+    else launch_moe_stream_classes_t<MS, 2, 4, 8, TILES>(a, mc, slots, s);
+}
+
+void launch_moe_stream_classes(const GemmArgs& a, const MoeClasses& mc, int mt, int slots, hipStream_t s) {
+    const long long ntiles = (a.N + 15) / 16;
+    const bool wide = (long long)slots * ((ntiles + MST_TILES - 1) / MST_TILES) >= MST_WIDE_MIN_WG;
+    if (mt == 16 && wide) launch_moe_stream_classes_k<1, MST_TILES_WIDE>(a, mc, slots, s);
+    else if (mt == 16) launch_moe_stream_classes_k<1>(a, mc, slots, s);
+    else launch_moe_stream_classes_k<2>(a, mc, slots, s);
 }
 
 }  // namespace w4a8

@@ -48,8 +48,9 @@ constexpr int MTL_STAGE = MTL_BM * MTL_ROWB;            // 20 KiB
 constexpr int MTL_LDS = 2 * MTL_STAGE;
 
 // GPS: groups per superblock, 2 (g = 64) or 1 (g = 128).  H16: binary16 group scales.
+// One workgroup's 128-row tile tr of one expert, whose blob is `blob` (the format is the template's).
 template <int GPS, bool ASYM, bool H16>
-__global__ __launch_bounds__(MTL_THREADS, 4) void gemm_moe_tile_kernel(GemmArgs a) {
+__device__ __forceinline__ void moe_tile_body(const GemmArgs& a, const TileRows tr, const uint8_t* blob) {
     static_assert(GPS == 1 || GPS == 2, "grouped formats: g in {64, 128}");
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -57,10 +58,7 @@ __global__ __launch_bounds__(MTL_THREADS, 4) void gemm_moe_tile_kernel(GemmArgs 
     const int ntl16 = (a.N + 15) / 16;
     const int ntiles = (ntl16 + 7) / 8;
     const int nt = blockIdx.x % ntiles;
-    const TileRows tr = moe_tile<MTL_BM>(a, blockIdx.x / ntiles, lane);
-    if (tr.expert < 0) return;                           // uniform over the workgroup
     const int m0 = tr.rbeg, mend = tr.rend, expert = tr.expert;
-    const uint8_t* blob = a.blob + size_t(expert) * a.expert_stride;
     const int nsb = a.K / SB_K;
     const uint8_t* codes = blob + a.codes_off;
     const float* scales = reinterpret_cast<const float*>(blob + a.scales_off);
@@ -259,6 +257,43 @@ __global__ __launch_bounds__(MTL_THREADS, 4) void gemm_moe_tile_kernel(GemmArgs 
                     reinterpret_cast<uint16_t*>(a.Y)[yi] = uint16_t(f32_to_bf16_rne(y));
             }
     }
+}
+
+template <int GPS, bool ASYM, bool H16>
+__global__ __launch_bounds__(MTL_THREADS, 4) void gemm_moe_tile_kernel(GemmArgs a) {
+    const int ntiles = ((a.N + 15) / 16 + 7) / 8;
+    const TileRows tr = moe_tile<MTL_BM>(a, int(blockIdx.x) / ntiles, int(threadIdx.x) & 63);
+    if (tr.expert < 0) return;                           // uniform over the workgroup
+    moe_tile_body<GPS, ASYM, H16>(a, tr, a.blob + size_t(tr.expert) * a.expert_stride);
+}
+
+// Format classes in one launch: the workgroup resolves its expert's class, then runs the code of
+// that class's format (every branch is uniform over the workgroup; only one is taken).
+__global__ __launch_bounds__(MTL_THREADS, 4) void gemm_moe_tile_classes_kernel(GemmArgs a, MoeClasses mc) {
+    const int ntiles = ((a.N + 15) / 16 + 7) / 8;
+    const TileRows tr = moe_tile<MTL_BM>(a, int(blockIdx.x) / ntiles, int(threadIdx.x) & 63);
+    if (tr.expert < 0) return;
+    const uint8_t* blob;
+    const int fmt = __builtin_amdgcn_readfirstlane(moe_class_resolve(mc, __builtin_amdgcn_readfirstlane(tr.expert), a, blob));
+#define W4A8_MTC(F_, GPS_, ASYM_, H16_) \
+    case F_: moe_tile_body<GPS_, ASYM_, H16_>(a, tr, blob); break;
+    switch (fmt) {
+        W4A8_MTC(0, 1, false, false)
+        W4A8_MTC(1, 2, false, false)
+        W4A8_MTC(2, 1, true, false)
+        W4A8_MTC(3, 2, true, false)
+        W4A8_MTC(4, 1, false, true)
+        W4A8_MTC(5, 2, false, true)
+        W4A8_MTC(6, 1, true, true)
+        W4A8_MTC(7, 2, true, true)
+        default: break;
+    }
+#undef W4A8_MTC
+}
+
+void launch_moe_tile_classes(const GemmArgs& a, const MoeClasses& mc, int slots, hipStream_t s) {
+    const int ntiles = ((a.N + 15) / 16 + 7) / 8;
+    gemm_moe_tile_classes_kernel<<<dim3(slots * ntiles), dim3(MTL_THREADS), MTL_LDS, s>>>(a, mc);
 }
 
 template <int GPS, bool ASYM, bool H16>

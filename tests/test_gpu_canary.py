@@ -4,8 +4,8 @@ Each output (and the MoE workspace) is a view into a larger buffer whose guard b
 after hold a fixed pattern; after the call the guards must be unchanged, so no kernel writes
 outside the rows and columns it owns (ragged tiles included).  Every entry point is then called
 twice on the same inputs and must give bit-identical outputs (the kernels fix every summation
-order; the format classes of w4a8_moe_forward_sets run on helper streams and must not change
-that)."""
+order; the format classes of w4a8_moe_forward_sets, in one launch or on helper streams, must
+not change that)."""
 import numpy as np
 import pytest
 import torch

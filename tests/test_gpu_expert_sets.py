@@ -1,6 +1,8 @@
 """GPU parity of a MoE layer whose experts come in format classes (P1 section 8: a group size
-and format per expert), through w4a8_moe_forward_sets: each class is one grouped launch over
-its expert range, against the oracle layer with per-expert group sizes."""
+and format per expert), through w4a8_moe_forward_sets, against the oracle layer with per-expert
+group sizes.  A grouped GEMM whose K fits the streaming kernels runs up to four sets in one
+launch pair (each workgroup takes its expert's format); other GEMMs, and layers of more sets,
+run one grouped launch per set."""
 import numpy as np
 import pytest
 import torch
@@ -60,12 +62,15 @@ def _run(cfg, Xb, ids, w, sets):
     return out
 
 
-@pytest.mark.parametrize("name", ["small_rtn", "c4_two_classes", "c5_4tok_two_classes",
+@pytest.mark.parametrize("name", ["small_rtn", "small_rtn_five_classes", "c4_two_classes", "c5_4tok_two_classes",
                                   "c5_full_two_classes_sampled"])
 def test_moe_forward_expert_sets(name):
     if name == "small_rtn":
         cfg, T, rtn = W.MoEConfig("small", 40, 512, 256, 8, 2, 64, True, 51), None, True
         classes = [(4, 64, True, 32), (2, 128, False, 16), (2, 128, True, 32)]
+    elif name == "small_rtn_five_classes":             # more sets than one launch takes: one launch per set
+        cfg, T, rtn = W.MoEConfig("small5", 40, 512, 256, 8, 2, 64, True, 53), None, True
+        classes = [(2, 64, True, 32), (2, 128, False, 16), (1, 128, True, 32), (2, 64, False, 16), (1, 64, True, 16)]
     elif name == "c4_two_classes":                     # hot experts take the 128-row MFMA tiles
         cfg, T, rtn = W.C4, None, False
         classes = [(32, 128, False, 32), (32, 64, True, 16)]
@@ -98,4 +103,32 @@ def test_one_set_equals_moe_forward():
     gu, dn = sets[0]
     L.w4a8_moe_forward(Xb.to(DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), cfg.E,
                        gu.blob, gu.stride, gu.desc, dn.blob, dn.stride, dn.desc, ws, ref)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("asym,sbits,split", [(True, 32, (3, 5)), (False, 16, (1, 3, 2, 2))])
+def test_sets_of_one_format_equal_one_set(asym, sbits, split):
+    """Experts split into sets that share one format give the bits of the single-set layer: one
+    launch over the sets runs each expert with the code of its own set's format, the same code
+    the single-set launch runs.  The skewed routing gives some experts 128-row MFMA tiles."""
+    cfg = W.MoEConfig("split", 300, 1024, 384, 8, 2, 64, asym, 61, zipf_s=1.5)
+    ids, w = W.moe_routing(cfg)
+    counts = np.bincount(ids.ravel(), minlength=cfg.E)
+    assert counts.max() >= 96, counts                  # the MFMA-tile launch has work
+    _print(f"sets of one format: split {split}, rows per expert {counts.tolist()}")
+    Xb = W.moe_activations(cfg)
+    dgu = L.desc(cfg.H, 2 * cfg.I, cfg.group_size, asym, scale_bits=sbits)
+    dd = L.desc(cfg.I, cfg.H, cfg.group_size, asym, scale_bits=sbits)
+    hgu, hd = {}, {}
+    for e in range(cfg.E):
+        hgu[e] = L.w4a8_pack_codes(dgu, *W.random_codes(7 * 1009 + e, cfg.H, 2 * cfg.I, cfg.group_size, asym))
+        hd[e] = L.w4a8_pack_codes(dd, *W.random_codes(7 * 2003 + e, cfg.I, cfg.H, cfg.group_size, asym))
+    one = [(L.experts_to_device(dgu, cfg.E, hgu), L.experts_to_device(dd, cfg.E, hd))]
+    many, e0 = [], 0
+    for n in split:
+        many.append((L.experts_to_device(dgu, n, {e - e0: hgu[e] for e in range(e0, e0 + n)}),
+                     L.experts_to_device(dd, n, {e - e0: hd[e] for e in range(e0, e0 + n)})))
+        e0 += n
+    ref = _run(cfg, Xb, ids, w, one)
+    out = _run(cfg, Xb, ids, w, many)
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

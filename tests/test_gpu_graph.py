@@ -1,6 +1,7 @@
-"""MoE layers captured into a HIP graph.  The format classes of w4a8_moe_forward_sets run side
-by side on helper streams, forked from the caller's stream and joined back with events; a graph
-captured on the caller's stream must hold those branches.  Each test replays the graph several
+"""MoE layers captured into a HIP graph.  The format classes of w4a8_moe_forward_sets run in one
+launch pair per GEMM (up to four sets, K <= 4096) or else side by side on helper streams, forked
+from the caller's stream and joined back with events; a graph captured on the caller's stream
+must hold those branches.  Each test replays the graph several
 times, with eager work and synchronizations in between, and every replay must reproduce the
 eager output bit for bit (the kernels are deterministic)."""
 import numpy as np
@@ -75,13 +76,27 @@ def test_moe_forward_graph_with_hot_experts():
 
 
 def test_moe_forward_sets_graph_two_classes():
-    """Two format classes side by side (class 1 on a helper stream), each with experts of many rows."""
+    """Two format classes in one launch pair per GEMM, each with experts of many rows."""
     _print("graph: moe_forward_sets, two classes")
     cfg, ids, w, X = _layer(400, 6, 2, 512, 256, 12)
     sets = []
     for i, g in enumerate((128, 64)):
         gd, gdev = _experts(20 + i, 3, cfg.H, 2 * cfg.I, g, i == 1)
         dd, ddev = _experts(30 + i, 3, cfg.I, cfg.H, g, i == 1)
+        sets.append((gdev, ddev))
+    ws = torch.empty(L.w4a8_moe_workspace_size(cfg.T, cfg.topk, cfg.H, cfg.I, cfg.E), dtype=torch.uint8, device=DEV)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=DEV)
+    _replays_match(lambda: L.w4a8_moe_forward_sets(X, ids, w, sets, ws, out), out)
+
+
+def test_moe_forward_sets_graph_five_classes():
+    """Five format classes: one launch per set, sets 1-4 on the helper streams."""
+    _print("graph: moe_forward_sets, five classes")
+    cfg, ids, w, X = _layer(400, 10, 2, 512, 256, 13)
+    sets = []
+    for i, (n, g, asym) in enumerate(((2, 128, False), (2, 64, True), (2, 128, True), (2, 64, False), (2, 128, False))):
+        gd, gdev = _experts(40 + i, n, cfg.H, 2 * cfg.I, g, asym)
+        dd, ddev = _experts(50 + i, n, cfg.I, cfg.H, g, asym)
         sets.append((gdev, ddev))
     ws = torch.empty(L.w4a8_moe_workspace_size(cfg.T, cfg.topk, cfg.H, cfg.I, cfg.E), dtype=torch.uint8, device=DEV)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=DEV)
