@@ -447,6 +447,45 @@ def test_moe_gemm_hot_expert_paths(g, asym, K, sbits):
     _print(check_float_output(Y.cpu().numpy(), Ybf.float().cpu().numpy(), Y64))
 
 
+@pytest.mark.parametrize("K,g,asym", [(4096, 64, True), (3200, 64, True), (4096, 128, False), (4096, 64, False)])
+def test_moe_gemm_wide_stream_tiles(K, g, asym):
+    """Grouped streaming kernel on launches of many workgroups (1024 experts, 512 rows, so
+    16-row tiles, and 2048 columns): each workgroup streams 32 column tiles.  At g = 64 with
+    zero points this is the instance that runs its column groups as a loop over pairs; K = 3200
+    leaves the last slice partly past K.  8 experts with 64 rows each (4 row tiles), the others
+    empty."""
+    T, k, E, N = 256, 2, 1024, 2048
+    t = np.arange(T)
+    ids = np.stack([(t % 4) * 256, (t % 4) * 256 + 1], axis=1).astype(np.int32)
+    cnt = np.bincount(ids.ravel(), minlength=E)
+    assert cnt.max() == 64 and int((cnt > 0).sum()) == 8
+    _print(f"wide streaming tiles K={K} g={g} asym={asym}")
+    d = L.desc(K, N, g, asym)
+    host, qw = {}, {}
+    for e in np.flatnonzero(cnt):
+        qw[e] = W.random_codes(17 * g + int(e), K, N, g, asym)
+        host[int(e)] = L.w4a8_pack_codes(d, *qw[e])
+    dev = L.experts_to_device(d, E, host)
+    Xb = W.random_activations(6, T, K, outlier_cols=2, outlier_scale=20.0)
+    Xq, sx = gpu_quant(Xb)
+    rows = torch.empty(T * k, dtype=torch.int32, device=DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    inv = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    L.w4a8_moe_align(torch.from_numpy(ids).to(DEV), E, rows, off, inv)
+    Y = torch.empty((T * k, N), dtype=torch.float32, device=DEV)
+    Ybf = torch.empty((T * k, N), dtype=torch.bfloat16, device=DEV)
+    L.w4a8_moe_gemm(Xq, sx, rows, k, off, E, T * k, dev.blob, dev.stride, d, Y, L.W4A8_OUT_F32)
+    L.w4a8_moe_gemm(Xq, sx, rows, k, off, E, T * k, dev.blob, dev.stride, d, Ybf, L.W4A8_OUT_BF16)
+    q, s = O.quant_act(W.bf16_values(Xb))
+    srt, offs, _ = O.moe_align(ids, E)
+    Y64 = np.zeros((T * k, N))
+    for e in qw:
+        a, b = offs[e], offs[e + 1]
+        toks = srt[a:b] // k
+        Y64[a:b] = O.gemm(q[toks], s[toks], *qw[e], g)
+    _print(check_float_output(Y.cpu().numpy(), Ybf.float().cpu().numpy(), Y64))
+
+
 @pytest.mark.parametrize("K,N,g,asym", [(7168, 400, 64, True), (4608, 272, 128, False), (5120, 128, 64, False)])
 def test_moe_gemm_tile_groups(K, N, g, asym):
     """Grouped GEMM at 16-row tiles with K in (4096, 8192], where each workgroup streams
