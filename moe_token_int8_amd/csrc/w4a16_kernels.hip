@@ -195,7 +195,7 @@ __global__ __launch_bounds__(1024) void gemm_a16_decode_kernel(A16Args a) {
 #pragma unroll
         for (int s = 0; s < SBN; ++s) {
             const int sb = s0 + s;
-            if (sb >= cb + clen) break;
+            if (sb >= cb + clen) continue;              // uniform per wave
             v4f acc[MS];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -496,8 +496,12 @@ int w4a16_gemm(const void* X, int M, int ldx, const void* blob, const w4a8_wdesc
         if (gps == 1) { if (asym) launch_a16_prefill<1, true>(a, s); else launch_a16_prefill<1, false>(a, s); }
         else { if (asym) launch_a16_prefill<2, true>(a, s); else launch_a16_prefill<2, false>(a, s); }
     } else if (M <= 16) {
-        if (gps == 1) { if (asym) launch_a16_decode<1, 32, 1, true>(a, L.Np, s); else launch_a16_decode<1, 32, 1, false>(a, L.Np, s); }
-        else { if (asym) launch_a16_decode<1, 32, 2, true>(a, L.Np, s); else launch_a16_decode<1, 32, 2, false>(a, L.Np, s); }
+        // 16-superblock chunks at both tile heights: with 32-superblock chunks the 16-row form
+        // exceeded the 128 registers a 1024-thread workgroup leaves each lane and kept part of
+        // its superblocks in scratch (K = 4096, N = 14336: g64 with zero points 18.6 -> 10.2 us
+        // at M = 1, 21.0 -> 11.9 us at M = 16; g128 10.2 -> 9.1 us at M = 1)
+        if (gps == 1) { if (asym) launch_a16_decode<1, 16, 1, true>(a, L.Np, s); else launch_a16_decode<1, 16, 1, false>(a, L.Np, s); }
+        else { if (asym) launch_a16_decode<1, 16, 2, true>(a, L.Np, s); else launch_a16_decode<1, 16, 2, false>(a, L.Np, s); }
     } else {
         if (gps == 1) { if (asym) launch_a16_decode<2, 16, 1, true>(a, L.Np, s); else launch_a16_decode<2, 16, 1, false>(a, L.Np, s); }
         else { if (asym) launch_a16_decode<2, 16, 2, true>(a, L.Np, s); else launch_a16_decode<2, 16, 2, false>(a, L.Np, s); }
