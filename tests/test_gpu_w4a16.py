@@ -49,7 +49,9 @@ def _case(M, K, N, g, asym, seed, outliers=2, oscale=30.0, codes=False):
 @pytest.mark.parametrize("M,K,N,g,asym", [(1, 4096, 14336, 128, False), (8, 4096, 14336, 128, False),
                                           (32, 4096, 14336, 128, False), (16, 1024, 1024, 128, False),
                                           (5, 512, 40, 64, True), (3, 384, 33, 128, True), (17, 7168, 96, 64, True),
-                                          (32, 8192, 48, 128, True), (2, 128, 16, 64, False), (20, 14336, 64, 128, True)])
+                                          (32, 8192, 48, 128, True), (2, 128, 16, 64, False), (20, 14336, 64, 128, True),
+                                          # 16-row tiles over several 16-superblock chunks, the last one ragged
+                                          (4, 2176, 72, 64, True), (12, 7168, 200, 128, False), (16, 3200, 64, 64, False)])
 def test_w4a16_decode_vs_oracle(M, K, N, g, asym):
     """Decode shapes (M <= 32): 16- and 32-row tiles, one and several K chunks, ragged N, a K of
     one superblock, symmetric and asymmetric codes, g = 64 and 128."""
